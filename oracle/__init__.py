@@ -1,0 +1,206 @@
+"""fp64 CPU oracle for Semi-Local Attention and the STU layer (ctypes binding).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the bench's
+CPU-baseline leg are the only code that may import this package.  The product
+library never loads it; it shares no code with the HIP path.
+
+The arithmetic lives in ``sla_oracle.c`` (plain C, fp64); this module builds it
+with gcc and converts numpy arrays to fp64 before each call.
+
+Functions whose results are "parity pinned" and the pins (tests/test_oracle_*):
+  visible / mask_dense / count_pairs / tiles  -- closed-form pair count, golden
+      masks, textbook special cases (full causal, sliding window, prefix only).
+  sla_fwd   -- dense numpy/torch fp64 reference, invariants (perturbation,
+      linearity, 1/N scaling, jagged independence, target permutation).
+  sla_bwd   -- central finite differences of sla_fwd, torch fp64 autograd.
+  layernorm / stu_layer_fwd -- torch fp64 functional composition, W2 = 0.
+  truncate  -- direct set construction, identity when tail >= history.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sla_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile sla_oracle.c into liboracle.so with gcc (fp64, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH) or \
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+               "-fno-fast-math", "-ffp-contract=off", "-o", tmp, _SRC, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        i64, i32, dbl = ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        lib.oracle_visible.argtypes = [i64] * 7
+        lib.oracle_visible.restype = ctypes.c_int
+        lib.oracle_mask_dense.argtypes = [i64, i64, i64, i64, i64, P]
+        lib.oracle_mask_dense.restype = None
+        lib.oracle_count_pairs.argtypes = [i32, P, P, i64, i64, i64]
+        lib.oracle_count_pairs.restype = i64
+        lib.oracle_tiles.argtypes = [i32, P, P, i64, i64, i64, i64, i64, P, i64]
+        lib.oracle_tiles.restype = i64
+        lib.oracle_sla_fwd.argtypes = [i32, P, P, i32, i32, i32, i64, i64, i64, dbl, dbl,
+                                       P, P, P, P, P]
+        lib.oracle_sla_fwd.restype = None
+        lib.oracle_sla_bwd.argtypes = [i32, P, P, i32, i32, i32, i64, i64, i64, dbl, dbl,
+                                       P, P, P, P, P, P, P, P, P]
+        lib.oracle_sla_bwd.restype = None
+        lib.oracle_round_bf16.argtypes = [dbl]
+        lib.oracle_round_bf16.restype = dbl
+        lib.oracle_layernorm.argtypes = [i64, i64, P, P, P, dbl, P]
+        lib.oracle_layernorm.restype = None
+        lib.oracle_stu_layer_fwd.argtypes = [i32, P, P, i32, i32, i32, i32, i64, i64, i64,
+                                             dbl, dbl, dbl, P, P, P, P, P, P, P, P, P,
+                                             i32, P, P]
+        lib.oracle_stu_layer_fwd.restype = None
+        lib.oracle_truncate.argtypes = [i32, P, P, i64, i64, P, P]
+        lib.oracle_truncate.restype = i64
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _offs(offsets):
+    return np.ascontiguousarray(offsets, dtype=np.int64)
+
+
+def _tg(num_targets):
+    return None if num_targets is None else np.ascontiguousarray(num_targets, dtype=np.int32)
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def visible(i, j, L, num_targets, k1, k2, ctx) -> bool:
+    return bool(_load().oracle_visible(i, j, L, num_targets, k1, k2, ctx))
+
+
+def mask_dense(L, num_targets, k1, k2, ctx) -> np.ndarray:
+    out = np.zeros((L, L), dtype=np.uint8)
+    _load().oracle_mask_dense(L, num_targets, k1, k2, ctx, _ptr(out))
+    return out
+
+
+def count_pairs(offsets, num_targets, k1, k2, ctx) -> int:
+    o = _offs(offsets)
+    t = _tg(num_targets)
+    return int(_load().oracle_count_pairs(len(o) - 1, _ptr(o), _ptr(t), k1, k2, ctx))
+
+
+def tiles(offsets, num_targets, k1, k2, ctx, bm, bn) -> np.ndarray:
+    """Non-empty (b, row_tile_start, key_tile_start) triples, int64 [n, 3]."""
+    o = _offs(offsets)
+    t = _tg(num_targets)
+    lib = _load()
+    n = lib.oracle_tiles(len(o) - 1, _ptr(o), _ptr(t), k1, k2, ctx, bm, bn, None, 0)
+    out = np.zeros((max(n, 1), 3), dtype=np.int64)
+    lib.oracle_tiles(len(o) - 1, _ptr(o), _ptr(t), k1, k2, ctx, bm, bn, _ptr(out), n)
+    return out[:n]
+
+
+def sla_fwd(q, k, v, offsets, num_targets, k1, k2, ctx, N, alpha=1.0,
+            row_sel: Optional[np.ndarray] = None) -> np.ndarray:
+    """O [T, H, dv] in fp64.  q, k: [T, H, dqk]; v: [T, H, dv]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T, H, dqk = q.shape
+    dv = v.shape[2]
+    o = np.zeros((T, H, dv), dtype=np.float64)
+    offs, tg = _offs(offsets), _tg(num_targets)
+    sel = None if row_sel is None else np.ascontiguousarray(row_sel, dtype=np.uint8)
+    _load().oracle_sla_fwd(len(offs) - 1, _ptr(offs), _ptr(tg), H, dqk, dv, k1, k2, ctx,
+                           float(N), float(alpha), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                           _ptr(sel))
+    return o
+
+
+def sla_bwd(q, k, v, dout, offsets, num_targets, k1, k2, ctx, N, alpha=1.0,
+            q_sel=None, k_sel=None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """(dQ, dK, dV) in fp64."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
+    T, H, dqk = q.shape
+    dv = v.shape[2]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dvv = np.zeros_like(v)
+    offs, tg = _offs(offsets), _tg(num_targets)
+    qs = None if q_sel is None else np.ascontiguousarray(q_sel, dtype=np.uint8)
+    ks = None if k_sel is None else np.ascontiguousarray(k_sel, dtype=np.uint8)
+    _load().oracle_sla_bwd(len(offs) - 1, _ptr(offs), _ptr(tg), H, dqk, dv, k1, k2, ctx,
+                           float(N), float(alpha), _ptr(q), _ptr(k), _ptr(v), _ptr(do),
+                           _ptr(dq), _ptr(dk), _ptr(dvv), _ptr(qs), _ptr(ks))
+    return dq, dk, dvv
+
+
+def round_bf16(x: float) -> float:
+    return float(_load().oracle_round_bf16(float(x)))
+
+
+def layernorm(x, w, b=None, eps=1e-5) -> np.ndarray:
+    x = _f64(x)
+    rows, cols = x.shape
+    y = np.zeros_like(x)
+    _load().oracle_layernorm(rows, cols, _ptr(x), _ptr(_f64(w)),
+                             None if b is None else _ptr(_f64(b)), float(eps), _ptr(y))
+    return y
+
+
+def stu_layer_fwd(x, offsets, num_targets, ln1_w, w_uvqk, ln2_w, w_out, *, heads, dqk, dv,
+                  k1, k2, ctx, N, alpha=1.0, eps=1e-5, ln1_b=None, b_uvqk=None, ln2_b=None,
+                  b_out=None, store_bf16=False, want_uvqk=False):
+    x = _f64(x)
+    T, D = x.shape
+    out = np.zeros_like(x)
+    nw = 2 * heads * dv + 2 * heads * dqk
+    uvqk = np.zeros((T, nw), dtype=np.float64) if want_uvqk else None
+    offs, tg = _offs(offsets), _tg(num_targets)
+    keep = [_f64(a) if a is not None else None
+            for a in (ln1_w, ln1_b, w_uvqk, b_uvqk, ln2_w, ln2_b, w_out, b_out)]
+    _load().oracle_stu_layer_fwd(len(offs) - 1, _ptr(offs), _ptr(tg), D, heads, dqk, dv, k1,
+                                 k2, ctx, float(N), float(alpha), float(eps), _ptr(x),
+                                 *[_ptr(a) for a in keep], int(bool(store_bf16)), _ptr(out),
+                                 _ptr(uvqk))
+    return (out, uvqk) if want_uvqk else out
+
+
+def truncate(offsets, num_targets, ctx, tail_len):
+    """(new_offsets [B+1], gather_idx [T']) as int64."""
+    offs, tg = _offs(offsets), _tg(num_targets)
+    B = len(offs) - 1
+    new_offs = np.zeros(B + 1, dtype=np.int64)
+    gidx = np.zeros(max(int(offs[-1]), 1), dtype=np.int64)
+    n = _load().oracle_truncate(B, _ptr(offs), _ptr(tg), ctx, tail_len, _ptr(new_offs),
+                                _ptr(gidx))
+    return new_offs, gidx[:n].copy()

@@ -1,0 +1,154 @@
+"""Pins for the oracle's LayerNorm, STU layer, bf16 rounding and truncation.
+
+STU layer: ULTRA-HSTU paper, section 3 Eq.1-5 in the order of Code Listing 1;
+fused projection split U, V, Q, K (HSTU notes section 2.4 Eq.1).  Truncation:
+ULTRA-HSTU section 4.3 and the torcheasyrec page's truncation bullet.
+"""
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from synthetic import bf16_round_f32
+from tests._helpers import dense_sla_torch
+
+
+def test_layernorm_matches_torch():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((17, 24)) * 3 + 1
+    w = rng.standard_normal(24)
+    b = rng.standard_normal(24)
+    y = oracle.layernorm(x, w, b, 1e-5)
+    ref = F.layer_norm(torch.from_numpy(x), (24,), torch.from_numpy(w), torch.from_numpy(b),
+                       1e-5).numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+    y0 = oracle.layernorm(x, w, None, 1e-5)
+    ref0 = F.layer_norm(torch.from_numpy(x), (24,), torch.from_numpy(w), None, 1e-5).numpy()
+    np.testing.assert_allclose(y0, ref0, rtol=1e-12, atol=1e-12)
+
+
+def _stu_case(seed, lens, D=16, H=2, dqk=4, dv=3, tg=None):
+    rng = np.random.default_rng(seed)
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T = int(offs[-1])
+    nw = 2 * H * dv + 2 * H * dqk
+    p = dict(
+        x=rng.standard_normal((T, D)),
+        ln1_w=1 + 0.1 * rng.standard_normal(D), ln1_b=0.1 * rng.standard_normal(D),
+        w_uvqk=rng.standard_normal((nw, D)) * 0.4, b_uvqk=0.1 * rng.standard_normal(nw),
+        ln2_w=1 + 0.1 * rng.standard_normal(H * dv), ln2_b=0.1 * rng.standard_normal(H * dv),
+        w_out=rng.standard_normal((D, H * dv)) * 0.3, b_out=0.1 * rng.standard_normal(D))
+    return offs, p
+
+
+def _stu_torch(offs, p, tg, H, dqk, dv, k1, k2, ctx, N, alpha, eps):
+    t = {k: torch.from_numpy(np.asarray(v, np.float64)) for k, v in p.items()}
+    x = t["x"]
+    D = x.shape[1]
+    n = F.layer_norm(x, (D,), t["ln1_w"], t["ln1_b"], eps)
+    z = F.silu(F.linear(n, t["w_uvqk"], t["b_uvqk"]))
+    T = x.shape[0]
+    u, v, q, k = torch.split(z, [H * dv, H * dv, H * dqk, H * dqk], dim=1)
+    a = dense_sla_torch(q.reshape(T, H, dqk), k.reshape(T, H, dqk), v.reshape(T, H, dv), offs,
+                        tg, k1, k2, ctx, N, alpha).reshape(T, H * dv)
+    y = F.layer_norm(a, (H * dv,), t["ln2_w"], t["ln2_b"], eps) * u
+    return (F.linear(y, t["w_out"], t["b_out"]) + x).numpy(), z.numpy()
+
+
+@pytest.mark.parametrize("tg", [None, [2, 1, 0]])
+def test_stu_layer_matches_torch_composition(tg):
+    lens = [6, 11, 9]
+    H, dqk, dv = 2, 4, 3
+    offs, p = _stu_case(3, lens, H=H, dqk=dqk, dv=dv)
+    out, uvqk = oracle.stu_layer_fwd(p["x"], offs, tg, p["ln1_w"], p["w_uvqk"], p["ln2_w"],
+                                     p["w_out"], heads=H, dqk=dqk, dv=dv, k1=3, k2=2, ctx=1,
+                                     N=11.0, alpha=0.9, eps=1e-5, ln1_b=p["ln1_b"],
+                                     b_uvqk=p["b_uvqk"], ln2_b=p["ln2_b"], b_out=p["b_out"],
+                                     want_uvqk=True)
+    ref, zref = _stu_torch(offs, p, tg, H, dqk, dv, 3, 2, 1, 11.0, 0.9, 1e-5)
+    np.testing.assert_allclose(uvqk, zref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-11)
+
+
+def test_stu_zero_output_projection_is_identity():
+    offs, p = _stu_case(5, [7, 4])
+    out = oracle.stu_layer_fwd(p["x"], offs, None, p["ln1_w"], p["w_uvqk"], p["ln2_w"],
+                               np.zeros_like(p["w_out"]), heads=2, dqk=4, dv=3, k1=3, k2=1,
+                               ctx=0, N=7.0)
+    assert np.array_equal(out, p["x"])
+
+
+def test_stu_storage_matched_mode_rounds_to_bf16():
+    offs, p = _stu_case(6, [9, 5])
+    kw = dict(heads=2, dqk=4, dv=3, k1=3, k2=1, ctx=0, N=9.0)
+    exact = oracle.stu_layer_fwd(p["x"], offs, None, p["ln1_w"], p["w_uvqk"], p["ln2_w"],
+                                 p["w_out"], **kw)
+    rounded, z = oracle.stu_layer_fwd(p["x"], offs, None, p["ln1_w"], p["w_uvqk"], p["ln2_w"],
+                                      p["w_out"], store_bf16=True, want_uvqk=True, **kw)
+    for a in (rounded, z):
+        f = a.astype(np.float32)
+        assert np.array_equal(f.astype(np.float64), a)
+        assert np.array_equal(bf16_round_f32(f), f)
+    rel = np.abs(rounded - exact).max() / np.sqrt((exact ** 2).mean())
+    assert 0 < rel < 3e-2
+
+
+def test_round_bf16_ties_and_values():
+    """bfloat16 keeps 8 significant bits, ties go to even."""
+    r = oracle.round_bf16
+    assert r(1.0) == 1.0
+    assert r(1.0 + 2 ** -8) == 1.0                  # tie -> even (1.0)
+    assert r(1.0 + 3 * 2 ** -8) == 1.0 + 2 ** -6    # tie -> even (1 + 4*2^-8)
+    assert r(1.0 + 2 ** -8 + 2 ** -20) == 1.0 + 2 ** -7
+    assert r(-3.0) == -3.0
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal(2000) * 10.0 ** rng.uniform(-3, 3, 2000)).astype(np.float32)
+    mine = np.array([r(float(a)) for a in x])
+    assert np.array_equal(mine, bf16_round_f32(x).astype(np.float64))
+
+
+# --------------------------------------------------------------------------
+# truncation
+# --------------------------------------------------------------------------
+def _truncate_by_sets(lens, tg, ctx, tail):
+    gidx, new_offs = [], [0]
+    base = 0
+    for L, T in zip(lens, tg):
+        U = L - T
+        c = min(ctx, U)
+        history = list(range(c, U))
+        keep = set(range(c)) | set(history[-tail:] if tail > 0 else []) | set(range(U, L))
+        gidx += [base + i for i in sorted(keep)]
+        new_offs.append(len(gidx))
+        base += L
+    return np.array(new_offs, np.int64), np.array(gidx, np.int64)
+
+
+def test_truncate_matches_set_construction():
+    rng = np.random.default_rng(3)
+    for _ in range(50):
+        B = int(rng.integers(1, 6))
+        lens = [int(x) for x in rng.integers(0, 60, size=B)]
+        tg = [int(rng.integers(0, L + 1)) for L in lens]
+        ctx, tail = int(rng.integers(0, 10)), int(rng.integers(1, 40))
+        offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+        no, gi = oracle.truncate(offs, tg, ctx, tail)
+        rno, rgi = _truncate_by_sets(lens, tg, ctx, tail)
+        assert np.array_equal(no, rno) and np.array_equal(gi, rgi)
+
+
+def test_truncate_is_identity_when_tail_covers_history():
+    lens = [30, 12]
+    offs = np.array([0, 30, 42], np.int64)
+    no, gi = oracle.truncate(offs, [4, 2], 3, 23)
+    assert np.array_equal(no, offs) and np.array_equal(gi, np.arange(42))
+
+
+def test_truncate_tzrec_example_lengths():
+    """torcheasyrec page: after truncation a sequence holds
+    contextual_seq_len + attn_truncation_tail_len + num_targets tokens."""
+    lens = [16 + 3000 + 64, 16 + 1024 + 64, 16 + 700 + 64]
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    no, gi = oracle.truncate(offs, [64, 64, 64], 16, 1024)
+    assert list(np.diff(no)) == [16 + 1024 + 64, 16 + 1024 + 64, 16 + 700 + 64]
