@@ -1,0 +1,186 @@
+"""Benchmark: SLA forward + backward at L = 16K on one MI355X.
+
+One step is the whole hot path over one batch: the on-device tile schedule,
+the forward, and the backward (gradient scale + schedule, dK/dV, dQ) of HSTU
+SiLU attention under the semi-local mask, on the long_16k workload (B = 8,
+lengths 16384 x 4 + U[4096, 16384] x 4, H = 4, d = 128, K1 = 1024, K2 = 128,
+contextual 16, bf16, seed 0), inputs resident in HBM before timing starts.
+
+Prints one JSON line: useful TFLOP/s (visible pairs only, 1792 flop per pair
+per head), plus tokens/s, the roofline of the dominant kernel (per-kernel time
+from HIP events recorded on the library's stream) and the fp64 CPU oracle
+timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = 2516.6   # MI355X dense bf16 / fp16 MFMA
+PEAK_HBM_GBS = 8000.0
+WORKLOAD = "long_16k"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-len", type=int, default=16384)
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_long_16k.json"),
+                    help="per-kernel HBM bytes measured with rocprofv3 --pmc (optional)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the SLA hot path "
+              "shards by sequence with no exchange, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_sequence_attention_amd as sla
+    from synthetic import make_sla_workload, CONFIGS
+
+    cfg = CONFIGS[WORKLOAD]
+    w = make_sla_workload(cfg, seed=args.seed, with_dout=True)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    dt = torch.bfloat16
+    q, k, v, do = (torch.from_numpy(a).to(dev).to(dt) for a in (w.q, w.k, w.v, w.dout))
+    offs = torch.from_numpy(w.offsets).to(dev)
+    kw = dict(k1=w.k1, k2=w.k2, contextual_len=w.contextual_len, max_seq_len=w.max_seq_len)
+    H, d = cfg.heads, cfg.d
+    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    p = sla.make_problem(dt, offs, None, w.total_tokens, H, d, d, **kw)
+    ws = torch.empty(max(sla.workspace_size(p, sla.SLA_OP_BWD),
+                         sla.workspace_size(p, sla.SLA_OP_FWD)), dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        sla.sla_fwd(q, k, v, offs, None, out=o, workspace=ws, **kw)
+        if ev is not None:
+            ev[1].record()
+        sla.sla_bwd(q, k, v, do, offs, None, dq=dq, dk=dk, dv=dv, workspace=ws,
+                    stage=sla.SLA_BWD_PREPARE, **kw)
+        if ev is not None:
+            ev[2].record()
+        sla.sla_bwd(q, k, v, do, offs, None, dq=dq, dk=dk, dv=dv, workspace=ws,
+                    stage=sla.SLA_BWD_DKDV, **kw)
+        if ev is not None:
+            ev[3].record()
+        sla.sla_bwd(q, k, v, do, offs, None, dq=dq, dk=dk, dv=dv, workspace=ws,
+                    stage=sla.SLA_BWD_DQ, **kw)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = sum(events[i][0].elapsed_time(events[i][4]) for i in range(args.steps)) / args.steps
+    phase = {name: float(np.mean([events[i][a].elapsed_time(events[i][b])
+                                  for i in range(args.steps)]))
+             for name, a, b in (("fwd", 0, 1), ("bwd_prepare", 1, 2), ("bwd_dkdv", 2, 3),
+                                ("bwd_dq", 3, 4))}
+
+    pairs = sla.count_pairs_host(w.offsets, None, w.k1, w.k2, w.contextual_len) * H
+    useful = pairs * (2 * (d + d) + 2 * (3 * d + 2 * d))
+    value = useful / (ms_step * 1e-3) / 1e12
+    tokens_s = w.total_tokens / (ms_step * 1e-3)
+    # algorithmic MFMA work of each kernel (per launch): forward S and P.V; dK/dV
+    # kernel S, dP, dV, dK; dQ kernel S, dP, dQ
+    kernel_flops = {"fwd": pairs * 4 * d, "bwd_dkdv": pairs * 8 * d, "bwd_dq": pairs * 6 * d}
+    dom = max(kernel_flops, key=lambda n: phase[n])
+    achieved = kernel_flops[dom] / (phase[dom] * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f).get(dom)
+
+    line = {
+        "metric": "SLA fwd+bwd useful TFLOP/s at L=16K (long_16k)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{WORKLOAD}: {cfg.description}, N={cfg.max_seq_len}, seed {args.seed}",
+            "total_tokens": w.total_tokens,
+            "visible_pairs_all_heads": pairs,
+            "useful_flop_per_step": useful,
+        },
+        "tokens_per_s": round(tokens_s, 1),
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_MFMA_TFLOPS, 2),
+        "phase_ms": {kk: round(vv, 4) for kk, vv in phase.items()},
+        "wall_s_timed_region": round(wall, 4),
+        "roofline": {
+            "kernel": dom,
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_MFMA_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_len)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, sample_len):
+    """The fp64 oracle as it stands, on a bounded sample: one sequence of
+    `sample_len` tokens of the same workload (all heads), forward + backward."""
+    import oracle
+    import sparse_sequence_attention_amd as sla
+    b = int(np.argmax(np.asarray(w.lengths) >= sample_len))
+    L = int(min(w.lengths[b], sample_len))
+    s0 = int(w.offsets[b])
+    sl = slice(s0, s0 + L)
+    offs = np.array([0, L], np.int64)
+    q, k, v, do = w.q[sl], w.k[sl], w.v[sl], w.dout[sl]
+    t0 = time.perf_counter()
+    oracle.sla_fwd(q, k, v, offs, None, w.k1, w.k2, w.contextual_len, w.max_seq_len)
+    oracle.sla_bwd(q, k, v, do, offs, None, w.k1, w.k2, w.contextual_len, w.max_seq_len)
+    t = time.perf_counter() - t0
+    H, d = q.shape[1], q.shape[2]
+    pairs = sla.count_pairs_host(offs, None, w.k1, w.k2, w.contextual_len) * H
+    useful = pairs * (2 * (d + d) + 2 * (3 * d + 2 * d))
+    return {"value": round(useful / t / 1e12, 6), "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"sequence {b} of the workload, first {L} tokens, all {H} heads, fwd+bwd "
+                      f"({t:.2f} s; {L / t:.1f} tokens/s)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,226 @@
+/*
+ * sla.h -- C ABI of the MI355X (gfx950) Semi-Local Attention library.
+ *
+ * The library computes, on one GPU, the hot path of ULTRA-HSTU's sequence
+ * encoder:
+ *   - HSTU pointwise attention A = (SiLU(alpha Q K^T) (.) M) V / N over jagged
+ *     sequences (ULTRA-HSTU paper, section 3 Eq.3; HSTU notes, section 2.4
+ *     Eq.2: pointwise SiLU, no softmax), under the semi-local mask M of
+ *     section 4.2.1 Eq.7: row i sees key j iff
+ *        j <= i  and  (i - j < K1  or  j < K2e),   K2e = max(K2, contextual_len)
+ *     (effective_k2 rule of the torcheasyrec "ULTRA HSTU" page), and target
+ *     (candidate) rows see only the history and themselves (HSTU notes, Q8,
+ *     M-FALCON mask): a target row i >= U sees j == i, or a history key j < U
+ *     with (U - j < K1 or j < K2e), where U = L - num_targets is the first
+ *     target slot;
+ *   - its backward (dQ, dK, dV);
+ *   - one STU layer forward around it (ULTRA-HSTU paper, section 3 Eq.1-5,
+ *     operation order of Code Listing 1);
+ *   - attention truncation between layers (ULTRA-HSTU paper, section 4.3;
+ *     torcheasyrec page, truncation bullet).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers are DEVICE pointers unless marked "host".  The caller allocates and
+ * owns every buffer, workspace included; the library never allocates or frees
+ * device memory and keeps no device state between calls.  All work is enqueued
+ * on the caller's stream (hipStream_t passed as void*; NULL = default stream)
+ * without any host synchronisation; outputs are valid once the stream reaches
+ * that point.  Calls are thread-safe.
+ *
+ * Jagged layout: sequence b owns tokens [offsets[b], offsets[b+1]) of every
+ * [T, ...] tensor.  offsets is int64 [B+1], offsets[0] = 0, non-decreasing,
+ * offsets[B] = total_tokens.  num_targets is int32 [B] (or NULL = no targets),
+ * 0 <= num_targets[b] <= L_b; targets are the last num_targets[b] tokens.
+ * These device-resident facts are trusted (checking them needs a sync).
+ *
+ * Per-head tensors are [T][H][d] row-major with a token stride ld (elements)
+ * >= H*d, so Q/K/V/U may be strided column blocks of one fused projection
+ * buffer; head h of token t starts at element t*ld + h*d.
+ *
+ * Errors: every call returns sla_status_t and never throws.  Host-checkable
+ * problems are rejected before any HIP call; the message of the last failure
+ * on the calling thread is available from sla_last_error().
+ */
+#ifndef SLA_MI355X_H
+#define SLA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SLA_OK = 0,
+    SLA_ERR_NULL = 1,        /* a required pointer is NULL                        */
+    SLA_ERR_INVALID = 2,     /* negative size, ld < H*d, max_seq_len < 1, ...     */
+    SLA_ERR_UNSUPPORTED = 3, /* head dim / dtype / alignment the kernels lack     */
+    SLA_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than *_workspace_size   */
+    SLA_ERR_HIP = 5,         /* a HIP runtime call or kernel launch failed        */
+    SLA_ERR_DEVICE = 6       /* the current device is not gfx950                  */
+} sla_status_t;
+
+typedef enum { SLA_F32 = 0, SLA_BF16 = 1 } sla_dtype_t;
+
+/* One SLA problem.  Host struct, read during the call only. */
+typedef struct {
+    int32_t dtype;               /* sla_dtype_t of Q, K, V, O, dO, dQ, dK, dV       */
+    int32_t batch;               /* B >= 0                                          */
+    int64_t total_tokens;        /* T = offsets[B] (host-known: the tensor shape)   */
+    const int64_t *offsets;      /* device int64 [B+1]                              */
+    const int32_t *num_targets;  /* device int32 [B], or NULL                       */
+    int32_t num_heads;           /* H >= 1                                          */
+    int32_t d_qk;                /* head dim of Q and K: 32, 64 or 128              */
+    int32_t d_v;                 /* head dim of V and O: must equal d_qk            */
+    int32_t k1;                  /* local window K1 >= 0 (keys, the row included)   */
+    int32_t k2;                  /* global prefix K2 >= 0                           */
+    int32_t contextual_len;      /* contextual prefix >= 0; K2e = max(k2, this)     */
+    int32_t max_seq_len;         /* N of the 1/N output scaling, >= 1               */
+    float alpha;                 /* pre-activation factor: SiLU(alpha * q.k)        */
+} sla_problem_t;
+
+/* Operation selector for sla_workspace_size / sla_schedule. */
+enum { SLA_OP_FWD = 0, SLA_OP_BWD = 1 };
+
+/* Bytes of device workspace sla_fwd (op = SLA_OP_FWD) or sla_bwd
+ * (op = SLA_OP_BWD) needs for problem p: the on-device tile schedule and, for
+ * the backward, fp32 partial sums of the split global-prefix key tiles.
+ * Depends only on host-known fields.  Returns 0 if p is invalid. */
+size_t sla_workspace_size(const sla_problem_t *p, int op);
+
+/* SLA forward (ULTRA-HSTU paper, section 4.2.1 Eq.6-7 with Eq.3):
+ *   O[i] = (1/N) * sum_{j visible from i} SiLU(alpha * q_i . k_j) * v_j
+ * q, k: [T][H][d_qk] with token strides ldq, ldk; v: [T][H][d_v] (ldv);
+ * o: [T][H][d_v] (ldo), fully written for every token (rows of empty
+ * sequences do not exist).  bf16 path: bf16 storage, fp32 accumulation,
+ * SiLU in fp32, P rounded to bf16 before the P.V product.  f32 path: fp32
+ * throughout.  Only the non-empty tiles of the local band, the global prefix
+ * and (for targets) the diagonal are visited.
+ * Errors: NULL -> SLA_ERR_NULL; bad sizes/strides -> SLA_ERR_INVALID; head dim
+ * not in {32,64,128}, d_qk != d_v, ld or pointer not 16-byte aligned ->
+ * SLA_ERR_UNSUPPORTED; ws_bytes < sla_workspace_size(p, SLA_OP_FWD) ->
+ * SLA_ERR_WORKSPACE. */
+sla_status_t sla_fwd(const sla_problem_t *p, const void *q, int64_t ldq, const void *k,
+                     int64_t ldk, const void *v, int64_t ldv, void *o, int64_t ldo,
+                     void *workspace, size_t ws_bytes, void *stream);
+
+/* SLA backward: given dO, the gradients of the forward above,
+ *   dV_j = (1/N) sum_i a_ij dO_i,            a_ij = SiLU(alpha s_ij), s_ij = q_i.k_j
+ *   dS_ij = (1/N) (dO_i . v_j) alpha SiLU'(alpha s_ij)
+ *   dQ_i = sum_j dS_ij k_j,   dK_j = sum_i dS_ij q_i
+ * over visible pairs only.  dq/dk/dv may be strided column blocks of one
+ * buffer (no concatenation needed, ULTRA-HSTU paper section 4.2.2).  Every
+ * output row is written (zero where a token sees / is seen by nothing).  No
+ * atomics: dK/dV are owned by key tiles, dQ by row tiles; the global-prefix
+ * key tiles are split over row chunks whose fp32 partial sums are added in a
+ * fixed order, so results are bitwise reproducible run to run.
+ * Errors as sla_fwd, with ws_bytes checked against SLA_OP_BWD. */
+sla_status_t sla_bwd(const sla_problem_t *p, const void *q, int64_t ldq, const void *k,
+                     int64_t ldk, const void *v, int64_t ldv, const void *dout, int64_t lddo,
+                     void *dq, int64_t lddq, void *dk, int64_t lddk, void *dv, int64_t lddv,
+                     void *workspace, size_t ws_bytes, void *stream);
+
+/* The backward in stages: sla_bwd(...) equals, on one stream,
+ *   sla_bwd_stage(SLA_BWD_PREPARE)  gradient scale + tile schedule (workspace)
+ *   sla_bwd_stage(SLA_BWD_DKDV)     dK, dV (key-tile kernel + prefix reduce)
+ *   sla_bwd_stage(SLA_BWD_DQ)       dQ (row-tile kernel)
+ * with identical arguments and workspace.  DKDV and DQ only read what PREPARE
+ * wrote (and write disjoint outputs), so after PREPARE they may run on two
+ * streams; a stage ignores the output pointers it does not write (they may be
+ * NULL).  SLA_BWD_ALL runs all three. */
+enum { SLA_BWD_ALL = 0, SLA_BWD_PREPARE = 1, SLA_BWD_DKDV = 2, SLA_BWD_DQ = 3 };
+sla_status_t sla_bwd_stage(const sla_problem_t *p, int stage, const void *q, int64_t ldq,
+                           const void *k, int64_t ldk, const void *v, int64_t ldv,
+                           const void *dout, int64_t lddo, void *dq, int64_t lddq, void *dk,
+                           int64_t lddk, void *dv, int64_t lddv, void *workspace,
+                           size_t ws_bytes, void *stream);
+
+/* Schedule inspection (the integer part of the hot path, exposed so that it
+ * can be checked bit for bit).  Writes the work list the kernels of `op` run:
+ *   op = SLA_OP_FWD: row-tile items (forward and dQ kernels)
+ *   op = SLA_OP_BWD: key-tile items (dK/dV kernel)
+ * as int32 records of SLA_SCHED_RECORD_INTS fields into `records` (device,
+ * capacity `capacity` records) and the record count into `*count` (device
+ * int32).  Record fields:
+ *   [0] b  [1] tile_lo  [2] tile_hi    (rows for FWD, keys for BWD; tokens
+ *                                       within sequence b, [lo, hi))
+ *   [3] n_ranges (0..3)
+ *   [4..9] up to 3 half-open ranges of the other operand, in tokens within b:
+ *        FWD: key ranges visited, each a union of whole key tiles of
+ *             sla_schedule_tile(op, 1) keys (last tile clipped at L_b);
+ *        BWD: row ranges visited (history rows, target rows), split into the
+ *             chunk this record covers;
+ *   [10] chunk index, [11] number of chunks of this key tile (1 = unsplit).
+ * Returns SLA_ERR_INVALID if capacity is below sla_schedule_capacity(p, op). */
+#define SLA_SCHED_RECORD_INTS 12
+int64_t sla_schedule_capacity(const sla_problem_t *p, int op);
+int32_t sla_schedule_tile(int op, int which /*0 = stationary tile, 1 = moving tile*/);
+sla_status_t sla_schedule(const sla_problem_t *p, int op, int32_t *records, int64_t capacity,
+                          int32_t *count, void *workspace, size_t ws_bytes, void *stream);
+
+/* The same work list computed on the host from HOST copies of offsets [B+1]
+ * and num_targets [B] (nullable); p->offsets / p->num_targets are ignored.
+ * Writes at most `capacity` records (records may be NULL to count only) and
+ * returns the number of records, or -1 on invalid input. */
+int64_t sla_schedule_host(const sla_problem_t *p, int op, const int64_t *offsets_host,
+                          const int32_t *num_targets_host, int32_t *records, int64_t capacity);
+
+/* Useful work: number of visible (row, key) pairs per head, summed over the
+ * batch, from HOST copies of offsets [B+1] and num_targets [B] (nullable).
+ * Useful FLOPs are this count times H times 2*(d_qk+d_v) (forward) and
+ * 2*(3*d_qk+2*d_v) (backward).  Returns -1 on invalid input. */
+int64_t sla_count_pairs_host(int32_t batch, const int64_t *offsets_host,
+                             const int32_t *num_targets_host, int32_t k1, int32_t k2,
+                             int32_t contextual_len);
+
+/* One STU layer forward, bf16 storage, fp32 accumulation and statistics
+ * (ULTRA-HSTU paper, section 3 Eq.1-5; Code Listing 1 order):
+ *   n    = LayerNorm(x) * ln1_w (+ ln1_b)                 row of D = hidden
+ *   uvqk = SiLU(n W1^T (+ b_uvqk)), split U | V | Q | K     (each [H][d], head-major)
+ *   A    = SLA(Q, K, V)                                   as sla_fwd
+ *   y    = (LayerNorm(A) * ln2_w (+ ln2_b)) (.) U           LayerNorm over the H*d_v row
+ *   out  = y W2^T (+ b_out) + x                           residual fused in the epilogue
+ * x, out: [T][D] bf16 contiguous (out may not alias x); w_uvqk: [2*H*d_v +
+ * 2*H*d_qk][D] bf16 (out-features major, as a Linear weight); w_out:
+ * [D][H*d_v] bf16; ln*_w, ln*_b, b_*: fp32 vectors; biases nullable.
+ * uvqk_out (nullable): [T][2*H*d_v + 2*H*d_qk] bf16 copy of U|V|Q|K; the
+ * layer keeps it in the workspace otherwise.  attn.dtype must be SLA_BF16,
+ * D a multiple of 64 and at most 1024, H*d_v at most 1024. */
+typedef struct {
+    sla_problem_t attn;
+    int32_t hidden;  /* D */
+    float ln_eps;    /* LayerNorm epsilon (e.g. 1e-5) */
+} stu_layer_desc_t;
+
+size_t stu_layer_workspace_size(const stu_layer_desc_t *d);
+sla_status_t stu_layer_fwd(const stu_layer_desc_t *d, const void *x, const float *ln1_w,
+                           const float *ln1_b, const void *w_uvqk, const float *b_uvqk,
+                           const float *ln2_w, const float *ln2_b, const void *w_out,
+                           const float *b_out, void *out, void *uvqk_out, void *workspace,
+                           size_t ws_bytes, void *stream);
+
+/* Attention truncation (ULTRA-HSTU paper, section 4.3; torcheasyrec page,
+ * truncation bullet): per sequence keep, in order, the contextual prefix
+ * [0, c), the most recent tail_len history tokens and the num_targets[b]
+ * targets, where U = L_b - num_targets[b], c = min(contextual_len, U), and
+ * the history is [c, U).  Writes new_offsets [B+1] (int64),
+ * new_num_targets [B] (int32, = num_targets, nullable), gather_idx
+ * [capacity] (int64 source token of each kept row, nullable) and x_out
+ * [capacity][hidden] (nullable; dtype element size 2 for bf16, 4 for f32).
+ * capacity >= min(total_tokens, B * (contextual_len + tail_len) + sum of
+ * targets) must hold; pass total_tokens when in doubt.  tail_len >= 1. */
+sla_status_t stu_truncate(int32_t batch, int64_t total_tokens, const int64_t *offsets,
+                          const int32_t *num_targets, int32_t contextual_len,
+                          int32_t tail_len, const void *x, int32_t hidden, int32_t dtype,
+                          int64_t *new_offsets, int32_t *new_num_targets, int64_t *gather_idx,
+                          void *x_out, int64_t capacity, void *stream);
+
+const char *sla_status_string(sla_status_t s);
+const char *sla_last_error(void); /* thread-local message of the last failure */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SLA_MI355X_H */

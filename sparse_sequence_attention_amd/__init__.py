@@ -1,0 +1,15 @@
+"""MI355X (gfx950) Semi-Local Attention: HSTU pointwise SiLU attention over
+jagged sequences under the ULTRA-HSTU semi-local mask, its backward, the STU
+layer around it and attention truncation, as hand-written HIP kernels behind a
+C ABI (include/sla.h).  This package is the Python binding of that library.
+"""
+from ._capi import (  # noqa: F401
+    SLAError, SLA_OP_FWD, SLA_OP_BWD, SLA_SCHED_RECORD_INTS, SLA_BWD_ALL, SLA_BWD_PREPARE,
+    SLA_BWD_DKDV, SLA_BWD_DQ,
+)
+from .config import STUConfig  # noqa: F401
+from .ops import (  # noqa: F401
+    sla_fwd, sla_bwd, sla_attention, sla_schedule, sla_schedule_host, schedule_tile, count_pairs_host,
+    stu_layer_fwd, stu_truncate, make_problem, workspace_size,
+)
+from .stack import STULayerWeights, stu_stack_fwd  # noqa: F401

@@ -1,0 +1,82 @@
+"""Build the gfx950 HIP library libsla_mi355x.so in-tree with hipcc.
+
+Every translation unit under csrc/ is compiled for --offload-arch=gfx950 with
+packed-fp32 instruction selection disabled, then linked into one shared
+library next to this file.  `python -m sparse_sequence_attention_amd.build`
+runs it from the command line.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(HERE, "_build")
+LIB_NAME = "libsla_mi355x.so"
+LIB_PATH = os.path.join(HERE, LIB_NAME)
+
+SOURCES = [
+    "sla_api.cpp",
+    "sla_sched.hip",
+    "sla_fwd_bf16.hip",
+    "sla_bwd_bf16.hip",
+    "sla_f32.hip",
+    "stu_kernels.hip",
+]
+
+ARCH = "gfx950"
+COMMON_FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    f"--offload-arch={ARCH}",
+    "-I", INCLUDE, "-I", CSRC,
+]
+# device code only: keep the compiler from emitting packed fp32 arithmetic
+HIP_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the HIP toolchain is required to build the library")
+
+
+def _compile(src: str) -> str:
+    path = os.path.join(CSRC, src)
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    cmd = [_hipcc()] + COMMON_FLAGS
+    if src.endswith(".hip"):
+        cmd += ["-x", "hip"] + HIP_FLAGS
+    cmd += ["-c", path, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    return obj
+
+
+def build(verbose: bool = True, jobs: int = 0) -> str:
+    """Compile all sources and link LIB_PATH (always rebuilds)."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    jobs = jobs or min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, LIB_PATH)
+    if verbose:
+        print(f"built {LIB_PATH}")
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    build()
+    sys.exit(0)

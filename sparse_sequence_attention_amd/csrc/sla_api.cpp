@@ -1,0 +1,499 @@
+// sla_api.cpp -- host side of the C ABI declared in include/sla.h: argument
+// validation (before any HIP call), workspace sizing from host-known sizes,
+// and kernel launches on the caller's stream.  No host synchronisation, no
+// device allocation.
+#include "sla.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+
+#include "sla_kernels.h"
+
+using namespace sla;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sla_status_t fail(sla_status_t s, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+sla_status_t hip_fail(hipError_t e, const char *what)
+{
+    return fail(SLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// gfx950 check, cached per device
+sla_status_t check_device()
+{
+    static std::mutex mu;
+    static std::unordered_map<int, bool> cache;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        auto it = cache.find(dev);
+        if (it != cache.end())
+            return it->second ? SLA_OK : fail(SLA_ERR_DEVICE, "device %d is not gfx950", dev);
+    }
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        cache[dev] = ok;
+    }
+    return ok ? SLA_OK : fail(SLA_ERR_DEVICE, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+}
+
+int k2_eff(const sla_problem_t *p) { return p->k2 > p->contextual_len ? p->k2 : p->contextual_len; }
+
+sla_status_t validate_problem(const sla_problem_t *p)
+{
+    if (!p) return fail(SLA_ERR_NULL, "problem is NULL");
+    if (p->dtype != SLA_F32 && p->dtype != SLA_BF16)
+        return fail(SLA_ERR_UNSUPPORTED, "dtype %d unsupported", p->dtype);
+    if (p->batch < 0 || p->total_tokens < 0)
+        return fail(SLA_ERR_INVALID, "negative batch (%d) or total_tokens (%lld)", p->batch,
+                    (long long)p->total_tokens);
+    if (p->total_tokens >= (int64_t)1 << 30)
+        return fail(SLA_ERR_UNSUPPORTED, "total_tokens %lld too large", (long long)p->total_tokens);
+    if (p->batch > 0 && !p->offsets) return fail(SLA_ERR_NULL, "offsets is NULL");
+    if (p->num_heads < 1) return fail(SLA_ERR_INVALID, "num_heads must be >= 1");
+    if (p->d_qk != 32 && p->d_qk != 64 && p->d_qk != 128)
+        return fail(SLA_ERR_UNSUPPORTED, "head dim %d not in {32, 64, 128}", p->d_qk);
+    if (p->d_v != p->d_qk)
+        return fail(SLA_ERR_UNSUPPORTED, "d_v (%d) must equal d_qk (%d)", p->d_v, p->d_qk);
+    if (p->k1 < 0 || p->k2 < 0 || p->contextual_len < 0)
+        return fail(SLA_ERR_INVALID, "k1, k2 and contextual_len must be >= 0");
+    if (p->max_seq_len < 1) return fail(SLA_ERR_INVALID, "max_seq_len must be >= 1");
+    if (!std::isfinite(p->alpha)) return fail(SLA_ERR_INVALID, "alpha must be finite");
+    return SLA_OK;
+}
+
+sla_status_t validate_tensor(const char *name, const void *ptr, int64_t ld, const sla_problem_t *p,
+                             int d)
+{
+    if (!ptr) return fail(SLA_ERR_NULL, "%s is NULL", name);
+    if (ld < (int64_t)p->num_heads * d)
+        return fail(SLA_ERR_INVALID, "%s: token stride %lld < H*d = %d", name, (long long)ld,
+                    p->num_heads * d);
+    const int elems16 = p->dtype == SLA_BF16 ? 8 : 4;
+    if (ld % elems16 != 0)
+        return fail(SLA_ERR_UNSUPPORTED, "%s: token stride %lld is not a multiple of 16 bytes",
+                    name, (long long)ld);
+    if (!aligned16(ptr)) return fail(SLA_ERR_UNSUPPORTED, "%s is not 16-byte aligned", name);
+    return SLA_OK;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+WsLayout layout(const sla_problem_t *p, int op)
+{
+    WsLayout w{};
+    const int64_t T = p->total_tokens, B = p->batch;
+    const int K2e = k2_eff(p);
+    w.fwd_items = T / FWD_BM + 2 * B + 1;
+    int64_t np_max = (K2e + BWD_BN - 1) / BWD_BN;
+    if (np_max > BWD_MAX_SPLIT_TILES) np_max = BWD_MAX_SPLIT_TILES;
+    int64_t chunk_sum = T / ((int64_t)BWD_BM * BWD_CHUNK_TILES) + 2 * B + 1;
+    if (chunk_sum > B * BWD_MAX_CHUNKS) chunk_sum = B * BWD_MAX_CHUNKS;
+    w.part_slots = np_max * chunk_sum;
+    w.bwd_items = T / BWD_BN + B + 1 + w.part_slots;
+    w.red_items = np_max * B;
+    w.sched_off = 0;
+    const size_t sched_bytes = sizeof(int32_t) * (4 * (size_t)(B + 1) + (size_t)B) +
+                               sizeof(float) * (ABSMAX_BLOCKS + 1);
+    w.part_off = round_up(sched_bytes, 256);
+    size_t part_bytes = 0;
+    if (op == SLA_OP_BWD)
+        part_bytes = (size_t)w.part_slots * p->num_heads * BWD_BN * (size_t)(p->d_qk + p->d_v) *
+                     sizeof(float);
+    w.total = w.part_off + round_up(part_bytes, 256);
+    return w;
+}
+
+sla_status_t make_params(const sla_problem_t *p, int op, void *ws, size_t ws_bytes, AttnParams &a)
+{
+    const WsLayout w = layout(p, op);
+    if (!ws) return fail(SLA_ERR_WORKSPACE, "workspace is NULL");
+    if (ws_bytes < w.total)
+        return fail(SLA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", ws_bytes, w.total);
+    if (!aligned16(ws)) return fail(SLA_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
+    const int64_t H = p->num_heads;
+    if (w.fwd_items * H > INT32_MAX || w.bwd_items * H > INT32_MAX)
+        return fail(SLA_ERR_UNSUPPORTED, "problem too large for one launch");
+    std::memset(&a, 0, sizeof(a));
+    a.offsets = p->offsets;
+    a.num_targets = p->num_targets;
+    a.B = p->batch;
+    a.H = p->num_heads;
+    a.d = p->d_qk;
+    a.k1 = p->k1;
+    a.k2e = k2_eff(p);
+    a.alpha = p->alpha;
+    a.inv_n = 1.0f / (float)p->max_seq_len;
+    a.out_scale = p->alpha / (float)p->max_seq_len;
+    a.neg_alpha_log2e = -p->alpha * 1.4426950408889634f;
+    int32_t *s = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + w.sched_off);
+    const int B1 = p->batch + 1;
+    a.s.fwd_base = s;
+    a.s.bwd_base = s + B1;
+    a.s.red_base = s + 2 * B1;
+    a.s.part_base = s + 3 * B1;
+    a.s.nch = s + 4 * B1;
+    a.absmax_part = reinterpret_cast<float *>(s + 4 * B1 + p->batch);
+    a.grad_scale = a.absmax_part + ABSMAX_BLOCKS;
+    a.T = p->total_tokens;
+    a.partials = reinterpret_cast<float *>(static_cast<char *>(ws) + w.part_off);
+    a.grid_fwd = (int)(w.fwd_items * H);
+    a.grid_bwd = (int)(w.bwd_items * H);
+    a.grid_red = (int)(w.red_items * H);
+    return SLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *sla_status_string(sla_status_t s)
+{
+    switch (s) {
+    case SLA_OK: return "SLA_OK";
+    case SLA_ERR_NULL: return "SLA_ERR_NULL";
+    case SLA_ERR_INVALID: return "SLA_ERR_INVALID";
+    case SLA_ERR_UNSUPPORTED: return "SLA_ERR_UNSUPPORTED";
+    case SLA_ERR_WORKSPACE: return "SLA_ERR_WORKSPACE";
+    case SLA_ERR_HIP: return "SLA_ERR_HIP";
+    case SLA_ERR_DEVICE: return "SLA_ERR_DEVICE";
+    }
+    return "SLA_ERR_UNKNOWN";
+}
+
+const char *sla_last_error(void) { return g_last_error.c_str(); }
+
+size_t sla_workspace_size(const sla_problem_t *p, int op)
+{
+    if (validate_problem(p) != SLA_OK) return 0;
+    if (op != SLA_OP_FWD && op != SLA_OP_BWD) return 0;
+    return layout(p, op).total;
+}
+
+int64_t sla_schedule_capacity(const sla_problem_t *p, int op)
+{
+    if (validate_problem(p) != SLA_OK) return -1;
+    const WsLayout w = layout(p, op);
+    return op == SLA_OP_FWD ? w.fwd_items : w.bwd_items;
+}
+
+int32_t sla_schedule_tile(int op, int which)
+{
+    if (op == SLA_OP_FWD) return which == 0 ? FWD_BM : FWD_BN;
+    if (op == SLA_OP_BWD) return which == 0 ? BWD_BN : BWD_BM;
+    return -1;
+}
+
+sla_status_t sla_schedule(const sla_problem_t *p, int op, int32_t *records, int64_t capacity,
+                          int32_t *count, void *workspace, size_t ws_bytes, void *stream)
+{
+    sla_status_t st = validate_problem(p);
+    if (st != SLA_OK) return st;
+    if (op != SLA_OP_FWD && op != SLA_OP_BWD) return fail(SLA_ERR_INVALID, "bad op %d", op);
+    if (!records || !count) return fail(SLA_ERR_NULL, "records or count is NULL");
+    if (capacity < layout(p, op).fwd_items && op == SLA_OP_FWD)
+        return fail(SLA_ERR_INVALID, "capacity below sla_schedule_capacity");
+    if (capacity < layout(p, op).bwd_items && op == SLA_OP_BWD)
+        return fail(SLA_ERR_INVALID, "capacity below sla_schedule_capacity");
+    AttnParams a;
+    if ((st = make_params(p, SLA_OP_FWD, workspace, ws_bytes, a)) != SLA_OK) return st;
+    if ((st = check_device()) != SLA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    a.absmax_part = nullptr;
+    hipError_t e = launch_sched(a, s);
+    if (e != hipSuccess) return hip_fail(e, "schedule kernel");
+    e = launch_sched_dump(a, op, records, capacity, count, s);
+    if (e != hipSuccess) return hip_fail(e, "schedule dump kernel");
+    return SLA_OK;
+}
+
+int64_t sla_schedule_host(const sla_problem_t *p, int op, const int64_t *offsets_host,
+                          const int32_t *num_targets_host, int32_t *records, int64_t capacity)
+{
+    if (!p) return fail(SLA_ERR_NULL, "problem is NULL"), -1;
+    sla_problem_t hp = *p;  // the device pointers are not used here
+    hp.offsets = offsets_host;
+    hp.num_targets = num_targets_host;
+    p = &hp;
+    if (validate_problem(p) != SLA_OK) return -1;
+    if (op != SLA_OP_FWD && op != SLA_OP_BWD) {
+        fail(SLA_ERR_INVALID, "bad op %d", op);
+        return -1;
+    }
+    if (p->batch > 0 && !offsets_host) {
+        fail(SLA_ERR_NULL, "offsets_host is NULL");
+        return -1;
+    }
+    const int K2e = k2_eff(p);
+    int64_t n = 0;
+    for (int b = 0; b < p->batch; ++b) {
+        const int64_t L64 = offsets_host[b + 1] - offsets_host[b];
+        const int64_t nt = num_targets_host ? num_targets_host[b] : 0;
+        if (L64 < 0 || L64 >= ((int64_t)1 << 30) || nt < 0 || nt > L64) {
+            fail(SLA_ERR_INVALID, "sequence %d: bad length or target count", b);
+            return -1;
+        }
+        const int L = (int)L64, U = (int)(L64 - nt);
+        const int items = seq_items(op, L, U, K2e);
+        for (int li = 0; li < items; ++li, ++n) {
+            if (records && n < capacity)
+                fill_record(op, b, L, U, p->k1, K2e, li, records + n * SLA_SCHED_RECORD_INTS);
+        }
+    }
+    return n;
+}
+
+sla_status_t sla_fwd(const sla_problem_t *p, const void *q, int64_t ldq, const void *k, int64_t ldk,
+                     const void *v, int64_t ldv, void *o, int64_t ldo, void *workspace,
+                     size_t ws_bytes, void *stream)
+{
+    sla_status_t st = validate_problem(p);
+    if (st != SLA_OK) return st;
+    if (p->batch == 0 || p->total_tokens == 0) return SLA_OK;  // nothing is read or written
+    if ((st = validate_tensor("q", q, ldq, p, p->d_qk)) != SLA_OK) return st;
+    if ((st = validate_tensor("k", k, ldk, p, p->d_qk)) != SLA_OK) return st;
+    if ((st = validate_tensor("v", v, ldv, p, p->d_v)) != SLA_OK) return st;
+    if ((st = validate_tensor("o", o, ldo, p, p->d_v)) != SLA_OK) return st;
+    AttnParams a;
+    if ((st = make_params(p, SLA_OP_FWD, workspace, ws_bytes, a)) != SLA_OK) return st;
+    if ((st = check_device()) != SLA_OK) return st;
+    if (p->batch == 0 || p->total_tokens == 0) return SLA_OK;
+    a.q = q; a.k = k; a.v = v; a.o = o;
+    a.absmax_part = nullptr;
+    a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.ldo = ldo;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_sched(a, s);
+    if (e != hipSuccess) return hip_fail(e, "schedule kernel");
+    e = p->dtype == SLA_BF16 ? launch_fwd_bf16(a, s) : launch_fwd_f32(a, s);
+    if (e != hipSuccess) return hip_fail(e, "forward kernel");
+    return SLA_OK;
+}
+
+sla_status_t sla_bwd_stage(const sla_problem_t *p, int stage, const void *q, int64_t ldq,
+                           const void *k, int64_t ldk, const void *v, int64_t ldv,
+                           const void *dout, int64_t lddo, void *dq, int64_t lddq, void *dk,
+                           int64_t lddk, void *dv, int64_t lddv, void *workspace,
+                           size_t ws_bytes, void *stream)
+{
+    sla_status_t st = validate_problem(p);
+    if (st != SLA_OK) return st;
+    if (stage < SLA_BWD_ALL || stage > SLA_BWD_DQ) return fail(SLA_ERR_INVALID, "bad stage %d", stage);
+    if (p->batch == 0 || p->total_tokens == 0) return SLA_OK;  // nothing is read or written
+    if ((st = validate_tensor("q", q, ldq, p, p->d_qk)) != SLA_OK) return st;
+    if ((st = validate_tensor("k", k, ldk, p, p->d_qk)) != SLA_OK) return st;
+    if ((st = validate_tensor("v", v, ldv, p, p->d_v)) != SLA_OK) return st;
+    if ((st = validate_tensor("dout", dout, lddo, p, p->d_v)) != SLA_OK) return st;
+    if (stage == SLA_BWD_ALL || stage == SLA_BWD_DQ)
+        if ((st = validate_tensor("dq", dq, lddq, p, p->d_qk)) != SLA_OK) return st;
+    if (stage == SLA_BWD_ALL || stage == SLA_BWD_DKDV) {
+        if ((st = validate_tensor("dk", dk, lddk, p, p->d_qk)) != SLA_OK) return st;
+        if ((st = validate_tensor("dv", dv, lddv, p, p->d_v)) != SLA_OK) return st;
+    }
+    AttnParams a;
+    if ((st = make_params(p, SLA_OP_BWD, workspace, ws_bytes, a)) != SLA_OK) return st;
+    if ((st = check_device()) != SLA_OK) return st;
+    a.q = q; a.k = k; a.v = v; a.dout = dout; a.dq = dq; a.dk = dk; a.dv = dv;
+    a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.lddo = lddo; a.lddq = lddq; a.lddk = lddk;
+    a.lddv = lddv;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    if (stage == SLA_BWD_ALL || stage == SLA_BWD_PREPARE) {
+        if (p->dtype == SLA_BF16) {
+            e = launch_absmax(a, s);
+            if (e != hipSuccess) return hip_fail(e, "gradient scale kernel");
+        } else {
+            a.absmax_part = nullptr;
+        }
+        e = launch_sched(a, s);
+        if (e != hipSuccess) return hip_fail(e, "schedule kernel");
+    }
+    const bool bf = p->dtype == SLA_BF16;
+    if (stage == SLA_BWD_ALL || stage == SLA_BWD_DKDV) {
+        e = bf ? launch_bwd_dkdv_bf16(a, s) : launch_bwd_dkdv_f32(a, s);
+        if (e != hipSuccess) return hip_fail(e, "dK/dV kernels");
+    }
+    if (stage == SLA_BWD_ALL || stage == SLA_BWD_DQ) {
+        e = bf ? launch_bwd_dq_bf16(a, s) : launch_bwd_dq_f32(a, s);
+        if (e != hipSuccess) return hip_fail(e, "dQ kernel");
+    }
+    return SLA_OK;
+}
+
+sla_status_t sla_bwd(const sla_problem_t *p, const void *q, int64_t ldq, const void *k, int64_t ldk,
+                     const void *v, int64_t ldv, const void *dout, int64_t lddo, void *dq,
+                     int64_t lddq, void *dk, int64_t lddk, void *dv, int64_t lddv, void *workspace,
+                     size_t ws_bytes, void *stream)
+{
+    return sla_bwd_stage(p, SLA_BWD_ALL, q, ldq, k, ldk, v, ldv, dout, lddo, dq, lddq, dk, lddk, dv,
+                         lddv, workspace, ws_bytes, stream);
+}
+
+int64_t sla_count_pairs_host(int32_t batch, const int64_t *offsets_host,
+                             const int32_t *num_targets_host, int32_t k1, int32_t k2,
+                             int32_t contextual_len)
+{
+    if (batch < 0 || k1 < 0 || k2 < 0 || contextual_len < 0) return -1;
+    if (batch > 0 && !offsets_host) return -1;
+    const int64_t K1 = k1, K2e = k2 > contextual_len ? k2 : contextual_len;
+    int64_t total = 0;
+    for (int b = 0; b < batch; ++b) {
+        const int64_t L = offsets_host[b + 1] - offsets_host[b];
+        const int64_t nt = num_targets_host ? num_targets_host[b] : 0;
+        if (L < 0 || nt < 0 || nt > L) return -1;
+        const int64_t U = L - nt;
+        // history row i: window [i-K1+1, i] clipped at 0, plus prefix keys below it
+        for (int64_t i = 0; i < U; ++i) {
+            const int64_t w0 = i - K1 + 1 > 0 ? i - K1 + 1 : 0;
+            const int64_t win = i + 1 - w0;
+            int64_t pre = K2e < w0 ? K2e : w0;
+            total += win + pre;
+        }
+        // each target: history keys of row U's window, the prefix below it, itself
+        if (nt > 0) {
+            const int64_t w0 = U - K1 + 1 > 0 ? U - K1 + 1 : 0;
+            const int64_t win = U > w0 ? U - w0 : 0;
+            const int64_t pre = K2e < w0 ? K2e : w0;
+            total += nt * (win + (pre < U ? pre : U) + 1);
+        }
+    }
+    return total;
+}
+
+size_t stu_layer_workspace_size(const stu_layer_desc_t *d)
+{
+    if (!d || validate_problem(&d->attn) != SLA_OK || d->hidden <= 0) return 0;
+    const sla_problem_t *p = &d->attn;
+    const size_t T = (size_t)p->total_tokens, H = (size_t)p->num_heads;
+    const size_t nw = 2 * H * p->d_v + 2 * H * p->d_qk;
+    size_t bytes = 0;
+    bytes += round_up(T * d->hidden * 2, 256);      // n
+    bytes += round_up(T * nw * 2, 256);             // uvqk
+    bytes += round_up(T * H * p->d_v * 2, 256);     // A
+    bytes += round_up(T * H * p->d_v * 2, 256);     // y
+    bytes += layout(p, SLA_OP_FWD).total;           // attention schedule
+    return bytes;
+}
+
+sla_status_t stu_layer_fwd(const stu_layer_desc_t *d, const void *x, const float *ln1_w,
+                           const float *ln1_b, const void *w_uvqk, const float *b_uvqk,
+                           const float *ln2_w, const float *ln2_b, const void *w_out,
+                           const float *b_out, void *out, void *uvqk_out, void *workspace,
+                           size_t ws_bytes, void *stream)
+{
+    if (!d) return fail(SLA_ERR_NULL, "layer descriptor is NULL");
+    const sla_problem_t *p = &d->attn;
+    sla_status_t st = validate_problem(p);
+    if (st != SLA_OK) return st;
+    if (p->dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "the STU layer is bf16 only");
+    if (!x || !ln1_w || !w_uvqk || !ln2_w || !w_out || !out)
+        return fail(SLA_ERR_NULL, "a required layer pointer is NULL");
+    const int D = d->hidden, H = p->num_heads, dv = p->d_v, dqk = p->d_qk;
+    const int NU = H * dv, NW = 2 * H * dv + 2 * H * dqk;
+    if (D <= 0 || D % 128 != 0 || D > 2048)
+        return fail(SLA_ERR_UNSUPPORTED, "hidden %d must be a positive multiple of 128, <= 2048", D);
+    if (NU % 64 != 0 || NU > 2048)
+        return fail(SLA_ERR_UNSUPPORTED, "H*d_v = %d must be a multiple of 64, <= 2048", NU);
+    if (!(d->ln_eps > 0.0f) || !std::isfinite(d->ln_eps))
+        return fail(SLA_ERR_INVALID, "ln_eps must be positive");
+    if (out == x) return fail(SLA_ERR_INVALID, "out must not alias x");
+    const void *ptrs[] = {x, w_uvqk, w_out, out, uvqk_out, workspace};
+    for (const void *q : ptrs)
+        if (q && !aligned16(q)) return fail(SLA_ERR_UNSUPPORTED, "a layer buffer is not 16-byte aligned");
+    const size_t need = stu_layer_workspace_size(d);
+    if (!workspace || ws_bytes < need)
+        return fail(SLA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", ws_bytes, need);
+    if ((st = check_device()) != SLA_OK) return st;
+    const int64_t T = p->total_tokens;
+    if (T == 0 || p->batch == 0) return SLA_OK;
+
+    char *w = static_cast<char *>(workspace);
+    void *n = w;
+    w += round_up((size_t)T * D * 2, 256);
+    void *uvqk_ws = w;
+    w += round_up((size_t)T * NW * 2, 256);
+    void *A = w;
+    w += round_up((size_t)T * NU * 2, 256);
+    void *y = w;
+    w += round_up((size_t)T * NU * 2, 256);
+    void *attn_ws = w;
+    const size_t attn_bytes = layout(p, SLA_OP_FWD).total;
+    void *uvqk = uvqk_out ? uvqk_out : uvqk_ws;
+    uint16_t *u16 = static_cast<uint16_t *>(uvqk);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_layernorm_bf16(x, ln1_w, ln1_b, n, T, D, d->ln_eps, s);
+    if (e != hipSuccess) return hip_fail(e, "layernorm");
+    e = launch_gemm_bf16(n, D, w_uvqk, D, b_uvqk, nullptr, 0, uvqk, NW, T, NW, D, 0, s);
+    if (e != hipSuccess) return hip_fail(e, "uvqk projection");
+    // U | V | Q | K column blocks of the fused projection
+    st = sla_fwd(p, u16 + 2 * NU, NW, u16 + 2 * NU + H * dqk, NW, u16 + NU, NW, A, NU, attn_ws,
+                 attn_bytes, stream);
+    if (st != SLA_OK) return st;
+    e = launch_gated_layernorm_bf16(A, NU, u16, NW, ln2_w, ln2_b, y, T, NU, d->ln_eps, s);
+    if (e != hipSuccess) return hip_fail(e, "gated layernorm");
+    e = launch_gemm_bf16(y, NU, w_out, NU, b_out, x, D, out, D, T, D, NU, 1, s);
+    if (e != hipSuccess) return hip_fail(e, "output projection");
+    return SLA_OK;
+}
+
+sla_status_t stu_truncate(int32_t batch, int64_t total_tokens, const int64_t *offsets,
+                          const int32_t *num_targets, int32_t contextual_len, int32_t tail_len,
+                          const void *x, int32_t hidden, int32_t dtype, int64_t *new_offsets,
+                          int32_t *new_num_targets, int64_t *gather_idx, void *x_out,
+                          int64_t capacity, void *stream)
+{
+    if (batch < 0 || total_tokens < 0 || contextual_len < 0)
+        return fail(SLA_ERR_INVALID, "negative batch, total_tokens or contextual_len");
+    if (tail_len < 1) return fail(SLA_ERR_INVALID, "tail_len must be >= 1");
+    if (!new_offsets || (batch > 0 && !offsets)) return fail(SLA_ERR_NULL, "offsets is NULL");
+    if (dtype != SLA_F32 && dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "bad dtype");
+    const int eb = dtype == SLA_BF16 ? 2 : 4;
+    if (x_out) {
+        if (!x) return fail(SLA_ERR_NULL, "x is NULL");
+        if (hidden <= 0 || ((int64_t)hidden * eb) % 16 != 0)
+            return fail(SLA_ERR_UNSUPPORTED, "hidden row must be a positive multiple of 16 bytes");
+        if (!aligned16(x) || !aligned16(x_out))
+            return fail(SLA_ERR_UNSUPPORTED, "x / x_out not 16-byte aligned");
+    }
+    if (capacity < 0) return fail(SLA_ERR_INVALID, "negative capacity");
+    if (batch > 0 && total_tokens >= (int64_t)1 << 30)
+        return fail(SLA_ERR_UNSUPPORTED, "total_tokens too large");
+    sla_status_t st = check_device();
+    if (st != SLA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_truncate(batch, total_tokens, offsets, num_targets, contextual_len,
+                                   tail_len, x, hidden, eb, new_offsets, new_num_targets,
+                                   gather_idx, x_out, capacity, nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "truncation kernels");
+    return SLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,419 @@
+// sla_bwd_bf16.hip -- SLA backward on gfx950: bf16 MFMA, fp32 accumulation,
+// no atomics.
+//
+// With a_ij = SiLU(alpha s_ij), s_ij = q_i . k_j, O_i = (1/N) sum_j a_ij v_j
+// (ULTRA-HSTU paper, section 3 Eq.3 under the semi-local mask of section
+// 4.2.1 Eq.7), the chain rule gives, over visible pairs,
+//   dV_j = (1/N) sum_i a_ij dO_i
+//   dS_ij = (alpha/N) (dO_i . v_j) sigma_ij (1 + t_ij (1 - sigma_ij)),  t = alpha s
+//   dQ_i = sum_j dS_ij k_j,     dK_j = sum_i dS_ij q_i.
+// The kernels keep s*sigma and g*sigma*(1 + t(1 - sigma)) (g = dO.v) in the
+// MFMA operands and apply 1/N and alpha once in the epilogues.  The products
+// that consume P or dS run on fp16 operands (P, dS, dO^T, Q^T, K^T); dS and dO
+// are multiplied by a power of two G that maps max|dO| into [1, 2) (computed on
+// the device before these kernels) so that fp16's range follows the gradient
+// scale, and the epilogues divide it out.
+//
+// Ownership split (the KV-parallel / Q-parallel pair of backward schedules the
+// WHALE notes describe): the dK/dV kernel owns a 128-key tile and walks the row
+// tiles that see it; the dQ kernel owns a 128-row tile and walks its key tiles,
+// recomputing S and dP.  Global-prefix key tiles are seen by every later row,
+// so they are cut into row chunks whose fp32 partial sums a third kernel adds
+// in chunk order: results are bitwise reproducible.
+#include "sla_device.h"
+#include "sla_kernels.h"
+#include "sla_tiles.h"
+
+namespace sla {
+
+// ---------------------------------------------------------------------------
+// dK / dV
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, 1) void sla_bwd_dkdv_bf16_kernel(AttnParams p)
+{
+    constexpr int BN = BWD_BN, BM = BWD_BM;
+    constexpr int NC = D / 16, NDB = D / 32;
+    static_assert(BM == 64, "row steps are 64-row tiles");
+    __shared__ __align__(16) uint16_t sq[2][BM * D];
+    __shared__ __align__(16) uint16_t sdo[2][BM * D];
+    __shared__ __align__(16) uint16_t sqt[2][D * BM];
+    __shared__ __align__(16) uint16_t sdot[2][D * BM];
+
+    const int nrec = p.s.bwd_base[p.B];
+    const int item = xcd_remap(blockIdx.x, nrec * p.H);
+    if (item < 0) return;
+    const int h = item / nrec;
+    const int rec = item - h * nrec;
+    const int b = find_seq(p.s.bwd_base, p.B, rec);
+    const SeqDims sd = seq_dims(p.offsets, p.num_targets, b);
+    int np, nch;
+    bwd_items(sd.L, sd.U, p.k2e, BN, BM, np, nch);
+    const BwdItem it = bwd_item(sd.L, sd.U, p.k1, p.k2e, BN, BM, rec - p.s.bwd_base[b], np, nch);
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int l32 = lane & 31, hl = lane >> 5;
+
+    const uint16_t *qg = reinterpret_cast<const uint16_t *>(p.q) + sd.base * p.ldq + h * D;
+    const uint16_t *kg = reinterpret_cast<const uint16_t *>(p.k) + sd.base * p.ldk + h * D;
+    const uint16_t *vg = reinterpret_cast<const uint16_t *>(p.v) + sd.base * p.ldv + h * D;
+    const uint16_t *gg = reinterpret_cast<const uint16_t *>(p.dout) + sd.base * p.lddo + h * D;
+
+    // stationary K^T and V^T operands: lane holds key kj, d-slots 16c + 8*hl .. +8
+    const int kj = it.c0 + 32 * wv + l32;
+    bf16x8 kb[NC], vb[NC];
+    {
+        const bool ok = kj < it.c1;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            kb[c] = as_bf16x8(ld16_or_zero(kg + (int64_t)kj * p.ldk + 16 * c + 8 * hl, ok));
+            vb[c] = as_bf16x8(ld16_or_zero(vg + (int64_t)kj * p.ldv + 16 * c + 8 * hl, ok));
+        }
+    }
+
+    // row steps: history tiles covering [ha, hb), then target tiles covering [ta, tb)
+    int h_first = 0, nh = 0, t_first = 0, nt = 0;
+    if (it.ha < it.hb) {
+        h_first = it.ha / BM;
+        nh = cdiv(it.hb, BM) - h_first;
+    }
+    if (it.ta < it.tb) {
+        t_first = (it.ta - sd.U) / BM;
+        nt = cdiv(it.tb - sd.U, BM) - t_first;
+    }
+    const int nsteps = nh + nt;
+
+    floatx16 dkacc[NDB], dvacc[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) {
+        dkacc[i] = zero16();
+        dvacc[i] = zero16();
+    }
+
+    Tile64<D> qt, gt;
+    auto step_rows = [&](int s, int &m0, int &m1) {
+        if (s < nh) {
+            m0 = (h_first + s) * BM;
+            m1 = imin(m0 + BM, sd.U);
+        } else {
+            m0 = sd.U + (t_first + s - nh) * BM;
+            m1 = imin(m0 + BM, sd.L);
+        }
+    };
+    int m0n = 0, m1n = 0;
+    if (nsteps > 0) {
+        step_rows(0, m0n, m1n);
+        qt.load(qg, p.ldq, m0n, m1n, tid);
+        gt.load(gg, p.lddo, m0n, m1n, tid);
+    }
+    const float nal2e = p.neg_alpha_log2e, alpha = p.alpha;
+    const float gscale = *p.grad_scale;
+    const bool key_tile_full = (it.c1 - it.c0 == BN);
+    for (int s = 0; s < nsteps; ++s) {
+        const int buf = s & 1;
+        const int m0 = m0n, m1 = m1n;
+        qt.store_rows(sq[buf], tid);
+        store_transposed_f16<D>(qt, sqt[buf], tid, 1.0f);
+        gt.store_rows(sdo[buf], tid);
+        store_transposed_f16<D>(gt, sdot[buf], tid, gscale);
+        if (s + 1 < nsteps) {
+            step_rows(s + 1, m0n, m1n);
+            qt.load(qg, p.ldq, m0n, m1n, tid);
+            gt.load(gg, p.lddo, m0n, m1n, tid);
+        }
+        __syncthreads();
+
+        // S = Q K^T and dP = dO V^T for two 32-row blocks (rows in the registers)
+        floatx16 sacc[2], pacc[2];
+#pragma unroll
+        for (int qb2 = 0; qb2 < 2; ++qb2) {
+            sacc[qb2] = zero16();
+            pacc[qb2] = zero16();
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                bf16x8 aq = lds_row_chunk<D>(sq[buf], 32 * qb2 + l32, 2 * c + hl);
+                sacc[qb2] = mfma32(aq, kb[c], sacc[qb2]);
+                bf16x8 ag = lds_row_chunk<D>(sdo[buf], 32 * qb2 + l32, 2 * c + hl);
+                pacc[qb2] = mfma32(ag, vb[c], pacc[qb2]);
+            }
+        }
+
+        // rows at or past m1 were loaded as zero, so they add nothing
+        const bool full = (m1 <= sd.U) && key_tile_full && (it.c0 + BN - 1 <= m0) &&
+                          ((m1 - 1 - it.c0 < p.k1) || (it.c0 + BN <= p.k2e));
+#pragma unroll
+        for (int qb2 = 0; qb2 < 2; ++qb2) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float sv = sacc[qb2][r], g = pacc[qb2][r];
+                if (!full) {
+                    const int i = m0 + 32 * qb2 + 8 * (r >> 2) + 4 * hl + (r & 3);
+                    if (!visible(i, kj, sd.U, p.k1, p.k2e)) {
+                        sv = 0.0f;
+                        g = 0.0f;
+                    }
+                }
+                const float sg = sigmoid_fast(sv, nal2e);
+                const float a = sv * sg;                        // SiLU(alpha s) / alpha
+                sacc[qb2][r] = a;
+                pacc[qb2][r] = g * gscale * (sg + alpha * a * (1.0f - sg));  // G g SiLU'(t)
+            }
+        }
+
+        // dV += P^T dO and dK += dS^T Q over four 16-row chunks
+#pragma unroll
+        for (int qc = 0; qc < 4; ++qc) {
+            const int o = 8 * (qc & 1);
+            const floatx16 &ps = sacc[qc >> 1];
+            const floatx16 &ds = pacc[qc >> 1];
+            halfx8 pa = cvt8h(ps[o], ps[o + 1], ps[o + 2], ps[o + 3], ps[o + 4], ps[o + 5],
+                              ps[o + 6], ps[o + 7]);
+            halfx8 da = cvt8h(ds[o], ds[o + 1], ds[o + 2], ds[o + 3], ds[o + 4], ds[o + 5],
+                              ds[o + 6], ds[o + 7]);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                halfx8 bg = lds_t_chunk_h(sdot[buf], 32 * db + l32, 2 * qc + hl);
+                dvacc[db] = mfma32h(pa, bg, dvacc[db]);
+                halfx8 bq = lds_t_chunk_h(sqt[buf], 32 * db + l32, 2 * qc + hl);
+                dkacc[db] = mfma32h(da, bq, dkacc[db]);
+            }
+        }
+    }
+
+    // accumulator: lane holds column d = 32*db + l32, register r holds key
+    // 32*wv + 8*(r/4) + 4*hl + r%4 of the tile
+    if (it.nchunk == 1) {
+        uint16_t *dkg = reinterpret_cast<uint16_t *>(p.dk) + sd.base * p.lddk + h * D;
+        uint16_t *dvg = reinterpret_cast<uint16_t *>(p.dv) + sd.base * p.lddv + h * D;
+        const float sk_ = p.out_scale / gscale, sv_ = sk_;  // both carry alpha / (N G)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int j = it.c0 + 32 * wv + 8 * (r >> 2) + 4 * hl + (r & 3);
+                if (j < it.c1) {
+                    __bf16 kv = (__bf16)(dkacc[db][r] * sk_);
+                    __bf16 vv = (__bf16)(dvacc[db][r] * sv_);
+                    dkg[(int64_t)j * p.lddk + 32 * db + l32] = __builtin_bit_cast(uint16_t, kv);
+                    dvg[(int64_t)j * p.lddv + 32 * db + l32] = __builtin_bit_cast(uint16_t, vv);
+                }
+            }
+        }
+    } else {
+        const int slot = p.s.part_base[b] + it.tile * nch + it.chunk;
+        float *part = p.partials + ((int64_t)slot * p.H + h) * BN * (2 * D);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int jl = 32 * wv + 8 * (r >> 2) + 4 * hl + (r & 3);
+                part[jl * (2 * D) + 32 * db + l32] = dkacc[db][r];
+                part[jl * (2 * D) + D + 32 * db + l32] = dvacc[db][r];
+            }
+        }
+    }
+}
+
+// Sum the chunk partials of each split prefix key tile in chunk order.
+template <int D>
+__global__ __launch_bounds__(256) void sla_bwd_reduce_kernel(AttnParams p)
+{
+    constexpr int BN = BWD_BN, W = 2 * D;
+    const int nrec = p.s.red_base[p.B];
+    const int item = blockIdx.x;
+    if (item >= nrec * p.H) return;
+    const int h = item / nrec;
+    const int rec = item - h * nrec;
+    const int b = find_seq(p.s.red_base, p.B, rec);
+    const SeqDims sd = seq_dims(p.offsets, p.num_targets, b);
+    const int tile = rec - p.s.red_base[b];
+    const int nch = p.s.nch[b];
+    const int slot0 = p.s.part_base[b] + tile * nch;
+    const int c0 = tile * BN, c1 = imin(c0 + BN, sd.L);
+    uint16_t *dkg = reinterpret_cast<uint16_t *>(p.dk) + sd.base * p.lddk + h * D;
+    uint16_t *dvg = reinterpret_cast<uint16_t *>(p.dv) + sd.base * p.lddv + h * D;
+    for (int e4 = threadIdx.x; e4 < BN * W / 4; e4 += blockDim.x) {
+        const int e = 4 * e4;
+        const int jl = e / W, col = e % W;
+        if (c0 + jl >= c1) continue;
+        float4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < nch; ++c) {
+            const float4 v = *reinterpret_cast<const float4 *>(
+                p.partials + ((int64_t)(slot0 + c) * p.H + h) * BN * W + e);
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
+        const bool is_k = col < D;
+        const float sc = p.out_scale / *p.grad_scale;
+        uint2 o = cvt4_u2(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
+        uint16_t *dst = is_k ? dkg + (int64_t)(c0 + jl) * p.lddk + col
+                             : dvg + (int64_t)(c0 + jl) * p.lddv + (col - D);
+        *reinterpret_cast<uint2 *>(dst) = o;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, 1) void sla_bwd_dq_bf16_kernel(AttnParams p)
+{
+    constexpr int BM = FWD_BM, BN = FWD_BN;
+    constexpr int NC = D / 16, NDB = D / 32;
+    __shared__ __align__(16) uint16_t sk[2][BN * D];
+    __shared__ __align__(16) uint16_t sv[2][BN * D];
+    __shared__ __align__(16) uint16_t skt[2][D * BN];
+
+    const int nrec = p.s.fwd_base[p.B];
+    const int item = xcd_remap(blockIdx.x, nrec * p.H);
+    if (item < 0) return;
+    const int h = item / nrec;
+    const int rec = item - h * nrec;
+    const int b = find_seq(p.s.fwd_base, p.B, rec);
+    const SeqDims sd = seq_dims(p.offsets, p.num_targets, b);
+    int r0, r1;
+    row_tile(sd.L, sd.U, BM, rec - p.s.fwd_base[b], r0, r1);
+    const Ranges kr = fwd_key_ranges(sd.L, sd.U, p.k1, p.k2e, r0, r1, BN);
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int l32 = lane & 31, hl = lane >> 5;
+
+    const uint16_t *qg = reinterpret_cast<const uint16_t *>(p.q) + sd.base * p.ldq + h * D;
+    const uint16_t *kg = reinterpret_cast<const uint16_t *>(p.k) + sd.base * p.ldk + h * D;
+    const uint16_t *vg = reinterpret_cast<const uint16_t *>(p.v) + sd.base * p.ldv + h * D;
+    const uint16_t *gg = reinterpret_cast<const uint16_t *>(p.dout) + sd.base * p.lddo + h * D;
+
+    const int qi = r0 + 32 * wv + l32;
+    bf16x8 qb[NC], gb[NC];
+    {
+        const bool ok = qi < r1;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            qb[c] = as_bf16x8(ld16_or_zero(qg + (int64_t)qi * p.ldq + 16 * c + 8 * hl, ok));
+            gb[c] = as_bf16x8(ld16_or_zero(gg + (int64_t)qi * p.lddo + 16 * c + 8 * hl, ok));
+        }
+    }
+
+    const TileCursor cur(kr, BN);
+    const int ntiles = cur.total;
+    floatx16 dqacc[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) dqacc[i] = zero16();
+
+    Tile64<D> kt, vt;
+    int c_next = cur.start(0, BN);
+    if (ntiles > 0) {
+        kt.load(kg, p.ldk, c_next, sd.L, tid);
+        vt.load(vg, p.ldv, c_next, sd.L, tid);
+    }
+    const float nal2e = p.neg_alpha_log2e, alpha = p.alpha;
+    const float gscale = *p.grad_scale;
+    for (int t = 0; t < ntiles; ++t) {
+        const int buf = t & 1;
+        const int c0 = c_next;
+        kt.store_rows(sk[buf], tid);
+        store_transposed_f16<D>(kt, skt[buf], tid, 1.0f);
+        vt.store_rows(sv[buf], tid);
+        c_next = cur.start(t + 1, BN);
+        if (t + 1 < ntiles) {
+            kt.load(kg, p.ldk, c_next, sd.L, tid);
+            vt.load(vg, p.ldv, c_next, sd.L, tid);
+        }
+        __syncthreads();
+
+        // S^T = K Q^T, dP^T = V dO^T (rows in the lane dimension)
+        floatx16 sacc[2], pacc[2];
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+            sacc[kb2] = zero16();
+            pacc[kb2] = zero16();
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                bf16x8 ak = lds_row_chunk<D>(sk[buf], 32 * kb2 + l32, 2 * c + hl);
+                sacc[kb2] = mfma32(ak, qb[c], sacc[kb2]);
+                bf16x8 av = lds_row_chunk<D>(sv[buf], 32 * kb2 + l32, 2 * c + hl);
+                pacc[kb2] = mfma32(av, gb[c], pacc[kb2]);
+            }
+        }
+
+        const bool full = (r0 < sd.U) && (c0 + BN <= sd.L) && (c0 + BN - 1 <= r0) &&
+                          ((r1 - 1 - c0 < p.k1) || (c0 + BN <= p.k2e));
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float s = sacc[kb2][r], g = pacc[kb2][r];
+                if (!full) {
+                    const int j = c0 + 32 * kb2 + 8 * (r >> 2) + 4 * hl + (r & 3);
+                    if (!visible(qi, j, sd.U, p.k1, p.k2e)) {
+                        s = 0.0f;
+                        g = 0.0f;
+                    }
+                }
+                const float sg = sigmoid_fast(s, nal2e);
+                pacc[kb2][r] = g * gscale * (sg + alpha * s * sg * (1.0f - sg));
+            }
+        }
+
+        // dQ^T += K^T dS^T over four 16-key chunks
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+            const floatx16 &src = pacc[kc >> 1];
+            const int o = 8 * (kc & 1);
+            halfx8 dsb = cvt8h(src[o], src[o + 1], src[o + 2], src[o + 3], src[o + 4],
+                               src[o + 5], src[o + 6], src[o + 7]);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                halfx8 a = lds_t_chunk_h(skt[buf], 32 * db + l32, 2 * kc + hl);
+                dqacc[db] = mfma32h(a, dsb, dqacc[db]);
+            }
+        }
+    }
+
+    if (qi < r1) {
+        uint16_t *orow = reinterpret_cast<uint16_t *>(p.dq) + (sd.base + qi) * p.lddq + h * D;
+        const float sc = p.out_scale / gscale;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                uint2 v = cvt4_u2(dqacc[db][4 * g] * sc, dqacc[db][4 * g + 1] * sc,
+                                  dqacc[db][4 * g + 2] * sc, dqacc[db][4 * g + 3] * sc);
+                *reinterpret_cast<uint2 *>(orow + 32 * db + 8 * g + 4 * hl) = v;
+            }
+        }
+    }
+}
+
+template <int D>
+static hipError_t launch_dkdv_d(const AttnParams &p, hipStream_t st)
+{
+    hipLaunchKernelGGL(sla_bwd_dkdv_bf16_kernel<D>, dim3(p.grid_bwd), dim3(256), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.grid_red == 0) return e;
+    hipLaunchKernelGGL(sla_bwd_reduce_kernel<D>, dim3(p.grid_red), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv_bf16(const AttnParams &p, hipStream_t st)
+{
+    switch (p.d) {
+    case 32: return launch_dkdv_d<32>(p, st);
+    case 64: return launch_dkdv_d<64>(p, st);
+    case 128: return launch_dkdv_d<128>(p, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_bwd_dq_bf16(const AttnParams &p, hipStream_t st)
+{
+    dim3 grid(p.grid_fwd), block(256);
+    switch (p.d) {
+    case 32: hipLaunchKernelGGL(sla_bwd_dq_bf16_kernel<32>, grid, block, 0, st, p); break;
+    case 64: hipLaunchKernelGGL(sla_bwd_dq_bf16_kernel<64>, grid, block, 0, st, p); break;
+    case 128: hipLaunchKernelGGL(sla_bwd_dq_bf16_kernel<128>, grid, block, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace sla

@@ -1,0 +1,160 @@
+// sla_device.h -- CDNA4 (gfx950) device helpers for the SLA kernels: bf16
+// vectors, the 32x32x16 bf16 MFMA, LDS swizzles, the pointwise SiLU and its
+// derivative in registers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sla_internal.h"
+
+namespace sla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
+typedef uint16_t bf16_t;  // bf16 storage as raw bits on the host-visible side
+
+// D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16).
+// Lane l holds A[m = l%32][k-slot 8*(l/32) .. +8], B[k-slot ..][n = l%32];
+// the accumulator register r of lane l is D[8*(r/4) + 4*(l/32) + r%4][l%32].
+// The k slots only have to agree between A and B; kernels choose which logical
+// index each slot carries.
+__device__ __forceinline__ floatx16 mfma32(const bf16x8 &a, const bf16x8 &b, const floatx16 &c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Same shape with fp16 operands.  The second product of each attention pair
+// (P.V, P^T.dO, dS^T.Q, dS.K) runs in fp16: its computed operand (P or dS) is
+// rounded to 11 significant bits instead of bf16's 8, which keeps the bf16
+// outputs within their error budget; the partner input is converted to fp16
+// when it is staged into LDS.
+__device__ __forceinline__ floatx16 mfma32h(const halfx8 &a, const halfx8 &b, const floatx16 &c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx16 zero16()
+{
+    floatx16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+    return z;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ uint4 as_u4(const bf16x8 &b) { return __builtin_bit_cast(uint4, b); }
+
+// 8 fp32 -> 8 bf16 (round to nearest even; v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16x8 cvt8(float a0, float a1, float a2, float a3, float a4, float a5,
+                                       float a6, float a7)
+{
+    floatx2 p0 = {a0, a1}, p1 = {a2, a3}, p2 = {a4, a5}, p3 = {a6, a7};
+    bf16x2 b0 = __builtin_convertvector(p0, bf16x2);
+    bf16x2 b1 = __builtin_convertvector(p1, bf16x2);
+    bf16x2 b2 = __builtin_convertvector(p2, bf16x2);
+    bf16x2 b3 = __builtin_convertvector(p3, bf16x2);
+    bf16x8 r;
+    r[0] = b0[0]; r[1] = b0[1]; r[2] = b1[0]; r[3] = b1[1];
+    r[4] = b2[0]; r[5] = b2[1]; r[6] = b3[0]; r[7] = b3[1];
+    return r;
+}
+
+__device__ __forceinline__ halfx8 as_halfx8(const uint4 &u) { return __builtin_bit_cast(halfx8, u); }
+
+// 8 fp32 -> 8 fp16 (round to nearest even; v_cvt_pk_f16_f32).
+__device__ __forceinline__ halfx8 cvt8h(float a0, float a1, float a2, float a3, float a4, float a5,
+                                        float a6, float a7)
+{
+    floatx2 p0 = {a0, a1}, p1 = {a2, a3}, p2 = {a4, a5}, p3 = {a6, a7};
+    halfx2 b0 = __builtin_convertvector(p0, halfx2);
+    halfx2 b1 = __builtin_convertvector(p1, halfx2);
+    halfx2 b2 = __builtin_convertvector(p2, halfx2);
+    halfx2 b3 = __builtin_convertvector(p3, halfx2);
+    halfx8 r;
+    r[0] = b0[0]; r[1] = b0[1]; r[2] = b1[0]; r[3] = b1[1];
+    r[4] = b2[0]; r[5] = b2[1]; r[6] = b3[0]; r[7] = b3[1];
+    return r;
+}
+
+__device__ __forceinline__ uint32_t cvt2h_u32(float a, float b)
+{
+    floatx2 p = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(p, halfx2));
+}
+
+__device__ __forceinline__ uint2 cvt4_u2(float a0, float a1, float a2, float a3)
+{
+    floatx2 p0 = {a0, a1}, p1 = {a2, a3};
+    bf16x2 b0 = __builtin_convertvector(p0, bf16x2);
+    bf16x2 b1 = __builtin_convertvector(p1, bf16x2);
+    uint2 r;
+    r.x = __builtin_bit_cast(uint32_t, b0);
+    r.y = __builtin_bit_cast(uint32_t, b1);
+    return r;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// ---------------------------------------------------------------------------
+// Pointwise activation in registers.  With t = alpha*s and
+// e = 2^(t * -log2(e)) = exp(-t):  sigma = 1 / (1 + e),  SiLU(t) = t * sigma.
+// The forward keeps s * sigma and applies alpha once, with 1/N, to the output.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float sigmoid_fast(float s, float neg_alpha_log2e)
+{
+    float e = __builtin_amdgcn_exp2f(s * neg_alpha_log2e);
+    return __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// ---------------------------------------------------------------------------
+// Memory helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ uint4 ld16_or_zero(const void *p, bool ok)
+{
+    uint4 z = {0u, 0u, 0u, 0u};
+    return ok ? *reinterpret_cast<const uint4 *>(p) : z;
+}
+
+// 16-byte chunk swizzle for a row-major tile whose rows hold `cpr` chunks: the
+// chunk index is XORed with the low bits of the row so that 8 consecutive rows
+// read at the same logical chunk hit 8 different bank groups.
+template <int CPR>
+__device__ __forceinline__ int swz_row(int row, int chunk)
+{
+    constexpr int m = (CPR >= 8 ? 8 : CPR) - 1;
+    return chunk ^ (row & m);
+}
+
+// Swizzle for the transposed tiles ([d][key] with 64-key rows = 8 chunks):
+// consecutive d of one aligned group of 8 land in distinct bank groups, and
+// rows 8 apart also differ.
+__device__ __forceinline__ int swz_t(int d, int chunk) { return chunk ^ ((d ^ (d >> 3)) & 7); }
+
+// Position of key k (0..63) inside a transposed 64-key row.  Within every 16-key
+// group the 4-key blocks are stored in the order 0, 2, 1, 3, which is the order
+// in which the 32x32 MFMA accumulator hands a lane its keys (rows
+// 8*(r/4) + 4*half + r%4): a lane's 8 operand slots then read one 16-byte chunk.
+__device__ __forceinline__ int tpos(int k)
+{
+    int kb4 = (k >> 2) & 3;
+    int pb = ((kb4 & 1) << 1) | (kb4 >> 1);
+    return (k & ~15) | (pb << 2) | (k & 3);
+}
+
+// Select the low (sel = 0x05040100) or high (0x07060302) bf16 halves of two
+// words: result = lo-word half | hi-word half << 16.
+__device__ __forceinline__ uint32_t pack_halves(uint32_t lo_word, uint32_t hi_word, uint32_t sel)
+{
+    return __builtin_amdgcn_perm(hi_word, lo_word, sel);
+}
+
+}  // namespace sla

@@ -1,0 +1,319 @@
+// sla_f32.hip -- fp32 SLA forward and backward (plain FMA kernels).
+//
+// The fp32 path exists for small parity workloads that ask for single
+// precision; it uses the same on-device schedule as the bf16 MFMA kernels but
+// plain vector FMAs: four threads share one row (or key), each holding a
+// quarter of the head dimension, and combine dot products with two lane
+// shuffles.  Key/row tiles are staged in LDS.
+//
+// Semantics as in sla_fwd_bf16.hip / sla_bwd_bf16.hip (ULTRA-HSTU paper,
+// section 3 Eq.3 and section 4.2.1 Eq.6-7): O_i = (1/N) sum_j SiLU(alpha
+// q_i.k_j) v_j over visible pairs, and its gradients.
+#include "sla_device.h"
+#include "sla_kernels.h"
+
+namespace sla {
+
+constexpr int F32_TPR = 4;  // threads per row / key
+
+__device__ __forceinline__ float quad_sum(float x)
+{
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    return x;
+}
+
+__device__ __forceinline__ float silu_f32(float t) { return t / (1.0f + expf(-t)); }
+__device__ __forceinline__ float sigmoid_f32(float t) { return 1.0f / (1.0f + expf(-t)); }
+
+// cooperative copy of rows [r0, r0+nrows) (zero past `limit`) of a [T][ld]
+// fp32 tensor into a dense [nrows][D] LDS tile
+template <int D>
+__device__ __forceinline__ void stage_rows_f32(float *lds, const float *g, int64_t ld, int r0,
+                                               int nrows, int limit)
+{
+    for (int e = threadIdx.x * 4; e < nrows * D; e += blockDim.x * 4) {
+        const int r = e / D, c = e % D;
+        float4 v = {0.f, 0.f, 0.f, 0.f};
+        if (r0 + r < limit) v = *reinterpret_cast<const float4 *>(g + (int64_t)(r0 + r) * ld + c);
+        *reinterpret_cast<float4 *>(lds + e) = v;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(FWD_BM *F32_TPR) void sla_fwd_f32_kernel(AttnParams p)
+{
+    constexpr int BM = FWD_BM, BN = FWD_BN, DQ = D / F32_TPR;
+    __shared__ __align__(16) float sk[BN * D];
+    __shared__ __align__(16) float sv[BN * D];
+    const int nrec = p.s.fwd_base[p.B];
+    const int item = xcd_remap(blockIdx.x, nrec * p.H);
+    if (item < 0) return;
+    const int h = item / nrec, rec = item - h * nrec;
+    const int b = find_seq(p.s.fwd_base, p.B, rec);
+    const SeqDims sd = seq_dims(p.offsets, p.num_targets, b);
+    int r0, r1;
+    row_tile(sd.L, sd.U, BM, rec - p.s.fwd_base[b], r0, r1);
+    const TileCursor cur(fwd_key_ranges(sd.L, sd.U, p.k1, p.k2e, r0, r1, BN), BN);
+
+    const float *qg = reinterpret_cast<const float *>(p.q) + sd.base * p.ldq + h * D;
+    const float *kg = reinterpret_cast<const float *>(p.k) + sd.base * p.ldk + h * D;
+    const float *vg = reinterpret_cast<const float *>(p.v) + sd.base * p.ldv + h * D;
+    const int row = threadIdx.x / F32_TPR, qt = threadIdx.x % F32_TPR;
+    const int i = r0 + row;
+    float q[DQ], acc[DQ];
+#pragma unroll
+    for (int c = 0; c < DQ; ++c) {
+        q[c] = i < r1 ? qg[(int64_t)i * p.ldq + qt * DQ + c] : 0.0f;
+        acc[c] = 0.0f;
+    }
+    for (int t = 0; t < cur.total; ++t) {
+        const int c0 = cur.start(t, BN);
+        __syncthreads();
+        stage_rows_f32<D>(sk, kg, p.ldk, c0, BN, sd.L);
+        stage_rows_f32<D>(sv, vg, p.ldv, c0, BN, sd.L);
+        __syncthreads();
+        for (int jj = 0; jj < BN; ++jj) {
+            float s = 0.0f;
+#pragma unroll
+            for (int c = 0; c < DQ; ++c) s += q[c] * sk[jj * D + qt * DQ + c];
+            s = quad_sum(s);
+            const bool vis = i < r1 && c0 + jj < sd.L && visible(i, c0 + jj, sd.U, p.k1, p.k2e);
+            const float a = vis ? silu_f32(p.alpha * s) : 0.0f;
+#pragma unroll
+            for (int c = 0; c < DQ; ++c) acc[c] += a * sv[jj * D + qt * DQ + c];
+        }
+    }
+    if (i < r1) {
+        float *o = reinterpret_cast<float *>(p.o) + (sd.base + i) * p.ldo + h * D + qt * DQ;
+#pragma unroll
+        for (int c = 0; c < DQ; ++c) o[c] = acc[c] * p.inv_n;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(FWD_BM *F32_TPR) void sla_bwd_dq_f32_kernel(AttnParams p)
+{
+    constexpr int BM = FWD_BM, BN = FWD_BN, DQ = D / F32_TPR;
+    __shared__ __align__(16) float sk[BN * D];
+    __shared__ __align__(16) float sv[BN * D];
+    const int nrec = p.s.fwd_base[p.B];
+    const int item = xcd_remap(blockIdx.x, nrec * p.H);
+    if (item < 0) return;
+    const int h = item / nrec, rec = item - h * nrec;
+    const int b = find_seq(p.s.fwd_base, p.B, rec);
+    const SeqDims sd = seq_dims(p.offsets, p.num_targets, b);
+    int r0, r1;
+    row_tile(sd.L, sd.U, BM, rec - p.s.fwd_base[b], r0, r1);
+    const TileCursor cur(fwd_key_ranges(sd.L, sd.U, p.k1, p.k2e, r0, r1, BN), BN);
+
+    const float *qg = reinterpret_cast<const float *>(p.q) + sd.base * p.ldq + h * D;
+    const float *kg = reinterpret_cast<const float *>(p.k) + sd.base * p.ldk + h * D;
+    const float *vg = reinterpret_cast<const float *>(p.v) + sd.base * p.ldv + h * D;
+    const float *gg = reinterpret_cast<const float *>(p.dout) + sd.base * p.lddo + h * D;
+    const int row = threadIdx.x / F32_TPR, qt = threadIdx.x % F32_TPR;
+    const int i = r0 + row;
+    float q[DQ], go[DQ], acc[DQ];
+#pragma unroll
+    for (int c = 0; c < DQ; ++c) {
+        q[c] = i < r1 ? qg[(int64_t)i * p.ldq + qt * DQ + c] : 0.0f;
+        go[c] = i < r1 ? gg[(int64_t)i * p.lddo + qt * DQ + c] : 0.0f;
+        acc[c] = 0.0f;
+    }
+    for (int t = 0; t < cur.total; ++t) {
+        const int c0 = cur.start(t, BN);
+        __syncthreads();
+        stage_rows_f32<D>(sk, kg, p.ldk, c0, BN, sd.L);
+        stage_rows_f32<D>(sv, vg, p.ldv, c0, BN, sd.L);
+        __syncthreads();
+        for (int jj = 0; jj < BN; ++jj) {
+            float s = 0.0f, g = 0.0f;
+#pragma unroll
+            for (int c = 0; c < DQ; ++c) {
+                s += q[c] * sk[jj * D + qt * DQ + c];
+                g += go[c] * sv[jj * D + qt * DQ + c];
+            }
+            s = quad_sum(s);
+            g = quad_sum(g);
+            const bool vis = i < r1 && c0 + jj < sd.L && visible(i, c0 + jj, sd.U, p.k1, p.k2e);
+            const float tt = p.alpha * s, sg = sigmoid_f32(tt);
+            const float ds = vis ? g * sg * (1.0f + tt * (1.0f - sg)) : 0.0f;
+#pragma unroll
+            for (int c = 0; c < DQ; ++c) acc[c] += ds * sk[jj * D + qt * DQ + c];
+        }
+    }
+    if (i < r1) {
+        float *o = reinterpret_cast<float *>(p.dq) + (sd.base + i) * p.lddq + h * D + qt * DQ;
+#pragma unroll
+        for (int c = 0; c < DQ; ++c) o[c] = acc[c] * p.out_scale;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(BWD_BN *F32_TPR) void sla_bwd_dkdv_f32_kernel(AttnParams p)
+{
+    constexpr int BN = BWD_BN, BM = BWD_BM, DQ = D / F32_TPR;
+    __shared__ __align__(16) float sq[BM * D];
+    __shared__ __align__(16) float sg_[BM * D];
+    const int nrec = p.s.bwd_base[p.B];
+    const int item = xcd_remap(blockIdx.x, nrec * p.H);
+    if (item < 0) return;
+    const int h = item / nrec, rec = item - h * nrec;
+    const int b = find_seq(p.s.bwd_base, p.B, rec);
+    const SeqDims sd = seq_dims(p.offsets, p.num_targets, b);
+    int np, nch;
+    bwd_items(sd.L, sd.U, p.k2e, BN, BM, np, nch);
+    const BwdItem it = bwd_item(sd.L, sd.U, p.k1, p.k2e, BN, BM, rec - p.s.bwd_base[b], np, nch);
+
+    const float *qg = reinterpret_cast<const float *>(p.q) + sd.base * p.ldq + h * D;
+    const float *kg = reinterpret_cast<const float *>(p.k) + sd.base * p.ldk + h * D;
+    const float *vg = reinterpret_cast<const float *>(p.v) + sd.base * p.ldv + h * D;
+    const float *gg = reinterpret_cast<const float *>(p.dout) + sd.base * p.lddo + h * D;
+    const int kl = threadIdx.x / F32_TPR, qt = threadIdx.x % F32_TPR;
+    const int j = it.c0 + kl;
+    const bool jok = j < it.c1;
+    float kr[DQ], vr[DQ], dk[DQ], dv[DQ];
+#pragma unroll
+    for (int c = 0; c < DQ; ++c) {
+        kr[c] = jok ? kg[(int64_t)j * p.ldk + qt * DQ + c] : 0.0f;
+        vr[c] = jok ? vg[(int64_t)j * p.ldv + qt * DQ + c] : 0.0f;
+        dk[c] = dv[c] = 0.0f;
+    }
+    int h_first = 0, nh = 0, t_first = 0, nt = 0;
+    if (it.ha < it.hb) {
+        h_first = it.ha / BM;
+        nh = cdiv(it.hb, BM) - h_first;
+    }
+    if (it.ta < it.tb) {
+        t_first = (it.ta - sd.U) / BM;
+        nt = cdiv(it.tb - sd.U, BM) - t_first;
+    }
+    for (int s = 0; s < nh + nt; ++s) {
+        int m0, m1;
+        if (s < nh) {
+            m0 = (h_first + s) * BM;
+            m1 = imin(m0 + BM, sd.U);
+        } else {
+            m0 = sd.U + (t_first + s - nh) * BM;
+            m1 = imin(m0 + BM, sd.L);
+        }
+        __syncthreads();
+        stage_rows_f32<D>(sq, qg, p.ldq, m0, BM, m1);
+        stage_rows_f32<D>(sg_, gg, p.lddo, m0, BM, m1);
+        __syncthreads();
+        for (int ii = 0; ii < BM; ++ii) {
+            float sv = 0.0f, g = 0.0f;
+#pragma unroll
+            for (int c = 0; c < DQ; ++c) {
+                sv += sq[ii * D + qt * DQ + c] * kr[c];
+                g += sg_[ii * D + qt * DQ + c] * vr[c];
+            }
+            sv = quad_sum(sv);
+            g = quad_sum(g);
+            const int i = m0 + ii;
+            const bool vis = jok && i < m1 && visible(i, j, sd.U, p.k1, p.k2e);
+            const float tt = p.alpha * sv, sgm = sigmoid_f32(tt);
+            const float a = vis ? sv * sgm : 0.0f;  // SiLU(alpha s) / alpha
+            const float ds = vis ? g * sgm * (1.0f + tt * (1.0f - sgm)) : 0.0f;
+#pragma unroll
+            for (int c = 0; c < DQ; ++c) {
+                dv[c] += a * sg_[ii * D + qt * DQ + c];
+                dk[c] += ds * sq[ii * D + qt * DQ + c];
+            }
+        }
+    }
+    if (it.nchunk == 1) {
+        if (jok) {
+            float *ok = reinterpret_cast<float *>(p.dk) + (sd.base + j) * p.lddk + h * D + qt * DQ;
+            float *ov = reinterpret_cast<float *>(p.dv) + (sd.base + j) * p.lddv + h * D + qt * DQ;
+#pragma unroll
+            for (int c = 0; c < DQ; ++c) {
+                ok[c] = dk[c] * p.out_scale;
+                ov[c] = dv[c] * p.out_scale;
+            }
+        }
+    } else {
+        const int slot = p.s.part_base[b] + it.tile * nch + it.chunk;
+        float *part = p.partials + ((int64_t)slot * p.H + h) * BN * (2 * D) + kl * (2 * D);
+#pragma unroll
+        for (int c = 0; c < DQ; ++c) {
+            part[qt * DQ + c] = dk[c];
+            part[D + qt * DQ + c] = dv[c];
+        }
+    }
+}
+
+// fp32 reduce of split prefix key tiles, in chunk order; dK and dV partials
+// both take the alpha/N scale.
+template <int D>
+__global__ __launch_bounds__(256) void sla_bwd_reduce_f32_kernel(AttnParams p)
+{
+    constexpr int BN = BWD_BN, W = 2 * D;
+    const int nrec = p.s.red_base[p.B];
+    const int item = blockIdx.x;
+    if (item >= nrec * p.H) return;
+    const int h = item / nrec, rec = item - h * nrec;
+    const int b = find_seq(p.s.red_base, p.B, rec);
+    const SeqDims sd = seq_dims(p.offsets, p.num_targets, b);
+    const int tile = rec - p.s.red_base[b];
+    const int nch = p.s.nch[b];
+    const int slot0 = p.s.part_base[b] + tile * nch;
+    const int c0 = tile * BN, c1 = imin(c0 + BN, sd.L);
+    float *dkg = reinterpret_cast<float *>(p.dk) + sd.base * p.lddk + h * D;
+    float *dvg = reinterpret_cast<float *>(p.dv) + sd.base * p.lddv + h * D;
+    for (int e = threadIdx.x; e < BN * W; e += blockDim.x) {
+        const int jl = e / W, col = e % W;
+        if (c0 + jl >= c1) continue;
+        float acc = 0.0f;
+        for (int c = 0; c < nch; ++c) acc += p.partials[((int64_t)(slot0 + c) * p.H + h) * BN * W + e];
+        if (col < D) dkg[(int64_t)(c0 + jl) * p.lddk + col] = acc * p.out_scale;
+        else dvg[(int64_t)(c0 + jl) * p.lddv + (col - D)] = acc * p.out_scale;
+    }
+}
+
+hipError_t launch_fwd_f32(const AttnParams &p, hipStream_t st)
+{
+    dim3 grid(p.grid_fwd), block(FWD_BM * F32_TPR);
+    switch (p.d) {
+    case 32: hipLaunchKernelGGL(sla_fwd_f32_kernel<32>, grid, block, 0, st, p); break;
+    case 64: hipLaunchKernelGGL(sla_fwd_f32_kernel<64>, grid, block, 0, st, p); break;
+    case 128: hipLaunchKernelGGL(sla_fwd_f32_kernel<128>, grid, block, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_dkdv_f32_d(const AttnParams &p, hipStream_t st)
+{
+    hipLaunchKernelGGL(sla_bwd_dkdv_f32_kernel<D>, dim3(p.grid_bwd), dim3(BWD_BN * F32_TPR), 0,
+                       st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.grid_red == 0) return e;
+    hipLaunchKernelGGL(sla_bwd_reduce_f32_kernel<D>, dim3(p.grid_red), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv_f32(const AttnParams &p, hipStream_t st)
+{
+    switch (p.d) {
+    case 32: return launch_dkdv_f32_d<32>(p, st);
+    case 64: return launch_dkdv_f32_d<64>(p, st);
+    case 128: return launch_dkdv_f32_d<128>(p, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_bwd_dq_f32(const AttnParams &p, hipStream_t st)
+{
+    dim3 grid(p.grid_fwd), block(FWD_BM * F32_TPR);
+    switch (p.d) {
+    case 32: hipLaunchKernelGGL(sla_bwd_dq_f32_kernel<32>, grid, block, 0, st, p); break;
+    case 64: hipLaunchKernelGGL(sla_bwd_dq_f32_kernel<64>, grid, block, 0, st, p); break;
+    case 128: hipLaunchKernelGGL(sla_bwd_dq_f32_kernel<128>, grid, block, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace sla

@@ -1,0 +1,72 @@
+// sla_kernels.h -- kernel parameter blocks and the host-side launch functions
+// that each .hip translation unit provides to the C-ABI layer (sla_api.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sla_internal.h"
+
+namespace sla {
+
+struct AttnParams {
+    const void *q, *k, *v;
+    void *o;
+    const void *dout;
+    void *dq, *dk, *dv;
+    int64_t ldq, ldk, ldv, ldo, lddo, lddq, lddk, lddv;  // token strides, elements
+    const int64_t *offsets;
+    const int32_t *num_targets;
+    int64_t T;              // total tokens
+    int B, H, d, k1, k2e;
+    float alpha;            // pre-activation factor
+    float inv_n;            // 1 / N
+    float out_scale;        // alpha / N
+    float neg_alpha_log2e;  // -alpha * log2(e)
+    Sched s;
+    float *partials;        // fp32 partial dK|dV of split prefix key tiles
+    float *absmax_part;     // [ABSMAX_BLOCKS] per-block max |dO|
+    float *grad_scale;      // [1] power of two with max|dO| * scale in [1, 2)
+    int grid_fwd;           // upper bound of forward / dQ work items (x heads)
+    int grid_bwd;           // upper bound of dK/dV work items (x heads)
+    int grid_red;           // upper bound of reduce items (x heads)
+};
+
+constexpr int ABSMAX_BLOCKS = 256;
+
+// Sizes (int32 counts / bytes) of the workspace regions, from host-known data.
+struct WsLayout {
+    size_t sched_off, part_off, total;
+    int64_t fwd_items, bwd_items, red_items, part_slots;  // upper bounds (per head)
+};
+
+hipError_t launch_sched(const AttnParams &p, hipStream_t st);
+// max |dO| per block into p.absmax_part (the schedule kernel folds it into
+// p.grad_scale when p.absmax_part is set)
+hipError_t launch_absmax(const AttnParams &p, hipStream_t st);
+hipError_t launch_sched_dump(const AttnParams &p, int op, int32_t *records, int64_t capacity,
+                             int32_t *count, hipStream_t st);
+hipError_t launch_fwd_bf16(const AttnParams &p, hipStream_t st);
+hipError_t launch_bwd_dkdv_bf16(const AttnParams &p, hipStream_t st);  // + prefix reduce
+hipError_t launch_bwd_dq_bf16(const AttnParams &p, hipStream_t st);
+hipError_t launch_fwd_f32(const AttnParams &p, hipStream_t st);
+hipError_t launch_bwd_dkdv_f32(const AttnParams &p, hipStream_t st);
+hipError_t launch_bwd_dq_f32(const AttnParams &p, hipStream_t st);
+
+// STU layer pieces (bf16 storage)
+hipError_t launch_layernorm_bf16(const void *x, const float *w, const float *b, void *y,
+                                 int64_t rows, int cols, float eps, hipStream_t st);
+hipError_t launch_gated_layernorm_bf16(const void *a, int64_t lda, const void *u, int64_t ldu,
+                                       const float *w, const float *b, void *y, int64_t rows,
+                                       int cols, float eps, hipStream_t st);
+// C[M][N] = epilogue(A[M][K] . W[N][K]^T): epi 0 = SiLU(acc + bias), 1 = acc + bias + R
+hipError_t launch_gemm_bf16(const void *A, int64_t lda, const void *W, int64_t ldw,
+                            const float *bias, const void *R, int64_t ldr, void *C, int64_t ldc,
+                            int64_t M, int N, int K, int epi, hipStream_t st);
+hipError_t launch_truncate(int B, int64_t T, const int64_t *offsets, const int32_t *num_targets,
+                           int ctx, int tail, const void *x, int hidden, int elem_bytes,
+                           int64_t *new_offsets, int32_t *new_num_targets, int64_t *gather_idx,
+                           void *x_out, int64_t capacity, int32_t *scratch_base,
+                           hipStream_t st);
+
+}  // namespace sla

@@ -1,0 +1,163 @@
+// sla_sched.hip -- on-device tile schedule of the SLA kernels.
+//
+// One workgroup turns the jagged offsets (and target counts) into per-sequence
+// prefix sums of the work items each kernel runs; the attention kernels then
+// locate their item without any host synchronisation (the WHALE notes'
+// observation that syncing on runtime shapes costs milliseconds per call is the
+// reason the schedule lives on the device).
+#include "sla_device.h"
+#include "sla_kernels.h"
+
+namespace sla {
+
+constexpr int SCHED_THREADS = 1024;
+
+__global__ __launch_bounds__(SCHED_THREADS) void sla_sched_kernel(const int64_t *offsets,
+                                                                  const int32_t *num_targets,
+                                                                  int B, int k2e, Sched s,
+                                                                  const float *absmax_part,
+                                                                  float *grad_scale)
+{
+    __shared__ int4 buf[2][SCHED_THREADS];
+    __shared__ int4 carry;
+    __shared__ float red[SCHED_THREADS / 64];
+    const int tid = threadIdx.x;
+    if (tid == 0) carry = make_int4(0, 0, 0, 0);
+    if (absmax_part) {
+        // gradient scale: the power of two that maps max|dO| into [1, 2)
+        float m = tid < ABSMAX_BLOCKS ? absmax_part[tid] : 0.0f;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+        if ((tid & 63) == 0) red[tid >> 6] = m;
+        __syncthreads();
+        if (tid == 0) {
+            float mx = 0.0f;
+            for (int i = 0; i < SCHED_THREADS / 64; ++i) mx = fmaxf(mx, red[i]);
+            float sc = 1.0f;
+            if (mx > 0.0f && mx < INFINITY) {
+                int e = ilogbf(mx);
+                e = e < -100 ? -100 : (e > 100 ? 100 : e);
+                sc = ldexpf(1.0f, -e);
+            }
+            *grad_scale = sc;
+        }
+    }
+    __syncthreads();
+    for (int start = 0; start < B; start += SCHED_THREADS) {
+        const int b = start + tid;
+        int4 v = make_int4(0, 0, 0, 0);
+        if (b < B) {
+            SeqDims sd = seq_dims(offsets, num_targets, b);
+            int np, nch;
+            v.x = row_tiles(sd.L, sd.U, FWD_BM);
+            v.y = bwd_items(sd.L, sd.U, k2e, BWD_BN, BWD_BM, np, nch);
+            v.z = nch > 1 ? np : 0;
+            v.w = nch > 1 ? np * nch : 0;
+            s.nch[b] = nch;
+        }
+        // inclusive Hillis-Steele scan of the four counters
+        int cur = 0;
+        buf[cur][tid] = v;
+        __syncthreads();
+        for (int off = 1; off < SCHED_THREADS; off <<= 1) {
+            int4 a = buf[cur][tid];
+            if (tid >= off) {
+                int4 c = buf[cur][tid - off];
+                a.x += c.x; a.y += c.y; a.z += c.z; a.w += c.w;
+            }
+            buf[cur ^ 1][tid] = a;
+            cur ^= 1;
+            __syncthreads();
+        }
+        int4 inc = buf[cur][tid];
+        int4 c0 = carry;
+        if (b < B) {
+            s.fwd_base[b] = c0.x + inc.x - v.x;
+            s.bwd_base[b] = c0.y + inc.y - v.y;
+            s.red_base[b] = c0.z + inc.z - v.z;
+            s.part_base[b] = c0.w + inc.w - v.w;
+        }
+        __syncthreads();
+        if (tid == SCHED_THREADS - 1) {
+            carry = make_int4(c0.x + inc.x, c0.y + inc.y, c0.z + inc.z, c0.w + inc.w);
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        int4 c = carry;
+        s.fwd_base[B] = c.x;
+        s.bwd_base[B] = c.y;
+        s.red_base[B] = c.z;
+        s.part_base[B] = c.w;
+    }
+}
+
+hipError_t launch_sched(const AttnParams &p, hipStream_t st)
+{
+    hipLaunchKernelGGL(sla_sched_kernel, dim3(1), dim3(SCHED_THREADS), 0, st, p.offsets,
+                       p.num_targets, p.B, p.k2e, p.s, (const float *)p.absmax_part,
+                       p.grad_scale);
+    return hipGetLastError();
+}
+
+// Per-block max |x| over the [T][H*d] rows (token stride ld) of a bf16 tensor;
+// a fixed grid and a fixed reduction order, so the result is deterministic.
+__global__ __launch_bounds__(256) void absmax_bf16_kernel(const uint16_t *x, int64_t ld,
+                                                          int64_t rows, int cols, float *part)
+{
+    __shared__ float red[4];
+    const int cpr = cols / 8;
+    const int64_t nchunks = rows * cpr;
+    float m = 0.0f;
+    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunks;
+         c += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = c / cpr;
+        const int k = (int)(c - r * cpr);
+        uint4 v = ld16(x + r * ld + 8 * k);
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+hipError_t launch_absmax(const AttnParams &p, hipStream_t st)
+{
+    hipLaunchKernelGGL(absmax_bf16_kernel, dim3(ABSMAX_BLOCKS), dim3(256), 0, st,
+                       (const uint16_t *)p.dout, p.lddo, p.T, p.H * p.d, p.absmax_part);
+    return hipGetLastError();
+}
+
+// Materialise the work list (one thread per record) so that it can be checked.
+__global__ void sla_sched_dump_kernel(const int64_t *offsets, const int32_t *num_targets, int B,
+                                      int k1, int k2e, Sched s, int op, int32_t *records,
+                                      int64_t capacity, int32_t *count)
+{
+    const int32_t *base = op == 0 ? s.fwd_base : s.bwd_base;
+    const int total = base[B];
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r == 0) *count = total;
+    if (r >= total || r >= capacity) return;
+    const int b = find_seq(base, B, (int)r);
+    const SeqDims sd = seq_dims(offsets, num_targets, b);
+    const int li = (int)r - base[b];
+    int32_t rec[12];
+    fill_record(op, b, sd.L, sd.U, k1, k2e, li, rec);
+    for (int i = 0; i < 12; ++i) records[r * 12 + i] = rec[i];
+}
+
+hipError_t launch_sched_dump(const AttnParams &p, int op, int32_t *records, int64_t capacity,
+                             int32_t *count, hipStream_t st)
+{
+    int64_t n = capacity > 0 ? capacity : 1;
+    int blocks = (int)((n + 255) / 256);
+    hipLaunchKernelGGL(sla_sched_dump_kernel, dim3(blocks), dim3(256), 0, st, p.offsets,
+                       p.num_targets, p.B, p.k1, p.k2e, p.s, op, records, capacity, count);
+    return hipGetLastError();
+}
+
+}  // namespace sla

@@ -1,0 +1,356 @@
+// stu_kernels.hip -- the STU layer around the attention (ULTRA-HSTU paper,
+// section 3 Eq.1-5, operation order of Code Listing 1) and attention
+// truncation (section 4.3), for gfx950:
+//   - row LayerNorm (Eq.1) and the gated LayerNorm(A) (.) U (Eq.4), fp32
+//     statistics over the whole row, bf16 in/out;
+//   - a bf16 MFMA GEMM C = A W^T with fused epilogues: SiLU(acc + b) for the
+//     U,V,Q,K projection (Eq.2, one fused projection as in HSTU notes section
+//     2.4 Eq.1) and acc + b + residual for the output projection (Eq.4-5; the
+//     residual as a 2-D bias in the GEMM epilogue, ULTRA-HSTU section 4.2.2);
+//   - the truncation index and row gather.
+#include "sla_device.h"
+#include "sla_kernels.h"
+
+namespace sla {
+
+// ---------------------------------------------------------------------------
+// LayerNorm: one wave per row, up to 4 x 512 columns
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float x)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+template <bool GATED>
+__global__ __launch_bounds__(256) void layernorm_bf16_kernel(const uint16_t *x, int64_t ldx,
+                                                             const uint16_t *u, int64_t ldu,
+                                                             const float *w, const float *bias,
+                                                             uint16_t *y, int64_t ldy,
+                                                             int64_t rows, int cols, float eps)
+{
+    constexpr int MAXC = 4;  // chunks of 8 per lane: cols <= 64 * 8 * 4
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const int nchunk = cols / 8;
+    float v[MAXC][8];
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int ch = lane + 64 * c;
+        if (ch < nchunk) {
+            uint4 raw = ld16(x + row * ldx + 8 * ch);
+            uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[c][2 * e] = bf16_lo(wd[e]);
+                v[c][2 * e + 1] = bf16_hi(wd[e]);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s += v[c][e];
+        }
+    }
+    const float mean = wave_sum(s) / (float)cols;
+    float q = 0.0f;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        if (lane + 64 * c < nchunk) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float d = v[c][e] - mean;
+                q += d * d;
+            }
+        }
+    }
+    const float rstd = rsqrtf(wave_sum(q) / (float)cols + eps);
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int ch = lane + 64 * c;
+        if (ch < nchunk) {
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int col = 8 * ch + e;
+                o[e] = (v[c][e] - mean) * rstd * w[col] + (bias ? bias[col] : 0.0f);
+            }
+            if (GATED) {
+                uint4 ur = ld16(u + row * ldu + 8 * ch);
+                uint32_t uw[4] = {ur.x, ur.y, ur.z, ur.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    o[2 * e] *= bf16_lo(uw[e]);
+                    o[2 * e + 1] *= bf16_hi(uw[e]);
+                }
+            }
+            uint2 lo = cvt4_u2(o[0], o[1], o[2], o[3]);
+            uint2 hi = cvt4_u2(o[4], o[5], o[6], o[7]);
+            uint4 outv = {lo.x, lo.y, hi.x, hi.y};
+            *reinterpret_cast<uint4 *>(y + row * ldy + 8 * ch) = outv;
+        }
+    }
+}
+
+hipError_t launch_layernorm_bf16(const void *x, const float *w, const float *b, void *y,
+                                 int64_t rows, int cols, float eps, hipStream_t st)
+{
+    if (rows <= 0) return hipSuccess;
+    dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    hipLaunchKernelGGL(layernorm_bf16_kernel<false>, grid, block, 0, st,
+                       (const uint16_t *)x, (int64_t)cols, (const uint16_t *)nullptr, (int64_t)0,
+                       w, b, (uint16_t *)y, (int64_t)cols, rows, cols, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_gated_layernorm_bf16(const void *a, int64_t lda, const void *u, int64_t ldu,
+                                       const float *w, const float *b, void *y, int64_t rows,
+                                       int cols, float eps, hipStream_t st)
+{
+    if (rows <= 0) return hipSuccess;
+    dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    hipLaunchKernelGGL(layernorm_bf16_kernel<true>, grid, block, 0, st, (const uint16_t *)a, lda,
+                       (const uint16_t *)u, ldu, w, b, (uint16_t *)y, (int64_t)cols, rows, cols,
+                       eps);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// GEMM  C[M][N] = epi(A[M][K] . W[N][K]^T)
+// Workgroup tile 128 x 128, 4 waves in 2 x 2, K steps of 64.  The waves compute
+// C^T blocks (W rows as the MFMA A operand, A rows as B) so that each lane ends
+// with four consecutive output columns of one row: 8-byte stores.
+// ---------------------------------------------------------------------------
+constexpr int GM = 128, GN = 128, GK = 64;
+
+template <int EPI>
+__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t *A, int64_t lda,
+                                                           const uint16_t *W, int64_t ldw,
+                                                           const float *bias, const uint16_t *R,
+                                                           int64_t ldr, uint16_t *C, int64_t ldc,
+                                                           int64_t M, int N, int K)
+{
+    __shared__ __align__(16) uint16_t sa[2][GM * GK];
+    __shared__ __align__(16) uint16_t sw[2][GN * GK];
+    const int ntn = N / GN;
+    const int64_t ntm = (M + GM - 1) / GM;
+    const int item = xcd_remap(blockIdx.x, (int)(ntm * ntn));
+    if (item < 0) return;
+    const int64_t m0 = (int64_t)(item / ntn) * GM;
+    const int n0 = (item % ntn) * GN;
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int l32 = lane & 31, hl = lane >> 5;
+    const int wm = wv & 1, wn = wv >> 1;  // wave's 64 x 64 sub-tile
+
+    // staging: thread loads rows (tid/8) + 32*i, chunk tid%8 of both tiles
+    const int sr = tid >> 3, sc = tid & 7;
+    uint4 ra[4], rw[4];
+    auto load = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t m = m0 + sr + 32 * i;
+            ra[i] = ld16_or_zero(A + m * lda + k0 + 8 * sc, m < M);
+            rw[i] = ld16(W + (int64_t)(n0 + sr + 32 * i) * ldw + k0 + 8 * sc);
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = sr + 32 * i;
+            *reinterpret_cast<uint4 *>(&sa[buf][r * GK + 8 * (sc ^ (r & 7))]) = ra[i];
+            *reinterpret_cast<uint4 *>(&sw[buf][r * GK + 8 * (sc ^ (r & 7))]) = rw[i];
+        }
+    };
+
+    floatx16 acc[2][2];  // [n block][m block] of C^T
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
+
+    const int nk = K / GK;
+    load(0);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        store(buf);
+        if (kt + 1 < nk) load((kt + 1) * GK);
+        __syncthreads();
+#pragma unroll
+        for (int kc = 0; kc < GK / 16; ++kc) {
+            bf16x8 wa[2], xb[2];
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                const int r = 64 * wn + 32 * nb + l32;
+                wa[nb] = as_bf16x8(*reinterpret_cast<const uint4 *>(
+                    &sw[buf][r * GK + 8 * ((2 * kc + hl) ^ (r & 7))]));
+            }
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                const int r = 64 * wm + 32 * mb + l32;
+                xb[mb] = as_bf16x8(*reinterpret_cast<const uint4 *>(
+                    &sa[buf][r * GK + 8 * ((2 * kc + hl) ^ (r & 7))]));
+            }
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = mfma32(wa[nb], xb[mb], acc[nb][mb]);
+        }
+    }
+
+    // epilogue: lane owns row m, registers hold columns n = 8*(r/4) + 4*hl + r%4
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        const int64_t m = m0 + 64 * wm + 32 * mb + l32;
+        if (m >= M) continue;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + 64 * wn + 32 * nb + 8 * g + 4 * hl;
+                float o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = acc[nb][mb][4 * g + e] + (bias ? bias[n + e] : 0.0f);
+                if (EPI == 0) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = o[e] * sigmoid_fast(o[e], -1.4426950408889634f);
+                } else {
+                    const uint2 rr = *reinterpret_cast<const uint2 *>(R + m * ldr + n);
+                    o[0] += bf16_lo(rr.x);
+                    o[1] += bf16_hi(rr.x);
+                    o[2] += bf16_lo(rr.y);
+                    o[3] += bf16_hi(rr.y);
+                }
+                *reinterpret_cast<uint2 *>(C + m * ldc + n) = cvt4_u2(o[0], o[1], o[2], o[3]);
+            }
+        }
+    }
+}
+
+hipError_t launch_gemm_bf16(const void *A, int64_t lda, const void *W, int64_t ldw,
+                            const float *bias, const void *R, int64_t ldr, void *C, int64_t ldc,
+                            int64_t M, int N, int K, int epi, hipStream_t st)
+{
+    if (M <= 0) return hipSuccess;
+    if (N % GN != 0 || K % GK != 0) return hipErrorInvalidValue;
+    const int64_t tiles = ((M + GM - 1) / GM) * (N / GN);
+    dim3 grid((unsigned)tiles), block(256);
+    if (epi == 0)
+        hipLaunchKernelGGL(gemm_bf16_kernel<0>, grid, block, 0, st, (const uint16_t *)A, lda,
+                           (const uint16_t *)W, ldw, bias, (const uint16_t *)R, ldr, (uint16_t *)C,
+                           ldc, M, N, K);
+    else
+        hipLaunchKernelGGL(gemm_bf16_kernel<1>, grid, block, 0, st, (const uint16_t *)A, lda,
+                           (const uint16_t *)W, ldw, bias, (const uint16_t *)R, ldr, (uint16_t *)C,
+                           ldc, M, N, K);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// attention truncation
+// ---------------------------------------------------------------------------
+// Per sequence: c = min(ctx, U) contextual tokens, history [c, U), kept history
+// [keep_from, U) with keep_from = c + max(0, (U - c) - tail), then the targets
+// [U, L).  The kept tokens after the contextual prefix are the contiguous run
+// [keep_from, L).
+__device__ __forceinline__ void trunc_dims(const int64_t *offsets, const int32_t *num_targets,
+                                           int b, int ctx, int tail, int &L, int &c,
+                                           int &keep_from)
+{
+    L = (int)(offsets[b + 1] - offsets[b]);
+    const int U = L - (num_targets ? num_targets[b] : 0);
+    c = imin(ctx, U);
+    const int hb = U - c;
+    keep_from = c + (hb > tail ? hb - tail : 0);
+}
+
+__global__ __launch_bounds__(1024) void truncate_offsets_kernel(int B, const int64_t *offsets,
+                                                                const int32_t *num_targets,
+                                                                int ctx, int tail,
+                                                                int64_t *new_offsets,
+                                                                int32_t *new_num_targets)
+{
+    __shared__ int64_t buf[2][1024];
+    __shared__ int64_t carry;
+    const int tid = threadIdx.x;
+    if (tid == 0) carry = 0;
+    __syncthreads();
+    for (int start = 0; start < B; start += 1024) {
+        const int b = start + tid;
+        int64_t v = 0;
+        if (b < B) {
+            int L, c, kf;
+            trunc_dims(offsets, num_targets, b, ctx, tail, L, c, kf);
+            v = c + (L - kf);
+            if (new_num_targets) new_num_targets[b] = num_targets ? num_targets[b] : 0;
+        }
+        int cur = 0;
+        buf[cur][tid] = v;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {
+            int64_t a = buf[cur][tid];
+            if (tid >= off) a += buf[cur][tid - off];
+            buf[cur ^ 1][tid] = a;
+            cur ^= 1;
+            __syncthreads();
+        }
+        const int64_t inc = buf[cur][tid];
+        const int64_t c0 = carry;
+        if (b < B) new_offsets[b] = c0 + inc - v;
+        __syncthreads();
+        if (tid == 1023) carry = c0 + inc;
+        __syncthreads();
+    }
+    if (tid == 0) new_offsets[B] = carry;
+}
+
+// one wave per kept row: index + 16-byte chunks of the row
+__global__ __launch_bounds__(256) void truncate_gather_kernel(
+    int B, const int64_t *offsets, const int32_t *num_targets, int ctx, int tail,
+    const int64_t *new_offsets, const uint8_t *x, int row_bytes, int64_t *gather_idx,
+    uint8_t *x_out, int64_t capacity)
+{
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int64_t total = new_offsets[B];
+    if (r >= total || r >= capacity) return;
+    int lo = 0, hi = B - 1;  // last b with new_offsets[b] <= r
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (new_offsets[mid] <= r) lo = mid;
+        else hi = mid - 1;
+    }
+    const int b = lo;
+    int L, c, kf;
+    trunc_dims(offsets, num_targets, b, ctx, tail, L, c, kf);
+    const int li = (int)(r - new_offsets[b]);
+    const int src = li < c ? li : kf + (li - c);
+    const int64_t srow = offsets[b] + src;
+    if (lane == 0 && gather_idx) gather_idx[r] = srow;
+    if (x_out) {
+        const uint8_t *s = x + srow * row_bytes;
+        uint8_t *d = x_out + r * row_bytes;
+        for (int e = 16 * lane; e < row_bytes; e += 16 * 64)
+            *reinterpret_cast<uint4 *>(d + e) = *reinterpret_cast<const uint4 *>(s + e);
+    }
+}
+
+hipError_t launch_truncate(int B, int64_t T, const int64_t *offsets, const int32_t *num_targets,
+                           int ctx, int tail, const void *x, int hidden, int elem_bytes,
+                           int64_t *new_offsets, int32_t *new_num_targets, int64_t *gather_idx,
+                           void *x_out, int64_t capacity, int32_t *, hipStream_t st)
+{
+    hipLaunchKernelGGL(truncate_offsets_kernel, dim3(1), dim3(1024), 0, st, B, offsets,
+                       num_targets, ctx, tail, new_offsets, new_num_targets);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t rows = capacity < T ? capacity : T;
+    if (rows <= 0 || (!gather_idx && !x_out)) return hipSuccess;
+    dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    hipLaunchKernelGGL(truncate_gather_kernel, grid, block, 0, st, B, offsets, num_targets, ctx,
+                       tail, (const int64_t *)new_offsets, (const uint8_t *)x,
+                       hidden * elem_bytes, gather_idx, (uint8_t *)x_out, capacity);
+    return hipGetLastError();
+}
+
+}  // namespace sla

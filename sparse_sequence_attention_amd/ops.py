@@ -1,0 +1,271 @@
+"""Thin torch-facing wrappers over the C ABI (argument marshalling only).
+
+Torch provides device memory and the current stream; every arithmetic step
+runs in the HIP kernels of libsla_mi355x.so.  Names follow the C entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _capi as C
+
+_DT = {torch.bfloat16: C.SLA_BF16, torch.float32: C.SLA_F32}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _head_tensor(name: str, t: torch.Tensor, T: int, H: int, dtype) -> int:
+    """Check a [T, H, d] view with unit inner stride; returns the token stride."""
+    if t.dim() != 3 or t.shape[0] != T or t.shape[1] != H:
+        raise ValueError(f"{name}: expected shape [T={T}, H={H}, d], got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.stride(2) != 1 or (H > 1 and t.stride(1) != t.shape[2]):
+        raise ValueError(f"{name}: heads must be packed ([T][H][d] with token stride >= H*d)")
+    return t.stride(0)
+
+
+def make_problem(dtype, offsets: torch.Tensor, num_targets: Optional[torch.Tensor], T: int, H: int,
+                 d_qk: int, d_v: int, k1: int, k2: int, contextual_len: int, max_seq_len: int,
+                 alpha: float = 1.0) -> C.SLAProblem:
+    if offsets.dtype != torch.int64 or offsets.dim() != 1:
+        raise TypeError("offsets must be a 1-D int64 tensor [B+1]")
+    if num_targets is not None and (num_targets.dtype != torch.int32 or
+                                    num_targets.numel() != offsets.numel() - 1):
+        raise TypeError("num_targets must be an int32 tensor [B]")
+    p = C.SLAProblem()
+    p.dtype = _DT[dtype] if not isinstance(dtype, int) else dtype
+    p.batch = offsets.numel() - 1
+    p.total_tokens = T
+    p.offsets = offsets.data_ptr()
+    p.num_targets = None if num_targets is None else num_targets.data_ptr()
+    p.num_heads, p.d_qk, p.d_v = H, d_qk, d_v
+    p.k1, p.k2, p.contextual_len = int(k1), int(k2), int(contextual_len)
+    p.max_seq_len = int(max_seq_len)
+    p.alpha = float(alpha)
+    return p
+
+
+def workspace_size(p: C.SLAProblem, op: int) -> int:
+    return int(C.load().sla_workspace_size(ctypes.byref(p), op))
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    if ws is not None and ws.numel() * ws.element_size() >= nbytes:
+        return ws
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def sla_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, offsets: torch.Tensor,
+            num_targets: Optional[torch.Tensor] = None, *, k1: int, k2: int,
+            contextual_len: int = 0, max_seq_len: int, alpha: float = 1.0,
+            out: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """O[T, H, d_v] = (1/N) (SiLU(alpha Q K^T) * M_SLA) V over jagged sequences."""
+    T, H, dqk = q.shape
+    dv = v.shape[2]
+    ldq = _head_tensor("q", q, T, H, q.dtype)
+    ldk = _head_tensor("k", k, T, H, q.dtype)
+    ldv = _head_tensor("v", v, T, H, q.dtype)
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
+    ldo = _head_tensor("out", out, T, H, q.dtype)
+    p = make_problem(q.dtype, offsets, num_targets, T, H, dqk, dv, k1, k2, contextual_len,
+                     max_seq_len, alpha)
+    nbytes = workspace_size(p, C.SLA_OP_FWD)
+    ws = _workspace(nbytes, q.device, workspace)
+    C.check(C.load().sla_fwd(ctypes.byref(p), _ptr(q), ldq, _ptr(k), ldk, _ptr(v), ldv, _ptr(out),
+                             ldo, _ptr(ws), ws.numel(), _stream(q.device)))
+    return out
+
+
+def sla_bwd(q, k, v, dout, offsets, num_targets=None, *, k1: int, k2: int,
+            contextual_len: int = 0, max_seq_len: int, alpha: float = 1.0, dq=None, dk=None,
+            dv=None, workspace: Optional[torch.Tensor] = None, stage: int = C.SLA_BWD_ALL):
+    """(dQ, dK, dV) of sla_fwd given dO (stage: see sla_bwd_stage in sla.h)."""
+    T, H, dqk = q.shape
+    dvd = v.shape[2]
+    ldq = _head_tensor("q", q, T, H, q.dtype)
+    ldk = _head_tensor("k", k, T, H, q.dtype)
+    ldv = _head_tensor("v", v, T, H, q.dtype)
+    lddo = _head_tensor("dout", dout, T, H, q.dtype)
+    dq = torch.empty((T, H, dqk), dtype=q.dtype, device=q.device) if dq is None else dq
+    dk = torch.empty((T, H, dqk), dtype=q.dtype, device=q.device) if dk is None else dk
+    dv = torch.empty((T, H, dvd), dtype=q.dtype, device=q.device) if dv is None else dv
+    lddq = _head_tensor("dq", dq, T, H, q.dtype)
+    lddk = _head_tensor("dk", dk, T, H, q.dtype)
+    lddv = _head_tensor("dv", dv, T, H, q.dtype)
+    p = make_problem(q.dtype, offsets, num_targets, T, H, dqk, dvd, k1, k2, contextual_len,
+                     max_seq_len, alpha)
+    nbytes = workspace_size(p, C.SLA_OP_BWD)
+    ws = _workspace(nbytes, q.device, workspace)
+    C.check(C.load().sla_bwd_stage(ctypes.byref(p), stage, _ptr(q), ldq, _ptr(k), ldk, _ptr(v),
+                                   ldv, _ptr(dout), lddo, _ptr(dq), lddq, _ptr(dk), lddk,
+                                   _ptr(dv), lddv, _ptr(ws), ws.numel(), _stream(q.device)))
+    return dq, dk, dv
+
+
+def sla_schedule(offsets, num_targets, *, op: int, heads: int, d: int, k1: int, k2: int,
+                 contextual_len: int = 0, total_tokens: int, dtype=torch.bfloat16) -> torch.Tensor:
+    """The kernels' work list as an int32 tensor [n, SLA_SCHED_RECORD_INTS] (on the device)."""
+    p = make_problem(dtype, offsets, num_targets, total_tokens, heads, d, d, k1, k2,
+                     contextual_len, 1)
+    lib = C.load()
+    cap = int(lib.sla_schedule_capacity(ctypes.byref(p), op))
+    if cap < 0:
+        C.check(C.SLA_ERR_INVALID)
+    rec = torch.zeros((max(cap, 1), C.SLA_SCHED_RECORD_INTS), dtype=torch.int32,
+                      device=offsets.device)
+    cnt = torch.zeros(1, dtype=torch.int32, device=offsets.device)
+    nbytes = workspace_size(p, C.SLA_OP_FWD)
+    ws = _workspace(nbytes, offsets.device, None)
+    C.check(lib.sla_schedule(ctypes.byref(p), op, _ptr(rec), cap, _ptr(cnt), _ptr(ws), ws.numel(),
+                             _stream(offsets.device)))
+    n = int(cnt.item())
+    return rec[:n]
+
+
+def sla_schedule_host(offsets, num_targets, *, op: int, heads: int, d: int, k1: int, k2: int,
+                      contextual_len: int = 0, dtype=torch.bfloat16):
+    """The work list computed on the host from host offsets (numpy int32 [n, 12])."""
+    import numpy as np
+    o = np.ascontiguousarray(offsets, dtype=np.int64)
+    t = None if num_targets is None else np.ascontiguousarray(num_targets, dtype=np.int32)
+    p = C.SLAProblem()
+    p.dtype = _DT[dtype]
+    p.batch = len(o) - 1
+    p.total_tokens = int(o[-1])
+    p.num_heads, p.d_qk, p.d_v = heads, d, d
+    p.k1, p.k2, p.contextual_len, p.max_seq_len, p.alpha = int(k1), int(k2), int(contextual_len), 1, 1.0
+    lib = C.load()
+    tp = None if t is None else t.ctypes.data_as(ctypes.c_void_p)
+    n = lib.sla_schedule_host(ctypes.byref(p), op, o.ctypes.data_as(ctypes.c_void_p), tp, None, 0)
+    if n < 0:
+        raise ValueError(lib.sla_last_error().decode())
+    rec = np.zeros((max(n, 1), C.SLA_SCHED_RECORD_INTS), dtype=np.int32)
+    lib.sla_schedule_host(ctypes.byref(p), op, o.ctypes.data_as(ctypes.c_void_p), tp,
+                          rec.ctypes.data_as(ctypes.c_void_p), n)
+    return rec[:n]
+
+
+def schedule_tile(op: int, which: int) -> int:
+    return int(C.load().sla_schedule_tile(op, which))
+
+
+def count_pairs_host(offsets, num_targets, k1: int, k2: int, contextual_len: int) -> int:
+    """Visible (row, key) pairs per head from host copies of offsets / num_targets."""
+    import numpy as np
+    o = np.ascontiguousarray(offsets, dtype=np.int64)
+    t = None if num_targets is None else np.ascontiguousarray(num_targets, dtype=np.int32)
+    n = C.load().sla_count_pairs_host(len(o) - 1, o.ctypes.data_as(ctypes.c_void_p),
+                                      None if t is None else t.ctypes.data_as(ctypes.c_void_p),
+                                      int(k1), int(k2), int(contextual_len))
+    if n < 0:
+        raise ValueError("invalid offsets / num_targets / window sizes")
+    return int(n)
+
+
+class SLAFunction(torch.autograd.Function):
+    """Autograd wrapper: forward sla_fwd, backward sla_bwd."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, offsets, num_targets, k1, k2, contextual_len, max_seq_len, alpha):
+        ctx.save_for_backward(q, k, v, offsets, num_targets)
+        ctx.args = (k1, k2, contextual_len, max_seq_len, alpha)
+        return sla_fwd(q, k, v, offsets, num_targets, k1=k1, k2=k2, contextual_len=contextual_len,
+                       max_seq_len=max_seq_len, alpha=alpha)
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, offsets, num_targets = ctx.saved_tensors
+        k1, k2, cl, n, alpha = ctx.args
+        dq, dk, dv = sla_bwd(q, k, v, dout.contiguous(), offsets, num_targets, k1=k1, k2=k2,
+                             contextual_len=cl, max_seq_len=n, alpha=alpha)
+        return dq, dk, dv, None, None, None, None, None, None, None
+
+
+def sla_attention(q, k, v, offsets, num_targets=None, *, k1, k2, contextual_len=0, max_seq_len,
+                  alpha=1.0):
+    return SLAFunction.apply(q, k, v, offsets, num_targets, k1, k2, contextual_len, max_seq_len,
+                             alpha)
+
+
+# ---------------------------------------------------------------------------
+# STU layer and truncation
+# ---------------------------------------------------------------------------
+def stu_layer_fwd(x: torch.Tensor, offsets: torch.Tensor, num_targets: Optional[torch.Tensor],
+                  ln1_w: torch.Tensor, w_uvqk: torch.Tensor, ln2_w: torch.Tensor,
+                  w_out: torch.Tensor, *, heads: int, d_qk: int, d_v: int, k1: int, k2: int,
+                  contextual_len: int, max_seq_len: int, alpha: float = 1.0,
+                  ln_eps: float = 1e-5, ln1_b=None, b_uvqk=None, ln2_b=None, b_out=None,
+                  out: Optional[torch.Tensor] = None, want_uvqk: bool = False,
+                  workspace: Optional[torch.Tensor] = None):
+    """One STU layer forward (bf16): LN -> UVQK GEMM + SiLU -> SLA -> LN(A)*U -> GEMM + x."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+        raise TypeError("x must be a contiguous bf16 [T, D] tensor")
+    T, D = x.shape
+    nw = 2 * heads * d_v + 2 * heads * d_qk
+    for name, w, shape in (("w_uvqk", w_uvqk, (nw, D)), ("w_out", w_out, (D, heads * d_v))):
+        if tuple(w.shape) != shape or w.dtype != torch.bfloat16 or not w.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous bf16 tensor of shape {shape}")
+    vecs = [ln1_w, ln1_b, b_uvqk, ln2_w, ln2_b, b_out]
+    for v_ in vecs:
+        if v_ is not None and (v_.dtype != torch.float32 or not v_.is_contiguous()):
+            raise TypeError("LayerNorm weights and biases must be contiguous float32 tensors")
+    d = C.STULayerDesc()
+    d.attn = make_problem(torch.bfloat16, offsets, num_targets, T, heads, d_qk, d_v, k1, k2,
+                          contextual_len, max_seq_len, alpha)
+    d.hidden = D
+    d.ln_eps = float(ln_eps)
+    lib = C.load()
+    nbytes = int(lib.stu_layer_workspace_size(ctypes.byref(d)))
+    ws = _workspace(nbytes, x.device, workspace)
+    out = torch.empty_like(x) if out is None else out
+    uvqk = torch.empty((T, nw), dtype=torch.bfloat16, device=x.device) if want_uvqk else None
+    C.check(lib.stu_layer_fwd(ctypes.byref(d), _ptr(x), _ptr(ln1_w), _ptr(ln1_b), _ptr(w_uvqk),
+                              _ptr(b_uvqk), _ptr(ln2_w), _ptr(ln2_b), _ptr(w_out), _ptr(b_out),
+                              _ptr(out), _ptr(uvqk), _ptr(ws), ws.numel(), _stream(x.device)))
+    return (out, uvqk) if want_uvqk else out
+
+
+def stu_truncate(x: Optional[torch.Tensor], offsets: torch.Tensor,
+                 num_targets: Optional[torch.Tensor], *, contextual_len: int, tail_len: int,
+                 capacity: Optional[int] = None, want_gather: bool = True):
+    """(x_out [capacity, D] or None, new_offsets [B+1], new_num_targets [B], gather_idx).
+
+    Rows past the new total (new_offsets[-1], on the device) are left unwritten."""
+    B = offsets.numel() - 1
+    T = int(x.shape[0]) if x is not None else None
+    if capacity is None:
+        if x is None:
+            raise ValueError("capacity is required without x")
+        capacity = T
+    total = T if T is not None else capacity
+    dev = offsets.device
+    new_offsets = torch.empty(B + 1, dtype=torch.int64, device=dev)
+    new_nt = torch.empty(max(B, 1), dtype=torch.int32, device=dev)
+    gidx = torch.empty(max(capacity, 1), dtype=torch.int64, device=dev) if want_gather else None
+    x_out = None
+    dtype_code, hidden = C.SLA_BF16, 0
+    if x is not None:
+        if x.dim() != 2 or not x.is_contiguous():
+            raise TypeError("x must be a contiguous [T, D] tensor")
+        dtype_code = _DT[x.dtype]
+        hidden = x.shape[1]
+        x_out = torch.empty((capacity, hidden), dtype=x.dtype, device=dev)
+    C.check(C.load().stu_truncate(B, total, _ptr(offsets), _ptr(num_targets), int(contextual_len),
+                                  int(tail_len), _ptr(x), hidden, dtype_code, _ptr(new_offsets),
+                                  _ptr(new_nt), _ptr(gidx), _ptr(x_out), int(capacity),
+                                  _stream(dev)))
+    return x_out, new_offsets, new_nt[:B], gidx

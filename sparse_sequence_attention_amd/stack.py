@@ -1,0 +1,63 @@
+"""STU stack forward driver: a loop over stu_layer_fwd with one stu_truncate
+call before the first truncated layer (ULTRA-HSTU paper, section 4.3: after
+N1 full-length layers keep the most recent UIH tokens for the remaining N2).
+
+The driver only sequences C-ABI calls.  It reads the truncated token count
+back once (one device-to-host copy of new_offsets[B]) to size the following
+layers' buffers.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import torch
+
+from . import ops
+from .config import STUConfig
+
+
+@dataclass
+class STULayerWeights:
+    ln1_w: torch.Tensor          # [D] fp32
+    w_uvqk: torch.Tensor         # [2*H*dv + 2*H*dqk, D] bf16
+    ln2_w: torch.Tensor          # [H*dv] fp32
+    w_out: torch.Tensor          # [D, H*dv] bf16
+    ln1_b: Optional[torch.Tensor] = None
+    b_uvqk: Optional[torch.Tensor] = None
+    ln2_b: Optional[torch.Tensor] = None
+    b_out: Optional[torch.Tensor] = None
+
+
+@dataclass
+class StackOutput:
+    x: torch.Tensor
+    offsets: torch.Tensor
+    num_targets: Optional[torch.Tensor]
+    gather_idx: Optional[torch.Tensor] = None   # source rows of the truncated layers
+    layer_tokens: List[int] = field(default_factory=list)
+
+
+def stu_stack_fwd(cfg: STUConfig, layers: List[STULayerWeights], x: torch.Tensor,
+                  offsets: torch.Tensor, num_targets: Optional[torch.Tensor]) -> StackOutput:
+    if len(layers) != cfg.attn_num_layers:
+        raise ValueError(f"{len(layers)} layer weights for {cfg.attn_num_layers} layers")
+    out = StackOutput(x=x, offsets=offsets, num_targets=num_targets)
+    cur, offs, tg = x, offsets, num_targets
+    for li, w in enumerate(layers):
+        if cfg.truncation_enabled and li == cfg.attn_truncation_split_layer:
+            xt, offs, tg, gidx = ops.stu_truncate(cur, offs, tg,
+                                                  contextual_len=cfg.contextual_seq_len,
+                                                  tail_len=cfg.attn_truncation_tail_len)
+            n = int(offs[-1].item())
+            cur = xt[:n]
+            out.gather_idx = gidx[:n]
+        out.layer_tokens.append(int(cur.shape[0]))
+        cur = ops.stu_layer_fwd(cur, offs, tg, w.ln1_w, w.w_uvqk, w.ln2_w, w.w_out,
+                                heads=cfg.num_heads, d_qk=cfg.attention_dim, d_v=cfg.hidden_dim,
+                                k1=cfg.kernel_k1, k2=cfg.kernel_k2,
+                                contextual_len=cfg.contextual_seq_len,
+                                max_seq_len=cfg.max_seq_len, alpha=cfg.alpha, ln_eps=cfg.ln_eps,
+                                ln1_b=w.ln1_b, b_uvqk=w.b_uvqk, ln2_b=w.ln2_b, b_out=w.b_out)
+    out.x, out.offsets, out.num_targets = cur, offs, tg
+    return out

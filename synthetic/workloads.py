@@ -126,6 +126,7 @@ class Workload:
     contextual_len: int = 0
     max_seq_len: int = 1
     alpha: float = 1.0
+    dtype: str = "bf16"          # storage type of q, k, v, dout
 
     @property
     def total_tokens(self) -> int:
@@ -173,7 +174,8 @@ def make_sla_workload(cfg: SLAConfig | str, seed: int = 0, *, lengths: Optional[
                     q=q, k=k, v=v, dout=dout,
                     k1=cfg.k1 if k1 is None else k1, k2=cfg.k2 if k2 is None else k2,
                     contextual_len=cfg.contextual_len if contextual_len is None else contextual_len,
-                    max_seq_len=cfg.max_seq_len if max_seq_len is None else max_seq_len)
+                    max_seq_len=cfg.max_seq_len if max_seq_len is None else max_seq_len,
+                    dtype=dt)
 
 
 # ----------------------------------------------------------------------------

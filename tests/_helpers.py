@@ -25,9 +25,41 @@ BF16_MEAN_TOL = 5e-3
 F32_MAX_TOL = 1e-5
 
 
+def bf16_storage_floor(ref):
+    """max |bf16(ref) - ref| / rms(ref): the error of storing the exact result in bf16."""
+    from synthetic import bf16_round_f32
+    ref = np.asarray(ref, dtype=np.float64)
+    return rel_errors(bf16_round_f32(ref.astype(np.float32)), ref)[0]
+
+
+def bf16_ulp(x):
+    """Spacing of bf16 numbers at |x| (8 significant bits)."""
+    ax = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(ax)) - 7)
+
+
 def assert_close_bf16(got, ref, what=""):
+    """bf16 tolerance: max|got-ref|/rms(ref) <= 2e-2 and mean <= 5e-3.
+
+    A bf16 output cannot be closer to the exact value than bf16 rounding of
+    that value.  When that rounding alone uses more than half of the 2e-2
+    budget (outputs with max|ref| > ~5 rms, e.g. one-key windows), each element
+    is allowed one bf16 ulp of its reference value on top of 2e-2 * rms."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
     mx, mn = rel_errors(got, ref)
-    assert mx <= BF16_MAX_TOL and mn <= BF16_MEAN_TOL, f"{what}: max {mx:.3e} mean {mn:.3e}"
+    floor = bf16_storage_floor(ref)
+    if floor <= 0.5 * BF16_MAX_TOL:
+        assert mx <= BF16_MAX_TOL and mn <= BF16_MEAN_TOL, \
+            f"{what}: max {mx:.3e} mean {mn:.3e} (storage floor {floor:.3e})"
+    else:
+        rms = float(np.sqrt(np.mean(ref * ref))) or 1.0
+        excess = (np.abs(got - ref) - bf16_ulp(ref)) / rms
+        ex = float(excess.max()) if excess.size else 0.0
+        print(f"  {what}: storage floor {floor:.3e} > {0.5 * BF16_MAX_TOL:.0e}: "
+              f"max excess over one bf16 ulp {ex:.3e}")
+        assert ex <= BF16_MAX_TOL and mn <= BF16_MEAN_TOL, \
+            f"{what}: max {mx:.3e} (excess {ex:.3e}) mean {mn:.3e} (storage floor {floor:.3e})"
     return mx, mn
 
 

@@ -1,0 +1,278 @@
+"""GPU parity of the SLA kernels against the fp64 oracle (through the C ABI).
+
+Tolerances: fp32 path max|gpu-ref|/rms(ref) <= 1e-5; bf16 path <= 2e-2 max and
+<= 5e-3 mean (both normalised by the reference RMS, per output tensor).
+Schedules and the skipped-pair invariants are bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_sequence_attention_amd as sla
+from sparse_sequence_attention_amd.config import FULL_CAUSAL_K1
+from synthetic import make_sla_workload
+from tests._helpers import assert_close_bf16, assert_close_f32, rel_errors
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _dev(w, dtype=None):
+    dt = dtype or (torch.bfloat16 if w.dtype == "bf16" else torch.float32)
+    t = lambda a: torch.from_numpy(a).to(DEV).to(dt)  # noqa: E731  (exact: values are bf16)
+    offs = torch.from_numpy(w.offsets).to(DEV)
+    tg = None if w.num_targets is None else torch.from_numpy(w.num_targets).to(DEV)
+    do = None if w.dout is None else t(w.dout)
+    return t(w.q), t(w.k), t(w.v), do, offs, tg
+
+
+def _kw(w):
+    return dict(k1=w.k1, k2=w.k2, contextual_len=w.contextual_len, max_seq_len=w.max_seq_len,
+                alpha=w.alpha)
+
+
+def _np(x):
+    return x.float().cpu().numpy().astype(np.float64)
+
+
+def _print_case(name, w):
+    print(f"[case] {name} seed={w.seed} B={w.batch} T={w.total_tokens} k1={w.k1} k2={w.k2} "
+          f"ctx={w.contextual_len} targets={w.num_targets is not None}", flush=True)
+
+
+# --------------------------------------------------------------------------
+# schedule: device records == host records (both pinned to the oracle on CPU)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(4))
+def test_device_schedule_matches_host(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 9))
+    lens = [int(x) for x in rng.integers(0, 3000, size=B)]
+    tg = [int(rng.integers(0, min(L, 300) + 1)) for L in lens] if seed % 2 else None
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    k1, k2, ctx = [(256, 64, 8), (1024, 128, 16), (5, 0, 0), (FULL_CAUSAL_K1, 0, 0)][seed]
+    print(f"[case] schedule seed={seed} lens={lens}", flush=True)
+    o_d = torch.from_numpy(offs).to(DEV)
+    t_d = None if tg is None else torch.tensor(tg, dtype=torch.int32, device=DEV)
+    for op in (sla.SLA_OP_FWD, sla.SLA_OP_BWD):
+        dev = sla.sla_schedule(o_d, t_d, op=op, heads=4, d=128, k1=k1, k2=k2, contextual_len=ctx,
+                               total_tokens=int(offs[-1])).cpu().numpy()
+        host = sla.sla_schedule_host(offs, tg, op=op, heads=4, d=128, k1=k1, k2=k2,
+                                     contextual_len=ctx)
+        assert np.array_equal(dev, host)
+
+
+# --------------------------------------------------------------------------
+# forward
+# --------------------------------------------------------------------------
+def test_fwd_f32_tiny_config():
+    """SLA forward, fp32: B=2 lengths {37, 64}, H=2, d=32, K1=8, K2=4, ctx=2."""
+    w = make_sla_workload("tiny_f32", seed=0)
+    _print_case("tiny_f32", w)
+    q, k, v, _, offs, tg = _dev(w)
+    o = sla.sla_fwd(q, k, v, offs, tg, **_kw(w))
+    torch.cuda.synchronize()
+    ref = oracle.sla_fwd(w.q, w.k, w.v, w.offsets, w.num_targets, w.k1, w.k2, w.contextual_len,
+                         w.max_seq_len)
+    assert_close_f32(_np(o), ref, "O")
+
+
+SMALL_CASES = [
+    # lengths, targets, k1, k2, ctx, d
+    ([37, 64], None, 8, 4, 2, 32),
+    ([1, 700, 129, 0, 256], None, 130, 64, 8, 128),
+    ([513, 64, 1000], [17, 64, 200], 100, 16, 8, 128),
+    ([300, 451], [1, 3], 1, 0, 0, 64),
+    ([400, 333], None, 0, 70, 0, 128),           # global prefix only
+    ([700, 260], None, FULL_CAUSAL_K1, 0, 0, 128),  # full causal
+    ([640, 200], [64, 0], 2, 128, 130, 128),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL_CASES)))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fwd_small(case, dtype):
+    lens, tg, k1, k2, ctx, d = SMALL_CASES[case]
+    w = make_sla_workload("jagged_2k", seed=10 + case, lengths=lens, num_targets=tg, heads=2, d=d,
+                          k1=k1, k2=k2, contextual_len=ctx, max_seq_len=max(1, max(lens)),
+                          dtype=dtype)
+    _print_case(f"fwd_small[{case}] {dtype}", w)
+    q, k, v, _, offs, tgd = _dev(w)
+    o = sla.sla_fwd(q, k, v, offs, tgd, **_kw(w))
+    torch.cuda.synchronize()
+    ref = oracle.sla_fwd(w.q, w.k, w.v, w.offsets, w.num_targets, w.k1, w.k2, w.contextual_len,
+                         w.max_seq_len)
+    (assert_close_bf16 if dtype == "bf16" else assert_close_f32)(_np(o), ref, "O")
+
+
+@pytest.mark.parametrize("case", range(len(SMALL_CASES)))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_small(case, dtype):
+    lens, tg, k1, k2, ctx, d = SMALL_CASES[case]
+    w = make_sla_workload("jagged_2k", seed=20 + case, lengths=lens, num_targets=tg, heads=2, d=d,
+                          k1=k1, k2=k2, contextual_len=ctx, max_seq_len=max(1, max(lens)),
+                          dtype=dtype, with_dout=True)
+    _print_case(f"bwd_small[{case}] {dtype}", w)
+    q, k, v, do, offs, tgd = _dev(w)
+    dq, dk, dv = sla.sla_bwd(q, k, v, do, offs, tgd, **_kw(w))
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.sla_bwd(w.q, w.k, w.v, w.dout, w.offsets, w.num_targets, w.k1, w.k2,
+                                w.contextual_len, w.max_seq_len)
+    chk = assert_close_bf16 if dtype == "bf16" else assert_close_f32
+    chk(_np(dq), rq, "dQ")
+    chk(_np(dk), rk, "dK")
+    chk(_np(dv), rv, "dV")
+
+
+def test_alpha_and_strided_views():
+    """alpha != 1 and Q/K/V as column blocks of one fused buffer."""
+    lens = [300, 77]
+    T, H, d = sum(lens), 2, 64
+    w = make_sla_workload("jagged_2k", seed=5, lengths=lens, heads=H, d=d, k1=50, k2=10,
+                          contextual_len=3, max_seq_len=300, with_dout=True)
+    w.alpha = 0.75
+    _print_case("strided", w)
+    fused = torch.zeros((T, 5 * H * d), dtype=torch.bfloat16, device=DEV)
+    for i, a in enumerate((w.q, w.k, w.v)):
+        fused[:, (1 + i) * H * d:(2 + i) * H * d] = torch.from_numpy(a.reshape(T, H * d)).to(DEV)
+    q = fused[:, H * d:2 * H * d].view(T, H, d)
+    k = fused[:, 2 * H * d:3 * H * d].view(T, H, d)
+    v = fused[:, 3 * H * d:4 * H * d].view(T, H, d)
+    offs = torch.from_numpy(w.offsets).to(DEV)
+    o = sla.sla_fwd(q, k, v, offs, None, **_kw(w))
+    do = torch.from_numpy(w.dout).to(DEV).bfloat16()
+    dbuf = torch.zeros((T, 4 * H * d), dtype=torch.bfloat16, device=DEV)
+    dq = dbuf[:, 0:H * d].view(T, H, d)
+    dk = dbuf[:, H * d:2 * H * d].view(T, H, d)
+    dv = dbuf[:, 3 * H * d:4 * H * d].view(T, H, d)
+    sla.sla_bwd(q, k, v, do, offs, None, dq=dq, dk=dk, dv=dv, **_kw(w))
+    torch.cuda.synchronize()
+    ref = oracle.sla_fwd(w.q, w.k, w.v, w.offsets, None, 50, 10, 3, 300, 0.75)
+    assert_close_bf16(_np(o), ref, "O")
+    rq, rk, rv = oracle.sla_bwd(w.q, w.k, w.v, w.dout, w.offsets, None, 50, 10, 3, 300, 0.75)
+    assert_close_bf16(_np(dq), rq, "dQ")
+    assert_close_bf16(_np(dk), rk, "dK")
+    assert_close_bf16(_np(dv), rv, "dV")
+    assert torch.all(dbuf[:, 2 * H * d:3 * H * d] == 0)   # the gap was not written
+
+
+# --------------------------------------------------------------------------
+# invariants on the GPU path
+# --------------------------------------------------------------------------
+def test_perturbing_invisible_keys_is_bitwise_neutral():
+    lens = [600]
+    w = make_sla_workload("jagged_2k", seed=3, lengths=lens, heads=2, d=128, k1=100, k2=16,
+                          contextual_len=0, max_seq_len=600)
+    q, k, v, _, offs, _ = _dev(w)
+    base = sla.sla_fwd(q, k, v, offs, None, **_kw(w)).clone()
+    # keys 200..399 are invisible to rows 0..199 (causal) and to rows >= 500 (window)
+    k2_, v2_ = k.clone(), v.clone()
+    k2_[200:400] += 3.0
+    v2_[200:400] -= 2.0
+    out = sla.sla_fwd(q, k2_, v2_, offs, None, **_kw(w))
+    torch.cuda.synchronize()
+    assert torch.equal(out[:200], base[:200])
+    assert torch.equal(out[500:], base[500:])
+    assert not torch.equal(out[200:500], base[200:500])
+
+
+def test_backward_is_bitwise_deterministic():
+    w = make_sla_workload("jagged_2k", seed=4, lengths=[2048, 1500, 700], heads=4, d=128,
+                          with_dout=True)
+    q, k, v, do, offs, tg = _dev(w)
+    a = [t.clone() for t in sla.sla_bwd(q, k, v, do, offs, tg, **_kw(w))]
+    b = sla.sla_bwd(q, k, v, do, offs, tg, **_kw(w))
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_batch_composition_does_not_change_results():
+    w = make_sla_workload("jagged_2k", seed=6, lengths=[900, 300, 1200], heads=2, d=128,
+                          num_targets=[10, 0, 64], with_dout=True)
+    q, k, v, do, offs, tg = _dev(w)
+    full = sla.sla_fwd(q, k, v, offs, tg, **_kw(w))
+    s0, s1 = 900, 1200
+    one = sla.sla_fwd(q[s0:s1].contiguous(), k[s0:s1].contiguous(), v[s0:s1].contiguous(),
+                      torch.tensor([0, 300], dtype=torch.int64, device=DEV),
+                      torch.tensor([0], dtype=torch.int32, device=DEV), **_kw(w))
+    torch.cuda.synchronize()
+    assert torch.equal(one, full[s0:s1])
+
+
+def test_empty_batch_and_empty_sequences():
+    w = make_sla_workload("jagged_2k", seed=7, lengths=[0, 5, 0, 130, 0], heads=2, d=64,
+                          with_dout=True)
+    q, k, v, do, offs, tg = _dev(w)
+    o = sla.sla_fwd(q, k, v, offs, tg, **_kw(w))
+    dq, dk, dv = sla.sla_bwd(q, k, v, do, offs, tg, **_kw(w))
+    torch.cuda.synchronize()
+    ref = oracle.sla_fwd(w.q, w.k, w.v, w.offsets, None, w.k1, w.k2, w.contextual_len,
+                         w.max_seq_len)
+    assert_close_bf16(_np(o), ref, "O")
+    z = torch.zeros((0, 2, 64), dtype=torch.bfloat16, device=DEV)
+    offs0 = torch.zeros(1, dtype=torch.int64, device=DEV)
+    e = sla.sla_fwd(z, z, z, offs0, None, k1=4, k2=0, max_seq_len=1)
+    assert e.shape == (0, 2, 64)
+
+
+# --------------------------------------------------------------------------
+# full-size workloads
+# --------------------------------------------------------------------------
+def test_jagged_2k_config_fwd_bwd():
+    """B=32 lengths U[512,2048], H=4, d=128, K1=256, K2=64, ctx=8: every output."""
+    w = make_sla_workload("jagged_2k", seed=0)
+    _print_case("jagged_2k", w)
+    q, k, v, do, offs, tg = _dev(w)
+    o = sla.sla_fwd(q, k, v, offs, tg, **_kw(w))
+    dq, dk, dv = sla.sla_bwd(q, k, v, do, offs, tg, **_kw(w))
+    torch.cuda.synchronize()
+    ref = oracle.sla_fwd(w.q, w.k, w.v, w.offsets, None, w.k1, w.k2, w.contextual_len,
+                         w.max_seq_len)
+    assert_close_bf16(_np(o), ref, "O")
+    rq, rk, rv = oracle.sla_bwd(w.q, w.k, w.v, w.dout, w.offsets, None, w.k1, w.k2,
+                                w.contextual_len, w.max_seq_len)
+    for name, g, r in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        mx, mn = assert_close_bf16(_np(g), r, name)
+        print(f"  {name}: max {mx:.3e} mean {mn:.3e}", flush=True)
+
+
+def _sample_rows(w, n, rng):
+    """Sampled tokens: first/last rows of sequences, tile edges and random rows."""
+    T = w.total_tokens
+    sel = np.zeros(T, np.uint8)
+    for b in range(w.batch):
+        s0, s1 = int(w.offsets[b]), int(w.offsets[b + 1])
+        for r in (s0, s0 + 1, s0 + 127, s0 + 128, s0 + 1023, s0 + 1024, s0 + 1151, s1 - 1,
+                  s1 - 2, s1 - 257):
+            if s0 <= r < s1:
+                sel[r] = 1
+    sel[rng.integers(0, T, size=n)] = 1
+    return sel
+
+
+@pytest.mark.parametrize("cfg", ["long_16k", "targets_16k"])
+def test_full_size_sampled(cfg):
+    """Production lengths in the bench's launch configuration, checked on sampled
+    rows (forward and dQ) and sampled keys (dK, dV) against the oracle."""
+    w = make_sla_workload(cfg, seed=0, with_dout=True)
+    _print_case(cfg, w)
+    q, k, v, do, offs, tg = _dev(w)
+    o = sla.sla_fwd(q, k, v, offs, tg, **_kw(w))
+    dq, dk, dv = sla.sla_bwd(q, k, v, do, offs, tg, **_kw(w))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    qs = _sample_rows(w, 96, rng)
+    ks = _sample_rows(w, 48, rng)
+    ref = oracle.sla_fwd(w.q, w.k, w.v, w.offsets, w.num_targets, w.k1, w.k2, w.contextual_len,
+                         w.max_seq_len, row_sel=qs)
+    sel = qs == 1
+    assert_close_bf16(_np(o)[sel], ref[sel], "O")
+    rq, rk, rv = oracle.sla_bwd(w.q, w.k, w.v, w.dout, w.offsets, w.num_targets, w.k1, w.k2,
+                                w.contextual_len, w.max_seq_len, q_sel=qs, k_sel=ks)
+    ksel = ks == 1
+    assert_close_bf16(_np(dq)[sel], rq[sel], "dQ")
+    assert_close_bf16(_np(dk)[ksel], rk[ksel], "dK")
+    assert_close_bf16(_np(dv)[ksel], rv[ksel], "dV")

@@ -1,0 +1,167 @@
+"""GPU parity of the STU layer, attention truncation and the STU stack against
+the fp64 oracle in its storage-matched mode (bf16 rounding at the points the
+GPU stores bf16).  Truncation indices are bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_sequence_attention_amd as sla
+from sparse_sequence_attention_amd.config import STUConfig
+from sparse_sequence_attention_amd.stack import STULayerWeights, stu_stack_fwd
+from synthetic import make_stack_workload
+from tests._helpers import assert_close_bf16, rel_errors
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _b(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV).bfloat16()
+
+
+def _f(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def _np(x):
+    return x.float().cpu().numpy().astype(np.float64)
+
+
+def _layer_weights(sw, li, with_bias=False, rng=None):
+    w = STULayerWeights(ln1_w=_f(sw.ln1_w[li]), w_uvqk=_b(sw.w_uvqk[li]), ln2_w=_f(sw.ln2_w[li]),
+                        w_out=_b(sw.w_out[li]))
+    host = dict(ln1_w=sw.ln1_w[li], w_uvqk=sw.w_uvqk[li], ln2_w=sw.ln2_w[li], w_out=sw.w_out[li])
+    if with_bias:
+        D, NU = sw.hidden, sw.heads * sw.d
+        nw = 4 * NU
+        hb = dict(ln1_b=0.1 * rng.standard_normal(D), b_uvqk=0.1 * rng.standard_normal(nw),
+                  ln2_b=0.1 * rng.standard_normal(NU), b_out=0.1 * rng.standard_normal(D))
+        hb = {k: v.astype(np.float32) for k, v in hb.items()}
+        w.ln1_b, w.b_uvqk, w.ln2_b, w.b_out = (_f(hb[k]) for k in ("ln1_b", "b_uvqk", "ln2_b",
+                                                                    "b_out"))
+        host.update(hb)
+    return w, host
+
+
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_stu_layer_matches_oracle(with_bias):
+    sw = make_stack_workload(seed=1, lengths=[700, 129, 1000, 64], layers=1, num_targets=16,
+                             contextual_len=8, k1=128, k2=32)
+    print(f"[case] stu layer bias={with_bias} T={int(sw.offsets[-1])}", flush=True)
+    rng = np.random.default_rng(5)
+    w, host = _layer_weights(sw, 0, with_bias, rng)
+    x = _b(sw.x)
+    offs = torch.from_numpy(sw.offsets).to(DEV)
+    tg = torch.from_numpy(sw.num_targets).to(DEV)
+    out, uvqk = sla.stu_layer_fwd(x, offs, tg, w.ln1_w, w.w_uvqk, w.ln2_w, w.w_out,
+                                  heads=sw.heads, d_qk=sw.d, d_v=sw.d, k1=sw.k1, k2=sw.k2,
+                                  contextual_len=sw.contextual_len, max_seq_len=sw.max_seq_len,
+                                  ln1_b=w.ln1_b, b_uvqk=w.b_uvqk, ln2_b=w.ln2_b, b_out=w.b_out,
+                                  want_uvqk=True)
+    torch.cuda.synchronize()
+    ref, ruvqk = oracle.stu_layer_fwd(sw.x, sw.offsets, sw.num_targets, host["ln1_w"],
+                                      host["w_uvqk"], host["ln2_w"], host["w_out"],
+                                      heads=sw.heads, dqk=sw.d, dv=sw.d, k1=sw.k1, k2=sw.k2,
+                                      ctx=sw.contextual_len, N=sw.max_seq_len,
+                                      ln1_b=host.get("ln1_b"), b_uvqk=host.get("b_uvqk"),
+                                      ln2_b=host.get("ln2_b"), b_out=host.get("b_out"),
+                                      store_bf16=True, want_uvqk=True)
+    assert_close_bf16(_np(uvqk), ruvqk, "UVQK")
+    mx, mn = assert_close_bf16(_np(out), ref, "out")
+    print(f"  out: max {mx:.3e} mean {mn:.3e}")
+
+
+def test_stu_zero_output_weight_returns_input():
+    sw = make_stack_workload(seed=2, lengths=[300, 200], layers=1)
+    w, _ = _layer_weights(sw, 0)
+    x = _b(sw.x)
+    offs = torch.from_numpy(sw.offsets).to(DEV)
+    out = sla.stu_layer_fwd(x, offs, None, w.ln1_w, w.w_uvqk, w.ln2_w,
+                            torch.zeros_like(w.w_out), heads=sw.heads, d_qk=sw.d, d_v=sw.d,
+                            k1=sw.k1, k2=sw.k2, contextual_len=sw.contextual_len,
+                            max_seq_len=sw.max_seq_len)
+    torch.cuda.synchronize()
+    assert torch.equal(out, x)
+
+
+def test_truncate_matches_oracle_bitwise():
+    rng = np.random.default_rng(3)
+    lens = [int(x) for x in rng.integers(0, 3000, size=9)] + [0, 5, 2000]
+    tg = [int(rng.integers(0, min(L, 100) + 1)) for L in lens]
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T = int(offs[-1])
+    x = rng.standard_normal((T, 256)).astype(np.float32)
+    xd = _b(x)
+    o_d = torch.from_numpy(offs).to(DEV)
+    t_d = torch.tensor(tg, dtype=torch.int32, device=DEV)
+    xo, no, nt, gi = sla.stu_truncate(xd, o_d, t_d, contextual_len=16, tail_len=1024)
+    torch.cuda.synchronize()
+    rno, rgi = oracle.truncate(offs, tg, 16, 1024)
+    n = int(rno[-1])
+    assert np.array_equal(no.cpu().numpy(), rno)
+    assert np.array_equal(gi[:n].cpu().numpy(), rgi)
+    assert np.array_equal(nt.cpu().numpy(), np.asarray(tg, np.int32))
+    assert torch.equal(xo[:n], xd[torch.from_numpy(rgi).to(DEV)])
+
+
+def _run_stack(sw, cfg):
+    layers = [_layer_weights(sw, li)[0] for li in range(sw.layers)]
+    x = _b(sw.x)
+    offs = torch.from_numpy(sw.offsets).to(DEV)
+    tg = torch.from_numpy(sw.num_targets).to(DEV)
+    res = stu_stack_fwd(cfg, layers, x, offs, tg)
+    torch.cuda.synchronize()
+    return res
+
+
+def _oracle_stack(sw, cfg):
+    x, offs, tg = sw.x.astype(np.float64), sw.offsets, sw.num_targets
+    gidx = None
+    for li in range(sw.layers):
+        if cfg.layer_is_truncated(li) and li == cfg.attn_truncation_split_layer:
+            offs, gidx = oracle.truncate(offs, tg, cfg.contextual_seq_len,
+                                         cfg.attn_truncation_tail_len)
+            x = x[gidx]
+        x = oracle.stu_layer_fwd(x, offs, tg, sw.ln1_w[li], sw.w_uvqk[li], sw.ln2_w[li],
+                                 sw.w_out[li], heads=sw.heads, dqk=sw.d, dv=sw.d,
+                                 k1=cfg.kernel_k1, k2=cfg.kernel_k2, ctx=cfg.contextual_seq_len,
+                                 N=cfg.max_seq_len, store_bf16=True)
+    return x, offs, gidx
+
+
+def _stack_cfg(sw):
+    return STUConfig(embedding_dim=sw.hidden, num_heads=sw.heads, hidden_dim=sw.d,
+                     attention_dim=sw.d, sla_k1=sw.k1, sla_k2=sw.k2,
+                     contextual_seq_len=sw.contextual_len, attn_num_layers=sw.layers,
+                     attn_truncation_split_layer=sw.split_layer,
+                     attn_truncation_tail_len=sw.tail_len, max_seq_len=sw.max_seq_len)
+
+
+def test_stack_small_with_truncation():
+    sw = make_stack_workload(seed=4, batch=4, min_len=512, max_len=1024, layers=4, split_layer=2,
+                             tail_len=256, k1=128, k2=32, contextual_len=16, num_targets=32)
+    cfg = _stack_cfg(sw)
+    print(f"[case] stack 4 layers T={int(sw.offsets[-1])}", flush=True)
+    res = _run_stack(sw, cfg)
+    ref, roffs, rgidx = _oracle_stack(sw, cfg)
+    assert np.array_equal(res.offsets.cpu().numpy(), roffs)
+    assert np.array_equal(res.gather_idx.cpu().numpy(), rgidx)
+    mx, mn = assert_close_bf16(_np(res.x), ref, "stack out")
+    print(f"  stack out: max {mx:.3e} mean {mn:.3e}  layer tokens {res.layer_tokens}")
+
+
+def test_stack_18_layers_full_config():
+    """18 layers, hidden 512, H=4, d=128, K1=512, K2=64, ctx 16, 64 targets, B=8,
+    L U[2048,4096], truncation before layer 9 to 16 + 1024 + 64 tokens."""
+    sw = make_stack_workload(seed=0)
+    cfg = _stack_cfg(sw)
+    print(f"[case] stack 18 layers T={int(sw.offsets[-1])}", flush=True)
+    res = _run_stack(sw, cfg)
+    ref, roffs, rgidx = _oracle_stack(sw, cfg)
+    assert np.array_equal(res.offsets.cpu().numpy(), roffs)
+    assert np.array_equal(res.gather_idx.cpu().numpy(), rgidx)
+    assert res.layer_tokens[:9] == [int(sw.offsets[-1])] * 9
+    assert res.layer_tokens[9:] == [8 * (16 + 1024 + 64)] * 9
+    mx, mn = assert_close_bf16(_np(res.x), ref, "stack out")
+    print(f"  stack out: max {mx:.3e} mean {mn:.3e}")
