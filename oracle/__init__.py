@@ -190,9 +190,17 @@ def stu_layer_fwd(x, offsets, num_targets, ln1_w, w_uvqk, ln2_w, w_out, *, heads
             for a in (ln1_w, ln1_b, w_uvqk, b_uvqk, ln2_w, ln2_b, w_out, b_out)]
     _load().oracle_stu_layer_fwd(len(offs) - 1, _ptr(offs), _ptr(tg), D, heads, dqk, dv, k1,
                                  k2, ctx, float(N), float(alpha), float(eps), _ptr(x),
-                                 *[_ptr(a) for a in keep], int(bool(store_bf16)), _ptr(out),
+                                 *[_ptr(a) for a in keep], _store_mask(store_bf16), _ptr(out),
                                  _ptr(uvqk))
     return (out, uvqk) if want_uvqk else out
+
+
+def _store_mask(store_bf16) -> int:
+    """True -> 3 (every storage point bf16); an int is passed through as the mask
+    (1 = branch tensors n, U/V/Q/K, A, y; 2 = layer output)."""
+    if isinstance(store_bf16, bool) or store_bf16 is None:
+        return 3 if store_bf16 else 0
+    return int(store_bf16)
 
 
 def truncate(offsets, num_targets, ctx, tail_len):

@@ -338,7 +338,9 @@ static void linear(int64_t rows, int64_t nin, int64_t nout, const double *x, con
  *   y    = LN(A; ln2_w, ln2_b) (.) U          (LN over the whole H*dv row)
  *   out  = y W2^T (+ b2) + x
  * x, out: [T][D]; W1: [2*H*dv + 2*H*dqk][D]; W2: [D][H*dv].
- * store_bf16 != 0 rounds n, U/V/Q/K, A, y and out to bfloat16.
+ * store_bf16 is a bit mask of storage points rounded to bfloat16:
+ *   1 = the branch tensors n, U/V/Q/K, A, y;   2 = the layer output (residual
+ *   stream).  3 rounds all five points.
  * uvqk_out (nullable): [T][2*H*dv + 2*H*dqk] after SiLU (and rounding). */
 EXPORT void oracle_stu_layer_fwd(int B, const int64_t *offsets, const int32_t *num_targets,
                                  int D, int H, int dqk, int dv, int64_t k1, int64_t k2,
@@ -356,11 +358,12 @@ EXPORT void oracle_stu_layer_fwd(int B, const int64_t *offsets, const int32_t *n
     double *vv = malloc(sizeof(double) * T * NU), *uu = malloc(sizeof(double) * T * NU);
     double *a = malloc(sizeof(double) * T * NU), *y = malloc(sizeof(double) * T * NU);
 
+    const int rb = store_bf16 & 1, ro = store_bf16 & 2;
     oracle_layernorm(T, D, x, ln1_w, ln1_b, eps, n);
-    if (store_bf16) round_all(n, T * D);
+    if (rb) round_all(n, T * D);
     linear(T, D, NW, n, w1, b1, z);
     for (int64_t i = 0; i < T * NW; ++i) z[i] = silu(z[i]);
-    if (store_bf16) round_all(z, T * NW);
+    if (rb) round_all(z, T * NW);
     if (uvqk_out) memcpy(uvqk_out, z, sizeof(double) * T * NW);
     for (int64_t t = 0; t < T; ++t) {
         const double *zr = z + t * NW;
@@ -371,13 +374,13 @@ EXPORT void oracle_stu_layer_fwd(int B, const int64_t *offsets, const int32_t *n
     }
     oracle_sla_fwd(B, offsets, num_targets, H, dqk, dv, k1, k2, ctx, N, alpha, qq, kk, vv, a,
                    NULL);
-    if (store_bf16) round_all(a, T * NU);
+    if (rb) round_all(a, T * NU);
     oracle_layernorm(T, NU, a, ln2_w, ln2_b, eps, y);
     for (int64_t i = 0; i < T * NU; ++i) y[i] *= uu[i];
-    if (store_bf16) round_all(y, T * NU);
+    if (rb) round_all(y, T * NU);
     linear(T, NU, D, y, w2, b2, out);
     for (int64_t i = 0; i < T * D; ++i) out[i] += x[i];
-    if (store_bf16) round_all(out, T * D);
+    if (ro) round_all(out, T * D);
 
     free(n); free(z); free(qq); free(kk); free(vv); free(uu); free(a); free(y);
 }

@@ -109,6 +109,9 @@ __global__ __launch_bounds__(256, 1) void sla_bwd_dkdv_bf16_kernel(AttnParams p)
     const float nal2e = p.neg_alpha_log2e, alpha = p.alpha;
     const float gscale = *p.grad_scale;
     const bool key_tile_full = (it.c1 - it.c0 == BN);
+    // g = dO.v enters dS only: carry the gradient scale in the stationary V
+#pragma unroll
+    for (int c = 0; c < NC; ++c) vb[c] = scale_bf16x8(vb[c], gscale);
     for (int s = 0; s < nsteps; ++s) {
         const int buf = s & 1;
         const int m0 = m0n, m1 = m1n;
@@ -153,10 +156,11 @@ __global__ __launch_bounds__(256, 1) void sla_bwd_dkdv_bf16_kernel(AttnParams p)
                         g = 0.0f;
                     }
                 }
-                const float sg = sigmoid_fast(sv, nal2e);
-                const float a = sv * sg;                        // SiLU(alpha s) / alpha
+                float e;
+                const float sg = sigmoid_e(sv, nal2e, e);
+                const float a = sv * sg;                         // SiLU(alpha s) / alpha
                 sacc[qb2][r] = a;
-                pacc[qb2][r] = g * gscale * (sg + alpha * a * (1.0f - sg));  // G g SiLU'(t)
+                pacc[qb2][r] = g * (sg * (1.0f + alpha * a * e));  // G g SiLU'(t)
             }
         }
 
@@ -307,6 +311,8 @@ __global__ __launch_bounds__(256, 1) void sla_bwd_dq_bf16_kernel(AttnParams p)
     }
     const float nal2e = p.neg_alpha_log2e, alpha = p.alpha;
     const float gscale = *p.grad_scale;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) gb[c] = scale_bf16x8(gb[c], gscale);
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1;
         const int c0 = c_next;
@@ -349,8 +355,9 @@ __global__ __launch_bounds__(256, 1) void sla_bwd_dq_bf16_kernel(AttnParams p)
                         g = 0.0f;
                     }
                 }
-                const float sg = sigmoid_fast(s, nal2e);
-                pacc[kb2][r] = g * gscale * (sg + alpha * s * sg * (1.0f - sg));
+                float e;
+                const float sg = sigmoid_e(s, nal2e, e);
+                pacc[kb2][r] = g * (sg * (1.0f + alpha * s * sg * e));
             }
         }
 

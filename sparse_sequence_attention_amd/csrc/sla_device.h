@@ -114,6 +114,27 @@ __device__ __forceinline__ float sigmoid_fast(float s, float neg_alpha_log2e)
     return __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// sigma and e = exp(-alpha s); 1 - sigma = e * sigma without cancellation.
+__device__ __forceinline__ float sigmoid_e(float s, float neg_alpha_log2e, float &e)
+{
+    e = __builtin_amdgcn_exp2f(s * neg_alpha_log2e);
+    return __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Multiply 8 bf16 values by a power of two (exact unless out of range).
+__device__ __forceinline__ bf16x8 scale_bf16x8(const bf16x8 &x, float sc)
+{
+    uint4 u = as_u4(x);
+    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16_lo(w[i]) * sc;
+        f[2 * i + 1] = bf16_hi(w[i]) * sc;
+    }
+    return cvt8(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
+}
+
 // ---------------------------------------------------------------------------
 // Memory helpers
 // ---------------------------------------------------------------------------

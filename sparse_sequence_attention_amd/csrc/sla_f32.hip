@@ -24,7 +24,15 @@ __device__ __forceinline__ float quad_sum(float x)
 }
 
 __device__ __forceinline__ float silu_f32(float t) { return t / (1.0f + expf(-t)); }
-__device__ __forceinline__ float sigmoid_f32(float t) { return 1.0f / (1.0f + expf(-t)); }
+
+// SiLU'(t) = sigma (1 + t (1 - sigma)) with 1 - sigma = e sigma, e = exp(-t), so
+// that no cancellation occurs when sigma is close to 1.
+__device__ __forceinline__ float dsilu_f32(float t)
+{
+    const float e = expf(-t);
+    const float sg = 1.0f / (1.0f + e);
+    return sg * (1.0f + t * (e * sg));
+}
 
 // cooperative copy of rows [r0, r0+nrows) (zero past `limit`) of a [T][ld]
 // fp32 tensor into a dense [nrows][D] LDS tile
@@ -73,6 +81,9 @@ __global__ __launch_bounds__(FWD_BM *F32_TPR) void sla_fwd_f32_kernel(AttnParams
         stage_rows_f32<D>(sk, kg, p.ldk, c0, BN, sd.L);
         stage_rows_f32<D>(sv, vg, p.ldv, c0, BN, sd.L);
         __syncthreads();
+        float part[DQ];  // per-tile partial sums keep the rounding error growth short
+#pragma unroll
+        for (int c = 0; c < DQ; ++c) part[c] = 0.0f;
         for (int jj = 0; jj < BN; ++jj) {
             float s = 0.0f;
 #pragma unroll
@@ -81,8 +92,10 @@ __global__ __launch_bounds__(FWD_BM *F32_TPR) void sla_fwd_f32_kernel(AttnParams
             const bool vis = i < r1 && c0 + jj < sd.L && visible(i, c0 + jj, sd.U, p.k1, p.k2e);
             const float a = vis ? silu_f32(p.alpha * s) : 0.0f;
 #pragma unroll
-            for (int c = 0; c < DQ; ++c) acc[c] += a * sv[jj * D + qt * DQ + c];
+            for (int c = 0; c < DQ; ++c) part[c] += a * sv[jj * D + qt * DQ + c];
         }
+#pragma unroll
+        for (int c = 0; c < DQ; ++c) acc[c] += part[c];
     }
     if (i < r1) {
         float *o = reinterpret_cast<float *>(p.o) + (sd.base + i) * p.ldo + h * D + qt * DQ;
@@ -126,6 +139,9 @@ __global__ __launch_bounds__(FWD_BM *F32_TPR) void sla_bwd_dq_f32_kernel(AttnPar
         stage_rows_f32<D>(sk, kg, p.ldk, c0, BN, sd.L);
         stage_rows_f32<D>(sv, vg, p.ldv, c0, BN, sd.L);
         __syncthreads();
+        float part[DQ];
+#pragma unroll
+        for (int c = 0; c < DQ; ++c) part[c] = 0.0f;
         for (int jj = 0; jj < BN; ++jj) {
             float s = 0.0f, g = 0.0f;
 #pragma unroll
@@ -136,11 +152,12 @@ __global__ __launch_bounds__(FWD_BM *F32_TPR) void sla_bwd_dq_f32_kernel(AttnPar
             s = quad_sum(s);
             g = quad_sum(g);
             const bool vis = i < r1 && c0 + jj < sd.L && visible(i, c0 + jj, sd.U, p.k1, p.k2e);
-            const float tt = p.alpha * s, sg = sigmoid_f32(tt);
-            const float ds = vis ? g * sg * (1.0f + tt * (1.0f - sg)) : 0.0f;
+            const float ds = vis ? g * dsilu_f32(p.alpha * s) : 0.0f;
 #pragma unroll
-            for (int c = 0; c < DQ; ++c) acc[c] += ds * sk[jj * D + qt * DQ + c];
+            for (int c = 0; c < DQ; ++c) part[c] += ds * sk[jj * D + qt * DQ + c];
         }
+#pragma unroll
+        for (int c = 0; c < DQ; ++c) acc[c] += part[c];
     }
     if (i < r1) {
         float *o = reinterpret_cast<float *>(p.dq) + (sd.base + i) * p.lddq + h * D + qt * DQ;
@@ -201,6 +218,9 @@ __global__ __launch_bounds__(BWD_BN *F32_TPR) void sla_bwd_dkdv_f32_kernel(AttnP
         stage_rows_f32<D>(sq, qg, p.ldq, m0, BM, m1);
         stage_rows_f32<D>(sg_, gg, p.lddo, m0, BM, m1);
         __syncthreads();
+        float pk[DQ], pv[DQ];
+#pragma unroll
+        for (int c = 0; c < DQ; ++c) pk[c] = pv[c] = 0.0f;
         for (int ii = 0; ii < BM; ++ii) {
             float sv = 0.0f, g = 0.0f;
 #pragma unroll
@@ -212,14 +232,19 @@ __global__ __launch_bounds__(BWD_BN *F32_TPR) void sla_bwd_dkdv_f32_kernel(AttnP
             g = quad_sum(g);
             const int i = m0 + ii;
             const bool vis = jok && i < m1 && visible(i, j, sd.U, p.k1, p.k2e);
-            const float tt = p.alpha * sv, sgm = sigmoid_f32(tt);
-            const float a = vis ? sv * sgm : 0.0f;  // SiLU(alpha s) / alpha
-            const float ds = vis ? g * sgm * (1.0f + tt * (1.0f - sgm)) : 0.0f;
+            const float tt = p.alpha * sv;
+            const float a = vis ? sv / (1.0f + expf(-tt)) : 0.0f;  // SiLU(alpha s) / alpha
+            const float ds = vis ? g * dsilu_f32(tt) : 0.0f;
 #pragma unroll
             for (int c = 0; c < DQ; ++c) {
-                dv[c] += a * sg_[ii * D + qt * DQ + c];
-                dk[c] += ds * sq[ii * D + qt * DQ + c];
+                pv[c] += a * sg_[ii * D + qt * DQ + c];
+                pk[c] += ds * sq[ii * D + qt * DQ + c];
             }
+        }
+#pragma unroll
+        for (int c = 0; c < DQ; ++c) {
+            dk[c] += pk[c];
+            dv[c] += pv[c];
         }
     }
     if (it.nchunk == 1) {

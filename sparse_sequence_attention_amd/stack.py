@@ -36,10 +36,13 @@ class StackOutput:
     num_targets: Optional[torch.Tensor]
     gather_idx: Optional[torch.Tensor] = None   # source rows of the truncated layers
     layer_tokens: List[int] = field(default_factory=list)
+    layer_inputs: List[torch.Tensor] = field(default_factory=list)   # with keep_layers
+    layer_outputs: List[torch.Tensor] = field(default_factory=list)
 
 
 def stu_stack_fwd(cfg: STUConfig, layers: List[STULayerWeights], x: torch.Tensor,
-                  offsets: torch.Tensor, num_targets: Optional[torch.Tensor]) -> StackOutput:
+                  offsets: torch.Tensor, num_targets: Optional[torch.Tensor],
+                  keep_layers: bool = False) -> StackOutput:
     if len(layers) != cfg.attn_num_layers:
         raise ValueError(f"{len(layers)} layer weights for {cfg.attn_num_layers} layers")
     out = StackOutput(x=x, offsets=offsets, num_targets=num_targets)
@@ -53,11 +56,15 @@ def stu_stack_fwd(cfg: STUConfig, layers: List[STULayerWeights], x: torch.Tensor
             cur = xt[:n]
             out.gather_idx = gidx[:n]
         out.layer_tokens.append(int(cur.shape[0]))
+        if keep_layers:
+            out.layer_inputs.append(cur)
         cur = ops.stu_layer_fwd(cur, offs, tg, w.ln1_w, w.w_uvqk, w.ln2_w, w.w_out,
                                 heads=cfg.num_heads, d_qk=cfg.attention_dim, d_v=cfg.hidden_dim,
                                 k1=cfg.kernel_k1, k2=cfg.kernel_k2,
                                 contextual_len=cfg.contextual_seq_len,
                                 max_seq_len=cfg.max_seq_len, alpha=cfg.alpha, ln_eps=cfg.ln_eps,
                                 ln1_b=w.ln1_b, b_uvqk=w.b_uvqk, ln2_b=w.ln2_b, b_out=w.b_out)
+        if keep_layers:
+            out.layer_outputs.append(cur)
     out.x, out.offsets, out.num_targets = cur, offs, tg
     return out

@@ -38,26 +38,29 @@ def bf16_ulp(x):
     return np.exp2(np.floor(np.log2(ax)) - 7)
 
 
-def assert_close_bf16(got, ref, what=""):
+def assert_close_bf16(got, ref, what="", ref_rounded=False):
     """bf16 tolerance: max|got-ref|/rms(ref) <= 2e-2 and mean <= 5e-3.
 
     A bf16 output cannot be closer to the exact value than bf16 rounding of
     that value.  When that rounding alone uses more than half of the 2e-2
     budget (outputs with max|ref| > ~5 rms, e.g. one-key windows), each element
-    is allowed one bf16 ulp of its reference value on top of 2e-2 * rms."""
+    is allowed one bf16 ulp of its reference value on top of 2e-2 * rms.  The
+    same one-ulp allowance applies when the reference is itself rounded to
+    bf16 (the oracle's storage-matched mode): near a rounding boundary the fp32
+    and fp64 values round to neighbouring bf16 numbers."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     mx, mn = rel_errors(got, ref)
     floor = bf16_storage_floor(ref)
-    if floor <= 0.5 * BF16_MAX_TOL:
+    if floor <= 0.5 * BF16_MAX_TOL and not ref_rounded:
         assert mx <= BF16_MAX_TOL and mn <= BF16_MEAN_TOL, \
             f"{what}: max {mx:.3e} mean {mn:.3e} (storage floor {floor:.3e})"
     else:
         rms = float(np.sqrt(np.mean(ref * ref))) or 1.0
         excess = (np.abs(got - ref) - bf16_ulp(ref)) / rms
         ex = float(excess.max()) if excess.size else 0.0
-        print(f"  {what}: storage floor {floor:.3e} > {0.5 * BF16_MAX_TOL:.0e}: "
-              f"max excess over one bf16 ulp {ex:.3e}")
+        print(f"  {what}: {'rounded reference' if ref_rounded else 'storage floor'} "
+              f"{floor:.3e}: max {mx:.3e}, max excess over one bf16 ulp {ex:.3e}")
         assert ex <= BF16_MAX_TOL and mn <= BF16_MEAN_TOL, \
             f"{what}: max {mx:.3e} (excess {ex:.3e}) mean {mn:.3e} (storage floor {floor:.3e})"
     return mx, mn

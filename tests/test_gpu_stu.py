@@ -67,8 +67,8 @@ def test_stu_layer_matches_oracle(with_bias):
                                       ln1_b=host.get("ln1_b"), b_uvqk=host.get("b_uvqk"),
                                       ln2_b=host.get("ln2_b"), b_out=host.get("b_out"),
                                       store_bf16=True, want_uvqk=True)
-    assert_close_bf16(_np(uvqk), ruvqk, "UVQK")
-    mx, mn = assert_close_bf16(_np(out), ref, "out")
+    assert_close_bf16(_np(uvqk), ruvqk, "UVQK", ref_rounded=True)
+    mx, mn = assert_close_bf16(_np(out), ref, "out", ref_rounded=True)
     print(f"  out: max {mx:.3e} mean {mn:.3e}")
 
 
@@ -105,17 +105,24 @@ def test_truncate_matches_oracle_bitwise():
     assert torch.equal(xo[:n], xd[torch.from_numpy(rgi).to(DEV)])
 
 
-def _run_stack(sw, cfg):
+def _run_stack(sw, cfg, keep_layers=False):
     layers = [_layer_weights(sw, li)[0] for li in range(sw.layers)]
     x = _b(sw.x)
     offs = torch.from_numpy(sw.offsets).to(DEV)
     tg = torch.from_numpy(sw.num_targets).to(DEV)
-    res = stu_stack_fwd(cfg, layers, x, offs, tg)
+    res = stu_stack_fwd(cfg, layers, x, offs, tg, keep_layers=keep_layers)
     torch.cuda.synchronize()
     return res
 
 
-def _oracle_stack(sw, cfg):
+def _oracle_layer(sw, cfg, li, x, offs, tg, store):
+    return oracle.stu_layer_fwd(x, offs, tg, sw.ln1_w[li], sw.w_uvqk[li], sw.ln2_w[li],
+                                sw.w_out[li], heads=sw.heads, dqk=sw.d, dv=sw.d,
+                                k1=cfg.kernel_k1, k2=cfg.kernel_k2, ctx=cfg.contextual_seq_len,
+                                N=cfg.max_seq_len, store_bf16=store)
+
+
+def _oracle_stack(sw, cfg, store=True):
     x, offs, tg = sw.x.astype(np.float64), sw.offsets, sw.num_targets
     gidx = None
     for li in range(sw.layers):
@@ -123,10 +130,7 @@ def _oracle_stack(sw, cfg):
             offs, gidx = oracle.truncate(offs, tg, cfg.contextual_seq_len,
                                          cfg.attn_truncation_tail_len)
             x = x[gidx]
-        x = oracle.stu_layer_fwd(x, offs, tg, sw.ln1_w[li], sw.w_uvqk[li], sw.ln2_w[li],
-                                 sw.w_out[li], heads=sw.heads, dqk=sw.d, dv=sw.d,
-                                 k1=cfg.kernel_k1, k2=cfg.kernel_k2, ctx=cfg.contextual_seq_len,
-                                 N=cfg.max_seq_len, store_bf16=True)
+        x = _oracle_layer(sw, cfg, li, x, offs, tg, store)
     return x, offs, gidx
 
 
@@ -138,30 +142,49 @@ def _stack_cfg(sw):
                      attn_truncation_tail_len=sw.tail_len, max_seq_len=sw.max_seq_len)
 
 
+def _check_stack(sw, every_layer=True):
+    """Per layer: the layer applied by the GPU to its own input matches the
+    storage-matched oracle applied to the same input (stated bf16 tolerance).
+    End to end: the GPU chain's error against the exact fp64 chain stays within
+    1.5x the error that bf16 storage alone causes (the storage-matched fp64
+    chain against the exact one); bf16 rounding of the residual stream makes
+    the chain drift by itself, whoever computes it."""
+    cfg = _stack_cfg(sw)
+    res = _run_stack(sw, cfg, keep_layers=True)
+    ref_exact, roffs, rgidx = _oracle_stack(sw, cfg, store=False)
+    assert np.array_equal(res.offsets.cpu().numpy(), roffs)
+    assert np.array_equal(res.gather_idx.cpu().numpy(), rgidx)
+    offs_l = [sw.offsets] * cfg.attn_truncation_split_layer + \
+        [roffs] * (sw.layers - cfg.attn_truncation_split_layer)
+    layers = range(sw.layers) if every_layer else (0, cfg.attn_truncation_split_layer,
+                                                   sw.layers - 1)
+    for li in layers:
+        xin = _np(res.layer_inputs[li])
+        ref = _oracle_layer(sw, cfg, li, xin, offs_l[li], sw.num_targets, True)
+        mx, mn = assert_close_bf16(_np(res.layer_outputs[li]), ref, f"layer {li}",
+                                   ref_rounded=True)
+        print(f"  layer {li:2d}: max {mx:.3e} mean {mn:.3e}", flush=True)
+    ref_store, _, _ = _oracle_stack(sw, cfg, store=True)
+    g_mx, g_mn = rel_errors(_np(res.x), ref_exact)
+    s_mx, s_mn = rel_errors(ref_store, ref_exact)
+    print(f"  chain vs exact fp64: gpu max {g_mx:.3e} mean {g_mn:.3e}; bf16-storage oracle "
+          f"max {s_mx:.3e} mean {s_mn:.3e}", flush=True)
+    assert g_mx <= 1.5 * s_mx and g_mn <= 1.5 * s_mn
+    return res
+
+
 def test_stack_small_with_truncation():
     sw = make_stack_workload(seed=4, batch=4, min_len=512, max_len=1024, layers=4, split_layer=2,
                              tail_len=256, k1=128, k2=32, contextual_len=16, num_targets=32)
-    cfg = _stack_cfg(sw)
     print(f"[case] stack 4 layers T={int(sw.offsets[-1])}", flush=True)
-    res = _run_stack(sw, cfg)
-    ref, roffs, rgidx = _oracle_stack(sw, cfg)
-    assert np.array_equal(res.offsets.cpu().numpy(), roffs)
-    assert np.array_equal(res.gather_idx.cpu().numpy(), rgidx)
-    mx, mn = assert_close_bf16(_np(res.x), ref, "stack out")
-    print(f"  stack out: max {mx:.3e} mean {mn:.3e}  layer tokens {res.layer_tokens}")
+    _check_stack(sw)
 
 
 def test_stack_18_layers_full_config():
     """18 layers, hidden 512, H=4, d=128, K1=512, K2=64, ctx 16, 64 targets, B=8,
     L U[2048,4096], truncation before layer 9 to 16 + 1024 + 64 tokens."""
     sw = make_stack_workload(seed=0)
-    cfg = _stack_cfg(sw)
     print(f"[case] stack 18 layers T={int(sw.offsets[-1])}", flush=True)
-    res = _run_stack(sw, cfg)
-    ref, roffs, rgidx = _oracle_stack(sw, cfg)
-    assert np.array_equal(res.offsets.cpu().numpy(), roffs)
-    assert np.array_equal(res.gather_idx.cpu().numpy(), rgidx)
+    res = _check_stack(sw, every_layer=False)
     assert res.layer_tokens[:9] == [int(sw.offsets[-1])] * 9
     assert res.layer_tokens[9:] == [8 * (16 + 1024 + 64)] * 9
-    mx, mn = assert_close_bf16(_np(res.x), ref, "stack out")
-    print(f"  stack out: max {mx:.3e} mean {mn:.3e}")
