@@ -62,13 +62,10 @@ __global__ __launch_bounds__(256, 1) void sla_bwd_dkdv_bf16_kernel(AttnParams p)
     // stationary K^T and V^T operands: lane holds key kj, d-slots 16c + 8*hl .. +8
     const int kj = it.c0 + 32 * wv + l32;
     bf16x8 kb[NC], vb[NC];
-    {
-        const bool ok = kj < it.c1;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            kb[c] = as_bf16x8(ld16_or_zero(kg + (int64_t)kj * p.ldk + 16 * c + 8 * hl, ok));
-            vb[c] = as_bf16x8(ld16_or_zero(vg + (int64_t)kj * p.ldv + 16 * c + 8 * hl, ok));
-        }
+    for (int c = 0; c < NC; ++c) {
+        kb[c] = as_bf16x8(ld16_row(kg, p.ldk, kj, it.c1, 16 * c + 8 * hl));
+        vb[c] = as_bf16x8(ld16_row(vg, p.ldv, kj, it.c1, 16 * c + 8 * hl));
     }
 
     // row steps: history tiles covering [ha, hb), then target tiles covering [ta, tb)
@@ -218,13 +215,16 @@ __global__ __launch_bounds__(256, 1) void sla_bwd_dkdv_bf16_kernel(AttnParams p)
     }
 }
 
-// Sum the chunk partials of each split prefix key tile in chunk order.
+// Sum the chunk partials of each split prefix key tile in chunk order.  Block
+// (item, slab) handles 1024 consecutive values of the [BN][2D] tile.
+constexpr int RED_SLAB = 1024;
+
 template <int D>
 __global__ __launch_bounds__(256) void sla_bwd_reduce_kernel(AttnParams p)
 {
-    constexpr int BN = BWD_BN, W = 2 * D;
+    constexpr int BN = BWD_BN, W = 2 * D, SLABS = BN * W / RED_SLAB;
     const int nrec = p.s.red_base[p.B];
-    const int item = blockIdx.x;
+    const int item = blockIdx.x / SLABS, slab = blockIdx.x % SLABS;
     if (item >= nrec * p.H) return;
     const int h = item / nrec;
     const int rec = item - h * nrec;
@@ -234,25 +234,33 @@ __global__ __launch_bounds__(256) void sla_bwd_reduce_kernel(AttnParams p)
     const int nch = p.s.nch[b];
     const int slot0 = p.s.part_base[b] + tile * nch;
     const int c0 = tile * BN, c1 = imin(c0 + BN, sd.L);
-    uint16_t *dkg = reinterpret_cast<uint16_t *>(p.dk) + sd.base * p.lddk + h * D;
-    uint16_t *dvg = reinterpret_cast<uint16_t *>(p.dv) + sd.base * p.lddv + h * D;
-    for (int e4 = threadIdx.x; e4 < BN * W / 4; e4 += blockDim.x) {
-        const int e = 4 * e4;
-        const int jl = e / W, col = e % W;
-        if (c0 + jl >= c1) continue;
-        float4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int c = 0; c < nch; ++c) {
-            const float4 v = *reinterpret_cast<const float4 *>(
-                p.partials + ((int64_t)(slot0 + c) * p.H + h) * BN * W + e);
-            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-        }
-        const bool is_k = col < D;
-        const float sc = p.out_scale / *p.grad_scale;
-        uint2 o = cvt4_u2(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
-        uint16_t *dst = is_k ? dkg + (int64_t)(c0 + jl) * p.lddk + col
-                             : dvg + (int64_t)(c0 + jl) * p.lddv + (col - D);
-        *reinterpret_cast<uint2 *>(dst) = o;
+    const int e = slab * RED_SLAB + 4 * threadIdx.x;
+    const int jl = e / W, col = e % W;
+    if (c0 + jl >= c1) return;
+    const float *src = p.partials + ((int64_t)slot0 * p.H + h) * BN * W + e;
+    const int64_t stride = (int64_t)p.H * BN * W;
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    int c = 0;
+    for (; c + 4 <= nch; c += 4) {  // four loads in flight, added in chunk order
+        const float4 v0 = *reinterpret_cast<const float4 *>(src + (c + 0) * stride);
+        const float4 v1 = *reinterpret_cast<const float4 *>(src + (c + 1) * stride);
+        const float4 v2 = *reinterpret_cast<const float4 *>(src + (c + 2) * stride);
+        const float4 v3 = *reinterpret_cast<const float4 *>(src + (c + 3) * stride);
+        acc.x += v0.x; acc.y += v0.y; acc.z += v0.z; acc.w += v0.w;
+        acc.x += v1.x; acc.y += v1.y; acc.z += v1.z; acc.w += v1.w;
+        acc.x += v2.x; acc.y += v2.y; acc.z += v2.z; acc.w += v2.w;
+        acc.x += v3.x; acc.y += v3.y; acc.z += v3.z; acc.w += v3.w;
     }
+    for (; c < nch; ++c) {
+        const float4 v = *reinterpret_cast<const float4 *>(src + c * stride);
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    const float sc = p.out_scale / *p.grad_scale;
+    uint2 o = cvt4_u2(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
+    uint16_t *dst = col < D
+        ? reinterpret_cast<uint16_t *>(p.dk) + (sd.base + c0 + jl) * p.lddk + h * D + col
+        : reinterpret_cast<uint16_t *>(p.dv) + (sd.base + c0 + jl) * p.lddv + h * D + (col - D);
+    *reinterpret_cast<uint2 *>(dst) = o;
 }
 
 // ---------------------------------------------------------------------------
@@ -288,13 +296,10 @@ __global__ __launch_bounds__(256, 1) void sla_bwd_dq_bf16_kernel(AttnParams p)
 
     const int qi = r0 + 32 * wv + l32;
     bf16x8 qb[NC], gb[NC];
-    {
-        const bool ok = qi < r1;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            qb[c] = as_bf16x8(ld16_or_zero(qg + (int64_t)qi * p.ldq + 16 * c + 8 * hl, ok));
-            gb[c] = as_bf16x8(ld16_or_zero(gg + (int64_t)qi * p.lddo + 16 * c + 8 * hl, ok));
-        }
+    for (int c = 0; c < NC; ++c) {
+        qb[c] = as_bf16x8(ld16_row(qg, p.ldq, qi, r1, 16 * c + 8 * hl));
+        gb[c] = as_bf16x8(ld16_row(gg, p.lddo, qi, r1, 16 * c + 8 * hl));
     }
 
     const TileCursor cur(kr, BN);
@@ -397,7 +402,8 @@ static hipError_t launch_dkdv_d(const AttnParams &p, hipStream_t st)
     hipLaunchKernelGGL(sla_bwd_dkdv_bf16_kernel<D>, dim3(p.grid_bwd), dim3(256), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.grid_red == 0) return e;
-    hipLaunchKernelGGL(sla_bwd_reduce_kernel<D>, dim3(p.grid_red), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(sla_bwd_reduce_kernel<D>, dim3(p.grid_red * (BWD_BN * 2 * D / RED_SLAB)),
+                       dim3(256), 0, st, p);
     return hipGetLastError();
 }
 

@@ -145,6 +145,23 @@ __device__ __forceinline__ uint4 ld16_or_zero(const void *p, bool ok)
     return ok ? *reinterpret_cast<const uint4 *>(p) : z;
 }
 
+// 16 bytes at column `col` of row r of a [rows][ld] bf16 tensor, zero when
+// r >= limit.  The load itself is unconditional (row clamped to limit-1, which
+// the caller guarantees is >= 0) so it stays one 16-byte load; the zeroing is
+// a select.
+__device__ __forceinline__ uint4 ld16_row(const uint16_t *base, int64_t ld, int r, int limit,
+                                          int col)
+{
+    const int rr = r < limit ? r : limit - 1;
+    uint4 v = *reinterpret_cast<const uint4 *>(base + (int64_t)rr * ld + col);
+    const bool ok = r < limit;
+    v.x = ok ? v.x : 0u;
+    v.y = ok ? v.y : 0u;
+    v.z = ok ? v.z : 0u;
+    v.w = ok ? v.w : 0u;
+    return v;
+}
+
 // 16-byte chunk swizzle for a row-major tile whose rows hold `cpr` chunks: the
 // chunk index is XORed with the low bits of the row so that 8 consecutive rows
 // read at the same logical chunk hit 8 different bank groups.

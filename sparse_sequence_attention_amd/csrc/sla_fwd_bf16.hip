@@ -41,7 +41,9 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
     const int b = find_seq(p.s.fwd_base, p.B, rec);
     const SeqDims sd = seq_dims(p.offsets, p.num_targets, b);
     int r0, r1;
-    row_tile(sd.L, sd.U, BM, rec - p.s.fwd_base[b], r0, r1);
+    row_tile(sd.L, sd.U, BM, rec - uniform(p.s.fwd_base[b]), r0, r1);
+    r0 = uniform(r0);
+    r1 = uniform(r1);
     const Ranges kr = fwd_key_ranges(sd.L, sd.U, p.k1, p.k2e, r0, r1, BN);
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -54,15 +56,11 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
     // Q^T operand: lane holds row qi, d-slots 16c + 8*hl .. +8
     const int qi = r0 + 32 * wv + l32;
     bf16x8 qb[NC];
-    {
-        const bool ok = qi < sd.L;
-        const uint16_t *qrow = qg + (int64_t)qi * p.ldq;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) qb[c] = as_bf16x8(ld16_or_zero(qrow + 16 * c + 8 * hl, ok));
-    }
+    for (int c = 0; c < NC; ++c) qb[c] = as_bf16x8(ld16_row(qg, p.ldq, qi, sd.L, 16 * c + 8 * hl));
 
     const TileCursor cur(kr, BN);
-    const int ntiles = cur.total;
+    const int ntiles = uniform(cur.total);
 
     floatx16 oacc[NDB];
 #pragma unroll
@@ -77,7 +75,7 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
     const float nal2e = p.neg_alpha_log2e;
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1;
-        const int c0 = c_next;
+        const int c0 = uniform(c_next);
         kt.store_rows(sk[buf], tid);
         store_transposed_f16<D>(vt, svt[buf], tid, 1.0f);
         c_next = cur.start(t + 1, BN);
@@ -99,18 +97,25 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
             }
         }
 
-        // mask (partial tiles only) and P = s * sigmoid(alpha s)
-        const bool full = (r0 < sd.U) && (c0 + BN <= sd.L) && (c0 + BN - 1 <= r0) &&
-                          ((r1 - 1 - c0 < p.k1) || (c0 + BN <= p.k2e));
+        // mask (partial tiles only, a workgroup-uniform branch), then
+        // P = s * sigmoid(alpha s)
+        const bool full = uniform((r0 < sd.U) && (c0 + BN <= sd.L) && (c0 + BN - 1 <= r0) &&
+                                  ((r1 - 1 - c0 < p.k1) || (c0 + BN <= p.k2e))) != 0;
+        if (!full) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int j = c0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
+                    sacc[kb][r] = visible(qi, j, sd.U, p.k1, p.k2e) ? sacc[kb][r] : 0.0f;
+                }
+            }
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float s = sacc[kb][r];
-                if (!full) {
-                    const int j = c0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-                    if (!visible(qi, j, sd.U, p.k1, p.k2e)) s = 0.0f;
-                }
+                const float s = sacc[kb][r];
                 sacc[kb][r] = s * sigmoid_fast(s, nal2e);
             }
         }

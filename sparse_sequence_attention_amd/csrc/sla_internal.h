@@ -46,10 +46,10 @@ struct SeqDims {
     int U;         // first target row (L when there are no targets)
 };
 
-// Up to three half-open ranges of the other operand, in tokens of the sequence.
+// Up to three half-open ranges of the other operand, in tokens of the sequence
+// (scalar fields: an indexed array would be placed in scratch memory).
 struct Ranges {
-    int lo[3];
-    int hi[3];
+    int lo0, hi0, lo1, hi1, lo2, hi2;
     int n;
 };
 
@@ -62,9 +62,10 @@ __host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 // and the history keys of the first target slot's window.
 __host__ __device__ inline bool visible(int i, int j, int U, int K1, int K2e)
 {
-    if (i < U) return j <= i && (i - j < K1 || j < K2e);
-    if (j == i) return true;
-    return j < U && (U - j < K1 || j < K2e);
+    // branch-free: both cases evaluated with non-short-circuit logic, then a select
+    const bool hist = (j <= i) & ((i - j < K1) | (j < K2e));
+    const bool tgt = (j == i) | ((j < U) & ((U - j < K1) | (j < K2e)));
+    return (i < U) ? hist : tgt;
 }
 
 // Number of row tiles (forward / dQ items) of a sequence: history rows from 0
@@ -86,40 +87,54 @@ __host__ __device__ inline void row_tile(int L, int U, int bm, int t, int &r0, i
     }
 }
 
-// Append [a, b) rounded out to whole bn-key tiles (clipped at L), merging with
-// the previous range when they touch or overlap.  Ranges arrive sorted by start.
-__host__ __device__ inline void push_tiles(Ranges &r, int a, int b, int bn, int L)
+// Round the key interval [a, b) out to whole bn-key tiles (clipped at L).
+__host__ __device__ inline void tile_round(int &a, int &b, int bn, int L)
 {
-    if (a >= b) return;
-    int lo = (a / bn) * bn;
-    int hi = imin(cdiv(b, bn) * bn, L);
-    if (r.n > 0 && lo <= r.hi[r.n - 1]) {
-        r.hi[r.n - 1] = imax(r.hi[r.n - 1], hi);
+    if (a >= b) {
+        a = b = 0;
         return;
     }
-    r.lo[r.n] = lo;
-    r.hi[r.n] = hi;
-    r.n++;
+    a = (a / bn) * bn;
+    b = imin(cdiv(b, bn) * bn, L);
 }
 
 // Keys visited by the row tile [r0, r1): the union of the visible keys, rounded
 // out to whole key tiles.  History tile: prefix [0, min(K2e, r1)) and band
 // [r0-K1+1, r1).  Target tile: prefix [0, min(K2e, U)), window of row U over
-// history keys [U-K1+1, U), and the diagonal [r0, r1).
+// history keys [U-K1+1, U), and the diagonal [r0, r1).  The three candidate
+// intervals start in increasing order; touching ones are merged.  (Scalars
+// only: an indexed array here would live in scratch memory.)
 __host__ __device__ inline Ranges fwd_key_ranges(int L, int U, int K1, int K2e, int r0, int r1,
                                                  int bn)
 {
-    Ranges r;
-    r.n = 0;
+    Ranges r{0, 0, 0, 0, 0, 0, 0};
     if (r0 >= r1) return r;
+    int aA, bA, aB, bB, aC, bC;
     if (r0 < U) {
-        push_tiles(r, 0, imin(K2e, r1), bn, L);
-        if (K1 >= 1) push_tiles(r, imax(0, r0 - K1 + 1), r1, bn, L);
+        aA = 0; bA = imin(K2e, r1);
+        aB = K1 >= 1 ? imax(0, r0 - K1 + 1) : 0; bB = K1 >= 1 ? r1 : 0;
+        aC = bC = 0;
     } else {
-        push_tiles(r, 0, imin(K2e, U), bn, L);
-        if (K1 >= 2) push_tiles(r, imax(0, U - K1 + 1), U, bn, L);
-        push_tiles(r, r0, r1, bn, L);
+        aA = 0; bA = imin(K2e, U);
+        aB = K1 >= 2 ? imax(0, U - K1 + 1) : 0; bB = K1 >= 2 ? U : 0;
+        aC = r0; bC = r1;
     }
+    tile_round(aA, bA, bn, L);
+    tile_round(aB, bB, bn, L);
+    tile_round(aC, bC, bn, L);
+    bool eA = aA < bA, eB = aB < bB, eC = aC < bC;
+    if (eA && eB && aB <= bA) { bA = imax(bA, bB); eB = false; }
+    if (eC && eB && aC <= bB) { bB = imax(bB, bC); eC = false; }
+    if (eC && !eB && eA && aC <= bA) { bA = imax(bA, bC); eC = false; }
+    // compact the non-empty ranges into slots 0..n-1
+    if (!eA) { aA = aB; bA = bB; eA = eB; aB = aC; bB = bC; eB = eC; eC = false; }
+    if (!eA) { aA = aB; bA = bB; eA = eB; eB = false; }
+    if (!eB) { aB = aC; bB = bC; eB = eC; eC = false; }
+    r.lo0 = aA; r.hi0 = bA; r.lo1 = aB; r.hi1 = bB; r.lo2 = aC; r.hi2 = bC;
+    r.n = eA ? (eB ? (eC ? 3 : 2) : 1) : 0;
+    if (r.n < 3) { r.lo2 = r.hi2 = 0; }
+    if (r.n < 2) { r.lo1 = r.hi1 = 0; }
+    if (r.n < 1) { r.lo0 = r.hi0 = 0; }
     return r;
 }
 
@@ -129,12 +144,12 @@ struct TileCursor {
     int lo0, lo1, lo2, n0, n01, total;
     __host__ __device__ TileCursor(const Ranges &r, int bn)
     {
-        lo0 = r.n > 0 ? r.lo[0] : 0;
-        lo1 = r.n > 1 ? r.lo[1] : 0;
-        lo2 = r.n > 2 ? r.lo[2] : 0;
-        int c0 = r.n > 0 ? cdiv(r.hi[0] - r.lo[0], bn) : 0;
-        int c1 = r.n > 1 ? cdiv(r.hi[1] - r.lo[1], bn) : 0;
-        int c2 = r.n > 2 ? cdiv(r.hi[2] - r.lo[2], bn) : 0;
+        lo0 = r.n > 0 ? r.lo0 : 0;
+        lo1 = r.n > 1 ? r.lo1 : 0;
+        lo2 = r.n > 2 ? r.lo2 : 0;
+        int c0 = r.n > 0 ? cdiv(r.hi0 - r.lo0, bn) : 0;
+        int c1 = r.n > 1 ? cdiv(r.hi1 - r.lo1, bn) : 0;
+        int c2 = r.n > 2 ? cdiv(r.hi2 - r.lo2, bn) : 0;
         n0 = c0;
         n01 = c0 + c1;
         total = c0 + c1 + c2;
@@ -286,12 +301,9 @@ __host__ __device__ inline void fill_record(int op, int b, int L, int U, int K1,
         rec[1] = r0;
         rec[2] = r1;
         rec[3] = kr.n;
-        for (int i = 0; i < 3; ++i) {
-            if (i < kr.n) {
-                rec[4 + 2 * i] = kr.lo[i];
-                rec[5 + 2 * i] = kr.hi[i];
-            }
-        }
+        rec[4] = kr.lo0; rec[5] = kr.hi0;
+        rec[6] = kr.lo1; rec[7] = kr.hi1;
+        rec[8] = kr.lo2; rec[9] = kr.hi2;
         rec[11] = 1;
     } else {
         int np, nch;
@@ -317,24 +329,45 @@ __host__ __device__ inline int seq_items(int op, int L, int U, int K2e)
     return bwd_items(L, U, K2e, BWD_BN, BWD_BM, np, nch);
 }
 
+// Workgroup-uniform value kept in a scalar register (the compiler cannot prove
+// that values loaded through the kernel's pointers are uniform).  Only for
+// values that are the same in every lane.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uniform64(int64_t x)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Largest b with base[b] <= item (base is non-decreasing, base[0] = 0).
+// UNIFORM: the item is the same in every lane (one work item per workgroup).
+template <bool UNIFORM = true>
 __device__ inline int find_seq(const int32_t *base, int B, int item)
 {
     int lo = 0, hi = B - 1;
     while (lo < hi) {
         int mid = (lo + hi + 1) >> 1;
-        if (base[mid] <= item) lo = mid;
+        int v = base[mid];
+        if (UNIFORM) v = uniform(v);
+        if (v <= item) lo = mid;
         else hi = mid - 1;
     }
-    return lo;
+    return UNIFORM ? uniform(lo) : lo;
 }
 
+template <bool UNIFORM = true>
 __device__ inline SeqDims seq_dims(const int64_t *offsets, const int32_t *num_targets, int b)
 {
     SeqDims s;
     s.base = offsets[b];
     s.L = (int)(offsets[b + 1] - s.base);
     s.U = s.L - (num_targets ? num_targets[b] : 0);
+    if (UNIFORM) {
+        s.base = uniform64(s.base);
+        s.L = uniform(s.L);
+        s.U = uniform(s.U);
+    }
     return s;
 }
 

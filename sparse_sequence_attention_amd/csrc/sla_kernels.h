@@ -32,7 +32,7 @@ struct AttnParams {
     int grid_red;           // upper bound of reduce items (x heads)
 };
 
-constexpr int ABSMAX_BLOCKS = 256;
+constexpr int ABSMAX_BLOCKS = 1024;
 
 // Sizes (int32 counts / bytes) of the workspace regions, from host-known data.
 struct WsLayout {

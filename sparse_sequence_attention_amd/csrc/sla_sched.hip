@@ -25,7 +25,8 @@ __global__ __launch_bounds__(SCHED_THREADS) void sla_sched_kernel(const int64_t 
     if (tid == 0) carry = make_int4(0, 0, 0, 0);
     if (absmax_part) {
         // gradient scale: the power of two that maps max|dO| into [1, 2)
-        float m = tid < ABSMAX_BLOCKS ? absmax_part[tid] : 0.0f;
+        float m = 0.0f;
+        for (int i = tid; i < ABSMAX_BLOCKS; i += SCHED_THREADS) m = fmaxf(m, absmax_part[i]);
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
         if ((tid & 63) == 0) red[tid >> 6] = m;
@@ -47,7 +48,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void sla_sched_kernel(const int64_t 
         const int b = start + tid;
         int4 v = make_int4(0, 0, 0, 0);
         if (b < B) {
-            SeqDims sd = seq_dims(offsets, num_targets, b);
+            SeqDims sd = seq_dims<false>(offsets, num_targets, b);
             int np, nch;
             v.x = row_tiles(sd.L, sd.U, FWD_BM);
             v.y = bwd_items(sd.L, sd.U, k2e, BWD_BN, BWD_BM, np, nch);
@@ -106,17 +107,24 @@ __global__ __launch_bounds__(256) void absmax_bf16_kernel(const uint16_t *x, int
                                                           int64_t rows, int cols, float *part)
 {
     __shared__ float red[4];
-    const int cpr = cols / 8;
-    const int64_t nchunks = rows * cpr;
+    const int cpr = cols / 8;  // 16-byte chunks per row
+    // the block covers `rpi` rows per pass, cpr threads per row (strided when
+    // a row has more chunks than the block has threads)
+    const int tpr = cpr < (int)blockDim.x ? cpr : (int)blockDim.x;
+    const int rpi = blockDim.x / tpr;
+    const int ro = threadIdx.x / tpr, ko = threadIdx.x % tpr;
     float m = 0.0f;
-    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunks;
-         c += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t r = c / cpr;
-        const int k = (int)(c - r * cpr);
-        uint4 v = ld16(x + r * ld + 8 * k);
-        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    if (ro < rpi) {
+        for (int64_t r = (int64_t)blockIdx.x * rpi + ro; r < rows; r += (int64_t)gridDim.x * rpi) {
+            const uint16_t *row = x + r * ld;
+            for (int k = ko; k < cpr; k += tpr) {
+                uint4 v = ld16(row + 8 * k);
+                uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
+                for (int i = 0; i < 4; ++i)
+                    m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
+            }
+        }
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
@@ -142,8 +150,8 @@ __global__ void sla_sched_dump_kernel(const int64_t *offsets, const int32_t *num
     const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (r == 0) *count = total;
     if (r >= total || r >= capacity) return;
-    const int b = find_seq(base, B, (int)r);
-    const SeqDims sd = seq_dims(offsets, num_targets, b);
+    const int b = find_seq<false>(base, B, (int)r);
+    const SeqDims sd = seq_dims<false>(offsets, num_targets, b);
     const int li = (int)r - base[b];
     int32_t rec[12];
     fill_record(op, b, sd.L, sd.U, k1, k2e, li, rec);

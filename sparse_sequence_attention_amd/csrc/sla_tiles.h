@@ -21,7 +21,7 @@ struct Tile64 {
     __device__ __forceinline__ static bool active(int tid) { return tid < ACTIVE; }
 
     // Load rows [row0, row0 + 64) of a [tokens][ld] tensor (head offset
-    // already applied to `base_ptr`); rows at or past `limit` read as zero.
+    // already applied to `base_ptr`); rows at or past `limit` (>= 1) read as zero.
     __device__ __forceinline__ void load(const uint16_t *base_ptr, int64_t ld, int row0, int limit,
                                          int tid)
     {
@@ -29,8 +29,7 @@ struct Tile64 {
         const int g = tid / CPR, c = tid % CPR;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = row0 + 4 * g + i;
-            uint4 v = ld16_or_zero(base_ptr + (int64_t)r * ld + 8 * c, r < limit);
+            uint4 v = ld16_row(base_ptr, ld, row0 + 4 * g + i, limit, 8 * c);
             w[i][0] = v.x; w[i][1] = v.y; w[i][2] = v.z; w[i][3] = v.w;
         }
     }

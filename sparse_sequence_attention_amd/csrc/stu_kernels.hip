@@ -149,8 +149,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t *A, in
     auto load = [&](int k0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int64_t m = m0 + sr + 32 * i;
-            ra[i] = ld16_or_zero(A + m * lda + k0 + 8 * sc, m < M);
+            ra[i] = ld16_row(A, lda, (int)(m0 + sr + 32 * i), (int)M, k0 + 8 * sc);
             rw[i] = ld16(W + (int64_t)(n0 + sr + 32 * i) * ldw + k0 + 8 * sc);
         }
     };
