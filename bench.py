@@ -49,7 +49,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the SLA hot path "
-              "shards by sequence with no exchange, see DESIGN.md", file=sys.stderr)
+              "shards by sequence with no exchange, so a multi-GPU figure is one GPU's "
+              "value times the GPU count", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -121,7 +122,7 @@ def main():
             traffic = json.load(f).get(dom)
 
     line = {
-        "metric": "SLA fwd+bwd useful TFLOP/s at L=16K (long_16k)",
+        "metric": "SLA fwd+bwd useful TFLOP/s & tokens/s at L=16K; % of bf16 MFMA peak",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
