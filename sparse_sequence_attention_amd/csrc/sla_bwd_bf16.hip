@@ -49,7 +49,8 @@ __global__ __launch_bounds__(256, 1) void sla_bwd_dkdv_bf16_kernel(AttnParams p)
     const SeqDims sd = seq_dims(p.offsets, p.num_targets, b);
     int np, nch;
     bwd_items(sd.L, sd.U, p.k2e, BN, BM, np, nch);
-    const BwdItem it = bwd_item(sd.L, sd.U, p.k1, p.k2e, BN, BM, rec - p.s.bwd_base[b], np, nch);
+    const BwdItem it = bwd_item(sd.L, sd.U, p.k1, p.k2e, BN, BM, rec - uniform(p.s.bwd_base[b]),
+                                np, nch);
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int l32 = lane & 31, hl = lane >> 5;
@@ -97,11 +98,13 @@ __global__ __launch_bounds__(256, 1) void sla_bwd_dkdv_bf16_kernel(AttnParams p)
             m1 = imin(m0 + BM, sd.L);
         }
     };
+    // rows at or past m1 of a step hold copies of row m1 - 1; such steps are
+    // never "full", and the mask removes those rows
     int m0n = 0, m1n = 0;
     if (nsteps > 0) {
         step_rows(0, m0n, m1n);
-        qt.load(qg, p.ldq, m0n, m1n, tid);
-        gt.load(gg, p.lddo, m0n, m1n, tid);
+        qt.load_clamped(qg, p.ldq, m0n, m1n, tid);
+        gt.load_clamped(gg, p.lddo, m0n, m1n, tid);
     }
     const float nal2e = p.neg_alpha_log2e, alpha = p.alpha;
     const float gscale = *p.grad_scale;
@@ -111,15 +114,15 @@ __global__ __launch_bounds__(256, 1) void sla_bwd_dkdv_bf16_kernel(AttnParams p)
     for (int c = 0; c < NC; ++c) vb[c] = scale_bf16x8(vb[c], gscale);
     for (int s = 0; s < nsteps; ++s) {
         const int buf = s & 1;
-        const int m0 = m0n, m1 = m1n;
+        const int m0 = uniform(m0n), m1 = uniform(m1n);
         qt.store_rows(sq[buf], tid);
         store_transposed_f16<D>(qt, sqt[buf], tid, 1.0f);
         gt.store_rows(sdo[buf], tid);
         store_transposed_f16<D>(gt, sdot[buf], tid, gscale);
         if (s + 1 < nsteps) {
             step_rows(s + 1, m0n, m1n);
-            qt.load(qg, p.ldq, m0n, m1n, tid);
-            gt.load(gg, p.lddo, m0n, m1n, tid);
+            qt.load_clamped(qg, p.ldq, m0n, m1n, tid);
+            gt.load_clamped(gg, p.lddo, m0n, m1n, tid);
         }
         __syncthreads();
 
@@ -138,21 +141,28 @@ __global__ __launch_bounds__(256, 1) void sla_bwd_dkdv_bf16_kernel(AttnParams p)
             }
         }
 
-        // rows at or past m1 were loaded as zero, so they add nothing
-        const bool full = (m1 <= sd.U) && key_tile_full && (it.c0 + BN - 1 <= m0) &&
-                          ((m1 - 1 - it.c0 < p.k1) || (it.c0 + BN <= p.k2e));
+        // mask (partial steps only, a workgroup-uniform branch): rows past m1
+        // and invisible pairs get s = g = 0, hence P = dS = 0
+        const bool full = uniform((m1 == m0 + BM) && (m1 <= sd.U) && key_tile_full &&
+                                  (it.c0 + BN - 1 <= m0) &&
+                                  ((m1 - 1 - it.c0 < p.k1) || (it.c0 + BN <= p.k2e))) != 0;
+        if (!full) {
+#pragma unroll
+            for (int qb2 = 0; qb2 < 2; ++qb2) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = m0 + 32 * qb2 + 8 * (r >> 2) + 4 * hl + (r & 3);
+                    const bool vis = (i < m1) && visible(i, kj, sd.U, p.k1, p.k2e);
+                    sacc[qb2][r] = vis ? sacc[qb2][r] : 0.0f;
+                    pacc[qb2][r] = vis ? pacc[qb2][r] : 0.0f;
+                }
+            }
+        }
 #pragma unroll
         for (int qb2 = 0; qb2 < 2; ++qb2) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float sv = sacc[qb2][r], g = pacc[qb2][r];
-                if (!full) {
-                    const int i = m0 + 32 * qb2 + 8 * (r >> 2) + 4 * hl + (r & 3);
-                    if (!visible(i, kj, sd.U, p.k1, p.k2e)) {
-                        sv = 0.0f;
-                        g = 0.0f;
-                    }
-                }
+                const float sv = sacc[qb2][r], g = pacc[qb2][r];
                 float e;
                 const float sg = sigmoid_e(sv, nal2e, e);
                 const float a = sv * sg;                         // SiLU(alpha s) / alpha
@@ -283,7 +293,9 @@ __global__ __launch_bounds__(256, 1) void sla_bwd_dq_bf16_kernel(AttnParams p)
     const int b = find_seq(p.s.fwd_base, p.B, rec);
     const SeqDims sd = seq_dims(p.offsets, p.num_targets, b);
     int r0, r1;
-    row_tile(sd.L, sd.U, BM, rec - p.s.fwd_base[b], r0, r1);
+    row_tile(sd.L, sd.U, BM, rec - uniform(p.s.fwd_base[b]), r0, r1);
+    r0 = uniform(r0);
+    r1 = uniform(r1);
     const Ranges kr = fwd_key_ranges(sd.L, sd.U, p.k1, p.k2e, r0, r1, BN);
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -294,6 +306,7 @@ __global__ __launch_bounds__(256, 1) void sla_bwd_dq_bf16_kernel(AttnParams p)
     const uint16_t *vg = reinterpret_cast<const uint16_t *>(p.v) + sd.base * p.ldv + h * D;
     const uint16_t *gg = reinterpret_cast<const uint16_t *>(p.dout) + sd.base * p.lddo + h * D;
 
+    // rows at or past r1 are zero, so their dS is zero
     const int qi = r0 + 32 * wv + l32;
     bf16x8 qb[NC], gb[NC];
 #pragma unroll
@@ -303,16 +316,18 @@ __global__ __launch_bounds__(256, 1) void sla_bwd_dq_bf16_kernel(AttnParams p)
     }
 
     const TileCursor cur(kr, BN);
-    const int ntiles = cur.total;
+    const int ntiles = uniform(cur.total);
     floatx16 dqacc[NDB];
 #pragma unroll
     for (int i = 0; i < NDB; ++i) dqacc[i] = zero16();
 
     Tile64<D> kt, vt;
+    // keys at or past L hold copies of key L - 1; such tiles are never "full",
+    // and the mask removes them
     int c_next = cur.start(0, BN);
     if (ntiles > 0) {
-        kt.load(kg, p.ldk, c_next, sd.L, tid);
-        vt.load(vg, p.ldv, c_next, sd.L, tid);
+        kt.load_clamped(kg, p.ldk, c_next, sd.L, tid);
+        vt.load_clamped(vg, p.ldv, c_next, sd.L, tid);
     }
     const float nal2e = p.neg_alpha_log2e, alpha = p.alpha;
     const float gscale = *p.grad_scale;
@@ -320,14 +335,14 @@ __global__ __launch_bounds__(256, 1) void sla_bwd_dq_bf16_kernel(AttnParams p)
     for (int c = 0; c < NC; ++c) gb[c] = scale_bf16x8(gb[c], gscale);
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1;
-        const int c0 = c_next;
+        const int c0 = uniform(c_next);
         kt.store_rows(sk[buf], tid);
         store_transposed_f16<D>(kt, skt[buf], tid, 1.0f);
         vt.store_rows(sv[buf], tid);
         c_next = cur.start(t + 1, BN);
         if (t + 1 < ntiles) {
-            kt.load(kg, p.ldk, c_next, sd.L, tid);
-            vt.load(vg, p.ldv, c_next, sd.L, tid);
+            kt.load_clamped(kg, p.ldk, c_next, sd.L, tid);
+            vt.load_clamped(vg, p.ldv, c_next, sd.L, tid);
         }
         __syncthreads();
 
@@ -346,20 +361,26 @@ __global__ __launch_bounds__(256, 1) void sla_bwd_dq_bf16_kernel(AttnParams p)
             }
         }
 
-        const bool full = (r0 < sd.U) && (c0 + BN <= sd.L) && (c0 + BN - 1 <= r0) &&
-                          ((r1 - 1 - c0 < p.k1) || (c0 + BN <= p.k2e));
+        // mask (partial tiles only, a workgroup-uniform branch)
+        const bool full = uniform((r0 < sd.U) && (c0 + BN <= sd.L) && (c0 + BN - 1 <= r0) &&
+                                  ((r1 - 1 - c0 < p.k1) || (c0 + BN <= p.k2e))) != 0;
+        if (!full) {
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int j = c0 + 32 * kb2 + 8 * (r >> 2) + 4 * hl + (r & 3);
+                    const bool vis = visible(qi, j, sd.U, p.k1, p.k2e);
+                    sacc[kb2][r] = vis ? sacc[kb2][r] : 0.0f;
+                    pacc[kb2][r] = vis ? pacc[kb2][r] : 0.0f;
+                }
+            }
+        }
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float s = sacc[kb2][r], g = pacc[kb2][r];
-                if (!full) {
-                    const int j = c0 + 32 * kb2 + 8 * (r >> 2) + 4 * hl + (r & 3);
-                    if (!visible(qi, j, sd.U, p.k1, p.k2e)) {
-                        s = 0.0f;
-                        g = 0.0f;
-                    }
-                }
+                const float s = sacc[kb2][r], g = pacc[kb2][r];
                 float e;
                 const float sg = sigmoid_e(s, nal2e, e);
                 pacc[kb2][r] = g * (sg * (1.0f + alpha * s * sg * e));

@@ -162,6 +162,17 @@ __device__ __forceinline__ uint4 ld16_row(const uint16_t *base, int64_t ld, int 
     return v;
 }
 
+// Row r of a [tokens][ld] bf16 tensor, clamped to row limit - 1 (limit >= 1):
+// a plain 16-byte load with no use of its value until the caller consumes it,
+// so it stays in flight; rows at or past `limit` hold a copy of the last valid
+// row, which the caller masks out.
+__device__ __forceinline__ uint4 ld16_clamped(const uint16_t *base, int64_t ld, int r, int limit,
+                                              int col)
+{
+    const int rr = r < limit ? r : limit - 1;
+    return *reinterpret_cast<const uint4 *>(base + (int64_t)rr * ld + col);
+}
+
 // 16-byte chunk swizzle for a row-major tile whose rows hold `cpr` chunks: the
 // chunk index is XORed with the low bits of the row so that 8 consecutive rows
 // read at the same logical chunk hit 8 different bank groups.

@@ -68,9 +68,11 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
 
     Tile64<D> kt, vt;
     int c_next = cur.start(0, BN);
+    // keys at or past L (last tile of a sequence) hold copies of key L - 1;
+    // such tiles are never "full", and the mask removes them
     if (ntiles > 0) {
-        kt.load(kg, p.ldk, c_next, sd.L, tid);
-        vt.load(vg, p.ldv, c_next, sd.L, tid);
+        kt.load_clamped(kg, p.ldk, c_next, sd.L, tid);
+        vt.load_clamped(vg, p.ldv, c_next, sd.L, tid);
     }
     const float nal2e = p.neg_alpha_log2e;
     for (int t = 0; t < ntiles; ++t) {
@@ -80,8 +82,8 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
         store_transposed_f16<D>(vt, svt[buf], tid, 1.0f);
         c_next = cur.start(t + 1, BN);
         if (t + 1 < ntiles) {
-            kt.load(kg, p.ldk, c_next, sd.L, tid);
-            vt.load(vg, p.ldv, c_next, sd.L, tid);
+            kt.load_clamped(kg, p.ldk, c_next, sd.L, tid);
+            vt.load_clamped(vg, p.ldv, c_next, sd.L, tid);
         }
         __syncthreads();
 

@@ -18,7 +18,8 @@ struct Tile64 {
     static constexpr int ELEMS = 64 * D;         // bf16 elements in the tile
     uint32_t w[4][4];                            // rows x 4 words (8 bf16)
 
-    __device__ __forceinline__ static bool active(int tid) { return tid < ACTIVE; }
+    // every thread of a 256-thread workgroup carries data when D = 128
+    __device__ __forceinline__ static bool active(int tid) { return ACTIVE >= 256 || tid < ACTIVE; }
 
     // Load rows [row0, row0 + 64) of a [tokens][ld] tensor (head offset
     // already applied to `base_ptr`); rows at or past `limit` (>= 1) read as zero.
@@ -30,6 +31,22 @@ struct Tile64 {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             uint4 v = ld16_row(base_ptr, ld, row0 + 4 * g + i, limit, 8 * c);
+            w[i][0] = v.x; w[i][1] = v.y; w[i][2] = v.z; w[i][3] = v.w;
+        }
+    }
+
+    // As load, but rows at or past `limit` hold a copy of row limit - 1 and
+    // must be masked by the consumer.  No select follows the loads, so they
+    // stay in flight until the tile is stored (used for tiles streamed in a
+    // loop, where a wait right after each load would expose its latency).
+    __device__ __forceinline__ void load_clamped(const uint16_t *base_ptr, int64_t ld, int row0,
+                                                 int limit, int tid)
+    {
+        if (!active(tid)) return;
+        const int g = tid / CPR, c = tid % CPR;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint4 v = ld16_clamped(base_ptr, ld, row0 + 4 * g + i, limit, 8 * c);
             w[i][0] = v.x; w[i][1] = v.y; w[i][2] = v.z; w[i][3] = v.w;
         }
     }
