@@ -81,13 +81,20 @@ typedef struct {
     float alpha;                 /* pre-activation factor: SiLU(alpha * q.k)        */
 } sla_problem_t;
 
-/* Operation selector for sla_workspace_size / sla_schedule. */
-enum { SLA_OP_FWD = 0, SLA_OP_BWD = 1 };
+/* Operation selector for sla_workspace_size (FWD, BWD) and the schedule
+ * inspection calls (FWD, BWD, DQ). */
+enum { SLA_OP_FWD = 0, SLA_OP_BWD = 1, SLA_OP_DQ = 2 };
 
 /* Bytes of device workspace sla_fwd (op = SLA_OP_FWD) or sla_bwd
  * (op = SLA_OP_BWD) needs for problem p: the on-device tile schedule and, for
- * the backward, fp32 partial sums of the split global-prefix key tiles.
- * Depends only on host-known fields.  Returns 0 if p is invalid. */
+ * the backward, fp32 partial sums of the split global-prefix key tiles plus,
+ * on the bf16 path with d in {64, 128} and a bounded window (at most 32 key
+ * tiles of 128 per 64-row tile, i.e. about K1 + K2e <= 3.5K), the fp16 dS
+ * blocks of all visited (64-row, 128-key) tiles and an fp16 copy of K, from
+ * which dQ is computed without recomputing S and dP (about
+ * 2 * T * H * 64 * 128 * (slots per row tile / 64) bytes: 1.6 GB for 110K
+ * tokens, 4 heads, K1 = 1024, K2e = 128).  Depends only on host-known fields.
+ * Returns 0 if p is invalid. */
 size_t sla_workspace_size(const sla_problem_t *p, int op);
 
 /* SLA forward (ULTRA-HSTU paper, section 4.2.1 Eq.6-7 with Eq.3):
@@ -95,7 +102,8 @@ size_t sla_workspace_size(const sla_problem_t *p, int op);
  * q, k: [T][H][d_qk] with token strides ldq, ldk; v: [T][H][d_v] (ldv);
  * o: [T][H][d_v] (ldo), fully written for every token (rows of empty
  * sequences do not exist).  bf16 path: bf16 storage, fp32 accumulation,
- * SiLU in fp32, P rounded to bf16 before the P.V product.  f32 path: fp32
+ * SiLU in fp32, P rounded to fp16 (and V converted to fp16) for the P.V
+ * product, so |SiLU(alpha s)| must stay below 65504.  f32 path: fp32
  * throughout.  Only the non-empty tiles of the local band, the global prefix
  * and (for targets) the diagonal are visited.
  * Errors: NULL -> SLA_ERR_NULL; bad sizes/strides -> SLA_ERR_INVALID; head dim
@@ -124,12 +132,14 @@ sla_status_t sla_bwd(const sla_problem_t *p, const void *q, int64_t ldq, const v
 
 /* The backward in stages: sla_bwd(...) equals, on one stream,
  *   sla_bwd_stage(SLA_BWD_PREPARE)  gradient scale + tile schedule (workspace)
- *   sla_bwd_stage(SLA_BWD_DKDV)     dK, dV (key-tile kernel + prefix reduce)
- *   sla_bwd_stage(SLA_BWD_DQ)       dQ (row-tile kernel)
- * with identical arguments and workspace.  DKDV and DQ only read what PREPARE
- * wrote (and write disjoint outputs), so after PREPARE they may run on two
- * streams; a stage ignores the output pointers it does not write (they may be
- * NULL).  SLA_BWD_ALL runs all three. */
+ *   sla_bwd_stage(SLA_BWD_DKDV)     dK, dV (key-tile kernel + prefix reduce);
+ *                                   also stores dS and fp16 K in the workspace
+ *                                   when the workspace holds them
+ *   sla_bwd_stage(SLA_BWD_DQ)       dQ (64-row tiles reading the stored dS, or
+ *                                   128-row tiles recomputing it)
+ * with identical arguments and workspace, in this order: DQ reads what DKDV
+ * stored.  A stage ignores the output pointers it does not write (they may
+ * be NULL).  SLA_BWD_ALL runs all three. */
 enum { SLA_BWD_ALL = 0, SLA_BWD_PREPARE = 1, SLA_BWD_DKDV = 2, SLA_BWD_DQ = 3 };
 sla_status_t sla_bwd_stage(const sla_problem_t *p, int stage, const void *q, int64_t ldq,
                            const void *k, int64_t ldk, const void *v, int64_t ldv,
@@ -139,8 +149,10 @@ sla_status_t sla_bwd_stage(const sla_problem_t *p, int stage, const void *q, int
 
 /* Schedule inspection (the integer part of the hot path, exposed so that it
  * can be checked bit for bit).  Writes the work list the kernels of `op` run:
- *   op = SLA_OP_FWD: row-tile items (forward and dQ kernels)
+ *   op = SLA_OP_FWD: row-tile items (forward, and dQ when it recomputes dS)
  *   op = SLA_OP_BWD: key-tile items (dK/dV kernel)
+ *   op = SLA_OP_DQ:  64-row tile items of dQ from stored dS (FWD layout; key
+ *                    tiles of 128 keys; their order is the dS slot order)
  * as int32 records of SLA_SCHED_RECORD_INTS fields into `records` (device,
  * capacity `capacity` records) and the record count into `*count` (device
  * int32).  Record fields:
@@ -148,7 +160,7 @@ sla_status_t sla_bwd_stage(const sla_problem_t *p, int stage, const void *q, int
  *                                       within sequence b, [lo, hi))
  *   [3] n_ranges (0..3)
  *   [4..9] up to 3 half-open ranges of the other operand, in tokens within b:
- *        FWD: key ranges visited, each a union of whole key tiles of
+ *        FWD, DQ: key ranges visited, each a union of whole key tiles of
  *             sla_schedule_tile(op, 1) keys (last tile clipped at L_b);
  *        BWD: row ranges visited (history rows, target rows), split into the
  *             chunk this record covers;

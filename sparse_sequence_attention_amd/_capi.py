@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "libsla_mi355x.so")
 SLA_OK, SLA_ERR_NULL, SLA_ERR_INVALID, SLA_ERR_UNSUPPORTED, SLA_ERR_WORKSPACE, SLA_ERR_HIP, \
     SLA_ERR_DEVICE = range(7)
 SLA_F32, SLA_BF16 = 0, 1
-SLA_OP_FWD, SLA_OP_BWD = 0, 1
+SLA_OP_FWD, SLA_OP_BWD, SLA_OP_DQ = 0, 1, 2
 SLA_SCHED_RECORD_INTS = 12
 SLA_BWD_ALL, SLA_BWD_PREPARE, SLA_BWD_DKDV, SLA_BWD_DQ = 0, 1, 2, 3
 

@@ -120,15 +120,28 @@ WsLayout layout(const sla_problem_t *p, int op)
     w.part_slots = np_max * chunk_sum;
     w.bwd_items = T / BWD_BN + B + 1 + w.part_slots;
     w.red_items = np_max * B;
+    w.rt_items = T / DS_BM + 2 * B + 1;
     w.sched_off = 0;
-    const size_t sched_bytes = sizeof(int32_t) * (4 * (size_t)(B + 1) + (size_t)B) +
+    const size_t sched_bytes = sizeof(int32_t) * (5 * (size_t)(B + 1) + (size_t)B) +
                                sizeof(float) * (ABSMAX_BLOCKS + 1);
     w.part_off = round_up(sched_bytes, 256);
-    size_t part_bytes = 0;
-    if (op == SLA_OP_BWD)
+    size_t part_bytes = 0, ds_bytes = 0, kh_bytes = 0;
+    w.ds_slots = 0;
+    if (op == SLA_OP_BWD) {
         part_bytes = (size_t)w.part_slots * p->num_heads * BWD_BN * (size_t)(p->d_qk + p->d_v) *
                      sizeof(float);
-    w.total = w.part_off + round_up(part_bytes, 256);
+        // dQ from stored dS: bf16, d in {64, 128}, and a bounded number of key
+        // tiles per row tile (a long local window stores O(L * K1) values)
+        const long long slots = ds_slots_bound(T, p->k1, K2e);
+        if (p->dtype == SLA_BF16 && (p->d_qk == 64 || p->d_qk == 128) && slots <= DS_MAX_SLOTS) {
+            w.ds_slots = (int)slots;
+            ds_bytes = (size_t)w.rt_items * p->num_heads * (size_t)slots * DS_BM * DS_BN * 2;
+            kh_bytes = (size_t)T * p->num_heads * p->d_qk * 2;
+        }
+    }
+    w.ds_off = w.part_off + round_up(part_bytes, 256);
+    w.kh_off = w.ds_off + round_up(ds_bytes, 256);
+    w.total = w.kh_off + round_up(kh_bytes, 256);
     return w;
 }
 
@@ -140,7 +153,7 @@ sla_status_t make_params(const sla_problem_t *p, int op, void *ws, size_t ws_byt
         return fail(SLA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", ws_bytes, w.total);
     if (!aligned16(ws)) return fail(SLA_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
     const int64_t H = p->num_heads;
-    if (w.fwd_items * H > INT32_MAX || w.bwd_items * H > INT32_MAX)
+    if (w.fwd_items * H > INT32_MAX || w.bwd_items * H > INT32_MAX || w.rt_items * H > INT32_MAX)
         return fail(SLA_ERR_UNSUPPORTED, "problem too large for one launch");
     std::memset(&a, 0, sizeof(a));
     a.offsets = p->offsets;
@@ -161,13 +174,20 @@ sla_status_t make_params(const sla_problem_t *p, int op, void *ws, size_t ws_byt
     a.s.red_base = s + 2 * B1;
     a.s.part_base = s + 3 * B1;
     a.s.nch = s + 4 * B1;
-    a.absmax_part = reinterpret_cast<float *>(s + 4 * B1 + p->batch);
+    a.s.rt_base = s + 4 * B1 + p->batch;
+    a.absmax_part = reinterpret_cast<float *>(s + 5 * B1 + p->batch);
     a.grad_scale = a.absmax_part + ABSMAX_BLOCKS;
     a.T = p->total_tokens;
     a.partials = reinterpret_cast<float *>(static_cast<char *>(ws) + w.part_off);
     a.grid_fwd = (int)(w.fwd_items * H);
     a.grid_bwd = (int)(w.bwd_items * H);
     a.grid_red = (int)(w.red_items * H);
+    a.grid_rt = (int)(w.rt_items * H);
+    a.ds_slots = w.ds_slots;
+    if (w.ds_slots > 0) {
+        a.ds = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + w.ds_off);
+        a.kh = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + w.kh_off);
+    }
     return SLA_OK;
 }
 
@@ -201,14 +221,16 @@ size_t sla_workspace_size(const sla_problem_t *p, int op)
 int64_t sla_schedule_capacity(const sla_problem_t *p, int op)
 {
     if (validate_problem(p) != SLA_OK) return -1;
-    const WsLayout w = layout(p, op);
-    return op == SLA_OP_FWD ? w.fwd_items : w.bwd_items;
+    if (op != SLA_OP_FWD && op != SLA_OP_BWD && op != SLA_OP_DQ) return -1;
+    const WsLayout w = layout(p, SLA_OP_FWD);
+    return op == SLA_OP_FWD ? w.fwd_items : (op == SLA_OP_BWD ? w.bwd_items : w.rt_items);
 }
 
 int32_t sla_schedule_tile(int op, int which)
 {
     if (op == SLA_OP_FWD) return which == 0 ? FWD_BM : FWD_BN;
     if (op == SLA_OP_BWD) return which == 0 ? BWD_BN : BWD_BM;
+    if (op == SLA_OP_DQ) return which == 0 ? DS_BM : DS_BN;
     return -1;
 }
 
@@ -217,11 +239,10 @@ sla_status_t sla_schedule(const sla_problem_t *p, int op, int32_t *records, int6
 {
     sla_status_t st = validate_problem(p);
     if (st != SLA_OK) return st;
-    if (op != SLA_OP_FWD && op != SLA_OP_BWD) return fail(SLA_ERR_INVALID, "bad op %d", op);
+    if (op != SLA_OP_FWD && op != SLA_OP_BWD && op != SLA_OP_DQ)
+        return fail(SLA_ERR_INVALID, "bad op %d", op);
     if (!records || !count) return fail(SLA_ERR_NULL, "records or count is NULL");
-    if (capacity < layout(p, op).fwd_items && op == SLA_OP_FWD)
-        return fail(SLA_ERR_INVALID, "capacity below sla_schedule_capacity");
-    if (capacity < layout(p, op).bwd_items && op == SLA_OP_BWD)
+    if (capacity < sla_schedule_capacity(p, op))
         return fail(SLA_ERR_INVALID, "capacity below sla_schedule_capacity");
     AttnParams a;
     if ((st = make_params(p, SLA_OP_FWD, workspace, ws_bytes, a)) != SLA_OK) return st;
@@ -244,7 +265,7 @@ int64_t sla_schedule_host(const sla_problem_t *p, int op, const int64_t *offsets
     hp.num_targets = num_targets_host;
     p = &hp;
     if (validate_problem(p) != SLA_OK) return -1;
-    if (op != SLA_OP_FWD && op != SLA_OP_BWD) {
+    if (op != SLA_OP_FWD && op != SLA_OP_BWD && op != SLA_OP_DQ) {
         fail(SLA_ERR_INVALID, "bad op %d", op);
         return -1;
     }

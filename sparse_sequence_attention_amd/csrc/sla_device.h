@@ -135,9 +135,53 @@ __device__ __forceinline__ bf16x8 scale_bf16x8(const bf16x8 &x, float sc)
     return cvt8(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
 }
 
+// 8 bf16 -> 8 fp16 (exact for |x| in fp16's normal range).
+__device__ __forceinline__ halfx8 bf16x8_to_halfx8(const bf16x8 &x)
+{
+    uint4 u = as_u4(x);
+    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    return cvt8h(bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1]), bf16_lo(w[2]),
+                 bf16_hi(w[2]), bf16_lo(w[3]), bf16_hi(w[3]));
+}
+
 // ---------------------------------------------------------------------------
 // Memory helpers
 // ---------------------------------------------------------------------------
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4_t;
+
+// Workgroup barrier for LDS written with ds_write: waits for this wave's LDS
+// accesses, then s_barrier.  Unlike __syncthreads it does not also wait for
+// the global loads in flight (the prefetch of later steps); the memory
+// clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane j points at 4 consecutive 16-bit values (an 8-byte run) and lane i
+// receives value i % 4 of the runs of lanes i / 4, 4 + i / 4, 8 + i / 4 and
+// 12 + i / 4.  With lane j pointing at run (row r0 + j / 4, columns
+// c0 + 4 * (j % 4) .. + 3) of a row-major [row][col] tile, lane i receives
+// column c0 + i of rows r0 .. r0 + 3: a 4-deep slice of an MFMA operand whose
+// contraction index runs along the tile's rows.
+__device__ __forceinline__ uint2 tr_read_b64(const uint16_t *lds_run)
+{
+    shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t *)lds_run);
+    return __builtin_bit_cast(uint2, v);
+}
+
+// Chunk (16 bytes) of a stored 64-row x 128-key dS block holding lane (kl, hl)'s
+// 8 values of row group qc for the keys of wave wv of the dK/dV kernel: the
+// fp16 operand that kernel feeds its dK product, stored as it is held.  Key
+// kl of the wave, rows 32*(qc/2) + 16*(qc%2) + 4*hl + {0..3, 8..11}.  The
+// lane pairs are interleaved and odd row groups shifted by 128 bytes so that
+// the transposing reads of the dQ kernel hit distinct banks.
+__host__ __device__ inline int ds_frag_chunk(int wv, int qc, int kl, int hl)
+{
+    return (wv * 4 + qc) * 64 + ((2 * kl + hl) ^ (8 * (qc & 1)));
+}
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 __device__ __forceinline__ uint4 ld16_or_zero(const void *p, bool ok)
 {

@@ -30,6 +30,13 @@ constexpr int BWD_CHUNK_TILES = 18;  // target row tiles per chunk of a split pr
 constexpr int BWD_MAX_CHUNKS = 16;   // at most this many chunks per prefix key tile
 constexpr int BWD_MAX_SPLIT_TILES = 4;  // prefix key tiles per sequence that may be split
 constexpr int NUM_XCD = 8;         // MI355X: 8 accelerator complex dies, own L2 each
+// Stored dS (bf16 backward, d in {64, 128}): the dK/dV kernel writes each
+// (64-row tile, 128-key tile) block of dS in fp16, and dQ = dS K reads it back
+// instead of recomputing S, dP and dS.  The blocks of a row tile sit in slots
+// 0..DS_MAX_SLOTS-1, in the order the row tile visits its key tiles.
+constexpr int DS_BM = BWD_BM;      // rows per dS block
+constexpr int DS_BN = BWD_BN;      // keys per dS block
+constexpr int DS_MAX_SLOTS = 32;   // more key tiles per row tile: dQ recomputes instead
 
 // Per-sequence prefix sums written by the schedule kernel (device, int32).
 struct Sched {
@@ -38,6 +45,7 @@ struct Sched {
     int32_t *red_base;   // [B+1] split key tiles to reduce
     int32_t *part_base;  // [B+1] fp32 partial slots
     int32_t *nch;        // [B]   chunks per prefix key tile (1 = unsplit)
+    int32_t *rt_base;    // [B+1] 64-row tiles (stored-dS dQ items, dS block rows)
 };
 
 struct SeqDims {
@@ -154,12 +162,39 @@ struct TileCursor {
         n01 = c0 + c1;
         total = c0 + c1 + c2;
     }
-    // first key of tile t (0 <= t < total)
+    // first key of tile t (0 <= t < total); selects rather than branches
     __host__ __device__ int start(int t, int bn) const
     {
-        return t < n0 ? lo0 + t * bn : (t < n01 ? lo1 + (t - n0) * bn : lo2 + (t - n01) * bn);
+        const bool in0 = t < n0, in1 = t < n01;
+        const int lo = in0 ? lo0 : (in1 ? lo1 : lo2);
+        const int first = in0 ? 0 : (in1 ? n0 : n01);
+        return lo + (t - first) * bn;
     }
 };
+
+// Slot of the key tile starting at key c0 among the tiles of the cursor built
+// from kr (its position in visiting order), or -1 when the tile is not visited.
+__host__ __device__ inline int cursor_slot(const Ranges &kr, int c0, int bn)
+{
+    if (kr.n > 0 && c0 >= kr.lo0 && c0 < kr.hi0) return (c0 - kr.lo0) / bn;
+    const int n0 = kr.n > 0 ? cdiv(kr.hi0 - kr.lo0, bn) : 0;
+    if (kr.n > 1 && c0 >= kr.lo1 && c0 < kr.hi1) return n0 + (c0 - kr.lo1) / bn;
+    const int n01 = n0 + (kr.n > 1 ? cdiv(kr.hi1 - kr.lo1, bn) : 0);
+    if (kr.n > 2 && c0 >= kr.lo2 && c0 < kr.hi2) return n01 + (c0 - kr.lo2) / bn;
+    return -1;
+}
+
+// Upper bound of the key tiles (of DS_BN keys) visited by one 64-row tile:
+// prefix tiles, the band of a history tile (K1 + 63 keys) or of row U (K1 - 1
+// keys), and up to two tiles of a target tile's own rows.  K1 and K2e beyond
+// the longest possible sequence (T tokens) act as T.
+__host__ __device__ inline long long ds_slots_bound(long long T, long long K1, long long K2e)
+{
+    const long long k1 = K1 < T ? K1 : T, k2 = K2e < T ? K2e : T;
+    long long n = (k2 + DS_BN - 1) / DS_BN + (k1 + 63 + DS_BN - 1) / DS_BN + 3;
+    const long long all = (T + DS_BN - 1) / DS_BN;
+    return n < all ? n : all;
+}
 
 // dK/dV items.  Key tiles of bn keys from key 0.  The rows that see the key
 // tile [c0, c1): history rows [c0, U) if the tile holds a global-prefix key,
@@ -294,10 +329,11 @@ __host__ __device__ inline void fill_record(int op, int b, int L, int U, int K1,
 {
     for (int i = 0; i < 12; ++i) rec[i] = 0;
     rec[0] = b;
-    if (op == 0) {
+    if (op == 0 || op == 2) {
+        const int bm = op == 0 ? FWD_BM : DS_BM, bn = op == 0 ? FWD_BN : DS_BN;
         int r0, r1;
-        row_tile(L, U, FWD_BM, li, r0, r1);
-        Ranges kr = fwd_key_ranges(L, U, K1, K2e, r0, r1, FWD_BN);
+        row_tile(L, U, bm, li, r0, r1);
+        Ranges kr = fwd_key_ranges(L, U, K1, K2e, r0, r1, bn);
         rec[1] = r0;
         rec[2] = r1;
         rec[3] = kr.n;
@@ -321,10 +357,12 @@ __host__ __device__ inline void fill_record(int op, int b, int L, int U, int K1,
     }
 }
 
-// Work items of one sequence for op (0 = row tiles, 1 = key tiles).
+// Work items of one sequence for op (0 = row tiles, 1 = key tiles, 2 = 64-row
+// tiles of the stored-dS dQ kernel).
 __host__ __device__ inline int seq_items(int op, int L, int U, int K2e)
 {
     if (op == 0) return row_tiles(L, U, FWD_BM);
+    if (op == 2) return row_tiles(L, U, DS_BM);
     int np, nch;
     return bwd_items(L, U, K2e, BWD_BN, BWD_BM, np, nch);
 }

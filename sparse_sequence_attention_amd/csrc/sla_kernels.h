@@ -30,14 +30,23 @@ struct AttnParams {
     int grid_fwd;           // upper bound of forward / dQ work items (x heads)
     int grid_bwd;           // upper bound of dK/dV work items (x heads)
     int grid_red;           // upper bound of reduce items (x heads)
+    // stored dS (null when dQ recomputes): fp16 dS blocks [64-row tile][head]
+    // [slot][DS_BM x DS_BN] in the dK/dV kernel's fragment order, and an fp16
+    // copy of K [T][H][d]
+    uint16_t *ds;
+    uint16_t *kh;
+    int ds_slots;           // slots per (row tile, head)
+    int grid_rt;            // upper bound of 64-row tiles (x heads)
 };
 
 constexpr int ABSMAX_BLOCKS = 1024;
 
 // Sizes (int32 counts / bytes) of the workspace regions, from host-known data.
 struct WsLayout {
-    size_t sched_off, part_off, total;
+    size_t sched_off, part_off, ds_off, kh_off, total;
     int64_t fwd_items, bwd_items, red_items, part_slots;  // upper bounds (per head)
+    int64_t rt_items;   // upper bound of 64-row tiles (per head)
+    int ds_slots;       // 0: dQ recomputes dS
 };
 
 hipError_t launch_sched(const AttnParams &p, hipStream_t st);
@@ -48,6 +57,7 @@ hipError_t launch_sched_dump(const AttnParams &p, int op, int32_t *records, int6
                              int32_t *count, hipStream_t st);
 hipError_t launch_fwd_bf16(const AttnParams &p, hipStream_t st);
 hipError_t launch_bwd_dkdv_bf16(const AttnParams &p, hipStream_t st);  // + prefix reduce
+// dQ: from the stored dS blocks when p.ds is set, else recomputing S, dP, dS
 hipError_t launch_bwd_dq_bf16(const AttnParams &p, hipStream_t st);
 hipError_t launch_fwd_f32(const AttnParams &p, hipStream_t st);
 hipError_t launch_bwd_dkdv_f32(const AttnParams &p, hipStream_t st);

@@ -19,10 +19,15 @@ __global__ __launch_bounds__(SCHED_THREADS) void sla_sched_kernel(const int64_t 
                                                                   float *grad_scale)
 {
     __shared__ int4 buf[2][SCHED_THREADS];
+    __shared__ int buf2[2][SCHED_THREADS];
     __shared__ int4 carry;
+    __shared__ int carry2;
     __shared__ float red[SCHED_THREADS / 64];
     const int tid = threadIdx.x;
-    if (tid == 0) carry = make_int4(0, 0, 0, 0);
+    if (tid == 0) {
+        carry = make_int4(0, 0, 0, 0);
+        carry2 = 0;
+    }
     if (absmax_part) {
         // gradient scale: the power of two that maps max|dO| into [1, 2)
         float m = 0.0f;
@@ -47,6 +52,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void sla_sched_kernel(const int64_t 
     for (int start = 0; start < B; start += SCHED_THREADS) {
         const int b = start + tid;
         int4 v = make_int4(0, 0, 0, 0);
+        int v2 = 0;
         if (b < B) {
             SeqDims sd = seq_dims<false>(offsets, num_targets, b);
             int np, nch;
@@ -54,33 +60,42 @@ __global__ __launch_bounds__(SCHED_THREADS) void sla_sched_kernel(const int64_t 
             v.y = bwd_items(sd.L, sd.U, k2e, BWD_BN, BWD_BM, np, nch);
             v.z = nch > 1 ? np : 0;
             v.w = nch > 1 ? np * nch : 0;
+            v2 = row_tiles(sd.L, sd.U, DS_BM);
             s.nch[b] = nch;
         }
-        // inclusive Hillis-Steele scan of the four counters
+        // inclusive Hillis-Steele scan of the five counters
         int cur = 0;
         buf[cur][tid] = v;
+        buf2[cur][tid] = v2;
         __syncthreads();
         for (int off = 1; off < SCHED_THREADS; off <<= 1) {
             int4 a = buf[cur][tid];
+            int a2 = buf2[cur][tid];
             if (tid >= off) {
                 int4 c = buf[cur][tid - off];
                 a.x += c.x; a.y += c.y; a.z += c.z; a.w += c.w;
+                a2 += buf2[cur][tid - off];
             }
             buf[cur ^ 1][tid] = a;
+            buf2[cur ^ 1][tid] = a2;
             cur ^= 1;
             __syncthreads();
         }
         int4 inc = buf[cur][tid];
+        int inc2 = buf2[cur][tid];
         int4 c0 = carry;
+        int c02 = carry2;
         if (b < B) {
             s.fwd_base[b] = c0.x + inc.x - v.x;
             s.bwd_base[b] = c0.y + inc.y - v.y;
             s.red_base[b] = c0.z + inc.z - v.z;
             s.part_base[b] = c0.w + inc.w - v.w;
+            s.rt_base[b] = c02 + inc2 - v2;
         }
         __syncthreads();
         if (tid == SCHED_THREADS - 1) {
             carry = make_int4(c0.x + inc.x, c0.y + inc.y, c0.z + inc.z, c0.w + inc.w);
+            carry2 = c02 + inc2;
         }
         __syncthreads();
     }
@@ -90,6 +105,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void sla_sched_kernel(const int64_t 
         s.bwd_base[B] = c.y;
         s.red_base[B] = c.z;
         s.part_base[B] = c.w;
+        s.rt_base[B] = carry2;
     }
 }
 
@@ -145,7 +161,7 @@ __global__ void sla_sched_dump_kernel(const int64_t *offsets, const int32_t *num
                                       int k1, int k2e, Sched s, int op, int32_t *records,
                                       int64_t capacity, int32_t *count)
 {
-    const int32_t *base = op == 0 ? s.fwd_base : s.bwd_base;
+    const int32_t *base = op == 0 ? s.fwd_base : (op == 1 ? s.bwd_base : s.rt_base);
     const int total = base[B];
     const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (r == 0) *count = total;

@@ -88,6 +88,9 @@ SMALL_CASES = [
     ([400, 333], None, 0, 70, 0, 128),           # global prefix only
     ([700, 260], None, FULL_CAUSAL_K1, 0, 0, 128),  # full causal
     ([640, 200], [64, 0], 2, 128, 130, 128),
+    # full causal over 5K tokens: more than 32 key tiles per 64-row tile, so
+    # the bf16 dQ recomputes dS instead of reading it back
+    ([2500, 2600], None, FULL_CAUSAL_K1, 0, 0, 128),
 ]
 
 

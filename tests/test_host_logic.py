@@ -117,6 +117,29 @@ def test_schedule_matches_oracle_tiles(seed):
             assert len(rows) == len(set(rows))
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_stored_ds_rows_match_dkdv_blocks(seed):
+    """The 64-row dQ items that read stored dS visit exactly the (row tile, key
+    tile) blocks the dK/dV items write: both are the non-empty tiles of the
+    mask at 64 rows x 128 keys, and the slot order is the record's range order."""
+    rng = np.random.default_rng(100 + seed)
+    lens, offs, tg = _rand_case(rng)
+    k1 = int(rng.choice([0, 1, 2, 5, 64, 130, 256, 1000]))
+    k2 = int(rng.choice([0, 3, 64, 128, 200]))
+    ctx = int(rng.choice([0, 2, 16, 150]))
+    bm, bn = ops.schedule_tile(C.SLA_OP_DQ, 0), ops.schedule_tile(C.SLA_OP_DQ, 1)
+    assert (bm, bn) == (ops.schedule_tile(C.SLA_OP_BWD, 1), ops.schedule_tile(C.SLA_OP_BWD, 0))
+    rec = ops.sla_schedule_host(offs, tg, op=C.SLA_OP_DQ, heads=1, d=128, k1=k1, k2=k2,
+                                contextual_len=ctx)
+    ref = {tuple(map(int, x)) for x in oracle.tiles(offs, tg, k1, k2, ctx, bm, bn)}
+    assert _fwd_pairs(rec, bn) == ref
+    recb = ops.sla_schedule_host(offs, tg, op=C.SLA_OP_BWD, heads=1, d=128, k1=k1, k2=k2,
+                                 contextual_len=ctx)
+    assert _bwd_pairs(recb, lens, tg, bm) == ref
+    n_rows = sum(-(-(L - t) // bm) + -(-t // bm) for L, t in zip(lens, tg or [0] * len(lens)))
+    assert len(rec) == n_rows
+
+
 def test_schedule_long_sequence_splits_prefix_tiles():
     offs = np.array([0, 16384], np.int64)
     rec = ops.sla_schedule_host(offs, None, op=C.SLA_OP_BWD, heads=4, d=128, k1=1024, k2=128,
