@@ -20,13 +20,13 @@
 // recomputing S and dP.  Global-prefix key tiles are seen by every later row,
 // so they are cut into row chunks whose fp32 partial sums a third kernel adds
 // in chunk order: results are bitwise reproducible.
-#include <type_traits>
-
 #include "sla_device.h"
 #include "sla_kernels.h"
 #include "sla_tiles.h"
 
 namespace sla {
+
+constexpr int DS_SLOT_TAB = 512;  // steps of a dK/dV item whose dS slot is tabulated
 
 // ---------------------------------------------------------------------------
 // dK / dV
@@ -41,6 +41,7 @@ __global__ __launch_bounds__(256, 1) void sla_bwd_dkdv_bf16_kernel(AttnParams p)
     __shared__ __align__(16) uint16_t sdo[2][BM * D];
     __shared__ __align__(16) uint16_t sqt[2][D * BM];
     __shared__ __align__(16) uint16_t sdot[2][D * BM];
+    __shared__ int16_t slot_tab[DS_SLOT_TAB];
 
     const int nrec = p.s.bwd_base[p.B];
     const int item = xcd_remap(blockIdx.x, nrec * p.H);
@@ -109,6 +110,21 @@ __global__ __launch_bounds__(256, 1) void sla_bwd_dkdv_bf16_kernel(AttnParams p)
             m1 = imin(m0 + BM, sd.L);
         }
     };
+    // stored-dS path: the slot of this key tile in the visiting order of the
+    // 64-row tile [m0, m1) that step s covers, tabulated for the first
+    // DS_SLOT_TAB steps before the loop (scalar work kept out of the steps)
+    auto step_slot = [&](int m0, int m1) {
+        const Ranges kr = fwd_key_ranges(sd.L, sd.U, p.k1, p.k2e, m0, m1, DS_BN);
+        return cursor_slot(kr, it.c0, DS_BN);
+    };
+    if (p.ds != nullptr) {
+        for (int st = tid; st < imin(nsteps, DS_SLOT_TAB); st += blockDim.x) {
+            int a0, a1;
+            step_rows(st, a0, a1);
+            slot_tab[st] = (int16_t)step_slot(a0, a1);
+        }
+    }
+
     // rows at or past m1 of a step hold copies of row m1 - 1; such steps are
     // never "full", and the mask removes those rows
     int m0n = 0, m1n = 0;
@@ -137,81 +153,82 @@ __global__ __launch_bounds__(256, 1) void sla_bwd_dkdv_bf16_kernel(AttnParams p)
         }
         __syncthreads();
 
-        // S = Q K^T and dP = dO V^T for two 32-row blocks (rows in the registers)
-        floatx16 sacc[2], pacc[2];
-#pragma unroll
-        for (int qb2 = 0; qb2 < 2; ++qb2) {
-            sacc[qb2] = zero16();
-            pacc[qb2] = zero16();
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                bf16x8 aq = lds_row_chunk<D>(sq[buf], 32 * qb2 + l32, 2 * c + hl);
-                sacc[qb2] = mfma32(aq, kb[c], sacc[qb2]);
-                bf16x8 ag = lds_row_chunk<D>(sdo[buf], 32 * qb2 + l32, 2 * c + hl);
-                pacc[qb2] = mfma32(ag, vb[c], pacc[qb2]);
-            }
-        }
-
         // mask (partial steps only, a workgroup-uniform branch): rows past m1
         // and invisible pairs get s = g = 0, hence P = dS = 0
         const bool full = uniform((m1 == m0 + BM) && (m1 <= sd.U) && key_tile_full &&
                                   (it.c0 + BN - 1 <= m0) &&
                                   ((m1 - 1 - it.c0 < p.k1) || (it.c0 + BN <= p.k2e))) != 0;
-        if (!full) {
-#pragma unroll
-            for (int qb2 = 0; qb2 < 2; ++qb2) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int i = m0 + 32 * qb2 + 8 * (r >> 2) + 4 * hl + (r & 3);
-                    const bool vis = (i < m1) && visible(i, kj, sd.U, p.k1, p.k2e);
-                    sacc[qb2][r] = vis ? sacc[qb2][r] : 0.0f;
-                    pacc[qb2][r] = vis ? pacc[qb2][r] : 0.0f;
-                }
-            }
-        }
-#pragma unroll
-        for (int qb2 = 0; qb2 < 2; ++qb2) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float sv = sacc[qb2][r], g = pacc[qb2][r];
-                float e;
-                const float sg = sigmoid_e(sv, nal2e, e);
-                const float a = sv * sg;                         // SiLU(alpha s) / alpha
-                sacc[qb2][r] = a;
-                pacc[qb2][r] = g * (sg * (1.0f + alpha * a * e));  // G g SiLU'(t)
-            }
-        }
+        // in terms of x = i - kj (element r of row block qb2 has x = x0 + c with
+        // the constant c = 32*qb2 + 8*(r/4) + r%4): rows before m1 of a history
+        // step see the key iff 0 <= x < W, W = m1 - kj, capped at K1 unless kj
+        // is a prefix key; rows of a target step iff x < m1 - kj and (x == 0
+        // or kj lies in row U's view)
+        const int x0 = m0 + 4 * hl - kj;
+        const bool tstep = m0 >= sd.U;
+        int W = m1 - kj;
+        if (!tstep && kj >= p.k2e) W = imin(W, p.k1);
+        const uint32_t Wu = (uint32_t)imax(W, 0);
+        const bool tv = !tstep || ((kj < sd.U) & ((sd.U - kj < p.k1) | (kj < p.k2e)));
 
         // stored-dS path: the slot of this key tile among the key tiles the
         // 64-row tile [m0, m1) visits (the order dQ reads them in)
         uint16_t *dsblk = nullptr;
         if (p.ds != nullptr) {
             const int rt = m0 < sd.U ? m0 / DS_BM : cdiv(sd.U, DS_BM) + (m0 - sd.U) / DS_BM;
-            const Ranges kr = fwd_key_ranges(sd.L, sd.U, p.k1, p.k2e, m0, m1, DS_BN);
-            const int slot = uniform(cursor_slot(kr, it.c0, DS_BN));
+            const int slot = s < DS_SLOT_TAB ? uniform((int)slot_tab[s])
+                                             : uniform(step_slot(m0, m1));
             if (slot >= 0 && slot < p.ds_slots)
                 dsblk = p.ds + (((int64_t)(rt_first + rt) * p.H + h) * p.ds_slots + slot) *
                                    (DS_BM * DS_BN);
         }
 
-        // dV += P^T dO and dK += dS^T Q over four 16-row chunks
+        // per 32-row block (rows in the registers): S = Q K^T, dP = dO V^T,
+        // then P and dS, then dV += P^T dO and dK += dS^T Q over its two
+        // 16-row chunks; one block's S and dP are live at a time
 #pragma unroll
-        for (int qc = 0; qc < 4; ++qc) {
-            const int o = 8 * (qc & 1);
-            const floatx16 &ps = sacc[qc >> 1];
-            const floatx16 &ds = pacc[qc >> 1];
-            halfx8 pa = cvt8h(ps[o], ps[o + 1], ps[o + 2], ps[o + 3], ps[o + 4], ps[o + 5],
-                              ps[o + 6], ps[o + 7]);
-            halfx8 da = cvt8h(ds[o], ds[o + 1], ds[o + 2], ds[o + 3], ds[o + 4], ds[o + 5],
-                              ds[o + 6], ds[o + 7]);
-            if (dsblk != nullptr)
-                *reinterpret_cast<halfx8 *>(dsblk + 8 * ds_frag_chunk(wv, qc, l32, hl)) = da;
+        for (int qb2 = 0; qb2 < 2; ++qb2) {
+            floatx16 sacc = zero16(), pacc = zero16();
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                halfx8 bg = lds_t_chunk_h(sdot[buf], 32 * db + l32, 2 * qc + hl);
-                dvacc[db] = mfma32h(pa, bg, dvacc[db]);
-                halfx8 bq = lds_t_chunk_h(sqt[buf], 32 * db + l32, 2 * qc + hl);
-                dkacc[db] = mfma32h(da, bq, dkacc[db]);
+            for (int c = 0; c < NC; ++c) {
+                bf16x8 aq = lds_row_chunk<D>(sq[buf], 32 * qb2 + l32, 2 * c + hl);
+                sacc = mfma32(aq, kb[c], sacc);
+                bf16x8 ag = lds_row_chunk<D>(sdo[buf], 32 * qb2 + l32, 2 * c + hl);
+                pacc = mfma32(ag, vb[c], pacc);
+            }
+            if (!full) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int x = x0 + 32 * qb2 + 8 * (r >> 2) + (r & 3);
+                    const bool vis = ((uint32_t)x < Wu) & (tv | (x == 0));
+                    sacc[r] = vis ? sacc[r] : 0.0f;
+                    pacc[r] = vis ? pacc[r] : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float sv = sacc[r], g = pacc[r];
+                float e;
+                const float sg = sigmoid_e(sv, nal2e, e);
+                const float a = sv * sg;                       // SiLU(alpha s) / alpha
+                sacc[r] = a;
+                pacc[r] = g * (sg * (1.0f + alpha * a * e));  // G g SiLU'(t)
+            }
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int qc = 2 * qb2 + h2, o = 8 * h2;
+                halfx8 pa = cvt8h(sacc[o], sacc[o + 1], sacc[o + 2], sacc[o + 3], sacc[o + 4],
+                                  sacc[o + 5], sacc[o + 6], sacc[o + 7]);
+                halfx8 da = cvt8h(pacc[o], pacc[o + 1], pacc[o + 2], pacc[o + 3], pacc[o + 4],
+                                  pacc[o + 5], pacc[o + 6], pacc[o + 7]);
+                if (dsblk != nullptr)
+                    *reinterpret_cast<halfx8 *>(dsblk + 8 * ds_frag_chunk(wv, qc, l32, hl)) = da;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    halfx8 bg = lds_t_chunk_h(sdot[buf], 32 * db + l32, 2 * qc + hl);
+                    dvacc[db] = mfma32h(pa, bg, dvacc[db]);
+                    halfx8 bq = lds_t_chunk_h(sqt[buf], 32 * db + l32, 2 * qc + hl);
+                    dkacc[db] = mfma32h(da, bq, dkacc[db]);
+                }
             }
         }
     }
@@ -463,165 +480,9 @@ hipError_t launch_bwd_dkdv_bf16(const AttnParams &p, hipStream_t st)
     }
 }
 
-// ---------------------------------------------------------------------------
-// dQ from the stored dS blocks: dQ_i = (alpha / (N G)) sum_j dS_ij k_j
-// ---------------------------------------------------------------------------
-// Work item: one 64-row tile of one head, 2*(D/32) waves.  It reads, in slot
-// order, the dS block the dK/dV kernel stored for each key tile it visits and
-// the fp16 copy of that key tile (no conversion: both are already fp16).
-// Loads run two steps ahead in registers and are written to the other of two
-// LDS stages after the current stage's products.  Wave w owns rows
-// 32*(w%2) .. +32 and d-columns 32*(w/2) .. +32:
-//   dQ^T (32 d x 32 rows) += K^T (32 d x 128 keys) . dS^T (128 keys x 32 rows)
-// with both operands read by the transposing LDS read, the keys (contraction
-// index) in natural order.
-template <int D>
-__device__ __forceinline__ int kh_swz(int key)  // chunk swizzle of the LDS K tile
-{
-    return (4 * (key & 3)) & (D / 8 - 1);
-}
-
-template <int D>
-__global__ __launch_bounds__(64 * 2 * (D / 32), 1) void sla_bwd_dq_ds_kernel(AttnParams p)
-{
-    constexpr int NT = 64 * 2 * (D / 32);       // threads
-    constexpr int CPR = D / 8;                  // 16-byte chunks per K row
-    constexpr int KCH = DS_BN * CPR;            // chunks per K tile
-    constexpr int SCH = DS_BM * DS_BN / 8;      // chunks per dS block
-    constexpr int KPT = KCH / NT, SPT = SCH / NT, LPT = KPT + SPT;  // loads per thread and step
-    static_assert(KCH % NT == 0 && SCH % NT == 0, "whole load rounds");
-    __shared__ __align__(16) uint16_t lds[2][(KCH + SCH) * 8];
-
-    const int nrec = uniform(p.s.rt_base[p.B]);
-    const int item = xcd_remap(blockIdx.x, nrec * p.H);
-    if (item < 0) return;
-    const int h = item / nrec;
-    const int rec = item - h * nrec;  // global 64-row tile index
-    const int b = find_seq(p.s.rt_base, p.B, rec);
-    const SeqDims sd = seq_dims(p.offsets, p.num_targets, b);
-    int r0, r1;
-    row_tile(sd.L, sd.U, DS_BM, rec - uniform(p.s.rt_base[b]), r0, r1);
-    r0 = uniform(r0);
-    r1 = uniform(r1);
-    const Ranges kr = fwd_key_ranges(sd.L, sd.U, p.k1, p.k2e, r0, r1, DS_BN);
-    const TileCursor cur(kr, DS_BN);
-    const int ntiles = uniform(imin(cur.total, p.ds_slots));  // the slot count bounds cur.total
-
-    const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
-    const int rb = wv & 1, dbk = wv >> 1;
-    const int64_t ldkh = (int64_t)p.H * D;
-    const uint16_t *khg = p.kh + sd.base * ldkh + h * D;
-    const uint16_t *dsg = p.ds + ((int64_t)rec * p.H + h) * ((int64_t)p.ds_slots * DS_BM * DS_BN);
-
-    // loads of step t (clamped to the last tile past the end: L2 hits, so the
-    // pipeline has no special cases).  K tile chunk P = key P / CPR, logical
-    // chunk P % CPR (keys past L read key L - 1: their dS is zero); dS chunk
-    // P as stored.
-    auto load = [&](int t, uint4 (&r)[LPT]) {
-        t = imin(t, ntiles - 1);
-        const int c0 = cur.start(t, DS_BN);
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int P = i * NT + tid;
-            const int row = imin(c0 + P / CPR, sd.L - 1);
-            r[i] = ld16(khg + (int64_t)row * ldkh + 8 * (P % CPR));
-        }
-        const uint16_t *blk = dsg + (int64_t)t * (DS_BM * DS_BN);
-#pragma unroll
-        for (int i = 0; i < SPT; ++i) r[KPT + i] = ld16(blk + 8 * (i * NT + tid));
-    };
-    // into LDS: K chunk (key, c) at physical chunk c ^ kh_swz(key)
-    auto store = [&](const uint4 (&r)[LPT], uint16_t *sb) {
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int P = i * NT + tid;
-            const int key = P / CPR;
-            *reinterpret_cast<uint4 *>(sb + 8 * (key * CPR + ((P % CPR) ^ kh_swz<D>(key)))) = r[i];
-        }
-#pragma unroll
-        for (int i = 0; i < SPT; ++i)
-            *reinterpret_cast<uint4 *>(sb + 8 * (KCH + i * NT + tid)) = r[KPT + i];
-    };
-
-    // per-lane offsets (elements) of the transposing reads for k-chunk 0;
-    // chunk kc adds a constant.  Quarter q = lane / 16 and role j = lane % 16:
-    // read r covers keys 8*(q/2) + 4*r + j/4 of the chunk.
-    const int q = lane >> 4, j = lane & 15;
-    int ds_off[2], kh_off[2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int k0 = 8 * (q >> 1) + 4 * r + (j >> 2);  // key within a 16-key chunk
-        // dS^T operand: rows 32*rb + 16*(q%2) + 4*(j%4) .. +3 of key k0
-        const int x4 = 8 * rb + 4 * (q & 1) + (j & 3);   // 4-row run index 0..15
-        const int qc = 2 * (x4 >> 3) + ((x4 >> 2) & 1), half = (x4 >> 1) & 1, hl = x4 & 1;
-        ds_off[r] = 8 * KCH + 8 * ds_frag_chunk(0, qc, k0, hl) + 4 * half;
-        // K^T operand: d-columns 32*dbk + 16*(q%2) + 4*(j%4) .. +3 of key k0
-        const int dcol = 32 * dbk + 16 * (q & 1) + 4 * (j & 3);
-        kh_off[r] = k0 * D + 8 * ((dcol >> 3) ^ kh_swz<D>(k0)) + (dcol & 7);
-    }
-
-    floatx16 acc = zero16();
-    auto compute = [&](const uint16_t *sb) {
-#pragma unroll
-        for (int kc = 0; kc < DS_BN / 16; ++kc) {
-            // key 16*kc + k0 of the tile: chunk of dK/dV wave kc / 2, key 16*(kc % 2) + k0
-            const int ds_kc = 8 * ds_frag_chunk(kc >> 1, 0, 16 * (kc & 1), 0);
-            const uint2 b0 = tr_read_b64(sb + ds_off[0] + ds_kc);
-            const uint2 b1 = tr_read_b64(sb + ds_off[1] + ds_kc);
-            const uint2 a0 = tr_read_b64(sb + kh_off[0] + 16 * kc * D);
-            const uint2 a1 = tr_read_b64(sb + kh_off[1] + 16 * kc * D);
-            const halfx8 bfr = __builtin_bit_cast(halfx8, make_uint4(b0.x, b0.y, b1.x, b1.y));
-            const halfx8 afr = __builtin_bit_cast(halfx8, make_uint4(a0.x, a0.y, a1.x, a1.y));
-            acc = mfma32h(afr, bfr, acc);
-        }
-    };
-
-    if (ntiles > 0) {
-        uint4 ra[LPT], rbf[LPT];
-        load(0, ra);
-        store(ra, lds[0]);
-        load(1, ra);
-        load(2, rbf);
-        __syncthreads();
-        // even step t: stage 0 holds t, ra holds t + 1, rbf holds t + 2
-        for (int t = 0; t < ntiles; t += 2) {
-            compute(lds[0]);
-            store(ra, lds[1]);      // waits for ra's loads only
-            load(t + 3, ra);
-            lds_barrier();
-            if (t + 1 >= ntiles) break;
-            compute(lds[1]);
-            store(rbf, lds[0]);
-            load(t + 4, rbf);
-            lds_barrier();
-        }
-    }
-
-    // register r of lane l: dQ^T[d = 32*dbk + 8*(r/4) + 4*(l/32) + r%4][row 32*rb + l%32]
-    const int qi = r0 + 32 * rb + (lane & 31), hl = lane >> 5;
-    if (qi < r1) {
-        uint16_t *orow = reinterpret_cast<uint16_t *>(p.dq) + (sd.base + qi) * p.lddq + h * D;
-        const float sc = p.out_scale / *p.grad_scale;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            uint2 v = cvt4_u2(acc[4 * g] * sc, acc[4 * g + 1] * sc, acc[4 * g + 2] * sc,
-                              acc[4 * g + 3] * sc);
-            *reinterpret_cast<uint2 *>(orow + 32 * dbk + 8 * g + 4 * hl) = v;
-        }
-    }
-}
-
 hipError_t launch_bwd_dq_bf16(const AttnParams &p, hipStream_t st)
 {
-    if (p.ds != nullptr) {
-        dim3 grid(p.grid_rt);
-        switch (p.d) {
-        case 64: hipLaunchKernelGGL(sla_bwd_dq_ds_kernel<64>, grid, dim3(256), 0, st, p); break;
-        case 128: hipLaunchKernelGGL(sla_bwd_dq_ds_kernel<128>, grid, dim3(512), 0, st, p); break;
-        default: return hipErrorInvalidValue;
-        }
-        return hipGetLastError();
-    }
+    if (p.ds != nullptr) return launch_bwd_dq_ds_bf16(p, st);
     dim3 grid(p.grid_fwd), block(256);
     switch (p.d) {
     case 32: hipLaunchKernelGGL(sla_bwd_dq_bf16_kernel<32>, grid, block, 0, st, p); break;

@@ -59,6 +59,7 @@ hipError_t launch_fwd_bf16(const AttnParams &p, hipStream_t st);
 hipError_t launch_bwd_dkdv_bf16(const AttnParams &p, hipStream_t st);  // + prefix reduce
 // dQ: from the stored dS blocks when p.ds is set, else recomputing S, dP, dS
 hipError_t launch_bwd_dq_bf16(const AttnParams &p, hipStream_t st);
+hipError_t launch_bwd_dq_ds_bf16(const AttnParams &p, hipStream_t st);  // stored-dS kernel
 hipError_t launch_fwd_f32(const AttnParams &p, hipStream_t st);
 hipError_t launch_bwd_dkdv_f32(const AttnParams &p, hipStream_t st);
 hipError_t launch_bwd_dq_f32(const AttnParams &p, hipStream_t st);
