@@ -87,52 +87,63 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
         }
         __syncthreads();
 
-        // S^T = K Q^T for two 32-key blocks
-        floatx16 sacc[2];
+        // mask (partial tiles only, a workgroup-uniform branch).  Element r of
+        // key block kb has x = qi - j = x0 - c with the constant
+        // c = 32*kb + 8*(r/4) + r%4: a history row sees key j iff x >= 0 and
+        // (x < K1 or j < K2e); keys past L give x < 0.  Tiles wholly inside
+        // or outside the global prefix need one interval test per element.
+        const bool full = uniform((r0 < sd.U) && (c0 + BN <= sd.L) && (c0 + BN - 1 <= r0) &&
+                                  ((r1 - 1 - c0 < p.k1) || (c0 + BN <= p.k2e))) != 0;
+        const int x0 = qi - c0 - 4 * hl;
+        const int mode = uniform(r0 >= sd.U ? 0 : (c0 >= p.k2e ? 1 : (c0 + BN <= p.k2e ? 2 : 0)));
+        const uint32_t k1u = (uint32_t)p.k1;
+
+        // per 32-key block: S^T = K Q^T, mask, P = s * sigmoid(alpha s), then
+        // O^T += V^T P^T over its two 16-key chunks; one block's S is live at a time
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            sacc[kb] = zero16();
+            floatx16 sacc = zero16();
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 bf16x8 a = lds_row_chunk<D>(sk[buf], 32 * kb + l32, 2 * c + hl);
-                sacc[kb] = mfma32(a, qb[c], sacc[kb]);
+                sacc = mfma32(a, qb[c], sacc);
             }
-        }
-
-        // mask (partial tiles only, a workgroup-uniform branch), then
-        // P = s * sigmoid(alpha s)
-        const bool full = uniform((r0 < sd.U) && (c0 + BN <= sd.L) && (c0 + BN - 1 <= r0) &&
-                                  ((r1 - 1 - c0 < p.k1) || (c0 + BN <= p.k2e))) != 0;
-        if (!full) {
+            if (!full) {
+                if (mode == 1) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+                    for (int r = 0; r < 16; ++r) {
+                        const int x = x0 - (32 * kb + 8 * (r >> 2) + (r & 3));
+                        sacc[r] = (uint32_t)x < k1u ? sacc[r] : 0.0f;
+                    }
+                } else if (mode == 2) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int j = c0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-                    sacc[kb][r] = visible(qi, j, sd.U, p.k1, p.k2e) ? sacc[kb][r] : 0.0f;
+                    for (int r = 0; r < 16; ++r) {
+                        const int x = x0 - (32 * kb + 8 * (r >> 2) + (r & 3));
+                        sacc[r] = x >= 0 ? sacc[r] : 0.0f;
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int j = c0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
+                        sacc[r] = visible(qi, j, sd.U, p.k1, p.k2e) ? sacc[r] : 0.0f;
+                    }
                 }
             }
-        }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float s = sacc[kb][r];
-                sacc[kb][r] = s * sigmoid_fast(s, nal2e);
+                const float sv = sacc[r];
+                sacc[r] = sv * sigmoid_fast(sv, nal2e);
             }
-        }
-
-        // O^T += V^T P^T over four 16-key chunks
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-            const floatx16 &src = sacc[kc >> 1];
-            const int o = 8 * (kc & 1);
-            halfx8 pb = cvt8h(src[o + 0], src[o + 1], src[o + 2], src[o + 3], src[o + 4],
-                              src[o + 5], src[o + 6], src[o + 7]);
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int kc = 2 * kb + h2, o = 8 * h2;
+                halfx8 pb = cvt8h(sacc[o + 0], sacc[o + 1], sacc[o + 2], sacc[o + 3], sacc[o + 4],
+                                  sacc[o + 5], sacc[o + 6], sacc[o + 7]);
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                halfx8 a = lds_t_chunk_h(svt[buf], 32 * db + l32, 2 * kc + hl);
-                oacc[db] = mfma32h(a, pb, oacc[db]);
+                for (int db = 0; db < NDB; ++db) {
+                    halfx8 a = lds_t_chunk_h(svt[buf], 32 * db + l32, 2 * kc + hl);
+                    oacc[db] = mfma32h(a, pb, oacc[db]);
+                }
             }
         }
     }
