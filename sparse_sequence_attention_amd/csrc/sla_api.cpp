@@ -135,7 +135,9 @@ WsLayout layout(const sla_problem_t *p, int op)
         const long long slots = ds_slots_bound(T, p->k1, K2e);
         if (p->dtype == SLA_BF16 && (p->d_qk == 64 || p->d_qk == 128) && slots <= DS_MAX_SLOTS) {
             w.ds_slots = (int)slots;
-            ds_bytes = (size_t)w.rt_items * p->num_heads * (size_t)slots * DS_BM * DS_BN * 2;
+            // block 0: zeros (written by the schedule kernel), read by dQ for
+            // key tiles a row half does not visit
+            ds_bytes = ((size_t)w.rt_items * p->num_heads * (size_t)slots + 1) * DS_BM * DS_BN * 2;
             kh_bytes = (size_t)T * p->num_heads * p->d_qk * 2;
         }
     }

@@ -178,8 +178,8 @@ __global__ __launch_bounds__(256, 1) void sla_bwd_dkdv_bf16_kernel(AttnParams p)
             const int slot = s < DS_SLOT_TAB ? uniform((int)slot_tab[s])
                                              : uniform(step_slot(m0, m1));
             if (slot >= 0 && slot < p.ds_slots)
-                dsblk = p.ds + (((int64_t)(rt_first + rt) * p.H + h) * p.ds_slots + slot) *
-                                   (DS_BM * DS_BN);
+                dsblk = p.ds + (1 + ((int64_t)(rt_first + rt) * p.H + h) * p.ds_slots + slot) *
+                                   (DS_BM * DS_BN);  // block 0 is the zero block
         }
 
         // per 32-row block (rows in the registers): S = Q K^T, dP = dO V^T,

@@ -150,13 +150,33 @@ __device__ __forceinline__ halfx8 bf16x8_to_halfx8(const bf16x8 &x)
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4_t;
 
-// Workgroup barrier for LDS written with ds_write: waits for this wave's LDS
-// accesses, then s_barrier.  Unlike __syncthreads it does not also wait for
-// the global loads in flight (the prefetch of later steps); the memory
-// clobber keeps the compiler from moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier()
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Direct HBM -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane
+// l's 16 bytes from `src` land at lds_wave_base + 16 * l.  lds_wave_base must
+// be the same in every lane of the wave.  Completion is tracked by vmcnt only:
+// wait with vm_wait before the barrier that publishes the data.
+__device__ __forceinline__ void gl_lds16(const void *src, uint16_t *lds_wave_base)
 {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)lds_wave_base, 16, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void vm_wait()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier for LDS filled by DMA only, without the memory fence of
+// __syncthreads: the fence would make every wave also wait for the DMA of
+// later stages in flight.  The caller waits (vm_wait) for the DMA it
+// publishes; the memory clobber keeps the compiler from moving LDS accesses
+// across the barrier.
+__device__ __forceinline__ void barrier_lds_dma()
+{
+    asm volatile("s_barrier" ::: "memory");
 }
 
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,

@@ -176,12 +176,15 @@ struct TileCursor {
 // from kr (its position in visiting order), or -1 when the tile is not visited.
 __host__ __device__ inline int cursor_slot(const Ranges &kr, int c0, int bn)
 {
-    if (kr.n > 0 && c0 >= kr.lo0 && c0 < kr.hi0) return (c0 - kr.lo0) / bn;
-    const int n0 = kr.n > 0 ? cdiv(kr.hi0 - kr.lo0, bn) : 0;
-    if (kr.n > 1 && c0 >= kr.lo1 && c0 < kr.hi1) return n0 + (c0 - kr.lo1) / bn;
-    const int n01 = n0 + (kr.n > 1 ? cdiv(kr.hi1 - kr.lo1, bn) : 0);
-    if (kr.n > 2 && c0 >= kr.lo2 && c0 < kr.hi2) return n01 + (c0 - kr.lo2) / bn;
-    return -1;
+    // selects, not branches (ranges past n are empty: lo = hi = 0)
+    const bool in0 = (c0 >= kr.lo0) & (c0 < kr.hi0);
+    const bool in1 = (c0 >= kr.lo1) & (c0 < kr.hi1);
+    const bool in2 = (c0 >= kr.lo2) & (c0 < kr.hi2);
+    const int n0 = (kr.hi0 - kr.lo0 + bn - 1) / bn;
+    const int n01 = n0 + (kr.hi1 - kr.lo1 + bn - 1) / bn;
+    const int lo = in0 ? kr.lo0 : (in1 ? kr.lo1 : kr.lo2);
+    const int first = in0 ? 0 : (in1 ? n0 : n01);
+    return (in0 | in1 | in2) ? first + (c0 - lo) / bn : -1;
 }
 
 // Upper bound of the key tiles (of DS_BN keys) visited by one 64-row tile:

@@ -30,9 +30,9 @@ struct AttnParams {
     int grid_fwd;           // upper bound of forward / dQ work items (x heads)
     int grid_bwd;           // upper bound of dK/dV work items (x heads)
     int grid_red;           // upper bound of reduce items (x heads)
-    // stored dS (null when dQ recomputes): fp16 dS blocks [64-row tile][head]
-    // [slot][DS_BM x DS_BN] in the dK/dV kernel's fragment order, and an fp16
-    // copy of K [T][H][d]
+    // stored dS (null when dQ recomputes): a zero block, then the fp16 dS
+    // blocks [64-row tile][head][slot][DS_BM x DS_BN] in the dK/dV kernel's
+    // fragment order; and an fp16 copy of K [T][H][d]
     uint16_t *ds;
     uint16_t *kh;
     int ds_slots;           // slots per (row tile, head)

@@ -16,8 +16,13 @@ __global__ __launch_bounds__(SCHED_THREADS) void sla_sched_kernel(const int64_t 
                                                                   const int32_t *num_targets,
                                                                   int B, int k2e, Sched s,
                                                                   const float *absmax_part,
-                                                                  float *grad_scale)
+                                                                  float *grad_scale,
+                                                                  uint4 *zero_block)
 {
+    // the stored-dS zero block (DS_BM x DS_BN fp16 = 1024 x 16 bytes)
+    if (zero_block != nullptr)
+        for (int i = threadIdx.x; i < DS_BM * DS_BN / 8; i += SCHED_THREADS)
+            zero_block[i] = make_uint4(0u, 0u, 0u, 0u);
     __shared__ int4 buf[2][SCHED_THREADS];
     __shared__ int buf2[2][SCHED_THREADS];
     __shared__ int4 carry;
@@ -113,7 +118,7 @@ hipError_t launch_sched(const AttnParams &p, hipStream_t st)
 {
     hipLaunchKernelGGL(sla_sched_kernel, dim3(1), dim3(SCHED_THREADS), 0, st, p.offsets,
                        p.num_targets, p.B, p.k2e, p.s, (const float *)p.absmax_part,
-                       p.grad_scale);
+                       p.grad_scale, reinterpret_cast<uint4 *>(p.ds));
     return hipGetLastError();
 }
 
