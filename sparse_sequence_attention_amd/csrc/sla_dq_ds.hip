@@ -14,15 +14,16 @@ namespace sla {
 // dQ from the stored dS blocks: dQ_i = (alpha / (N G)) sum_j dS_ij k_j
 // ---------------------------------------------------------------------------
 // Work item: one 128-row tile of one head (the forward's row tiles: its two
-// 64-row halves are the dS block rows), 8 waves.  Step t visits the t-th key
-// tile of the 128-row tile (the union of the halves' key tiles) and reads
-// the fp16 K tile and each half's stored dS block for it; a half that does
-// not visit that key tile reads the zero block instead, and so do steps past
-// the end, so every step does the same work.  The data is copied HBM -> LDS
-// by the DMA path one step ahead into the other of two stages; with at most
-// eight DMA loads per thread and stage the compiler keeps exact wait counts.
+// 64-row halves are the dS block rows), 8 waves, two workgroups per CU.  Step
+// t covers half t%2 (64 keys) of the (t/2)-th key tile of the 128-row tile
+// (the union of the halves' key tiles): the fp16 K rows and each half's
+// stored dS for those keys.  A half that does not visit that key tile reads
+// the zero block instead, and so do steps past the end, so every step does
+// the same work.  The data is copied HBM -> LDS by the DMA path one step
+// ahead into the other of two stages; with at most eight DMA loads per
+// thread and stage the compiler keeps exact wait counts.
 // Wave w owns rows 32*(w%4) .. +32 and d-columns (D/2)*(w/4) .. +D/2:
-//   dQ^T (d x 32 rows) += K^T (d x 128 keys) . dS^T (128 keys x 32 rows)
+//   dQ^T (d x 32 rows) += K^T (d x 64 keys) . dS^T (64 keys x 32 rows)
 // with both operands read by the transposing LDS read, keys (the
 // contraction index) in natural order.
 template <int D>
@@ -35,20 +36,21 @@ template <int N>
 using stage_t = std::integral_constant<int, N>;
 
 constexpr int DQ_THREADS = 512;
+constexpr int DQ_KEYS = DS_BN / 2;  // keys per step
 
 template <int D>
-__global__ __launch_bounds__(DQ_THREADS, 1) void sla_bwd_dq_ds_kernel(AttnParams p)
+__global__ __launch_bounds__(DQ_THREADS, 2) void sla_bwd_dq_ds_kernel(AttnParams p)
 {
     constexpr int NT = DQ_THREADS;
     constexpr int CPR = D / 8;                  // 16-byte chunks per K row
-    constexpr int KCH = DS_BN * CPR;            // chunks per K tile
-    constexpr int BCH = DS_BM * DS_BN / 8;      // chunks per dS block
-    constexpr int SCH = 2 * BCH;                // the two halves' blocks
+    constexpr int KCH = DQ_KEYS * CPR;          // chunks of K per step
+    constexpr int HCH = DS_BM * DQ_KEYS / 8;    // chunks of one half block (64 rows x 64 keys)
+    constexpr int SCH = 2 * HCH;                // both row halves
     constexpr int KPT = KCH / NT, SPT = SCH / NT;  // DMA loads per thread and step
     constexpr int NDBW = D / 64;                // 32-wide d blocks per wave
     static_assert(KCH % NT == 0 && SCH % NT == 0, "whole DMA rounds");
     static_assert(KPT + SPT <= 8, "at most 8 DMA loads per thread and stage");
-    // one array per stage: K tile, then the two dS blocks
+    // one array per stage: K rows, then the two halves' dS
     __shared__ __align__(16) uint16_t st0[(KCH + SCH) * 8], st1[(KCH + SCH) * 8];
 
     const int nrec = uniform(p.s.fwd_base[p.B]);
@@ -68,6 +70,7 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void sla_bwd_dq_ds_kernel(AttnParams
     const Ranges kr1 = fwd_key_ranges(sd.L, sd.U, p.k1, p.k2e, rh, r1, DS_BN);  // empty if rh == r1
     const TileCursor cur(kr, DS_BN);
     const int ntiles = uniform(cur.total);
+    const int nsteps = 2 * ntiles;
     // 64-row tile index of the first half (history halves from 0, targets from U)
     const int rt0 = uniform(p.s.rt_base[b]) +
                     (r0 < sd.U ? r0 / DS_BM : cdiv(sd.U, DS_BM) + (r0 - sd.U) / DS_BM);
@@ -99,28 +102,32 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void sla_bwd_dq_ds_kernel(AttnParams
     };
     auto dst = [&](auto S) -> uint16_t * { return kst(S) + KCH * 8; };
 
-    // DMA of step t (t >= ntiles: the last key tile, with zero dS): K tile
-    // chunk P (key P / CPR, physical chunk P % CPR) holds logical chunk
-    // (P % CPR) ^ kh_swz(key), keys past L read key L - 1 (their dS is zero);
-    // dS chunks 0..BCH-1 from half 0's block, BCH.. from half 1's
+    // DMA of step t (t >= nsteps: the last keys again, with zero dS): K row
+    // chunk P (key P / CPR of the step, physical chunk P % CPR) holds logical
+    // chunk (P % CPR) ^ kh_swz(key), keys past L read key L - 1 (their dS is
+    // zero); dS chunks 0..HCH-1 from half 0's block, HCH.. from half 1's, each
+    // the key half t%2 of the stored block (the dK/dV kernel stores its waves'
+    // 32-key fragments one after another, so a key half is contiguous)
     auto issue = [&](int t, auto S) {
-        const int tt = imin(t, ntiles - 1);
-        const int c0 = cur.start(tt, DS_BN);
-        const uint16_t *b0 = p.ds + BLK * block_of(0, kr0, c0, t < ntiles);
-        const uint16_t *b1 = p.ds + BLK * block_of(1, kr1, c0, t < ntiles);
+        const int tt = imin(t, nsteps - 1);
+        const int c0 = cur.start(tt >> 1, DS_BN);
+        const int kh = tt & 1;
+        const bool live = t < nsteps;
+        const uint16_t *b0 = p.ds + BLK * block_of(0, kr0, c0, live) + 8 * HCH * kh;
+        const uint16_t *b1 = p.ds + BLK * block_of(1, kr1, c0, live) + 8 * HCH * kh;
         uint16_t *ks = kst(S), *ds = dst(S);
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int P = i * NT + wv * 64 + lane;
             const int key = P / CPR;
             const int c = (P % CPR) ^ kh_swz<D>(key);
-            const int row = imin(c0 + key, sd.L - 1);
+            const int row = imin(c0 + DQ_KEYS * kh + key, sd.L - 1);
             gl_lds16(khg + (int64_t)row * ldkh + 8 * c, ks + (i * NT + wv * 64) * 8);
         }
 #pragma unroll
         for (int i = 0; i < SPT; ++i) {
             const int P = i * NT + wv * 64 + lane;  // uniform half per DMA round
-            const uint16_t *src = (i * NT < BCH) ? b0 + 8 * P : b1 + 8 * (P - BCH);
+            const uint16_t *src = (i * NT < HCH) ? b0 + 8 * P : b1 + 8 * (P - HCH);
             gl_lds16(src, ds + (i * NT + wv * 64) * 8);
         }
     };
@@ -134,10 +141,10 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void sla_bwd_dq_ds_kernel(AttnParams
     for (int r = 0; r < 2; ++r) {
         const int k0 = 8 * (q >> 1) + 4 * r + (j >> 2);  // key within a 16-key chunk
         // dS^T operand: rows 32*(rb%2) + 16*(q%2) + 4*(j%4) .. +3 of key k0 in
-        // the block of half rb / 2
+        // the half block of row half rb / 2
         const int x4 = 8 * (rb & 1) + 4 * (q & 1) + (j & 3);  // 4-row run index 0..15
         const int qc = 2 * (x4 >> 3) + ((x4 >> 2) & 1), half = (x4 >> 1) & 1, hl = x4 & 1;
-        ds_off[r] = 8 * ((rb >> 1) * BCH + ds_frag_chunk(0, qc, k0, hl)) + 4 * half;
+        ds_off[r] = 8 * ((rb >> 1) * HCH + ds_frag_chunk(0, qc, k0, hl)) + 4 * half;
         // K^T operand: d-columns 32*db' + 16*(q%2) + 4*(j%4) .. +3 of key k0
 #pragma unroll
         for (int db = 0; db < NDBW; ++db) {
@@ -161,8 +168,8 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void sla_bwd_dq_ds_kernel(AttnParams
         __builtin_amdgcn_sched_barrier(0);  // keep the refill ahead of this step's reads
         const uint16_t *ks = kst(S), *dss = dst(S);
 #pragma unroll
-        for (int kc = 0; kc < DS_BN / 16; ++kc) {
-            // key 16*kc + k0 of the tile: chunk of dK/dV wave kc / 2, key 16*(kc % 2) + k0
+        for (int kc = 0; kc < DQ_KEYS / 16; ++kc) {
+            // key 16*kc + k0 of the step: 32-key fragment kc / 2, key 16*(kc % 2) + k0
             const int ds_kc = 8 * ds_frag_chunk(kc >> 1, 0, 16 * (kc & 1), 0);
             const uint2 b0 = tr_read_b64(dss + ds_off[0] + ds_kc);
             const uint2 b1 = tr_read_b64(dss + ds_off[1] + ds_kc);
@@ -177,9 +184,9 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void sla_bwd_dq_ds_kernel(AttnParams
         }
     };
 
-    if (ntiles > 0) {
+    if (nsteps > 0) {
         issue(0, stage_t<0>{});
-        for (int t = 0; t < ntiles; t += 2) {
+        for (int t = 0; t < nsteps; t += 2) {
             step(t, stage_t<0>{});
             step(t + 1, stage_t<1>{});
         }
