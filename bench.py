@@ -42,11 +42,63 @@ def parse():
     ap.add_argument("--cpu-sample-len", type=int, default=16384)
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_long_16k.json"),
                     help="per-kernel HBM bytes measured with rocprofv3 --pmc (optional)")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="after the timed steps, run a plain fp32 negation of 256 MiB (read and "
+                         "written once) whose FETCH_SIZE / WRITE_SIZE calibrate the counters")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU run: read the rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE csv "
+                         "output of a --calibration-copy run and write --traffic")
     return ap.parse_args()
+
+
+# kernels whose HBM traffic the bench line reports, by the name rocprofv3 gives them
+PMC_KERNELS = {"fwd": "sla_fwd_bf16_kernel<128>", "bwd_dkdv": "sla_bwd_dkdv_bf16_kernel<128",
+               "bwd_dq": "sla_bwd_dq_ds_kernel<128>"}
+CALIB_BYTES = 256 * 1024 * 1024
+CALIB_NAME = "neg_kernel_cuda"
+
+
+def summarize_pmc(fetch_dir, write_dir, out):
+    """Per-dispatch HBM bytes of the SLA kernels from FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch), each scaled so that the calibration negation of
+    256 MiB reads and writes exactly 256 MiB."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024)
+        return vals
+
+    res = {"calibration": {"kernel": "torch.neg of 256 MiB fp32", "bytes": CALIB_BYTES}}
+    for counter, d, key in (("FETCH_SIZE", fetch_dir, "fetch"), ("WRITE_SIZE", write_dir, "write")):
+        vals = per_kernel(d, counter)
+        cal = [v for k, vs in vals.items() if CALIB_NAME in k for v in vs]
+        if not cal:
+            raise SystemExit(f"no calibration dispatch in {d}")
+        factor = CALIB_BYTES / (sum(cal) / len(cal))
+        res["calibration"][f"{key}_scale"] = round(factor, 4)
+        for short, name in PMC_KERNELS.items():
+            vs = [v for k, vl in vals.items() if name in k for v in vl]
+            if vs:
+                res.setdefault(short, {})[f"{key}_bytes"] = int(factor * sum(vs) / len(vs))
+    for short in PMC_KERNELS:
+        if short in res and "fetch_bytes" in res[short] and "write_bytes" in res[short]:
+            res[short]["hbm_bytes"] = res[short]["fetch_bytes"] + res[short]["write_bytes"]
+    with open(out, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res))
 
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the SLA hot path "
               "shards by sequence with no exchange, so a multi-GPU figure is one GPU's "
@@ -101,6 +153,13 @@ def main():
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if args.calibration_copy:
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     ms_step = sum(events[i][0].elapsed_time(events[i][4]) for i in range(args.steps)) / args.steps
     phase = {name: float(np.mean([events[i][a].elapsed_time(events[i][b])
                                   for i in range(args.steps)]))
@@ -119,7 +178,7 @@ def main():
     traffic = None
     if os.path.exists(args.traffic):
         with open(args.traffic) as f:
-            traffic = json.load(f).get(dom)
+            traffic = json.load(f).get(dom, {}).get("hbm_bytes")
 
     line = {
         "metric": "SLA fwd+bwd useful TFLOP/s & tokens/s at L=16K; % of bf16 MFMA peak",
