@@ -115,9 +115,12 @@ __device__ __forceinline__ float sigmoid_fast(float s, float neg_alpha_log2e)
 }
 
 // sigma and e = exp(-alpha s); 1 - sigma = e * sigma without cancellation.
+// The exponent is capped at 2^100 so that e * sigma stays finite for very
+// negative alpha s (where sigma and SiLU' are 0 to fp32 precision anyway);
+// uncapped, e = inf and sigma = 0 would make e * sigma a NaN.
 __device__ __forceinline__ float sigmoid_e(float s, float neg_alpha_log2e, float &e)
 {
-    e = __builtin_amdgcn_exp2f(s * neg_alpha_log2e);
+    e = __builtin_amdgcn_exp2f(fminf(s * neg_alpha_log2e, 100.0f));
     return __builtin_amdgcn_rcpf(1.0f + e);
 }
 

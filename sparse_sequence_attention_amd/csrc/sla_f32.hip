@@ -29,7 +29,9 @@ __device__ __forceinline__ float silu_f32(float t) { return t / (1.0f + expf(-t)
 // that no cancellation occurs when sigma is close to 1.
 __device__ __forceinline__ float dsilu_f32(float t)
 {
-    const float e = expf(-t);
+    // e capped at exp(80): for t < -80, SiLU'(t) is 0 to fp32 precision, and
+    // an infinite e would turn e * sg into a NaN
+    const float e = expf(fminf(-t, 80.0f));
     const float sg = 1.0f / (1.0f + e);
     return sg * (1.0f + t * (e * sg));
 }

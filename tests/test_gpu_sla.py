@@ -129,6 +129,39 @@ def test_bwd_small(case, dtype):
     chk(_np(dv), rv, "dV")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_large_logits_stay_finite(dtype):
+    """Q and K scaled up so that |s| reaches a few hundred: SiLU and SiLU' of
+    very negative arguments underflow to 0 instead of producing NaNs."""
+    w = make_sla_workload("jagged_2k", seed=31, lengths=[300, 200], heads=2, d=64, k1=64, k2=8,
+                          contextual_len=2, max_seq_len=300, dtype=dtype, with_dout=True)
+    # fp32 keeps its 1e-5 bound only while rounding of s stays small: a milder
+    # scale there, still past the range where exp(-s) overflows fp32 (|s| > 88)
+    scale = 8.0 if dtype == "bf16" else 4.0
+    for a in (w.q, w.k):
+        a *= scale
+    if dtype == "bf16":
+        from synthetic import bf16_round_f32
+        w.q[...] = bf16_round_f32(w.q)
+        w.k[...] = bf16_round_f32(w.k)
+    _print_case(f"large logits {dtype}", w)
+    q, k, v, do, offs, tgd = _dev(w)
+    o = sla.sla_fwd(q, k, v, offs, tgd, **_kw(w))
+    dq, dk, dv = sla.sla_bwd(q, k, v, do, offs, tgd, **_kw(w))
+    torch.cuda.synchronize()
+    s_max = float(np.abs(np.einsum("thd,shd->hts", w.q[:300].astype(np.float64),
+                                   w.k[:300].astype(np.float64))).max())
+    assert s_max > 100.0, s_max
+    ro = oracle.sla_fwd(w.q, w.k, w.v, w.offsets, w.num_targets, w.k1, w.k2, w.contextual_len,
+                        w.max_seq_len)
+    rq, rk, rv = oracle.sla_bwd(w.q, w.k, w.v, w.dout, w.offsets, w.num_targets, w.k1, w.k2,
+                                w.contextual_len, w.max_seq_len)
+    chk = assert_close_bf16 if dtype == "bf16" else assert_close_f32
+    for name, g, r in (("O", o, ro), ("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        assert torch.isfinite(g.float()).all(), name
+        chk(_np(g), r, name)
+
+
 def test_alpha_and_strided_views():
     """alpha != 1 and Q/K/V as column blocks of one fused buffer."""
     lens = [300, 77]
