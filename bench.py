@@ -171,8 +171,11 @@ def main():
     value = useful / (ms_step * 1e-3) / 1e12
     tokens_s = w.total_tokens / (ms_step * 1e-3)
     # algorithmic MFMA work of each kernel (per launch): forward S and P.V; dK/dV
-    # kernel S, dP, dV, dK; dQ kernel S, dP, dQ
-    kernel_flops = {"fwd": pairs * 4 * d, "bwd_dkdv": pairs * 8 * d, "bwd_dq": pairs * 6 * d}
+    # kernel S, dP, dV, dK; dQ kernel dS.K when it reads the stored dS, else
+    # S, dP, dQ
+    dq_stored = sla.bwd_dq_mode(p) == 1
+    kernel_flops = {"fwd": pairs * 4 * d, "bwd_dkdv": pairs * 8 * d,
+                    "bwd_dq": pairs * (2 if dq_stored else 6) * d}
     dom = max(kernel_flops, key=lambda n: phase[n])
     achieved = kernel_flops[dom] / (phase[dom] * 1e-3) / 1e12
     traffic = None

@@ -97,6 +97,14 @@ enum { SLA_OP_FWD = 0, SLA_OP_BWD = 1, SLA_OP_DQ = 2 };
  * Returns 0 if p is invalid. */
 size_t sla_workspace_size(const sla_problem_t *p, int op);
 
+/* Which dQ algorithm sla_bwd runs for problem p: 1 = dQ = dS.K from the fp16
+ * dS blocks the dK/dV stage stores in the workspace (bf16, d in {64, 128},
+ * at most 32 key tiles of 128 per 64-row tile), 0 = dQ recomputes S and dP
+ * from Q, K, V and dO.  Both give the gradient of the forward above within
+ * the bf16 tolerance; with 1, SLA_BWD_DQ must follow SLA_BWD_DKDV on the same
+ * workspace.  Returns -1 if p is invalid.  Depends only on host-known fields. */
+int sla_bwd_dq_mode(const sla_problem_t *p);
+
 /* SLA forward (ULTRA-HSTU paper, section 4.2.1 Eq.6-7 with Eq.3):
  *   O[i] = (1/N) * sum_{j visible from i} SiLU(alpha * q_i . k_j) * v_j
  * q, k: [T][H][d_qk] with token strides ldq, ldk; v: [T][H][d_v] (ldv);

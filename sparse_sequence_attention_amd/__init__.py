@@ -4,12 +4,12 @@ layer around it and attention truncation, as hand-written HIP kernels behind a
 C ABI (include/sla.h).  This package is the Python binding of that library.
 """
 from ._capi import (  # noqa: F401
-    SLAError, SLA_OP_FWD, SLA_OP_BWD, SLA_SCHED_RECORD_INTS, SLA_BWD_ALL, SLA_BWD_PREPARE,
+    SLAError, SLA_OP_FWD, SLA_OP_BWD, SLA_OP_DQ, SLA_SCHED_RECORD_INTS, SLA_BWD_ALL, SLA_BWD_PREPARE,
     SLA_BWD_DKDV, SLA_BWD_DQ,
 )
 from .config import STUConfig  # noqa: F401
 from .ops import (  # noqa: F401
     sla_fwd, sla_bwd, sla_attention, sla_schedule, sla_schedule_host, schedule_tile, count_pairs_host,
-    stu_layer_fwd, stu_truncate, make_problem, workspace_size,
+    stu_layer_fwd, stu_truncate, make_problem, workspace_size, bwd_dq_mode,
 )
 from .stack import STULayerWeights, stu_stack_fwd  # noqa: F401

@@ -21,7 +21,7 @@ SLA_BWD_ALL, SLA_BWD_PREPARE, SLA_BWD_DKDV, SLA_BWD_DQ = 0, 1, 2, 3
 
 # every symbol include/sla.h declares
 EXPORTS = (
-    "sla_workspace_size", "sla_fwd", "sla_bwd", "sla_bwd_stage", "sla_schedule_capacity", "sla_schedule_tile",
+    "sla_workspace_size", "sla_bwd_dq_mode", "sla_fwd", "sla_bwd", "sla_bwd_stage", "sla_schedule_capacity", "sla_schedule_tile",
     "sla_schedule", "sla_schedule_host", "sla_count_pairs_host", "stu_layer_workspace_size", "stu_layer_fwd",
     "stu_truncate", "sla_status_string", "sla_last_error",
 )
@@ -74,6 +74,8 @@ def load(path: str = LIB_PATH):
         PP = ctypes.POINTER(SLAProblem)
         lib.sla_workspace_size.argtypes = [PP, ctypes.c_int]
         lib.sla_workspace_size.restype = sz
+        lib.sla_bwd_dq_mode.argtypes = [PP]
+        lib.sla_bwd_dq_mode.restype = ctypes.c_int
         lib.sla_fwd.argtypes = [PP, P, i64, P, i64, P, i64, P, i64, P, sz, P]
         lib.sla_fwd.restype = ctypes.c_int
         lib.sla_bwd.argtypes = [PP, P, i64, P, i64, P, i64, P, i64, P, i64, P, i64, P, i64, P, sz,

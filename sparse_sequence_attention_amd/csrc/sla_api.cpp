@@ -220,6 +220,12 @@ size_t sla_workspace_size(const sla_problem_t *p, int op)
     return layout(p, op).total;
 }
 
+int sla_bwd_dq_mode(const sla_problem_t *p)
+{
+    if (validate_problem(p) != SLA_OK) return -1;
+    return layout(p, SLA_OP_BWD).ds_slots > 0 ? 1 : 0;
+}
+
 int64_t sla_schedule_capacity(const sla_problem_t *p, int op)
 {
     if (validate_problem(p) != SLA_OK) return -1;

@@ -61,6 +61,11 @@ def workspace_size(p: C.SLAProblem, op: int) -> int:
     return int(C.load().sla_workspace_size(ctypes.byref(p), op))
 
 
+def bwd_dq_mode(p: C.SLAProblem) -> int:
+    """1 if the backward computes dQ from stored dS blocks, 0 if it recomputes them."""
+    return int(C.load().sla_bwd_dq_mode(ctypes.byref(p)))
+
+
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
     if ws is not None and ws.numel() * ws.element_size() >= nbytes:
         return ws

@@ -218,6 +218,27 @@ def test_workspace_size_is_host_only(lib):
     assert lib.sla_workspace_size(None, C.SLA_OP_FWD) == 0
 
 
+def test_bwd_dq_mode(lib):
+    # stored dS: bf16, d in {64, 128} and at most 32 key tiles per 64-row tile
+    big = dict(batch=8, total_tokens=106496, k1=1024, k2=128, ctx=16)
+    assert lib.sla_bwd_dq_mode(ctypes.byref(_problem(**big))) == 1
+    assert lib.sla_bwd_dq_mode(ctypes.byref(_problem(d=64, **big))) == 1
+    assert lib.sla_bwd_dq_mode(ctypes.byref(_problem(d=32, **big))) == 0
+    assert lib.sla_bwd_dq_mode(ctypes.byref(_problem(dtype=C.SLA_F32, **big))) == 0
+    # full causal over 5000 tokens: 40 key tiles per row tile -> recompute
+    full = dict(batch=1, total_tokens=5000, k1=2**31 - 1, k2=0)
+    assert lib.sla_bwd_dq_mode(ctypes.byref(_problem(**full))) == 0
+    assert lib.sla_bwd_dq_mode(ctypes.byref(_problem(d=48, dv=48))) == -1
+    assert lib.sla_bwd_dq_mode(None) == -1
+    # the stored blocks are part of the backward workspace
+    p1, p0 = _problem(**big), _problem(dtype=C.SLA_F32, **big)
+    extra = lib.sla_workspace_size(ctypes.byref(p1), C.SLA_OP_BWD) - \
+        lib.sla_workspace_size(ctypes.byref(p1), C.SLA_OP_FWD)
+    extra0 = lib.sla_workspace_size(ctypes.byref(p0), C.SLA_OP_BWD) - \
+        lib.sla_workspace_size(ctypes.byref(p0), C.SLA_OP_FWD)
+    assert extra - extra0 >= 106496 * 4 * 128 * 2  # at least the fp16 copy of K
+
+
 def test_bwd_and_layer_argument_errors(lib):
     p = _problem()
     st = lib.sla_bwd(ctypes.byref(p), FAKE, 512, FAKE, 512, FAKE, 512, None, 512, FAKE, 512,
