@@ -20,6 +20,8 @@
 // recomputing S and dP.  Global-prefix key tiles are seen by every later row,
 // so they are cut into row chunks whose fp32 partial sums a third kernel adds
 // in chunk order: results are bitwise reproducible.
+#include <type_traits>
+
 #include "sla_device.h"
 #include "sla_kernels.h"
 #include "sla_tiles.h"
@@ -31,16 +33,40 @@ constexpr int DS_SLOT_TAB = 512;  // steps of a dK/dV item whose dS slot is tabu
 // ---------------------------------------------------------------------------
 // dK / dV
 // ---------------------------------------------------------------------------
+// 16-byte chunk swizzle of the fp16 [rows][D] LDS tiles of the dK/dV kernel:
+// logical chunk c of row r sits at c ^ hswz<D>(r).  With u = r*D/128 (the
+// 256-byte bank row), the 16 rows that a 16-lane group of a 16-byte read
+// touches, and the 4 rows x 32 bytes of a 16-lane group of a transposing read,
+// fall in distinct banks.
 template <int D>
-__global__ __launch_bounds__(256, 1) void sla_bwd_dkdv_bf16_kernel(AttnParams p)
+__device__ __forceinline__ int hswz(int r)
+{
+    constexpr int HALF = D / 16;  // half the chunks of a row
+    const int u = r * D / 128;
+    return (2 * (u & (HALF - 1))) ^ ((u / HALF) & 1);
+}
+
+template <int N>
+using dkdv_stage = std::integral_constant<int, N>;
+
+constexpr int DKDV_THREADS = 512;
+
+template <int D>
+__global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(AttnParams p)
 {
     constexpr int BN = BWD_BN, BM = BWD_BM;
-    constexpr int NC = D / 16, NDB = D / 32;
-    static_assert(BM == 64, "row steps are 64-row tiles");
-    __shared__ __align__(16) uint16_t sq[2][BM * D];
-    __shared__ __align__(16) uint16_t sdo[2][BM * D];
-    __shared__ __align__(16) uint16_t sqt[2][D * BM];
-    __shared__ __align__(16) uint16_t sdot[2][D * BM];
+    constexpr int NT = DKDV_THREADS;
+    constexpr int NC = D / 16, NDB = D / 32, CPR = D / 8;
+    constexpr int TILE = BM * D;             // fp16 elements of one staged 64-row tile
+    constexpr int TCH = BM * CPR;            // 16-byte chunks of one staged tile
+    constexpr int SPT = 2 * TCH / NT;        // DMA loads per thread and stage (Q, then dO)
+    static_assert(BM == 64 && BN == 128, "64-row steps over 128-key tiles");
+    static_assert((2 * TCH) % NT == 0 && SPT <= 8, "whole DMA rounds, at most 8 per stage");
+    // K and V of the key tile and two stages of [Q | G dO] rows, all fp16 with
+    // swizzled chunks; one array per stage so that the compiler can tell the
+    // DMA into one stage from the reads of the other
+    __shared__ __align__(16) uint16_t kt[BN * D], vt[BN * D];
+    __shared__ __align__(16) uint16_t st0[2 * TILE], st1[2 * TILE];
     __shared__ int16_t slot_tab[DS_SLOT_TAB];
 
     const int nrec = p.s.bwd_base[p.B];
@@ -55,29 +81,33 @@ __global__ __launch_bounds__(256, 1) void sla_bwd_dkdv_bf16_kernel(AttnParams p)
     const BwdItem it = bwd_item(sd.L, sd.U, p.k1, p.k2e, BN, BM, rec - uniform(p.s.bwd_base[b]),
                                 np, nch);
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    // 8 waves: wave w owns keys 32*(w%4) .. +32 of the tile and rows
+    // 32*(w/4) .. +32 of every 64-row step; the two row halves of a key block
+    // add their dK/dV sums at the end.  Two waves per SIMD.
+    const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
+    const int kw = wv & 3, rh = wv >> 2;
     const int l32 = lane & 31, hl = lane >> 5;
+    const int kj = it.c0 + 32 * kw + l32;  // this lane's key (operands, mask)
 
     const uint16_t *qg = reinterpret_cast<const uint16_t *>(p.q) + sd.base * p.ldq + h * D;
     const uint16_t *kg = reinterpret_cast<const uint16_t *>(p.k) + sd.base * p.ldk + h * D;
     const uint16_t *vg = reinterpret_cast<const uint16_t *>(p.v) + sd.base * p.ldv + h * D;
     const uint16_t *gg = reinterpret_cast<const uint16_t *>(p.dout) + sd.base * p.lddo + h * D;
 
-    // stationary K^T and V^T operands: lane holds key kj, d-slots 16c + 8*hl .. +8
-    const int kj = it.c0 + 32 * wv + l32;
-    bf16x8 kb[NC], vb[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        kb[c] = as_bf16x8(ld16_row(kg, p.ldk, kj, it.c1, 16 * c + 8 * hl));
-        vb[c] = as_bf16x8(ld16_row(vg, p.ldv, kj, it.c1, 16 * c + 8 * hl));
-    }
-    // stored-dS path: the fp16 copy of this key tile that dQ = dS K reads
-    // (written once per key tile, by its first chunk)
-    if (p.kh != nullptr && it.chunk == 0 && kj < it.c1) {
-        uint16_t *khr = p.kh + (sd.base + kj) * ((int64_t)p.H * D) + h * D + 8 * hl;
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-            *reinterpret_cast<halfx8 *>(khr + 16 * c) = bf16x8_to_halfx8(kb[c]);
+    // K and V of the tile into LDS as fp16 (keys past c1 as zeros); the first
+    // chunk of a key tile also writes the fp16 copy of K that dQ = dS K reads
+    // on the stored-dS path
+    const bool write_kh = p.kh != nullptr && it.chunk == 0;
+    for (int i = tid; i < BN * CPR; i += NT) {
+        const int key = i / CPR, c = i % CPR;
+        const halfx8 kh8 = bf16x8_to_halfx8(as_bf16x8(ld16_row(kg, p.ldk, it.c0 + key, it.c1, 8 * c)));
+        const halfx8 vh8 = bf16x8_to_halfx8(as_bf16x8(ld16_row(vg, p.ldv, it.c0 + key, it.c1, 8 * c)));
+        const int off = key * D + 8 * (c ^ hswz<D>(key));
+        *reinterpret_cast<halfx8 *>(kt + off) = kh8;
+        *reinterpret_cast<halfx8 *>(vt + off) = vh8;
+        if (write_kh && it.c0 + key < it.c1)
+            *reinterpret_cast<halfx8 *>(p.kh + (sd.base + it.c0 + key) * ((int64_t)p.H * D) +
+                                        h * D + 8 * c) = kh8;
     }
     const int rt_first = p.ds != nullptr ? uniform(p.s.rt_base[b]) : 0;
 
@@ -91,16 +121,7 @@ __global__ __launch_bounds__(256, 1) void sla_bwd_dkdv_bf16_kernel(AttnParams p)
         t_first = (it.ta - sd.U) / BM;
         nt = cdiv(it.tb - sd.U, BM) - t_first;
     }
-    const int nsteps = nh + nt;
-
-    floatx16 dkacc[NDB], dvacc[NDB];
-#pragma unroll
-    for (int i = 0; i < NDB; ++i) {
-        dkacc[i] = zero16();
-        dvacc[i] = zero16();
-    }
-
-    Tile64<D> qt, gt;
+    const int nsteps = uniform(nh + nt);
     auto step_rows = [&](int s, int &m0, int &m1) {
         if (s < nh) {
             m0 = (h_first + s) * BM;
@@ -118,52 +139,102 @@ __global__ __launch_bounds__(256, 1) void sla_bwd_dkdv_bf16_kernel(AttnParams p)
         return cursor_slot(kr, it.c0, DS_BN);
     };
     if (p.ds != nullptr) {
-        for (int st = tid; st < imin(nsteps, DS_SLOT_TAB); st += blockDim.x) {
+        for (int st = tid; st < imin(nsteps, DS_SLOT_TAB); st += NT) {
             int a0, a1;
             step_rows(st, a0, a1);
             slot_tab[st] = (int16_t)step_slot(a0, a1);
         }
     }
 
-    // rows at or past m1 of a step hold copies of row m1 - 1; such steps are
-    // never "full", and the mask removes those rows
-    int m0n = 0, m1n = 0;
-    if (nsteps > 0) {
-        step_rows(0, m0n, m1n);
-        qt.load_clamped(qg, p.ldq, m0n, m1n, tid);
-        gt.load_clamped(gg, p.lddo, m0n, m1n, tid);
-    }
     const float nal2e = p.neg_alpha_log2e, alpha = p.alpha;
     const float gscale = *p.grad_scale;
     const bool key_tile_full = (it.c1 - it.c0 == BN);
-    // g = dO.v enters dS only: carry the gradient scale in the stationary V
+
+    auto stage = [&](auto S) -> uint16_t * {
+        if constexpr (decltype(S)::value == 0) return st0;
+        else return st1;
+    };
+    // DMA of the bf16 Q and dO rows of step t (clamped to the last step) into
+    // a stage: chunk P = i*NT + 64*wave + lane of the stage is physical chunk
+    // P % CPR of row (P / CPR) % BM of tile P / TCH (0: Q, 1: dO) and holds
+    // its logical chunk (P % CPR) ^ hswz(row); rows at or past m1 read row
+    // m1 - 1 (masked: such steps are never full)
+    auto issue = [&](int t, auto S) {
+        int m0, m1;
+        step_rows(imin(t, nsteps - 1), m0, m1);
+        uint16_t *sb = stage(S);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) vb[c] = scale_bf16x8(vb[c], gscale);
-    for (int s = 0; s < nsteps; ++s) {
-        const int buf = s & 1;
-        const int m0 = uniform(m0n), m1 = uniform(m1n);
-        qt.store_rows(sq[buf], tid);
-        store_transposed_f16<D>(qt, sqt[buf], tid, 1.0f);
-        gt.store_rows(sdo[buf], tid);
-        store_transposed_f16<D>(gt, sdot[buf], tid, gscale);
-        if (s + 1 < nsteps) {
-            step_rows(s + 1, m0n, m1n);
-            qt.load_clamped(qg, p.ldq, m0n, m1n, tid);
-            gt.load_clamped(gg, p.lddo, m0n, m1n, tid);
+        for (int i = 0; i < SPT; ++i) {
+            const int P = i * NT + wv * 64 + lane;
+            const int tile = (i * NT + wv * 64) / TCH;  // wave-uniform
+            const int row = (P % TCH) / CPR, pc = P % CPR;
+            const int grow = imin(m0 + row, m1 - 1);
+            const uint16_t *src = tile == 0 ? qg + (int64_t)grow * p.ldq : gg + (int64_t)grow * p.lddo;
+            gl_lds16(src + 8 * (pc ^ hswz<D>(row)), sb + (i * NT + wv * 64) * 8);
         }
+    };
+    // in place, each thread its own DMA chunks: bf16 -> fp16 (dO times G)
+    auto convert = [&](auto S) {
+        uint16_t *sb = stage(S);
+#pragma unroll
+        for (int i = 0; i < SPT; ++i) {
+            const int P = i * NT + wv * 64 + lane;
+            const float sc = (i * NT + wv * 64) / TCH == 0 ? 1.0f : gscale;
+            uint4 u = *reinterpret_cast<const uint4 *>(sb + 8 * P);
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+            const halfx8 hv = cvt8h(bf16_lo(w[0]) * sc, bf16_hi(w[0]) * sc, bf16_lo(w[1]) * sc,
+                                    bf16_hi(w[1]) * sc, bf16_lo(w[2]) * sc, bf16_hi(w[2]) * sc,
+                                    bf16_lo(w[3]) * sc, bf16_hi(w[3]) * sc);
+            *reinterpret_cast<halfx8 *>(sb + 8 * P) = hv;
+        }
+    };
+
+    // per-lane LDS offsets (elements).  Row operands: row ar = 32*rh + l32 of
+    // a staged tile and key row br = 32*kw + l32 of K / V, logical chunk
+    // 2c + hl.  Transposing reads (quarter q = lane/16, j = lane%16): rows
+    // 32*rh + 16*h2 + 8*rr + 4*(q/2) + j/4, columns 32*db + 16*(q%2) + 4*(j%4).
+    const int ar = 32 * rh + l32, br = 32 * kw + l32;
+    const int q4 = lane >> 4, j16 = lane & 15;
+    auto a_off = [&](int c) { return ar * D + 8 * ((2 * c + hl) ^ hswz<D>(ar)); };
+    auto b_off = [&](int c) { return br * D + 8 * ((2 * c + hl) ^ hswz<D>(br)); };
+    auto t_off = [&](int h2, int rr, int db) {
+        const int row = 32 * rh + 16 * h2 + 8 * rr + 4 * (q4 >> 1) + (j16 >> 2);
+        const int col = 32 * db + 16 * (q4 & 1) + 4 * (j16 & 3);
+        return row * D + 8 * ((col >> 3) ^ hswz<D>(row)) + (col & 7);
+    };
+
+    floatx16 dkacc[NDB], dvacc[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) {
+        dkacc[i] = zero16();
+        dvacc[i] = zero16();
+    }
+
+    // step t: wait for its DMA, convert, publish (the barrier also frees the
+    // other stage, read by step t - 1), refill the other stage with step
+    // t + 1, then the products of this wave's 32 rows x 32 keys
+    auto step = [&](int t, auto S) {
+        constexpr int sidx = decltype(S)::value;
+        vm_wait<0>();
+        convert(S);
         __syncthreads();
+        issue(t + 1, dkdv_stage<1 - sidx>{});
+        const uint16_t *sq = stage(S), *sg = stage(S) + TILE;
+        int m0, m1;
+        step_rows(t, m0, m1);
+        m0 = uniform(m0);
+        m1 = uniform(m1);
 
         // mask (partial steps only, a workgroup-uniform branch): rows past m1
-        // and invisible pairs get s = g = 0, hence P = dS = 0
+        // and invisible pairs get s = g = 0, hence P = dS = 0.  In terms of
+        // x = i - kj (register r has x = x0 + 8*(r/4) + r%4): rows before m1
+        // of a history step see the key iff 0 <= x < W, W = m1 - kj, capped
+        // at K1 unless kj is a prefix key; rows of a target step iff
+        // x < m1 - kj and (x == 0 or kj lies in row U's view)
         const bool full = uniform((m1 == m0 + BM) && (m1 <= sd.U) && key_tile_full &&
                                   (it.c0 + BN - 1 <= m0) &&
                                   ((m1 - 1 - it.c0 < p.k1) || (it.c0 + BN <= p.k2e))) != 0;
-        // in terms of x = i - kj (element r of row block qb2 has x = x0 + c with
-        // the constant c = 32*qb2 + 8*(r/4) + r%4): rows before m1 of a history
-        // step see the key iff 0 <= x < W, W = m1 - kj, capped at K1 unless kj
-        // is a prefix key; rows of a target step iff x < m1 - kj and (x == 0
-        // or kj lies in row U's view)
-        const int x0 = m0 + 4 * hl - kj;
+        const int x0 = m0 + 32 * rh + 4 * hl - kj;
         const bool tstep = m0 >= sd.U;
         int W = m1 - kj;
         if (!tstep && kj >= p.k2e) W = imin(W, p.k1);
@@ -175,93 +246,133 @@ __global__ __launch_bounds__(256, 1) void sla_bwd_dkdv_bf16_kernel(AttnParams p)
         uint16_t *dsblk = nullptr;
         if (p.ds != nullptr) {
             const int rt = m0 < sd.U ? m0 / DS_BM : cdiv(sd.U, DS_BM) + (m0 - sd.U) / DS_BM;
-            const int slot = s < DS_SLOT_TAB ? uniform((int)slot_tab[s])
+            const int slot = t < DS_SLOT_TAB ? uniform((int)slot_tab[t])
                                              : uniform(step_slot(m0, m1));
             if (slot >= 0 && slot < p.ds_slots)
                 dsblk = p.ds + (1 + ((int64_t)(rt_first + rt) * p.H + h) * p.ds_slots + slot) *
                                    (DS_BM * DS_BN);  // block 0 is the zero block
         }
 
-        // per 32-row block (rows in the registers): S = Q K^T, dP = dO V^T,
-        // then P and dS, then dV += P^T dO and dK += dS^T Q over its two
-        // 16-row chunks; one block's S and dP are live at a time
+        // S = Q K^T and G dP = (G dO) V^T for this wave's 32 rows x 32 keys
+        floatx16 sacc = zero16(), pacc = zero16();
 #pragma unroll
-        for (int qb2 = 0; qb2 < 2; ++qb2) {
-            floatx16 sacc = zero16(), pacc = zero16();
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                bf16x8 aq = lds_row_chunk<D>(sq[buf], 32 * qb2 + l32, 2 * c + hl);
-                sacc = mfma32(aq, kb[c], sacc);
-                bf16x8 ag = lds_row_chunk<D>(sdo[buf], 32 * qb2 + l32, 2 * c + hl);
-                pacc = mfma32(ag, vb[c], pacc);
-            }
-            if (!full) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int x = x0 + 32 * qb2 + 8 * (r >> 2) + (r & 3);
-                    const bool vis = ((uint32_t)x < Wu) & (tv | (x == 0));
-                    sacc[r] = vis ? sacc[r] : 0.0f;
-                    pacc[r] = vis ? pacc[r] : 0.0f;
-                }
-            }
+        for (int c = 0; c < NC; ++c) {
+            const halfx8 aq = *reinterpret_cast<const halfx8 *>(sq + a_off(c));
+            const halfx8 bk = *reinterpret_cast<const halfx8 *>(kt + b_off(c));
+            sacc = mfma32h(aq, bk, sacc);
+            const halfx8 ag = *reinterpret_cast<const halfx8 *>(sg + a_off(c));
+            const halfx8 bv = *reinterpret_cast<const halfx8 *>(vt + b_off(c));
+            pacc = mfma32h(ag, bv, pacc);
+        }
+        if (!full) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float sv = sacc[r], g = pacc[r];
-                float e;
-                const float sg = sigmoid_e(sv, nal2e, e);
-                const float a = sv * sg;                       // SiLU(alpha s) / alpha
-                sacc[r] = a;
-                pacc[r] = g * (sg * (1.0f + alpha * a * e));  // G g SiLU'(t)
-            }
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                const int qc = 2 * qb2 + h2, o = 8 * h2;
-                halfx8 pa = cvt8h(sacc[o], sacc[o + 1], sacc[o + 2], sacc[o + 3], sacc[o + 4],
-                                  sacc[o + 5], sacc[o + 6], sacc[o + 7]);
-                halfx8 da = cvt8h(pacc[o], pacc[o + 1], pacc[o + 2], pacc[o + 3], pacc[o + 4],
-                                  pacc[o + 5], pacc[o + 6], pacc[o + 7]);
-                if (dsblk != nullptr)
-                    *reinterpret_cast<halfx8 *>(dsblk + 8 * ds_frag_chunk(wv, qc, l32, hl)) = da;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    halfx8 bg = lds_t_chunk_h(sdot[buf], 32 * db + l32, 2 * qc + hl);
-                    dvacc[db] = mfma32h(pa, bg, dvacc[db]);
-                    halfx8 bq = lds_t_chunk_h(sqt[buf], 32 * db + l32, 2 * qc + hl);
-                    dkacc[db] = mfma32h(da, bq, dkacc[db]);
-                }
+                const int x = x0 + 8 * (r >> 2) + (r & 3);
+                const bool vis = ((uint32_t)x < Wu) & (tv | (x == 0));
+                sacc[r] = vis ? sacc[r] : 0.0f;
+                pacc[r] = vis ? pacc[r] : 0.0f;
             }
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float sv = sacc[r], g = pacc[r];
+            float e;
+            const float sgm = sigmoid_e(sv, nal2e, e);
+            const float a = sv * sgm;                      // SiLU(alpha s) / alpha
+            sacc[r] = a;
+            pacc[r] = g * (sgm * (1.0f + alpha * a * e));  // G g SiLU'(t)
+        }
+        // dV += P^T (G dO), dK += (G dS)^T Q over the two 16-row chunks; the
+        // accumulator's row order (8*(r/4) + 4*hl + r%4) is the k order of
+        // the transposing reads
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int o = 8 * h2;
+            const halfx8 pa = cvt8h(sacc[o], sacc[o + 1], sacc[o + 2], sacc[o + 3], sacc[o + 4],
+                                    sacc[o + 5], sacc[o + 6], sacc[o + 7]);
+            const halfx8 da = cvt8h(pacc[o], pacc[o + 1], pacc[o + 2], pacc[o + 3], pacc[o + 4],
+                                    pacc[o + 5], pacc[o + 6], pacc[o + 7]);
+            if (dsblk != nullptr)
+                *reinterpret_cast<halfx8 *>(dsblk + 8 * ds_frag_chunk(kw, 2 * rh + h2, l32, hl)) =
+                    da;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const uint2 g0 = tr_read_b64(sg + t_off(h2, 0, db));
+                const uint2 g1 = tr_read_b64(sg + t_off(h2, 1, db));
+                dvacc[db] = mfma32h(pa, __builtin_bit_cast(halfx8, make_uint4(g0.x, g0.y, g1.x, g1.y)),
+                                    dvacc[db]);
+                const uint2 q0 = tr_read_b64(sq + t_off(h2, 0, db));
+                const uint2 q1 = tr_read_b64(sq + t_off(h2, 1, db));
+                dkacc[db] = mfma32h(da, __builtin_bit_cast(halfx8, make_uint4(q0.x, q0.y, q1.x, q1.y)),
+                                    dkacc[db]);
+            }
+        }
+    };
+
+    if (nsteps > 0) {
+        issue(0, dkdv_stage<0>{});
+        for (int t = 0; t < nsteps; t += 2) {
+            step(t, dkdv_stage<0>{});
+            if (t + 1 < nsteps) step(t + 1, dkdv_stage<1>{});
+        }
+        vm_wait<0>();  // no DMA left in flight
+    }
+
+    // the two row halves of key block kw: the rh = 1 wave hands its dK sum to
+    // the rh = 0 wave and takes the rh = 0 wave's dV sum, through LDS (all
+    // stages and tiles are free now); region e holds 32 keys x D floats
+    __syncthreads();
+    auto region = [&](int e) -> float * {
+        uint16_t *a = e < 2 ? kt : (e < 4 ? vt : (e < 6 ? st0 : st1));
+        return reinterpret_cast<float *>(a) + (e & 1) * (32 * D);
+    };
+    floatx16 *mine = rh == 0 ? dkacc : dvacc;    // the sum this wave writes out
+    floatx16 *other = rh == 0 ? dvacc : dkacc;   // the sum it hands over
+    {
+        float *xo = region(2 * kw + (1 - rh));
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) xo[(db * 16 + r) * 64 + lane] = other[db][r];
+    }
+    __syncthreads();
+    {
+        const float *xi = region(2 * kw + rh);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mine[db][r] += xi[(db * 16 + r) * 64 + lane];
     }
 
     // accumulator: lane holds column d = 32*db + l32, register r holds key
-    // 32*wv + 8*(r/4) + 4*hl + r%4 of the tile
+    // 32*kw + 8*(r/4) + 4*hl + r%4 of the tile; dV (P carries 1/alpha) and dK
+    // both scale by alpha / (N G)
+    const float sc = p.out_scale / gscale;
     if (it.nchunk == 1) {
-        uint16_t *dkg = reinterpret_cast<uint16_t *>(p.dk) + sd.base * p.lddk + h * D;
-        uint16_t *dvg = reinterpret_cast<uint16_t *>(p.dv) + sd.base * p.lddv + h * D;
-        const float sk_ = p.out_scale / gscale, sv_ = sk_;  // both carry alpha / (N G)
+        uint16_t *dst = rh == 0 ? reinterpret_cast<uint16_t *>(p.dk) + sd.base * p.lddk + h * D
+                                : reinterpret_cast<uint16_t *>(p.dv) + sd.base * p.lddv + h * D;
+        const int64_t ld = rh == 0 ? p.lddk : p.lddv;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int j = it.c0 + 32 * wv + 8 * (r >> 2) + 4 * hl + (r & 3);
+                const int j = it.c0 + 32 * kw + 8 * (r >> 2) + 4 * hl + (r & 3);
                 if (j < it.c1) {
-                    __bf16 kv = (__bf16)(dkacc[db][r] * sk_);
-                    __bf16 vv = (__bf16)(dvacc[db][r] * sv_);
-                    dkg[(int64_t)j * p.lddk + 32 * db + l32] = __builtin_bit_cast(uint16_t, kv);
-                    dvg[(int64_t)j * p.lddv + 32 * db + l32] = __builtin_bit_cast(uint16_t, vv);
+                    const __bf16 v = (__bf16)(mine[db][r] * sc);
+                    dst[(int64_t)j * ld + 32 * db + l32] = __builtin_bit_cast(uint16_t, v);
                 }
             }
         }
     } else {
+        // fp32 partials [key][dK | dV] of this chunk
         const int slot = p.s.part_base[b] + it.tile * nch + it.chunk;
-        float *part = p.partials + ((int64_t)slot * p.H + h) * BN * (2 * D);
+        float *part = p.partials + ((int64_t)slot * p.H + h) * BN * (2 * D) + rh * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int jl = 32 * wv + 8 * (r >> 2) + 4 * hl + (r & 3);
-                part[jl * (2 * D) + 32 * db + l32] = dkacc[db][r];
-                part[jl * (2 * D) + D + 32 * db + l32] = dvacc[db][r];
+                const int jl = 32 * kw + 8 * (r >> 2) + 4 * hl + (r & 3);
+                part[jl * (2 * D) + 32 * db + l32] = mine[db][r];
             }
         }
     }
@@ -462,7 +573,8 @@ __global__ __launch_bounds__(256, 1) void sla_bwd_dq_bf16_kernel(AttnParams p)
 template <int D>
 static hipError_t launch_dkdv_d(const AttnParams &p, hipStream_t st)
 {
-    hipLaunchKernelGGL(sla_bwd_dkdv_bf16_kernel<D>, dim3(p.grid_bwd), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(sla_bwd_dkdv_bf16_kernel<D>, dim3(p.grid_bwd), dim3(DKDV_THREADS), 0, st,
+                       p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.grid_red == 0) return e;
     hipLaunchKernelGGL(sla_bwd_reduce_kernel<D>, dim3(p.grid_red * (BWD_BN * 2 * D / RED_SLAB)),
