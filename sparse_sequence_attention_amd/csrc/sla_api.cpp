@@ -136,8 +136,9 @@ WsLayout layout(const sla_problem_t *p, int op)
         if (p->dtype == SLA_BF16 && (p->d_qk == 64 || p->d_qk == 128) && slots <= DS_MAX_SLOTS) {
             w.ds_slots = (int)slots;
             // block 0: zeros (written by the schedule kernel), read by dQ for
-            // key tiles a row half does not visit
-            ds_bytes = ((size_t)w.rt_items * p->num_heads * (size_t)slots + 1) * DS_BM * DS_BN * 2;
+            // key tiles a row half does not visit; the last block: discarded
+            // dS stores of the dK/dV kernel
+            ds_bytes = ((size_t)w.rt_items * p->num_heads * (size_t)slots + 2) * DS_BM * DS_BN * 2;
             kh_bytes = (size_t)T * p->num_heads * p->d_qk * 2;
         }
     }
@@ -189,6 +190,7 @@ sla_status_t make_params(const sla_problem_t *p, int op, void *ws, size_t ws_byt
     if (w.ds_slots > 0) {
         a.ds = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + w.ds_off);
         a.kh = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + w.kh_off);
+        a.ds_discard = 1 + w.rt_items * H * (int64_t)w.ds_slots;
     }
     return SLA_OK;
 }

@@ -33,21 +33,20 @@ constexpr int DS_SLOT_TAB = 512;  // steps of a dK/dV item whose dS slot is tabu
 // ---------------------------------------------------------------------------
 // dK / dV
 // ---------------------------------------------------------------------------
-// 16-byte chunk swizzle of the fp16 [rows][D] LDS tiles of the dK/dV kernel:
-// logical chunk c of row r sits at c ^ hswz<D>(r).  With u = r*D/128 (the
-// 256-byte bank row), the 16 rows that a 16-lane group of a 16-byte read
-// touches, and the 4 rows x 32 bytes of a 16-lane group of a transposing read,
-// fall in distinct banks.
+// 16-byte chunk swizzle of the fp16 [64][D] Q / G dO tiles of the dK/dV
+// kernel: logical chunk c of row r sits at c ^ hswz<D>(r).  With u = r*D/128
+// (the 256-byte bank row) and Q4 = D/32, hswz = 4*(u % Q4) + (u / Q4) % 4:
+// the 16 rows that a 16-lane pass of a 16-byte read touches, and the 4 rows x
+// 64 bytes that a 32-lane pass of a transposing read touches, fall in
+// distinct banks (gfx950 serves ds_read_b128 16 lanes and ds_read_b64_tr_b16
+// 32 lanes at a time).
 template <int D>
 __device__ __forceinline__ int hswz(int r)
 {
-    constexpr int HALF = D / 16;  // half the chunks of a row
+    constexpr int Q4 = D / 32;
     const int u = r * D / 128;
-    return (2 * (u & (HALF - 1))) ^ ((u / HALF) & 1);
+    return 4 * (u % Q4) + (u / Q4) % 4;
 }
-
-template <int N>
-using dkdv_stage = std::integral_constant<int, N>;
 
 constexpr int DKDV_THREADS = 512;
 
@@ -57,16 +56,20 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
     constexpr int BN = BWD_BN, BM = BWD_BM;
     constexpr int NT = DKDV_THREADS;
     constexpr int NC = D / 16, NDB = D / 32, CPR = D / 8;
-    constexpr int TILE = BM * D;             // fp16 elements of one staged 64-row tile
+    constexpr int TILE = BM * D;             // elements of one staged 64-row tile
     constexpr int TCH = BM * CPR;            // 16-byte chunks of one staged tile
-    constexpr int SPT = 2 * TCH / NT;        // DMA loads per thread and stage (Q, then dO)
+    constexpr int SPT = 2 * TCH / NT;        // DMA loads per thread and step (Q, then dO)
+    constexpr int KVS = D + 8;               // padded K / V row: 16-byte reads of 16
+                                             // consecutive keys hit distinct banks
     static_assert(BM == 64 && BN == 128, "64-row steps over 128-key tiles");
-    static_assert((2 * TCH) % NT == 0 && SPT <= 8, "whole DMA rounds, at most 8 per stage");
-    // K and V of the key tile and two stages of [Q | G dO] rows, all fp16 with
-    // swizzled chunks; one array per stage so that the compiler can tell the
-    // DMA into one stage from the reads of the other
-    __shared__ __align__(16) uint16_t kt[BN * D], vt[BN * D];
-    __shared__ __align__(16) uint16_t st0[2 * TILE], st1[2 * TILE];
+    static_assert((2 * TCH) % NT == 0 && SPT <= 8, "whole DMA rounds, at most 8 per step");
+    // kv: K then V of the key tile (fp16, padded rows).  land: the bf16 Q and
+    // dO rows of the next step, filled by DMA (its own array, so the compiler
+    // can tell the DMA from the reads of cs).  cs: the current step's Q and
+    // G dO rows in fp16, swizzled.
+    __shared__ __align__(16) uint16_t kv[2 * BN * KVS];
+    __shared__ __align__(16) uint16_t land[2 * TILE];
+    __shared__ __align__(16) uint16_t cs[2 * TILE];
     __shared__ int16_t slot_tab[DS_SLOT_TAB];
 
     const int nrec = p.s.bwd_base[p.B];
@@ -102,9 +105,8 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
         const int key = i / CPR, c = i % CPR;
         const halfx8 kh8 = bf16x8_to_halfx8(as_bf16x8(ld16_row(kg, p.ldk, it.c0 + key, it.c1, 8 * c)));
         const halfx8 vh8 = bf16x8_to_halfx8(as_bf16x8(ld16_row(vg, p.ldv, it.c0 + key, it.c1, 8 * c)));
-        const int off = key * D + 8 * (c ^ hswz<D>(key));
-        *reinterpret_cast<halfx8 *>(kt + off) = kh8;
-        *reinterpret_cast<halfx8 *>(vt + off) = vh8;
+        *reinterpret_cast<halfx8 *>(kv + key * KVS + 8 * c) = kh8;
+        *reinterpret_cast<halfx8 *>(kv + (BN + key) * KVS + 8 * c) = vh8;
         if (write_kh && it.c0 + key < it.c1)
             *reinterpret_cast<halfx8 *>(p.kh + (sd.base + it.c0 + key) * ((int64_t)p.H * D) +
                                         h * D + 8 * c) = kh8;
@@ -150,53 +152,45 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
     const float gscale = *p.grad_scale;
     const bool key_tile_full = (it.c1 - it.c0 == BN);
 
-    auto stage = [&](auto S) -> uint16_t * {
-        if constexpr (decltype(S)::value == 0) return st0;
-        else return st1;
+    // this thread's chunks of a step: chunk P = i*NT + 64*wave + lane is
+    // logical chunk P % CPR of row (P % TCH) / CPR of tile P / TCH (0: Q,
+    // 1: dO); the DMA lands it at land[8P], the conversion moves it to its
+    // swizzled place in cs
+    // tile of this thread's i-th chunk (wave-uniform; a compile-time
+    // constant when a DMA round never straddles the two tiles)
+    auto chunk_tile = [&](int i) {
+        if constexpr (TCH % NT == 0) return (i * NT) / TCH;
+        else return (i * NT + wv * 64) / TCH;
     };
-    // DMA of the bf16 Q and dO rows of step t (clamped to the last step) into
-    // a stage: chunk P = i*NT + 64*wave + lane of the stage is physical chunk
-    // P % CPR of row (P / CPR) % BM of tile P / TCH (0: Q, 1: dO) and holds
-    // its logical chunk (P % CPR) ^ hswz(row); rows at or past m1 read row
-    // m1 - 1 (masked: such steps are never full)
-    auto issue = [&](int t, auto S) {
+    // DMA of the bf16 rows of step t (clamped to the last step): a
+    // workgroup-uniform row base plus a 32-bit per-lane offset; rows at or
+    // past m1 read row m1 - 1 (masked: such steps are never full)
+    const uint32_t ldq_b = (uint32_t)p.ldq * 2u, lddo_b = (uint32_t)p.lddo * 2u;
+    auto issue = [&](int t) {
         int m0, m1;
         step_rows(imin(t, nsteps - 1), m0, m1);
-        uint16_t *sb = stage(S);
+        m0 = uniform(m0);
+        const int last = uniform(m1 - 1 - m0);
+        const char *qrow = reinterpret_cast<const char *>(qg + (int64_t)m0 * p.ldq);
+        const char *grow = reinterpret_cast<const char *>(gg + (int64_t)m0 * p.lddo);
 #pragma unroll
         for (int i = 0; i < SPT; ++i) {
             const int P = i * NT + wv * 64 + lane;
-            const int tile = (i * NT + wv * 64) / TCH;  // wave-uniform
-            const int row = (P % TCH) / CPR, pc = P % CPR;
-            const int grow = imin(m0 + row, m1 - 1);
-            const uint16_t *src = tile == 0 ? qg + (int64_t)grow * p.ldq : gg + (int64_t)grow * p.lddo;
-            gl_lds16(src + 8 * (pc ^ hswz<D>(row)), sb + (i * NT + wv * 64) * 8);
-        }
-    };
-    // in place, each thread its own DMA chunks: bf16 -> fp16 (dO times G)
-    auto convert = [&](auto S) {
-        uint16_t *sb = stage(S);
-#pragma unroll
-        for (int i = 0; i < SPT; ++i) {
-            const int P = i * NT + wv * 64 + lane;
-            const float sc = (i * NT + wv * 64) / TCH == 0 ? 1.0f : gscale;
-            uint4 u = *reinterpret_cast<const uint4 *>(sb + 8 * P);
-            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-            const halfx8 hv = cvt8h(bf16_lo(w[0]) * sc, bf16_hi(w[0]) * sc, bf16_lo(w[1]) * sc,
-                                    bf16_hi(w[1]) * sc, bf16_lo(w[2]) * sc, bf16_hi(w[2]) * sc,
-                                    bf16_lo(w[3]) * sc, bf16_hi(w[3]) * sc);
-            *reinterpret_cast<halfx8 *>(sb + 8 * P) = hv;
+            const int tile = chunk_tile(i);
+            const uint32_t row = (uint32_t)imin((P % TCH) / CPR, last), c = P % CPR;
+            const char *src = tile == 0 ? qrow + (row * ldq_b + 16u * c) : grow + (row * lddo_b + 16u * c);
+            gl_lds16(src, land + (i * NT + wv * 64) * 8);
         }
     };
 
     // per-lane LDS offsets (elements).  Row operands: row ar = 32*rh + l32 of
-    // a staged tile and key row br = 32*kw + l32 of K / V, logical chunk
-    // 2c + hl.  Transposing reads (quarter q = lane/16, j = lane%16): rows
+    // a staged tile (logical chunk 2c + hl) and key row br = 32*kw + l32 of
+    // K / V.  Transposing reads (quarter q = lane/16, j = lane%16): rows
     // 32*rh + 16*h2 + 8*rr + 4*(q/2) + j/4, columns 32*db + 16*(q%2) + 4*(j%4).
     const int ar = 32 * rh + l32, br = 32 * kw + l32;
     const int q4 = lane >> 4, j16 = lane & 15;
     auto a_off = [&](int c) { return ar * D + 8 * ((2 * c + hl) ^ hswz<D>(ar)); };
-    auto b_off = [&](int c) { return br * D + 8 * ((2 * c + hl) ^ hswz<D>(br)); };
+    const int b_base = br * KVS + 8 * hl;  // + 16 c (K), + BN*KVS (V)
     auto t_off = [&](int h2, int rr, int db) {
         const int row = 32 * rh + 16 * h2 + 8 * rr + 4 * (q4 >> 1) + (j16 >> 2);
         const int col = 32 * db + 16 * (q4 & 1) + 4 * (j16 & 3);
@@ -210,16 +204,48 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
         dvacc[i] = zero16();
     }
 
-    // step t: wait for its DMA, convert, publish (the barrier also frees the
-    // other stage, read by step t - 1), refill the other stage with step
-    // t + 1, then the products of this wave's 32 rows x 32 keys
-    auto step = [&](int t, auto S) {
-        constexpr int sidx = decltype(S)::value;
+    // the step loop, compiled once with and once without the dS stores so
+    // that the stores are unconditional where they exist
+    auto run = [&](auto HAS_DS) {
+    constexpr bool has_ds = decltype(HAS_DS)::value;
+    // stored-dS path: each step's two dS chunks per lane are stored one step
+    // later, right after the next DMA is issued, so that the wait at the top
+    // of a step only covers operations issued a whole step before
+    uint16_t *pend_blk = has_ds ? p.ds + p.ds_discard * (DS_BM * DS_BN) : nullptr;
+    halfx8 pend[2] = {};
+    if (nsteps > 0) issue(0);
+    for (int t = 0; t < nsteps; ++t) {
+        // wait for this step's DMA, take this thread's chunks, then once
+        // every wave is done with the previous step put them in cs as fp16
+        // (dO times G), refill land with step t + 1, store the previous
+        // step's dS and publish cs.  The barriers wait for LDS only: the DMA
+        // and the stores just issued stay in flight.
         vm_wait<0>();
-        convert(S);
-        __syncthreads();
-        issue(t + 1, dkdv_stage<1 - sidx>{});
-        const uint16_t *sq = stage(S), *sg = stage(S) + TILE;
+        uint4 raw[SPT];
+#pragma unroll
+        for (int i = 0; i < SPT; ++i) raw[i] = *reinterpret_cast<const uint4 *>(land + 8 * (i * NT + wv * 64 + lane));
+        barrier_lds();
+#pragma unroll
+        for (int i = 0; i < SPT; ++i) {
+            const int P = i * NT + wv * 64 + lane;
+            const int tile = chunk_tile(i);
+            const int row = (P % TCH) / CPR, c = P % CPR;
+            const float sc = tile == 0 ? 1.0f : gscale;
+            const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+            const halfx8 hv = cvt8h(bf16_lo(w[0]) * sc, bf16_hi(w[0]) * sc, bf16_lo(w[1]) * sc,
+                                    bf16_hi(w[1]) * sc, bf16_lo(w[2]) * sc, bf16_hi(w[2]) * sc,
+                                    bf16_lo(w[3]) * sc, bf16_hi(w[3]) * sc);
+            *reinterpret_cast<halfx8 *>(cs + tile * TILE + row * D + 8 * (c ^ hswz<D>(row))) = hv;
+        }
+        issue(t + 1);
+        if constexpr (has_ds) {
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+                *reinterpret_cast<halfx8 *>(pend_blk + 8 * ds_frag_chunk(kw, 2 * rh + h2, l32, hl)) =
+                    pend[h2];
+        }
+        barrier_lds();
+        const uint16_t *sq = cs, *sg = cs + TILE;
         int m0, m1;
         step_rows(t, m0, m1);
         m0 = uniform(m0);
@@ -241,16 +267,17 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
         const uint32_t Wu = (uint32_t)imax(W, 0);
         const bool tv = !tstep || ((kj < sd.U) & ((sd.U - kj < p.k1) | (kj < p.k2e)));
 
-        // stored-dS path: the slot of this key tile among the key tiles the
-        // 64-row tile [m0, m1) visits (the order dQ reads them in)
-        uint16_t *dsblk = nullptr;
-        if (p.ds != nullptr) {
+        // stored-dS path: the block of this key tile's slot among the key
+        // tiles the 64-row tile [m0, m1) visits (the order dQ reads them
+        // in), or the discard block
+        if constexpr (has_ds) {
             const int rt = m0 < sd.U ? m0 / DS_BM : cdiv(sd.U, DS_BM) + (m0 - sd.U) / DS_BM;
             const int slot = t < DS_SLOT_TAB ? uniform((int)slot_tab[t])
                                              : uniform(step_slot(m0, m1));
-            if (slot >= 0 && slot < p.ds_slots)
-                dsblk = p.ds + (1 + ((int64_t)(rt_first + rt) * p.H + h) * p.ds_slots + slot) *
-                                   (DS_BM * DS_BN);  // block 0 is the zero block
+            const int64_t blk = (slot >= 0 && slot < p.ds_slots)
+                                    ? 1 + ((int64_t)(rt_first + rt) * p.H + h) * p.ds_slots + slot
+                                    : p.ds_discard;  // block 0 is the zero block
+            pend_blk = p.ds + blk * (DS_BM * DS_BN);
         }
 
         // S = Q K^T and G dP = (G dO) V^T for this wave's 32 rows x 32 keys
@@ -258,10 +285,10 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const halfx8 aq = *reinterpret_cast<const halfx8 *>(sq + a_off(c));
-            const halfx8 bk = *reinterpret_cast<const halfx8 *>(kt + b_off(c));
+            const halfx8 bk = *reinterpret_cast<const halfx8 *>(kv + b_base + 16 * c);
             sacc = mfma32h(aq, bk, sacc);
             const halfx8 ag = *reinterpret_cast<const halfx8 *>(sg + a_off(c));
-            const halfx8 bv = *reinterpret_cast<const halfx8 *>(vt + b_off(c));
+            const halfx8 bv = *reinterpret_cast<const halfx8 *>(kv + BN * KVS + b_base + 16 * c);
             pacc = mfma32h(ag, bv, pacc);
         }
         if (!full) {
@@ -273,14 +300,16 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
                 pacc[r] = vis ? pacc[r] : 0.0f;
             }
         }
+        // P = s sigma (= SiLU(t) / alpha) and G dS = G g sigma (1 + t (1 - sigma))
+        // = G g (sigma + a * (alpha - alpha sigma)).  exp(-t) overflowing to
+        // inf gives sigma = 0, a = 0 and dS = 0, its limit, with no NaN.
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const float sv = sacc[r], g = pacc[r];
-            float e;
-            const float sgm = sigmoid_e(sv, nal2e, e);
-            const float a = sv * sgm;                      // SiLU(alpha s) / alpha
+            const float sgm = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sv * nal2e));
+            const float a = sv * sgm;
             sacc[r] = a;
-            pacc[r] = g * (sgm * (1.0f + alpha * a * e));  // G g SiLU'(t)
+            pacc[r] = g * fmaf(a, fmaf(-alpha, sgm, alpha), sgm);
         }
         // dV += P^T (G dO), dK += (G dS)^T Q over the two 16-row chunks; the
         // accumulator's row order (8*(r/4) + 4*hl + r%4) is the k order of
@@ -292,9 +321,7 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
                                     sacc[o + 5], sacc[o + 6], sacc[o + 7]);
             const halfx8 da = cvt8h(pacc[o], pacc[o + 1], pacc[o + 2], pacc[o + 3], pacc[o + 4],
                                     pacc[o + 5], pacc[o + 6], pacc[o + 7]);
-            if (dsblk != nullptr)
-                *reinterpret_cast<halfx8 *>(dsblk + 8 * ds_frag_chunk(kw, 2 * rh + h2, l32, hl)) =
-                    da;
+            if constexpr (has_ds) pend[h2] = da;
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
                 const uint2 g0 = tr_read_b64(sg + t_off(h2, 0, db));
@@ -307,24 +334,28 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
                                     dkacc[db]);
             }
         }
-    };
-
-    if (nsteps > 0) {
-        issue(0, dkdv_stage<0>{});
-        for (int t = 0; t < nsteps; t += 2) {
-            step(t, dkdv_stage<0>{});
-            if (t + 1 < nsteps) step(t + 1, dkdv_stage<1>{});
-        }
-        vm_wait<0>();  // no DMA left in flight
     }
+    if constexpr (has_ds) {
+        if (nsteps > 0) {
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+                *reinterpret_cast<halfx8 *>(pend_blk + 8 * ds_frag_chunk(kw, 2 * rh + h2, l32, hl)) =
+                    pend[h2];
+        }
+    }
+    vm_wait<0>();  // no DMA (of the clamped step past the end) left in flight
+    };
+    if (p.ds != nullptr) run(std::true_type{});
+    else run(std::false_type{});
 
     // the two row halves of key block kw: the rh = 1 wave hands its dK sum to
-    // the rh = 0 wave and takes the rh = 0 wave's dV sum, through LDS (all
-    // stages and tiles are free now); region e holds 32 keys x D floats
+    // the rh = 0 wave and takes the rh = 0 wave's dV sum, through LDS (free
+    // after the barrier); region e holds 32 keys x D floats
     __syncthreads();
     auto region = [&](int e) -> float * {
-        uint16_t *a = e < 2 ? kt : (e < 4 ? vt : (e < 6 ? st0 : st1));
-        return reinterpret_cast<float *>(a) + (e & 1) * (32 * D);
+        // kv holds regions 0-3, land 4-5, cs 6-7
+        uint16_t *a = e < 4 ? kv + (e & 3) * (64 * D) : (e < 6 ? land : cs) + (e & 1) * (64 * D);
+        return reinterpret_cast<float *>(a);
     };
     floatx16 *mine = rh == 0 ? dkacc : dvacc;    // the sum this wave writes out
     floatx16 *other = rh == 0 ? dvacc : dkacc;   // the sum it hands over

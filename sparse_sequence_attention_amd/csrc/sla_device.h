@@ -182,6 +182,14 @@ __device__ __forceinline__ void barrier_lds_dma()
     asm volatile("s_barrier" ::: "memory");
 }
 
+// Workgroup barrier that publishes this wave's LDS writes (and waits for its
+// LDS reads) but leaves global loads and stores, including DMA into other
+// LDS buffers, in flight; __syncthreads' fence would wait for those too.
+__device__ __forceinline__ void barrier_lds()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
 // lane j points at 4 consecutive 16-bit values (an 8-byte run) and lane i
 // receives value i % 4 of the runs of lanes i / 4, 4 + i / 4, 8 + i / 4 and

@@ -32,9 +32,12 @@ struct AttnParams {
     int grid_red;           // upper bound of reduce items (x heads)
     // stored dS (null when dQ recomputes): a zero block, then the fp16 dS
     // blocks [64-row tile][head][slot][DS_BM x DS_BN] in the dK/dV kernel's
-    // fragment order; and an fp16 copy of K [T][H][d]
+    // fragment order, then one discard block (the target of dS stores of
+    // tiles that have no slot, so that every step stores the same number of
+    // blocks); and an fp16 copy of K [T][H][d]
     uint16_t *ds;
     uint16_t *kh;
+    int64_t ds_discard;     // block index of the discard block
     int ds_slots;           // slots per (row tile, head)
     int grid_rt;            // upper bound of 64-row tiles (x heads)
 };
