@@ -63,13 +63,13 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
                                              // consecutive keys hit distinct banks
     static_assert(BM == 64 && BN == 128, "64-row steps over 128-key tiles");
     static_assert((2 * TCH) % NT == 0 && SPT <= 8, "whole DMA rounds, at most 8 per step");
-    // kv: K then V of the key tile (fp16, padded rows).  land: the bf16 Q and
-    // dO rows of the next step, filled by DMA (its own array, so the compiler
-    // can tell the DMA from the reads of cs).  cs: the current step's Q and
-    // G dO rows in fp16, swizzled.
+    // kv: K then V of the key tile (fp16, padded rows).  cs0 / cs1: two
+    // stages of Q and G dO rows (swizzled); the DMA brings a step's bf16 rows
+    // into one stage while the other is read, and each thread then converts
+    // its own chunks in place to fp16.  Separate arrays, so that the compiler
+    // can tell the DMA into one stage from the reads of the other.
     __shared__ __align__(16) uint16_t kv[2 * BN * KVS];
-    __shared__ __align__(16) uint16_t land[2 * TILE];
-    __shared__ __align__(16) uint16_t cs[2 * TILE];
+    __shared__ __align__(16) uint16_t cs0[2 * TILE], cs1[2 * TILE];
     __shared__ int16_t slot_tab[DS_SLOT_TAB];
 
     const int nrec = p.s.bwd_base[p.B];
@@ -152,34 +152,57 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
     const float gscale = *p.grad_scale;
     const bool key_tile_full = (it.c1 - it.c0 == BN);
 
-    // this thread's chunks of a step: chunk P = i*NT + 64*wave + lane is
-    // logical chunk P % CPR of row (P % TCH) / CPR of tile P / TCH (0: Q,
-    // 1: dO); the DMA lands it at land[8P], the conversion moves it to its
-    // swizzled place in cs
-    // tile of this thread's i-th chunk (wave-uniform; a compile-time
-    // constant when a DMA round never straddles the two tiles)
+    // this thread's chunks of a step: chunk P = i*NT + 64*wave + lane of a
+    // stage is physical chunk P % CPR of row (P % TCH) / CPR of tile P / TCH
+    // (0: Q, 1: dO); the DMA fills it with logical chunk (P % CPR) ^ hswz(row)
+    // and the same thread converts it in place.  The tile of the i-th chunk
+    // is wave-uniform, and a compile-time constant when a DMA round never
+    // straddles the two tiles.
     auto chunk_tile = [&](int i) {
         if constexpr (TCH % NT == 0) return (i * NT) / TCH;
         else return (i * NT + wv * 64) / TCH;
     };
-    // DMA of the bf16 rows of step t (clamped to the last step): a
-    // workgroup-uniform row base plus a 32-bit per-lane offset; rows at or
+    auto stage = [&](auto S) -> uint16_t * {
+        if constexpr (decltype(S)::value == 0) return cs0;
+        else return cs1;
+    };
+    // DMA of the bf16 rows of step t (clamped to the last step) into a stage:
+    // a workgroup-uniform row base plus a 32-bit per-lane offset; rows at or
     // past m1 read row m1 - 1 (masked: such steps are never full)
     const uint32_t ldq_b = (uint32_t)p.ldq * 2u, lddo_b = (uint32_t)p.lddo * 2u;
-    auto issue = [&](int t) {
+    auto issue = [&](int t, auto S) {
         int m0, m1;
         step_rows(imin(t, nsteps - 1), m0, m1);
         m0 = uniform(m0);
         const int last = uniform(m1 - 1 - m0);
         const char *qrow = reinterpret_cast<const char *>(qg + (int64_t)m0 * p.ldq);
         const char *grow = reinterpret_cast<const char *>(gg + (int64_t)m0 * p.lddo);
+        uint16_t *sb = stage(S);
 #pragma unroll
         for (int i = 0; i < SPT; ++i) {
             const int P = i * NT + wv * 64 + lane;
             const int tile = chunk_tile(i);
-            const uint32_t row = (uint32_t)imin((P % TCH) / CPR, last), c = P % CPR;
+            const int prow = (P % TCH) / CPR;
+            const uint32_t row = (uint32_t)imin(prow, last);
+            const uint32_t c = (uint32_t)((P % CPR) ^ hswz<D>(prow));
             const char *src = tile == 0 ? qrow + (row * ldq_b + 16u * c) : grow + (row * lddo_b + 16u * c);
-            gl_lds16(src, land + (i * NT + wv * 64) * 8);
+            gl_lds16(src, sb + (i * NT + wv * 64) * 8);
+        }
+    };
+    // this thread's chunks of a stage, bf16 -> fp16 in place (dO times G)
+    auto convert = [&](auto S) {
+        uint16_t *sb = stage(S);
+        uint4 raw[SPT];
+#pragma unroll
+        for (int i = 0; i < SPT; ++i) raw[i] = *reinterpret_cast<const uint4 *>(sb + 8 * (i * NT + wv * 64 + lane));
+#pragma unroll
+        for (int i = 0; i < SPT; ++i) {
+            const float sc = chunk_tile(i) == 0 ? 1.0f : gscale;
+            const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+            const halfx8 hv = cvt8h(bf16_lo(w[0]) * sc, bf16_hi(w[0]) * sc, bf16_lo(w[1]) * sc,
+                                    bf16_hi(w[1]) * sc, bf16_lo(w[2]) * sc, bf16_hi(w[2]) * sc,
+                                    bf16_lo(w[3]) * sc, bf16_hi(w[3]) * sc);
+            *reinterpret_cast<halfx8 *>(sb + 8 * (i * NT + wv * 64 + lane)) = hv;
         }
     };
 
@@ -204,48 +227,17 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
         dvacc[i] = zero16();
     }
 
-    // the step loop, compiled once with and once without the dS stores so
-    // that the stores are unconditional where they exist
-    auto run = [&](auto HAS_DS) {
-    constexpr bool has_ds = decltype(HAS_DS)::value;
-    // stored-dS path: each step's two dS chunks per lane are stored one step
-    // later, right after the next DMA is issued, so that the wait at the top
-    // of a step only covers operations issued a whole step before
-    uint16_t *pend_blk = has_ds ? p.ds + p.ds_discard * (DS_BM * DS_BN) : nullptr;
-    halfx8 pend[2] = {};
-    if (nsteps > 0) issue(0);
-    for (int t = 0; t < nsteps; ++t) {
-        // wait for this step's DMA, take this thread's chunks, then once
-        // every wave is done with the previous step put them in cs as fp16
-        // (dO times G), refill land with step t + 1, store the previous
-        // step's dS and publish cs.  The barriers wait for LDS only: the DMA
-        // and the stores just issued stay in flight.
-        vm_wait<0>();
-        uint4 raw[SPT];
-#pragma unroll
-        for (int i = 0; i < SPT; ++i) raw[i] = *reinterpret_cast<const uint4 *>(land + 8 * (i * NT + wv * 64 + lane));
+    // step t in stage S: publish the stage (converted by every thread) with
+    // a barrier that also frees the other stage (read by step t - 1), start
+    // the DMA of step t + 1 into it, compute S, dP, P, dS, dV and dK, then
+    // wait for that DMA and convert this thread's share of it in place.  One
+    // barrier per step; it waits for LDS only, so the DMA stays in flight.
+    auto step = [&](int t, auto S, auto HAS_DS) {
+        constexpr int sidx = decltype(S)::value;
+        constexpr bool has_ds = decltype(HAS_DS)::value;
         barrier_lds();
-#pragma unroll
-        for (int i = 0; i < SPT; ++i) {
-            const int P = i * NT + wv * 64 + lane;
-            const int tile = chunk_tile(i);
-            const int row = (P % TCH) / CPR, c = P % CPR;
-            const float sc = tile == 0 ? 1.0f : gscale;
-            const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-            const halfx8 hv = cvt8h(bf16_lo(w[0]) * sc, bf16_hi(w[0]) * sc, bf16_lo(w[1]) * sc,
-                                    bf16_hi(w[1]) * sc, bf16_lo(w[2]) * sc, bf16_hi(w[2]) * sc,
-                                    bf16_lo(w[3]) * sc, bf16_hi(w[3]) * sc);
-            *reinterpret_cast<halfx8 *>(cs + tile * TILE + row * D + 8 * (c ^ hswz<D>(row))) = hv;
-        }
-        issue(t + 1);
-        if constexpr (has_ds) {
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2)
-                *reinterpret_cast<halfx8 *>(pend_blk + 8 * ds_frag_chunk(kw, 2 * rh + h2, l32, hl)) =
-                    pend[h2];
-        }
-        barrier_lds();
-        const uint16_t *sq = cs, *sg = cs + TILE;
+        issue(t + 1, std::integral_constant<int, 1 - sidx>{});
+        const uint16_t *sq = stage(S), *sg = stage(S) + TILE;
         int m0, m1;
         step_rows(t, m0, m1);
         m0 = uniform(m0);
@@ -266,19 +258,6 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
         if (!tstep && kj >= p.k2e) W = imin(W, p.k1);
         const uint32_t Wu = (uint32_t)imax(W, 0);
         const bool tv = !tstep || ((kj < sd.U) & ((sd.U - kj < p.k1) | (kj < p.k2e)));
-
-        // stored-dS path: the block of this key tile's slot among the key
-        // tiles the 64-row tile [m0, m1) visits (the order dQ reads them
-        // in), or the discard block
-        if constexpr (has_ds) {
-            const int rt = m0 < sd.U ? m0 / DS_BM : cdiv(sd.U, DS_BM) + (m0 - sd.U) / DS_BM;
-            const int slot = t < DS_SLOT_TAB ? uniform((int)slot_tab[t])
-                                             : uniform(step_slot(m0, m1));
-            const int64_t blk = (slot >= 0 && slot < p.ds_slots)
-                                    ? 1 + ((int64_t)(rt_first + rt) * p.H + h) * p.ds_slots + slot
-                                    : p.ds_discard;  // block 0 is the zero block
-            pend_blk = p.ds + blk * (DS_BM * DS_BN);
-        }
 
         // S = Q K^T and G dP = (G dO) V^T for this wave's 32 rows x 32 keys
         floatx16 sacc = zero16(), pacc = zero16();
@@ -311,39 +290,67 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
             sacc[r] = a;
             pacc[r] = g * fmaf(a, fmaf(-alpha, sgm, alpha), sgm);
         }
+        halfx8 pa[2], da[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int o = 8 * h2;
+            pa[h2] = cvt8h(sacc[o], sacc[o + 1], sacc[o + 2], sacc[o + 3], sacc[o + 4], sacc[o + 5],
+                           sacc[o + 6], sacc[o + 7]);
+            da[h2] = cvt8h(pacc[o], pacc[o + 1], pacc[o + 2], pacc[o + 3], pacc[o + 4], pacc[o + 5],
+                           pacc[o + 6], pacc[o + 7]);
+        }
         // dV += P^T (G dO), dK += (G dS)^T Q over the two 16-row chunks; the
         // accumulator's row order (8*(r/4) + 4*hl + r%4) is the k order of
         // the transposing reads
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-            const int o = 8 * h2;
-            const halfx8 pa = cvt8h(sacc[o], sacc[o + 1], sacc[o + 2], sacc[o + 3], sacc[o + 4],
-                                    sacc[o + 5], sacc[o + 6], sacc[o + 7]);
-            const halfx8 da = cvt8h(pacc[o], pacc[o + 1], pacc[o + 2], pacc[o + 3], pacc[o + 4],
-                                    pacc[o + 5], pacc[o + 6], pacc[o + 7]);
-            if constexpr (has_ds) pend[h2] = da;
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
                 const uint2 g0 = tr_read_b64(sg + t_off(h2, 0, db));
                 const uint2 g1 = tr_read_b64(sg + t_off(h2, 1, db));
-                dvacc[db] = mfma32h(pa, __builtin_bit_cast(halfx8, make_uint4(g0.x, g0.y, g1.x, g1.y)),
+                dvacc[db] = mfma32h(pa[h2], __builtin_bit_cast(halfx8, make_uint4(g0.x, g0.y, g1.x, g1.y)),
                                     dvacc[db]);
                 const uint2 q0 = tr_read_b64(sq + t_off(h2, 0, db));
                 const uint2 q1 = tr_read_b64(sq + t_off(h2, 1, db));
-                dkacc[db] = mfma32h(da, __builtin_bit_cast(halfx8, make_uint4(q0.x, q0.y, q1.x, q1.y)),
+                dkacc[db] = mfma32h(da[h2], __builtin_bit_cast(halfx8, make_uint4(q0.x, q0.y, q1.x, q1.y)),
                                     dkacc[db]);
             }
         }
-    }
-    if constexpr (has_ds) {
-        if (nsteps > 0) {
+        // the next stage (its DMA was issued at the top of this step) while
+        // the products run, then this step's dS stores: the next wait, a step
+        // later, finds both the next DMA and these stores long issued
+        vm_wait<0>();
+        convert(std::integral_constant<int, 1 - sidx>{});
+        // stored-dS path: the block of this key tile's slot among the key
+        // tiles the 64-row tile [m0, m1) visits (the order dQ reads them
+        // in), or the discard block
+        if constexpr (has_ds) {
+            const int rt = m0 < sd.U ? m0 / DS_BM : cdiv(sd.U, DS_BM) + (m0 - sd.U) / DS_BM;
+            const int slot = t < DS_SLOT_TAB ? uniform((int)slot_tab[t])
+                                             : uniform(step_slot(m0, m1));
+            const int64_t blk = (slot >= 0 && slot < p.ds_slots)
+                                    ? 1 + ((int64_t)(rt_first + rt) * p.H + h) * p.ds_slots + slot
+                                    : p.ds_discard;  // block 0 is the zero block
+            uint16_t *dsblk = p.ds + blk * (DS_BM * DS_BN);
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2)
-                *reinterpret_cast<halfx8 *>(pend_blk + 8 * ds_frag_chunk(kw, 2 * rh + h2, l32, hl)) =
-                    pend[h2];
+                *reinterpret_cast<halfx8 *>(dsblk + 8 * ds_frag_chunk(kw, 2 * rh + h2, l32, hl)) =
+                    da[h2];
         }
-    }
-    vm_wait<0>();  // no DMA (of the clamped step past the end) left in flight
+    };
+    // the step loop, compiled once with and once without the dS stores so
+    // that the stores are unconditional where they exist; two steps per
+    // iteration so that each stage's addresses are compile-time
+    auto run = [&](auto HAS_DS) {
+        if (nsteps == 0) return;
+        issue(0, std::integral_constant<int, 0>{});
+        vm_wait<0>();
+        convert(std::integral_constant<int, 0>{});
+        for (int t = 0; t < nsteps; t += 2) {
+            step(t, std::integral_constant<int, 0>{}, HAS_DS);
+            if (t + 1 < nsteps) step(t + 1, std::integral_constant<int, 1>{}, HAS_DS);
+        }
+        vm_wait<0>();  // no DMA (of the clamped step past the end) left in flight
     };
     if (p.ds != nullptr) run(std::true_type{});
     else run(std::false_type{});
@@ -353,8 +360,8 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
     // after the barrier); region e holds 32 keys x D floats
     __syncthreads();
     auto region = [&](int e) -> float * {
-        // kv holds regions 0-3, land 4-5, cs 6-7
-        uint16_t *a = e < 4 ? kv + (e & 3) * (64 * D) : (e < 6 ? land : cs) + (e & 1) * (64 * D);
+        // kv holds regions 0-3, cs0 4-5, cs1 6-7
+        uint16_t *a = e < 4 ? kv + (e & 3) * (64 * D) : (e < 6 ? cs0 : cs1) + (e & 1) * (64 * D);
         return reinterpret_cast<float *>(a);
     };
     floatx16 *mine = rh == 0 ? dkacc : dvacc;    // the sum this wave writes out
