@@ -6,32 +6,55 @@
 // there is no running max or rescale: the output accumulates SiLU(S) V
 // directly and 1/N is applied once at the end.
 //
-// Work item: one row tile of up to 128 rows (4 waves x 32) of one head.  It
-// visits only the key tiles holding visible keys (global prefix, local band,
-// and for target rows the history window of the first target plus the
-// diagonal), 64 keys per step.  Per step each wave computes
-//   S^T (64 keys x 32 rows) = K Q^T      (K from LDS, Q^T held in registers)
+// Work item: one row tile of up to 128 rows (4 waves x 32) of one head, two
+// workgroups per CU.  It visits only the key tiles holding visible keys
+// (global prefix, local band, and for target rows the history window of the
+// first target plus the diagonal), 64 keys per step.  Per step each wave
+// computes, per 32-key block,
+//   S^T (32 keys x 32 rows) = K Q^T      (K from LDS, Q^T held in registers)
 //   P^T = mask(S^T) * sigmoid(alpha S^T)  in registers, rounded to fp16
-//   O^T (D x 32 rows)     += V^T P^T     (V^T from LDS, converted to fp16)
+//   O^T (D x 32 rows)     += V^T P^T     (V^T by transposing LDS reads)
 // Computing S transposed puts the rows in the MFMA's lane dimension, so P^T
-// feeds the second MFMA as its B operand straight from the accumulator; the
-// V tile is transposed once when it is staged into LDS.  K/V tiles are double
-// buffered and the next tile's HBM loads are in flight during the MFMAs.
+// feeds the second MFMA as its B operand straight from the accumulator.  The
+// K and V rows of the next step come HBM -> LDS by DMA into the idle one of
+// two stages, already in the swizzled layout; after the step's products each
+// thread converts its own V chunks there to fp16 in place.  One LDS-only
+// barrier per step, so the DMA stays in flight across it.
+#include <type_traits>
+
 #include "sla_device.h"
 #include "sla_kernels.h"
-#include "sla_tiles.h"
 
 namespace sla {
+
+// 16-byte chunk swizzle of the [64][D] K and V stage tiles: logical chunk c
+// of row r sits at c ^ fswz<D>(r), u = r*D/128 (the 256-byte bank row),
+// Q4 = D/32.  The 16 rows of a 16-lane pass of a 16-byte read, and the 4 rows
+// x 64 bytes of a 32-lane pass of a transposing read, hit distinct banks.
+template <int D>
+__device__ __forceinline__ int fswz(int r)
+{
+    constexpr int Q4 = D / 32;
+    const int u = r * D / 128;
+    return 4 * (u % Q4) + (u / Q4) % 4;
+}
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
 {
     constexpr int BM = FWD_BM, BN = FWD_BN;
+    constexpr int NT = 256;
     constexpr int NC = D / 16;   // 16-wide contraction chunks of Q.K
     constexpr int NDB = D / 32;  // 32-wide output blocks
-    static_assert(BN == 64, "transposed tiles assume 64 keys");
-    __shared__ __align__(16) uint16_t sk[2][BN * D];
-    __shared__ __align__(16) uint16_t svt[2][D * BN];
+    constexpr int CPR = D / 8;   // 16-byte chunks per row
+    constexpr int TCH = BN * CPR;   // chunks of one 64-key K (or V) tile
+    constexpr int KPT = TCH / NT;   // DMA loads per thread and tile
+    static_assert(BN == 64 && BM == 128, "64-key steps over 128-row tiles");
+    static_assert(TCH % NT == 0 && 2 * KPT <= 8, "whole DMA rounds, at most 8 per stage");
+    // two stages of [K | V] rows (K bf16, V fp16 after the in-place
+    // conversion); separate arrays so that the compiler can tell the DMA into
+    // one from the reads of the other
+    __shared__ __align__(16) uint16_t st0[2 * BN * D], st1[2 * BN * D];
 
     const int nrec = p.s.fwd_base[p.B];
     const int item = xcd_remap(blockIdx.x, nrec * p.H);
@@ -46,7 +69,7 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
     r1 = uniform(r1);
     const Ranges kr = fwd_key_ranges(sd.L, sd.U, p.k1, p.k2e, r0, r1, BN);
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
     const int l32 = lane & 31, hl = lane >> 5;
 
     const uint16_t *qg = reinterpret_cast<const uint16_t *>(p.q) + sd.base * p.ldq + h * D;
@@ -66,26 +89,68 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
 #pragma unroll
     for (int i = 0; i < NDB; ++i) oacc[i] = zero16();
 
-    Tile64<D> kt, vt;
-    int c_next = cur.start(0, BN);
-    // keys at or past L (last tile of a sequence) hold copies of key L - 1;
-    // such tiles are never "full", and the mask removes them
-    if (ntiles > 0) {
-        kt.load_clamped(kg, p.ldk, c_next, sd.L, tid);
-        vt.load_clamped(vg, p.ldv, c_next, sd.L, tid);
-    }
-    const float nal2e = p.neg_alpha_log2e;
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        const int c0 = uniform(c_next);
-        kt.store_rows(sk[buf], tid);
-        store_transposed_f16<D>(vt, svt[buf], tid, 1.0f);
-        c_next = cur.start(t + 1, BN);
-        if (t + 1 < ntiles) {
-            kt.load_clamped(kg, p.ldk, c_next, sd.L, tid);
-            vt.load_clamped(vg, p.ldv, c_next, sd.L, tid);
+    auto stage = [&](auto S) -> uint16_t * {
+        if constexpr (decltype(S)::value == 0) return st0;
+        else return st1;
+    };
+    // DMA of the K and V rows of key tile t into a stage: chunk P = i*NT + tid
+    // of a tile is physical chunk P % CPR of key row P / CPR and holds its
+    // logical chunk (P % CPR) ^ fswz(row); keys at or past L read key L - 1
+    // (such tiles are never "full", and the mask removes them)
+    const uint32_t ldk_b = (uint32_t)p.ldk * 2u, ldv_b = (uint32_t)p.ldv * 2u;
+    auto issue = [&](int t, auto S) {
+        const int c0 = uniform(cur.start(t, BN));
+        const int last = uniform(sd.L - 1 - c0);
+        const char *krow = reinterpret_cast<const char *>(kg + (int64_t)c0 * p.ldk);
+        const char *vrow = reinterpret_cast<const char *>(vg + (int64_t)c0 * p.ldv);
+        uint16_t *sb = stage(S);
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int P = i * NT + tid;
+            const int prow = P / CPR;
+            const uint32_t row = (uint32_t)imin(prow, last);
+            const uint32_t c = (uint32_t)((P % CPR) ^ fswz<D>(prow));
+            gl_lds16(krow + (row * ldk_b + 16u * c), sb + (i * NT + wv * 64) * 8);
+            gl_lds16(vrow + (row * ldv_b + 16u * c), sb + (TCH + i * NT + wv * 64) * 8);
         }
-        __syncthreads();
+    };
+    // this thread's V chunks of a stage, bf16 -> fp16 in place
+    auto convert = [&](auto S) {
+        uint16_t *sv = stage(S) + BN * D;
+        uint4 raw[KPT];
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) raw[i] = *reinterpret_cast<const uint4 *>(sv + 8 * (i * NT + tid));
+#pragma unroll
+        for (int i = 0; i < KPT; ++i)
+            *reinterpret_cast<halfx8 *>(sv + 8 * (i * NT + tid)) = bf16x8_to_halfx8(as_bf16x8(raw[i]));
+    };
+
+    // per-lane LDS offsets (elements).  K operand: key row 32*kb + l32,
+    // logical chunk 2c + hl.  V^T operand by transposing reads (quarter
+    // q = lane/16, j = lane%16): keys 32*kb + 16*h2 + 8*rr + 4*(q/2) + j/4,
+    // d-columns 32*db + 16*(q%2) + 4*(j%4); the keys come in the order in
+    // which the S^T accumulator hands them to P^T (8*(r/4) + 4*hl + r%4).
+    const int q4 = lane >> 4, j16 = lane & 15;
+    auto k_off = [&](int kb, int c) {
+        const int r = 32 * kb + l32;
+        return r * D + 8 * ((2 * c + hl) ^ fswz<D>(r));
+    };
+    auto v_off = [&](int kb, int h2, int rr, int db) {
+        const int row = 32 * kb + 16 * h2 + 8 * rr + 4 * (q4 >> 1) + (j16 >> 2);
+        const int col = 32 * db + 16 * (q4 & 1) + 4 * (j16 & 3);
+        return row * D + 8 * ((col >> 3) ^ fswz<D>(row)) + (col & 7);
+    };
+
+    const float nal2e = p.neg_alpha_log2e;
+    const uint32_t k1u = (uint32_t)p.k1;
+    auto step = [&](int t, auto S) {
+        constexpr int sidx = decltype(S)::value;
+        barrier_lds();  // publishes stage S, frees the other (read by step t - 1)
+        // unconditional (the last step re-reads its own tile): a DMA under a
+        // branch costs the compiler its wait counts
+        issue(imin(t + 1, ntiles - 1), std::integral_constant<int, 1 - sidx>{});
+        const uint16_t *sk = stage(S), *sv = stage(S) + BN * D;
+        const int c0 = uniform(cur.start(t, BN));
 
         // mask (partial tiles only, a workgroup-uniform branch).  Element r of
         // key block kb has x = qi - j = x0 - c with the constant
@@ -96,7 +161,6 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
                                   ((r1 - 1 - c0 < p.k1) || (c0 + BN <= p.k2e))) != 0;
         const int x0 = qi - c0 - 4 * hl;
         const int mode = uniform(r0 >= sd.U ? 0 : (c0 >= p.k2e ? 1 : (c0 + BN <= p.k2e ? 2 : 0)));
-        const uint32_t k1u = (uint32_t)p.k1;
 
         // per 32-key block: S^T = K Q^T, mask, P = s * sigmoid(alpha s), then
         // O^T += V^T P^T over its two 16-key chunks; one block's S is live at a time
@@ -105,7 +169,7 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
             floatx16 sacc = zero16();
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                bf16x8 a = lds_row_chunk<D>(sk[buf], 32 * kb + l32, 2 * c + hl);
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sk + k_off(kb, c));
                 sacc = mfma32(a, qb[c], sacc);
             }
             if (!full) {
@@ -136,15 +200,32 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
             }
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
-                const int kc = 2 * kb + h2, o = 8 * h2;
-                halfx8 pb = cvt8h(sacc[o + 0], sacc[o + 1], sacc[o + 2], sacc[o + 3], sacc[o + 4],
-                                  sacc[o + 5], sacc[o + 6], sacc[o + 7]);
+                const int o = 8 * h2;
+                const halfx8 pb = cvt8h(sacc[o + 0], sacc[o + 1], sacc[o + 2], sacc[o + 3],
+                                        sacc[o + 4], sacc[o + 5], sacc[o + 6], sacc[o + 7]);
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    halfx8 a = lds_t_chunk_h(svt[buf], 32 * db + l32, 2 * kc + hl);
-                    oacc[db] = mfma32h(a, pb, oacc[db]);
+                    const uint2 v0 = tr_read_b64(sv + v_off(kb, h2, 0, db));
+                    const uint2 v1 = tr_read_b64(sv + v_off(kb, h2, 1, db));
+                    oacc[db] = mfma32h(__builtin_bit_cast(halfx8, make_uint4(v0.x, v0.y, v1.x, v1.y)),
+                                       pb, oacc[db]);
                 }
             }
+        }
+        // the next stage: wait for its DMA (issued at the top of this step)
+        // explicitly, then convert it.  After the last step this re-converts
+        // a stage nobody reads.
+        vm_wait<0>();
+        convert(std::integral_constant<int, 1 - sidx>{});
+    };
+
+    if (ntiles > 0) {
+        issue(0, std::integral_constant<int, 0>{});
+        vm_wait<0>();
+        convert(std::integral_constant<int, 0>{});
+        for (int t = 0; t < ntiles; t += 2) {
+            step(t, std::integral_constant<int, 0>{});
+            if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
         }
     }
 
