@@ -165,11 +165,18 @@ __device__ __forceinline__ void gl_lds16(const void *src, uint16_t *lds_wave_bas
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding.
+// The s_waitcnt builtin (rather than inline asm) lets the compiler's own wait
+// tracking see the wait, so it adds no conservative vmcnt(0) later; the empty
+// asm statements with a memory clobber keep every memory access on its side.
+// gfx9 encoding: vmcnt[3:0] and [15:14], expcnt[6:4] and lgkmcnt[11:8] (the
+// latter two left at their maxima, i.e. not waited for).
 template <int N>
 __device__ __forceinline__ void vm_wait()
 {
     static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
 }
 
 // Workgroup barrier for LDS filled by DMA only, without the memory fence of

@@ -52,6 +52,11 @@ __global__ __launch_bounds__(DQ_THREADS, 2) void sla_bwd_dq_ds_kernel(AttnParams
     static_assert(KPT + SPT <= 8, "at most 8 DMA loads per thread and stage");
     // one array per stage: K rows, then the two halves' dS
     __shared__ __align__(16) uint16_t st0[(KCH + SCH) * 8], st1[(KCH + SCH) * 8];
+    // per step: key tile start and the two halves' dS block indices, computed
+    // once per item (each half visits at most DS_MAX_SLOTS key tiles, so a
+    // 128-row tile has at most 2 * 2 * DS_MAX_SLOTS steps)
+    constexpr int DQ_TAB = 4 * DS_MAX_SLOTS;
+    __shared__ int4 steptab[DQ_TAB];
 
     const int nrec = uniform(p.s.fwd_base[p.B]);
     const int item = xcd_remap(blockIdx.x, nrec * p.H);
@@ -102,27 +107,42 @@ __global__ __launch_bounds__(DQ_THREADS, 2) void sla_bwd_dq_ds_kernel(AttnParams
     };
     auto dst = [&](auto S) -> uint16_t * { return kst(S) + KCH * 8; };
 
+    for (int t = tid; t < imin(nsteps, DQ_TAB); t += NT) {
+        const int c0 = cur.start(t >> 1, DS_BN);
+        steptab[t] = make_int4(c0, (int)block_of(0, kr0, c0, true), (int)block_of(1, kr1, c0, true), 0);
+    }
+    __syncthreads();
+
     // DMA of step t (t >= nsteps: the last keys again, with zero dS): K row
     // chunk P (key P / CPR of the step, physical chunk P % CPR) holds logical
     // chunk (P % CPR) ^ kh_swz(key), keys past L read key L - 1 (their dS is
     // zero); dS chunks 0..HCH-1 from half 0's block, HCH.. from half 1's, each
     // the key half t%2 of the stored block (the dK/dV kernel stores its waves'
-    // 32-key fragments one after another, so a key half is contiguous)
+    // 32-key fragments one after another, so a key half is contiguous).  The
+    // K rows are a workgroup-uniform base plus a 32-bit lane offset.
+    const uint32_t ldkh_b = (uint32_t)ldkh * 2u;
     auto issue = [&](int t, auto S) {
-        const int tt = imin(t, nsteps - 1);
-        const int c0 = cur.start(tt >> 1, DS_BN);
+        const int tt = imin(imin(t, nsteps - 1), DQ_TAB - 1);
+        const int4 e = steptab[tt];
         const int kh = tt & 1;
-        const bool live = t < nsteps;
-        const uint16_t *b0 = p.ds + BLK * block_of(0, kr0, c0, live) + 8 * HCH * kh;
-        const uint16_t *b1 = p.ds + BLK * block_of(1, kr1, c0, live) + 8 * HCH * kh;
+        const int live = t < nsteps;
+        // rows kbase + key, clamped to L - 1, as base kb0 = min(kbase, L - 1)
+        // plus a lane offset in [0, L - 1 - kb0] (kbase may lie past the end
+        // of the sequence for the second half of its last key tile)
+        const int kbase = uniform(e.x) + DQ_KEYS * kh;
+        const int kb0 = imin(kbase, sd.L - 1);
+        const int last = sd.L - 1 - kb0, skip = kbase - kb0;
+        const uint16_t *b0 = p.ds + BLK * (int64_t)(live * uniform(e.y)) + 8 * HCH * kh;
+        const uint16_t *b1 = p.ds + BLK * (int64_t)(live * uniform(e.z)) + 8 * HCH * kh;
+        const char *krow = reinterpret_cast<const char *>(khg + (int64_t)kb0 * ldkh);
         uint16_t *ks = kst(S), *ds = dst(S);
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int P = i * NT + wv * 64 + lane;
             const int key = P / CPR;
-            const int c = (P % CPR) ^ kh_swz<D>(key);
-            const int row = imin(c0 + DQ_KEYS * kh + key, sd.L - 1);
-            gl_lds16(khg + (int64_t)row * ldkh + 8 * c, ks + (i * NT + wv * 64) * 8);
+            const uint32_t c = (uint32_t)((P % CPR) ^ kh_swz<D>(key));
+            const uint32_t row = (uint32_t)imin(key + skip, last);
+            gl_lds16(krow + (row * ldkh_b + 16u * c), ks + (i * NT + wv * 64) * 8);
         }
 #pragma unroll
         for (int i = 0; i < SPT; ++i) {
