@@ -323,7 +323,8 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
         convert(std::integral_constant<int, 1 - sidx>{});
         // stored-dS path: the block of this key tile's slot among the key
         // tiles the 64-row tile [m0, m1) visits (the order dQ reads them
-        // in), or the discard block
+        // in), or the discard block; streamed out (dQ reads it back from HBM
+        // after this kernel)
         if constexpr (has_ds) {
             const int rt = m0 < sd.U ? m0 / DS_BM : cdiv(sd.U, DS_BM) + (m0 - sd.U) / DS_BM;
             const int slot = t < DS_SLOT_TAB ? uniform((int)slot_tab[t])
@@ -334,8 +335,7 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
             uint16_t *dsblk = p.ds + blk * (DS_BM * DS_BN);
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2)
-                *reinterpret_cast<halfx8 *>(dsblk + 8 * ds_frag_chunk(kw, 2 * rh + h2, l32, hl)) =
-                    da[h2];
+                st16_nt(dsblk + 8 * ds_frag_chunk(kw, 2 * rh + h2, l32, hl), da[h2]);
         }
     };
     // the step loop, compiled once with and once without the dS stores so

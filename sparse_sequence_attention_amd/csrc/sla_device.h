@@ -221,6 +221,14 @@ __host__ __device__ inline int ds_frag_chunk(int wv, int qc, int kl, int hl)
     return (wv * 4 + qc) * 64 + ((2 * kl + hl) ^ (8 * (qc & 1)));
 }
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+// 16-byte store marked non-temporal (streamed out, not kept in the caches):
+// for data written once and read back only by a later kernel.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st16_nt(void *p, const halfx8 &v)
+{
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v), reinterpret_cast<u32x4_t *>(p));
+}
 __device__ __forceinline__ uint4 ld16_or_zero(const void *p, bool ok)
 {
     uint4 z = {0u, 0u, 0u, 0u};
