@@ -164,6 +164,14 @@ __device__ __forceinline__ void gl_lds16(const void *src, uint16_t *lds_wave_bas
     __builtin_amdgcn_global_load_lds(src, (lds_void_t *)lds_wave_base, 16, 0, 0);
 }
 
+// As gl_lds16, for data read exactly once: the non-temporal hint keeps it
+// from displacing reused data in the caches.
+__device__ __forceinline__ void gl_lds16_nt(const void *src, uint16_t *lds_wave_base)
+{
+    constexpr int kNonTemporal = 2;  // cache-policy bit NT
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)lds_wave_base, 16, 0, kNonTemporal);
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding.
 // The s_waitcnt builtin (rather than inline asm) lets the compiler's own wait
 // tracking see the wait, so it adds no conservative vmcnt(0) later; the empty

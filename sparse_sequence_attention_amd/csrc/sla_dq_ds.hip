@@ -148,7 +148,7 @@ __global__ __launch_bounds__(DQ_THREADS, 2) void sla_bwd_dq_ds_kernel(AttnParams
         for (int i = 0; i < SPT; ++i) {
             const int P = i * NT + wv * 64 + lane;  // uniform half per DMA round
             const uint16_t *src = (i * NT < HCH) ? b0 + 8 * P : b1 + 8 * (P - HCH);
-            gl_lds16(src, ds + (i * NT + wv * 64) * 8);
+            gl_lds16_nt(src, ds + (i * NT + wv * 64) * 8);  // each dS block is read once
         }
     };
 
