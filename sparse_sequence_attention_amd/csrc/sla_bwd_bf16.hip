@@ -58,11 +58,9 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
     constexpr int NC = D / 16, NDB = D / 32, CPR = D / 8;
     constexpr int TILE = BM * D;             // elements of one staged 64-row tile
     constexpr int TCH = BM * CPR;            // 16-byte chunks of one staged tile
-    constexpr int SPT = 2 * TCH / NT;        // DMA loads per thread and step (Q, then dO)
     constexpr int KVS = D + 8;               // padded K / V row: 16-byte reads of 16
                                              // consecutive keys hit distinct banks
     static_assert(BM == 64 && BN == 128, "64-row steps over 128-key tiles");
-    static_assert((2 * TCH) % NT == 0 && SPT <= 8, "whole DMA rounds, at most 8 per step");
     // kv: K then V of the key tile (fp16, padded rows).  cs0 / cs1: two
     // stages of Q and G dO rows (swizzled); the DMA brings a step's bf16 rows
     // into one stage while the other is read, and each thread then converts
@@ -152,16 +150,16 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
     const float gscale = *p.grad_scale;
     const bool key_tile_full = (it.c1 - it.c0 == BN);
 
-    // this thread's chunks of a step: chunk P = i*NT + 64*wave + lane of a
-    // stage is physical chunk P % CPR of row (P % TCH) / CPR of tile P / TCH
-    // (0: Q, 1: dO); the DMA fills it with logical chunk (P % CPR) ^ hswz(row)
-    // and the same thread converts it in place.  The tile of the i-th chunk
-    // is wave-uniform, and a compile-time constant when a DMA round never
-    // straddles the two tiles.
-    auto chunk_tile = [&](int i) {
-        if constexpr (TCH % NT == 0) return (i * NT) / TCH;
-        else return (i * NT + wv * 64) / TCH;
-    };
+    // Staging is done by the rh = 0 waves alone: the SIMD issues the older
+    // wave of a pair first, so these finish their products earlier and would
+    // otherwise wait at the barrier.  Staging thread t (< NS) owns chunks
+    // P = i*NS + t of a stage: physical chunk P % CPR of row (P % TCH) / CPR
+    // of tile P / TCH (0: Q, 1: dO); the DMA fills it with logical chunk
+    // (P % CPR) ^ hswz(row) and the same thread converts it in place.
+    constexpr int NS = NT / 2;            // staging threads
+    constexpr int SPS = 2 * TCH / NS;     // DMA loads per staging thread and step
+    static_assert(TCH % NS == 0 && SPS <= 8, "whole DMA rounds, at most 8 per thread");
+    auto chunk_tile = [&](int i) { return (i * NS) / TCH; };
     auto stage = [&](auto S) -> uint16_t * {
         if constexpr (decltype(S)::value == 0) return cs0;
         else return cs1;
@@ -179,30 +177,30 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
         const char *grow = reinterpret_cast<const char *>(gg + (int64_t)m0 * p.lddo);
         uint16_t *sb = stage(S);
 #pragma unroll
-        for (int i = 0; i < SPT; ++i) {
-            const int P = i * NT + wv * 64 + lane;
+        for (int i = 0; i < SPS; ++i) {
+            const int P = i * NS + wv * 64 + lane;
             const int tile = chunk_tile(i);
             const int prow = (P % TCH) / CPR;
             const uint32_t row = (uint32_t)imin(prow, last);
             const uint32_t c = (uint32_t)((P % CPR) ^ hswz<D>(prow));
             const char *src = tile == 0 ? qrow + (row * ldq_b + 16u * c) : grow + (row * lddo_b + 16u * c);
-            gl_lds16(src, sb + (i * NT + wv * 64) * 8);
+            gl_lds16(src, sb + (i * NS + wv * 64) * 8);
         }
     };
     // this thread's chunks of a stage, bf16 -> fp16 in place (dO times G)
     auto convert = [&](auto S) {
         uint16_t *sb = stage(S);
-        uint4 raw[SPT];
+        uint4 raw[SPS];
 #pragma unroll
-        for (int i = 0; i < SPT; ++i) raw[i] = *reinterpret_cast<const uint4 *>(sb + 8 * (i * NT + wv * 64 + lane));
+        for (int i = 0; i < SPS; ++i) raw[i] = *reinterpret_cast<const uint4 *>(sb + 8 * (i * NS + wv * 64 + lane));
 #pragma unroll
-        for (int i = 0; i < SPT; ++i) {
+        for (int i = 0; i < SPS; ++i) {
             const float sc = chunk_tile(i) == 0 ? 1.0f : gscale;
             const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
             const halfx8 hv = cvt8h(bf16_lo(w[0]) * sc, bf16_hi(w[0]) * sc, bf16_lo(w[1]) * sc,
                                     bf16_hi(w[1]) * sc, bf16_lo(w[2]) * sc, bf16_hi(w[2]) * sc,
                                     bf16_lo(w[3]) * sc, bf16_hi(w[3]) * sc);
-            *reinterpret_cast<halfx8 *>(sb + 8 * (i * NT + wv * 64 + lane)) = hv;
+            *reinterpret_cast<halfx8 *>(sb + 8 * (i * NS + wv * 64 + lane)) = hv;
         }
     };
 
@@ -236,7 +234,7 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
         constexpr int sidx = decltype(S)::value;
         constexpr bool has_ds = decltype(HAS_DS)::value;
         barrier_lds();
-        issue(t + 1, std::integral_constant<int, 1 - sidx>{});
+        if (rh == 0) issue(t + 1, std::integral_constant<int, 1 - sidx>{});
         const uint16_t *sq = stage(S), *sg = stage(S) + TILE;
         int m0, m1;
         step_rows(t, m0, m1);
@@ -319,8 +317,10 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
         // the next stage (its DMA was issued at the top of this step) while
         // the products run, then this step's dS stores: the next wait, a step
         // later, finds both the next DMA and these stores long issued
-        vm_wait<0>();
-        convert(std::integral_constant<int, 1 - sidx>{});
+        if (rh == 0) {
+            vm_wait<0>();
+            convert(std::integral_constant<int, 1 - sidx>{});
+        }
         // stored-dS path: the block of this key tile's slot among the key
         // tiles the 64-row tile [m0, m1) visits (the order dQ reads them
         // in), or the discard block; streamed out (dQ reads it back from HBM
@@ -343,9 +343,11 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
     // iteration so that each stage's addresses are compile-time
     auto run = [&](auto HAS_DS) {
         if (nsteps == 0) return;
-        issue(0, std::integral_constant<int, 0>{});
-        vm_wait<0>();
-        convert(std::integral_constant<int, 0>{});
+        if (rh == 0) {
+            issue(0, std::integral_constant<int, 0>{});
+            vm_wait<0>();
+            convert(std::integral_constant<int, 0>{});
+        }
         for (int t = 0; t < nsteps; t += 2) {
             step(t, std::integral_constant<int, 0>{}, HAS_DS);
             if (t + 1 < nsteps) step(t + 1, std::integral_constant<int, 1>{}, HAS_DS);
