@@ -32,7 +32,17 @@
  * [T, ...] tensor.  offsets is int64 [B+1], offsets[0] = 0, non-decreasing,
  * offsets[B] = total_tokens.  num_targets is int32 [B] (or NULL = no targets),
  * 0 <= num_targets[b] <= L_b; targets are the last num_targets[b] tokens.
- * These device-resident facts are trusted (checking them needs a sync).
+ * These device-resident facts are trusted (checking them needs a sync),
+ * unless the environment variable SLA_VALIDATE is set to a value other than
+ * "0": then sla_fwd, sla_bwd, sla_bwd_stage, sla_schedule, stu_layer_fwd and
+ * stu_truncate first run a check kernel on the caller's stream, synchronise
+ * it, and return SLA_ERR_INVALID (message: which fact, which sequence) before
+ * any other kernel when offsets[0] != 0, offsets decrease, offsets[B] !=
+ * total_tokens, a num_targets[b] lies outside [0, L_b], or (stu_truncate)
+ * contextual_len + num_targets[b] > L_b for a sequence that keeps history.
+ * The check borrows the first 8 bytes of the workspace (of new_offsets for
+ * stu_truncate) and is a debugging aid: it costs a synchronisation per call
+ * and cannot be captured in a graph.
  *
  * Per-head tensors are [T][H][d] row-major with a token stride ld (elements)
  * >= H*d, so Q/K/V/U may be strided column blocks of one fused projection

@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -103,6 +104,39 @@ sla_status_t validate_tensor(const char *name, const void *ptr, int64_t ld, cons
                     name, (long long)ld);
     if (!aligned16(ptr)) return fail(SLA_ERR_UNSUPPORTED, "%s is not 16-byte aligned", name);
     return SLA_OK;
+}
+
+// Optional validation mode (environment SLA_VALIDATE, read at every call):
+// check the device-resident layout facts, synchronising the stream, before
+// any other kernel of the call.  scratch: 8 bytes of device memory the call
+// owns and overwrites later anyway.
+bool validate_mode()
+{
+    const char *e = std::getenv("SLA_VALIDATE");
+    return e && e[0] && !(e[0] == '0' && e[1] == 0);
+}
+
+sla_status_t validate_layout(int B, int64_t T, const int64_t *offsets, const int32_t *num_targets,
+                             int ctx, void *scratch, hipStream_t s)
+{
+    if (!validate_mode() || B == 0) return SLA_OK;
+    if (!scratch) return fail(SLA_ERR_NULL, "validation needs the workspace");
+    int32_t *res = static_cast<int32_t *>(scratch);
+    hipError_t e = launch_validate(offsets, num_targets, B, T, ctx, res, s);
+    if (e != hipSuccess) return hip_fail(e, "validation kernel");
+    int32_t host[2] = {0, -1};
+    e = hipMemcpyAsync(host, res, sizeof(host), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "validation copy");
+    switch (host[0]) {
+    case 0: return SLA_OK;
+    case 1: return fail(SLA_ERR_INVALID, "offsets[0] != 0");
+    case 2: return fail(SLA_ERR_INVALID, "offsets decrease at sequence %d", host[1]);
+    case 3: return fail(SLA_ERR_INVALID, "offsets[B] != total_tokens (%lld)", (long long)T);
+    case 4: return fail(SLA_ERR_INVALID, "num_targets[%d] outside [0, L_b]", host[1]);
+    case 5: return fail(SLA_ERR_INVALID, "contextual_len + num_targets[%d] > L_b", host[1]);
+    default: return fail(SLA_ERR_INVALID, "layout check failed (code %d)", host[0]);
+    }
 }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -258,6 +292,9 @@ sla_status_t sla_schedule(const sla_problem_t *p, int op, int32_t *records, int6
     if ((st = make_params(p, SLA_OP_FWD, workspace, ws_bytes, a)) != SLA_OK) return st;
     if ((st = check_device()) != SLA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = validate_layout(p->batch, p->total_tokens, p->offsets, p->num_targets, -1, workspace,
+                              s)) != SLA_OK)
+        return st;
     a.absmax_part = nullptr;
     hipError_t e = launch_sched(a, s);
     if (e != hipSuccess) return hip_fail(e, "schedule kernel");
@@ -321,6 +358,9 @@ sla_status_t sla_fwd(const sla_problem_t *p, const void *q, int64_t ldq, const v
     a.absmax_part = nullptr;
     a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.ldo = ldo;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = validate_layout(p->batch, p->total_tokens, p->offsets, p->num_targets, -1, workspace,
+                              s)) != SLA_OK)
+        return st;
     hipError_t e = launch_sched(a, s);
     if (e != hipSuccess) return hip_fail(e, "schedule kernel");
     e = p->dtype == SLA_BF16 ? launch_fwd_bf16(a, s) : launch_fwd_f32(a, s);
@@ -355,6 +395,9 @@ sla_status_t sla_bwd_stage(const sla_problem_t *p, int stage, const void *q, int
     a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.lddo = lddo; a.lddq = lddq; a.lddk = lddk;
     a.lddv = lddv;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = validate_layout(p->batch, p->total_tokens, p->offsets, p->num_targets, -1, workspace,
+                              s)) != SLA_OK)
+        return st;
     hipError_t e = hipSuccess;
     if (stage == SLA_BWD_ALL || stage == SLA_BWD_PREPARE) {
         if (p->dtype == SLA_BF16) {
@@ -480,6 +523,8 @@ sla_status_t stu_layer_fwd(const stu_layer_desc_t *d, const void *x, const float
     uint16_t *u16 = static_cast<uint16_t *>(uvqk);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = validate_layout(p->batch, T, p->offsets, p->num_targets, -1, workspace, s)) != SLA_OK)
+        return st;
     hipError_t e = launch_layernorm_bf16(x, ln1_w, ln1_b, n, T, D, d->ln_eps, s);
     if (e != hipSuccess) return hip_fail(e, "layernorm");
     e = launch_gemm_bf16(n, D, w_uvqk, D, b_uvqk, nullptr, 0, uvqk, NW, T, NW, D, 0, s);
@@ -520,6 +565,9 @@ sla_status_t stu_truncate(int32_t batch, int64_t total_tokens, const int64_t *of
     sla_status_t st = check_device();
     if (st != SLA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = validate_layout(batch, total_tokens, offsets, num_targets, contextual_len,
+                              new_offsets, s)) != SLA_OK)
+        return st;
     hipError_t e = launch_truncate(batch, total_tokens, offsets, num_targets, contextual_len,
                                    tail_len, x, hidden, eb, new_offsets, new_num_targets,
                                    gather_idx, x_out, capacity, nullptr, s);

@@ -53,6 +53,10 @@ struct WsLayout {
 };
 
 hipError_t launch_sched(const AttnParams &p, hipStream_t st);
+// Optional check of the jagged layout; result: int32[2] device scratch
+// (code, sequence).  ctx < 0 skips the truncation check.
+hipError_t launch_validate(const int64_t *offsets, const int32_t *num_targets, int B, int64_t T,
+                           int ctx, int32_t *result, hipStream_t st);
 // max |dO| per block into p.absmax_part (the schedule kernel folds it into
 // p.grad_scale when p.absmax_part is set)
 hipError_t launch_absmax(const AttnParams &p, hipStream_t st);

@@ -161,6 +161,59 @@ hipError_t launch_absmax(const AttnParams &p, hipStream_t st)
     return hipGetLastError();
 }
 
+// Checks of the device-resident preconditions of the jagged layout (the
+// optional validation mode).  One workgroup; result[0] = the smallest failing
+// code (0: none), result[1] = the first sequence it fails for.  Codes: 1
+// offsets[0] != 0, 2 offsets decrease at b, 3 offsets[B] != T, 4 num_targets[b]
+// outside [0, L_b], 5 contextual_len + num_targets[b] > L_b (ctx >= 0 only).
+constexpr int VALIDATE_THREADS = 256;
+
+__global__ __launch_bounds__(VALIDATE_THREADS) void sla_validate_kernel(
+    const int64_t *offsets, const int32_t *num_targets, int B, int64_t T, int ctx, int32_t *result)
+{
+    __shared__ int64_t best[VALIDATE_THREADS];
+    int64_t mine = INT64_MAX;  // (code << 32) | b of this thread's first failure
+    auto note = [&](int code, int b) {
+        const int64_t v = ((int64_t)code << 32) | (uint32_t)b;
+        mine = v < mine ? v : mine;
+    };
+    if (threadIdx.x == 0) {
+        if (offsets[0] != 0) note(1, 0);
+        if (offsets[B] != T) note(3, B);
+    }
+    for (int b = threadIdx.x; b < B; b += VALIDATE_THREADS) {
+        const int64_t L = offsets[b + 1] - offsets[b];
+        if (L < 0) note(2, b);
+        if (num_targets) {
+            const int64_t nt = num_targets[b];
+            if (nt < 0 || nt > L) note(4, b);
+            else if (ctx >= 0 && nt < L && ctx + nt > L) note(5, b);
+        }
+    }
+    best[threadIdx.x] = mine;
+    __syncthreads();
+    for (int o = VALIDATE_THREADS / 2; o > 0; o >>= 1) {
+        if (threadIdx.x < o) {
+            const int64_t a = best[threadIdx.x], c = best[threadIdx.x + o];
+            best[threadIdx.x] = a < c ? a : c;
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        const int64_t v = best[0];
+        result[0] = v == INT64_MAX ? 0 : (int32_t)(v >> 32);
+        result[1] = v == INT64_MAX ? -1 : (int32_t)(v & 0xffffffff);
+    }
+}
+
+hipError_t launch_validate(const int64_t *offsets, const int32_t *num_targets, int B, int64_t T,
+                           int ctx, int32_t *result, hipStream_t st)
+{
+    hipLaunchKernelGGL(sla_validate_kernel, dim3(1), dim3(VALIDATE_THREADS), 0, st, offsets,
+                       num_targets, B, T, ctx, result);
+    return hipGetLastError();
+}
+
 // Materialise the work list (one thread per record) so that it can be checked.
 __global__ void sla_sched_dump_kernel(const int64_t *offsets, const int32_t *num_targets, int B,
                                       int k1, int k2e, Sched s, int op, int32_t *records,
