@@ -14,6 +14,8 @@ Functions whose results are "parity pinned" and the pins (tests/test_oracle_*):
       linearity, 1/N scaling, jagged independence, target permutation).
   sla_bwd   -- central finite differences of sla_fwd, torch fp64 autograd.
   layernorm / stu_layer_fwd -- torch fp64 functional composition, W2 = 0.
+  stu_layer_bwd -- torch fp64 autograd of that composition; central finite
+      differences of stu_layer_fwd; dout = 0 gives zero gradients.
   truncate  -- direct set construction, identity when tail >= history.
 """
 from __future__ import annotations
@@ -76,6 +78,9 @@ def _load():
                                              dbl, dbl, dbl, P, P, P, P, P, P, P, P, P,
                                              i32, P, P]
         lib.oracle_stu_layer_fwd.restype = None
+        lib.oracle_stu_layer_bwd.argtypes = [i32, P, P, i32, i32, i32, i32, i64, i64, i64,
+                                             dbl, dbl, dbl] + [P] * 19
+        lib.oracle_stu_layer_bwd.restype = None
         lib.oracle_truncate.argtypes = [i32, P, P, i64, i64, P, P]
         lib.oracle_truncate.restype = i64
         lib.oracle_num_threads.argtypes = []
@@ -193,6 +198,32 @@ def stu_layer_fwd(x, offsets, num_targets, ln1_w, w_uvqk, ln2_w, w_out, *, heads
                                  *[_ptr(a) for a in keep], _store_mask(store_bf16), _ptr(out),
                                  _ptr(uvqk))
     return (out, uvqk) if want_uvqk else out
+
+
+def stu_layer_bwd(x, offsets, num_targets, ln1_w, w_uvqk, ln2_w, w_out, dout, *, heads, dqk,
+                  dv, k1, k2, ctx, N, alpha=1.0, eps=1e-5, ln1_b=None, b_uvqk=None, ln2_b=None,
+                  b_out=None):
+    """Gradients of stu_layer_fwd's output given dout, as a dict: dx [T, D],
+    dln1_w / dln1_b [D], dw_uvqk [NW, D], db_uvqk [NW], dln2_w / dln2_b [H*dv],
+    dw_out [D, H*dv], db_out [D] (fp64; the forward is recomputed in fp64)."""
+    x = _f64(x)
+    T, D = x.shape
+    nu = heads * dv
+    nw = 2 * nu + 2 * heads * dqk
+    g = dict(dx=np.zeros_like(x), dln1_w=np.zeros(D), dln1_b=np.zeros(D),
+             dw_uvqk=np.zeros((nw, D)), db_uvqk=np.zeros(nw), dln2_w=np.zeros(nu),
+             dln2_b=np.zeros(nu), dw_out=np.zeros((D, nu)), db_out=np.zeros(D))
+    offs, tg = _offs(offsets), _tg(num_targets)
+    keep = [_f64(a) if a is not None else None
+            for a in (ln1_w, ln1_b, w_uvqk, b_uvqk, ln2_w, ln2_b, w_out, b_out)]
+    do = _f64(dout)
+    _load().oracle_stu_layer_bwd(len(offs) - 1, _ptr(offs), _ptr(tg), D, heads, dqk, dv, k1,
+                                 k2, ctx, float(N), float(alpha), float(eps), _ptr(x),
+                                 *[_ptr(a) for a in keep], _ptr(do),
+                                 *[_ptr(g[k]) for k in ("dx", "dln1_w", "dln1_b", "dw_uvqk",
+                                                         "db_uvqk", "dln2_w", "dln2_b",
+                                                         "dw_out", "db_out")])
+    return g
 
 
 def _store_mask(store_bf16) -> int:

@@ -385,6 +385,191 @@ EXPORT void oracle_stu_layer_fwd(int B, const int64_t *offsets, const int32_t *n
     free(n); free(z); free(qq); free(kk); free(vv); free(uu); free(a); free(y);
 }
 
+/* Row statistics of LayerNorm: xh = (x - mean) * rstd, rstd = 1/sqrt(var + eps)
+ * (biased variance), as in oracle_layernorm. */
+static void ln_stats(int64_t rows, int64_t cols, const double *x, double eps, double *xh,
+                     double *rstd)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *xr = x + r * cols;
+        double mean = 0.0;
+        for (int64_t c = 0; c < cols; ++c) mean += xr[c];
+        mean /= (double)cols;
+        double var = 0.0;
+        for (int64_t c = 0; c < cols; ++c) var += (xr[c] - mean) * (xr[c] - mean);
+        var /= (double)cols;
+        rstd[r] = 1.0 / sqrt(var + eps);
+        for (int64_t c = 0; c < cols; ++c) xh[r * cols + c] = (xr[c] - mean) * rstd[r];
+    }
+}
+
+/* Backward of y = xh * w + b with xh the row-normalised x: given dy, adds the
+ * column sums dw += sum_r dy * xh and db += sum_r dy (if non-NULL) and writes
+ * dx = rstd * (g - mean(g) - xh * mean(g * xh)) with g = dy * w, per row. */
+static void ln_backward(int64_t rows, int64_t cols, const double *dy, const double *xh,
+                        const double *rstd, const double *w, double *dx, double *dw, double *db)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            dw[c] += dy[r * cols + c] * xh[r * cols + c];
+            if (db) db[c] += dy[r * cols + c];
+        }
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        double m1 = 0.0, m2 = 0.0;
+        for (int64_t c = 0; c < cols; ++c) {
+            const double g = dy[r * cols + c] * w[c];
+            m1 += g;
+            m2 += g * xh[r * cols + c];
+        }
+        m1 /= (double)cols;
+        m2 /= (double)cols;
+        for (int64_t c = 0; c < cols; ++c) {
+            const double g = dy[r * cols + c] * w[c];
+            dx[r * cols + c] = rstd[r] * (g - m1 - xh[r * cols + c] * m2);
+        }
+    }
+}
+
+/* SiLU'(z) = sigma(z) (1 + z (1 - sigma(z))). */
+static double dsilu(double z)
+{
+    const double s = 1.0 / (1.0 + exp(-z));
+    return s * (1.0 + z * (1.0 - s));
+}
+
+/* Gradients of one STU layer (the forward of oracle_stu_layer_fwd) given
+ * dout = dL/dout: recomputes the forward in fp64, then applies the chain rule
+ * step by step backwards through
+ *   out = y W2^T + b2 + x,  y = (ah * g2 + b2n) (.) U,  ah = LN-normalised A,
+ *   A = SLA(Q, K, V),  [U V Q K] = SiLU(z),  z = n W1^T + b1,
+ *   n = xh * g1 + b1n,  xh = LN-normalised x.
+ * Outputs (all overwritten; biases' gradients only where the pointer is
+ * non-NULL): dx [T][D], dln1_w/b [D], dw1 [NW][D], db1 [NW], dln2_w/b [NU],
+ * dw2 [D][NU], db2 [D]. */
+EXPORT void oracle_stu_layer_bwd(int B, const int64_t *offsets, const int32_t *num_targets,
+                                 int D, int H, int dqk, int dv, int64_t k1, int64_t k2,
+                                 int64_t ctx, double N, double alpha, double eps,
+                                 const double *x, const double *ln1_w, const double *ln1_b,
+                                 const double *w1, const double *b1, const double *ln2_w,
+                                 const double *ln2_b, const double *w2, const double *b2,
+                                 const double *dout, double *dx, double *dln1_w, double *dln1_b,
+                                 double *dw1, double *db1, double *dln2_w, double *dln2_b,
+                                 double *dw2, double *db2)
+{
+    (void)b2;
+    const int64_t T = offsets[B];
+    const int64_t NU = (int64_t)H * dv, NQ = (int64_t)H * dqk, NW = 2 * NU + 2 * NQ;
+    double *xh1 = malloc(sizeof(double) * T * D), *rstd1 = malloc(sizeof(double) * T);
+    double *n = malloc(sizeof(double) * T * D);
+    double *z = malloc(sizeof(double) * T * NW), *s = malloc(sizeof(double) * T * NW);
+    double *qq = malloc(sizeof(double) * T * NQ), *kk = malloc(sizeof(double) * T * NQ);
+    double *vv = malloc(sizeof(double) * T * NU), *uu = malloc(sizeof(double) * T * NU);
+    double *a = malloc(sizeof(double) * T * NU), *ah = malloc(sizeof(double) * T * NU);
+    double *rstd2 = malloc(sizeof(double) * T), *yh = malloc(sizeof(double) * T * NU);
+    double *y = malloc(sizeof(double) * T * NU), *dy = malloc(sizeof(double) * T * NU);
+    double *dyh = malloc(sizeof(double) * T * NU), *da = malloc(sizeof(double) * T * NU);
+    double *dq = malloc(sizeof(double) * T * NQ), *dk = malloc(sizeof(double) * T * NQ);
+    double *dvv = malloc(sizeof(double) * T * NU), *dz = malloc(sizeof(double) * T * NW);
+    double *dn = malloc(sizeof(double) * T * D);
+
+    /* forward */
+    ln_stats(T, D, x, eps, xh1, rstd1);
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t c = 0; c < D; ++c)
+            n[t * D + c] = xh1[t * D + c] * ln1_w[c] + (ln1_b ? ln1_b[c] : 0.0);
+    linear(T, D, NW, n, w1, b1, z);
+    for (int64_t i = 0; i < T * NW; ++i) s[i] = silu(z[i]);
+    for (int64_t t = 0; t < T; ++t) {
+        const double *sr = s + t * NW;
+        memcpy(uu + t * NU, sr, sizeof(double) * NU);
+        memcpy(vv + t * NU, sr + NU, sizeof(double) * NU);
+        memcpy(qq + t * NQ, sr + 2 * NU, sizeof(double) * NQ);
+        memcpy(kk + t * NQ, sr + 2 * NU + NQ, sizeof(double) * NQ);
+    }
+    oracle_sla_fwd(B, offsets, num_targets, H, dqk, dv, k1, k2, ctx, N, alpha, qq, kk, vv, a,
+                   NULL);
+    ln_stats(T, NU, a, eps, ah, rstd2);
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t c = 0; c < NU; ++c) {
+            yh[t * NU + c] = ah[t * NU + c] * ln2_w[c] + (ln2_b ? ln2_b[c] : 0.0);
+            y[t * NU + c] = yh[t * NU + c] * uu[t * NU + c];
+        }
+
+    /* out = y W2^T + b2 + x:  dW2 = dout^T y, db2 = colsum(dout), dy = dout W2 */
+    for (int64_t i = 0; i < D * NU; ++i) dw2[i] = 0.0;
+    if (db2)
+        for (int64_t c = 0; c < D; ++c) db2[c] = 0.0;
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t d = 0; d < D; ++d) {
+            const double g = dout[t * D + d];
+            if (db2) db2[d] += g;
+            for (int64_t c = 0; c < NU; ++c) dw2[d * NU + c] += g * y[t * NU + c];
+        }
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t c = 0; c < NU; ++c) {
+            double acc = 0.0;
+            for (int64_t d = 0; d < D; ++d) acc += dout[t * D + d] * w2[d * NU + c];
+            dy[t * NU + c] = acc;
+        }
+
+    /* y = yh (.) U:  dU = dy (.) yh, dyh = dy (.) U; yh = ah * g2 + b2n */
+    for (int64_t i = 0; i < T * NU; ++i) dyh[i] = dy[i] * uu[i];
+    for (int64_t c = 0; c < NU; ++c) {
+        dln2_w[c] = 0.0;
+        if (dln2_b) dln2_b[c] = 0.0;
+    }
+    ln_backward(T, NU, dyh, ah, rstd2, ln2_w, da, dln2_w, dln2_b);
+
+    /* A = SLA(Q, K, V) */
+    oracle_sla_bwd(B, offsets, num_targets, H, dqk, dv, k1, k2, ctx, N, alpha, qq, kk, vv, da, dq,
+                   dk, dvv, NULL, NULL);
+
+    /* [U V Q K] = SiLU(z):  dz = d[U V Q K] (.) SiLU'(z) */
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        double *dzr = dz + t * NW;
+        const double *zr = z + t * NW;
+        for (int64_t c = 0; c < NU; ++c) dzr[c] = dy[t * NU + c] * yh[t * NU + c];
+        for (int64_t c = 0; c < NU; ++c) dzr[NU + c] = dvv[t * NU + c];
+        for (int64_t c = 0; c < NQ; ++c) dzr[2 * NU + c] = dq[t * NQ + c];
+        for (int64_t c = 0; c < NQ; ++c) dzr[2 * NU + NQ + c] = dk[t * NQ + c];
+        for (int64_t c = 0; c < NW; ++c) dzr[c] *= dsilu(zr[c]);
+    }
+
+    /* z = n W1^T + b1:  dW1 = dz^T n, db1 = colsum(dz), dn = dz W1 */
+    for (int64_t i = 0; i < NW * D; ++i) dw1[i] = 0.0;
+    if (db1)
+        for (int64_t c = 0; c < NW; ++c) db1[c] = 0.0;
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t o = 0; o < NW; ++o) {
+            const double g = dz[t * NW + o];
+            if (db1) db1[o] += g;
+            for (int64_t c = 0; c < D; ++c) dw1[o * D + c] += g * n[t * D + c];
+        }
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t c = 0; c < D; ++c) {
+            double acc = 0.0;
+            for (int64_t o = 0; o < NW; ++o) acc += dz[t * NW + o] * w1[o * D + c];
+            dn[t * D + c] = acc;
+        }
+
+    /* n = xh * g1 + b1n, plus the residual path of out */
+    for (int64_t c = 0; c < D; ++c) {
+        dln1_w[c] = 0.0;
+        if (dln1_b) dln1_b[c] = 0.0;
+    }
+    ln_backward(T, D, dn, xh1, rstd1, ln1_w, dx, dln1_w, dln1_b);
+    for (int64_t i = 0; i < T * D; ++i) dx[i] += dout[i];
+
+    free(xh1); free(rstd1); free(n); free(z); free(s); free(qq); free(kk); free(vv); free(uu);
+    free(a); free(ah); free(rstd2); free(yh); free(y); free(dy); free(dyh); free(da); free(dq);
+    free(dk); free(dvv); free(dz); free(dn);
+}
+
 /* ------------------------------------------------------------------------ */
 /* attention truncation                                                      */
 /* ------------------------------------------------------------------------ */

@@ -152,3 +152,78 @@ def test_truncate_tzrec_example_lengths():
     offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
     no, gi = oracle.truncate(offs, [64, 64, 64], 16, 1024)
     assert list(np.diff(no)) == [16 + 1024 + 64, 16 + 1024 + 64, 16 + 700 + 64]
+
+
+# ---------------------------------------------------------------------------
+# STU layer backward (gradients of the layer above given dL/dout)
+# ---------------------------------------------------------------------------
+_GRAD_KEYS = {"x": "dx", "ln1_w": "dln1_w", "ln1_b": "dln1_b", "w_uvqk": "dw_uvqk",
+              "b_uvqk": "db_uvqk", "ln2_w": "dln2_w", "ln2_b": "dln2_b", "w_out": "dw_out",
+              "b_out": "db_out"}
+
+
+def _stu_bwd_args(p):
+    return dict(ln1_b=p["ln1_b"], b_uvqk=p["b_uvqk"], ln2_b=p["ln2_b"], b_out=p["b_out"])
+
+
+@pytest.mark.parametrize("tg", [None, [2, 1, 0]])
+def test_stu_layer_bwd_matches_torch_autograd(tg):
+    lens = [6, 11, 9]
+    H, dqk, dv = 2, 4, 3
+    offs, p = _stu_case(7, lens, H=H, dqk=dqk, dv=dv)
+    rng = np.random.default_rng(8)
+    dout = rng.standard_normal(p["x"].shape)
+    kw = dict(heads=H, dqk=dqk, dv=dv, k1=3, k2=2, ctx=1, N=11.0, alpha=0.9, eps=1e-5)
+    g = oracle.stu_layer_bwd(p["x"], offs, tg, p["ln1_w"], p["w_uvqk"], p["ln2_w"], p["w_out"],
+                             dout, **kw, **_stu_bwd_args(p))
+    t = {k: torch.tensor(np.asarray(v, np.float64), requires_grad=True) for k, v in p.items()}
+    x = t["x"]
+    D, T = x.shape[1], x.shape[0]
+    n = F.layer_norm(x, (D,), t["ln1_w"], t["ln1_b"], 1e-5)
+    z = F.silu(F.linear(n, t["w_uvqk"], t["b_uvqk"]))
+    u, v, q, k = torch.split(z, [H * dv, H * dv, H * dqk, H * dqk], dim=1)
+    a = dense_sla_torch(q.reshape(T, H, dqk), k.reshape(T, H, dqk), v.reshape(T, H, dv), offs,
+                        tg, 3, 2, 1, 11.0, 0.9).reshape(T, H * dv)
+    y = F.layer_norm(a, (H * dv,), t["ln2_w"], t["ln2_b"], 1e-5) * u
+    out = F.linear(y, t["w_out"], t["b_out"]) + x
+    (out * torch.from_numpy(dout)).sum().backward()
+    for name, key in _GRAD_KEYS.items():
+        np.testing.assert_allclose(g[key], t[name].grad.numpy(), rtol=1e-9, atol=1e-10,
+                                   err_msg=name)
+
+
+def test_stu_layer_bwd_matches_finite_differences():
+    offs, p = _stu_case(9, [5, 7], D=8, H=1, dqk=4, dv=4)
+    rng = np.random.default_rng(10)
+    dout = rng.standard_normal(p["x"].shape)
+    kw = dict(heads=1, dqk=4, dv=4, k1=3, k2=1, ctx=0, N=7.0, alpha=1.0, eps=1e-5)
+
+    def loss(pp):
+        out = oracle.stu_layer_fwd(pp["x"], offs, None, pp["ln1_w"], pp["w_uvqk"], pp["ln2_w"],
+                                   pp["w_out"], ln1_b=pp["ln1_b"], b_uvqk=pp["b_uvqk"],
+                                   ln2_b=pp["ln2_b"], b_out=pp["b_out"], **kw)
+        return float((out * dout).sum())
+
+    g = oracle.stu_layer_bwd(p["x"], offs, None, p["ln1_w"], p["w_uvqk"], p["ln2_w"],
+                             p["w_out"], dout, **kw, **_stu_bwd_args(p))
+    h = 1e-6
+    for name, idx in [("x", (3, 2)), ("x", (10, 7)), ("ln1_w", (5,)), ("ln1_b", (1,)),
+                      ("w_uvqk", (0, 3)), ("w_uvqk", (9, 1)), ("b_uvqk", (13,)),
+                      ("ln2_w", (2,)), ("ln2_b", (0,)), ("w_out", (4, 3)), ("b_out", (6,))]:
+        pp = {k: np.array(v, dtype=np.float64, copy=True) for k, v in p.items()}
+        pp[name][idx] += h
+        up = loss(pp)
+        pp[name][idx] -= 2 * h
+        dn = loss(pp)
+        fd = (up - dn) / (2 * h)
+        got = g[_GRAD_KEYS[name]][idx]
+        assert abs(got - fd) <= 1e-6 * max(1.0, abs(fd)), (name, idx, got, fd)
+
+
+def test_stu_layer_bwd_of_zero_dout_is_zero():
+    offs, p = _stu_case(11, [4, 6])
+    g = oracle.stu_layer_bwd(p["x"], offs, None, p["ln1_w"], p["w_uvqk"], p["ln2_w"],
+                             p["w_out"], np.zeros_like(p["x"]), heads=2, dqk=4, dv=3, k1=2,
+                             k2=1, ctx=0, N=6.0, **_stu_bwd_args(p))
+    for key, val in g.items():
+        assert not np.any(val), key
