@@ -34,8 +34,8 @@
  * 0 <= num_targets[b] <= L_b; targets are the last num_targets[b] tokens.
  * These device-resident facts are trusted (checking them needs a sync),
  * unless the environment variable SLA_VALIDATE is set to a value other than
- * "0": then sla_fwd, sla_bwd, sla_bwd_stage, sla_schedule, stu_layer_fwd and
- * stu_truncate first run a check kernel on the caller's stream, synchronise
+ * "0": then sla_fwd, sla_bwd, sla_bwd_stage, sla_schedule, stu_layer_fwd,
+ * stu_layer_bwd and stu_truncate first run a check kernel on the caller's stream, synchronise
  * it, and return SLA_ERR_INVALID (message: which fact, which sequence) before
  * any other kernel when offsets[0] != 0, offsets decrease, offsets[B] !=
  * total_tokens, a num_targets[b] lies outside [0, L_b], or (stu_truncate)
@@ -216,8 +216,10 @@ int64_t sla_count_pairs_host(int32_t batch, const int64_t *offsets_host,
  * 2*H*d_qk][D] bf16 (out-features major, as a Linear weight); w_out:
  * [D][H*d_v] bf16; ln*_w, ln*_b, b_*: fp32 vectors; biases nullable.
  * uvqk_out (nullable): [T][2*H*d_v + 2*H*d_qk] bf16 copy of U|V|Q|K; the
- * layer keeps it in the workspace otherwise.  attn.dtype must be SLA_BF16,
- * D a multiple of 64 and at most 1024, H*d_v at most 1024. */
+ * layer keeps it in the workspace otherwise.  attn_out (nullable): [T][H*d_v]
+ * bf16 copy of A, the activation stu_layer_bwd takes instead of recomputing
+ * the attention.  attn.dtype must be SLA_BF16, D a multiple of 128 and at
+ * most 2048, H*d_v a multiple of 64 and at most 2048. */
 typedef struct {
     sla_problem_t attn;
     int32_t hidden;  /* D */
@@ -228,8 +230,37 @@ size_t stu_layer_workspace_size(const stu_layer_desc_t *d);
 sla_status_t stu_layer_fwd(const stu_layer_desc_t *d, const void *x, const float *ln1_w,
                            const float *ln1_b, const void *w_uvqk, const float *b_uvqk,
                            const float *ln2_w, const float *ln2_b, const void *w_out,
-                           const float *b_out, void *out, void *uvqk_out, void *workspace,
-                           size_t ws_bytes, void *stream);
+                           const float *b_out, void *out, void *uvqk_out, void *attn_out,
+                           void *workspace, size_t ws_bytes, void *stream);
+
+/* Gradients of one STU layer (the stu_layer_fwd chain differentiated in
+ * reverse; ULTRA-HSTU paper, section 4.2.2 selective rematerialisation: the
+ * normalised input and the fused projection are recomputed from x, the
+ * attention output A is taken from the forward when given):
+ *   dW2 = dout^T y, db_out = column sums of dout, dy = dout W2
+ *   gated LayerNorm backward -> dU, dA, dln2_w, dln2_b
+ *   sla_bwd(Q, K, V; dA) -> dQ, dK, dV
+ *   dz = d[U|V|Q|K] (.) SiLU'(z), z the projection before SiLU
+ *   dW1 = dz^T n, db_uvqk = column sums of dz, dn = dz W1
+ *   LayerNorm backward -> dx (+ dout, the residual), dln1_w, dln1_b
+ * Inputs as stu_layer_fwd (same descriptor, weights and x); attn (nullable):
+ * A from stu_layer_fwd's attn_out, recomputed with the attention forward when
+ * NULL; dout: [T][D] bf16.  Outputs: dx [T][D] bf16 (required, may not alias
+ * an input); the parameter gradients are fp32 of the parameters' shapes
+ * (dw_uvqk [2*H*d_v + 2*H*d_qk][D], dw_out [D][H*d_v]) and each is nullable
+ * (not computed).  Gradients are written, not accumulated.  Weight gradients
+ * are fp32 sums over tokens of bf16 products, split over token ranges and
+ * added in a fixed order: results are deterministic.  Limits as the forward,
+ * plus H*d_v and 2*H*d_qk multiples of 128 (the weight-gradient tiles).
+ * Workspace: stu_layer_bwd_workspace_size(d) bytes, 16-byte aligned. */
+size_t stu_layer_bwd_workspace_size(const stu_layer_desc_t *d);
+sla_status_t stu_layer_bwd(const stu_layer_desc_t *d, const void *x, const void *attn,
+                           const float *ln1_w, const float *ln1_b, const void *w_uvqk,
+                           const float *b_uvqk, const float *ln2_w, const float *ln2_b,
+                           const void *w_out, const float *b_out, const void *dout, void *dx,
+                           float *dln1_w, float *dln1_b, float *dw_uvqk, float *db_uvqk,
+                           float *dln2_w, float *dln2_b, float *dw_out, float *db_out,
+                           void *workspace, size_t ws_bytes, void *stream);
 
 /* Attention truncation (ULTRA-HSTU paper, section 4.3; torcheasyrec page,
  * truncation bullet): per sequence keep, in order, the contextual prefix

@@ -79,7 +79,7 @@ def _load():
                                              i32, P, P]
         lib.oracle_stu_layer_fwd.restype = None
         lib.oracle_stu_layer_bwd.argtypes = [i32, P, P, i32, i32, i32, i32, i64, i64, i64,
-                                             dbl, dbl, dbl] + [P] * 19
+                                             dbl, dbl, dbl] + [P] * 10 + [i32] + [P] * 9
         lib.oracle_stu_layer_bwd.restype = None
         lib.oracle_truncate.argtypes = [i32, P, P, i64, i64, P, P]
         lib.oracle_truncate.restype = i64
@@ -202,10 +202,13 @@ def stu_layer_fwd(x, offsets, num_targets, ln1_w, w_uvqk, ln2_w, w_out, *, heads
 
 def stu_layer_bwd(x, offsets, num_targets, ln1_w, w_uvqk, ln2_w, w_out, dout, *, heads, dqk,
                   dv, k1, k2, ctx, N, alpha=1.0, eps=1e-5, ln1_b=None, b_uvqk=None, ln2_b=None,
-                  b_out=None):
+                  b_out=None, store_bf16=False):
     """Gradients of stu_layer_fwd's output given dout, as a dict: dx [T, D],
     dln1_w / dln1_b [D], dw_uvqk [NW, D], db_uvqk [NW], dln2_w / dln2_b [H*dv],
-    dw_out [D, H*dv], db_out [D] (fp64; the forward is recomputed in fp64)."""
+    dw_out [D, H*dv], db_out [D] (fp64; the forward is recomputed in fp64).
+    store_bf16: round to bf16 every activation and gradient a bf16
+    implementation stores between steps (n, z, U/V/Q/K, A, y, dy, dU, dA, dQ,
+    dK, dV, dz, dn, dx); the exact chain otherwise."""
     x = _f64(x)
     T, D = x.shape
     nu = heads * dv
@@ -219,7 +222,7 @@ def stu_layer_bwd(x, offsets, num_targets, ln1_w, w_uvqk, ln2_w, w_out, dout, *,
     do = _f64(dout)
     _load().oracle_stu_layer_bwd(len(offs) - 1, _ptr(offs), _ptr(tg), D, heads, dqk, dv, k1,
                                  k2, ctx, float(N), float(alpha), float(eps), _ptr(x),
-                                 *[_ptr(a) for a in keep], _ptr(do),
+                                 *[_ptr(a) for a in keep], _ptr(do), int(bool(store_bf16)),
                                  *[_ptr(g[k]) for k in ("dx", "dln1_w", "dln1_b", "dw_uvqk",
                                                          "db_uvqk", "dln2_w", "dln2_b",
                                                          "dw_out", "db_out")])

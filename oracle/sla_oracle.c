@@ -447,18 +447,24 @@ static double dsilu(double z)
  *   n = xh * g1 + b1n,  xh = LN-normalised x.
  * Outputs (all overwritten; biases' gradients only where the pointer is
  * non-NULL): dx [T][D], dln1_w/b [D], dw1 [NW][D], db1 [NW], dln2_w/b [NU],
- * dw2 [D][NU], db2 [D]. */
+ * dw2 [D][NU], db2 [D].
+ * store_bf16 != 0 rounds to bfloat16 every tensor a bf16 implementation
+ * stores between steps: the recomputed n, z (the stored pre-activation that
+ * SiLU' is evaluated at), U/V/Q/K = SiLU(z) (taken of the unrounded z), A and
+ * y; the gradients dy, dU, dA, dQ, dK, dV, dz, dn and the output dx.  The
+ * parameter gradients are sums of products of those stored values. */
 EXPORT void oracle_stu_layer_bwd(int B, const int64_t *offsets, const int32_t *num_targets,
                                  int D, int H, int dqk, int dv, int64_t k1, int64_t k2,
                                  int64_t ctx, double N, double alpha, double eps,
                                  const double *x, const double *ln1_w, const double *ln1_b,
                                  const double *w1, const double *b1, const double *ln2_w,
                                  const double *ln2_b, const double *w2, const double *b2,
-                                 const double *dout, double *dx, double *dln1_w, double *dln1_b,
-                                 double *dw1, double *db1, double *dln2_w, double *dln2_b,
-                                 double *dw2, double *db2)
+                                 const double *dout, int store_bf16, double *dx, double *dln1_w,
+                                 double *dln1_b, double *dw1, double *db1, double *dln2_w,
+                                 double *dln2_b, double *dw2, double *db2)
 {
     (void)b2;
+    const int rb = store_bf16 != 0;
     const int64_t T = offsets[B];
     const int64_t NU = (int64_t)H * dv, NQ = (int64_t)H * dqk, NW = 2 * NU + 2 * NQ;
     double *xh1 = malloc(sizeof(double) * T * D), *rstd1 = malloc(sizeof(double) * T);
@@ -479,8 +485,13 @@ EXPORT void oracle_stu_layer_bwd(int B, const int64_t *offsets, const int32_t *n
     for (int64_t t = 0; t < T; ++t)
         for (int64_t c = 0; c < D; ++c)
             n[t * D + c] = xh1[t * D + c] * ln1_w[c] + (ln1_b ? ln1_b[c] : 0.0);
+    if (rb) round_all(n, T * D);
     linear(T, D, NW, n, w1, b1, z);
     for (int64_t i = 0; i < T * NW; ++i) s[i] = silu(z[i]);
+    if (rb) {
+        round_all(z, T * NW);
+        round_all(s, T * NW);
+    }
     for (int64_t t = 0; t < T; ++t) {
         const double *sr = s + t * NW;
         memcpy(uu + t * NU, sr, sizeof(double) * NU);
@@ -490,12 +501,14 @@ EXPORT void oracle_stu_layer_bwd(int B, const int64_t *offsets, const int32_t *n
     }
     oracle_sla_fwd(B, offsets, num_targets, H, dqk, dv, k1, k2, ctx, N, alpha, qq, kk, vv, a,
                    NULL);
+    if (rb) round_all(a, T * NU);
     ln_stats(T, NU, a, eps, ah, rstd2);
     for (int64_t t = 0; t < T; ++t)
         for (int64_t c = 0; c < NU; ++c) {
             yh[t * NU + c] = ah[t * NU + c] * ln2_w[c] + (ln2_b ? ln2_b[c] : 0.0);
             y[t * NU + c] = yh[t * NU + c] * uu[t * NU + c];
         }
+    if (rb) round_all(y, T * NU);
 
     /* out = y W2^T + b2 + x:  dW2 = dout^T y, db2 = colsum(dout), dy = dout W2 */
     for (int64_t i = 0; i < D * NU; ++i) dw2[i] = 0.0;
@@ -514,6 +527,7 @@ EXPORT void oracle_stu_layer_bwd(int B, const int64_t *offsets, const int32_t *n
             for (int64_t d = 0; d < D; ++d) acc += dout[t * D + d] * w2[d * NU + c];
             dy[t * NU + c] = acc;
         }
+    if (rb) round_all(dy, T * NU);
 
     /* y = yh (.) U:  dU = dy (.) yh, dyh = dy (.) U; yh = ah * g2 + b2n */
     for (int64_t i = 0; i < T * NU; ++i) dyh[i] = dy[i] * uu[i];
@@ -522,21 +536,33 @@ EXPORT void oracle_stu_layer_bwd(int B, const int64_t *offsets, const int32_t *n
         if (dln2_b) dln2_b[c] = 0.0;
     }
     ln_backward(T, NU, dyh, ah, rstd2, ln2_w, da, dln2_w, dln2_b);
+    if (rb) round_all(da, T * NU);
 
     /* A = SLA(Q, K, V) */
     oracle_sla_bwd(B, offsets, num_targets, H, dqk, dv, k1, k2, ctx, N, alpha, qq, kk, vv, da, dq,
                    dk, dvv, NULL, NULL);
+    if (rb) {
+        round_all(dq, T * NQ);
+        round_all(dk, T * NQ);
+        round_all(dvv, T * NU);
+    }
 
     /* [U V Q K] = SiLU(z):  dz = d[U V Q K] (.) SiLU'(z) */
 #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < T; ++t) {
         double *dzr = dz + t * NW;
         const double *zr = z + t * NW;
-        for (int64_t c = 0; c < NU; ++c) dzr[c] = dy[t * NU + c] * yh[t * NU + c];
+        for (int64_t c = 0; c < NU; ++c) {
+            const double du = dy[t * NU + c] * yh[t * NU + c];
+            dzr[c] = rb ? oracle_round_bf16(du) : du;
+        }
         for (int64_t c = 0; c < NU; ++c) dzr[NU + c] = dvv[t * NU + c];
         for (int64_t c = 0; c < NQ; ++c) dzr[2 * NU + c] = dq[t * NQ + c];
         for (int64_t c = 0; c < NQ; ++c) dzr[2 * NU + NQ + c] = dk[t * NQ + c];
-        for (int64_t c = 0; c < NW; ++c) dzr[c] *= dsilu(zr[c]);
+        for (int64_t c = 0; c < NW; ++c) {
+            dzr[c] *= dsilu(zr[c]);
+            if (rb) dzr[c] = oracle_round_bf16(dzr[c]);
+        }
     }
 
     /* z = n W1^T + b1:  dW1 = dz^T n, db1 = colsum(dz), dn = dz W1 */
@@ -556,6 +582,7 @@ EXPORT void oracle_stu_layer_bwd(int B, const int64_t *offsets, const int32_t *n
             for (int64_t o = 0; o < NW; ++o) acc += dz[t * NW + o] * w1[o * D + c];
             dn[t * D + c] = acc;
         }
+    if (rb) round_all(dn, T * D);
 
     /* n = xh * g1 + b1n, plus the residual path of out */
     for (int64_t c = 0; c < D; ++c) {
@@ -564,6 +591,7 @@ EXPORT void oracle_stu_layer_bwd(int B, const int64_t *offsets, const int32_t *n
     }
     ln_backward(T, D, dn, xh1, rstd1, ln1_w, dx, dln1_w, dln1_b);
     for (int64_t i = 0; i < T * D; ++i) dx[i] += dout[i];
+    if (rb) round_all(dx, T * D);
 
     free(xh1); free(rstd1); free(n); free(z); free(s); free(qq); free(kk); free(vv); free(uu);
     free(a); free(ah); free(rstd2); free(yh); free(y); free(dy); free(dyh); free(da); free(dq);

@@ -29,6 +29,7 @@ SOURCES = [
     "sla_dq_ds.hip",
     "sla_f32.hip",
     "stu_kernels.hip",
+    "stu_bwd.hip",
 ]
 
 ARCH = "gfx950"

@@ -229,6 +229,63 @@ sla_status_t make_params(const sla_problem_t *p, int op, void *ws, size_t ws_byt
     return SLA_OK;
 }
 
+// STU layer backward workspace: recomputed activations, their gradients, a
+// transposed weight, fp32 partial sums, and the attention workspace last.
+struct StuBwdLayout {
+    size_t n, z, uvqk, A, y, dy, dA, dz, dn, wt, part, vec, attn, total;
+    int split_out, split_uvqk;
+};
+
+// token ranges of a weight-gradient product: about 512 workgroups in all,
+// at least 256 tokens per range
+int tn_splits(int64_t T, int M, int N)
+{
+    const int64_t tiles = (int64_t)(M / 128) * (N / 128);
+    int64_t s = tiles > 0 ? (512 + tiles - 1) / tiles : 1;
+    const int64_t cap = (T + 255) / 256;
+    if (s > cap) s = cap;
+    return (int)(s < 1 ? 1 : s);
+}
+
+StuBwdLayout stu_bwd_layout(const stu_layer_desc_t *d)
+{
+    const sla_problem_t *p = &d->attn;
+    const size_t T = (size_t)p->total_tokens, D = (size_t)d->hidden;
+    const size_t NU = (size_t)p->num_heads * p->d_v;
+    const size_t NW = 2 * NU + 2 * (size_t)p->num_heads * p->d_qk;
+    StuBwdLayout L{};
+    size_t at = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = at;
+        at += round_up(bytes, 256);
+        return o;
+    };
+    L.n = take(T * D * 2);
+    L.z = take(T * NW * 2);
+    L.uvqk = take(T * NW * 2);
+    L.A = take(T * NU * 2);
+    L.y = take(T * NU * 2);
+    L.dy = take(T * NU * 2);
+    L.dA = take(T * NU * 2);
+    L.dz = take(T * NW * 2);
+    L.dn = take(T * D * 2);
+    L.wt = take(NW * D * 2);
+    L.split_out = tn_splits((int64_t)T, (int)D, (int)NU);
+    L.split_uvqk = tn_splits((int64_t)T, (int)NW, (int)D);
+    size_t part = (size_t)L.split_out * D * NU;
+    const size_t pu = (size_t)L.split_uvqk * NW * D;
+    if (pu > part) part = pu;
+    const size_t cs = (size_t)colsum_blocks((int64_t)T) * (NW > D ? NW : D);
+    if (cs > part) part = cs;
+    const size_t ln = 2 * (size_t)ln_bwd_blocks((int64_t)T) * (NU > D ? NU : D);
+    if (ln > part) part = ln;
+    L.part = take(part * 4);
+    L.vec = take((NW > D ? NW : D) * 4);
+    L.attn = at;
+    L.total = at + layout(p, SLA_OP_BWD).total;
+    return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -479,8 +536,8 @@ size_t stu_layer_workspace_size(const stu_layer_desc_t *d)
 sla_status_t stu_layer_fwd(const stu_layer_desc_t *d, const void *x, const float *ln1_w,
                            const float *ln1_b, const void *w_uvqk, const float *b_uvqk,
                            const float *ln2_w, const float *ln2_b, const void *w_out,
-                           const float *b_out, void *out, void *uvqk_out, void *workspace,
-                           size_t ws_bytes, void *stream)
+                           const float *b_out, void *out, void *uvqk_out, void *attn_out,
+                           void *workspace, size_t ws_bytes, void *stream)
 {
     if (!d) return fail(SLA_ERR_NULL, "layer descriptor is NULL");
     const sla_problem_t *p = &d->attn;
@@ -498,7 +555,7 @@ sla_status_t stu_layer_fwd(const stu_layer_desc_t *d, const void *x, const float
     if (!(d->ln_eps > 0.0f) || !std::isfinite(d->ln_eps))
         return fail(SLA_ERR_INVALID, "ln_eps must be positive");
     if (out == x) return fail(SLA_ERR_INVALID, "out must not alias x");
-    const void *ptrs[] = {x, w_uvqk, w_out, out, uvqk_out, workspace};
+    const void *ptrs[] = {x, w_uvqk, w_out, out, uvqk_out, attn_out, workspace};
     for (const void *q : ptrs)
         if (q && !aligned16(q)) return fail(SLA_ERR_UNSUPPORTED, "a layer buffer is not 16-byte aligned");
     const size_t need = stu_layer_workspace_size(d);
@@ -513,7 +570,7 @@ sla_status_t stu_layer_fwd(const stu_layer_desc_t *d, const void *x, const float
     w += round_up((size_t)T * D * 2, 256);
     void *uvqk_ws = w;
     w += round_up((size_t)T * NW * 2, 256);
-    void *A = w;
+    void *A = attn_out ? attn_out : w;
     w += round_up((size_t)T * NU * 2, 256);
     void *y = w;
     w += round_up((size_t)T * NU * 2, 256);
@@ -527,7 +584,7 @@ sla_status_t stu_layer_fwd(const stu_layer_desc_t *d, const void *x, const float
         return st;
     hipError_t e = launch_layernorm_bf16(x, ln1_w, ln1_b, n, T, D, d->ln_eps, s);
     if (e != hipSuccess) return hip_fail(e, "layernorm");
-    e = launch_gemm_bf16(n, D, w_uvqk, D, b_uvqk, nullptr, 0, uvqk, NW, T, NW, D, 0, s);
+    e = launch_gemm_bf16(n, D, w_uvqk, D, b_uvqk, nullptr, 0, uvqk, NW, nullptr, 0, T, NW, D, 0, s);
     if (e != hipSuccess) return hip_fail(e, "uvqk projection");
     // U | V | Q | K column blocks of the fused projection
     st = sla_fwd(p, u16 + 2 * NU, NW, u16 + 2 * NU + H * dqk, NW, u16 + NU, NW, A, NU, attn_ws,
@@ -535,8 +592,140 @@ sla_status_t stu_layer_fwd(const stu_layer_desc_t *d, const void *x, const float
     if (st != SLA_OK) return st;
     e = launch_gated_layernorm_bf16(A, NU, u16, NW, ln2_w, ln2_b, y, T, NU, d->ln_eps, s);
     if (e != hipSuccess) return hip_fail(e, "gated layernorm");
-    e = launch_gemm_bf16(y, NU, w_out, NU, b_out, x, D, out, D, T, D, NU, 1, s);
+    e = launch_gemm_bf16(y, NU, w_out, NU, b_out, x, D, out, D, nullptr, 0, T, D, NU, 1, s);
     if (e != hipSuccess) return hip_fail(e, "output projection");
+    return SLA_OK;
+}
+
+size_t stu_layer_bwd_workspace_size(const stu_layer_desc_t *d)
+{
+    if (!d || validate_problem(&d->attn) != SLA_OK || d->hidden <= 0) return 0;
+    return stu_bwd_layout(d).total;
+}
+
+sla_status_t stu_layer_bwd(const stu_layer_desc_t *d, const void *x, const void *attn,
+                           const float *ln1_w, const float *ln1_b, const void *w_uvqk,
+                           const float *b_uvqk, const float *ln2_w, const float *ln2_b,
+                           const void *w_out, const float *b_out, const void *dout, void *dx,
+                           float *dln1_w, float *dln1_b, float *dw_uvqk, float *db_uvqk,
+                           float *dln2_w, float *dln2_b, float *dw_out, float *db_out,
+                           void *workspace, size_t ws_bytes, void *stream)
+{
+    if (!d) return fail(SLA_ERR_NULL, "layer descriptor is NULL");
+    const sla_problem_t *p = &d->attn;
+    sla_status_t st = validate_problem(p);
+    if (st != SLA_OK) return st;
+    if (p->dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "the STU layer is bf16 only");
+    if (!ln1_w || !w_uvqk || !ln2_w || !w_out)
+        return fail(SLA_ERR_NULL, "a required layer pointer is NULL");
+    if (p->total_tokens > 0 && (!x || !dout || !dx))
+        return fail(SLA_ERR_NULL, "x, dout or dx is NULL");
+    const int D = d->hidden, H = p->num_heads, dv = p->d_v, dqk = p->d_qk;
+    const int NU = H * dv, NQK = H * dqk, NW = 2 * NU + 2 * NQK;
+    if (D <= 0 || D % 128 != 0 || D > 2048)
+        return fail(SLA_ERR_UNSUPPORTED, "hidden %d must be a positive multiple of 128, <= 2048", D);
+    if (NU % 128 != 0 || NU > 2048)
+        return fail(SLA_ERR_UNSUPPORTED, "H*d_v = %d must be a multiple of 128, <= 2048", NU);
+    if ((2 * NQK) % 128 != 0)
+        return fail(SLA_ERR_UNSUPPORTED, "2*H*d_qk = %d must be a multiple of 128", 2 * NQK);
+    if (!(d->ln_eps > 0.0f) || !std::isfinite(d->ln_eps))
+        return fail(SLA_ERR_INVALID, "ln_eps must be positive");
+    if (dx && (dx == x || dx == dout || dx == attn))
+        return fail(SLA_ERR_INVALID, "dx must not alias an input");
+    const void *ptrs[] = {x, attn, w_uvqk, w_out, dout, dx, workspace};
+    for (const void *q : ptrs)
+        if (q && !aligned16(q)) return fail(SLA_ERR_UNSUPPORTED, "a layer buffer is not 16-byte aligned");
+    const StuBwdLayout L = stu_bwd_layout(d);
+    if (!workspace || ws_bytes < L.total)
+        return fail(SLA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", ws_bytes, L.total);
+    if ((st = check_device()) != SLA_OK) return st;
+    const int64_t T = p->total_tokens;
+    if (T == 0 || p->batch == 0) {
+        // no tokens: every parameter gradient is zero
+        hipStream_t s0 = static_cast<hipStream_t>(stream);
+        const struct { float *ptr; size_t n; } z[] = {
+            {dln1_w, (size_t)D}, {dln1_b, (size_t)D}, {dw_uvqk, (size_t)NW * D},
+            {db_uvqk, (size_t)NW}, {dln2_w, (size_t)NU}, {dln2_b, (size_t)NU},
+            {dw_out, (size_t)D * NU}, {db_out, (size_t)D}};
+        for (const auto &g : z)
+            if (g.ptr) {
+                hipError_t e = launch_fill_f32(g.ptr, g.n, 0.0f, s0);
+                if (e != hipSuccess) return hip_fail(e, "gradient fill");
+            }
+        return SLA_OK;
+    }
+
+    char *base = static_cast<char *>(workspace);
+    uint16_t *n = reinterpret_cast<uint16_t *>(base + L.n);
+    uint16_t *z = reinterpret_cast<uint16_t *>(base + L.z);
+    uint16_t *uvqk = reinterpret_cast<uint16_t *>(base + L.uvqk);
+    uint16_t *A = attn ? static_cast<uint16_t *>(const_cast<void *>(attn))
+                       : reinterpret_cast<uint16_t *>(base + L.A);
+    uint16_t *y = reinterpret_cast<uint16_t *>(base + L.y);
+    uint16_t *dy = reinterpret_cast<uint16_t *>(base + L.dy);
+    uint16_t *dA = reinterpret_cast<uint16_t *>(base + L.dA);
+    uint16_t *dz = reinterpret_cast<uint16_t *>(base + L.dz);
+    uint16_t *dn = reinterpret_cast<uint16_t *>(base + L.dn);
+    uint16_t *wt = reinterpret_cast<uint16_t *>(base + L.wt);
+    float *part = reinterpret_cast<float *>(base + L.part);
+    float *scratch_w = reinterpret_cast<float *>(base + L.vec);  // sums of unwanted gradients
+    void *attn_ws = base + L.attn;
+    const size_t attn_bytes = L.total - L.attn;
+    auto or_scratch = [&](float *g) { return g ? g : scratch_w; };
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = validate_layout(p->batch, T, p->offsets, p->num_targets, -1, workspace, s)) != SLA_OK)
+        return st;
+    hipError_t e;
+#define STU_TRY(call, what)                      \
+    do {                                         \
+        e = (call);                              \
+        if (e != hipSuccess) return hip_fail(e, what); \
+    } while (0)
+    // recomputed activations: n, z, uvqk = SiLU(z), A (unless saved), y
+    STU_TRY(launch_layernorm_bf16(x, ln1_w, ln1_b, n, T, D, d->ln_eps, s), "layernorm");
+    STU_TRY(launch_gemm_bf16(n, D, w_uvqk, D, b_uvqk, nullptr, 0, uvqk, NW, z, NW, T, NW, D, 3, s),
+            "uvqk projection");
+    if (!attn) {
+        st = sla_fwd(p, uvqk + 2 * NU, NW, uvqk + 2 * NU + NQK, NW, uvqk + NU, NW, A, NU, attn_ws,
+                     attn_bytes, stream);
+        if (st != SLA_OK) return st;
+    }
+    STU_TRY(launch_gated_layernorm_bf16(A, NU, uvqk, NW, ln2_w, ln2_b, y, T, NU, d->ln_eps, s),
+            "gated layernorm");
+    // output projection: dy = dout W2 (W2^T staged as [NU][D]), dW2 = dout^T y, db_out
+    STU_TRY(launch_transpose_bf16(w_out, D, NU, wt, s), "weight transpose");
+    STU_TRY(launch_gemm_bf16(dout, D, wt, D, nullptr, nullptr, 0, dy, NU, nullptr, 0, T, NU, D, 2,
+                             s),
+            "dy product");
+    if (dw_out)
+        STU_TRY(launch_gemm_tn_bf16(dout, D, y, NU, T, D, NU, part, L.split_out, dw_out, s),
+                "output weight gradient");
+    if (db_out) STU_TRY(launch_colsum_bf16(dout, D, T, D, part, db_out, s), "output bias gradient");
+    // gated LayerNorm: dA, dU (into the U block of dz), dln2
+    STU_TRY(launch_ln_bwd_bf16(true, A, NU, dy, NU, uvqk, NW, ln2_w, ln2_b, nullptr, 0, dA, NU, dz,
+                               NW, part, part + (size_t)ln_bwd_blocks(T) * NU, or_scratch(dln2_w),
+                               dln2_b, T, NU, d->ln_eps, s),
+            "gated layernorm backward");
+    // attention: dQ, dK, dV into their blocks of dz
+    st = sla_bwd(p, uvqk + 2 * NU, NW, uvqk + 2 * NU + NQK, NW, uvqk + NU, NW, dA, NU, dz + 2 * NU,
+                 NW, dz + 2 * NU + NQK, NW, dz + NU, NW, attn_ws, attn_bytes, stream);
+    if (st != SLA_OK) return st;
+    // SiLU: dz = d[U|V|Q|K] (.) SiLU'(z); dW1 = dz^T n, db_uvqk, dn = dz W1
+    STU_TRY(launch_dsilu_bf16(dz, NW, z, NW, T, NW, s), "SiLU backward");
+    if (dw_uvqk)
+        STU_TRY(launch_gemm_tn_bf16(dz, NW, n, D, T, NW, D, part, L.split_uvqk, dw_uvqk, s),
+                "projection weight gradient");
+    if (db_uvqk) STU_TRY(launch_colsum_bf16(dz, NW, T, NW, part, db_uvqk, s), "projection bias gradient");
+    STU_TRY(launch_transpose_bf16(w_uvqk, NW, D, wt, s), "weight transpose");
+    STU_TRY(launch_gemm_bf16(dz, NW, wt, NW, nullptr, nullptr, 0, dn, D, nullptr, 0, T, D, NW, 2, s),
+            "dn product");
+    // LayerNorm 1 with the residual: dx = LN backward + dout
+    STU_TRY(launch_ln_bwd_bf16(false, x, D, dn, D, nullptr, 0, ln1_w, ln1_b, dout, D, dx, D,
+                               nullptr, 0, part, part + (size_t)ln_bwd_blocks(T) * D,
+                               or_scratch(dln1_w), dln1_b, T, D, d->ln_eps, s),
+            "layernorm backward");
+#undef STU_TRY
     return SLA_OK;
 }
 

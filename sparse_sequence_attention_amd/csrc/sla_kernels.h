@@ -77,10 +77,35 @@ hipError_t launch_layernorm_bf16(const void *x, const float *w, const float *b, 
 hipError_t launch_gated_layernorm_bf16(const void *a, int64_t lda, const void *u, int64_t ldu,
                                        const float *w, const float *b, void *y, int64_t rows,
                                        int cols, float eps, hipStream_t st);
-// C[M][N] = epilogue(A[M][K] . W[N][K]^T): epi 0 = SiLU(acc + bias), 1 = acc + bias + R
+// C[M][N] = epilogue(A[M][K] . W[N][K]^T), z = acc + bias: epi 0 = SiLU(z),
+// 1 = z + R, 2 = z, 3 = SiLU(z) with z also stored to Z
 hipError_t launch_gemm_bf16(const void *A, int64_t lda, const void *W, int64_t ldw,
                             const float *bias, const void *R, int64_t ldr, void *C, int64_t ldc,
-                            int64_t M, int N, int K, int epi, hipStream_t st);
+                            void *Z, int64_t ldz, int64_t M, int N, int K, int epi,
+                            hipStream_t st);
+
+// STU layer backward pieces (stu_bwd.hip)
+// C[M][N] = sum_t A[t][m] B[t][n] over T rows, fp32: `splits` token ranges
+// into part [splits][M][N], then summed in split order into out.  M, N
+// multiples of 128.
+hipError_t launch_gemm_tn_bf16(const void *A, int64_t lda, const void *B, int64_t ldb, int64_t T,
+                               int M, int N, float *part, int splits, float *out, hipStream_t st);
+int colsum_blocks(int64_t T);
+hipError_t launch_colsum_bf16(const void *X, int64_t ld, int64_t T, int C, float *part, float *out,
+                              hipStream_t st);
+int ln_bwd_blocks(int64_t rows);
+// LayerNorm backward (gated: y = (LN(x) w + b) (.) u, du also written);
+// part_w / part_b: [ln_bwd_blocks(rows)][cols]; db nullable; res (plain
+// only, nullable) is added to dx.
+hipError_t launch_ln_bwd_bf16(bool gated, const void *x, int64_t ldx, const void *dy, int64_t lddy,
+                              const void *u, int64_t ldu, const float *w, const float *b,
+                              const void *res, int64_t ldres, void *dx, int64_t lddx, void *du,
+                              int64_t lddu, float *part_w, float *part_b, float *dw, float *db,
+                              int64_t rows, int cols, float eps, hipStream_t st);
+hipError_t launch_dsilu_bf16(void *ds, int64_t ldd, const void *z, int64_t ldz, int64_t rows,
+                             int cols, hipStream_t st);
+hipError_t launch_transpose_bf16(const void *src, int R, int C, void *dst, hipStream_t st);
+hipError_t launch_fill_f32(float *dst, size_t n, float v, hipStream_t st);
 hipError_t launch_truncate(int B, int64_t T, const int64_t *offsets, const int32_t *num_targets,
                            int ctx, int tail, const void *x, int hidden, int elem_bytes,
                            int64_t *new_offsets, int32_t *new_num_targets, int64_t *gather_idx,

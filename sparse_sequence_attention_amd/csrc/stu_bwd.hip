@@ -1,0 +1,456 @@
+// stu_bwd.hip -- kernels of the STU layer backward (ULTRA-HSTU paper, section 3
+// Eq.1-5 differentiated in the reverse of the Code Listing 1 order; selective
+// rematerialisation as in section 4.2.2: the normalised input and the fused
+// projection are recomputed, the attention output is kept):
+//   - a weight-gradient GEMM C[m][n] = sum_t A[t][m] B[t][n] over the token
+//     dimension, split over token ranges into fp32 partials that a second
+//     kernel adds in a fixed order (no atomics);
+//   - LayerNorm and gated-LayerNorm backward, one wave per row, with per-block
+//     column partial sums for the norm parameters;
+//   - SiLU' applied to the gradient of the projection output, column sums of
+//     a [T][C] tensor, and a bf16 matrix transpose.
+#include "sla_device.h"
+#include "sla_kernels.h"
+
+namespace sla {
+
+// ---------------------------------------------------------------------------
+// C_part[s][m][n] = sum_{t in split s} A[t][m] * B[t][n]   (bf16 in, fp32 out)
+// ---------------------------------------------------------------------------
+// Tile 128 (m) x 128 (n), 4 waves of 64 x 64, steps of 64 tokens.  Both tiles
+// are staged row-major ([token][column], 256-byte rows, chunk-swizzled) and the
+// MFMA operands (8 consecutive tokens of one column per lane) come from
+// transposing LDS reads; A and B use the same token order, so the sum is exact
+// in any order of the 8 k-slots.
+constexpr int WG_M = 128, WG_N = 128, WG_T = 64;
+
+__device__ __forceinline__ int wg_swz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+
+__global__ __launch_bounds__(256, 2) void gemm_tn_kernel(const uint16_t *A, int64_t lda,
+                                                         const uint16_t *B, int64_t ldb,
+                                                         float *part, int64_t T, int M, int N,
+                                                         int64_t rows_per_split, int splits)
+{
+    __shared__ __align__(16) uint16_t sa[2][WG_T * WG_M];
+    __shared__ __align__(16) uint16_t sb[2][WG_T * WG_N];
+    const int ntm = M / WG_M, ntn = N / WG_N;
+    const int item = blockIdx.x;
+    const int s = item / (ntm * ntn), rem = item - s * (ntm * ntn);
+    const int m0 = (rem / ntn) * WG_M, n0 = (rem % ntn) * WG_N;
+    const int64_t t0 = (int64_t)s * rows_per_split;
+    int64_t t1 = t0 + rows_per_split < T ? t0 + rows_per_split : T;
+    if (t1 < t0) t1 = t0;  // a split past the last token writes zeros
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int wm = wv & 1, wn = wv >> 1;
+    const int q4 = lane >> 4, j16 = lane & 15;
+
+    // staging: thread loads chunk tid % 16 of rows tid / 16 + 16 i (i < 4)
+    const int sr = tid >> 4, sc = tid & 15;
+    uint4 ra[4], rb[4];
+    auto load = [&](int64_t tb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t t = tb + sr + 16 * i;
+            const bool ok = t < t1;
+            const int64_t tt = ok ? t : t0;  // a valid row; zeroed below
+            ra[i] = ld16_or_zero(A + tt * lda + m0 + 8 * sc, ok);
+            rb[i] = ld16_or_zero(B + tt * ldb + n0 + 8 * sc, ok);
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = sr + 16 * i;
+            *reinterpret_cast<uint4 *>(&sa[buf][r * WG_M + 8 * (sc ^ wg_swz(r))]) = ra[i];
+            *reinterpret_cast<uint4 *>(&sb[buf][r * WG_N + 8 * (sc ^ wg_swz(r))]) = rb[i];
+        }
+    };
+    // transposing read: rows 16*kc + 8*rr + 4*(q/2) + j/4, columns c0 + 16*(q%2) + 4*(j%4)
+    auto tr = [&](const uint16_t *tile, int kc, int c0) {
+        uint2 v[2];
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            const int row = 16 * kc + 8 * rr + 4 * (q4 >> 1) + (j16 >> 2);
+            const int col = c0 + 16 * (q4 & 1) + 4 * (j16 & 3);
+            v[rr] = tr_read_b64(tile + row * 128 + 8 * ((col >> 3) ^ wg_swz(row)) + (col & 7));
+        }
+        return __builtin_bit_cast(bf16x8, make_uint4(v[0].x, v[0].y, v[1].x, v[1].y));
+    };
+
+    floatx16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
+
+    const int64_t nsteps = (t1 - t0 + WG_T - 1) / WG_T;
+    if (nsteps > 0) load(t0);
+    for (int64_t st = 0; st < nsteps; ++st) {
+        const int buf = (int)(st & 1);
+        store(buf);
+        if (st + 1 < nsteps) load(t0 + (st + 1) * WG_T);
+        __syncthreads();
+#pragma unroll
+        for (int kc = 0; kc < WG_T / 16; ++kc) {
+            bf16x8 a[2], b[2];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) a[mb] = tr(sa[buf], kc, 64 * wm + 32 * mb);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) b[nb] = tr(sb[buf], kc, 64 * wn + 32 * nb);
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(a[mb], b[nb], acc[mb][nb]);
+        }
+        __syncthreads();  // the next store overwrites the other buffer's reader
+    }
+
+    // register r of acc[mb][nb]: m = 64*wm + 32*mb + 8*(r/4) + 4*hl + r%4, n = 64*wn + 32*nb + l32
+    const int l32 = lane & 31, hl = lane >> 5;
+    float *ps = part + (int64_t)s * M * N;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + 64 * wm + 32 * mb + 8 * (r >> 2) + 4 * hl + (r & 3);
+                const int n = n0 + 64 * wn + 32 * nb + l32;
+                ps[(int64_t)m * N + n] = acc[mb][nb][r];
+            }
+}
+
+// out[i] = sum_s part[s][i] in split order (also used for the column partials)
+__global__ __launch_bounds__(256) void sum_partials_kernel(const float *part, int64_t count,
+                                                           int splits, float *out)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= count) return;
+    float acc = 0.0f;
+    for (int s = 0; s < splits; ++s) acc += part[(int64_t)s * count + i];
+    out[i] = acc;
+}
+
+hipError_t launch_gemm_tn_bf16(const void *A, int64_t lda, const void *B, int64_t ldb, int64_t T,
+                               int M, int N, float *part, int splits, float *out, hipStream_t st)
+{
+    if (M % WG_M != 0 || N % WG_N != 0 || splits < 1) return hipErrorInvalidValue;
+    int64_t rows = (T + splits - 1) / splits;
+    rows = (rows + WG_T - 1) / WG_T * WG_T;
+    const int tiles = (M / WG_M) * (N / WG_N);
+    hipLaunchKernelGGL(gemm_tn_kernel, dim3((unsigned)(tiles * splits)), dim3(256), 0, st,
+                       (const uint16_t *)A, lda, (const uint16_t *)B, ldb, part, T, M, N, rows,
+                       splits);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t count = (int64_t)M * N;
+    hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
+                       st, part, count, splits, out);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Column sums of a [T][C] bf16 tensor (token stride ld): per block of
+// COLSUM_ROWS rows a partial, then the fixed-order sum.
+// ---------------------------------------------------------------------------
+constexpr int COLSUM_ROWS = 512;
+
+__global__ __launch_bounds__(256) void colsum_kernel(const uint16_t *X, int64_t ld, int64_t T,
+                                                     int C, float *part)
+{
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    const int64_t r0 = (int64_t)blockIdx.y * COLSUM_ROWS;
+    if (c >= C) return;
+    const int64_t r1 = r0 + COLSUM_ROWS < T ? r0 + COLSUM_ROWS : T;
+    float acc = 0.0f;
+    for (int64_t r = r0; r < r1; ++r) {
+        const uint32_t w = X[r * ld + c];
+        acc += __uint_as_float(w << 16);
+    }
+    part[(int64_t)blockIdx.y * C + c] = acc;
+}
+
+int colsum_blocks(int64_t T) { return (int)((T + COLSUM_ROWS - 1) / COLSUM_ROWS); }
+
+hipError_t launch_colsum_bf16(const void *X, int64_t ld, int64_t T, int C, float *part, float *out,
+                              hipStream_t st)
+{
+    const int nb = colsum_blocks(T);
+    if (nb == 0) return hipSuccess;
+    hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)((C + 255) / 256), (unsigned)nb), dim3(256), 0,
+                       st, (const uint16_t *)X, ld, T, C, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)((C + 255) / 256)), dim3(256), 0, st,
+                       part, (int64_t)C, nb, out);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// LayerNorm backward, one wave per row, LN_ROWS rows per workgroup (4 waves
+// taking every fourth row).  With xh = (x - mean) * rstd of the row:
+//   plain:  g = dy * w;                  dx = rstd (g - mean g - xh mean(g xh)) + res
+//           partial_w += dy * xh,        partial_b += dy
+//   gated (y = (xh * w + b) (.) u):  dyh = dy * u, du = dy * (xh * w + b),
+//           g = dyh * w;                 dx = rstd (g - mean g - xh mean(g xh))
+//           partial_w += dyh * xh,       partial_b += dyh
+// Rows of up to 64 x 8 x 4 = 2048 columns; each lane owns 8-column chunks.
+// ---------------------------------------------------------------------------
+constexpr int LN_ROWS = 64;
+
+__device__ __forceinline__ float wave_sum_b(float x)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+__device__ __forceinline__ void unpack8(const uint4 &r, float *f)
+{
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f[2 * e] = bf16_lo(w[e]);
+        f[2 * e + 1] = bf16_hi(w[e]);
+    }
+}
+
+__device__ __forceinline__ uint4 pack8(const float *f)
+{
+    const uint2 lo = cvt4_u2(f[0], f[1], f[2], f[3]);
+    const uint2 hi = cvt4_u2(f[4], f[5], f[6], f[7]);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+template <bool GATED>
+__global__ __launch_bounds__(256) void ln_bwd_kernel(
+    const uint16_t *x, int64_t ldx, const uint16_t *dy, int64_t lddy, const uint16_t *u,
+    int64_t ldu, const float *w, const float *b, const uint16_t *res, int64_t ldres, uint16_t *dx,
+    int64_t lddx, uint16_t *du, int64_t lddu, float *part_w, float *part_b, int64_t rows, int cols,
+    float eps)
+{
+    constexpr int MAXC = 4;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int nchunk = cols / 8;
+    float pw[MAXC][8], pb[MAXC][8];
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pw[c][e] = pb[c][e] = 0.0f;
+
+    const int64_t r0 = (int64_t)blockIdx.x * LN_ROWS;
+    for (int64_t row = r0 + wv; row < r0 + LN_ROWS && row < rows; row += 4) {
+        float xv[MAXC][8], gv[MAXC][8];
+        float s = 0.0f;
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) {
+            const int ch = lane + 64 * c;
+            if (ch < nchunk) {
+                unpack8(ld16(x + row * ldx + 8 * ch), xv[c]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s += xv[c][e];
+            }
+        }
+        const float mean = wave_sum_b(s) / (float)cols;
+        float q = 0.0f;
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c)
+            if (lane + 64 * c < nchunk)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float d = xv[c][e] - mean;
+                    q += d * d;
+                }
+        const float rstd = rsqrtf(wave_sum_b(q) / (float)cols + eps);
+        // xh, the upstream gradient of the normalised affine output, g
+        float m1 = 0.0f, m2 = 0.0f;
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) {
+            const int ch = lane + 64 * c;
+            if (ch < nchunk) {
+                float dv[8];
+                unpack8(ld16(dy + row * lddy + 8 * ch), dv);
+                float uv[8];
+                if (GATED) unpack8(ld16(u + row * ldu + 8 * ch), uv);
+                float duv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int col = 8 * ch + e;
+                    const float xh = (xv[c][e] - mean) * rstd;
+                    xv[c][e] = xh;
+                    float dyh = dv[e];
+                    if (GATED) {
+                        duv[e] = dv[e] * (xh * w[col] + (b ? b[col] : 0.0f));
+                        dyh = dv[e] * uv[e];
+                    }
+                    pw[c][e] += dyh * xh;
+                    pb[c][e] += dyh;
+                    const float g = dyh * w[col];
+                    gv[c][e] = g;
+                    m1 += g;
+                    m2 += g * xh;
+                }
+                if (GATED) *reinterpret_cast<uint4 *>(du + row * lddu + 8 * ch) = pack8(duv);
+            }
+        }
+        m1 = wave_sum_b(m1) / (float)cols;
+        m2 = wave_sum_b(m2) / (float)cols;
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) {
+            const int ch = lane + 64 * c;
+            if (ch < nchunk) {
+                float o[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] = rstd * (gv[c][e] - m1 - xv[c][e] * m2);
+                if (!GATED && res) {
+                    float rv[8];
+                    unpack8(ld16(res + row * ldres + 8 * ch), rv);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) o[e] += rv[e];
+                }
+                *reinterpret_cast<uint4 *>(dx + row * lddx + 8 * ch) = pack8(o);
+            }
+        }
+    }
+    // column partials of this block: the four waves' sums added in wave order
+    __shared__ float red[4][2][64 * 8];
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int ch = lane + 64 * c;
+        if (c > 0) __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            red[wv][0][lane * 8 + e] = pw[c][e];
+            red[wv][1][lane * 8 + e] = pb[c][e];
+        }
+        __syncthreads();
+        if (wv == 0 && ch < nchunk) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int col = 8 * ch + e;
+                float sw = 0.0f, sb = 0.0f;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    sw += red[k][0][lane * 8 + e];
+                    sb += red[k][1][lane * 8 + e];
+                }
+                part_w[(int64_t)blockIdx.x * cols + col] = sw;
+                part_b[(int64_t)blockIdx.x * cols + col] = sb;
+            }
+        }
+    }
+}
+
+int ln_bwd_blocks(int64_t rows) { return (int)((rows + LN_ROWS - 1) / LN_ROWS); }
+
+hipError_t launch_ln_bwd_bf16(bool gated, const void *x, int64_t ldx, const void *dy, int64_t lddy,
+                              const void *u, int64_t ldu, const float *w, const float *b,
+                              const void *res, int64_t ldres, void *dx, int64_t lddx, void *du,
+                              int64_t lddu, float *part_w, float *part_b, float *dw, float *db,
+                              int64_t rows, int cols, float eps, hipStream_t st)
+{
+    const int nb = ln_bwd_blocks(rows);
+    if (nb == 0) return hipSuccess;
+    if (cols % 8 != 0 || cols > 2048) return hipErrorInvalidValue;
+    if (gated)
+        hipLaunchKernelGGL(ln_bwd_kernel<true>, dim3((unsigned)nb), dim3(256), 0, st,
+                           (const uint16_t *)x, ldx, (const uint16_t *)dy, lddy,
+                           (const uint16_t *)u, ldu, w, b, (const uint16_t *)res, ldres,
+                           (uint16_t *)dx, lddx, (uint16_t *)du, lddu, part_w, part_b, rows, cols,
+                           eps);
+    else
+        hipLaunchKernelGGL(ln_bwd_kernel<false>, dim3((unsigned)nb), dim3(256), 0, st,
+                           (const uint16_t *)x, ldx, (const uint16_t *)dy, lddy,
+                           (const uint16_t *)u, ldu, w, b, (const uint16_t *)res, ldres,
+                           (uint16_t *)dx, lddx, (uint16_t *)du, lddu, part_w, part_b, rows, cols,
+                           eps);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, st,
+                       part_w, (int64_t)cols, nb, dw);
+    e = hipGetLastError();
+    if (e != hipSuccess || !db) return e;
+    hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, st,
+                       part_b, (int64_t)cols, nb, db);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// dz = ds * SiLU'(z), in place on ds, over [T][C] (C a multiple of 8)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void dsilu_kernel(uint16_t *ds, int64_t ldd, const uint16_t *z,
+                                                    int64_t ldz, int64_t rows, int cols)
+{
+    const int cpr = cols / 8;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= rows * cpr) return;
+    const int64_t r = i / cpr;
+    const int c = (int)(i % cpr);
+    float dv[8], zv[8];
+    unpack8(ld16(ds + r * ldd + 8 * c), dv);
+    unpack8(ld16(z + r * ldz + 8 * c), zv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        // sigma(z) (1 + z (1 - sigma(z))); exp(-z) overflowing to inf gives
+        // sigma = 0 and a zero derivative, the limit
+        const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * zv[e]));
+        dv[e] *= sg * (1.0f + zv[e] * (1.0f - sg));
+    }
+    *reinterpret_cast<uint4 *>(ds + r * ldd + 8 * c) = pack8(dv);
+}
+
+hipError_t launch_dsilu_bf16(void *ds, int64_t ldd, const void *z, int64_t ldz, int64_t rows,
+                             int cols, hipStream_t st)
+{
+    if (rows <= 0) return hipSuccess;
+    if (cols % 8 != 0) return hipErrorInvalidValue;
+    const int64_t n = rows * (cols / 8);
+    hipLaunchKernelGGL(dsilu_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       (uint16_t *)ds, ldd, (const uint16_t *)z, ldz, rows, cols);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// dst[c][r] = src[r][c] for a [R][C] bf16 matrix (R, C multiples of 64)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t *src, int R, int C,
+                                                        uint16_t *dst)
+{
+    __shared__ uint16_t tile[64][66];
+    const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+        const int r = i / 64, c = i % 64;
+        tile[r][c] = src[(int64_t)(r0 + r) * C + c0 + c];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+        const int c = i / 64, r = i % 64;
+        dst[(int64_t)(c0 + c) * R + r0 + r] = tile[r][c];
+    }
+}
+
+hipError_t launch_transpose_bf16(const void *src, int R, int C, void *dst, hipStream_t st)
+{
+    if (R % 64 != 0 || C % 64 != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)(C / 64), (unsigned)(R / 64)), dim3(256), 0,
+                       st, (const uint16_t *)src, R, C, (uint16_t *)dst);
+    return hipGetLastError();
+}
+
+// dst[0 .. n) = v
+__global__ __launch_bounds__(256) void fill_f32_kernel(float *dst, int64_t n, float v)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) dst[i] = v;
+}
+
+hipError_t launch_fill_f32(float *dst, size_t n, float v, hipStream_t st)
+{
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dst,
+                       (int64_t)n, v);
+    return hipGetLastError();
+}
+
+}  // namespace sla

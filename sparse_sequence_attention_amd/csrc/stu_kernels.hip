@@ -116,7 +116,9 @@ hipError_t launch_gated_layernorm_bf16(const void *a, int64_t lda, const void *u
 }
 
 // ---------------------------------------------------------------------------
-// GEMM  C[M][N] = epi(A[M][K] . W[N][K]^T)
+// GEMM  C[M][N] = epi(A[M][K] . W[N][K]^T), with z = acc (+ bias[n]):
+//   EPI 0: C = SiLU(z)        EPI 1: C = z + R (residual)
+//   EPI 2: C = z              EPI 3: C = SiLU(z) and Z = z (the pre-activation)
 // Workgroup tile 128 x 128, 4 waves in 2 x 2, K steps of 64.  The waves compute
 // C^T blocks (W rows as the MFMA A operand, A rows as B) so that each lane ends
 // with four consecutive output columns of one row: 8-byte stores.
@@ -128,7 +130,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t *A, in
                                                            const uint16_t *W, int64_t ldw,
                                                            const float *bias, const uint16_t *R,
                                                            int64_t ldr, uint16_t *C, int64_t ldc,
-                                                           int64_t M, int N, int K)
+                                                           uint16_t *Z, int64_t ldz, int64_t M,
+                                                           int N, int K)
 {
     __shared__ __align__(16) uint16_t sa[2][GM * GK];
     __shared__ __align__(16) uint16_t sw[2][GN * GK];
@@ -210,10 +213,12 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t *A, in
                 float o[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o[e] = acc[nb][mb][4 * g + e] + (bias ? bias[n + e] : 0.0f);
-                if (EPI == 0) {
+                if (EPI == 3)
+                    *reinterpret_cast<uint2 *>(Z + m * ldz + n) = cvt4_u2(o[0], o[1], o[2], o[3]);
+                if (EPI == 0 || EPI == 3) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) o[e] = o[e] * sigmoid_fast(o[e], -1.4426950408889634f);
-                } else {
+                } else if (EPI == 1) {
                     const uint2 rr = *reinterpret_cast<const uint2 *>(R + m * ldr + n);
                     o[0] += bf16_lo(rr.x);
                     o[1] += bf16_hi(rr.x);
@@ -228,20 +233,20 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t *A, in
 
 hipError_t launch_gemm_bf16(const void *A, int64_t lda, const void *W, int64_t ldw,
                             const float *bias, const void *R, int64_t ldr, void *C, int64_t ldc,
-                            int64_t M, int N, int K, int epi, hipStream_t st)
+                            void *Z, int64_t ldz, int64_t M, int N, int K, int epi, hipStream_t st)
 {
     if (M <= 0) return hipSuccess;
-    if (N % GN != 0 || K % GK != 0) return hipErrorInvalidValue;
+    if (N % GN != 0 || K % GK != 0 || epi < 0 || epi > 3) return hipErrorInvalidValue;
+    if ((epi == 1 && !R) || (epi == 3 && !Z)) return hipErrorInvalidValue;
     const int64_t tiles = ((M + GM - 1) / GM) * (N / GN);
     dim3 grid((unsigned)tiles), block(256);
-    if (epi == 0)
-        hipLaunchKernelGGL(gemm_bf16_kernel<0>, grid, block, 0, st, (const uint16_t *)A, lda,
-                           (const uint16_t *)W, ldw, bias, (const uint16_t *)R, ldr, (uint16_t *)C,
-                           ldc, M, N, K);
-    else
-        hipLaunchKernelGGL(gemm_bf16_kernel<1>, grid, block, 0, st, (const uint16_t *)A, lda,
-                           (const uint16_t *)W, ldw, bias, (const uint16_t *)R, ldr, (uint16_t *)C,
-                           ldc, M, N, K);
+    auto kern = epi == 0 ? gemm_bf16_kernel<0>
+                : epi == 1 ? gemm_bf16_kernel<1>
+                : epi == 2 ? gemm_bf16_kernel<2>
+                           : gemm_bf16_kernel<3>;
+    hipLaunchKernelGGL(kern, grid, block, 0, st, (const uint16_t *)A, lda, (const uint16_t *)W, ldw,
+                       bias, (const uint16_t *)R, ldr, (uint16_t *)C, ldc, (uint16_t *)Z, ldz, M, N,
+                       K);
     return hipGetLastError();
 }
 

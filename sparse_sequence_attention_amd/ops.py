@@ -215,8 +215,11 @@ def stu_layer_fwd(x: torch.Tensor, offsets: torch.Tensor, num_targets: Optional[
                   contextual_len: int, max_seq_len: int, alpha: float = 1.0,
                   ln_eps: float = 1e-5, ln1_b=None, b_uvqk=None, ln2_b=None, b_out=None,
                   out: Optional[torch.Tensor] = None, want_uvqk: bool = False,
-                  workspace: Optional[torch.Tensor] = None):
-    """One STU layer forward (bf16): LN -> UVQK GEMM + SiLU -> SLA -> LN(A)*U -> GEMM + x."""
+                  want_attn: bool = False, workspace: Optional[torch.Tensor] = None):
+    """One STU layer forward (bf16): LN -> UVQK GEMM + SiLU -> SLA -> LN(A)*U -> GEMM + x.
+
+    Returns out, then uvqk [T, NW] if want_uvqk, then the attention output
+    A [T, H*d_v] if want_attn (what stu_layer_bwd keeps from the forward)."""
     if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
         raise TypeError("x must be a contiguous bf16 [T, D] tensor")
     T, D = x.shape
@@ -238,10 +241,64 @@ def stu_layer_fwd(x: torch.Tensor, offsets: torch.Tensor, num_targets: Optional[
     ws = _workspace(nbytes, x.device, workspace)
     out = torch.empty_like(x) if out is None else out
     uvqk = torch.empty((T, nw), dtype=torch.bfloat16, device=x.device) if want_uvqk else None
+    attn = torch.empty((T, heads * d_v), dtype=torch.bfloat16, device=x.device) if want_attn else None
     C.check(lib.stu_layer_fwd(ctypes.byref(d), _ptr(x), _ptr(ln1_w), _ptr(ln1_b), _ptr(w_uvqk),
                               _ptr(b_uvqk), _ptr(ln2_w), _ptr(ln2_b), _ptr(w_out), _ptr(b_out),
-                              _ptr(out), _ptr(uvqk), _ptr(ws), ws.numel(), _stream(x.device)))
-    return (out, uvqk) if want_uvqk else out
+                              _ptr(out), _ptr(uvqk), _ptr(attn), _ptr(ws), ws.numel(),
+                              _stream(x.device)))
+    extra = tuple(t for t, want in ((uvqk, want_uvqk), (attn, want_attn)) if want)
+    return (out,) + extra if extra else out
+
+
+def stu_layer_bwd(x: torch.Tensor, dout: torch.Tensor, offsets: torch.Tensor,
+                  num_targets: Optional[torch.Tensor], ln1_w: torch.Tensor, w_uvqk: torch.Tensor,
+                  ln2_w: torch.Tensor, w_out: torch.Tensor, *, heads: int, d_qk: int, d_v: int,
+                  k1: int, k2: int, contextual_len: int, max_seq_len: int, alpha: float = 1.0,
+                  ln_eps: float = 1e-5, ln1_b=None, b_uvqk=None, ln2_b=None, b_out=None,
+                  attn: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Gradients of stu_layer_fwd given dout, as a dict: dx (bf16 [T, D]) and the
+    fp32 parameter gradients dln1_w, dw_uvqk, dln2_w, dw_out, plus dln1_b,
+    db_uvqk, dln2_b, db_out for the biases that are given.  attn: the saved
+    attention output (stu_layer_fwd(want_attn=True)); recomputed when None."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+        raise TypeError("x must be a contiguous bf16 [T, D] tensor")
+    if dout.shape != x.shape or dout.dtype != torch.bfloat16 or not dout.is_contiguous():
+        raise TypeError("dout must be a contiguous bf16 tensor shaped like x")
+    T, D = x.shape
+    nu = heads * d_v
+    nw = 2 * nu + 2 * heads * d_qk
+    for name, w, shape in (("w_uvqk", w_uvqk, (nw, D)), ("w_out", w_out, (D, nu))):
+        if tuple(w.shape) != shape or w.dtype != torch.bfloat16 or not w.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous bf16 tensor of shape {shape}")
+    if attn is not None and (tuple(attn.shape) != (T, nu) or attn.dtype != torch.bfloat16 or
+                             not attn.is_contiguous()):
+        raise TypeError(f"attn must be a contiguous bf16 tensor of shape {(T, nu)}")
+    for v_ in (ln1_w, ln1_b, b_uvqk, ln2_w, ln2_b, b_out):
+        if v_ is not None and (v_.dtype != torch.float32 or not v_.is_contiguous()):
+            raise TypeError("LayerNorm weights and biases must be contiguous float32 tensors")
+    d = C.STULayerDesc()
+    d.attn = make_problem(torch.bfloat16, offsets, num_targets, T, heads, d_qk, d_v, k1, k2,
+                          contextual_len, max_seq_len, alpha)
+    d.hidden = D
+    d.ln_eps = float(ln_eps)
+    lib = C.load()
+    nbytes = int(lib.stu_layer_bwd_workspace_size(ctypes.byref(d)))
+    ws = _workspace(nbytes, x.device, workspace)
+    f32 = dict(dtype=torch.float32, device=x.device)
+    g = {"dx": torch.empty_like(x), "dln1_w": torch.empty(D, **f32),
+         "dw_uvqk": torch.empty((nw, D), **f32), "dln2_w": torch.empty(nu, **f32),
+         "dw_out": torch.empty((D, nu), **f32)}
+    for name, bias, n in (("dln1_b", ln1_b, D), ("db_uvqk", b_uvqk, nw), ("dln2_b", ln2_b, nu),
+                          ("db_out", b_out, D)):
+        if bias is not None:
+            g[name] = torch.empty(n, **f32)
+    C.check(lib.stu_layer_bwd(
+        ctypes.byref(d), _ptr(x), _ptr(attn), _ptr(ln1_w), _ptr(ln1_b), _ptr(w_uvqk), _ptr(b_uvqk),
+        _ptr(ln2_w), _ptr(ln2_b), _ptr(w_out), _ptr(b_out), _ptr(dout), _ptr(g["dx"]),
+        _ptr(g["dln1_w"]), _ptr(g.get("dln1_b")), _ptr(g["dw_uvqk"]), _ptr(g.get("db_uvqk")),
+        _ptr(g["dln2_w"]), _ptr(g.get("dln2_b")), _ptr(g["dw_out"]), _ptr(g.get("db_out")),
+        _ptr(ws), ws.numel(), _stream(x.device)))
+    return g
 
 
 def stu_truncate(x: Optional[torch.Tensor], offsets: torch.Tensor,

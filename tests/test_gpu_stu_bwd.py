@@ -1,0 +1,148 @@
+"""GPU parity of the STU layer backward (stu_layer_bwd) against the fp64 oracle
+(oracle.stu_layer_bwd, pinned to torch autograd and finite differences), with
+the attention output saved by the forward or recomputed, ragged and empty
+sequences, and run-to-run determinism.
+
+Tolerance: the bf16 mean bar (5e-3 of the rms) as is, the max bar (2e-2 of
+the rms) widened by the storage floor F, the max distance between the oracle
+in its storage-matched mode (bf16 rounding wherever the layer stores a tensor
+between steps) and the exact oracle.  The weight gradients are sums over all
+tokens of products of stored bf16 values, and F alone reaches several 1e-2 of
+their rms; two bf16 pipelines whose stored values differ by one rounding here
+and there (the GPU's and the storage-matched oracle's) differ by up to about
+F / 2.  Both oracle modes are checked against."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_sequence_attention_amd as sla
+from synthetic import bf16_round_f32, make_stack_workload
+from tests._helpers import BF16_MAX_TOL, BF16_MEAN_TOL, rel_errors
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+GRADS = ("dx", "dln1_w", "dln1_b", "dw_uvqk", "db_uvqk", "dln2_w", "dln2_b", "dw_out", "db_out")
+
+
+def _b(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV).bfloat16()
+
+
+def _f(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def _case(seed, lengths, num_targets, with_bias, ctx=8, k1=128, k2=32):
+    sw = make_stack_workload(seed=seed, lengths=lengths, layers=1, num_targets=num_targets,
+                             contextual_len=ctx, k1=k1, k2=k2)
+    rng = np.random.default_rng(seed + 100)
+    D, NU = sw.hidden, sw.heads * sw.d
+    nw = 4 * NU
+    host = dict(ln1_w=(1.0 + 0.2 * rng.standard_normal(D)).astype(np.float32),
+                w_uvqk=sw.w_uvqk[0],
+                ln2_w=(1.0 + 0.2 * rng.standard_normal(NU)).astype(np.float32),
+                w_out=sw.w_out[0])
+    if with_bias:
+        host.update(ln1_b=0.1 * rng.standard_normal(D), b_uvqk=0.1 * rng.standard_normal(nw),
+                    ln2_b=0.1 * rng.standard_normal(NU), b_out=0.1 * rng.standard_normal(D))
+    host = {k: np.asarray(v, dtype=np.float32) for k, v in host.items()}
+    T = int(sw.offsets[-1])
+    dout = bf16_round_f32(rng.standard_normal((T, D)).astype(np.float32))
+    return sw, host, dout
+
+
+def _kw(sw):
+    return dict(heads=sw.heads, d_qk=sw.d, d_v=sw.d, k1=sw.k1, k2=sw.k2,
+                contextual_len=sw.contextual_len, max_seq_len=sw.max_seq_len)
+
+
+def _dev_params(host):
+    dev = {k: (_b(v) if k in ("w_uvqk", "w_out") else _f(v)) for k, v in host.items()}
+    return dev
+
+
+def _run(sw, host, dout, save_attn):
+    p = _dev_params(host)
+    x = _b(sw.x)
+    offs = torch.from_numpy(sw.offsets).to(DEV)
+    tg = torch.from_numpy(sw.num_targets).to(DEV) if sw.num_targets is not None else None
+    bias = {k: p.get(k) for k in ("ln1_b", "b_uvqk", "ln2_b", "b_out")}
+    attn = None
+    if save_attn:
+        _, attn = sla.stu_layer_fwd(x, offs, tg, p["ln1_w"], p["w_uvqk"], p["ln2_w"], p["w_out"],
+                                    want_attn=True, **bias, **_kw(sw))
+    g = sla.stu_layer_bwd(x, _b(dout), offs, tg, p["ln1_w"], p["w_uvqk"], p["ln2_w"], p["w_out"],
+                          attn=attn, **bias, **_kw(sw))
+    torch.cuda.synchronize()
+    return g
+
+
+def _oracle(sw, host, dout, store_bf16):
+    return oracle.stu_layer_bwd(sw.x, sw.offsets, sw.num_targets, host["ln1_w"], host["w_uvqk"],
+                                host["ln2_w"], host["w_out"], dout, heads=sw.heads, dqk=sw.d,
+                                dv=sw.d, k1=sw.k1, k2=sw.k2, ctx=sw.contextual_len,
+                                N=sw.max_seq_len, ln1_b=host.get("ln1_b"),
+                                b_uvqk=host.get("b_uvqk"), ln2_b=host.get("ln2_b"),
+                                b_out=host.get("b_out"), store_bf16=store_bf16)
+
+
+def _check(g, sw, host, dout):
+    stored = _oracle(sw, host, dout, True)
+    exact = _oracle(sw, host, dout, False)
+    for k in GRADS:
+        if k not in g:
+            continue
+        got = g[k].float().cpu().numpy().astype(np.float64)
+        floor, _ = rel_errors(stored[k], exact[k])
+        smx, smn = rel_errors(got, stored[k])
+        emx, emn = rel_errors(got, exact[k])
+        print(f"  {k:8s} vs stored: max {smx:.3e} mean {smn:.3e} | vs exact: max {emx:.3e} "
+              f"mean {emn:.3e} | floor {floor:.3e}", flush=True)
+        for what, mx, mn in (("storage-matched", smx, smn), ("exact", emx, emn)):
+            assert mn <= BF16_MEAN_TOL, f"{k}: mean {mn:.3e} against the {what} oracle"
+            assert mx <= BF16_MAX_TOL + floor, \
+                f"{k}: max {mx:.3e} against the {what} oracle (floor {floor:.3e})"
+
+
+@pytest.mark.parametrize("save_attn", [True, False])
+def test_stu_layer_bwd_matches_oracle(save_attn):
+    sw, host, dout = _case(1, [700, 129, 1000, 64], 16, with_bias=True)
+    print(f"[case] stu bwd save_attn={save_attn} T={int(sw.offsets[-1])}", flush=True)
+    g = _run(sw, host, dout, save_attn)
+    _check(g, sw, host, dout)
+
+
+def test_stu_layer_bwd_ragged_and_empty_sequences():
+    sw, host, dout = _case(2, [0, 1, 300, 57, 0, 129], 0, with_bias=False, ctx=0, k1=64, k2=8)
+    sw.num_targets = None
+    print(f"[case] stu bwd ragged T={int(sw.offsets[-1])}", flush=True)
+    g = _run(sw, host, dout, save_attn=False)
+    assert set(g) == {"dx", "dln1_w", "dw_uvqk", "dln2_w", "dw_out"}
+    _check(g, sw, host, dout)
+
+
+def test_stu_layer_bwd_is_deterministic_and_saved_attn_matches_recompute():
+    sw, host, dout = _case(3, [513, 700, 33], 8, with_bias=True)
+    print(f"[case] stu bwd determinism T={int(sw.offsets[-1])}", flush=True)
+    a = _run(sw, host, dout, save_attn=False)
+    b = _run(sw, host, dout, save_attn=False)
+    c = _run(sw, host, dout, save_attn=True)
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+        # the saved A comes from the same kernels on the same inputs
+        assert torch.equal(a[k], c[k]), k
+
+
+def test_stu_layer_bwd_without_tokens_gives_zero_parameter_gradients():
+    sw, host, _ = _case(4, [64], 0, with_bias=True)
+    p = _dev_params(host)
+    x = torch.empty((0, sw.hidden), dtype=torch.bfloat16, device=DEV)
+    offs = torch.zeros(3, dtype=torch.int64, device=DEV)
+    bias = {k: p[k] for k in ("ln1_b", "b_uvqk", "ln2_b", "b_out")}
+    g = sla.stu_layer_bwd(x, x.clone(), offs, None, p["ln1_w"], p["w_uvqk"], p["ln2_w"],
+                          p["w_out"], **bias, **_kw(sw))
+    torch.cuda.synchronize()
+    assert g["dx"].numel() == 0
+    for k in GRADS[1:]:
+        assert torch.count_nonzero(g[k]).item() == 0, k

@@ -247,11 +247,17 @@ def test_bwd_and_layer_argument_errors(lib):
     d = C.STULayerDesc()
     d.attn = _problem(dtype=C.SLA_F32)
     d.hidden, d.ln_eps = 512, 1e-5
-    args = [FAKE] * 12 + [ctypes.c_size_t(1 << 30), None]
-    assert lib.stu_layer_fwd(ctypes.byref(d), *args[:12], 1 << 30, None) == C.SLA_ERR_UNSUPPORTED
+    args = [FAKE] * 13
+    assert lib.stu_layer_fwd(ctypes.byref(d), *args, 1 << 30, None) == C.SLA_ERR_UNSUPPORTED
+    bargs = [FAKE] * 21  # 20 tensors and the workspace
+    assert lib.stu_layer_bwd(ctypes.byref(d), *bargs, 1 << 30, None) == C.SLA_ERR_UNSUPPORTED
     d.attn = _problem()
     d.hidden = 200
-    assert lib.stu_layer_fwd(ctypes.byref(d), *args[:12], 1 << 30, None) == C.SLA_ERR_UNSUPPORTED
+    assert lib.stu_layer_fwd(ctypes.byref(d), *args, 1 << 30, None) == C.SLA_ERR_UNSUPPORTED
+    assert lib.stu_layer_bwd(ctypes.byref(d), *bargs, 1 << 30, None) == C.SLA_ERR_UNSUPPORTED
+    d.hidden = 512
+    bargs_null_dx = [FAKE] * 11 + [None] + [FAKE] * 9
+    assert lib.stu_layer_bwd(ctypes.byref(d), *bargs_null_dx, 1 << 30, None) == C.SLA_ERR_NULL
     assert lib.stu_truncate(2, 10, FAKE, None, 1, 0, FAKE, 512, 1, FAKE, None, None, None, 10,
                             None) == C.SLA_ERR_INVALID
 
