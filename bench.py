@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--workload", choices=(WORKLOAD, "stu_layer"), default=WORKLOAD,
+                    help="long_16k: the SLA forward + backward (default); stu_layer: one full "
+                         "STU layer forward + backward at the 18-layer stack's shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-len", type=int, default=16384)
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_long_16k.json"),
@@ -105,6 +108,9 @@ def main():
               "value times the GPU count", file=sys.stderr)
         sys.exit(2)
 
+    if args.workload == "stu_layer":
+        bench_stu_layer(args)
+        return
     import torch
     import sparse_sequence_attention_amd as sla
     from synthetic import make_sla_workload, CONFIGS
@@ -218,6 +224,101 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_len)
+    print(json.dumps(line), flush=True)
+
+
+def bench_stu_layer(args):
+    """One STU layer (the first, full-length layer of the 18-layer stack:
+    B = 8, lengths U[2048, 4096], 64 targets, contextual 16, D = 512, H = 4,
+    d = 128, K1 = 512, K2 = 64, N = 4096), forward with the attention output
+    kept, then the backward with every parameter gradient.  Useful FLOPs: the
+    two projections forward (2 T D NW + 2 T NU D) and backward (twice that:
+    input and weight gradients), the attention's visible pairs (512 flop per
+    pair and head forward, 1280 backward); the backward's recomputation of
+    the projection is not counted."""
+    import torch
+    import sparse_sequence_attention_amd as sla
+    from synthetic import make_stack_workload
+
+    sw = make_stack_workload(seed=args.seed, layers=1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    rng = np.random.default_rng(args.seed + 1)
+    T, D, H, d = int(sw.offsets[-1]), sw.hidden, sw.heads, sw.d
+    NU, NW = H * d, 4 * H * d
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev).bfloat16()  # noqa
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)  # noqa
+    x = bf(sw.x)
+    dout = bf(rng.standard_normal((T, D), dtype=np.float32))
+    ln1_w, ln2_w = f32(sw.ln1_w[0]), f32(sw.ln2_w[0])
+    w_uvqk, w_out = bf(sw.w_uvqk[0]), bf(sw.w_out[0])
+    offs = torch.from_numpy(sw.offsets).to(dev)
+    tg = torch.from_numpy(sw.num_targets).to(dev)
+    kw = dict(heads=H, d_qk=d, d_v=d, k1=sw.k1, k2=sw.k2, contextual_len=sw.contextual_len,
+              max_seq_len=sw.max_seq_len)
+    out = torch.empty_like(x)
+    ws_f, ws_b = (torch.empty(sla.stu_layer_workspace_bytes(T, D, offs, tg, backward=b, **kw),
+                              dtype=torch.uint8, device=dev) for b in (False, True))
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        _, attn = sla.stu_layer_fwd(x, offs, tg, ln1_w, w_uvqk, ln2_w, w_out, out=out,
+                                    want_attn=True, workspace=ws_f, **kw)
+        if ev is not None:
+            ev[1].record()
+        g = sla.stu_layer_bwd(x, dout, offs, tg, ln1_w, w_uvqk, ln2_w, w_out, attn=attn,
+                              workspace=ws_b, **kw)
+        if ev is not None:
+            ev[2].record()
+        return g
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    ms = fwd + bwd
+    pairs = sla.count_pairs_host(sw.offsets, sw.num_targets, sw.k1, sw.k2, sw.contextual_len) * H
+    gemm_fwd = 2 * T * D * NW + 2 * T * NU * D
+    useful_fwd = gemm_fwd + pairs * 4 * d
+    useful_bwd = 2 * gemm_fwd + pairs * 10 * d
+    value = (useful_fwd + useful_bwd) / (ms * 1e-3) / 1e12
+    line = {
+        "metric": "STU layer fwd+bwd useful TFLOP/s (18-layer stack shape, full-length layer)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"stu_layer: B=8, L_b ~ U[2048, 4096], 64 targets, ctx 16, D={D}, "
+                        f"H={H}, d={d}, K1={sw.k1}, K2={sw.k2}, N={sw.max_seq_len}, "
+                        f"seed {args.seed}",
+            "total_tokens": T,
+            "visible_pairs_all_heads": pairs,
+            "useful_flop_fwd": useful_fwd,
+            "useful_flop_bwd": useful_bwd,
+        },
+        "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_MFMA_TFLOPS, 2),
+        "phase_ms": {"fwd": round(fwd, 4), "bwd": round(bwd, 4)},
+        "phase_tflops": {"fwd": round(useful_fwd / (fwd * 1e-3) / 1e12, 2),
+                         "bwd": round(useful_bwd / (bwd * 1e-3) / 1e12, 2)},
+        "wall_s_timed_region": round(wall, 4),
+    }
     print(json.dumps(line), flush=True)
 
 

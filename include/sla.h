@@ -236,9 +236,11 @@ sla_status_t stu_layer_fwd(const stu_layer_desc_t *d, const void *x, const float
 /* Gradients of one STU layer (the stu_layer_fwd chain differentiated in
  * reverse; ULTRA-HSTU paper, section 4.2.2 selective rematerialisation: the
  * normalised input and the fused projection are recomputed from x, the
- * attention output A is taken from the forward when given):
- *   dW2 = dout^T y, db_out = column sums of dout, dy = dout W2
- *   gated LayerNorm backward -> dU, dA, dln2_w, dln2_b
+ * attention output A is taken from the forward when given, and y is formed
+ * inside the gated LayerNorm backward):
+ *   dy = dout W2
+ *   gated LayerNorm backward -> dU, dA, dln2_w, dln2_b and y
+ *   dW2 = dout^T y, db_out = column sums of dout
  *   sla_bwd(Q, K, V; dA) -> dQ, dK, dV
  *   dz = d[U|V|Q|K] (.) SiLU'(z), z the projection before SiLU
  *   dW1 = dz^T n, db_uvqk = column sums of dz, dn = dz W1

@@ -232,7 +232,7 @@ sla_status_t make_params(const sla_problem_t *p, int op, void *ws, size_t ws_byt
 // STU layer backward workspace: recomputed activations, their gradients, a
 // transposed weight, fp32 partial sums, and the attention workspace last.
 struct StuBwdLayout {
-    size_t n, z, uvqk, A, y, dy, dA, dz, dn, wt, part, vec, attn, total;
+    size_t n, z, uvqk, A, y, dy, dA, dz, dn, wt, part, vec, mid, attn, total;
     int split_out, split_uvqk;
 };
 
@@ -281,6 +281,7 @@ StuBwdLayout stu_bwd_layout(const stu_layer_desc_t *d)
     if (ln > part) part = ln;
     L.part = take(part * 4);
     L.vec = take((NW > D ? NW : D) * 4);
+    L.mid = take((size_t)SUM_MID_FLOATS * 4);
     L.attn = at;
     L.total = at + layout(p, SLA_OP_BWD).total;
     return L;
@@ -669,6 +670,7 @@ sla_status_t stu_layer_bwd(const stu_layer_desc_t *d, const void *x, const void 
     uint16_t *wt = reinterpret_cast<uint16_t *>(base + L.wt);
     float *part = reinterpret_cast<float *>(base + L.part);
     float *scratch_w = reinterpret_cast<float *>(base + L.vec);  // sums of unwanted gradients
+    float *mid = reinterpret_cast<float *>(base + L.mid);
     void *attn_ws = base + L.attn;
     const size_t attn_bytes = L.total - L.attn;
     auto or_scratch = [&](float *g) { return g ? g : scratch_w; };
@@ -682,7 +684,7 @@ sla_status_t stu_layer_bwd(const stu_layer_desc_t *d, const void *x, const void 
         e = (call);                              \
         if (e != hipSuccess) return hip_fail(e, what); \
     } while (0)
-    // recomputed activations: n, z, uvqk = SiLU(z), A (unless saved), y
+    // recomputed activations: n, z, uvqk = SiLU(z), A (unless saved)
     STU_TRY(launch_layernorm_bf16(x, ln1_w, ln1_b, n, T, D, d->ln_eps, s), "layernorm");
     STU_TRY(launch_gemm_bf16(n, D, w_uvqk, D, b_uvqk, nullptr, 0, uvqk, NW, z, NW, T, NW, D, 3, s),
             "uvqk projection");
@@ -691,22 +693,23 @@ sla_status_t stu_layer_bwd(const stu_layer_desc_t *d, const void *x, const void 
                      attn_bytes, stream);
         if (st != SLA_OK) return st;
     }
-    STU_TRY(launch_gated_layernorm_bf16(A, NU, uvqk, NW, ln2_w, ln2_b, y, T, NU, d->ln_eps, s),
-            "gated layernorm");
-    // output projection: dy = dout W2 (W2^T staged as [NU][D]), dW2 = dout^T y, db_out
+    // output projection input gradient: dy = dout W2 (W2^T staged as [NU][D])
     STU_TRY(launch_transpose_bf16(w_out, D, NU, wt, s), "weight transpose");
     STU_TRY(launch_gemm_bf16(dout, D, wt, D, nullptr, nullptr, 0, dy, NU, nullptr, 0, T, NU, D, 2,
                              s),
             "dy product");
+    // gated LayerNorm: dA, dU (into the U block of dz), dln2, and y itself
+    STU_TRY(launch_ln_bwd_bf16(true, A, NU, dy, NU, uvqk, NW, ln2_w, ln2_b, nullptr, 0, dA, NU, dz,
+                               NW, dw_out ? y : nullptr, NU, part,
+                               part + (size_t)ln_bwd_blocks(T) * NU, mid, or_scratch(dln2_w),
+                               dln2_b, T, NU, d->ln_eps, s),
+            "gated layernorm backward");
+    // output projection weights: dW2 = dout^T y, db_out
     if (dw_out)
         STU_TRY(launch_gemm_tn_bf16(dout, D, y, NU, T, D, NU, part, L.split_out, dw_out, s),
                 "output weight gradient");
-    if (db_out) STU_TRY(launch_colsum_bf16(dout, D, T, D, part, db_out, s), "output bias gradient");
-    // gated LayerNorm: dA, dU (into the U block of dz), dln2
-    STU_TRY(launch_ln_bwd_bf16(true, A, NU, dy, NU, uvqk, NW, ln2_w, ln2_b, nullptr, 0, dA, NU, dz,
-                               NW, part, part + (size_t)ln_bwd_blocks(T) * NU, or_scratch(dln2_w),
-                               dln2_b, T, NU, d->ln_eps, s),
-            "gated layernorm backward");
+    if (db_out)
+        STU_TRY(launch_colsum_bf16(dout, D, T, D, part, db_out, mid, s), "output bias gradient");
     // attention: dQ, dK, dV into their blocks of dz
     st = sla_bwd(p, uvqk + 2 * NU, NW, uvqk + 2 * NU + NQK, NW, uvqk + NU, NW, dA, NU, dz + 2 * NU,
                  NW, dz + 2 * NU + NQK, NW, dz + NU, NW, attn_ws, attn_bytes, stream);
@@ -716,14 +719,15 @@ sla_status_t stu_layer_bwd(const stu_layer_desc_t *d, const void *x, const void 
     if (dw_uvqk)
         STU_TRY(launch_gemm_tn_bf16(dz, NW, n, D, T, NW, D, part, L.split_uvqk, dw_uvqk, s),
                 "projection weight gradient");
-    if (db_uvqk) STU_TRY(launch_colsum_bf16(dz, NW, T, NW, part, db_uvqk, s), "projection bias gradient");
+    if (db_uvqk)
+        STU_TRY(launch_colsum_bf16(dz, NW, T, NW, part, db_uvqk, mid, s), "projection bias gradient");
     STU_TRY(launch_transpose_bf16(w_uvqk, NW, D, wt, s), "weight transpose");
     STU_TRY(launch_gemm_bf16(dz, NW, wt, NW, nullptr, nullptr, 0, dn, D, nullptr, 0, T, D, NW, 2, s),
             "dn product");
     // LayerNorm 1 with the residual: dx = LN backward + dout
     STU_TRY(launch_ln_bwd_bf16(false, x, D, dn, D, nullptr, 0, ln1_w, ln1_b, dout, D, dx, D,
-                               nullptr, 0, part, part + (size_t)ln_bwd_blocks(T) * D,
-                               or_scratch(dln1_w), dln1_b, T, D, d->ln_eps, s),
+                               nullptr, 0, nullptr, 0, part, part + (size_t)ln_bwd_blocks(T) * D,
+                               mid, or_scratch(dln1_w), dln1_b, T, D, d->ln_eps, s),
             "layernorm backward");
 #undef STU_TRY
     return SLA_OK;

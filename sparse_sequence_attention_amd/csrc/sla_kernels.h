@@ -90,17 +90,24 @@ hipError_t launch_gemm_bf16(const void *A, int64_t lda, const void *W, int64_t l
 // multiples of 128.
 hipError_t launch_gemm_tn_bf16(const void *A, int64_t lda, const void *B, int64_t ldb, int64_t T,
                                int M, int N, float *part, int splits, float *out, hipStream_t st);
+// out[i] = sum_s part[s][i] (count % 4 == 0) in a fixed order; mid (nullable,
+// SUM_MID_FLOATS floats) spreads a short range with many splits over more
+// workgroups.
+constexpr int64_t SUM_MID_FLOATS = 131072;
+hipError_t sum_splits(const float *part, int64_t count, int splits, float *out, float *mid,
+                      hipStream_t st);
 int colsum_blocks(int64_t T);
 hipError_t launch_colsum_bf16(const void *X, int64_t ld, int64_t T, int C, float *part, float *out,
-                              hipStream_t st);
+                              float *mid, hipStream_t st);
 int ln_bwd_blocks(int64_t rows);
-// LayerNorm backward (gated: y = (LN(x) w + b) (.) u, du also written);
-// part_w / part_b: [ln_bwd_blocks(rows)][cols]; db nullable; res (plain
-// only, nullable) is added to dx.
+// LayerNorm backward (gated: y = (LN(x) w + b) (.) u; du and, when y is
+// non-NULL, y also written); part_w / part_b: [ln_bwd_blocks(rows)][cols];
+// db nullable; res (plain only, nullable) is added to dx.
 hipError_t launch_ln_bwd_bf16(bool gated, const void *x, int64_t ldx, const void *dy, int64_t lddy,
                               const void *u, int64_t ldu, const float *w, const float *b,
                               const void *res, int64_t ldres, void *dx, int64_t lddx, void *du,
-                              int64_t lddu, float *part_w, float *part_b, float *dw, float *db,
+                              int64_t lddu, void *y, int64_t ldy, float *part_w, float *part_b,
+                              float *mid, float *dw, float *db,
                               int64_t rows, int cols, float eps, hipStream_t st);
 hipError_t launch_dsilu_bf16(void *ds, int64_t ldd, const void *z, int64_t ldz, int64_t rows,
                              int cols, hipStream_t st);

@@ -1,7 +1,8 @@
 // stu_bwd.hip -- kernels of the STU layer backward (ULTRA-HSTU paper, section 3
 // Eq.1-5 differentiated in the reverse of the Code Listing 1 order; selective
 // rematerialisation as in section 4.2.2: the normalised input and the fused
-// projection are recomputed, the attention output is kept):
+// projection are recomputed, the attention output is kept, and y is formed
+// inside the gated LayerNorm backward):
 //   - a weight-gradient GEMM C[m][n] = sum_t A[t][m] B[t][n] over the token
 //     dimension, split over token ranges into fp32 partials that a second
 //     kernel adds in a fixed order (no atomics);
@@ -22,6 +23,16 @@ namespace sla {
 // MFMA operands (8 consecutive tokens of one column per lane) come from
 // transposing LDS reads; A and B use the same token order, so the sum is exact
 // in any order of the 8 k-slots.
+__device__ __forceinline__ void unpack8(const uint4 &r, float *f)
+{
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f[2 * e] = bf16_lo(w[e]);
+        f[2 * e + 1] = bf16_hi(w[e]);
+    }
+}
+
 constexpr int WG_M = 128, WG_N = 128, WG_T = 64;
 
 __device__ __forceinline__ int wg_swz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
@@ -121,15 +132,73 @@ __global__ __launch_bounds__(256, 2) void gemm_tn_kernel(const uint16_t *A, int6
             }
 }
 
-// out[i] = sum_s part[s][i] in split order (also used for the column partials)
-__global__ __launch_bounds__(256) void sum_partials_kernel(const float *part, int64_t count,
-                                                           int splits, float *out)
+// ---------------------------------------------------------------------------
+// out[i] = sum over s < splits of part[s][i], i < count (count % 4 == 0), in a
+// fixed order: block (x, y) covers floats [256 x, 256 x + 256) (a float4 per
+// lane) and the splits of group y; wave w adds splits s0 + w, s0 + w + 4, ...
+// in increasing order and the four waves' sums are added in wave order.  A
+// short float range with many splits is spread over G groups whose sums go
+// to `mid` [G][count], then a second launch adds the G group sums.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void sum_splits_kernel(const float *part, int64_t count,
+                                                         int splits, int per, float *out)
 {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= count) return;
-    float acc = 0.0f;
-    for (int s = 0; s < splits; ++s) acc += part[(int64_t)s * count + i];
-    out[i] = acc;
+    __shared__ floatx4 red[4][64];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t i = (int64_t)blockIdx.x * 256 + 4 * lane;
+    const int s0 = (int)blockIdx.y * per;
+    const int s1 = s0 + per < splits ? s0 + per : splits;
+    floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (i < count) {
+        const floatx4 *p = reinterpret_cast<const floatx4 *>(part + i);
+        const int64_t step = count / 4;  // one split, in float4
+        int s = s0 + wv;
+        for (; s + 12 < s1; s += 16) {
+            const floatx4 a = p[(int64_t)s * step], b = p[(int64_t)(s + 4) * step];
+            const floatx4 c = p[(int64_t)(s + 8) * step], d = p[(int64_t)(s + 12) * step];
+            acc += a;
+            acc += b;
+            acc += c;
+            acc += d;
+        }
+        for (; s < s1; s += 4) acc += p[(int64_t)s * step];
+    }
+    red[wv][lane] = acc;
+    __syncthreads();
+    if (wv == 0 && i < count) {
+        floatx4 r = red[0][lane];
+        r += red[1][lane];
+        r += red[2][lane];
+        r += red[3][lane];
+        *reinterpret_cast<floatx4 *>(out + (int64_t)blockIdx.y * count + i) = r;
+    }
+}
+
+hipError_t sum_splits(const float *part, int64_t count, int splits, float *out, float *mid,
+                      hipStream_t st)
+{
+    if (count <= 0) return hipSuccess;
+    if (count % 4 != 0 || splits < 1) return hipErrorInvalidValue;
+    const int64_t gx = (count + 255) / 256;
+    int groups = 1;
+    if (mid && gx < 256 && splits >= 32) {
+        const int64_t want = (256 + gx - 1) / gx;
+        groups = (int)(splits / 16 < want ? splits / 16 : want);
+    }
+    const int per = (splits + groups - 1) / groups;
+    groups = (splits + per - 1) / per;
+    if (groups == 1) {
+        hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)gx, 1), dim3(256), 0, st, part, count,
+                           splits, splits, out);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)gx, (unsigned)groups), dim3(256), 0, st,
+                       part, count, splits, per, mid);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)gx, 1), dim3(256), 0, st,
+                       (const float *)mid, count, groups, groups, out);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm_tn_bf16(const void *A, int64_t lda, const void *B, int64_t ldb, int64_t T,
@@ -144,47 +213,60 @@ hipError_t launch_gemm_tn_bf16(const void *A, int64_t lda, const void *B, int64_
                        splits);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t count = (int64_t)M * N;
-    hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
-                       st, part, count, splits, out);
-    return hipGetLastError();
+    return sum_splits(part, (int64_t)M * N, splits, out, nullptr, st);
 }
 
 // ---------------------------------------------------------------------------
-// Column sums of a [T][C] bf16 tensor (token stride ld): per block of
-// COLSUM_ROWS rows a partial, then the fixed-order sum.
+// Column sums of a [T][C] bf16 tensor (token stride ld, C % 8 == 0): block
+// (x, y) covers columns [512 x, 512 x + 512) (8 per lane) of rows
+// [COLSUM_ROWS y, ...); wave w adds rows r0 + w, r0 + w + 4, ... in order and
+// the waves' sums are added in wave order into part[y][c]; then the
+// fixed-order sum over the row blocks.
 // ---------------------------------------------------------------------------
-constexpr int COLSUM_ROWS = 512;
+constexpr int COLSUM_ROWS = 128;
 
 __global__ __launch_bounds__(256) void colsum_kernel(const uint16_t *X, int64_t ld, int64_t T,
                                                      int C, float *part)
 {
-    const int c = blockIdx.x * 256 + threadIdx.x;
+    __shared__ float red[4][64 * 8];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int c = (int)blockIdx.x * 512 + 8 * lane;
     const int64_t r0 = (int64_t)blockIdx.y * COLSUM_ROWS;
-    if (c >= C) return;
     const int64_t r1 = r0 + COLSUM_ROWS < T ? r0 + COLSUM_ROWS : T;
-    float acc = 0.0f;
-    for (int64_t r = r0; r < r1; ++r) {
-        const uint32_t w = X[r * ld + c];
-        acc += __uint_as_float(w << 16);
+    float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    if (c < C) {
+        for (int64_t r = r0 + wv; r < r1; r += 4) {
+            float v[8];
+            unpack8(ld16(X + r * ld + c), v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += v[e];
+        }
     }
-    part[(int64_t)blockIdx.y * C + c] = acc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[wv][8 * lane + e] = acc[e];
+    __syncthreads();
+    if (wv == 0 && c < C) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            part[(int64_t)blockIdx.y * C + c + e] =
+                ((red[0][8 * lane + e] + red[1][8 * lane + e]) + red[2][8 * lane + e]) +
+                red[3][8 * lane + e];
+    }
 }
 
 int colsum_blocks(int64_t T) { return (int)((T + COLSUM_ROWS - 1) / COLSUM_ROWS); }
 
 hipError_t launch_colsum_bf16(const void *X, int64_t ld, int64_t T, int C, float *part, float *out,
-                              hipStream_t st)
+                              float *mid, hipStream_t st)
 {
     const int nb = colsum_blocks(T);
     if (nb == 0) return hipSuccess;
-    hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)((C + 255) / 256), (unsigned)nb), dim3(256), 0,
+    if (C % 8 != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)((C + 511) / 512), (unsigned)nb), dim3(256), 0,
                        st, (const uint16_t *)X, ld, T, C, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)((C + 255) / 256)), dim3(256), 0, st,
-                       part, (int64_t)C, nb, out);
-    return hipGetLastError();
+    return sum_splits(part, (int64_t)C, nb, out, mid, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -192,12 +274,14 @@ hipError_t launch_colsum_bf16(const void *X, int64_t ld, int64_t T, int C, float
 // taking every fourth row).  With xh = (x - mean) * rstd of the row:
 //   plain:  g = dy * w;                  dx = rstd (g - mean g - xh mean(g xh)) + res
 //           partial_w += dy * xh,        partial_b += dy
-//   gated (y = (xh * w + b) (.) u):  dyh = dy * u, du = dy * (xh * w + b),
+//   gated (y = (xh * w + b) (.) u, also written when y is non-NULL: the
+//   output projection's weight gradient needs it):
+//                                    dyh = dy * u, du = dy * (xh * w + b),
 //           g = dyh * w;                 dx = rstd (g - mean g - xh mean(g xh))
 //           partial_w += dyh * xh,       partial_b += dyh
 // Rows of up to 64 x 8 x 4 = 2048 columns; each lane owns 8-column chunks.
 // ---------------------------------------------------------------------------
-constexpr int LN_ROWS = 64;
+constexpr int LN_ROWS = 16;
 
 __device__ __forceinline__ float wave_sum_b(float x)
 {
@@ -206,15 +290,6 @@ __device__ __forceinline__ float wave_sum_b(float x)
     return x;
 }
 
-__device__ __forceinline__ void unpack8(const uint4 &r, float *f)
-{
-    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        f[2 * e] = bf16_lo(w[e]);
-        f[2 * e + 1] = bf16_hi(w[e]);
-    }
-}
 
 __device__ __forceinline__ uint4 pack8(const float *f)
 {
@@ -227,8 +302,8 @@ template <bool GATED>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(
     const uint16_t *x, int64_t ldx, const uint16_t *dy, int64_t lddy, const uint16_t *u,
     int64_t ldu, const float *w, const float *b, const uint16_t *res, int64_t ldres, uint16_t *dx,
-    int64_t lddx, uint16_t *du, int64_t lddu, float *part_w, float *part_b, int64_t rows, int cols,
-    float eps)
+    int64_t lddx, uint16_t *du, int64_t lddu, uint16_t *y, int64_t ldy, float *part_w,
+    float *part_b, int64_t rows, int cols, float eps)
 {
     constexpr int MAXC = 4;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -273,7 +348,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
                 unpack8(ld16(dy + row * lddy + 8 * ch), dv);
                 float uv[8];
                 if (GATED) unpack8(ld16(u + row * ldu + 8 * ch), uv);
-                float duv[8];
+                float duv[8], yv[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int col = 8 * ch + e;
@@ -281,7 +356,10 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
                     xv[c][e] = xh;
                     float dyh = dv[e];
                     if (GATED) {
-                        duv[e] = dv[e] * (xh * w[col] + (b ? b[col] : 0.0f));
+                        // same expression as the forward's gated LayerNorm
+                        const float yh = xh * w[col] + (b ? b[col] : 0.0f);
+                        yv[e] = yh * uv[e];
+                        duv[e] = dv[e] * yh;
                         dyh = dv[e] * uv[e];
                     }
                     pw[c][e] += dyh * xh;
@@ -291,7 +369,10 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
                     m1 += g;
                     m2 += g * xh;
                 }
-                if (GATED) *reinterpret_cast<uint4 *>(du + row * lddu + 8 * ch) = pack8(duv);
+                if (GATED) {
+                    *reinterpret_cast<uint4 *>(du + row * lddu + 8 * ch) = pack8(duv);
+                    if (y) *reinterpret_cast<uint4 *>(y + row * ldy + 8 * ch) = pack8(yv);
+                }
             }
         }
         m1 = wave_sum_b(m1) / (float)cols;
@@ -347,7 +428,8 @@ int ln_bwd_blocks(int64_t rows) { return (int)((rows + LN_ROWS - 1) / LN_ROWS); 
 hipError_t launch_ln_bwd_bf16(bool gated, const void *x, int64_t ldx, const void *dy, int64_t lddy,
                               const void *u, int64_t ldu, const float *w, const float *b,
                               const void *res, int64_t ldres, void *dx, int64_t lddx, void *du,
-                              int64_t lddu, float *part_w, float *part_b, float *dw, float *db,
+                              int64_t lddu, void *y, int64_t ldy, float *part_w, float *part_b,
+                              float *mid, float *dw, float *db,
                               int64_t rows, int cols, float eps, hipStream_t st)
 {
     const int nb = ln_bwd_blocks(rows);
@@ -357,23 +439,21 @@ hipError_t launch_ln_bwd_bf16(bool gated, const void *x, int64_t ldx, const void
         hipLaunchKernelGGL(ln_bwd_kernel<true>, dim3((unsigned)nb), dim3(256), 0, st,
                            (const uint16_t *)x, ldx, (const uint16_t *)dy, lddy,
                            (const uint16_t *)u, ldu, w, b, (const uint16_t *)res, ldres,
-                           (uint16_t *)dx, lddx, (uint16_t *)du, lddu, part_w, part_b, rows, cols,
+                           (uint16_t *)dx, lddx, (uint16_t *)du, lddu, (uint16_t *)y, ldy, part_w,
+                           part_b, rows, cols,
                            eps);
     else
         hipLaunchKernelGGL(ln_bwd_kernel<false>, dim3((unsigned)nb), dim3(256), 0, st,
                            (const uint16_t *)x, ldx, (const uint16_t *)dy, lddy,
                            (const uint16_t *)u, ldu, w, b, (const uint16_t *)res, ldres,
-                           (uint16_t *)dx, lddx, (uint16_t *)du, lddu, part_w, part_b, rows, cols,
+                           (uint16_t *)dx, lddx, (uint16_t *)du, lddu, (uint16_t *)y, ldy, part_w,
+                           part_b, rows, cols,
                            eps);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, st,
-                       part_w, (int64_t)cols, nb, dw);
-    e = hipGetLastError();
+    e = sum_splits(part_w, (int64_t)cols, nb, dw, mid, st);
     if (e != hipSuccess || !db) return e;
-    hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, st,
-                       part_b, (int64_t)cols, nb, db);
-    return hipGetLastError();
+    return sum_splits(part_b, (int64_t)cols, nb, db, mid, st);
 }
 
 // ---------------------------------------------------------------------------

@@ -250,6 +250,21 @@ def stu_layer_fwd(x: torch.Tensor, offsets: torch.Tensor, num_targets: Optional[
     return (out,) + extra if extra else out
 
 
+def stu_layer_workspace_bytes(T: int, D: int, offsets: torch.Tensor,
+                              num_targets: Optional[torch.Tensor], *, heads: int, d_qk: int,
+                              d_v: int, k1: int, k2: int, contextual_len: int, max_seq_len: int,
+                              alpha: float = 1.0, backward: bool = False) -> int:
+    """Workspace bytes of stu_layer_fwd (or stu_layer_bwd) for T tokens of width D."""
+    d = C.STULayerDesc()
+    d.attn = make_problem(torch.bfloat16, offsets, num_targets, T, heads, d_qk, d_v, k1, k2,
+                          contextual_len, max_seq_len, alpha)
+    d.hidden = D
+    d.ln_eps = 1e-5
+    lib = C.load()
+    fn = lib.stu_layer_bwd_workspace_size if backward else lib.stu_layer_workspace_size
+    return int(fn(ctypes.byref(d)))
+
+
 def stu_layer_bwd(x: torch.Tensor, dout: torch.Tensor, offsets: torch.Tensor,
                   num_targets: Optional[torch.Tensor], ln1_w: torch.Tensor, w_uvqk: torch.Tensor,
                   ln2_w: torch.Tensor, w_out: torch.Tensor, *, heads: int, d_qk: int, d_v: int,
