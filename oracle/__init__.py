@@ -16,6 +16,11 @@ Functions whose results are "parity pinned" and the pins (tests/test_oracle_*):
   layernorm / stu_layer_fwd -- torch fp64 functional composition, W2 = 0.
   stu_layer_bwd -- torch fp64 autograd of that composition; central finite
       differences of stu_layer_fwd; dout = 0 gives zero gradients.
+  stu_layer_bwd(store_bf16=True) -- torch fp64 autograd of the composition
+      with bf16 rounding of every stored value and of its gradient.
+  sla_fwd_candidates -- dense fp64 torch reference and sla_fwd's target rows
+      on the combined [history | candidates] layout; microbatch invariance;
+      candidates do not see each other.
   truncate  -- direct set construction, identity when tail >= history.
 """
 from __future__ import annotations
@@ -70,6 +75,9 @@ def _load():
         lib.oracle_sla_bwd.argtypes = [i32, P, P, i32, i32, i32, i64, i64, i64, dbl, dbl,
                                        P, P, P, P, P, P, P, P, P]
         lib.oracle_sla_bwd.restype = None
+        lib.oracle_sla_fwd_candidates.argtypes = [i32, P, P, i32, i32, i32, i64, i64, i64,
+                                                  dbl, dbl, P, P, P, P, P, P]
+        lib.oracle_sla_fwd_candidates.restype = None
         lib.oracle_round_bf16.argtypes = [dbl]
         lib.oracle_round_bf16.restype = dbl
         lib.oracle_layernorm.argtypes = [i64, i64, P, P, P, dbl, P]
@@ -134,6 +142,23 @@ def tiles(offsets, num_targets, k1, k2, ctx, bm, bn) -> np.ndarray:
     out = np.zeros((max(n, 1), 3), dtype=np.int64)
     lib.oracle_tiles(len(o) - 1, _ptr(o), _ptr(t), k1, k2, ctx, bm, bn, _ptr(out), n)
     return out[:n]
+
+
+def sla_fwd_candidates(k_hist, v_hist, hist_offsets, q_c, k_c, v_c, cand_offsets, k1, k2, ctx,
+                       N, alpha=1.0) -> np.ndarray:
+    """O_c [C, H, dv] in fp64: each candidate scored against the history keys
+    the first candidate position sees, plus itself (M-FALCON)."""
+    k_hist, v_hist = _f64(k_hist), _f64(v_hist)
+    q_c, k_c, v_c = _f64(q_c), _f64(k_c), _f64(v_c)
+    C, H, dqk = q_c.shape
+    dv = v_c.shape[2]
+    o = np.zeros((C, H, dv), dtype=np.float64)
+    ho, co = _offs(hist_offsets), _offs(cand_offsets)
+    assert len(ho) == len(co)
+    _load().oracle_sla_fwd_candidates(len(ho) - 1, _ptr(ho), _ptr(co), H, dqk, dv, k1, k2, ctx,
+                                      float(N), float(alpha), _ptr(k_hist), _ptr(v_hist),
+                                      _ptr(q_c), _ptr(k_c), _ptr(v_c), _ptr(o))
+    return o
 
 
 def sla_fwd(q, k, v, offsets, num_targets, k1, k2, ctx, N, alpha=1.0,

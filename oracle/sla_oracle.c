@@ -195,6 +195,50 @@ EXPORT void oracle_sla_fwd(int B, const int64_t *offsets, const int32_t *num_tar
     }
 }
 
+/* Candidate scoring against a cached history (M-FALCON; HSTU notes, section
+ * 2.6, and the target-aware mask of the ULTRA-HSTU setting): sequence b has a
+ * history of U_b = hist_offsets[b+1] - hist_offsets[b] tokens whose keys and
+ * values (k_hist, v_hist, [T_hist][H][d]) are computed once, and candidates
+ * cand_offsets[b] .. cand_offsets[b+1] with their own q, k, v ([C][H][d]).
+ * Candidate c scores against the history keys that the first candidate
+ * position U_b sees (j < U_b with U_b - j < K1 or j < K2e) and against
+ * itself; candidates never see each other:
+ *   o_c = (1/N) ( sum_j SiLU(alpha q_c . k_j) v_j + SiLU(alpha q_c . k_c) v_c ). */
+EXPORT void oracle_sla_fwd_candidates(int B, const int64_t *hist_offsets,
+                                      const int64_t *cand_offsets, int H, int dqk, int dv,
+                                      int64_t k1, int64_t k2, int64_t ctx, double N, double alpha,
+                                      const double *k_hist, const double *v_hist,
+                                      const double *qc, const double *kc, const double *vc,
+                                      double *oc)
+{
+    int64_t K2e = k2_effective(k2, ctx);
+    for (int b = 0; b < B; ++b) {
+        const int64_t hb = hist_offsets[b], U = hist_offsets[b + 1] - hist_offsets[b];
+        const int64_t cb = cand_offsets[b], nc = cand_offsets[b + 1] - cand_offsets[b];
+#pragma omp parallel for collapse(2) schedule(dynamic, 16)
+        for (int64_t c = 0; c < nc; ++c) {
+            for (int h = 0; h < H; ++h) {
+                const int64_t tc = cb + c;
+                double acc[512];
+                for (int e = 0; e < dv; ++e) acc[e] = 0.0;
+                const double *q = qc + (tc * H + h) * dqk;
+                for (int64_t j = 0; j < U; ++j) {
+                    if (!(U - j < k1 || j < K2e)) continue;
+                    const int64_t tj = hb + j;
+                    const double a = silu(alpha * dot(q, k_hist + (tj * H + h) * dqk, dqk));
+                    const double *vj = v_hist + (tj * H + h) * dv;
+                    for (int e = 0; e < dv; ++e) acc[e] += a * vj[e];
+                }
+                const double a = silu(alpha * dot(q, kc + (tc * H + h) * dqk, dqk));
+                const double *vs = vc + (tc * H + h) * dv;
+                for (int e = 0; e < dv; ++e) acc[e] += a * vs[e];
+                double *o = oc + (tc * H + h) * dv;
+                for (int e = 0; e < dv; ++e) o[e] = acc[e] / N;
+            }
+        }
+    }
+}
+
 /* Gradients of O = (1/N) sum_j SiLU(alpha q_i.k_j) v_j given dO:
  *   a_ij  = SiLU(alpha s_ij),   s_ij = q_i . k_j
  *   dV_j  = (1/N) sum_i a_ij dO_i
