@@ -38,9 +38,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--workload", choices=(WORKLOAD, "stu_layer"), default=WORKLOAD,
+    ap.add_argument("--workload", choices=(WORKLOAD, "stu_layer", "mfalcon"), default=WORKLOAD,
                     help="long_16k: the SLA forward + backward (default); stu_layer: one full "
-                         "STU layer forward + backward at the 18-layer stack's shape")
+                         "STU layer forward + backward at the 18-layer stack's shape; mfalcon: "
+                         "candidate scoring against cached history keys/values")
+    ap.add_argument("--candidates", type=int, default=4096,
+                    help="mfalcon: candidates per sequence")
+    ap.add_argument("--microbatch", type=int, default=1024,
+                    help="mfalcon: candidates per sequence and call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-len", type=int, default=16384)
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_long_16k.json"),
@@ -55,7 +60,7 @@ def parse():
 
 
 # kernels whose HBM traffic the bench line reports, by the name rocprofv3 gives them
-PMC_KERNELS = {"fwd": "sla_fwd_bf16_kernel<128>", "bwd_dkdv": "sla_bwd_dkdv_bf16_kernel<128",
+PMC_KERNELS = {"fwd": "sla_fwd_bf16_kernel<128, false>", "bwd_dkdv": "sla_bwd_dkdv_bf16_kernel<128",
                "bwd_dq": "sla_bwd_dq_ds_kernel<128>"}
 CALIB_BYTES = 256 * 1024 * 1024
 CALIB_NAME = "neg_kernel_cuda"
@@ -110,6 +115,9 @@ def main():
 
     if args.workload == "stu_layer":
         bench_stu_layer(args)
+        return
+    if args.workload == "mfalcon":
+        bench_mfalcon(args)
         return
     import torch
     import sparse_sequence_attention_amd as sla
@@ -317,6 +325,115 @@ def bench_stu_layer(args):
         "phase_ms": {"fwd": round(fwd, 4), "bwd": round(bwd, 4)},
         "phase_tflops": {"fwd": round(useful_fwd / (fwd * 1e-3) / 1e12, 2),
                          "bwd": round(useful_bwd / (bwd * 1e-3) / 1e12, 2)},
+        "wall_s_timed_region": round(wall, 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_mfalcon(args):
+    """Candidate scoring against a cached history (M-FALCON): the targets_16k
+    histories (B = 16, 16 contextual + U[8192, 16384] tokens; K1 = 1024,
+    K2 = 128, H = 4, d = 128, N = 16656) with their keys/values resident, and
+    `--candidates` candidates per sequence scored in microbatches of
+    `--microbatch` per sequence (one sla_fwd_candidates call each).  A step
+    scores every candidate once.  Useful FLOPs: 4d per (candidate, visible
+    key, head); each candidate sees the history window of the first
+    candidate slot, the global prefix below it, and itself."""
+    import torch
+    import sparse_sequence_attention_amd as sla
+    from synthetic import CONFIGS
+
+    cfg = CONFIGS["targets_16k"]
+    rng = np.random.default_rng(args.seed)
+    hist = [L - 256 for L in cfg.lengths(rng)]  # the sequences without their 256 targets
+    B, H, d = len(hist), cfg.heads, cfg.d
+    m, bm = args.candidates, min(args.microbatch, args.candidates)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    ho = np.concatenate([[0], np.cumsum(hist)]).astype(np.int64)
+    Th = int(ho[-1])
+
+    def normal(n):
+        x = torch.empty((n, H, d), dtype=torch.float32, device=dev)
+        x.normal_(0.0, cfg.std, generator=torch.Generator(device=dev).manual_seed(n + args.seed))
+        return x.bfloat16()
+
+    kh, vh = normal(Th), normal(Th + 1)[:Th].contiguous()
+    C = B * m
+    qc, kc, vc = normal(C), normal(C + 2)[:C].contiguous(), normal(C + 3)[:C].contiguous()
+    out = torch.empty_like(qc)
+    hist_offs = torch.from_numpy(ho).to(dev)
+    kw = dict(k1=cfg.k1, k2=cfg.k2, contextual_len=cfg.contextual_len,
+              max_seq_len=cfg.max_seq_len)
+    # microbatch j: candidates [j*bm, (j+1)*bm) of every sequence, as views
+    # of one [B][m] candidate layout
+    nmb = (m + bm - 1) // bm
+    views = []
+    for j in range(nmb):
+        n = min(bm, m - j * bm)
+        idx = (torch.arange(B, device=dev)[:, None] * m + j * bm +
+               torch.arange(n, device=dev)[None, :]).reshape(-1)
+        offs = torch.arange(0, B * n + 1, n, dtype=torch.int64, device=dev)
+        views.append((offs, qc[idx].contiguous(), kc[idx].contiguous(), vc[idx].contiguous(),
+                      torch.empty((B * n, H, d), dtype=torch.bfloat16, device=dev)))
+    ws = torch.empty(max(1, sla.workspace_size(sla.make_problem(torch.bfloat16, hist_offs, None,
+                                                                max(Th, B * bm), H, d, d,
+                                                                cfg.k1, cfg.k2,
+                                                                cfg.contextual_len,
+                                                                cfg.max_seq_len),
+                                               sla.SLA_OP_FWD)),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        for offs, q_, k_, v_, o_ in views:
+            sla.sla_fwd_candidates(kh, vh, hist_offs, q_, k_, v_, offs, out=o_, workspace=ws,
+                                   **kw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for _ in range(args.steps):
+        step()
+    ev[1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev[0].elapsed_time(ev[1]) / args.steps
+    K2e = max(cfg.k2, cfg.contextual_len)
+    per_cand = 0
+    for U in hist:
+        w0 = max(0, U - cfg.k1 + 1)
+        per_cand += (U - w0) + min(K2e, w0, U) + 1
+    pairs = per_cand * m * H
+    useful = pairs * 4 * d
+    value = useful / (ms * 1e-3) / 1e12
+    line = {
+        "metric": "M-FALCON candidate scoring useful TFLOP/s and candidates/s (cached history)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"mfalcon: B={B} histories of 16 ctx + U[8192,16384] tokens "
+                        f"(T_hist={Th}), {m} candidates per sequence in microbatches of {bm}, "
+                        f"K1={cfg.k1}, K2={cfg.k2}, H={H}, d={d}, N={cfg.max_seq_len}, "
+                        f"seed {args.seed}",
+            "candidates_per_step": B * m,
+            "calls_per_step": nmb,
+            "visible_pairs_all_heads": pairs,
+            "useful_flop_per_step": useful,
+        },
+        "candidates_per_s": round(B * m / (ms * 1e-3), 1),
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_MFMA_TFLOPS, 2),
         "wall_s_timed_region": round(wall, 4),
     }
     print(json.dumps(line), flush=True)

@@ -34,8 +34,9 @@
  * 0 <= num_targets[b] <= L_b; targets are the last num_targets[b] tokens.
  * These device-resident facts are trusted (checking them needs a sync),
  * unless the environment variable SLA_VALIDATE is set to a value other than
- * "0": then sla_fwd, sla_bwd, sla_bwd_stage, sla_schedule, stu_layer_fwd,
- * stu_layer_bwd and stu_truncate first run a check kernel on the caller's stream, synchronise
+ * "0": then sla_fwd, sla_fwd_candidates (both layouts), sla_bwd,
+ * sla_bwd_stage, sla_schedule, stu_layer_fwd, stu_layer_bwd and stu_truncate
+ * first run a check kernel on the caller's stream, synchronise
  * it, and return SLA_ERR_INVALID (message: which fact, which sequence) before
  * any other kernel when offsets[0] != 0, offsets decrease, offsets[B] !=
  * total_tokens, a num_targets[b] lies outside [0, L_b], or (stu_truncate)
@@ -204,6 +205,34 @@ int64_t sla_schedule_host(const sla_problem_t *p, int op, const int64_t *offsets
 int64_t sla_count_pairs_host(int32_t batch, const int64_t *offsets_host,
                              const int32_t *num_targets_host, int32_t k1, int32_t k2,
                              int32_t contextual_len);
+
+/* Candidate scoring against a cached history (M-FALCON; HSTU notes, section
+ * 2.6; the target rows of the ULTRA-HSTU mask): the history's keys and values
+ * are computed once, and any number of candidates, in microbatches of the
+ * caller's choosing, are scored against them.  p describes the history:
+ * batch B, total_tokens = T_hist, offsets [B+1] of the history tokens, heads,
+ * d, k1, k2, contextual_len, max_seq_len N, alpha; p->num_targets must be
+ * NULL and p->dtype SLA_BF16.  cand_offsets (device int64 [B+1], offsets[0]
+ * = 0, non-decreasing, offsets[B] = total_candidates) lays out the
+ * candidates of each sequence.  Candidate c of sequence b (history length
+ * U_b) gets
+ *   o_c = (1/N) ( sum over history keys j with U_b - j < K1 or j < K2eff of
+ *                 SiLU(alpha q_c . k_j) v_j  +  SiLU(alpha q_c . k_c) v_c ),
+ * i.e. the row of a target placed right after the history.  Candidates never
+ * see each other, and each candidate's sum runs over the same key tiles in
+ * the same order whichever candidates share the call, so scoring them in one
+ * call or in several microbatches gives the same values bit for bit.  k_hist, v_hist: [T_hist][H][d] with
+ * token strides ldk, ldv (not read when T_hist = 0); q_c, k_c, v_c, o_c:
+ * [total_candidates][H][d] with their own strides.  Workspace:
+ * sla_fwd_candidates_workspace_size(p, total_candidates) bytes, 16-byte
+ * aligned.  Conventions and errors as sla_fwd. */
+size_t sla_fwd_candidates_workspace_size(const sla_problem_t *p, int64_t total_candidates);
+sla_status_t sla_fwd_candidates(const sla_problem_t *p, const int64_t *cand_offsets,
+                                int64_t total_candidates, const void *k_hist, int64_t ldk,
+                                const void *v_hist, int64_t ldv, const void *q_c, int64_t ldq,
+                                const void *k_c, int64_t ldkc, const void *v_c, int64_t ldvc,
+                                void *o_c, int64_t ldo, void *workspace, size_t ws_bytes,
+                                void *stream);
 
 /* One STU layer forward, bf16 storage, fp32 accumulation and statistics
  * (ULTRA-HSTU paper, section 3 Eq.1-5; Code Listing 1 order):

@@ -21,7 +21,8 @@ SLA_BWD_ALL, SLA_BWD_PREPARE, SLA_BWD_DKDV, SLA_BWD_DQ = 0, 1, 2, 3
 
 # every symbol include/sla.h declares
 EXPORTS = (
-    "sla_workspace_size", "sla_bwd_dq_mode", "sla_fwd", "sla_bwd", "sla_bwd_stage", "sla_schedule_capacity", "sla_schedule_tile",
+    "sla_workspace_size", "sla_bwd_dq_mode", "sla_fwd", "sla_fwd_candidates_workspace_size",
+    "sla_fwd_candidates", "sla_bwd", "sla_bwd_stage", "sla_schedule_capacity", "sla_schedule_tile",
     "sla_schedule", "sla_schedule_host", "sla_count_pairs_host", "stu_layer_workspace_size", "stu_layer_fwd",
     "stu_layer_bwd_workspace_size", "stu_layer_bwd", "stu_truncate", "sla_status_string", "sla_last_error",
 )
@@ -84,6 +85,11 @@ def load(path: str = LIB_PATH):
         lib.sla_bwd_stage.argtypes = [PP, ctypes.c_int, P, i64, P, i64, P, i64, P, i64, P, i64, P,
                                       i64, P, i64, P, sz, P]
         lib.sla_bwd_stage.restype = ctypes.c_int
+        lib.sla_fwd_candidates_workspace_size.argtypes = [PP, i64]
+        lib.sla_fwd_candidates_workspace_size.restype = sz
+        lib.sla_fwd_candidates.argtypes = [PP, P, i64, P, i64, P, i64, P, i64, P, i64, P, i64, P,
+                                           i64, P, sz, P]
+        lib.sla_fwd_candidates.restype = ctypes.c_int
         lib.sla_schedule_capacity.argtypes = [PP, ctypes.c_int]
         lib.sla_schedule_capacity.restype = i64
         lib.sla_schedule_tile.argtypes = [ctypes.c_int, ctypes.c_int]

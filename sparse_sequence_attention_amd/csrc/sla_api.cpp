@@ -426,6 +426,67 @@ sla_status_t sla_fwd(const sla_problem_t *p, const void *q, int64_t ldq, const v
     return SLA_OK;
 }
 
+size_t sla_fwd_candidates_workspace_size(const sla_problem_t *p, int64_t total_candidates)
+{
+    if (validate_problem(p) != SLA_OK || total_candidates < 0 ||
+        total_candidates >= (int64_t)1 << 30)
+        return 0;
+    sla_problem_t pw = *p;
+    if (total_candidates > pw.total_tokens) pw.total_tokens = total_candidates;
+    return layout(&pw, SLA_OP_FWD).total;
+}
+
+sla_status_t sla_fwd_candidates(const sla_problem_t *p, const int64_t *cand_offsets,
+                                int64_t total_candidates, const void *k_hist, int64_t ldk,
+                                const void *v_hist, int64_t ldv, const void *q_c, int64_t ldq,
+                                const void *k_c, int64_t ldkc, const void *v_c, int64_t ldvc,
+                                void *o_c, int64_t ldo, void *workspace, size_t ws_bytes,
+                                void *stream)
+{
+    sla_status_t st = validate_problem(p);
+    if (st != SLA_OK) return st;
+    if (p->dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "candidate scoring is bf16 only");
+    if (p->num_targets)
+        return fail(SLA_ERR_INVALID, "the history problem has no targets (num_targets must be NULL)");
+    if (total_candidates < 0) return fail(SLA_ERR_INVALID, "negative total_candidates");
+    if (total_candidates >= (int64_t)1 << 30)
+        return fail(SLA_ERR_UNSUPPORTED, "total_candidates too large");
+    if (p->batch > 0 && !cand_offsets) return fail(SLA_ERR_NULL, "cand_offsets is NULL");
+    if (p->batch == 0 || total_candidates == 0) return SLA_OK;  // nothing is read or written
+    sla_problem_t pc = *p;
+    pc.total_tokens = total_candidates;
+    if (p->total_tokens > 0) {
+        if ((st = validate_tensor("k_hist", k_hist, ldk, p, p->d_qk)) != SLA_OK) return st;
+        if ((st = validate_tensor("v_hist", v_hist, ldv, p, p->d_v)) != SLA_OK) return st;
+    }
+    if ((st = validate_tensor("q_c", q_c, ldq, &pc, p->d_qk)) != SLA_OK) return st;
+    if ((st = validate_tensor("k_c", k_c, ldkc, &pc, p->d_qk)) != SLA_OK) return st;
+    if ((st = validate_tensor("v_c", v_c, ldvc, &pc, p->d_v)) != SLA_OK) return st;
+    if ((st = validate_tensor("o_c", o_c, ldo, &pc, p->d_v)) != SLA_OK) return st;
+    sla_problem_t pw = *p;  // workspace and grid bound: the larger row count
+    if (total_candidates > pw.total_tokens) pw.total_tokens = total_candidates;
+    AttnParams a;
+    if ((st = make_params(&pw, SLA_OP_FWD, workspace, ws_bytes, a)) != SLA_OK) return st;
+    if ((st = check_device()) != SLA_OK) return st;
+    a.q = q_c; a.k = k_hist; a.v = v_hist; a.o = o_c; a.kc = k_c; a.vc = v_c;
+    a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.ldo = ldo; a.ldkc = ldkc; a.ldvc = ldvc;
+    a.cand_offsets = cand_offsets;
+    a.num_targets = nullptr;
+    a.absmax_part = nullptr;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = validate_layout(p->batch, p->total_tokens, p->offsets, nullptr, -1, workspace, s)) !=
+        SLA_OK)
+        return st;
+    if ((st = validate_layout(p->batch, total_candidates, cand_offsets, nullptr, -1, workspace,
+                              s)) != SLA_OK)
+        return st;
+    hipError_t e = launch_sched(a, s);
+    if (e != hipSuccess) return hip_fail(e, "schedule kernel");
+    e = launch_fwd_candidates_bf16(a, s);
+    if (e != hipSuccess) return hip_fail(e, "candidate forward kernel");
+    return SLA_OK;
+}
+
 sla_status_t sla_bwd_stage(const sla_problem_t *p, int stage, const void *q, int64_t ldq,
                            const void *k, int64_t ldk, const void *v, int64_t ldv,
                            const void *dout, int64_t lddo, void *dq, int64_t lddq, void *dk,

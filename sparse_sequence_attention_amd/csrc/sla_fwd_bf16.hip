@@ -39,7 +39,16 @@ __device__ __forceinline__ int fswz(int r)
     return 4 * (u % Q4) + (u / Q4) % 4;
 }
 
-template <int D>
+// CAND: candidate scoring against a cached history (p.cand_offsets): the item
+// list holds the candidate row tiles only; sequence b is virtually
+// [history (U keys) | padding up to a multiple of the key tile | candidates],
+// history keys and values come from k, v, the candidates' rows, keys and
+// values from q, kc, vc, and O rows go to the candidate layout.  The padding
+// (never visible) keeps candidate keys out of the history's key tiles, so a
+// candidate's sum runs over the same history tiles in the same order and
+// then its own key, wherever it sits among the candidates: scores do not
+// depend on which other candidates share the call.
+template <int D, bool CAND>
 __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
 {
     constexpr int BM = FWD_BM, BN = FWD_BN;
@@ -62,9 +71,18 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
     const int h = item / nrec;
     const int rec = item - h * nrec;
     const int b = find_seq(p.s.fwd_base, p.B, rec);
-    const SeqDims sd = seq_dims(p.offsets, p.num_targets, b);
+    SeqDims sd = seq_dims(p.offsets, CAND ? nullptr : p.num_targets, b);
+    int64_t cbase = 0;  // first candidate of the sequence (CAND)
+    int uc = sd.U;      // first candidate row of the virtual sequence (CAND)
+    if constexpr (CAND) {
+        cbase = uniform64(p.cand_offsets[b]);
+        const int nc = uniform((int)(p.cand_offsets[b + 1] - cbase));
+        sd.U = sd.L;                // the history length: visibility as a target
+        uc = cdiv(sd.U, BN) * BN;   // candidates start on a key-tile boundary
+        sd.L = uc + nc;
+    }
     int r0, r1;
-    row_tile(sd.L, sd.U, BM, rec - uniform(p.s.fwd_base[b]), r0, r1);
+    row_tile(sd.L, uc, BM, rec - uniform(p.s.fwd_base[b]) + (CAND ? cdiv(uc, BM) : 0), r0, r1);
     r0 = uniform(r0);
     r1 = uniform(r1);
     const Ranges kr = fwd_key_ranges(sd.L, sd.U, p.k1, p.k2e, r0, r1, BN);
@@ -76,11 +94,15 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
     const uint16_t *kg = reinterpret_cast<const uint16_t *>(p.k) + sd.base * p.ldk + h * D;
     const uint16_t *vg = reinterpret_cast<const uint16_t *>(p.v) + sd.base * p.ldv + h * D;
 
-    // Q^T operand: lane holds row qi, d-slots 16c + 8*hl .. +8
+    // Q^T operand: lane holds row qi, d-slots 16c + 8*hl .. +8 (CAND: the
+    // candidate rows, qi - U of the sequence's candidates)
     const int qi = r0 + 32 * wv + l32;
+    const uint16_t *qsrc = CAND ? reinterpret_cast<const uint16_t *>(p.q) + cbase * p.ldq + h * D
+                                : qg;
+    const int qrow = CAND ? qi - uc : qi, qlim = CAND ? sd.L - uc : sd.L;
     bf16x8 qb[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qb[c] = as_bf16x8(ld16_row(qg, p.ldq, qi, sd.L, 16 * c + 8 * hl));
+    for (int c = 0; c < NC; ++c) qb[c] = as_bf16x8(ld16_row(qsrc, p.ldq, qrow, qlim, 16 * c + 8 * hl));
 
     const TileCursor cur(kr, BN);
     const int ntiles = uniform(cur.total);
@@ -98,11 +120,33 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
     // logical chunk (P % CPR) ^ fswz(row); keys at or past L read key L - 1
     // (such tiles are never "full", and the mask removes them)
     const uint32_t ldk_b = (uint32_t)p.ldk * 2u, ldv_b = (uint32_t)p.ldv * 2u;
+    // CAND: keys at or past the history length are the candidates' own
+    const char *kcg = nullptr, *vcg = nullptr;
+    if constexpr (CAND) {
+        kcg = reinterpret_cast<const char *>(reinterpret_cast<const uint16_t *>(p.kc) +
+                                             cbase * p.ldkc + h * D);
+        vcg = reinterpret_cast<const char *>(reinterpret_cast<const uint16_t *>(p.vc) +
+                                             cbase * p.ldvc + h * D);
+    }
     auto issue = [&](int t, auto S) {
         const int c0 = uniform(cur.start(t, BN));
-        const int last = uniform(sd.L - 1 - c0);
+        int last = uniform(sd.L - 1 - c0);
         const char *krow = reinterpret_cast<const char *>(kg + (int64_t)c0 * p.ldk);
         const char *vrow = reinterpret_cast<const char *>(vg + (int64_t)c0 * p.ldv);
+        uint32_t lk = ldk_b, lv = ldv_b;
+        if constexpr (CAND) {
+            // a key tile lies wholly below uc (history, whose padding keys
+            // U <= j < uc, never visible, read history key U - 1) or wholly
+            // in the candidates
+            if (c0 >= uc) {
+                krow = kcg + (int64_t)(c0 - uc) * p.ldkc * 2;
+                vrow = vcg + (int64_t)(c0 - uc) * p.ldvc * 2;
+                lk = (uint32_t)p.ldkc * 2u;
+                lv = (uint32_t)p.ldvc * 2u;
+            } else {
+                last = uniform(sd.U - 1 - c0);
+            }
+        }
         uint16_t *sb = stage(S);
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
@@ -110,8 +154,8 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
             const int prow = P / CPR;
             const uint32_t row = (uint32_t)imin(prow, last);
             const uint32_t c = (uint32_t)((P % CPR) ^ fswz<D>(prow));
-            gl_lds16(krow + (row * ldk_b + 16u * c), sb + (i * NT + wv * 64) * 8);
-            gl_lds16(vrow + (row * ldv_b + 16u * c), sb + (TCH + i * NT + wv * 64) * 8);
+            gl_lds16(krow + (row * lk + 16u * c), sb + (i * NT + wv * 64) * 8);
+            gl_lds16(vrow + (row * lv + 16u * c), sb + (TCH + i * NT + wv * 64) * 8);
         }
     };
     // this thread's V chunks of a stage, bf16 -> fp16 in place
@@ -157,8 +201,13 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
         // c = 32*kb + 8*(r/4) + r%4: a history row sees key j iff x >= 0 and
         // (x < K1 or j < K2e); keys past L give x < 0.  Tiles wholly inside
         // or outside the global prefix need one interval test per element.
-        const bool full = uniform((r0 < sd.U) && (c0 + BN <= sd.L) && (c0 + BN - 1 <= r0) &&
-                                  ((r1 - 1 - c0 < p.k1) || (c0 + BN <= p.k2e))) != 0;
+        // Target rows see the same history keys (those of the first target
+        // slot), so a history tile wholly inside that view needs no mask
+        // either; the diagonal and boundary tiles do.
+        const bool full = uniform(((r0 < sd.U) && (c0 + BN <= sd.L) && (c0 + BN - 1 <= r0) &&
+                                   ((r1 - 1 - c0 < p.k1) || (c0 + BN <= p.k2e))) ||
+                                  ((r0 >= sd.U) && (c0 + BN <= sd.U) &&
+                                   ((c0 >= sd.U - p.k1 + 1) || (c0 + BN <= p.k2e)))) != 0;
         const int x0 = qi - c0 - 4 * hl;
         const int mode = uniform(r0 >= sd.U ? 0 : (c0 >= p.k2e ? 1 : (c0 + BN <= p.k2e ? 2 : 0)));
 
@@ -231,7 +280,8 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
 
     // epilogue: O[qi][d] for d = 32*db + 8*g + 4*hl + 0..3
     if (qi < r1) {
-        uint16_t *orow = reinterpret_cast<uint16_t *>(p.o) + (sd.base + qi) * p.ldo + h * D;
+        const int64_t orow_i = CAND ? cbase + (qi - uc) : sd.base + qi;
+        uint16_t *orow = reinterpret_cast<uint16_t *>(p.o) + orow_i * p.ldo + h * D;
         const float sc = p.out_scale;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
@@ -245,16 +295,25 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
     }
 }
 
-hipError_t launch_fwd_bf16(const AttnParams &p, hipStream_t st)
+template <bool CAND>
+static hipError_t launch_fwd(const AttnParams &p, hipStream_t st)
 {
     dim3 grid(p.grid_fwd), block(256);
     switch (p.d) {
-    case 32: hipLaunchKernelGGL(sla_fwd_bf16_kernel<32>, grid, block, 0, st, p); break;
-    case 64: hipLaunchKernelGGL(sla_fwd_bf16_kernel<64>, grid, block, 0, st, p); break;
-    case 128: hipLaunchKernelGGL(sla_fwd_bf16_kernel<128>, grid, block, 0, st, p); break;
+    case 32: hipLaunchKernelGGL((sla_fwd_bf16_kernel<32, CAND>), grid, block, 0, st, p); break;
+    case 64: hipLaunchKernelGGL((sla_fwd_bf16_kernel<64, CAND>), grid, block, 0, st, p); break;
+    case 128: hipLaunchKernelGGL((sla_fwd_bf16_kernel<128, CAND>), grid, block, 0, st, p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16(const AttnParams &p, hipStream_t st) { return launch_fwd<false>(p, st); }
+
+hipError_t launch_fwd_candidates_bf16(const AttnParams &p, hipStream_t st)
+{
+    if (!p.cand_offsets) return hipErrorInvalidValue;
+    return launch_fwd<true>(p, st);
 }
 
 }  // namespace sla

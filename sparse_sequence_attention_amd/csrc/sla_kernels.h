@@ -40,6 +40,13 @@ struct AttnParams {
     int64_t ds_discard;     // block index of the discard block
     int ds_slots;           // slots per (row tile, head)
     int grid_rt;            // upper bound of 64-row tiles (x heads)
+    // candidate scoring against a cached history (null: the ordinary forward).
+    // Sequence b is then the history offsets[b] .. offsets[b+1] (keys k, v)
+    // followed by the candidates cand_offsets[b] .. cand_offsets[b+1] (rows
+    // q, o; their own keys kc, vc); only the candidate rows are computed.
+    const int64_t *cand_offsets;
+    const void *kc, *vc;
+    int64_t ldkc, ldvc;
 };
 
 constexpr int ABSMAX_BLOCKS = 1024;
@@ -53,6 +60,8 @@ struct WsLayout {
 };
 
 hipError_t launch_sched(const AttnParams &p, hipStream_t st);
+// forward over candidate rows only (p.cand_offsets set), bf16
+hipError_t launch_fwd_candidates_bf16(const AttnParams &p, hipStream_t st);
 // Optional check of the jagged layout; result: int32[2] device scratch
 // (code, sequence).  ctx < 0 skips the truncation check.
 hipError_t launch_validate(const int64_t *offsets, const int32_t *num_targets, int B, int64_t T,

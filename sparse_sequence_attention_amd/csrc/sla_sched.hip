@@ -17,7 +17,8 @@ __global__ __launch_bounds__(SCHED_THREADS) void sla_sched_kernel(const int64_t 
                                                                   int B, int k2e, Sched s,
                                                                   const float *absmax_part,
                                                                   float *grad_scale,
-                                                                  uint4 *zero_block)
+                                                                  uint4 *zero_block,
+                                                                  const int64_t *cand_offsets)
 {
     // the stored-dS zero block (DS_BM x DS_BN fp16 = 1024 x 16 bytes)
     if (zero_block != nullptr)
@@ -58,7 +59,11 @@ __global__ __launch_bounds__(SCHED_THREADS) void sla_sched_kernel(const int64_t 
         const int b = start + tid;
         int4 v = make_int4(0, 0, 0, 0);
         int v2 = 0;
-        if (b < B) {
+        if (b < B && cand_offsets) {
+            // candidate scoring: forward row tiles over the candidates only
+            v.x = cdiv((int)(cand_offsets[b + 1] - cand_offsets[b]), FWD_BM);
+            s.nch[b] = 1;
+        } else if (b < B) {
             SeqDims sd = seq_dims<false>(offsets, num_targets, b);
             int np, nch;
             v.x = row_tiles(sd.L, sd.U, FWD_BM);
@@ -118,7 +123,7 @@ hipError_t launch_sched(const AttnParams &p, hipStream_t st)
 {
     hipLaunchKernelGGL(sla_sched_kernel, dim3(1), dim3(SCHED_THREADS), 0, st, p.offsets,
                        p.num_targets, p.B, p.k2e, p.s, (const float *)p.absmax_part,
-                       p.grad_scale, reinterpret_cast<uint4 *>(p.ds));
+                       p.grad_scale, reinterpret_cast<uint4 *>(p.ds), p.cand_offsets);
     return hipGetLastError();
 }
 

@@ -31,6 +31,8 @@ def _head_tensor(name: str, t: torch.Tensor, T: int, H: int, dtype) -> int:
         raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
+    if T == 0:
+        return H * t.shape[2]  # no rows: nothing is read or written
     if t.stride(2) != 1 or (H > 1 and t.stride(1) != t.shape[2]):
         raise ValueError(f"{name}: heads must be packed ([T][H][d] with token stride >= H*d)")
     return t.stride(0)
@@ -92,6 +94,39 @@ def sla_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, offsets: torch.Te
     ws = _workspace(nbytes, q.device, workspace)
     C.check(C.load().sla_fwd(ctypes.byref(p), _ptr(q), ldq, _ptr(k), ldk, _ptr(v), ldv, _ptr(out),
                              ldo, _ptr(ws), ws.numel(), _stream(q.device)))
+    return out
+
+
+def sla_fwd_candidates(k_hist: torch.Tensor, v_hist: torch.Tensor, hist_offsets: torch.Tensor,
+                       q_c: torch.Tensor, k_c: torch.Tensor, v_c: torch.Tensor,
+                       cand_offsets: torch.Tensor, *, k1: int, k2: int, contextual_len: int = 0,
+                       max_seq_len: int, alpha: float = 1.0, out: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """O_c[C, H, d_v]: candidates scored against the cached history keys/values
+    (each sees the history window of the first candidate slot and itself)."""
+    Th, H, dqk = k_hist.shape
+    Cn = q_c.shape[0]
+    dv = v_c.shape[2]
+    dt = q_c.dtype
+    ldk = _head_tensor("k_hist", k_hist, Th, H, dt)
+    ldv = _head_tensor("v_hist", v_hist, Th, H, dt)
+    ldq = _head_tensor("q_c", q_c, Cn, H, dt)
+    ldkc = _head_tensor("k_c", k_c, Cn, H, dt)
+    ldvc = _head_tensor("v_c", v_c, Cn, H, dt)
+    if out is None:
+        out = torch.empty((Cn, H, dv), dtype=dt, device=q_c.device)
+    ldo = _head_tensor("out", out, Cn, H, dt)
+    if cand_offsets.dtype != torch.int64 or cand_offsets.numel() != hist_offsets.numel():
+        raise TypeError("cand_offsets must be an int64 tensor [B+1] like hist_offsets")
+    p = make_problem(dt, hist_offsets, None, Th, H, dqk, dv, k1, k2, contextual_len, max_seq_len,
+                     alpha)
+    lib = C.load()
+    nbytes = int(lib.sla_fwd_candidates_workspace_size(ctypes.byref(p), Cn))
+    ws = _workspace(nbytes, q_c.device, workspace)
+    C.check(lib.sla_fwd_candidates(ctypes.byref(p), _ptr(cand_offsets), Cn, _ptr(k_hist), ldk,
+                                   _ptr(v_hist), ldv, _ptr(q_c), ldq, _ptr(k_c), ldkc, _ptr(v_c),
+                                   ldvc, _ptr(out), ldo, _ptr(ws), ws.numel(),
+                                   _stream(q_c.device)))
     return out
 
 
