@@ -21,6 +21,10 @@ Functions whose results are "parity pinned" and the pins (tests/test_oracle_*):
   sla_fwd_candidates -- dense fp64 torch reference and sla_fwd's target rows
       on the combined [history | candidates] layout; microbatch invariance;
       candidates do not see each other.
+  round_e4m3 / quant_rows_fp8 -- torch's float32 -> float8_e4m3fn conversion;
+      the row maximum maps to 448; scale * q reconstructs within half an ulp.
+  stu_layer_fwd_fp8 -- a torch fp64 composition that quantises with torch's
+      float8_e4m3fn conversion; FP8 error against the bf16 layer.
   truncate  -- direct set construction, identity when tail >= history.
 """
 from __future__ import annotations
@@ -89,6 +93,13 @@ def _load():
         lib.oracle_stu_layer_bwd.argtypes = [i32, P, P, i32, i32, i32, i32, i64, i64, i64,
                                              dbl, dbl, dbl] + [P] * 10 + [i32] + [P] * 9
         lib.oracle_stu_layer_bwd.restype = None
+        lib.oracle_round_e4m3.argtypes = [dbl]
+        lib.oracle_round_e4m3.restype = dbl
+        lib.oracle_quant_rows_fp8.argtypes = [i64, i64, P, P, P]
+        lib.oracle_quant_rows_fp8.restype = None
+        lib.oracle_stu_layer_fwd_fp8.argtypes = [i32, P, P, i32, i32, i32, i32, i64, i64, i64,
+                                                 dbl, dbl, dbl] + [P] * 11
+        lib.oracle_stu_layer_fwd_fp8.restype = None
         lib.oracle_truncate.argtypes = [i32, P, P, i64, i64, P, P]
         lib.oracle_truncate.restype = i64
         lib.oracle_num_threads.argtypes = []
@@ -252,6 +263,41 @@ def stu_layer_bwd(x, offsets, num_targets, ln1_w, w_uvqk, ln2_w, w_out, dout, *,
                                                          "db_uvqk", "dln2_w", "dln2_b",
                                                          "dw_out", "db_out")])
     return g
+
+
+def round_e4m3(x) -> np.ndarray:
+    """Nearest FP8 E4M3 (e4m3fn) values, ties to even, saturating at +-448."""
+    f = _load().oracle_round_e4m3
+    return np.vectorize(lambda v: f(float(v)), otypes=[np.float64])(np.asarray(x, np.float64))
+
+
+def quant_rows_fp8(x) -> Tuple[np.ndarray, np.ndarray]:
+    """(q [R, C] e4m3 values, scale [R]) with x ~ q * scale[:, None]."""
+    x = _f64(x)
+    R, Cn = x.shape
+    q = np.zeros_like(x)
+    sc = np.zeros(R)
+    _load().oracle_quant_rows_fp8(R, Cn, _ptr(x), _ptr(q), _ptr(sc))
+    return q, sc
+
+
+def stu_layer_fwd_fp8(x, offsets, num_targets, ln1_w, w_uvqk, ln2_w, w_out, *, heads, dqk, dv,
+                      k1, k2, ctx, N, alpha=1.0, eps=1e-5, ln1_b=None, b_uvqk=None, ln2_b=None,
+                      b_out=None, want_uvqk=False):
+    """The STU layer with both projections in FP8 (row-wise quantised n, y and
+    weights; bf16 storage elsewhere).  Returns out [T, D] (and uvqk)."""
+    x = _f64(x)
+    T, D = x.shape
+    nw = 2 * heads * dv + 2 * heads * dqk
+    out = np.zeros_like(x)
+    uvqk = np.zeros((T, nw)) if want_uvqk else None
+    offs, tg = _offs(offsets), _tg(num_targets)
+    keep = [_f64(a) if a is not None else None
+            for a in (ln1_w, ln1_b, w_uvqk, b_uvqk, ln2_w, ln2_b, w_out, b_out)]
+    _load().oracle_stu_layer_fwd_fp8(len(offs) - 1, _ptr(offs), _ptr(tg), D, heads, dqk, dv, k1,
+                                     k2, ctx, float(N), float(alpha), float(eps), _ptr(x),
+                                     *[_ptr(a) for a in keep], _ptr(out), _ptr(uvqk))
+    return (out, uvqk) if want_uvqk else out
 
 
 def _store_mask(store_bf16) -> int:

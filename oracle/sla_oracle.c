@@ -338,6 +338,45 @@ static void round_all(double *a, int64_t n)
     for (int64_t i = 0; i < n; ++i) a[i] = oracle_round_bf16(a[i]);
 }
 
+/* Round x to the nearest FP8 E4M3 value (OCP "e4m3fn": 3 mantissa bits,
+ * exponent bias 7, largest finite 448, subnormal spacing 2^-9), ties to even;
+ * magnitudes past 448 saturate to +-448. */
+EXPORT double oracle_round_e4m3(double x)
+{
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e;
+    frexp(x, &e);          /* |x| in [2^(e-1), 2^e) */
+    int qexp = e - 4;      /* 3 bits below the leading one */
+    if (qexp < -9) qexp = -9;
+    double y = ldexp(nearbyint(ldexp(x, -qexp)), qexp);
+    if (y > 448.0) y = 448.0;
+    if (y < -448.0) y = -448.0;
+    return y;
+}
+
+/* Row-wise FP8 quantisation (ULTRA-HSTU paper, section 4.2.2, mixed
+ * precision: a scale per row, computed and applied where the row is
+ * produced): with a = max |x[r][:]|, the row is stored as
+ * q = e4m3(x * (448 / a)) and the scale s = a / 448, so x ~ q * s.  An
+ * all-zero row has s = 1 and q = 0.  q holds the e4m3 values (as doubles). */
+EXPORT void oracle_quant_rows_fp8(int64_t rows, int64_t cols, const double *x, double *q,
+                                  double *scale)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *xr = x + r * cols;
+        double a = 0.0;
+        for (int64_t c = 0; c < cols; ++c) a = fmax(a, fabs(xr[c]));
+        if (a == 0.0) {
+            scale[r] = 1.0;
+            for (int64_t c = 0; c < cols; ++c) q[r * cols + c] = 0.0;
+            continue;
+        }
+        const double inv = 448.0 / a;
+        scale[r] = a / 448.0;
+        for (int64_t c = 0; c < cols; ++c) q[r * cols + c] = oracle_round_e4m3(xr[c] * inv);
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* LayerNorm and the STU layer                                               */
 /* ------------------------------------------------------------------------ */
@@ -427,6 +466,74 @@ EXPORT void oracle_stu_layer_fwd(int B, const int64_t *offsets, const int32_t *n
     if (ro) round_all(out, T * D);
 
     free(n); free(z); free(qq); free(kk); free(vv); free(uu); free(a); free(y);
+}
+
+/* One STU layer forward with both projections in FP8 (ULTRA-HSTU paper,
+ * section 4.2.2, mixed precision; everything else as oracle_stu_layer_fwd in
+ * its bf16-storage mode): the normalised input n and the gated output y are
+ * quantised row-wise where they are produced, the weights row-wise (one scale
+ * per output feature), and each projection is the exact product of the
+ * quantised operands times the two scales:
+ *   z[t][o]   = sn[t] sw1[o] sum_c nq[t][c] w1q[o][c] + b1[o]
+ *   out[t][o] = sy[t] sw2[o] sum_c yq[t][c] w2q[o][c] + b2[o] + x[t][o]
+ * U/V/Q/K, A and out are rounded to bf16 (stored tensors); n and y are not
+ * (they go straight into the quantiser). */
+EXPORT void oracle_stu_layer_fwd_fp8(int B, const int64_t *offsets, const int32_t *num_targets,
+                                     int D, int H, int dqk, int dv, int64_t k1, int64_t k2,
+                                     int64_t ctx, double N, double alpha, double eps,
+                                     const double *x, const double *ln1_w, const double *ln1_b,
+                                     const double *w1, const double *b1, const double *ln2_w,
+                                     const double *ln2_b, const double *w2, const double *b2,
+                                     double *out, double *uvqk_out)
+{
+    const int64_t T = offsets[B];
+    const int64_t NU = (int64_t)H * dv, NQ = (int64_t)H * dqk, NW = 2 * NU + 2 * NQ;
+    double *n = malloc(sizeof(double) * T * D), *nq = malloc(sizeof(double) * T * D);
+    double *sn = malloc(sizeof(double) * T), *sy = malloc(sizeof(double) * T);
+    double *w1q = malloc(sizeof(double) * NW * D), *sw1 = malloc(sizeof(double) * NW);
+    double *w2q = malloc(sizeof(double) * D * NU), *sw2 = malloc(sizeof(double) * D);
+    double *z = malloc(sizeof(double) * T * NW);
+    double *qq = malloc(sizeof(double) * T * NQ), *kk = malloc(sizeof(double) * T * NQ);
+    double *vv = malloc(sizeof(double) * T * NU), *uu = malloc(sizeof(double) * T * NU);
+    double *a = malloc(sizeof(double) * T * NU), *y = malloc(sizeof(double) * T * NU);
+    double *yq = malloc(sizeof(double) * T * NU);
+
+    oracle_quant_rows_fp8(NW, D, w1, w1q, sw1);
+    oracle_quant_rows_fp8(D, NU, w2, w2q, sw2);
+    oracle_layernorm(T, D, x, ln1_w, ln1_b, eps, n);
+    oracle_quant_rows_fp8(T, D, n, nq, sn);
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t o = 0; o < NW; ++o) {
+            double acc = 0.0;
+            for (int64_t c = 0; c < D; ++c) acc += nq[t * D + c] * w1q[o * D + c];
+            const double zz = sn[t] * sw1[o] * acc + (b1 ? b1[o] : 0.0);
+            z[t * NW + o] = oracle_round_bf16(silu(zz));
+        }
+    if (uvqk_out) memcpy(uvqk_out, z, sizeof(double) * T * NW);
+    for (int64_t t = 0; t < T; ++t) {
+        const double *zr = z + t * NW;
+        memcpy(uu + t * NU, zr, sizeof(double) * NU);
+        memcpy(vv + t * NU, zr + NU, sizeof(double) * NU);
+        memcpy(qq + t * NQ, zr + 2 * NU, sizeof(double) * NQ);
+        memcpy(kk + t * NQ, zr + 2 * NU + NQ, sizeof(double) * NQ);
+    }
+    oracle_sla_fwd(B, offsets, num_targets, H, dqk, dv, k1, k2, ctx, N, alpha, qq, kk, vv, a,
+                   NULL);
+    round_all(a, T * NU);
+    oracle_layernorm(T, NU, a, ln2_w, ln2_b, eps, y);
+    for (int64_t i = 0; i < T * NU; ++i) y[i] *= uu[i];
+    oracle_quant_rows_fp8(T, NU, y, yq, sy);
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t o = 0; o < D; ++o) {
+            double acc = 0.0;
+            for (int64_t c = 0; c < NU; ++c) acc += yq[t * NU + c] * w2q[o * NU + c];
+            out[t * D + o] =
+                oracle_round_bf16(sy[t] * sw2[o] * acc + (b2 ? b2[o] : 0.0) + x[t * D + o]);
+        }
+    free(n); free(nq); free(sn); free(sy); free(w1q); free(sw1); free(w2q); free(sw2); free(z);
+    free(qq); free(kk); free(vv); free(uu); free(a); free(y); free(yq);
 }
 
 /* Row statistics of LayerNorm: xh = (x - mean) * rstd, rstd = 1/sqrt(var + eps)
