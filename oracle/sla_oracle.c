@@ -358,22 +358,28 @@ EXPORT double oracle_round_e4m3(double x)
  * precision: a scale per row, computed and applied where the row is
  * produced): with a = max |x[r][:]|, the row is stored as
  * q = e4m3(x * (448 / a)) and the scale s = a / 448, so x ~ q * s.  An
- * all-zero row has s = 1 and q = 0.  q holds the e4m3 values (as doubles). */
+ * all-zero row has s = 1 and q = 0.  q holds the e4m3 values (as doubles).
+ * The code q is an integer decided by floating point, so it is decided in
+ * the precision the kernels use: x is taken as an fp32 value, and 448 / a,
+ * the product and a / 448 are single IEEE fp32 operations. */
 EXPORT void oracle_quant_rows_fp8(int64_t rows, int64_t cols, const double *x, double *q,
                                   double *scale)
 {
     for (int64_t r = 0; r < rows; ++r) {
         const double *xr = x + r * cols;
-        double a = 0.0;
-        for (int64_t c = 0; c < cols; ++c) a = fmax(a, fabs(xr[c]));
-        if (a == 0.0) {
+        float a = 0.0f;
+        for (int64_t c = 0; c < cols; ++c) a = fmaxf(a, fabsf((float)xr[c]));
+        if (a == 0.0f) {
             scale[r] = 1.0;
             for (int64_t c = 0; c < cols; ++c) q[r * cols + c] = 0.0;
             continue;
         }
-        const double inv = 448.0 / a;
-        scale[r] = a / 448.0;
-        for (int64_t c = 0; c < cols; ++c) q[r * cols + c] = oracle_round_e4m3(xr[c] * inv);
+        const float inv = 448.0f / a;
+        scale[r] = (double)(a / 448.0f);
+        for (int64_t c = 0; c < cols; ++c) {
+            const float p = (float)xr[c] * inv;
+            q[r * cols + c] = oracle_round_e4m3((double)p);
+        }
     }
 }
 
