@@ -38,10 +38,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--workload", choices=(WORKLOAD, "stu_layer", "mfalcon"), default=WORKLOAD,
+    ap.add_argument("--workload", choices=(WORKLOAD, "stu_layer", "stu_stack", "mfalcon"),
+                    default=WORKLOAD,
                     help="long_16k: the SLA forward + backward (default); stu_layer: one full "
-                         "STU layer forward + backward at the 18-layer stack's shape; mfalcon: "
-                         "candidate scoring against cached history keys/values")
+                         "STU layer forward + backward at the 18-layer stack's shape; "
+                         "stu_stack: the 18-layer STU stack forward; mfalcon: candidate "
+                         "scoring against cached history keys/values")
+    ap.add_argument("--fp8", action="store_true",
+                    help="stu_stack: both projections of every layer in FP8")
     ap.add_argument("--candidates", type=int, default=4096,
                     help="mfalcon: candidates per sequence")
     ap.add_argument("--microbatch", type=int, default=1024,
@@ -118,6 +122,9 @@ def main():
         return
     if args.workload == "mfalcon":
         bench_mfalcon(args)
+        return
+    if args.workload == "stu_stack":
+        bench_stu_stack(args)
         return
     import torch
     import sparse_sequence_attention_amd as sla
@@ -325,6 +332,95 @@ def bench_stu_layer(args):
         "phase_ms": {"fwd": round(fwd, 4), "bwd": round(bwd, 4)},
         "phase_tflops": {"fwd": round(useful_fwd / (fwd * 1e-3) / 1e12, 2),
                          "bwd": round(useful_bwd / (bwd * 1e-3) / 1e12, 2)},
+        "wall_s_timed_region": round(wall, 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_stu_stack(args):
+    """The 18-layer STU stack forward (B = 8, L_b ~ U[2048, 4096], 64 targets,
+    contextual 16, hidden 512, H = 4, d = 128, K1 = 512, K2 = 64, N = 4096;
+    attention truncation before layer 9 keeps contextual 16 + the last 1024
+    history tokens + the targets), random Xavier-uniform weights, bf16 or (with
+    --fp8) FP8 projections.  A step is the whole stack, truncation included.
+    Useful FLOPs per layer: 2 T_l D NW + 2 T_l NU D for the projections and
+    512 per visible (row, key) pair and head for the attention."""
+    import torch
+    import sparse_sequence_attention_amd as sla
+    from sparse_sequence_attention_amd.config import STUConfig
+    from sparse_sequence_attention_amd.stack import STULayerWeights, stu_stack_fwd
+    from synthetic import make_stack_workload
+
+    sw = make_stack_workload(seed=args.seed)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cfg = STUConfig(embedding_dim=sw.hidden, num_heads=sw.heads, hidden_dim=sw.d,
+                    attention_dim=sw.d, sla_k1=sw.k1, sla_k2=sw.k2,
+                    contextual_seq_len=sw.contextual_len, attn_num_layers=sw.layers,
+                    attn_truncation_split_layer=sw.split_layer,
+                    attn_truncation_tail_len=sw.tail_len, max_seq_len=sw.max_seq_len)
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)  # noqa: E731
+    layers = [STULayerWeights(ln1_w=f(sw.ln1_w[i]), w_uvqk=f(sw.w_uvqk[i]).bfloat16(),
+                              ln2_w=f(sw.ln2_w[i]), w_out=f(sw.w_out[i]).bfloat16())
+              for i in range(sw.layers)]
+    if args.fp8:
+        for w in layers:
+            w.quantize_fp8()
+    x = f(sw.x).bfloat16()
+    offs = torch.from_numpy(sw.offsets).to(dev)
+    tg = torch.from_numpy(sw.num_targets).to(dev)
+
+    def step():
+        return stu_stack_fwd(cfg, layers, x, offs, tg, fp8=args.fp8)
+
+    for _ in range(args.warmup):
+        res = step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for _ in range(args.steps):
+        res = step()
+    ev[1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev[0].elapsed_time(ev[1]) / args.steps
+    H, d, D = sw.heads, sw.d, sw.hidden
+    NU, NW = H * d, 4 * H * d
+    full_pairs = sla.count_pairs_host(sw.offsets, sw.num_targets, sw.k1, sw.k2,
+                                      sw.contextual_len) * H
+    t_offs = res.offsets.cpu().numpy()
+    t_tg = res.num_targets.cpu().numpy() if res.num_targets is not None else None
+    trunc_pairs = sla.count_pairs_host(t_offs, t_tg, sw.k1, sw.k2, sw.contextual_len) * H
+    useful = 0
+    for li, T_l in enumerate(res.layer_tokens):
+        pairs = full_pairs if li < sw.split_layer else trunc_pairs
+        useful += 2 * T_l * D * NW + 2 * T_l * NU * D + pairs * 4 * d
+    value = useful / (ms * 1e-3) / 1e12
+    line = {
+        "metric": "STU stack forward useful TFLOP/s (18 layers, truncation after layer 9)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8+bf16" if args.fp8 else "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"stu_stack: 18 layers, B=8, L_b ~ U[2048, 4096] (T={sw.offsets[-1]}), "
+                        f"64 targets, ctx 16, D={D}, H={H}, d={d}, K1={sw.k1}, K2={sw.k2}, "
+                        f"N={sw.max_seq_len}, truncation before layer {sw.split_layer} to "
+                        f"ctx + {sw.tail_len} + targets, "
+                        f"{'FP8' if args.fp8 else 'bf16'} projections, seed {args.seed}",
+            "layer_tokens": res.layer_tokens,
+            "useful_flop_per_step": useful,
+        },
+        "tokens_per_s": round(int(sw.offsets[-1]) / (ms * 1e-3), 1),
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_MFMA_TFLOPS, 2),
         "wall_s_timed_region": round(wall, 4),
     }
     print(json.dumps(line), flush=True)

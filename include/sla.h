@@ -35,8 +35,8 @@
  * These device-resident facts are trusted (checking them needs a sync),
  * unless the environment variable SLA_VALIDATE is set to a value other than
  * "0": then sla_fwd, sla_fwd_candidates (both layouts), sla_bwd,
- * sla_bwd_stage, sla_schedule, stu_layer_fwd, stu_layer_bwd and stu_truncate
- * first run a check kernel on the caller's stream, synchronise
+ * sla_bwd_stage, sla_schedule, stu_layer_fwd, stu_layer_fwd_fp8, stu_layer_bwd
+ * and stu_truncate first run a check kernel on the caller's stream, synchronise
  * it, and return SLA_ERR_INVALID (message: which fact, which sequence) before
  * any other kernel when offsets[0] != 0, offsets decrease, offsets[B] !=
  * total_tokens, a num_targets[b] lies outside [0, L_b], or (stu_truncate)
@@ -292,6 +292,39 @@ sla_status_t stu_layer_bwd(const stu_layer_desc_t *d, const void *x, const void 
                            float *dln1_w, float *dln1_b, float *dw_uvqk, float *db_uvqk,
                            float *dln2_w, float *dln2_b, float *dw_out, float *db_out,
                            void *workspace, size_t ws_bytes, void *stream);
+
+/* FP8 projections (ULTRA-HSTU paper, section 4.2.2, mixed precision: both
+ * STU GEMMs in FP8, everything else bf16; row-wise scaling and quantisation
+ * fused into the LayerNorm in front of each GEMM; the post-attention GEMM
+ * adds the 2-D residual in its epilogue).  Format FP8 E4M3 (OCP e4m3fn,
+ * largest finite 448), one scale per row: row x is stored as
+ * q = e4m3(x * 448 / max|x|) (round to nearest even) with scale
+ * max|x| / 448, so x ~ q * scale; an all-zero row has q = 0, scale = 1.
+ *
+ * stu_quantize_rows_fp8: x bf16 [rows][cols] (contiguous; cols a multiple of
+ * 16, at most 2048) -> q [rows][cols] e4m3 bytes, scale fp32 [rows].  Used
+ * once per weight matrix (rows = output features): w_uvqk [NW][D] and
+ * w_out [D][H*d_v] as stu_layer_fwd takes them.
+ *
+ * stu_layer_fwd_fp8: stu_layer_fwd with the quantised weights (w_*_q e4m3,
+ * w_*_scale fp32 per output feature):
+ *   n  = LayerNorm(x) quantised row-wise (never stored in bf16)
+ *   uvqk = SiLU(sn[t] sw1[o] (nq . w1q[o]) (+ b_uvqk[o]))      bf16
+ *   A  = SLA(Q, K, V)                                          bf16
+ *   y  = (LayerNorm(A) * ln2_w (+ ln2_b)) (.) U quantised row-wise
+ *   out = sy[t] sw2[o] (yq . w2q[o]) (+ b_out[o]) + x          bf16
+ * Other arguments, outputs and limits as stu_layer_fwd, plus H*d_v a multiple
+ * of 128.  Workspace: stu_layer_fp8_workspace_size(d) bytes. */
+sla_status_t stu_quantize_rows_fp8(const void *x, int64_t rows, int32_t cols, void *q,
+                                   float *scale, void *stream);
+size_t stu_layer_fp8_workspace_size(const stu_layer_desc_t *d);
+sla_status_t stu_layer_fwd_fp8(const stu_layer_desc_t *d, const void *x, const float *ln1_w,
+                               const float *ln1_b, const void *w_uvqk_q,
+                               const float *w_uvqk_scale, const float *b_uvqk,
+                               const float *ln2_w, const float *ln2_b, const void *w_out_q,
+                               const float *w_out_scale, const float *b_out, void *out,
+                               void *uvqk_out, void *attn_out, void *workspace, size_t ws_bytes,
+                               void *stream);
 
 /* Attention truncation (ULTRA-HSTU paper, section 4.3; torcheasyrec page,
  * truncation bullet): per sequence keep, in order, the contextual prefix

@@ -24,7 +24,8 @@ EXPORTS = (
     "sla_workspace_size", "sla_bwd_dq_mode", "sla_fwd", "sla_fwd_candidates_workspace_size",
     "sla_fwd_candidates", "sla_bwd", "sla_bwd_stage", "sla_schedule_capacity", "sla_schedule_tile",
     "sla_schedule", "sla_schedule_host", "sla_count_pairs_host", "stu_layer_workspace_size", "stu_layer_fwd",
-    "stu_layer_bwd_workspace_size", "stu_layer_bwd", "stu_truncate", "sla_status_string", "sla_last_error",
+    "stu_layer_bwd_workspace_size", "stu_layer_bwd", "stu_quantize_rows_fp8",
+    "stu_layer_fp8_workspace_size", "stu_layer_fwd_fp8", "stu_truncate", "sla_status_string", "sla_last_error",
 )
 
 
@@ -109,6 +110,12 @@ def load(path: str = LIB_PATH):
         lib.stu_layer_bwd_workspace_size.restype = sz
         lib.stu_layer_bwd.argtypes = [DP] + [P] * 21 + [sz, P]
         lib.stu_layer_bwd.restype = ctypes.c_int
+        lib.stu_quantize_rows_fp8.argtypes = [P, i64, i32, P, P, P]
+        lib.stu_quantize_rows_fp8.restype = ctypes.c_int
+        lib.stu_layer_fp8_workspace_size.argtypes = [DP]
+        lib.stu_layer_fp8_workspace_size.restype = sz
+        lib.stu_layer_fwd_fp8.argtypes = [DP] + [P] * 15 + [sz, P]
+        lib.stu_layer_fwd_fp8.restype = ctypes.c_int
         lib.stu_truncate.argtypes = [i32, i64, P, P, i32, i32, P, i32, i32, P, P, P, P, i64, P]
         lib.stu_truncate.restype = ctypes.c_int
         lib.sla_status_string.argtypes = [ctypes.c_int]

@@ -30,6 +30,7 @@ SOURCES = [
     "sla_f32.hip",
     "stu_kernels.hip",
     "stu_bwd.hip",
+    "stu_fp8.hip",
 ]
 
 ARCH = "gfx950"

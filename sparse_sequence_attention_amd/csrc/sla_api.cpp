@@ -794,6 +794,112 @@ sla_status_t stu_layer_bwd(const stu_layer_desc_t *d, const void *x, const void 
     return SLA_OK;
 }
 
+sla_status_t stu_quantize_rows_fp8(const void *x, int64_t rows, int32_t cols, void *q,
+                                   float *scale, void *stream)
+{
+    if (rows < 0) return fail(SLA_ERR_INVALID, "negative rows");
+    if (rows == 0) return SLA_OK;
+    if (!x || !q || !scale) return fail(SLA_ERR_NULL, "x, q or scale is NULL");
+    if (cols <= 0 || cols % 16 != 0 || cols > 2048)
+        return fail(SLA_ERR_UNSUPPORTED, "cols %d must be a positive multiple of 16, <= 2048",
+                    cols);
+    if (!aligned16(x) || !aligned16(q)) return fail(SLA_ERR_UNSUPPORTED, "x or q not 16-byte aligned");
+    sla_status_t st = check_device();
+    if (st != SLA_OK) return st;
+    hipError_t e = launch_quant_rows_fp8(x, cols, rows, cols, q, scale,
+                                         static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "quantisation kernel");
+    return SLA_OK;
+}
+
+size_t stu_layer_fp8_workspace_size(const stu_layer_desc_t *d)
+{
+    if (!d || validate_problem(&d->attn) != SLA_OK || d->hidden <= 0) return 0;
+    const sla_problem_t *p = &d->attn;
+    const size_t T = (size_t)p->total_tokens, H = (size_t)p->num_heads;
+    const size_t NU = H * p->d_v, NW = 2 * H * p->d_v + 2 * H * p->d_qk;
+    size_t bytes = 0;
+    bytes += round_up(T * d->hidden, 256);  // n, e4m3
+    bytes += round_up(T * 4, 256);          // its row scales
+    bytes += round_up(T * NW * 2, 256);     // uvqk
+    bytes += round_up(T * NU * 2, 256);     // A
+    bytes += round_up(T * NU, 256);         // y, e4m3
+    bytes += round_up(T * 4, 256);          // its row scales
+    bytes += layout(p, SLA_OP_FWD).total;   // attention schedule
+    return bytes;
+}
+
+sla_status_t stu_layer_fwd_fp8(const stu_layer_desc_t *d, const void *x, const float *ln1_w,
+                               const float *ln1_b, const void *w_uvqk_q,
+                               const float *w_uvqk_scale, const float *b_uvqk,
+                               const float *ln2_w, const float *ln2_b, const void *w_out_q,
+                               const float *w_out_scale, const float *b_out, void *out,
+                               void *uvqk_out, void *attn_out, void *workspace, size_t ws_bytes,
+                               void *stream)
+{
+    if (!d) return fail(SLA_ERR_NULL, "layer descriptor is NULL");
+    const sla_problem_t *p = &d->attn;
+    sla_status_t st = validate_problem(p);
+    if (st != SLA_OK) return st;
+    if (p->dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "the STU layer is bf16 only");
+    if (!x || !ln1_w || !w_uvqk_q || !w_uvqk_scale || !ln2_w || !w_out_q || !w_out_scale || !out)
+        return fail(SLA_ERR_NULL, "a required layer pointer is NULL");
+    const int D = d->hidden, H = p->num_heads, dv = p->d_v, dqk = p->d_qk;
+    const int NU = H * dv, NW = 2 * H * dv + 2 * H * dqk;
+    if (D <= 0 || D % 128 != 0 || D > 2048)
+        return fail(SLA_ERR_UNSUPPORTED, "hidden %d must be a positive multiple of 128, <= 2048", D);
+    if (NU % 128 != 0 || NU > 2048)
+        return fail(SLA_ERR_UNSUPPORTED, "H*d_v = %d must be a multiple of 128, <= 2048", NU);
+    if (!(d->ln_eps > 0.0f) || !std::isfinite(d->ln_eps))
+        return fail(SLA_ERR_INVALID, "ln_eps must be positive");
+    if (out == x) return fail(SLA_ERR_INVALID, "out must not alias x");
+    const void *ptrs[] = {x, w_uvqk_q, w_out_q, out, uvqk_out, attn_out, workspace};
+    for (const void *q : ptrs)
+        if (q && !aligned16(q)) return fail(SLA_ERR_UNSUPPORTED, "a layer buffer is not 16-byte aligned");
+    const size_t need = stu_layer_fp8_workspace_size(d);
+    if (!workspace || ws_bytes < need)
+        return fail(SLA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", ws_bytes, need);
+    if ((st = check_device()) != SLA_OK) return st;
+    const int64_t T = p->total_tokens;
+    if (T == 0 || p->batch == 0) return SLA_OK;
+
+    char *w = static_cast<char *>(workspace);
+    void *nq = w;
+    w += round_up((size_t)T * D, 256);
+    float *sn = reinterpret_cast<float *>(w);
+    w += round_up((size_t)T * 4, 256);
+    void *uvqk_ws = w;
+    w += round_up((size_t)T * NW * 2, 256);
+    void *A = attn_out ? attn_out : w;
+    w += round_up((size_t)T * NU * 2, 256);
+    void *yq = w;
+    w += round_up((size_t)T * NU, 256);
+    float *sy = reinterpret_cast<float *>(w);
+    w += round_up((size_t)T * 4, 256);
+    void *attn_ws = w;
+    const size_t attn_bytes = layout(p, SLA_OP_FWD).total;
+    void *uvqk = uvqk_out ? uvqk_out : uvqk_ws;
+    uint16_t *u16 = static_cast<uint16_t *>(uvqk);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = validate_layout(p->batch, T, p->offsets, p->num_targets, -1, workspace, s)) != SLA_OK)
+        return st;
+    hipError_t e = launch_ln_quant_fp8(false, x, D, nullptr, 0, ln1_w, ln1_b, nq, sn, T, D,
+                                       d->ln_eps, s);
+    if (e != hipSuccess) return hip_fail(e, "layernorm + quantisation");
+    e = launch_gemm_fp8(nq, sn, w_uvqk_q, w_uvqk_scale, b_uvqk, nullptr, 0, uvqk, NW, T, NW, D, 0,
+                        s);
+    if (e != hipSuccess) return hip_fail(e, "uvqk projection (fp8)");
+    st = sla_fwd(p, u16 + 2 * NU, NW, u16 + 2 * NU + H * dqk, NW, u16 + NU, NW, A, NU, attn_ws,
+                 attn_bytes, stream);
+    if (st != SLA_OK) return st;
+    e = launch_ln_quant_fp8(true, A, NU, u16, NW, ln2_w, ln2_b, yq, sy, T, NU, d->ln_eps, s);
+    if (e != hipSuccess) return hip_fail(e, "gated layernorm + quantisation");
+    e = launch_gemm_fp8(yq, sy, w_out_q, w_out_scale, b_out, x, D, out, D, T, D, NU, 1, s);
+    if (e != hipSuccess) return hip_fail(e, "output projection (fp8)");
+    return SLA_OK;
+}
+
 sla_status_t stu_truncate(int32_t batch, int64_t total_tokens, const int64_t *offsets,
                           const int32_t *num_targets, int32_t contextual_len, int32_t tail_len,
                           const void *x, int32_t hidden, int32_t dtype, int64_t *new_offsets,

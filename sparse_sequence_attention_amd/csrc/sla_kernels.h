@@ -122,6 +122,18 @@ hipError_t launch_dsilu_bf16(void *ds, int64_t ldd, const void *z, int64_t ldz, 
                              int cols, hipStream_t st);
 hipError_t launch_transpose_bf16(const void *src, int R, int C, void *dst, hipStream_t st);
 hipError_t launch_fill_f32(float *dst, size_t n, float v, hipStream_t st);
+
+// FP8 projections (stu_fp8.hip): row-wise e4m3 quantisation q = e4m3(x 448 /
+// max|x|), scale = max|x| / 448; cols % 8 == 0, <= 2048
+hipError_t launch_quant_rows_fp8(const void *x, int64_t ldx, int64_t rows, int cols, void *q,
+                                 float *scale, hipStream_t st);
+hipError_t launch_ln_quant_fp8(bool gated, const void *x, int64_t ldx, const void *u, int64_t ldu,
+                               const float *w, const float *b, void *q, float *scale, int64_t rows,
+                               int cols, float eps, hipStream_t st);
+// C[M][N] = epi(sa[m] sw[n] A[m][:] . W[n][:] + bias[n]); epi 0 = SiLU, 1 = + R
+hipError_t launch_gemm_fp8(const void *A, const float *sa, const void *W, const float *sw,
+                           const float *bias, const void *R, int64_t ldr, void *C, int64_t ldc,
+                           int64_t M, int N, int K, int epi, hipStream_t st);
 hipError_t launch_truncate(int B, int64_t T, const int64_t *offsets, const int32_t *num_targets,
                            int ctx, int tail, const void *x, int hidden, int elem_bytes,
                            int64_t *new_offsets, int32_t *new_num_targets, int64_t *gather_idx,

@@ -285,6 +285,62 @@ def stu_layer_fwd(x: torch.Tensor, offsets: torch.Tensor, num_targets: Optional[
     return (out,) + extra if extra else out
 
 
+def stu_quantize_rows_fp8(x: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Row-wise e4m3 quantisation of a contiguous bf16 [R, C] matrix:
+    (q uint8 [R, C] holding e4m3 bytes, scale float32 [R]), x ~ q * scale."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous() or not x.is_cuda:
+        raise TypeError("x must be a contiguous bf16 [R, C] GPU tensor")
+    R, Cn = x.shape
+    q = torch.empty((R, Cn), dtype=torch.uint8, device=x.device)
+    sc = torch.empty(R, dtype=torch.float32, device=x.device)
+    C.check(C.load().stu_quantize_rows_fp8(_ptr(x), R, Cn, _ptr(q), _ptr(sc), _stream(x.device)))
+    return q, sc
+
+
+def stu_layer_fwd_fp8(x: torch.Tensor, offsets: torch.Tensor, num_targets: Optional[torch.Tensor],
+                      ln1_w: torch.Tensor, w_uvqk_q: torch.Tensor, w_uvqk_scale: torch.Tensor,
+                      ln2_w: torch.Tensor, w_out_q: torch.Tensor, w_out_scale: torch.Tensor, *,
+                      heads: int, d_qk: int, d_v: int, k1: int, k2: int, contextual_len: int,
+                      max_seq_len: int, alpha: float = 1.0, ln_eps: float = 1e-5, ln1_b=None,
+                      b_uvqk=None, ln2_b=None, b_out=None, out: Optional[torch.Tensor] = None,
+                      want_uvqk: bool = False, want_attn: bool = False,
+                      workspace: Optional[torch.Tensor] = None):
+    """stu_layer_fwd with both projections in FP8 (weights from
+    stu_quantize_rows_fp8).  Returns out (then uvqk, attn if asked)."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+        raise TypeError("x must be a contiguous bf16 [T, D] tensor")
+    T, D = x.shape
+    nu = heads * d_v
+    nw = 2 * nu + 2 * heads * d_qk
+    for name, w, shape in (("w_uvqk_q", w_uvqk_q, (nw, D)), ("w_out_q", w_out_q, (D, nu))):
+        if tuple(w.shape) != shape or w.dtype != torch.uint8 or not w.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous uint8 (e4m3) tensor of shape {shape}")
+    for name, sc, n in (("w_uvqk_scale", w_uvqk_scale, nw), ("w_out_scale", w_out_scale, D)):
+        if sc.dtype != torch.float32 or sc.numel() != n or not sc.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous float32 tensor of {n} scales")
+    for v_ in (ln1_w, ln1_b, b_uvqk, ln2_w, ln2_b, b_out):
+        if v_ is not None and (v_.dtype != torch.float32 or not v_.is_contiguous()):
+            raise TypeError("LayerNorm weights and biases must be contiguous float32 tensors")
+    d = C.STULayerDesc()
+    d.attn = make_problem(torch.bfloat16, offsets, num_targets, T, heads, d_qk, d_v, k1, k2,
+                          contextual_len, max_seq_len, alpha)
+    d.hidden = D
+    d.ln_eps = float(ln_eps)
+    lib = C.load()
+    nbytes = int(lib.stu_layer_fp8_workspace_size(ctypes.byref(d)))
+    ws = _workspace(nbytes, x.device, workspace)
+    out = torch.empty_like(x) if out is None else out
+    uvqk = torch.empty((T, nw), dtype=torch.bfloat16, device=x.device) if want_uvqk else None
+    attn = torch.empty((T, nu), dtype=torch.bfloat16, device=x.device) if want_attn else None
+    C.check(lib.stu_layer_fwd_fp8(ctypes.byref(d), _ptr(x), _ptr(ln1_w), _ptr(ln1_b),
+                                  _ptr(w_uvqk_q), _ptr(w_uvqk_scale), _ptr(b_uvqk), _ptr(ln2_w),
+                                  _ptr(ln2_b), _ptr(w_out_q), _ptr(w_out_scale), _ptr(b_out),
+                                  _ptr(out), _ptr(uvqk), _ptr(attn), _ptr(ws), ws.numel(),
+                                  _stream(x.device)))
+    extra = tuple(t for t, want in ((uvqk, want_uvqk), (attn, want_attn)) if want)
+    return (out,) + extra if extra else out
+
+
 def stu_layer_workspace_bytes(T: int, D: int, offsets: torch.Tensor,
                               num_targets: Optional[torch.Tensor], *, heads: int, d_qk: int,
                               d_v: int, k1: int, k2: int, contextual_len: int, max_seq_len: int,

@@ -27,6 +27,17 @@ class STULayerWeights:
     b_uvqk: Optional[torch.Tensor] = None
     ln2_b: Optional[torch.Tensor] = None
     b_out: Optional[torch.Tensor] = None
+    # FP8 copies of the projection weights (e4m3 bytes and per-row scales),
+    # filled by quantize_fp8() for stu_stack_fwd(fp8=True)
+    w_uvqk_q: Optional[torch.Tensor] = None
+    w_uvqk_scale: Optional[torch.Tensor] = None
+    w_out_q: Optional[torch.Tensor] = None
+    w_out_scale: Optional[torch.Tensor] = None
+
+    def quantize_fp8(self) -> "STULayerWeights":
+        self.w_uvqk_q, self.w_uvqk_scale = ops.stu_quantize_rows_fp8(self.w_uvqk)
+        self.w_out_q, self.w_out_scale = ops.stu_quantize_rows_fp8(self.w_out)
+        return self
 
 
 @dataclass
@@ -42,7 +53,9 @@ class StackOutput:
 
 def stu_stack_fwd(cfg: STUConfig, layers: List[STULayerWeights], x: torch.Tensor,
                   offsets: torch.Tensor, num_targets: Optional[torch.Tensor],
-                  keep_layers: bool = False) -> StackOutput:
+                  keep_layers: bool = False, fp8: bool = False) -> StackOutput:
+    """fp8: both projections of every layer in FP8 (stu_layer_fwd_fp8), with
+    the weights' FP8 copies from STULayerWeights.quantize_fp8()."""
     if len(layers) != cfg.attn_num_layers:
         raise ValueError(f"{len(layers)} layer weights for {cfg.attn_num_layers} layers")
     out = StackOutput(x=x, offsets=offsets, num_targets=num_targets)
@@ -58,12 +71,17 @@ def stu_stack_fwd(cfg: STUConfig, layers: List[STULayerWeights], x: torch.Tensor
         out.layer_tokens.append(int(cur.shape[0]))
         if keep_layers:
             out.layer_inputs.append(cur)
-        cur = ops.stu_layer_fwd(cur, offs, tg, w.ln1_w, w.w_uvqk, w.ln2_w, w.w_out,
-                                heads=cfg.num_heads, d_qk=cfg.attention_dim, d_v=cfg.hidden_dim,
-                                k1=cfg.kernel_k1, k2=cfg.kernel_k2,
-                                contextual_len=cfg.contextual_seq_len,
-                                max_seq_len=cfg.max_seq_len, alpha=cfg.alpha, ln_eps=cfg.ln_eps,
-                                ln1_b=w.ln1_b, b_uvqk=w.b_uvqk, ln2_b=w.ln2_b, b_out=w.b_out)
+        kw = dict(heads=cfg.num_heads, d_qk=cfg.attention_dim, d_v=cfg.hidden_dim,
+                  k1=cfg.kernel_k1, k2=cfg.kernel_k2, contextual_len=cfg.contextual_seq_len,
+                  max_seq_len=cfg.max_seq_len, alpha=cfg.alpha, ln_eps=cfg.ln_eps,
+                  ln1_b=w.ln1_b, b_uvqk=w.b_uvqk, ln2_b=w.ln2_b, b_out=w.b_out)
+        if fp8:
+            if w.w_uvqk_q is None or w.w_out_q is None:
+                raise ValueError(f"layer {li}: FP8 weights missing (call quantize_fp8())")
+            cur = ops.stu_layer_fwd_fp8(cur, offs, tg, w.ln1_w, w.w_uvqk_q, w.w_uvqk_scale,
+                                        w.ln2_w, w.w_out_q, w.w_out_scale, **kw)
+        else:
+            cur = ops.stu_layer_fwd(cur, offs, tg, w.ln1_w, w.w_uvqk, w.ln2_w, w.w_out, **kw)
         if keep_layers:
             out.layer_outputs.append(cur)
     out.x, out.offsets, out.num_targets = cur, offs, tg

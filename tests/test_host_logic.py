@@ -26,7 +26,7 @@ def lib():
 def _declared_functions():
     text = open(os.path.join(ROOT, "include", "sla.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"\b((?:sla|stu)_[a-z_]+)\s*\(", text)
+    names = re.findall(r"\b((?:sla|stu)_[a-z_0-9]+)\s*\(", text)
     return sorted(set(names))
 
 
