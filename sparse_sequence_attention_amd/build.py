@@ -31,6 +31,7 @@ SOURCES = [
     "stu_kernels.hip",
     "stu_bwd.hip",
     "stu_fp8.hip",
+    "gemm_nt.hip",
 ]
 
 ARCH = "gfx950"

@@ -93,6 +93,17 @@ hipError_t launch_gemm_bf16(const void *A, int64_t lda, const void *W, int64_t l
                             void *Z, int64_t ldz, int64_t M, int N, int K, int epi,
                             hipStream_t st);
 
+// The projection GEMM core (gemm_nt.hip): 256 x 128|256 tiles, DMA-fed
+// four-stage ring, row-contiguous stores.  bf16: N % 128, K % 32; FP8: N % 128,
+// K % 64, epi 0..2 (sa, sw the row scales of A and W).
+hipError_t launch_gemm_nt_bf16(const void *A, int64_t lda, const void *W, int64_t ldw,
+                               const float *bias, const void *R, int64_t ldr, void *C, int64_t ldc,
+                               void *Z, int64_t ldz, int64_t M, int N, int K, int epi,
+                               hipStream_t st);
+hipError_t launch_gemm_nt_fp8(const void *A, const float *sa, const void *W, const float *sw,
+                              const float *bias, const void *R, int64_t ldr, void *C, int64_t ldc,
+                              int64_t M, int N, int K, int epi, hipStream_t st);
+
 // STU layer backward pieces (stu_bwd.hip)
 // C[M][N] = sum_t A[t][m] B[t][n] over T rows, fp32: `splits` token ranges
 // into part [splits][M][N], then summed in split order into out.  M, N

@@ -119,135 +119,13 @@ hipError_t launch_gated_layernorm_bf16(const void *a, int64_t lda, const void *u
 // GEMM  C[M][N] = epi(A[M][K] . W[N][K]^T), with z = acc (+ bias[n]):
 //   EPI 0: C = SiLU(z)        EPI 1: C = z + R (residual)
 //   EPI 2: C = z              EPI 3: C = SiLU(z) and Z = z (the pre-activation)
-// Workgroup tile 128 x 128, 4 waves in 2 x 2, K steps of 64.  The waves compute
-// C^T blocks (W rows as the MFMA A operand, A rows as B) so that each lane ends
-// with four consecutive output columns of one row: 8-byte stores.
+// (the kernel lives in gemm_nt.hip, shared with the FP8 projections)
 // ---------------------------------------------------------------------------
-constexpr int GM = 128, GN = 128, GK = 64;
-
-template <int EPI>
-__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t *A, int64_t lda,
-                                                           const uint16_t *W, int64_t ldw,
-                                                           const float *bias, const uint16_t *R,
-                                                           int64_t ldr, uint16_t *C, int64_t ldc,
-                                                           uint16_t *Z, int64_t ldz, int64_t M,
-                                                           int N, int K)
-{
-    __shared__ __align__(16) uint16_t sa[2][GM * GK];
-    __shared__ __align__(16) uint16_t sw[2][GN * GK];
-    const int ntn = N / GN;
-    const int64_t ntm = (M + GM - 1) / GM;
-    const int item = xcd_remap(blockIdx.x, (int)(ntm * ntn));
-    if (item < 0) return;
-    const int64_t m0 = (int64_t)(item / ntn) * GM;
-    const int n0 = (item % ntn) * GN;
-
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int l32 = lane & 31, hl = lane >> 5;
-    const int wm = wv & 1, wn = wv >> 1;  // wave's 64 x 64 sub-tile
-
-    // staging: thread loads rows (tid/8) + 32*i, chunk tid%8 of both tiles
-    const int sr = tid >> 3, sc = tid & 7;
-    uint4 ra[4], rw[4];
-    auto load = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            ra[i] = ld16_row(A, lda, (int)(m0 + sr + 32 * i), (int)M, k0 + 8 * sc);
-            rw[i] = ld16(W + (int64_t)(n0 + sr + 32 * i) * ldw + k0 + 8 * sc);
-        }
-    };
-    auto store = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = sr + 32 * i;
-            *reinterpret_cast<uint4 *>(&sa[buf][r * GK + 8 * (sc ^ (r & 7))]) = ra[i];
-            *reinterpret_cast<uint4 *>(&sw[buf][r * GK + 8 * (sc ^ (r & 7))]) = rw[i];
-        }
-    };
-
-    floatx16 acc[2][2];  // [n block][m block] of C^T
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
-
-    const int nk = K / GK;
-    load(0);
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        store(buf);
-        if (kt + 1 < nk) load((kt + 1) * GK);
-        __syncthreads();
-#pragma unroll
-        for (int kc = 0; kc < GK / 16; ++kc) {
-            bf16x8 wa[2], xb[2];
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                const int r = 64 * wn + 32 * nb + l32;
-                wa[nb] = as_bf16x8(*reinterpret_cast<const uint4 *>(
-                    &sw[buf][r * GK + 8 * ((2 * kc + hl) ^ (r & 7))]));
-            }
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                const int r = 64 * wm + 32 * mb + l32;
-                xb[mb] = as_bf16x8(*reinterpret_cast<const uint4 *>(
-                    &sa[buf][r * GK + 8 * ((2 * kc + hl) ^ (r & 7))]));
-            }
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = mfma32(wa[nb], xb[mb], acc[nb][mb]);
-        }
-    }
-
-    // epilogue: lane owns row m, registers hold columns n = 8*(r/4) + 4*hl + r%4
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-        const int64_t m = m0 + 64 * wm + 32 * mb + l32;
-        if (m >= M) continue;
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + 64 * wn + 32 * nb + 8 * g + 4 * hl;
-                float o[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = acc[nb][mb][4 * g + e] + (bias ? bias[n + e] : 0.0f);
-                if (EPI == 3)
-                    *reinterpret_cast<uint2 *>(Z + m * ldz + n) = cvt4_u2(o[0], o[1], o[2], o[3]);
-                if (EPI == 0 || EPI == 3) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) o[e] = o[e] * sigmoid_fast(o[e], -1.4426950408889634f);
-                } else if (EPI == 1) {
-                    const uint2 rr = *reinterpret_cast<const uint2 *>(R + m * ldr + n);
-                    o[0] += bf16_lo(rr.x);
-                    o[1] += bf16_hi(rr.x);
-                    o[2] += bf16_lo(rr.y);
-                    o[3] += bf16_hi(rr.y);
-                }
-                *reinterpret_cast<uint2 *>(C + m * ldc + n) = cvt4_u2(o[0], o[1], o[2], o[3]);
-            }
-        }
-    }
-}
-
 hipError_t launch_gemm_bf16(const void *A, int64_t lda, const void *W, int64_t ldw,
                             const float *bias, const void *R, int64_t ldr, void *C, int64_t ldc,
                             void *Z, int64_t ldz, int64_t M, int N, int K, int epi, hipStream_t st)
 {
-    if (M <= 0) return hipSuccess;
-    if (N % GN != 0 || K % GK != 0 || epi < 0 || epi > 3) return hipErrorInvalidValue;
-    if ((epi == 1 && !R) || (epi == 3 && !Z)) return hipErrorInvalidValue;
-    const int64_t tiles = ((M + GM - 1) / GM) * (N / GN);
-    dim3 grid((unsigned)tiles), block(256);
-    auto kern = epi == 0 ? gemm_bf16_kernel<0>
-                : epi == 1 ? gemm_bf16_kernel<1>
-                : epi == 2 ? gemm_bf16_kernel<2>
-                           : gemm_bf16_kernel<3>;
-    hipLaunchKernelGGL(kern, grid, block, 0, st, (const uint16_t *)A, lda, (const uint16_t *)W, ldw,
-                       bias, (const uint16_t *)R, ldr, (uint16_t *)C, ldc, (uint16_t *)Z, ldz, M, N,
-                       K);
-    return hipGetLastError();
+    return launch_gemm_nt_bf16(A, lda, W, ldw, bias, R, ldr, C, ldc, Z, ldz, M, N, K, epi, st);
 }
 
 // ---------------------------------------------------------------------------
