@@ -232,20 +232,8 @@ sla_status_t make_params(const sla_problem_t *p, int op, void *ws, size_t ws_byt
 // STU layer backward workspace: recomputed activations, their gradients, a
 // transposed weight, fp32 partial sums, and the attention workspace last.
 struct StuBwdLayout {
-    size_t n, z, uvqk, A, y, dy, dA, dz, dn, wt, part, vec, mid, attn, total;
-    int split_out, split_uvqk;
+    size_t n, z, uvqk, A, y, dy, dA, dz, dn, wt, part, vec, mid, zero, attn, total;
 };
-
-// token ranges of a weight-gradient product: about 512 workgroups in all,
-// at least 256 tokens per range
-int tn_splits(int64_t T, int M, int N)
-{
-    const int64_t tiles = (int64_t)(M / 128) * (N / 128);
-    int64_t s = tiles > 0 ? (512 + tiles - 1) / tiles : 1;
-    const int64_t cap = (T + 255) / 256;
-    if (s > cap) s = cap;
-    return (int)(s < 1 ? 1 : s);
-}
 
 StuBwdLayout stu_bwd_layout(const stu_layer_desc_t *d)
 {
@@ -270,10 +258,8 @@ StuBwdLayout stu_bwd_layout(const stu_layer_desc_t *d)
     L.dz = take(T * NW * 2);
     L.dn = take(T * D * 2);
     L.wt = take(NW * D * 2);
-    L.split_out = tn_splits((int64_t)T, (int)D, (int)NU);
-    L.split_uvqk = tn_splits((int64_t)T, (int)NW, (int)D);
-    size_t part = (size_t)L.split_out * D * NU;
-    const size_t pu = (size_t)L.split_uvqk * NW * D;
+    size_t part = (size_t)tn_plan((int64_t)T, (int)D, (int)NU).splits * D * NU;
+    const size_t pu = (size_t)tn_plan((int64_t)T, (int)NW, (int)D).splits * NW * D;
     if (pu > part) part = pu;
     const size_t cs = (size_t)colsum_blocks((int64_t)T) * (NW > D ? NW : D);
     if (cs > part) part = cs;
@@ -282,6 +268,7 @@ StuBwdLayout stu_bwd_layout(const stu_layer_desc_t *d)
     L.part = take(part * 4);
     L.vec = take((NW > D ? NW : D) * 4);
     L.mid = take((size_t)SUM_MID_FLOATS * 4);
+    L.zero = take(1024);  // a zero token row for the weight-gradient products
     L.attn = at;
     L.total = at + layout(p, SLA_OP_BWD).total;
     return L;
@@ -732,6 +719,7 @@ sla_status_t stu_layer_bwd(const stu_layer_desc_t *d, const void *x, const void 
     float *part = reinterpret_cast<float *>(base + L.part);
     float *scratch_w = reinterpret_cast<float *>(base + L.vec);  // sums of unwanted gradients
     float *mid = reinterpret_cast<float *>(base + L.mid);
+    float *zero = reinterpret_cast<float *>(base + L.zero);
     void *attn_ws = base + L.attn;
     const size_t attn_bytes = L.total - L.attn;
     auto or_scratch = [&](float *g) { return g ? g : scratch_w; };
@@ -745,6 +733,7 @@ sla_status_t stu_layer_bwd(const stu_layer_desc_t *d, const void *x, const void 
         e = (call);                              \
         if (e != hipSuccess) return hip_fail(e, what); \
     } while (0)
+    STU_TRY(launch_fill_f32(zero, 256, 0.0f, s), "zero row");
     // recomputed activations: n, z, uvqk = SiLU(z), A (unless saved)
     STU_TRY(launch_layernorm_bf16(x, ln1_w, ln1_b, n, T, D, d->ln_eps, s), "layernorm");
     STU_TRY(launch_gemm_bf16(n, D, w_uvqk, D, b_uvqk, nullptr, 0, uvqk, NW, z, NW, T, NW, D, 3, s),
@@ -767,7 +756,7 @@ sla_status_t stu_layer_bwd(const stu_layer_desc_t *d, const void *x, const void 
             "gated layernorm backward");
     // output projection weights: dW2 = dout^T y, db_out
     if (dw_out)
-        STU_TRY(launch_gemm_tn_bf16(dout, D, y, NU, T, D, NU, part, L.split_out, dw_out, s),
+        STU_TRY(launch_gemm_tn_bf16(dout, D, y, NU, T, D, NU, zero, part, dw_out, s),
                 "output weight gradient");
     if (db_out)
         STU_TRY(launch_colsum_bf16(dout, D, T, D, part, db_out, mid, s), "output bias gradient");
@@ -778,7 +767,7 @@ sla_status_t stu_layer_bwd(const stu_layer_desc_t *d, const void *x, const void 
     // SiLU: dz = d[U|V|Q|K] (.) SiLU'(z); dW1 = dz^T n, db_uvqk, dn = dz W1
     STU_TRY(launch_dsilu_bf16(dz, NW, z, NW, T, NW, s), "SiLU backward");
     if (dw_uvqk)
-        STU_TRY(launch_gemm_tn_bf16(dz, NW, n, D, T, NW, D, part, L.split_uvqk, dw_uvqk, s),
+        STU_TRY(launch_gemm_tn_bf16(dz, NW, n, D, T, NW, D, zero, part, dw_uvqk, s),
                 "projection weight gradient");
     if (db_uvqk)
         STU_TRY(launch_colsum_bf16(dz, NW, T, NW, part, db_uvqk, mid, s), "projection bias gradient");

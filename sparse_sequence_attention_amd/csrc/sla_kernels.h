@@ -105,11 +105,17 @@ hipError_t launch_gemm_nt_fp8(const void *A, const float *sa, const void *W, con
                               int64_t M, int N, int K, int epi, hipStream_t st);
 
 // STU layer backward pieces (stu_bwd.hip)
-// C[M][N] = sum_t A[t][m] B[t][n] over T rows, fp32: `splits` token ranges
-// into part [splits][M][N], then summed in split order into out.  M, N
-// multiples of 128.
+// C[M][N] = sum_t A[t][m] B[t][n] over T rows, fp32: tn_plan(T, M, N).splits
+// token ranges into part [splits][M][N], then summed in range order into out.
+// M, N multiples of 128; zero: >= 512 bytes of zeros (16-byte aligned).
+struct TnPlan {
+    int tile, splits;
+    int64_t rows;  // tokens per range (a multiple of 32)
+};
+TnPlan tn_plan(int64_t T, int M, int N);
 hipError_t launch_gemm_tn_bf16(const void *A, int64_t lda, const void *B, int64_t ldb, int64_t T,
-                               int M, int N, float *part, int splits, float *out, hipStream_t st);
+                               int M, int N, const void *zero, float *part, float *out,
+                               hipStream_t st);
 // out[i] = sum_s part[s][i] (count % 4 == 0) in a fixed order; mid (nullable,
 // SUM_MID_FLOATS floats) spreads a short range with many splits over more
 // workgroups.

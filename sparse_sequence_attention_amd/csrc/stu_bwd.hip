@@ -15,14 +15,6 @@
 
 namespace sla {
 
-// ---------------------------------------------------------------------------
-// C_part[s][m][n] = sum_{t in split s} A[t][m] * B[t][n]   (bf16 in, fp32 out)
-// ---------------------------------------------------------------------------
-// Tile 128 (m) x 128 (n), 4 waves of 64 x 64, steps of 64 tokens.  Both tiles
-// are staged row-major ([token][column], 256-byte rows, chunk-swizzled) and the
-// MFMA operands (8 consecutive tokens of one column per lane) come from
-// transposing LDS reads; A and B use the same token order, so the sum is exact
-// in any order of the 8 k-slots.
 __device__ __forceinline__ void unpack8(const uint4 &r, float *f)
 {
     const uint32_t w[4] = {r.x, r.y, r.z, r.w};
@@ -33,103 +25,167 @@ __device__ __forceinline__ void unpack8(const uint4 &r, float *f)
     }
 }
 
-constexpr int WG_M = 128, WG_N = 128, WG_T = 64;
+// ---------------------------------------------------------------------------
+// C_part[s][m][n] = sum_{t in split s} A[t][m] * B[t][n]   (bf16 in, fp32 out)
+// ---------------------------------------------------------------------------
+// Tile TB x TB (TB = 256: 8 waves of 64 x 128; TB = 128: 8 waves of 64 x 32)
+// per token range.  The A and B columns of 32 tokens stream HBM -> LDS by
+// DMA through a four-stage ring (three stages ahead), row-major
+// ([token][column]); the MFMA operands, 8 consecutive tokens of one column per
+// lane, come from transposing LDS reads, with the same token order for A and
+// B.  Tokens past the range read a zero row (`zero`, >= TB * 2 bytes), so the
+// tail needs no masking.  16-byte chunk c of token row r sits at
+// c ^ (4 (r & 3)): the four rows of a transposing read pass land in four
+// different quarters of the banks.
+constexpr int TN_T = 32;  // tokens per stage
 
-__device__ __forceinline__ int wg_swz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
-
-__global__ __launch_bounds__(256, 2) void gemm_tn_kernel(const uint16_t *A, int64_t lda,
-                                                         const uint16_t *B, int64_t ldb,
-                                                         float *part, int64_t T, int M, int N,
-                                                         int64_t rows_per_split, int splits)
+template <int TB>
+__global__ __launch_bounds__(512, (TB == 256 ? 1 : 2)) void gemm_tn_kernel(
+    const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, const uint16_t *zero,
+    float *part, int64_t T, int M, int N, int64_t rows_per_split)
 {
-    __shared__ __align__(16) uint16_t sa[2][WG_T * WG_M];
-    __shared__ __align__(16) uint16_t sb[2][WG_T * WG_N];
-    const int ntm = M / WG_M, ntn = N / WG_N;
+    constexpr int RB = TB * 2;                  // bytes per token row of one operand
+    constexpr int STAGE = 2 * TN_T * RB;        // A rows then B rows
+    constexpr int PER = STAGE / 1024 / 8;       // DMA instructions per thread and stage
+    constexpr int WMR = 64;                     // m per wave
+    constexpr int WNC = TB == 256 ? 128 : 32;   // n per wave
+    constexpr int NFM = WMR / 32, NFN = WNC / 32;
+    constexpr int NWM = TB / WMR;               // waves along m
+    static_assert(NWM * (TB / WNC) == 8, "8 waves");
+    __shared__ __align__(16) uint8_t st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGE];
+
+    const int ntm = M / TB, ntn = N / TB;
     const int item = blockIdx.x;
     const int s = item / (ntm * ntn), rem = item - s * (ntm * ntn);
-    const int m0 = (rem / ntn) * WG_M, n0 = (rem % ntn) * WG_N;
+    const int m0 = (rem / ntn) * TB, n0 = (rem % ntn) * TB;
     const int64_t t0 = (int64_t)s * rows_per_split;
     int64_t t1 = t0 + rows_per_split < T ? t0 + rows_per_split : T;
-    if (t1 < t0) t1 = t0;  // a split past the last token writes zeros
+    if (t1 < t0) t1 = t0;  // a range past the last token writes zeros
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int wm = wv & 1, wn = wv >> 1;
+    const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
+    const int wm = wv % NWM, wn = wv / NWM;
     const int q4 = lane >> 4, j16 = lane & 15;
 
-    // staging: thread loads chunk tid % 16 of rows tid / 16 + 16 i (i < 4)
-    const int sr = tid >> 4, sc = tid & 15;
-    uint4 ra[4], rb[4];
-    auto load = [&](int64_t tb) {
+    auto stage = [&](auto S) -> uint8_t * {
+        constexpr int sidx = decltype(S)::value;
+        if constexpr (sidx == 0) return st0;
+        else if constexpr (sidx == 1) return st1;
+        else if constexpr (sidx == 2) return st2;
+        else return st3;
+    };
+    // wave-chunk q (1 KB) = stage rows [q * 1024 / RB, ...): lane -> row
+    // (q * 1024 + 16 lane) / RB, physical chunk ((16 lane) % RB) / 16
+    auto issue = [&](int64_t step, auto S) {
+        uint8_t *sb = stage(S);
+        const int64_t tb = t0 + step * TN_T;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t t = tb + sr + 16 * i;
-            const bool ok = t < t1;
-            const int64_t tt = ok ? t : t0;  // a valid row; zeroed below
-            ra[i] = ld16_or_zero(A + tt * lda + m0 + 8 * sc, ok);
-            rb[i] = ld16_or_zero(B + tt * ldb + n0 + 8 * sc, ok);
+        for (int i = 0; i < PER; ++i) {
+            const int q = i * 8 + wv;
+            const int byte = q * 1024 + 16 * lane;
+            const int row = byte / RB;              // 0 .. 2 TN_T - 1 (A rows, then B rows)
+            const int pc = (byte % RB) / 16;
+            const int r = row % TN_T;               // token within the stage
+            const int lc = pc ^ (4 * (r & 3));
+            const int64_t t = tb + r;
+            const uint16_t *src;
+            if (t < t1) src = row < TN_T ? A + t * lda + m0 + 8 * lc : B + t * ldb + n0 + 8 * lc;
+            else src = zero + 8 * lc;
+            gl_lds16(src, reinterpret_cast<uint16_t *>(sb + q * 1024));
         }
     };
-    auto store = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = sr + 16 * i;
-            *reinterpret_cast<uint4 *>(&sa[buf][r * WG_M + 8 * (sc ^ wg_swz(r))]) = ra[i];
-            *reinterpret_cast<uint4 *>(&sb[buf][r * WG_N + 8 * (sc ^ wg_swz(r))]) = rb[i];
-        }
-    };
-    // transposing read: rows 16*kc + 8*rr + 4*(q/2) + j/4, columns c0 + 16*(q%2) + 4*(j%4)
-    auto tr = [&](const uint16_t *tile, int kc, int c0) {
+    // transposing read: tokens 16 kc + 8 rr + 4 (q4 / 2) + j16 / 4, columns
+    // c0 + 16 (q4 % 2) + 4 (j16 % 4) of the operand region at `base`
+    auto tr = [&](const uint8_t *base, int kc, int c0) {
         uint2 v[2];
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr) {
             const int row = 16 * kc + 8 * rr + 4 * (q4 >> 1) + (j16 >> 2);
             const int col = c0 + 16 * (q4 & 1) + 4 * (j16 & 3);
-            v[rr] = tr_read_b64(tile + row * 128 + 8 * ((col >> 3) ^ wg_swz(row)) + (col & 7));
+            const int pc = (col >> 3) ^ (4 * (row & 3));
+            v[rr] = tr_read_b64(reinterpret_cast<const uint16_t *>(base + row * RB + 16 * pc) +
+                                (col & 7));
         }
         return __builtin_bit_cast(bf16x8, make_uint4(v[0].x, v[0].y, v[1].x, v[1].y));
     };
 
-    floatx16 acc[2][2];
+    floatx16 acc[NFM][NFN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NFM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
+        for (int j = 0; j < NFN; ++j) acc[i][j] = zero16();
 
-    const int64_t nsteps = (t1 - t0 + WG_T - 1) / WG_T;
-    if (nsteps > 0) load(t0);
-    for (int64_t st = 0; st < nsteps; ++st) {
-        const int buf = (int)(st & 1);
-        store(buf);
-        if (st + 1 < nsteps) load(t0 + (st + 1) * WG_T);
-        __syncthreads();
+    auto compute = [&](auto S) {
+        const uint8_t *sa = stage(S), *sbb = stage(S) + TN_T * RB;
 #pragma unroll
-        for (int kc = 0; kc < WG_T / 16; ++kc) {
-            bf16x8 a[2], b[2];
+        for (int kc = 0; kc < TN_T / 16; ++kc) {
+            bf16x8 a[NFM], b[NFN];
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) a[mb] = tr(sa[buf], kc, 64 * wm + 32 * mb);
+            for (int i = 0; i < NFM; ++i) a[i] = tr(sa, kc, WMR * wm + 32 * i);
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) b[nb] = tr(sb[buf], kc, 64 * wn + 32 * nb);
+            for (int j = 0; j < NFN; ++j) b[j] = tr(sbb, kc, WNC * wn + 32 * j);
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+            for (int i = 0; i < NFM; ++i)
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(a[mb], b[nb], acc[mb][nb]);
+                for (int j = 0; j < NFN; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
         }
-        __syncthreads();  // the next store overwrites the other buffer's reader
-    }
+    };
 
-    // register r of acc[mb][nb]: m = 64*wm + 32*mb + 8*(r/4) + 4*hl + r%4, n = 64*wn + 32*nb + l32
+    // the ring as in the projection GEMM: unconditional DMAs (clamped past the
+    // last step), branch-free groups of four steps, then the remainder
+    const int64_t nk = (t1 - t0 + TN_T - 1) / TN_T;
+    auto step = [&](int64_t k, auto S) {
+        constexpr int sidx = decltype(S)::value;
+        vm_wait<2 * PER>();
+        barrier_lds();
+        issue(k + 3 < nk ? k + 3 : (nk > 0 ? nk - 1 : 0), std::integral_constant<int, (sidx + 3) % 4>{});
+        compute(S);
+    };
+    issue(0, std::integral_constant<int, 0>{});
+    issue(nk > 1 ? 1 : 0, std::integral_constant<int, 1>{});
+    issue(nk > 2 ? 2 : 0, std::integral_constant<int, 2>{});
+    const int64_t ng = nk / 4;
+    for (int64_t g = 0; g < ng; ++g) {
+        step(4 * g, std::integral_constant<int, 0>{});
+        step(4 * g + 1, std::integral_constant<int, 1>{});
+        step(4 * g + 2, std::integral_constant<int, 2>{});
+        step(4 * g + 3, std::integral_constant<int, 3>{});
+    }
+    const int rem4 = uniform((int)(nk - 4 * ng));
+    if (rem4 > 0) step(4 * ng, std::integral_constant<int, 0>{});
+    if (rem4 > 1) step(4 * ng + 1, std::integral_constant<int, 1>{});
+    if (rem4 > 2) step(4 * ng + 2, std::integral_constant<int, 2>{});
+    vm_wait<0>();
+
+    // register r of acc[i][j]: m = 8 (r / 4) + 4 hl + r % 4, n = l32
     const int l32 = lane & 31, hl = lane >> 5;
     float *ps = part + (int64_t)s * M * N;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int i = 0; i < NFM; ++i)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int j = 0; j < NFN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int m = m0 + 64 * wm + 32 * mb + 8 * (r >> 2) + 4 * hl + (r & 3);
-                const int n = n0 + 64 * wn + 32 * nb + l32;
-                ps[(int64_t)m * N + n] = acc[mb][nb][r];
+                const int m = m0 + WMR * wm + 32 * i + 8 * (r >> 2) + 4 * hl + (r & 3);
+                const int n = n0 + WNC * wn + 32 * j + l32;
+                ps[(int64_t)m * N + n] = acc[i][j][r];
             }
+}
+
+// 256-wide tiles when there are at least 8 of them, else 128; token ranges
+// for about one (256) or two (128) workgroups per CU, at least 256 tokens each
+TnPlan tn_plan(int64_t T, int M, int N)
+{
+    TnPlan p{};
+    p.tile = (M % 256 == 0 && N % 256 == 0 && (M / 256) * (N / 256) >= 8) ? 256 : 128;
+    const int64_t tiles = (int64_t)(M / p.tile) * (N / p.tile);
+    const int64_t target = p.tile == 256 ? 256 : 512;
+    int64_t splits = tiles > 0 ? (target + tiles - 1) / tiles : 1;
+    const int64_t cap = (T + 255) / 256;
+    if (splits > cap) splits = cap;
+    p.splits = (int)(splits < 1 ? 1 : splits);
+    int64_t rows = (T + p.splits - 1) / p.splits;
+    p.rows = (rows + TN_T - 1) / TN_T * TN_T;
+    return p;
 }
 
 // ---------------------------------------------------------------------------
@@ -202,18 +258,24 @@ hipError_t sum_splits(const float *part, int64_t count, int splits, float *out, 
 }
 
 hipError_t launch_gemm_tn_bf16(const void *A, int64_t lda, const void *B, int64_t ldb, int64_t T,
-                               int M, int N, float *part, int splits, float *out, hipStream_t st)
+                               int M, int N, const void *zero, float *part, float *out,
+                               hipStream_t st)
 {
-    if (M % WG_M != 0 || N % WG_N != 0 || splits < 1) return hipErrorInvalidValue;
-    int64_t rows = (T + splits - 1) / splits;
-    rows = (rows + WG_T - 1) / WG_T * WG_T;
-    const int tiles = (M / WG_M) * (N / WG_N);
-    hipLaunchKernelGGL(gemm_tn_kernel, dim3((unsigned)(tiles * splits)), dim3(256), 0, st,
-                       (const uint16_t *)A, lda, (const uint16_t *)B, ldb, part, T, M, N, rows,
-                       splits);
+    if (M % 128 != 0 || N % 128 != 0 || lda % 8 != 0 || ldb % 8 != 0 || !zero)
+        return hipErrorInvalidValue;
+    const TnPlan pl = tn_plan(T, M, N);
+    const int tiles = (M / pl.tile) * (N / pl.tile);
+    if (pl.tile == 256)
+        hipLaunchKernelGGL(gemm_tn_kernel<256>, dim3((unsigned)(tiles * pl.splits)), dim3(512), 0,
+                           st, (const uint16_t *)A, lda, (const uint16_t *)B, ldb,
+                           (const uint16_t *)zero, part, T, M, N, pl.rows);
+    else
+        hipLaunchKernelGGL(gemm_tn_kernel<128>, dim3((unsigned)(tiles * pl.splits)), dim3(512), 0,
+                           st, (const uint16_t *)A, lda, (const uint16_t *)B, ldb,
+                           (const uint16_t *)zero, part, T, M, N, pl.rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return sum_splits(part, (int64_t)M * N, splits, out, nullptr, st);
+    return sum_splits(part, (int64_t)M * N, pl.splits, out, nullptr, st);
 }
 
 // ---------------------------------------------------------------------------
