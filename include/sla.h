@@ -326,6 +326,23 @@ sla_status_t stu_layer_fwd_fp8(const stu_layer_desc_t *d, const void *x, const f
                                void *uvqk_out, void *attn_out, void *workspace, size_t ws_bytes,
                                void *stream);
 
+/* Target (candidate) rows of a jagged batch gathered into a column block of a
+ * dense output (Mixture of Transducers, ULTRA-HSTU paper section 4.3 and
+ * Appendix A, and the torcheasyrec page's MoT bullet: every channel runs its own STU stack over
+ * its own UIH sequence with the shared contextual and candidate tokens, and
+ * the channels' candidate embeddings are concatenated along the feature
+ * dimension).  Writes target_offsets [B+1] (int64, device: sequence b's
+ * targets are rows target_offsets[b] .. target_offsets[b+1] of out) and, when
+ * out is non-NULL, copies the last num_targets[b] rows of each sequence of
+ * x [total_tokens][hidden] into out rows in order, columns [col_offset,
+ * col_offset + hidden) of rows of ld_out elements.  dtype as x (bf16 or
+ * f32); hidden, ld_out and col_offset multiples of 16 bytes; capacity >= the
+ * total number of targets (rows past capacity are not written). */
+sla_status_t stu_gather_targets(int32_t batch, int64_t total_tokens, const int64_t *offsets,
+                                const int32_t *num_targets, const void *x, int32_t hidden,
+                                int32_t dtype, int64_t *target_offsets, void *out, int64_t ld_out,
+                                int64_t col_offset, int64_t capacity, void *stream);
+
 /* Attention truncation (ULTRA-HSTU paper, section 4.3; torcheasyrec page,
  * truncation bullet): per sequence keep, in order, the contextual prefix
  * [0, c), the most recent tail_len history tokens and the num_targets[b]

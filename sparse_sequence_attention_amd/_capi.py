@@ -25,7 +25,7 @@ EXPORTS = (
     "sla_fwd_candidates", "sla_bwd", "sla_bwd_stage", "sla_schedule_capacity", "sla_schedule_tile",
     "sla_schedule", "sla_schedule_host", "sla_count_pairs_host", "stu_layer_workspace_size", "stu_layer_fwd",
     "stu_layer_bwd_workspace_size", "stu_layer_bwd", "stu_quantize_rows_fp8",
-    "stu_layer_fp8_workspace_size", "stu_layer_fwd_fp8", "stu_truncate", "sla_status_string", "sla_last_error",
+    "stu_layer_fp8_workspace_size", "stu_layer_fwd_fp8", "stu_gather_targets", "stu_truncate", "sla_status_string", "sla_last_error",
 )
 
 
@@ -116,6 +116,8 @@ def load(path: str = LIB_PATH):
         lib.stu_layer_fp8_workspace_size.restype = sz
         lib.stu_layer_fwd_fp8.argtypes = [DP] + [P] * 15 + [sz, P]
         lib.stu_layer_fwd_fp8.restype = ctypes.c_int
+        lib.stu_gather_targets.argtypes = [i32, i64, P, P, P, i32, i32, P, P, i64, i64, i64, P]
+        lib.stu_gather_targets.restype = ctypes.c_int
         lib.stu_truncate.argtypes = [i32, i64, P, P, i32, i32, P, i32, i32, P, P, P, P, i64, P]
         lib.stu_truncate.restype = ctypes.c_int
         lib.sla_status_string.argtypes = [ctypes.c_int]

@@ -889,6 +889,42 @@ sla_status_t stu_layer_fwd_fp8(const stu_layer_desc_t *d, const void *x, const f
     return SLA_OK;
 }
 
+sla_status_t stu_gather_targets(int32_t batch, int64_t total_tokens, const int64_t *offsets,
+                                const int32_t *num_targets, const void *x, int32_t hidden,
+                                int32_t dtype, int64_t *target_offsets, void *out, int64_t ld_out,
+                                int64_t col_offset, int64_t capacity, void *stream)
+{
+    if (batch < 0 || total_tokens < 0) return fail(SLA_ERR_INVALID, "negative batch or total_tokens");
+    if (!target_offsets) return fail(SLA_ERR_NULL, "target_offsets is NULL");
+    if (batch > 0 && (!offsets || !num_targets))
+        return fail(SLA_ERR_NULL, "offsets or num_targets is NULL");
+    if (dtype != SLA_F32 && dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "bad dtype");
+    const int eb = dtype == SLA_BF16 ? 2 : 4;
+    if (capacity < 0) return fail(SLA_ERR_INVALID, "negative capacity");
+    if (out) {
+        if (!x) return fail(SLA_ERR_NULL, "x is NULL");
+        if (hidden <= 0 || ((int64_t)hidden * eb) % 16 != 0)
+            return fail(SLA_ERR_UNSUPPORTED, "hidden row must be a positive multiple of 16 bytes");
+        if (col_offset < 0 || ld_out < col_offset + hidden)
+            return fail(SLA_ERR_INVALID, "columns [col_offset, col_offset + hidden) exceed ld_out");
+        if ((ld_out * eb) % 16 != 0 || (col_offset * eb) % 16 != 0)
+            return fail(SLA_ERR_UNSUPPORTED, "ld_out and col_offset must be multiples of 16 bytes");
+        if (!aligned16(x) || !aligned16(out))
+            return fail(SLA_ERR_UNSUPPORTED, "x / out not 16-byte aligned");
+    }
+    sla_status_t st = check_device();
+    if (st != SLA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = validate_layout(batch, total_tokens, offsets, num_targets, -1, target_offsets, s)) !=
+        SLA_OK)
+        return st;
+    hipError_t e = launch_gather_targets(batch, offsets, num_targets, x, hidden * eb,
+                                         target_offsets, out, ld_out * eb, col_offset * eb,
+                                         capacity, s);
+    if (e != hipSuccess) return hip_fail(e, "target gather kernels");
+    return SLA_OK;
+}
+
 sla_status_t stu_truncate(int32_t batch, int64_t total_tokens, const int64_t *offsets,
                           const int32_t *num_targets, int32_t contextual_len, int32_t tail_len,
                           const void *x, int32_t hidden, int32_t dtype, int64_t *new_offsets,

@@ -139,6 +139,12 @@ hipError_t launch_dsilu_bf16(void *ds, int64_t ldd, const void *z, int64_t ldz, 
                              int cols, hipStream_t st);
 hipError_t launch_transpose_bf16(const void *src, int R, int C, void *dst, hipStream_t st);
 hipError_t launch_fill_f32(float *dst, size_t n, float v, hipStream_t st);
+// target rows of each sequence into rows toffs[b] .. of out, bytes
+// [col_bytes, col_bytes + row_bytes) of each out row; toffs [B+1] written
+hipError_t launch_gather_targets(int B, const int64_t *offsets, const int32_t *num_targets,
+                                 const void *x, int row_bytes, int64_t *toffs, void *out,
+                                 int64_t ld_out_bytes, int64_t col_bytes, int64_t capacity,
+                                 hipStream_t st);
 
 // FP8 projections (stu_fp8.hip): row-wise e4m3 quantisation q = e4m3(x 448 /
 // max|x|), scale = max|x| / 448; cols % 8 == 0, <= 2048

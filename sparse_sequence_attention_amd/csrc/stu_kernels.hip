@@ -235,4 +235,76 @@ hipError_t launch_truncate(int B, int64_t T, const int64_t *offsets, const int32
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// target rows (candidates) of a jagged batch, gathered into a column block of
+// a [total targets][ld_out] output (Mixture of Transducers: each channel's
+// candidate embeddings side by side)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void target_offsets_kernel(int B, const int32_t *num_targets,
+                                                              int64_t *toffs)
+{
+    __shared__ int64_t buf[2][1024];
+    __shared__ int64_t carry;
+    const int tid = threadIdx.x;
+    if (tid == 0) carry = 0;
+    __syncthreads();
+    for (int start = 0; start < B; start += 1024) {
+        const int b = start + tid;
+        const int64_t v = b < B ? (num_targets ? num_targets[b] : 0) : 0;
+        int cur = 0;
+        buf[cur][tid] = v;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {
+            int64_t a = buf[cur][tid];
+            if (tid >= off) a += buf[cur][tid - off];
+            buf[cur ^ 1][tid] = a;
+            cur ^= 1;
+            __syncthreads();
+        }
+        const int64_t c0 = carry;
+        if (b < B) toffs[b] = c0 + buf[cur][tid] - v;
+        __syncthreads();
+        if (tid == 1023) carry = c0 + buf[cur][tid];
+        __syncthreads();
+    }
+    if (tid == 0) toffs[B] = carry;
+}
+
+__global__ __launch_bounds__(256) void gather_targets_kernel(
+    int B, const int64_t *offsets, const int32_t *num_targets, const int64_t *toffs,
+    const uint8_t *x, int row_bytes, uint8_t *out, int64_t ld_out_bytes, int64_t col_bytes,
+    int64_t capacity)
+{
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int64_t total = toffs[B];
+    if (r >= total || r >= capacity) return;
+    int lo = 0, hi = B - 1;  // last b with toffs[b] <= r (sequences without targets skipped)
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (toffs[mid] <= r) lo = mid;
+        else hi = mid - 1;
+    }
+    const int b = lo;
+    const int64_t srow = offsets[b + 1] - num_targets[b] + (r - toffs[b]);
+    const uint8_t *src = x + srow * row_bytes;
+    uint8_t *dst = out + r * ld_out_bytes + col_bytes;
+    for (int e = 16 * lane; e < row_bytes; e += 16 * 64)
+        *reinterpret_cast<uint4 *>(dst + e) = *reinterpret_cast<const uint4 *>(src + e);
+}
+
+hipError_t launch_gather_targets(int B, const int64_t *offsets, const int32_t *num_targets,
+                                 const void *x, int row_bytes, int64_t *toffs, void *out,
+                                 int64_t ld_out_bytes, int64_t col_bytes, int64_t capacity,
+                                 hipStream_t st)
+{
+    hipLaunchKernelGGL(target_offsets_kernel, dim3(1), dim3(1024), 0, st, B, num_targets, toffs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !out || capacity <= 0) return e;
+    hipLaunchKernelGGL(gather_targets_kernel, dim3((unsigned)((capacity + 3) / 4)), dim3(256), 0,
+                       st, B, offsets, num_targets, (const int64_t *)toffs, (const uint8_t *)x,
+                       row_bytes, (uint8_t *)out, ld_out_bytes, col_bytes, capacity);
+    return hipGetLastError();
+}
+
 }  // namespace sla

@@ -407,6 +407,31 @@ def stu_layer_bwd(x: torch.Tensor, dout: torch.Tensor, offsets: torch.Tensor,
     return g
 
 
+def stu_gather_targets(x: torch.Tensor, offsets: torch.Tensor, num_targets: torch.Tensor,
+                       out: Optional[torch.Tensor] = None, col_offset: int = 0,
+                       capacity: Optional[int] = None):
+    """(out, target_offsets): the last num_targets[b] rows of every sequence of
+    x [T, D], in order, written to columns [col_offset, col_offset + D) of out
+    [capacity, W] (allocated [capacity, D] when None; capacity defaults to T)."""
+    if x.dim() != 2 or not x.is_contiguous() or x.dtype not in _DT:
+        raise TypeError("x must be a contiguous bf16 or float32 [T, D] tensor")
+    T, D = x.shape
+    if num_targets is None or num_targets.dtype != torch.int32:
+        raise TypeError("num_targets must be an int32 tensor [B]")
+    B = offsets.numel() - 1
+    cap = T if capacity is None else int(capacity)
+    if out is None:
+        out = torch.empty((cap, D), dtype=x.dtype, device=x.device)
+    if out.dtype != x.dtype or out.dim() != 2 or out.stride(1) != 1:
+        raise TypeError("out must be a row-major [rows, W] tensor of x's dtype")
+    toffs = torch.empty(B + 1, dtype=torch.int64, device=x.device)
+    C.check(C.load().stu_gather_targets(B, T, _ptr(offsets), _ptr(num_targets), _ptr(x), D,
+                                        _DT[x.dtype], _ptr(toffs), _ptr(out), out.stride(0),
+                                        int(col_offset), min(cap, out.shape[0]),
+                                        _stream(x.device)))
+    return out, toffs
+
+
 def stu_truncate(x: Optional[torch.Tensor], offsets: torch.Tensor,
                  num_targets: Optional[torch.Tensor], *, contextual_len: int, tail_len: int,
                  capacity: Optional[int] = None, want_gather: bool = True):

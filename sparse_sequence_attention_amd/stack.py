@@ -86,3 +86,36 @@ def stu_stack_fwd(cfg: STUConfig, layers: List[STULayerWeights], x: torch.Tensor
             out.layer_outputs.append(cur)
     out.x, out.offsets, out.num_targets = cur, offs, tg
     return out
+
+
+@dataclass
+class MoTChannel:
+    """One channel of a Mixture of Transducers: its own STU stack (config,
+    layer weights) over its own jagged sequences [contextual | UIH of this
+    channel | the shared candidates]."""
+    cfg: STUConfig
+    layers: List[STULayerWeights]
+    x: torch.Tensor
+    offsets: torch.Tensor
+
+
+def mot_fwd(channels: List[MoTChannel], num_targets: torch.Tensor, fp8: bool = False):
+    """Mixture of Transducers (ULTRA-HSTU paper, section 4.3 and Appendix A;
+    the torcheasyrec page's MoT bullet): every channel runs its own stack,
+    and the channels' candidate (target) embeddings are concatenated along
+    the feature dimension, channel by channel.  All channels carry the same
+    candidates: num_targets [B] is shared.  Returns (emb [sum of targets,
+    sum of D_c], target_offsets [B+1])."""
+    if not channels:
+        raise ValueError("no channels")
+    outs = [stu_stack_fwd(ch.cfg, ch.layers, ch.x, ch.offsets, num_targets, fp8=fp8)
+            for ch in channels]
+    widths = [int(o.x.shape[1]) for o in outs]
+    cap = int(channels[0].x.shape[0])
+    emb = torch.empty((cap, sum(widths)), dtype=outs[0].x.dtype, device=outs[0].x.device)
+    col, toffs = 0, None
+    for o, w in zip(outs, widths):
+        _, toffs = ops.stu_gather_targets(o.x, o.offsets, o.num_targets, out=emb, col_offset=col)
+        col += w
+    n = int(toffs[-1].item())
+    return emb[:n], toffs
