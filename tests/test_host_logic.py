@@ -277,3 +277,58 @@ def test_stu_config_rules():
     # example: 4 layers, split 2 -> layers 2..3 see the truncated sequence
     t = STUConfig(attn_num_layers=4, attn_truncation_split_layer=2, attn_truncation_tail_len=512)
     assert [t.layer_is_truncated(i) for i in range(4)] == [False, False, True, True]
+
+
+def test_candidate_scoring_argument_errors(lib):
+    p = _problem()
+    cand = FAKE
+
+    def call(p, cand=cand, total=64, k=FAKE, ldq=512, ws=FAKE):
+        return lib.sla_fwd_candidates(ctypes.byref(p), cand, total, k, 512, FAKE, 512, FAKE, ldq,
+                                      FAKE, 512, FAKE, 512, FAKE, 512, ws, 1 << 30, None)
+
+    assert call(_problem(dtype=C.SLA_F32)) == C.SLA_ERR_UNSUPPORTED   # bf16 only
+    pt = _problem()
+    pt.num_targets = 0x30000
+    assert call(pt) == C.SLA_ERR_INVALID                               # history has no targets
+    assert call(p, total=-1) == C.SLA_ERR_INVALID
+    assert call(p, cand=None) == C.SLA_ERR_NULL
+    assert call(p, k=None) == C.SLA_ERR_NULL                           # history keys needed
+    assert call(p, ldq=100) == C.SLA_ERR_INVALID                       # ld < H*d
+    assert call(p, ws=None) == C.SLA_ERR_WORKSPACE
+    assert call(p, total=0) == C.SLA_OK                                # nothing to score
+    # workspace covers the larger of the history and candidate row counts
+    small = lib.sla_fwd_candidates_workspace_size(ctypes.byref(p), 10)
+    big = lib.sla_fwd_candidates_workspace_size(ctypes.byref(p), 100000)
+    assert 0 < small <= big
+
+
+def test_fp8_argument_errors(lib):
+    assert lib.stu_quantize_rows_fp8(FAKE, 4, 24, FAKE, FAKE, None) == C.SLA_ERR_UNSUPPORTED
+    assert lib.stu_quantize_rows_fp8(FAKE, 4, 4096, FAKE, FAKE, None) == C.SLA_ERR_UNSUPPORTED
+    assert lib.stu_quantize_rows_fp8(None, 4, 512, FAKE, FAKE, None) == C.SLA_ERR_NULL
+    assert lib.stu_quantize_rows_fp8(FAKE, -1, 512, FAKE, FAKE, None) == C.SLA_ERR_INVALID
+    assert lib.stu_quantize_rows_fp8(None, 0, 512, None, None, None) == C.SLA_OK
+    d = C.STULayerDesc()
+    d.attn = _problem()
+    d.hidden, d.ln_eps = 512, 1e-5
+    args = [FAKE] * 15
+    args[11] = ctypes.c_void_p(0x40000)                                # out (must not alias x)
+    assert lib.stu_layer_fwd_fp8(ctypes.byref(d), *args, 0, None) == C.SLA_ERR_WORKSPACE
+    nul = list(args)
+    nul[4] = None                                                      # w_uvqk_scale
+    assert lib.stu_layer_fwd_fp8(ctypes.byref(d), *nul, 1 << 30, None) == C.SLA_ERR_NULL
+    d.attn = _problem(heads=1, d=64)                                   # H*d_v = 64
+    assert lib.stu_layer_fwd_fp8(ctypes.byref(d), *args, 1 << 30, None) == C.SLA_ERR_UNSUPPORTED
+
+
+def test_gather_targets_argument_errors(lib):
+    def call(ld=1024, col=0, hidden=512, tg=FAKE, toffs=FAKE, dtype=C.SLA_BF16):
+        return lib.stu_gather_targets(2, 100, FAKE, tg, FAKE, hidden, dtype, toffs, FAKE, ld, col,
+                                      100, None)
+    assert call(toffs=None) == C.SLA_ERR_NULL
+    assert call(tg=None) == C.SLA_ERR_NULL
+    assert call(col=600) == C.SLA_ERR_INVALID                          # past ld_out
+    assert call(hidden=12) == C.SLA_ERR_UNSUPPORTED                    # not 16-byte rows
+    assert call(col=4) == C.SLA_ERR_UNSUPPORTED                        # misaligned column block
+    assert call(dtype=7) == C.SLA_ERR_UNSUPPORTED
