@@ -3,9 +3,9 @@
 // input and weight), fp32 accumulation and a bf16 output.
 //
 // Tile 256 (M) x BN (N) per workgroup of 8 waves (4 x 2, each 64 x BN/2).
-// Operands stream HBM -> LDS by DMA (global_load_lds) through a ring of four
-// stages of 64 bytes of K (32 bf16 or 64 fp8 values) per row, three stages
-// ahead of the one being multiplied, with one barrier per stage; stage rows
+// Operands stream HBM -> LDS by DMA (global_load_lds) through a ring of three
+// or four stages of 64 bytes of K (32 bf16 or 64 fp8 values) per row, the
+// next stages in flight while one is multiplied, one barrier per stage; stage rows
 // are 64 bytes, chunk c of row r stored at c ^ f(r) so that the 16-lane
 // passes of the operand reads hit distinct banks.
 //
@@ -31,7 +31,6 @@ typedef int intx8_t __attribute__((ext_vector_type(8)));
 
 constexpr int GB_M = 256;   // rows of A per tile
 constexpr int GB_RB = 64;   // bytes of K per stage row
-constexpr int GB_NS = 4;    // stages
 constexpr int GB_NT = 512;  // threads
 
 // stage-row swizzle: 16-byte chunk c of row r sits at c ^ gswz(r)
@@ -48,8 +47,10 @@ __device__ __forceinline__ int wperm(int j)
     return 16 * ((j >> 2) & 1) + 4 * (j >> 3) + (j & 3);
 }
 
-template <bool FP8, int BN, int EPI>
-__global__ __launch_bounds__(GB_NT, 1) void gemm_nt_kernel(
+// NS stages (3 or 4); MINB workgroups per CU (2 needs <= 128 VGPRs and
+// 2 x NS x STAGE bytes of LDS)
+template <bool FP8, int BN, int EPI, int NS, int MINB>
+__global__ __launch_bounds__(GB_NT, MINB) void gemm_nt_kernel(
     const uint8_t *A, int64_t lda, const float *sa, const uint8_t *W, int64_t ldw,
     const float *sw, const float *bias, const uint16_t *R, int64_t ldr, uint16_t *C, int64_t ldc,
     uint16_t *Z, int64_t ldz, int64_t M, int N, int Kb)
@@ -59,7 +60,9 @@ __global__ __launch_bounds__(GB_NT, 1) void gemm_nt_kernel(
     constexpr int PER = ROWS / 16 / 8;        // DMA instructions per thread and stage
     constexpr int NBW = BN / 64;              // 32-column fragments per wave
     static_assert(ROWS % 128 == 0, "whole DMA rounds");
-    __shared__ __align__(16) uint8_t st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGE];
+    static_assert(NS == 3 || NS == 4, "three or four stages");
+    __shared__ __align__(16) uint8_t st0[STAGE], st1[STAGE], st2[STAGE];
+    __shared__ __align__(16) uint8_t st3[NS == 4 ? STAGE : 16];
 
     const int ntn = N / BN;
     const int64_t ntm = (M + GB_M - 1) / GB_M;
@@ -158,35 +161,36 @@ __global__ __launch_bounds__(GB_NT, 1) void gemm_nt_kernel(
         }
     };
 
-    // main loop: stage k % 4 holds K step k; steps k+1, k+2 (and, after this
-    // step's issue, k+3) are in flight.  The DMAs are issued unconditionally
-    // (past the last step they reload it into a stage nobody reads any more):
-    // a DMA under a branch makes the compiler wait for all of them at the
-    // merge, which would serialise the ring.
+    // main loop: stage k % NS holds K step k; the next NS - 2 steps (and,
+    // after this step's issue, NS - 1) are in flight.  The DMAs are issued
+    // unconditionally (past the last step they reload it into a stage nobody
+    // reads any more): a DMA under a branch makes the compiler wait for all
+    // of them at the merge, which would serialise the ring.
     const int nk = Kb / GB_RB;
     auto step = [&](int k, auto S) {
         constexpr int s = decltype(S)::value;
-        vm_wait<2 * PER>();  // this thread's stage-k DMAs have landed
-        barrier_lds();       // everyone's have; stage k - 1 is free
-        issue(imin(k + 3, nk - 1), std::integral_constant<int, (s + 3) % 4>{});
+        vm_wait<(NS - 2) * PER>();  // this thread's stage-k DMAs have landed
+        barrier_lds();              // everyone's have; stage k - 1 is free
+        issue(imin(k + NS - 1, nk - 1), std::integral_constant<int, (s + NS - 1) % NS>{});
         compute(S);
     };
     issue(0, std::integral_constant<int, 0>{});
     issue(imin(1, nk - 1), std::integral_constant<int, 1>{});
-    issue(imin(2, nk - 1), std::integral_constant<int, 2>{});
-    // whole groups of four steps without branches (a branch between steps
+    if constexpr (NS == 4) issue(imin(2, nk - 1), std::integral_constant<int, 2>{});
+    // whole groups of NS steps without branches (a branch between steps
     // costs the same conservative wait), then the remainder
-    const int ng = nk / 4;
+    const int ng = nk / NS;
     for (int g = 0; g < ng; ++g) {
-        step(4 * g, std::integral_constant<int, 0>{});
-        step(4 * g + 1, std::integral_constant<int, 1>{});
-        step(4 * g + 2, std::integral_constant<int, 2>{});
-        step(4 * g + 3, std::integral_constant<int, 3>{});
+        step(NS * g, std::integral_constant<int, 0>{});
+        step(NS * g + 1, std::integral_constant<int, 1>{});
+        step(NS * g + 2, std::integral_constant<int, 2>{});
+        if constexpr (NS == 4) step(NS * g + 3, std::integral_constant<int, 3 % NS>{});
     }
-    const int rem = uniform(nk - 4 * ng);
-    if (rem > 0) step(4 * ng, std::integral_constant<int, 0>{});
-    if (rem > 1) step(4 * ng + 1, std::integral_constant<int, 1>{});
-    if (rem > 2) step(4 * ng + 2, std::integral_constant<int, 2>{});
+    const int rem = uniform(nk - NS * ng);
+    if (rem > 0) step(NS * ng, std::integral_constant<int, 0>{});
+    if (rem > 1) step(NS * ng + 1, std::integral_constant<int, 1>{});
+    if constexpr (NS == 4)
+        if (rem > 2) step(NS * ng + 2, std::integral_constant<int, 2>{});
 
     // epilogue: lane holds row m = 64 wm + 32 mb + l32 and, per n fragment,
     // columns 16 hl + 0..15 of its 32.  Every wave stages its own 64 x BN/2
@@ -197,15 +201,16 @@ __global__ __launch_bounds__(GB_NT, 1) void gemm_nt_kernel(
     constexpr int WCOLS = BN / 2;         // columns per wave
     constexpr int CPW = WCOLS / 8;        // 16-byte chunks per block row
     constexpr int SLICE = 64 * CPW * 16;  // bytes per wave
-    static_assert(2 * SLICE <= STAGE, "two wave slices per stage");
+    constexpr int SPS = STAGE / SLICE;  // wave slices per stage
+    static_assert(SPS * NS >= 8, "every wave has a slice");
     uint8_t *slice;
-    switch (wv >> 1) {
+    switch (wv / SPS) {
     case 0: slice = st0; break;
     case 1: slice = st1; break;
     case 2: slice = st2; break;
     default: slice = st3; break;
     }
-    slice += (wv & 1) * SLICE;
+    slice += (wv % SPS) * SLICE;
     auto eswz = [](int r) { return CPW == 16 ? (r & 15) : ((r >> 1) & (CPW - 1)); };
     auto spos = [&](int r, int c) { return slice + r * (CPW * 16) + 16 * (c ^ eswz(r)); };
     vm_wait<0>();
@@ -271,7 +276,7 @@ __global__ __launch_bounds__(GB_NT, 1) void gemm_nt_kernel(
     }
 }
 
-template <bool FP8, int BN>
+template <bool FP8, int BN, int NS, int MINB>
 hipError_t launch_nt(const void *A, int64_t lda, const float *sa, const void *W, int64_t ldw,
                      const float *sw, const float *bias, const void *R, int64_t ldr, void *C,
                      int64_t ldc, void *Z, int64_t ldz, int64_t M, int N, int Kb, int epi,
@@ -283,32 +288,33 @@ hipError_t launch_nt(const void *A, int64_t lda, const float *sa, const void *W,
     (const uint8_t *)A, lda, sa, (const uint8_t *)W, ldw, sw, bias, (const uint16_t *)R, ldr, \
         (uint16_t *)C, ldc, (uint16_t *)Z, ldz, M, N, Kb
     switch (epi) {
-    case 0: hipLaunchKernelGGL((gemm_nt_kernel<FP8, BN, 0>), grid, block, 0, st, GNT_ARGS); break;
-    case 1: hipLaunchKernelGGL((gemm_nt_kernel<FP8, BN, 1>), grid, block, 0, st, GNT_ARGS); break;
-    case 2: hipLaunchKernelGGL((gemm_nt_kernel<FP8, BN, 2>), grid, block, 0, st, GNT_ARGS); break;
-    default: hipLaunchKernelGGL((gemm_nt_kernel<FP8, BN, 3>), grid, block, 0, st, GNT_ARGS); break;
+    case 0: hipLaunchKernelGGL((gemm_nt_kernel<FP8, BN, 0, NS, MINB>), grid, block, 0, st, GNT_ARGS); break;
+    case 1: hipLaunchKernelGGL((gemm_nt_kernel<FP8, BN, 1, NS, MINB>), grid, block, 0, st, GNT_ARGS); break;
+    case 2: hipLaunchKernelGGL((gemm_nt_kernel<FP8, BN, 2, NS, MINB>), grid, block, 0, st, GNT_ARGS); break;
+    default: hipLaunchKernelGGL((gemm_nt_kernel<FP8, BN, 3, NS, MINB>), grid, block, 0, st, GNT_ARGS); break;
     }
 #undef GNT_ARGS
     return hipGetLastError();
 }
 
-// 256-column tiles when they give at least two workgroups per CU (bf16; the
-// FP8 operand fragments take twice the registers, so FP8 stays at 128), else
-// 128
+// bf16: 256 x 128 tiles in a three-stage ring, two workgroups per CU (one
+// workgroup's epilogue runs under the other's products; measured faster than
+// 256 x 256 tiles with one workgroup per CU on every projection shape of the
+// layer).  FP8: the operand fragments take twice the registers, so 256 x 128
+// tiles with four stages and one workgroup per CU.
 template <bool FP8>
 hipError_t launch_nt_any(const void *A, int64_t lda, const float *sa, const void *W, int64_t ldw,
                          const float *sw, const float *bias, const void *R, int64_t ldr, void *C,
                          int64_t ldc, void *Z, int64_t ldz, int64_t M, int N, int Kb, int epi,
                          hipStream_t st)
 {
-    const int64_t mt = (M + GB_M - 1) / GB_M;
     if constexpr (!FP8) {
-        if (N % 256 == 0 && mt * (N / 256) >= 512)
-            return launch_nt<FP8, 256>(A, lda, sa, W, ldw, sw, bias, R, ldr, C, ldc, Z, ldz, M, N,
-                                       Kb, epi, st);
+        return launch_nt<FP8, 128, 3, 2>(A, lda, sa, W, ldw, sw, bias, R, ldr, C, ldc, Z, ldz, M,
+                                         N, Kb, epi, st);
+    } else {
+        return launch_nt<FP8, 128, 4, 1>(A, lda, sa, W, ldw, sw, bias, R, ldr, C, ldc, Z, ldz, M,
+                                         N, Kb, epi, st);
     }
-    return launch_nt<FP8, 128>(A, lda, sa, W, ldw, sw, bias, R, ldr, C, ldc, Z, ldz, M, N, Kb,
-                               epi, st);
 }
 
 }  // namespace
