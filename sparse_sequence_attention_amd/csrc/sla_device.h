@@ -197,6 +197,15 @@ __device__ __forceinline__ void barrier_lds_dma()
     asm volatile("s_barrier" ::: "memory");
 }
 
+// Instruction classes of __builtin_amdgcn_sched_group_barrier (LLVM AMDGPU
+// IGroupLP masks): a sequence of (class, count) groups in one basic block
+// asks the scheduler to emit that many instructions of each class in that
+// order, which interleaves independent MFMA and VALU work of one wave.
+constexpr int SG_VALU = 0x002 | 0x400;  // vector ALU, transcendentals included
+constexpr int SG_MFMA = 0x008;
+constexpr int SG_VMEM_READ = 0x020;     // global loads, DMA into LDS included
+constexpr int SG_DS_READ = 0x100;
+
 // Workgroup barrier that publishes this wave's LDS writes (and waits for its
 // LDS reads) but leaves global loads and stores, including DMA into other
 // LDS buffers, in flight; __syncthreads' fence would wait for those too.

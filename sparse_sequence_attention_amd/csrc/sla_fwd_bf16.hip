@@ -204,23 +204,25 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
         // Target rows see the same history keys (those of the first target
         // slot), so a history tile wholly inside that view needs no mask
         // either; the diagonal and boundary tiles do.
-        const bool full = uniform(((r0 < sd.U) && (c0 + BN <= sd.L) && (c0 + BN - 1 <= r0) &&
-                                   ((r1 - 1 - c0 < p.k1) || (c0 + BN <= p.k2e))) ||
-                                  ((r0 >= sd.U) && (c0 + BN <= sd.U) &&
-                                   ((c0 >= sd.U - p.k1 + 1) || (c0 + BN <= p.k2e)))) != 0;
+        // bitwise, not short-circuit: no branch between the DMA issue and
+        // the products
+        const bool full = uniform(((r0 < sd.U) & (c0 + BN <= sd.L) & (c0 + BN - 1 <= r0) &
+                                   ((r1 - 1 - c0 < p.k1) | (c0 + BN <= p.k2e))) |
+                                  ((r0 >= sd.U) & (c0 + BN <= sd.U) &
+                                   ((c0 >= sd.U - p.k1 + 1) | (c0 + BN <= p.k2e)))) != 0;
         const int x0 = qi - c0 - 4 * hl;
         const int mode = uniform(r0 >= sd.U ? 0 : (c0 >= p.k2e ? 1 : (c0 + BN <= p.k2e ? 2 : 0)));
 
-        // per 32-key block: S^T = K Q^T, mask, P = s * sigmoid(alpha s), then
-        // O^T += V^T P^T over its two 16-key chunks; one block's S is live at a time
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            floatx16 sacc = zero16();
+        auto s_blk = [&](int kb) {
+            floatx16 acc = zero16();
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sk + k_off(kb, c));
-                sacc = mfma32(a, qb[c], sacc);
+                acc = mfma32(a, qb[c], acc);
             }
+            return acc;
+        };
+        auto mask_blk = [&](float *sacc, int kb) {
             if (!full) {
                 if (mode == 1) {
 #pragma unroll
@@ -242,25 +244,61 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
                     }
                 }
             }
+        };
+        auto silu_blk = [&](const floatx16 &sacc, float *f) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float sv = sacc[r];
-                sacc[r] = sv * sigmoid_fast(sv, nal2e);
+                f[r] = sv * sigmoid_fast(sv, nal2e);
             }
+        };
+        auto pv_blk = [&](int kb, const float *f) {
+            const halfx8 p0 = cvt8h(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
+            const halfx8 p1 = cvt8h(f[8], f[9], f[10], f[11], f[12], f[13], f[14], f[15]);
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
-                const int o = 8 * h2;
-                const halfx8 pb = cvt8h(sacc[o + 0], sacc[o + 1], sacc[o + 2], sacc[o + 3],
-                                        sacc[o + 4], sacc[o + 5], sacc[o + 6], sacc[o + 7]);
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
                     const uint2 v0 = tr_read_b64(sv + v_off(kb, h2, 0, db));
                     const uint2 v1 = tr_read_b64(sv + v_off(kb, h2, 1, db));
                     oacc[db] = mfma32h(__builtin_bit_cast(halfx8, make_uint4(v0.x, v0.y, v1.x, v1.y)),
-                                       pb, oacc[db]);
+                                       h2 ? p1 : p0, oacc[db]);
                 }
             }
+        };
+        // The two 32-key blocks run software-pipelined in one wave: block 1's
+        // S^T products under block 0's SiLU, block 0's P.V products under
+        // block 1's SiLU (the MFMA pipe and the VALU work concurrently on
+        // independent instructions of one wave).  The mask zeroes P after
+        // the SiLU (SiLU(0) = 0), so no branch splits a block's products
+        // from the other block's SiLU; the next tile's DMA is spread over
+        // block 0's products instead of leaving in one burst after the
+        // barrier.  Per step: 16 S^T and 16 P.V MFMAs, 2 x 16 SiLU.
+        floatx16 sa = s_blk(0);
+        floatx16 sb = s_blk(1);
+        float fa[16], fb[16];
+        silu_blk(sa, fa);
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * NC; ++i) {
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+            if (i < 2 * NC - 2) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+            if (i < NC) __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
+            else __builtin_amdgcn_sched_group_barrier(SG_VALU, 10, 0);
         }
+        mask_blk(fa, 0);
+        pv_blk(0, fa);
+        silu_blk(sb, fb);
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 1);
+        __builtin_amdgcn_sched_group_barrier(SG_VALU, 8, 1);
+#pragma unroll
+        for (int i = 0; i < 2 * NDB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 1);
+            if (i < 2 * NDB - 2) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 1);
+            __builtin_amdgcn_sched_group_barrier(SG_VALU, 10, 1);
+        }
+        mask_blk(fb, 1);
+        pv_blk(1, fb);
         // the next stage: wait for its DMA (issued at the top of this step)
         // explicitly, then convert it.  After the last step this re-converts
         // a stage nobody reads.
