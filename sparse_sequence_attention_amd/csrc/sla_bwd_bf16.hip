@@ -280,13 +280,13 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
         // P = s sigma (= SiLU(t) / alpha) and G dS = G g sigma (1 + t (1 - sigma))
         // = G g (sigma + a * (alpha - alpha sigma)).  exp(-t) overflowing to
         // inf gives sigma = 0, a = 0 and dS = 0, its limit, with no NaN.
+        float sgv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float sv = sacc[r], g = pacc[r];
+            const float sv = sacc[r];
             const float sgm = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sv * nal2e));
-            const float a = sv * sgm;
-            sacc[r] = a;
-            pacc[r] = g * fmaf(a, fmaf(-alpha, sgm, alpha), sgm);
+            sgv[r] = sgm;
+            sacc[r] = sv * sgm;
         }
         halfx8 pa[2], da[2];
 #pragma unroll
@@ -294,6 +294,13 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
             const int o = 8 * h2;
             pa[h2] = cvt8h(sacc[o], sacc[o + 1], sacc[o + 2], sacc[o + 3], sacc[o + 4], sacc[o + 5],
                            sacc[o + 6], sacc[o + 7]);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            pacc[r] = pacc[r] * fmaf(sacc[r], fmaf(-alpha, sgv[r], alpha), sgv[r]);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int o = 8 * h2;
             da[h2] = cvt8h(pacc[o], pacc[o + 1], pacc[o + 2], pacc[o + 3], pacc[o + 4], pacc[o + 5],
                            pacc[o + 6], pacc[o + 7]);
         }
@@ -308,11 +315,33 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
                 const uint2 g1 = tr_read_b64(sg + t_off(h2, 1, db));
                 dvacc[db] = mfma32h(pa[h2], __builtin_bit_cast(halfx8, make_uint4(g0.x, g0.y, g1.x, g1.y)),
                                     dvacc[db]);
+            }
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
                 const uint2 q0 = tr_read_b64(sq + t_off(h2, 0, db));
                 const uint2 q1 = tr_read_b64(sq + t_off(h2, 1, db));
                 dkacc[db] = mfma32h(da[h2], __builtin_bit_cast(halfx8, make_uint4(q0.x, q0.y, q1.x, q1.y)),
                                     dkacc[db]);
             }
+        }
+        // schedule: P first (5 VALU per element and its conversion), then
+        // the dV products with dS (3 VALU per element) issued between them,
+        // so that the MFMA pipe and the VALU work at the same time, then dK
+        __builtin_amdgcn_sched_group_barrier(SG_VALU, 88, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * NDB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_VALU, 7, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 2 * NDB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+            if (i < 2 * NDB - 2) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
         }
         // the next stage (its DMA was issued at the top of this step) while
         // the products run, then this step's dS stores: the next wait, a step
