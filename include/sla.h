@@ -243,7 +243,8 @@ sla_status_t sla_fwd_candidates(const sla_problem_t *p, const int64_t *cand_offs
  *   out  = y W2^T (+ b_out) + x                           residual fused in the epilogue
  * x, out: [T][D] bf16 contiguous (out may not alias x); w_uvqk: [2*H*d_v +
  * 2*H*d_qk][D] bf16 (out-features major, as a Linear weight); w_out:
- * [D][H*d_v] bf16; ln*_w, ln*_b, b_*: fp32 vectors; biases nullable.
+ * [D][H*d_v] bf16; ln*_w, ln*_b, b_*: fp32 vectors (ln*_w and ln*_b
+ * 16-byte aligned, as every bf16 buffer); biases nullable.
  * uvqk_out (nullable): [T][2*H*d_v + 2*H*d_qk] bf16 copy of U|V|Q|K; the
  * layer keeps it in the workspace otherwise.  attn_out (nullable): [T][H*d_v]
  * bf16 copy of A, the activation stu_layer_bwd takes instead of recomputing

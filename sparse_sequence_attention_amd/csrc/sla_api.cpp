@@ -604,7 +604,8 @@ sla_status_t stu_layer_fwd(const stu_layer_desc_t *d, const void *x, const float
     if (!(d->ln_eps > 0.0f) || !std::isfinite(d->ln_eps))
         return fail(SLA_ERR_INVALID, "ln_eps must be positive");
     if (out == x) return fail(SLA_ERR_INVALID, "out must not alias x");
-    const void *ptrs[] = {x, w_uvqk, w_out, out, uvqk_out, attn_out, workspace};
+    const void *ptrs[] = {x, w_uvqk, w_out, out, uvqk_out, attn_out, workspace,
+                          ln1_w, ln1_b, ln2_w, ln2_b};
     for (const void *q : ptrs)
         if (q && !aligned16(q)) return fail(SLA_ERR_UNSUPPORTED, "a layer buffer is not 16-byte aligned");
     const size_t need = stu_layer_workspace_size(d);
@@ -681,7 +682,7 @@ sla_status_t stu_layer_bwd(const stu_layer_desc_t *d, const void *x, const void 
         return fail(SLA_ERR_INVALID, "ln_eps must be positive");
     if (dx && (dx == x || dx == dout || dx == attn))
         return fail(SLA_ERR_INVALID, "dx must not alias an input");
-    const void *ptrs[] = {x, attn, w_uvqk, w_out, dout, dx, workspace};
+    const void *ptrs[] = {x, attn, w_uvqk, w_out, dout, dx, workspace, ln1_w, ln1_b, ln2_w, ln2_b};
     for (const void *q : ptrs)
         if (q && !aligned16(q)) return fail(SLA_ERR_UNSUPPORTED, "a layer buffer is not 16-byte aligned");
     const StuBwdLayout L = stu_bwd_layout(d);
@@ -842,7 +843,8 @@ sla_status_t stu_layer_fwd_fp8(const stu_layer_desc_t *d, const void *x, const f
     if (!(d->ln_eps > 0.0f) || !std::isfinite(d->ln_eps))
         return fail(SLA_ERR_INVALID, "ln_eps must be positive");
     if (out == x) return fail(SLA_ERR_INVALID, "out must not alias x");
-    const void *ptrs[] = {x, w_uvqk_q, w_out_q, out, uvqk_out, attn_out, workspace};
+    const void *ptrs[] = {x, w_uvqk_q, w_out_q, out, uvqk_out, attn_out, workspace,
+                          ln1_w, ln1_b, ln2_w, ln2_b};
     for (const void *q : ptrs)
         if (q && !aligned16(q)) return fail(SLA_ERR_UNSUPPORTED, "a layer buffer is not 16-byte aligned");
     const size_t need = stu_layer_fp8_workspace_size(d);

@@ -14,7 +14,7 @@
 namespace sla {
 
 // ---------------------------------------------------------------------------
-// LayerNorm: one wave per row, up to 4 x 512 columns
+// LayerNorm: a wave per row (two rows for up to 512 columns), up to 2048 columns
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float wave_sum(float x)
 {
@@ -23,96 +23,140 @@ __device__ __forceinline__ float wave_sum(float x)
     return x;
 }
 
-template <bool GATED>
+// Each wave normalises RPW rows of up to 512 * NCH columns; every load of a
+// row (x, the gate u, the weight and bias) is issued before the reductions,
+// so a wave waits for memory once.  Lane l holds the 16-byte chunks l,
+// l + 64, ... of a row.
+template <bool GATED, int NCH, int RPW>
 __global__ __launch_bounds__(256) void layernorm_bf16_kernel(const uint16_t *x, int64_t ldx,
                                                              const uint16_t *u, int64_t ldu,
                                                              const float *w, const float *bias,
                                                              uint16_t *y, int64_t ldy,
                                                              int64_t rows, int cols, float eps)
 {
-    constexpr int MAXC = 4;  // chunks of 8 per lane: cols <= 64 * 8 * 4
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;
+    const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW;
+    if (row0 >= rows) return;
     const int nchunk = cols / 8;
-    float v[MAXC][8];
-    float s = 0.0f;
+    uint4 xr[RPW][NCH], ur[RPW][NCH];
+    float4 wv[NCH][2], bv[NCH][2];
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
+    for (int c = 0; c < NCH; ++c) {
         const int ch = lane + 64 * c;
         if (ch < nchunk) {
-            uint4 raw = ld16(x + row * ldx + 8 * ch);
-            uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                v[c][2 * e] = bf16_lo(wd[e]);
-                v[c][2 * e + 1] = bf16_hi(wd[e]);
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s += v[c][e];
-        }
-    }
-    const float mean = wave_sum(s) / (float)cols;
-    float q = 0.0f;
-#pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
-        if (lane + 64 * c < nchunk) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float d = v[c][e] - mean;
-                q += d * d;
-            }
-        }
-    }
-    const float rstd = rsqrtf(wave_sum(q) / (float)cols + eps);
-#pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
-        const int ch = lane + 64 * c;
-        if (ch < nchunk) {
-            float o[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int col = 8 * ch + e;
-                o[e] = (v[c][e] - mean) * rstd * w[col] + (bias ? bias[col] : 0.0f);
-            }
-            if (GATED) {
-                uint4 ur = ld16(u + row * ldu + 8 * ch);
-                uint32_t uw[4] = {ur.x, ur.y, ur.z, ur.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    o[2 * e] *= bf16_lo(uw[e]);
-                    o[2 * e + 1] *= bf16_hi(uw[e]);
+            for (int k = 0; k < RPW; ++k) {
+                if (row0 + k < rows) {
+                    xr[k][c] = ld16(x + (row0 + k) * ldx + 8 * ch);
+                    if (GATED) ur[k][c] = ld16(u + (row0 + k) * ldu + 8 * ch);
                 }
             }
-            uint2 lo = cvt4_u2(o[0], o[1], o[2], o[3]);
-            uint2 hi = cvt4_u2(o[4], o[5], o[6], o[7]);
-            uint4 outv = {lo.x, lo.y, hi.x, hi.y};
-            *reinterpret_cast<uint4 *>(y + row * ldy + 8 * ch) = outv;
+            wv[c][0] = *reinterpret_cast<const float4 *>(w + 8 * ch);
+            wv[c][1] = *reinterpret_cast<const float4 *>(w + 8 * ch + 4);
+            if (bias) {
+                bv[c][0] = *reinterpret_cast<const float4 *>(bias + 8 * ch);
+                bv[c][1] = *reinterpret_cast<const float4 *>(bias + 8 * ch + 4);
+            } else {
+                bv[c][0] = bv[c][1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
         }
     }
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) {
+        const int64_t row = row0 + k;
+        if (row >= rows) break;
+        float v[NCH][8];
+        float s = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            if (lane + 64 * c < nchunk) {
+                const uint32_t wd[4] = {xr[k][c].x, xr[k][c].y, xr[k][c].z, xr[k][c].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[c][2 * e] = bf16_lo(wd[e]);
+                    v[c][2 * e + 1] = bf16_hi(wd[e]);
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s += v[c][e];
+            }
+        }
+        const float mean = wave_sum(s) / (float)cols;
+        float q = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            if (lane + 64 * c < nchunk) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float d = v[c][e] - mean;
+                    q += d * d;
+                }
+            }
+        }
+        const float rstd = rsqrtf(wave_sum(q) / (float)cols + eps);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int ch = lane + 64 * c;
+            if (ch < nchunk) {
+                const float wf[8] = {wv[c][0].x, wv[c][0].y, wv[c][0].z, wv[c][0].w,
+                                     wv[c][1].x, wv[c][1].y, wv[c][1].z, wv[c][1].w};
+                const float bf[8] = {bv[c][0].x, bv[c][0].y, bv[c][0].z, bv[c][0].w,
+                                     bv[c][1].x, bv[c][1].y, bv[c][1].z, bv[c][1].w};
+                float o[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] = (v[c][e] - mean) * rstd * wf[e] + bf[e];
+                if (GATED) {
+                    const uint32_t uw[4] = {ur[k][c].x, ur[k][c].y, ur[k][c].z, ur[k][c].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        o[2 * e] *= bf16_lo(uw[e]);
+                        o[2 * e + 1] *= bf16_hi(uw[e]);
+                    }
+                }
+                const uint2 lo = cvt4_u2(o[0], o[1], o[2], o[3]);
+                const uint2 hi = cvt4_u2(o[4], o[5], o[6], o[7]);
+                *reinterpret_cast<uint4 *>(y + row * ldy + 8 * ch) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            }
+        }
+    }
+}
+
+// cols % 8 == 0 and cols <= 2048 (checked by the callers)
+template <bool GATED>
+static hipError_t launch_ln(const uint16_t *x, int64_t ldx, const uint16_t *u, int64_t ldu,
+                            const float *w, const float *b, uint16_t *y, int64_t ldy, int64_t rows,
+                            int cols, float eps, hipStream_t st)
+{
+    if (rows <= 0) return hipSuccess;
+    if (cols % 8 != 0 || cols > 2048) return hipErrorInvalidValue;
+    const dim3 block(256);
+    if (cols <= 512) {
+        constexpr int RPW = 2;
+        hipLaunchKernelGGL((layernorm_bf16_kernel<GATED, 1, RPW>),
+                           dim3((unsigned)((rows + 4 * RPW - 1) / (4 * RPW))), block, 0, st, x, ldx,
+                           u, ldu, w, b, y, ldy, rows, cols, eps);
+    } else if (cols <= 1024) {
+        hipLaunchKernelGGL((layernorm_bf16_kernel<GATED, 2, 1>), dim3((unsigned)((rows + 3) / 4)),
+                           block, 0, st, x, ldx, u, ldu, w, b, y, ldy, rows, cols, eps);
+    } else {
+        hipLaunchKernelGGL((layernorm_bf16_kernel<GATED, 4, 1>), dim3((unsigned)((rows + 3) / 4)),
+                           block, 0, st, x, ldx, u, ldu, w, b, y, ldy, rows, cols, eps);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_layernorm_bf16(const void *x, const float *w, const float *b, void *y,
                                  int64_t rows, int cols, float eps, hipStream_t st)
 {
-    if (rows <= 0) return hipSuccess;
-    dim3 grid((unsigned)((rows + 3) / 4)), block(256);
-    hipLaunchKernelGGL(layernorm_bf16_kernel<false>, grid, block, 0, st,
-                       (const uint16_t *)x, (int64_t)cols, (const uint16_t *)nullptr, (int64_t)0,
-                       w, b, (uint16_t *)y, (int64_t)cols, rows, cols, eps);
-    return hipGetLastError();
+    return launch_ln<false>((const uint16_t *)x, (int64_t)cols, nullptr, 0, w, b, (uint16_t *)y,
+                            (int64_t)cols, rows, cols, eps, st);
 }
 
 hipError_t launch_gated_layernorm_bf16(const void *a, int64_t lda, const void *u, int64_t ldu,
                                        const float *w, const float *b, void *y, int64_t rows,
                                        int cols, float eps, hipStream_t st)
 {
-    if (rows <= 0) return hipSuccess;
-    dim3 grid((unsigned)((rows + 3) / 4)), block(256);
-    hipLaunchKernelGGL(layernorm_bf16_kernel<true>, grid, block, 0, st, (const uint16_t *)a, lda,
-                       (const uint16_t *)u, ldu, w, b, (uint16_t *)y, (int64_t)cols, rows, cols,
-                       eps);
-    return hipGetLastError();
+    return launch_ln<true>((const uint16_t *)a, lda, (const uint16_t *)u, ldu, w, b, (uint16_t *)y,
+                           (int64_t)cols, rows, cols, eps, st);
 }
 
 // ---------------------------------------------------------------------------
