@@ -342,6 +342,8 @@ hipError_t launch_colsum_bf16(const void *X, int64_t ld, int64_t T, int C, float
 //           g = dyh * w;                 dx = rstd (g - mean g - xh mean(g xh))
 //           partial_w += dyh * xh,       partial_b += dyh
 // Rows of up to 64 x 8 x 4 = 2048 columns; each lane owns 8-column chunks.
+// A wave issues all loads of its next row before the arithmetic of the
+// current one, and reads the weight (and bias) chunks once.
 // ---------------------------------------------------------------------------
 constexpr int LN_ROWS = 16;
 
@@ -360,31 +362,60 @@ __device__ __forceinline__ uint4 pack8(const float *f)
     return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
-template <bool GATED>
+template <bool GATED, int NCH>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(
     const uint16_t *x, int64_t ldx, const uint16_t *dy, int64_t lddy, const uint16_t *u,
     int64_t ldu, const float *w, const float *b, const uint16_t *res, int64_t ldres, uint16_t *dx,
     int64_t lddx, uint16_t *du, int64_t lddu, uint16_t *y, int64_t ldy, float *part_w,
     float *part_b, int64_t rows, int cols, float eps)
 {
-    constexpr int MAXC = 4;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int nchunk = cols / 8;
-    float pw[MAXC][8], pb[MAXC][8];
+    float pw[NCH][8], pb[NCH][8], wf[NCH][8], bf[NCH][8];
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c)
+    for (int c = 0; c < NCH; ++c) {
+        const int ch = lane + 64 * c;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pw[c][e] = pb[c][e] = 0.0f;
-
-    const int64_t r0 = (int64_t)blockIdx.x * LN_ROWS;
-    for (int64_t row = r0 + wv; row < r0 + LN_ROWS && row < rows; row += 4) {
-        float xv[MAXC][8], gv[MAXC][8];
-        float s = 0.0f;
+        for (int e = 0; e < 8; ++e) pw[c][e] = pb[c][e] = wf[c][e] = bf[c][e] = 0.0f;
+        if (ch < nchunk) {
 #pragma unroll
-        for (int c = 0; c < MAXC; ++c) {
+            for (int e = 0; e < 8; ++e) {
+                wf[c][e] = w[8 * ch + e];
+                if (GATED && b) bf[c][e] = b[8 * ch + e];
+            }
+        }
+    }
+    // the loads of a row, issued together; the next row's are issued before
+    // this row's arithmetic
+    struct RowIn {
+        uint4 x[NCH], dy[NCH], u[NCH], res[NCH];
+    };
+    auto load = [&](int64_t row, RowIn &in) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
             const int ch = lane + 64 * c;
             if (ch < nchunk) {
-                unpack8(ld16(x + row * ldx + 8 * ch), xv[c]);
+                in.x[c] = ld16(x + row * ldx + 8 * ch);
+                in.dy[c] = ld16(dy + row * lddy + 8 * ch);
+                if (GATED) in.u[c] = ld16(u + row * ldu + 8 * ch);
+                if (!GATED && res) in.res[c] = ld16(res + row * ldres + 8 * ch);
+            }
+        }
+    };
+
+    const int64_t r0 = (int64_t)blockIdx.x * LN_ROWS;
+    const int64_t rend = r0 + LN_ROWS < rows ? r0 + LN_ROWS : rows;
+    int64_t row = r0 + wv;
+    RowIn cur, nxt;
+    if (row < rend) load(row, cur);
+    for (; row < rend; row += 4) {
+        if (row + 4 < rend) load(row + 4, nxt);
+        float xv[NCH][8], gv[NCH][8];
+        float s = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            if (lane + 64 * c < nchunk) {
+                unpack8(cur.x[c], xv[c]);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) s += xv[c][e];
             }
@@ -392,7 +423,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
         const float mean = wave_sum_b(s) / (float)cols;
         float q = 0.0f;
 #pragma unroll
-        for (int c = 0; c < MAXC; ++c)
+        for (int c = 0; c < NCH; ++c)
             if (lane + 64 * c < nchunk)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -403,30 +434,29 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
         // xh, the upstream gradient of the normalised affine output, g
         float m1 = 0.0f, m2 = 0.0f;
 #pragma unroll
-        for (int c = 0; c < MAXC; ++c) {
+        for (int c = 0; c < NCH; ++c) {
             const int ch = lane + 64 * c;
             if (ch < nchunk) {
                 float dv[8];
-                unpack8(ld16(dy + row * lddy + 8 * ch), dv);
+                unpack8(cur.dy[c], dv);
                 float uv[8];
-                if (GATED) unpack8(ld16(u + row * ldu + 8 * ch), uv);
+                if (GATED) unpack8(cur.u[c], uv);
                 float duv[8], yv[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const int col = 8 * ch + e;
                     const float xh = (xv[c][e] - mean) * rstd;
                     xv[c][e] = xh;
                     float dyh = dv[e];
                     if (GATED) {
                         // same expression as the forward's gated LayerNorm
-                        const float yh = xh * w[col] + (b ? b[col] : 0.0f);
+                        const float yh = xh * wf[c][e] + bf[c][e];
                         yv[e] = yh * uv[e];
                         duv[e] = dv[e] * yh;
                         dyh = dv[e] * uv[e];
                     }
                     pw[c][e] += dyh * xh;
                     pb[c][e] += dyh;
-                    const float g = dyh * w[col];
+                    const float g = dyh * wf[c][e];
                     gv[c][e] = g;
                     m1 += g;
                     m2 += g * xh;
@@ -440,7 +470,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
         m1 = wave_sum_b(m1) / (float)cols;
         m2 = wave_sum_b(m2) / (float)cols;
 #pragma unroll
-        for (int c = 0; c < MAXC; ++c) {
+        for (int c = 0; c < NCH; ++c) {
             const int ch = lane + 64 * c;
             if (ch < nchunk) {
                 float o[8];
@@ -448,18 +478,19 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
                 for (int e = 0; e < 8; ++e) o[e] = rstd * (gv[c][e] - m1 - xv[c][e] * m2);
                 if (!GATED && res) {
                     float rv[8];
-                    unpack8(ld16(res + row * ldres + 8 * ch), rv);
+                    unpack8(cur.res[c], rv);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) o[e] += rv[e];
                 }
                 *reinterpret_cast<uint4 *>(dx + row * lddx + 8 * ch) = pack8(o);
             }
         }
+        cur = nxt;
     }
     // column partials of this block: the four waves' sums added in wave order
     __shared__ float red[4][2][64 * 8];
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
+    for (int c = 0; c < NCH; ++c) {
         const int ch = lane + 64 * c;
         if (c > 0) __syncthreads();
 #pragma unroll
@@ -497,20 +528,21 @@ hipError_t launch_ln_bwd_bf16(bool gated, const void *x, int64_t ldx, const void
     const int nb = ln_bwd_blocks(rows);
     if (nb == 0) return hipSuccess;
     if (cols % 8 != 0 || cols > 2048) return hipErrorInvalidValue;
-    if (gated)
-        hipLaunchKernelGGL(ln_bwd_kernel<true>, dim3((unsigned)nb), dim3(256), 0, st,
-                           (const uint16_t *)x, ldx, (const uint16_t *)dy, lddy,
-                           (const uint16_t *)u, ldu, w, b, (const uint16_t *)res, ldres,
-                           (uint16_t *)dx, lddx, (uint16_t *)du, lddu, (uint16_t *)y, ldy, part_w,
-                           part_b, rows, cols,
-                           eps);
-    else
-        hipLaunchKernelGGL(ln_bwd_kernel<false>, dim3((unsigned)nb), dim3(256), 0, st,
-                           (const uint16_t *)x, ldx, (const uint16_t *)dy, lddy,
-                           (const uint16_t *)u, ldu, w, b, (const uint16_t *)res, ldres,
-                           (uint16_t *)dx, lddx, (uint16_t *)du, lddu, (uint16_t *)y, ldy, part_w,
-                           part_b, rows, cols,
-                           eps);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(256), 0, st, (const uint16_t *)x, ldx,
+                           (const uint16_t *)dy, lddy, (const uint16_t *)u, ldu, w, b,
+                           (const uint16_t *)res, ldres, (uint16_t *)dx, lddx, (uint16_t *)du,
+                           lddu, (uint16_t *)y, ldy, part_w, part_b, rows, cols, eps);
+    };
+    if (gated) {
+        if (cols <= 512) go(ln_bwd_kernel<true, 1>);
+        else if (cols <= 1024) go(ln_bwd_kernel<true, 2>);
+        else go(ln_bwd_kernel<true, 4>);
+    } else {
+        if (cols <= 512) go(ln_bwd_kernel<false, 1>);
+        else if (cols <= 1024) go(ln_bwd_kernel<false, 2>);
+        else go(ln_bwd_kernel<false, 4>);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = sum_splits(part_w, (int64_t)cols, nb, dw, mid, st);
