@@ -107,27 +107,45 @@ hipError_t launch_quant_rows_fp8(const void *x, int64_t ldx, int64_t rows, int c
 // ---------------------------------------------------------------------------
 // LayerNorm (gated: (LN(a) w + b) (.) u) of a bf16 row, quantised: one wave
 // per row; writes q [rows][cols] e4m3 and scale [rows].  Same statistics as
-// the bf16 LayerNorm kernels (fp32, biased variance, two passes).
+// the bf16 LayerNorm kernels (fp32, biased variance, two passes).  Every
+// load of the row (x, the gate u, weight and bias) is issued before the
+// reductions; lane l holds the 16-byte chunks l, l + 64, ... (NCH of them).
 // ---------------------------------------------------------------------------
-template <bool GATED>
+template <bool GATED, int NCH>
 __global__ __launch_bounds__(256) void ln_quant_fp8_kernel(const uint16_t *x, int64_t ldx,
                                                            const uint16_t *u, int64_t ldu,
                                                            const float *w, const float *bias,
                                                            uint8_t *q, float *scale, int64_t rows,
                                                            int cols, float eps)
 {
-    constexpr int MAXC = 4;
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
     const int nchunk = cols / 8;
-    float v[MAXC][8];
-    float s = 0.0f;
+    uint4 xr[NCH], ur[NCH];
+    float4 wv[NCH][2], bv[NCH][2];
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
+    for (int c = 0; c < NCH; ++c) {
         const int ch = lane + 64 * c;
         if (ch < nchunk) {
-            bf16x8_to_f(ld16(x + row * ldx + 8 * ch), v[c]);
+            xr[c] = ld16(x + row * ldx + 8 * ch);
+            if (GATED) ur[c] = ld16(u + row * ldu + 8 * ch);
+            wv[c][0] = *reinterpret_cast<const float4 *>(w + 8 * ch);
+            wv[c][1] = *reinterpret_cast<const float4 *>(w + 8 * ch + 4);
+            if (bias) {
+                bv[c][0] = *reinterpret_cast<const float4 *>(bias + 8 * ch);
+                bv[c][1] = *reinterpret_cast<const float4 *>(bias + 8 * ch + 4);
+            } else {
+                bv[c][0] = bv[c][1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
+        }
+    }
+    float v[NCH][8];
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        if (lane + 64 * c < nchunk) {
+            bf16x8_to_f(xr[c], v[c]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) s += v[c][e];
         }
@@ -135,7 +153,7 @@ __global__ __launch_bounds__(256) void ln_quant_fp8_kernel(const uint16_t *x, in
     const float mean = wave_sum_f(s) / (float)cols;
     float qs = 0.0f;
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c)
+    for (int c = 0; c < NCH; ++c)
         if (lane + 64 * c < nchunk)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -145,15 +163,18 @@ __global__ __launch_bounds__(256) void ln_quant_fp8_kernel(const uint16_t *x, in
     const float rstd = rsqrtf(wave_sum_f(qs) / (float)cols + eps);
     float a = 0.0f;
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
+    for (int c = 0; c < NCH; ++c) {
         const int ch = lane + 64 * c;
         if (ch < nchunk) {
             float uv[8];
-            if (GATED) bf16x8_to_f(ld16(u + row * ldu + 8 * ch), uv);
+            if (GATED) bf16x8_to_f(ur[c], uv);
+            const float wf[8] = {wv[c][0].x, wv[c][0].y, wv[c][0].z, wv[c][0].w,
+                                 wv[c][1].x, wv[c][1].y, wv[c][1].z, wv[c][1].w};
+            const float bf[8] = {bv[c][0].x, bv[c][0].y, bv[c][0].z, bv[c][0].w,
+                                 bv[c][1].x, bv[c][1].y, bv[c][1].z, bv[c][1].w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int col = 8 * ch + e;
-                float o = (v[c][e] - mean) * rstd * w[col] + (bias ? bias[col] : 0.0f);
+                float o = (v[c][e] - mean) * rstd * wf[e] + bf[e];
                 if (GATED) o *= uv[e];
                 v[c][e] = o;
                 a = fmaxf(a, fabsf(o));
@@ -163,7 +184,7 @@ __global__ __launch_bounds__(256) void ln_quant_fp8_kernel(const uint16_t *x, in
     a = wave_max_f(a);
     const float inv = a > 0.0f ? 448.0f / a : 0.0f;
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
+    for (int c = 0; c < NCH; ++c) {
         const int ch = lane + 64 * c;
         if (ch < nchunk)
             *reinterpret_cast<uint2 *>(q + row * cols + 8 * ch) = to_e4m3x8(v[c], inv);
@@ -178,13 +199,19 @@ hipError_t launch_ln_quant_fp8(bool gated, const void *x, int64_t ldx, const voi
     if (rows <= 0) return hipSuccess;
     if (cols % 8 != 0 || cols > 2048) return hipErrorInvalidValue;
     dim3 grid((unsigned)((rows + 3) / 4)), block(256);
-    if (gated)
-        hipLaunchKernelGGL(ln_quant_fp8_kernel<true>, grid, block, 0, st, (const uint16_t *)x, ldx,
-                           (const uint16_t *)u, ldu, w, b, (uint8_t *)q, scale, rows, cols, eps);
-    else
-        hipLaunchKernelGGL(ln_quant_fp8_kernel<false>, grid, block, 0, st, (const uint16_t *)x,
-                           ldx, (const uint16_t *)u, ldu, w, b, (uint8_t *)q, scale, rows, cols,
-                           eps);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, block, 0, st, (const uint16_t *)x, ldx, (const uint16_t *)u,
+                           ldu, w, b, (uint8_t *)q, scale, rows, cols, eps);
+    };
+    if (gated) {
+        if (cols <= 512) go(ln_quant_fp8_kernel<true, 1>);
+        else if (cols <= 1024) go(ln_quant_fp8_kernel<true, 2>);
+        else go(ln_quant_fp8_kernel<true, 4>);
+    } else {
+        if (cols <= 512) go(ln_quant_fp8_kernel<false, 1>);
+        else if (cols <= 1024) go(ln_quant_fp8_kernel<false, 2>);
+        else go(ln_quant_fp8_kernel<false, 4>);
+    }
     return hipGetLastError();
 }
 
