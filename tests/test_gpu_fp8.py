@@ -50,9 +50,9 @@ def test_row_quantisation_matches_oracle():
     assert not np.any(got[7]) and sc[7].item() == 1.0
 
 
-def _layer_case(seed, lengths, with_bias):
+def _layer_case(seed, lengths, with_bias, hidden=512, heads=4):
     sw = make_stack_workload(seed=seed, lengths=lengths, layers=1, num_targets=16,
-                             contextual_len=8, k1=128, k2=32)
+                             contextual_len=8, k1=128, k2=32, hidden=hidden, heads=heads)
     rng = np.random.default_rng(seed + 50)
     D, NU = sw.hidden, sw.heads * sw.d
     host = dict(ln1_w=(1.0 + 0.2 * rng.standard_normal(D)).astype(np.float32),
@@ -65,10 +65,14 @@ def _layer_case(seed, lengths, with_bias):
     return sw, {k: np.asarray(v, np.float32) for k, v in host.items()}
 
 
-@pytest.mark.parametrize("with_bias", [False, True])
-def test_fp8_layer_matches_oracle(with_bias):
-    sw, host = _layer_case(1, [700, 129, 1000, 64], with_bias)
-    print(f"[case] fp8 layer bias={with_bias} T={int(sw.offsets[-1])}", flush=True)
+@pytest.mark.parametrize("with_bias,hidden,heads", [(False, 512, 4), (True, 512, 4),
+                                                    (True, 1024, 8), (True, 2048, 16)])
+def test_fp8_layer_matches_oracle(with_bias, hidden, heads):
+    """The last two cases: rows of 1024 and 2048 columns, the LayerNorm
+    quantisation's two- and four-chunk widths."""
+    lengths = [700, 129, 1000, 64] if hidden == 512 else [100, 37]
+    sw, host = _layer_case(1, lengths, with_bias, hidden, heads)
+    print(f"[case] fp8 layer bias={with_bias} hidden={hidden} T={int(sw.offsets[-1])}", flush=True)
     f = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(DEV)  # noqa: E731
     x = f(sw.x).bfloat16()
     w1q, s1 = sla.stu_quantize_rows_fp8(f(host["w_uvqk"]).bfloat16())

@@ -72,6 +72,35 @@ def test_stu_layer_matches_oracle(with_bias):
     print(f"  out: max {mx:.3e} mean {mn:.3e}")
 
 
+@pytest.mark.parametrize("hidden,heads", [(1024, 8), (2048, 16)])
+def test_stu_layer_wide_rows_match_oracle(hidden, heads):
+    """Rows of 1024 and 2048 columns (hidden, and H*d_v for the gated
+    LayerNorm): the LayerNorm kernels' two- and four-chunk widths."""
+    sw = make_stack_workload(seed=7, lengths=[100, 37], layers=1, num_targets=8, hidden=hidden,
+                             heads=heads, contextual_len=4, k1=64, k2=16)
+    print(f"[case] stu layer hidden={hidden} heads={heads} T={int(sw.offsets[-1])}", flush=True)
+    rng = np.random.default_rng(11)
+    w, host = _layer_weights(sw, 0, True, rng)
+    ln1 = (1.0 + 0.2 * rng.standard_normal(hidden)).astype(np.float32)
+    ln2 = (1.0 + 0.2 * rng.standard_normal(heads * sw.d)).astype(np.float32)
+    w.ln1_w, w.ln2_w = _f(ln1), _f(ln2)
+    host["ln1_w"], host["ln2_w"] = ln1, ln2
+    out = sla.stu_layer_fwd(_b(sw.x), torch.from_numpy(sw.offsets).to(DEV),
+                            torch.from_numpy(sw.num_targets).to(DEV), w.ln1_w, w.w_uvqk, w.ln2_w,
+                            w.w_out, heads=sw.heads, d_qk=sw.d, d_v=sw.d, k1=sw.k1, k2=sw.k2,
+                            contextual_len=sw.contextual_len, max_seq_len=sw.max_seq_len,
+                            ln1_b=w.ln1_b, b_uvqk=w.b_uvqk, ln2_b=w.ln2_b, b_out=w.b_out)
+    torch.cuda.synchronize()
+    ref, _ = oracle.stu_layer_fwd(sw.x, sw.offsets, sw.num_targets, host["ln1_w"],
+                                  host["w_uvqk"], host["ln2_w"], host["w_out"], heads=sw.heads,
+                                  dqk=sw.d, dv=sw.d, k1=sw.k1, k2=sw.k2, ctx=sw.contextual_len,
+                                  N=sw.max_seq_len, ln1_b=host["ln1_b"], b_uvqk=host["b_uvqk"],
+                                  ln2_b=host["ln2_b"], b_out=host["b_out"], store_bf16=True,
+                                  want_uvqk=True)
+    mx, mn = assert_close_bf16(_np(out), ref, "out", ref_rounded=True)
+    print(f"  out: max {mx:.3e} mean {mn:.3e}")
+
+
 def test_stu_zero_output_weight_returns_input():
     sw = make_stack_workload(seed=2, lengths=[300, 200], layers=1)
     w, _ = _layer_weights(sw, 0)

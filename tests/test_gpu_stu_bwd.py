@@ -33,9 +33,9 @@ def _f(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
 
 
-def _case(seed, lengths, num_targets, with_bias, ctx=8, k1=128, k2=32):
+def _case(seed, lengths, num_targets, with_bias, ctx=8, k1=128, k2=32, hidden=512, heads=4):
     sw = make_stack_workload(seed=seed, lengths=lengths, layers=1, num_targets=num_targets,
-                             contextual_len=ctx, k1=k1, k2=k2)
+                             contextual_len=ctx, k1=k1, k2=k2, hidden=hidden, heads=heads)
     rng = np.random.default_rng(seed + 100)
     D, NU = sw.hidden, sw.heads * sw.d
     nw = 4 * NU
@@ -110,6 +110,17 @@ def test_stu_layer_bwd_matches_oracle(save_attn):
     sw, host, dout = _case(1, [700, 129, 1000, 64], 16, with_bias=True)
     print(f"[case] stu bwd save_attn={save_attn} T={int(sw.offsets[-1])}", flush=True)
     g = _run(sw, host, dout, save_attn)
+    _check(g, sw, host, dout)
+
+
+@pytest.mark.parametrize("hidden,heads", [(1024, 8), (2048, 16)])
+def test_stu_layer_bwd_wide_rows(hidden, heads):
+    """Rows of 1024 and 2048 columns: the LayerNorm backward's two- and
+    four-chunk widths, and wider projections."""
+    sw, host, dout = _case(5, [100, 37], 8, with_bias=True, ctx=4, k1=64, k2=16, hidden=hidden,
+                           heads=heads)
+    print(f"[case] stu bwd hidden={hidden} heads={heads} T={int(sw.offsets[-1])}", flush=True)
+    g = _run(sw, host, dout, save_attn=True)
     _check(g, sw, host, dout)
 
 
