@@ -139,16 +139,27 @@ __global__ __launch_bounds__(256) void absmax_bf16_kernel(const uint16_t *x, int
     const int tpr = cpr < (int)blockDim.x ? cpr : (int)blockDim.x;
     const int rpi = blockDim.x / tpr;
     const int ro = threadIdx.x / tpr, ko = threadIdx.x % tpr;
+    // four rows per iteration, their loads issued together (a max is
+    // independent of the order)
+    constexpr int U = 4;
     float m = 0.0f;
     if (ro < rpi) {
-        for (int64_t r = (int64_t)blockIdx.x * rpi + ro; r < rows; r += (int64_t)gridDim.x * rpi) {
-            const uint16_t *row = x + r * ld;
+        const int64_t stride = (int64_t)gridDim.x * rpi;
+        for (int64_t r = (int64_t)blockIdx.x * rpi + ro; r < rows; r += U * stride) {
             for (int k = ko; k < cpr; k += tpr) {
-                uint4 v = ld16(row + 8 * k);
-                uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                uint4 v[U];
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
+                for (int j = 0; j < U; ++j) {
+                    const int64_t rj = r + j * stride;
+                    v[j] = rj < rows ? ld16(x + rj * ld + 8 * k) : make_uint4(0u, 0u, 0u, 0u);
+                }
+#pragma unroll
+                for (int j = 0; j < U; ++j) {
+                    const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
+                }
             }
         }
     }
