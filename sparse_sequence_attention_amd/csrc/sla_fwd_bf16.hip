@@ -12,8 +12,9 @@
 // first target plus the diagonal), 64 keys per step.  Per step each wave
 // computes, per 32-key block,
 //   S^T (32 keys x 32 rows) = K Q^T      (K from LDS, Q^T held in registers)
-//   P^T = mask(S^T) * sigmoid(alpha S^T)  in registers, rounded to fp16
+//   P^T = mask(S^T * sigmoid(alpha S^T))  in registers, rounded to fp16
 //   O^T (D x 32 rows)     += V^T P^T     (V^T by transposing LDS reads)
+// with the two blocks' products and SiLU interleaved in one wave.
 // Computing S transposed puts the rows in the MFMA's lane dimension, so P^T
 // feeds the second MFMA as its B operand straight from the accumulator.  The
 // K and V rows of the next step come HBM -> LDS by DMA into the idle one of
