@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--microbatch", type=int, default=1024,
                     help="mfalcon: candidates per sequence and call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peak-probe", action="store_true",
+                    help="skip the MFMA-only probe (run after the timed steps) that reports the "
+                         "bf16 MFMA rate and shader clock measured on this GPU")
     ap.add_argument("--cpu-sample-len", type=int, default=16384)
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_long_16k.json"),
                     help="per-kernel HBM bytes measured with rocprofv3 --pmc (optional)")
@@ -237,6 +240,16 @@ def main():
             "traffic": traffic,
         },
     }
+    if not args.no_peak_probe:
+        # after the timed region: the MFMA-only rate and the shader clock on this GPU
+        pm = sla.probe_mfma_peak()
+        line["peak_measured"] = {
+            "kernel": "MFMA-only: bf16 32x32x16, four independent chains per wave, 16 waves per CU",
+            "tflops": round(pm["tflops"], 1),
+            "sclk_ghz": round(pm["sclk_ghz"], 3),
+            "pct_of_measured_peak": round(100.0 * value / pm["tflops"], 2),
+            "roofline_frac_of_measured_peak": round(achieved / pm["tflops"], 4),
+        }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_len)
     print(json.dumps(line), flush=True)

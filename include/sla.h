@@ -360,6 +360,17 @@ sla_status_t stu_truncate(int32_t batch, int64_t total_tokens, const int64_t *of
                           int64_t *new_offsets, int32_t *new_num_targets, int64_t *gather_idx,
                           void *x_out, int64_t capacity, void *stream);
 
+/* Measurement aid, not part of the attention path: the bf16 dense MFMA rate
+ * the current device sustains, measured with an MFMA-only kernel (four
+ * workgroups of four waves per CU, each wave `iters` rounds of four
+ * independent v_mfma_f32_32x32x16_bf16 chains; one warm-up launch, then one
+ * launch timed with HIP events on `stream`, which is synchronised).  Writes
+ * the rate in TFLOP/s to *tflops and the shader clock observed during the
+ * timed launch (shader-clock counter over the 100 MHz constant clock) in GHz
+ * to *sclk_ghz.  Allocates and frees a small device buffer.  1 <= iters <=
+ * 1048576 (4096: about 1 ms). */
+sla_status_t sla_probe_mfma_peak(int32_t iters, double *tflops, double *sclk_ghz, void *stream);
+
 const char *sla_status_string(sla_status_t s);
 const char *sla_last_error(void); /* thread-local message of the last failure */
 

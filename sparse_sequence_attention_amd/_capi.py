@@ -25,7 +25,8 @@ EXPORTS = (
     "sla_fwd_candidates", "sla_bwd", "sla_bwd_stage", "sla_schedule_capacity", "sla_schedule_tile",
     "sla_schedule", "sla_schedule_host", "sla_count_pairs_host", "stu_layer_workspace_size", "stu_layer_fwd",
     "stu_layer_bwd_workspace_size", "stu_layer_bwd", "stu_quantize_rows_fp8",
-    "stu_layer_fp8_workspace_size", "stu_layer_fwd_fp8", "stu_gather_targets", "stu_truncate", "sla_status_string", "sla_last_error",
+    "stu_layer_fp8_workspace_size", "stu_layer_fwd_fp8", "stu_gather_targets", "stu_truncate", "sla_probe_mfma_peak", "sla_status_string",
+    "sla_last_error",
 )
 
 
@@ -101,6 +102,9 @@ def load(path: str = LIB_PATH):
         lib.sla_schedule_host.restype = i64
         lib.sla_count_pairs_host.argtypes = [i32, P, P, i32, i32, i32]
         lib.sla_count_pairs_host.restype = i64
+        DBL = ctypes.POINTER(ctypes.c_double)
+        lib.sla_probe_mfma_peak.argtypes = [i32, DBL, DBL, P]
+        lib.sla_probe_mfma_peak.restype = i32
         DP = ctypes.POINTER(STULayerDesc)
         lib.stu_layer_workspace_size.argtypes = [DP]
         lib.stu_layer_workspace_size.restype = sz

@@ -32,6 +32,7 @@ SOURCES = [
     "stu_bwd.hip",
     "stu_fp8.hip",
     "gemm_nt.hip",
+    "sla_probe.hip",
 ]
 
 ARCH = "gfx950"

@@ -278,6 +278,46 @@ StuBwdLayout stu_bwd_layout(const stu_layer_desc_t *d)
 
 extern "C" {
 
+sla_status_t sla_probe_mfma_peak(int32_t iters, double *tflops, double *sclk_ghz, void *stream)
+{
+    if (!tflops || !sclk_ghz) return fail(SLA_ERR_NULL, "tflops or sclk_ghz is NULL");
+    if (iters < 1 || iters > (1 << 20)) return fail(SLA_ERR_INVALID, "iters %d outside [1, 2^20]", iters);
+    sla_status_t st = check_device();
+    if (st != SLA_OK) return st;
+    int dev = -1, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "device attributes");
+    const int blocks = 4 * cus;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float *sink = nullptr;
+    unsigned long long *clk = nullptr;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    unsigned long long hclk[2] = {0, 0};
+    float ms = 0.0f;
+    e = hipMalloc(&sink, sizeof(float) * (size_t)blocks * 256);
+    if (e == hipSuccess) e = hipMalloc(&clk, 2 * sizeof(unsigned long long));
+    if (e == hipSuccess) e = hipEventCreate(&e0);
+    if (e == hipSuccess) e = hipEventCreate(&e1);
+    if (e == hipSuccess) e = launch_mfma_peak(blocks, iters, sink, clk, s);  // warm-up
+    if (e == hipSuccess) e = hipEventRecord(e0, s);
+    if (e == hipSuccess) e = launch_mfma_peak(blocks, iters, sink, clk, s);
+    if (e == hipSuccess) e = hipEventRecord(e1, s);
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+    if (e == hipSuccess) e = hipMemcpy(hclk, clk, sizeof(hclk), hipMemcpyDeviceToHost);
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    if (clk) (void)hipFree(clk);
+    if (sink) (void)hipFree(sink);
+    if (e != hipSuccess) return hip_fail(e, "MFMA probe");
+    if (!(ms > 0.0f)) return fail(SLA_ERR_DEVICE, "MFMA probe: no elapsed time");
+    *tflops = mfma_peak_flops(blocks, iters) / ((double)ms * 1e-3) / 1e12;
+    // the constant clock counts at 100 MHz: GHz = cycles / (ticks * 10)
+    *sclk_ghz = hclk[1] > 0 ? (double)hclk[0] / ((double)hclk[1] * 10.0) : 0.0;
+    return SLA_OK;
+}
+
 const char *sla_status_string(sla_status_t s)
 {
     switch (s) {

@@ -129,6 +129,12 @@ int ln_bwd_blocks(int64_t rows);
 // LayerNorm backward (gated: y = (LN(x) w + b) (.) u; du and, when y is
 // non-NULL, y also written); part_w / part_b: [ln_bwd_blocks(rows)][cols];
 // db nullable; res (plain only, nullable) is added to dx.
+// MFMA-only throughput probe (sla_probe.hip): `blocks` workgroups of four
+// waves, each wave `iters` rounds of four bf16 32x32x16 MFMAs; clk[0] gets the
+// shader clocks and clk[1] the 100 MHz ticks that wave 0 of workgroup 0 saw.
+hipError_t launch_mfma_peak(int blocks, int iters, float *sink, unsigned long long *clk,
+                            hipStream_t st);
+double mfma_peak_flops(int blocks, int iters);
 hipError_t launch_ln_bwd_bf16(bool gated, const void *x, int64_t ldx, const void *dy, int64_t lddy,
                               const void *u, int64_t ldu, const float *w, const float *b,
                               const void *res, int64_t ldres, void *dx, int64_t lddx, void *du,

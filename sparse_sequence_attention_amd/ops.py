@@ -216,6 +216,16 @@ def count_pairs_host(offsets, num_targets, k1: int, k2: int, contextual_len: int
     return int(n)
 
 
+def probe_mfma_peak(iters: int = 4096, device=None) -> dict:
+    """bf16 dense MFMA rate measured on the current device with an MFMA-only
+    kernel, and the shader clock during it (sla_probe_mfma_peak)."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    tf, ghz = ctypes.c_double(0.0), ctypes.c_double(0.0)
+    C.check(C.load().sla_probe_mfma_peak(int(iters), ctypes.byref(tf), ctypes.byref(ghz),
+                                         _stream(dev)))
+    return {"tflops": tf.value, "sclk_ghz": ghz.value}
+
+
 class SLAFunction(torch.autograd.Function):
     """Autograd wrapper: forward sla_fwd, backward sla_bwd."""
 

@@ -86,3 +86,13 @@ def test_truncation_needs_room_for_the_context(monkeypatch):
     out = sla.stu_truncate(x, offs, tg_ok, contextual_len=16, tail_len=32)
     torch.cuda.synchronize()
     assert out[1].tolist()[0] == 0
+
+
+def test_mfma_probe_reports_a_plausible_rate_and_clock():
+    """The MFMA-only probe the bench reports next to the data-sheet peak: a
+    rate between a fifth of and just above the 2516.6 TFLOP/s bf16 figure,
+    and a shader clock between 1 and 3 GHz."""
+    pm = sla.probe_mfma_peak(iters=1024)
+    print(f"[case] mfma probe {pm}", flush=True)
+    assert 500.0 < pm["tflops"] < 2600.0
+    assert 1.0 < pm["sclk_ghz"] < 3.0

@@ -265,6 +265,15 @@ def test_bwd_and_layer_argument_errors(lib):
 # --------------------------------------------------------------------------
 # config rules (torcheasyrec page)
 # --------------------------------------------------------------------------
+def test_mfma_probe_argument_errors(lib):
+    import ctypes
+    d = ctypes.c_double(0.0)
+    assert lib.sla_probe_mfma_peak(4096, None, ctypes.byref(d), None) == C.SLA_ERR_NULL
+    assert lib.sla_probe_mfma_peak(0, ctypes.byref(d), ctypes.byref(d), None) == C.SLA_ERR_INVALID
+    assert lib.sla_probe_mfma_peak((1 << 20) + 1, ctypes.byref(d), ctypes.byref(d),
+                                   None) == C.SLA_ERR_INVALID
+
+
 def test_stu_config_rules():
     c = STUConfig(sla_k1=256, sla_k2=32, contextual_seq_len=64)
     assert c.sla_enabled and c.effective_k2 == 64
