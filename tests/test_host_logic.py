@@ -38,6 +38,22 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
 
 
+@pytest.mark.parametrize("lang", ["c", "c++"])
+def test_public_header_compiles_standalone(lang, tmp_path):
+    """include/sla.h is a plain C header: it compiles on its own as C and C++
+    (no HIP or torch types in the boundary)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc" if lang == "c" else "g++")
+    if cc is None:
+        pytest.skip("no host C/C++ compiler")
+    hdr = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                       "sla.h")
+    r = subprocess.run([cc, "-fsyntax-only", "-Wall", "-Werror", "-x", lang, hdr],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
 def test_status_strings(lib):
     for s in range(7):
         assert lib.sla_status_string(s).decode().startswith("SLA_")
