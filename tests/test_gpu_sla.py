@@ -257,9 +257,11 @@ def test_empty_batch_and_empty_sequences():
 # --------------------------------------------------------------------------
 # full-size workloads
 # --------------------------------------------------------------------------
-def test_jagged_2k_config_fwd_bwd():
-    """B=32 lengths U[512,2048], H=4, d=128, K1=256, K2=64, ctx=8: every output."""
-    w = make_sla_workload("jagged_2k", seed=0)
+@pytest.mark.parametrize("seed", [0, 1, 2, 3, 4])
+def test_jagged_2k_config_fwd_bwd(seed):
+    """B=32 lengths U[512,2048], H=4, d=128, K1=256, K2=64, ctx=8: every output,
+    seeds 0-4 (the lengths and values change with the seed)."""
+    w = make_sla_workload("jagged_2k", seed=seed)
     _print_case("jagged_2k", w)
     q, k, v, do, offs, tg = _dev(w)
     o = sla.sla_fwd(q, k, v, offs, tg, **_kw(w))
