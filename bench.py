@@ -115,9 +115,9 @@ def main():
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.traffic)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the SLA hot path "
-              "shards by sequence with no exchange, so a multi-GPU figure is one GPU's "
-              "value times the GPU count", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): there is no "
+              "multi-GPU path to time; the attention would shard by sequence with no "
+              "exchange, which nothing here runs or measures", file=sys.stderr)
         sys.exit(2)
 
     if args.workload == "stu_layer":
