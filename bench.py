@@ -54,7 +54,9 @@ def parse():
     ap.add_argument("--no-peak-probe", action="store_true",
                     help="skip the MFMA-only probe (run after the timed steps) that reports the "
                          "bf16 MFMA rate and shader clock measured on this GPU")
-    ap.add_argument("--cpu-sample-len", type=int, default=16384)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=65536,
+                    help="cpu_baseline: whole sequences from the start of the workload up to "
+                         "about this many tokens (long_16k: its four 16384-token sequences)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_long_16k.json"),
                     help="per-kernel HBM bytes measured with rocprofv3 --pmc (optional)")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -251,7 +253,7 @@ def main():
             "roofline_frac_of_measured_peak": round(achieved / pm["tflops"], 4),
         }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_len)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
     print(json.dumps(line), flush=True)
 
 
@@ -548,17 +550,29 @@ def bench_mfalcon(args):
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(w, sample_len):
-    """The fp64 oracle as it stands, on a bounded sample: one sequence of
-    `sample_len` tokens of the same workload (all heads), forward + backward."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(w, sample_tokens):
+    """The fp64 oracle as it stands, on a bounded sample: the first whole
+    sequences of the same workload (all heads) up to about `sample_tokens`
+    tokens, forward + backward."""
     import oracle
     import sparse_sequence_attention_amd as sla
-    b = int(np.argmax(np.asarray(w.lengths) >= sample_len))
-    L = int(min(w.lengths[b], sample_len))
-    s0 = int(w.offsets[b])
-    sl = slice(s0, s0 + L)
-    offs = np.array([0, L], np.int64)
-    q, k, v, do = w.q[sl], w.k[sl], w.v[sl], w.dout[sl]
+    ends = np.asarray(w.offsets[1:])
+    reach = np.nonzero(ends >= sample_tokens)[0]
+    m = int(reach[0]) + 1 if len(reach) else len(ends)  # sequences in the sample
+    n = int(ends[m - 1])
+    offs = np.asarray(w.offsets[:m + 1], np.int64)
+    q, k, v, do = w.q[:n], w.k[:n], w.v[:n], w.dout[:n]
     t0 = time.perf_counter()
     oracle.sla_fwd(q, k, v, offs, None, w.k1, w.k2, w.contextual_len, w.max_seq_len)
     oracle.sla_bwd(q, k, v, do, offs, None, w.k1, w.k2, w.contextual_len, w.max_seq_len)
@@ -567,9 +581,10 @@ def cpu_baseline(w, sample_len):
     pairs = sla.count_pairs_host(offs, None, w.k1, w.k2, w.contextual_len) * H
     useful = pairs * (2 * (d + d) + 2 * (3 * d + 2 * d))
     return {"value": round(useful / t / 1e12, 6), "unit": "TFLOP/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"sequence {b} of the workload, first {L} tokens, all {H} heads, fwd+bwd "
-                      f"({t:.2f} s; {L / t:.1f} tokens/s)"}
+            "cores": oracle.num_threads(), "kind": "oracle", "cpu_model": _cpu_model(),
+            "sample": f"sequences 0-{m - 1} of the workload ({n} tokens, lengths "
+                      f"{[int(x) for x in np.diff(offs)]}), all {H} heads, fwd+bwd "
+                      f"({t:.2f} s; {n / t:.1f} tokens/s)"}
 
 
 if __name__ == "__main__":
