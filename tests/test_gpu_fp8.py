@@ -1,8 +1,10 @@
 """GPU parity of the FP8 projections (row-wise e4m3 quantisation, FP8 GEMMs)
 against the fp64 oracle's FP8 mode, which quantises the same way.
 
-Quantisation of bf16 rows (the weights): codes and scales bit-exact (the
-oracle decides the codes in fp32, as the kernels do).
+Quantisation of bf16 rows (the weights): the oracle decides each code in
+fp64, the kernel in fp32; codes agree except where the exact quotient lies
+within fp32 rounding of a point halfway between two e4m3 values, and there
+they are neighbours.  Scales agree to fp32 rounding.
 
 The layer, against the FP8 oracle: U|V|Q|K (the first FP8 GEMM, whose input
 codes come from the same bf16 x) within the bf16 bar.  The output goes
@@ -43,10 +45,20 @@ def test_row_quantisation_matches_oracle():
     print("[case] quantise 2048 x 512", flush=True)
     q, sc = sla.stu_quantize_rows_fp8(xb.to(DEV))
     torch.cuda.synchronize()
-    rq, rs = oracle.quant_rows_fp8(xb.double().numpy())
-    assert np.array_equal(sc.cpu().numpy().astype(np.float64), rs)
+    xd = xb.double().numpy()
+    rq, rs = oracle.quant_rows_fp8(xd)
+    gs = sc.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(gs - rs) <= 2.0 ** -24 * rs)
     got = _e4m3_values(q)
-    assert np.array_equal(got, rq), int((got != rq).sum())
+    diff = got != rq
+    print(f"  codes differing from the fp64 decision: {int(diff.sum())} of {got.size}")
+    if diff.any():
+        v = (xd * (448.0 / np.abs(xd).max(axis=1, keepdims=True).clip(1e-300)))[diff]
+        mid = (np.abs(got[diff]) + np.abs(rq[diff])) / 2
+        assert np.all(np.abs(np.abs(v) - mid) <= 2.0 ** -22 * mid), "a flip away from a midpoint"
+        step = np.abs(np.abs(got[diff]) - np.abs(rq[diff]))
+        assert np.all(step <= 2.0 ** (np.floor(np.log2(mid)) - 2)), "codes not neighbours"
+    assert diff.sum() <= 1e-4 * got.size
     assert not np.any(got[7]) and sc[7].item() == 1.0
 
 

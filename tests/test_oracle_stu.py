@@ -309,3 +309,66 @@ def test_stu_layer_bwd_of_zero_dout_is_zero():
                              k2=1, ctx=0, N=6.0, **_stu_bwd_args(p))
     for key, val in g.items():
         assert not np.any(val), key
+
+
+# --------------------------------------------------------------------------
+# storage-matched forward mode: each rounding point on its own
+# --------------------------------------------------------------------------
+_FWD_POINTS = ("n", "z", "a", "y", "out")
+
+
+def _stu_torch_rounded(offs, p, tg, H, dqk, dv, kw, points):
+    """The STU layer as a torch fp64 composition (ULTRA-HSTU paper, section 3
+    Eq.1-5 in the order of Code Listing 1), rounding to bf16 with the
+    frexp-based round-to-nearest-even above at the named points only: n (the
+    normalised input), z (U|V|Q|K after SiLU), a (the attention output), y
+    (the gated LayerNorm output) and out (the layer output, i.e. the residual
+    stream)."""
+    r = lambda name, t: _rne_bf16_torch(t) if name in points else t  # noqa: E731
+    t = {k: torch.from_numpy(np.asarray(v, np.float64)) for k, v in p.items()}
+    x = t["x"]
+    T, D = x.shape
+    n = r("n", F.layer_norm(x, (D,), t["ln1_w"], t["ln1_b"], kw["eps"]))
+    z = r("z", F.silu(F.linear(n, t["w_uvqk"], t["b_uvqk"])))
+    u, v, q, k = torch.split(z, [H * dv, H * dv, H * dqk, H * dqk], dim=1)
+    a = dense_sla_torch(q.reshape(T, H, dqk), k.reshape(T, H, dqk), v.reshape(T, H, dv), offs,
+                        tg, kw["k1"], kw["k2"], kw["ctx"], kw["N"], kw["alpha"]).reshape(T, H * dv)
+    a = r("a", a)
+    y = r("y", F.layer_norm(a, (H * dv,), t["ln2_w"], t["ln2_b"], kw["eps"]) * u)
+    out = r("out", F.linear(y, t["w_out"], t["b_out"]) + x)
+    return out.numpy(), z.numpy()
+
+
+@pytest.mark.parametrize("mask,points", [(1, ("n", "z", "a", "y")), (2, ("out",)),
+                                         (3, _FWD_POINTS)])
+@pytest.mark.parametrize("tg", [None, [2, 1, 0]])
+def test_stu_storage_mode_matches_rounded_composition(mask, points, tg):
+    """oracle.stu_layer_fwd(store_bf16=mask) equals the torch composition that
+    rounds at exactly the points of that mask (bit 1: the branch tensors n,
+    U|V|Q|K, A, y; bit 2: the layer output), and differs from it as soon as
+    any one of those points is left unrounded: each rounding point is
+    present, and none is applied twice or in the wrong place."""
+    lens = [6, 11, 9]
+    H, dqk, dv = 2, 4, 3
+    offs, p = _stu_case(21, lens, H=H, dqk=dqk, dv=dv)
+    # inputs as a bf16 implementation receives them
+    p = {k: (bf16_round_f32(np.asarray(v, np.float32)).astype(np.float64)
+             if k in ("x", "w_uvqk", "w_out") else v) for k, v in p.items()}
+    kw = dict(k1=3, k2=2, ctx=1, N=11.0, alpha=0.9, eps=1e-5)
+    out, z = oracle.stu_layer_fwd(p["x"], offs, tg, p["ln1_w"], p["w_uvqk"], p["ln2_w"],
+                                  p["w_out"], heads=H, dqk=dqk, dv=dv, ln1_b=p["ln1_b"],
+                                  b_uvqk=p["b_uvqk"], ln2_b=p["ln2_b"], b_out=p["b_out"],
+                                  store_bf16=mask, want_uvqk=True, **kw)
+    ref, zref = _stu_torch_rounded(offs, p, tg, H, dqk, dv, kw, points)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(z, zref, rtol=1e-12, atol=1e-12)
+    for drop in points:
+        alt, _ = _stu_torch_rounded(offs, p, tg, H, dqk, dv, kw,
+                                    tuple(q for q in points if q != drop))
+        assert np.abs(alt - out).max() > 1e-6, f"rounding point {drop} has no effect"
+    # a rounding point outside the mask is not applied either
+    for extra in _FWD_POINTS:
+        if extra in points:
+            continue
+        alt, _ = _stu_torch_rounded(offs, p, tg, H, dqk, dv, kw, points + (extra,))
+        assert np.abs(alt - out).max() > 1e-6, f"rounding point {extra} applied by mask {mask}"
