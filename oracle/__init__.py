@@ -22,7 +22,8 @@ Functions whose results are "parity pinned" and the pins (tests/test_oracle_*):
       on the combined [history | candidates] layout; microbatch invariance;
       candidates do not see each other.
   round_e4m3 / quant_rows_fp8 -- torch's float32 -> float8_e4m3fn conversion;
-      the row maximum maps to 448; scale * q reconstructs within half an ulp.
+      a nearest-value search over the e4m3 table (fp64 decision) and over
+      numpy's fp32 quotients (fp32 decision); the row maximum maps to 448.
   stu_layer_fwd_fp8 -- a torch fp64 composition that quantises with torch's
       float8_e4m3fn conversion; FP8 error against the bf16 layer.
   truncate  -- direct set construction, identity when tail >= history.
@@ -95,7 +96,7 @@ def _load():
         lib.oracle_stu_layer_bwd.restype = None
         lib.oracle_round_e4m3.argtypes = [dbl]
         lib.oracle_round_e4m3.restype = dbl
-        lib.oracle_quant_rows_fp8.argtypes = [i64, i64, P, P, P]
+        lib.oracle_quant_rows_fp8.argtypes = [i64, i64, P, P, P, i32]
         lib.oracle_quant_rows_fp8.restype = None
         lib.oracle_stu_layer_fwd_fp8.argtypes = [i32, P, P, i32, i32, i32, i32, i64, i64, i64,
                                                  dbl, dbl, dbl] + [P] * 11
@@ -271,13 +272,19 @@ def round_e4m3(x) -> np.ndarray:
     return np.vectorize(lambda v: f(float(v)), otypes=[np.float64])(np.asarray(x, np.float64))
 
 
-def quant_rows_fp8(x) -> Tuple[np.ndarray, np.ndarray]:
-    """(q [R, C] e4m3 values, scale [R]) with x ~ q * scale[:, None]."""
+def quant_rows_fp8(x, decision: str = "fp32") -> Tuple[np.ndarray, np.ndarray]:
+    """(q [R, C] e4m3 values, scale [R]) with x ~ q * scale[:, None].
+
+    decision: "fp32" takes 448 / max|x|, the product and the scale as fp32
+    operations (the kernels' precision, used for every comparison with them);
+    "fp64" gives the nearest e4m3 value of the fp64 quotient."""
+    if decision not in ("fp32", "fp64"):
+        raise ValueError("decision must be 'fp32' or 'fp64'")
     x = _f64(x)
     R, Cn = x.shape
     q = np.zeros_like(x)
     sc = np.zeros(R)
-    _load().oracle_quant_rows_fp8(R, Cn, _ptr(x), _ptr(q), _ptr(sc))
+    _load().oracle_quant_rows_fp8(R, Cn, _ptr(x), _ptr(q), _ptr(sc), int(decision == "fp32"))
     return q, sc
 
 

@@ -359,25 +359,48 @@ EXPORT double oracle_round_e4m3(double x)
  * produced): with a = max |x[r][:]|, the row is stored as
  * q = e4m3(x * (448 / a)) and the scale s = a / 448, so x ~ q * s.  An
  * all-zero row has s = 1 and q = 0.  q holds the e4m3 values (as doubles).
- * The quotient, the product and the scale are taken in fp64, so each code is
- * the rounding of the (nearly) exact x / s; an implementation that forms
- * them in fp32 can land on the neighbouring code where x / s lies within
- * fp32 rounding of a point halfway between two e4m3 values. */
+ *
+ * The code q is an integer that floating point decides, and the paper fixes
+ * no precision for that arithmetic, so it is a parameter:
+ *   fp32_decision = 1: x taken as an fp32 value, and 448 / a, the product and
+ *     a / 448 each one correctly rounded fp32 operation (the precision the
+ *     kernels compute in; the mode every comparison with them uses);
+ *   fp32_decision = 0: the quotient, the product and the scale in fp64, so
+ *     each code is the nearest e4m3 value of the (nearly) exact x / s.
+ * The two differ by one e4m3 step, and only where x / s lies within fp32
+ * rounding of a point halfway between two e4m3 values. */
 EXPORT void oracle_quant_rows_fp8(int64_t rows, int64_t cols, const double *x, double *q,
-                                  double *scale)
+                                  double *scale, int fp32_decision)
 {
     for (int64_t r = 0; r < rows; ++r) {
         const double *xr = x + r * cols;
-        double a = 0.0;
-        for (int64_t c = 0; c < cols; ++c) a = fmax(a, fabs(xr[c]));
-        if (a == 0.0) {
-            scale[r] = 1.0;
-            for (int64_t c = 0; c < cols; ++c) q[r * cols + c] = 0.0;
-            continue;
+        double *qr = q + r * cols;
+        if (fp32_decision) {
+            float a = 0.0f;
+            for (int64_t c = 0; c < cols; ++c) a = fmaxf(a, fabsf((float)xr[c]));
+            if (a == 0.0f) {
+                scale[r] = 1.0;
+                for (int64_t c = 0; c < cols; ++c) qr[c] = 0.0;
+                continue;
+            }
+            const float inv = 448.0f / a;
+            scale[r] = (double)(a / 448.0f);
+            for (int64_t c = 0; c < cols; ++c) {
+                const float prod = (float)xr[c] * inv;
+                qr[c] = oracle_round_e4m3((double)prod);
+            }
+        } else {
+            double a = 0.0;
+            for (int64_t c = 0; c < cols; ++c) a = fmax(a, fabs(xr[c]));
+            if (a == 0.0) {
+                scale[r] = 1.0;
+                for (int64_t c = 0; c < cols; ++c) qr[c] = 0.0;
+                continue;
+            }
+            const double inv = 448.0 / a;
+            scale[r] = a / 448.0;
+            for (int64_t c = 0; c < cols; ++c) qr[c] = oracle_round_e4m3(xr[c] * inv);
         }
-        const double inv = 448.0 / a;
-        scale[r] = a / 448.0;
-        for (int64_t c = 0; c < cols; ++c) q[r * cols + c] = oracle_round_e4m3(xr[c] * inv);
     }
 }
 
@@ -481,7 +504,8 @@ EXPORT void oracle_stu_layer_fwd(int B, const int64_t *offsets, const int32_t *n
  *   z[t][o]   = sn[t] sw1[o] sum_c nq[t][c] w1q[o][c] + b1[o]
  *   out[t][o] = sy[t] sw2[o] sum_c yq[t][c] w2q[o][c] + b2[o] + x[t][o]
  * U/V/Q/K, A and out are rounded to bf16 (stored tensors); n and y are not
- * (they go straight into the quantiser). */
+ * (they go straight into the quantiser).  Codes are decided in fp32 (the
+ * kernels' precision; the paper fixes none). */
 EXPORT void oracle_stu_layer_fwd_fp8(int B, const int64_t *offsets, const int32_t *num_targets,
                                      int D, int H, int dqk, int dv, int64_t k1, int64_t k2,
                                      int64_t ctx, double N, double alpha, double eps,
@@ -502,10 +526,10 @@ EXPORT void oracle_stu_layer_fwd_fp8(int B, const int64_t *offsets, const int32_
     double *a = malloc(sizeof(double) * T * NU), *y = malloc(sizeof(double) * T * NU);
     double *yq = malloc(sizeof(double) * T * NU);
 
-    oracle_quant_rows_fp8(NW, D, w1, w1q, sw1);
-    oracle_quant_rows_fp8(D, NU, w2, w2q, sw2);
+    oracle_quant_rows_fp8(NW, D, w1, w1q, sw1, 1);
+    oracle_quant_rows_fp8(D, NU, w2, w2q, sw2, 1);
     oracle_layernorm(T, D, x, ln1_w, ln1_b, eps, n);
-    oracle_quant_rows_fp8(T, D, n, nq, sn);
+    oracle_quant_rows_fp8(T, D, n, nq, sn, 1);
 #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < T; ++t)
         for (int64_t o = 0; o < NW; ++o) {
@@ -527,7 +551,7 @@ EXPORT void oracle_stu_layer_fwd_fp8(int B, const int64_t *offsets, const int32_
     round_all(a, T * NU);
     oracle_layernorm(T, NU, a, ln2_w, ln2_b, eps, y);
     for (int64_t i = 0; i < T * NU; ++i) y[i] *= uu[i];
-    oracle_quant_rows_fp8(T, NU, y, yq, sy);
+    oracle_quant_rows_fp8(T, NU, y, yq, sy, 1);
 #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < T; ++t)
         for (int64_t o = 0; o < D; ++o) {

@@ -46,19 +46,38 @@ def test_row_quantisation_matches_oracle():
     q, sc = sla.stu_quantize_rows_fp8(xb.to(DEV))
     torch.cuda.synchronize()
     xd = xb.double().numpy()
-    rq, rs = oracle.quant_rows_fp8(xd)
-    gs = sc.cpu().numpy().astype(np.float64)
-    assert np.all(np.abs(gs - rs) <= 2.0 ** -24 * rs)
+    # the codes are decided in fp32 on both sides (the paper fixes no
+    # precision for them): bit-exact codes and scales
+    q32, s32 = oracle.quant_rows_fp8(xd, "fp32")
     got = _e4m3_values(q)
+    gs = sc.cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, q32) and np.array_equal(gs, s32)
+    # against the fp64 decision (the nearest code of the exact quotient)
+    rq, rs = oracle.quant_rows_fp8(xd, "fp64")
+    assert np.all(np.abs(gs - rs) <= 2.0 ** -24 * rs)
     diff = got != rq
-    print(f"  codes differing from the fp64 decision: {int(diff.sum())} of {got.size}")
+    # values of x 448 / max|x| within 2^-22 of an e4m3 midpoint: the only
+    # places where a decision in fp32 may round the other way.  bf16 inputs
+    # have 8 significant bits, so exact ties are common (about 0.5% here).
+    vall = np.abs(xd * (448.0 / np.abs(xd).max(axis=1, keepdims=True).clip(1e-300)))
+    tab = np.unique(np.abs(_e4m3_values(torch.arange(256, dtype=torch.uint8))))
+    tab = tab[np.isfinite(tab)]
+    mids = (tab[:-1] + tab[1:]) / 2
+    i = np.clip(np.searchsorted(mids, vall), 1, len(mids) - 1)
+    near = np.minimum(np.abs(vall - mids[i - 1]), np.abs(vall - mids[i]))
+    ties = int((near <= 2.0 ** -22 * vall).sum())
+    print(f"  codes differing from the fp64 decision: {int(diff.sum())} of {got.size} "
+          f"({ties} values within 2^-22 of a midpoint)")
+    assert diff.sum() <= ties
     if diff.any():
-        v = (xd * (448.0 / np.abs(xd).max(axis=1, keepdims=True).clip(1e-300)))[diff]
+        v = vall[diff]
         mid = (np.abs(got[diff]) + np.abs(rq[diff])) / 2
         assert np.all(np.abs(np.abs(v) - mid) <= 2.0 ** -22 * mid), "a flip away from a midpoint"
+        # adjacent e4m3 codes: 3 mantissa bits, spacing 2^(e - 3) in binade
+        # [2^e, 2^(e+1)) for e >= -6 and the subnormal spacing 2^-9 below 2^-6
         step = np.abs(np.abs(got[diff]) - np.abs(rq[diff]))
-        assert np.all(step <= 2.0 ** (np.floor(np.log2(mid)) - 2)), "codes not neighbours"
-    assert diff.sum() <= 1e-4 * got.size
+        spacing = 2.0 ** (np.maximum(np.floor(np.log2(mid)), -6) - 3)
+        assert np.all(step == spacing), "codes not neighbours"
     assert not np.any(got[7]) and sc[7].item() == 1.0
 
 

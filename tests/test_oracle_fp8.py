@@ -4,8 +4,10 @@ the operand is produced).
 
 E4M3 rounding is pinned to torch's own float32 -> float8_e4m3fn conversion
 and, for fp64 inputs, to a nearest-value search over the table of e4m3
-values; the FP8 layer to a torch fp64 composition that quantises with that
-search."""
+values.  Row quantisation is pinned in both of its decision precisions: the
+fp64 one to that search over fp64 quotients, the fp32 one (the kernels') to
+the same search over numpy's IEEE fp32 quotients.  The FP8 layer is pinned to
+a torch fp64 composition that quantises the fp32 way."""
 import numpy as np
 import pytest
 import torch
@@ -78,14 +80,27 @@ def test_e4m3_rounding_of_fp64_values_is_nearest():
     assert np.array_equal(oracle.round_e4m3(x), _nearest_e4m3(x))
 
 
+def _quant_fp32(m):
+    """Row quantisation decided in fp32, by numpy's IEEE fp32 arithmetic: a
+    = max|x| and 448 / a, the product and a / 448 each one fp32 operation,
+    then the nearest e4m3 value of that fp32 product."""
+    m32 = np.asarray(m, np.float64).astype(np.float32)
+    a = np.abs(m32).max(axis=1, keepdims=True)
+    nz = a > 0
+    inv = np.where(nz, np.float32(448.0) / np.where(nz, a, np.float32(1.0)), np.float32(0.0))
+    q = _nearest_e4m3((m32 * inv.astype(np.float32)).astype(np.float64))
+    s = np.where(nz, (a / np.float32(448.0)).astype(np.float64), 1.0)
+    return q, s[:, 0]
+
+
 def test_row_quantisation():
-    """Codes decided in fp64 (ULTRA-HSTU paper, section 4.2.2: a scale per
-    row, the row maximum mapped to the top of the e4m3 range): a = max|x|,
-    s = a / 448, q = nearest e4m3 of x * (448 / a)."""
+    """ULTRA-HSTU paper, section 4.2.2 (a scale per row, the row maximum
+    mapped to the top of the e4m3 range): a = max|x|, s = a / 448, q =
+    nearest e4m3 of x * (448 / a), with that arithmetic in fp64 or in fp32."""
     rng = np.random.default_rng(1)
     x = (rng.standard_normal((7, 64)) * rng.uniform(0.01, 100, size=(7, 1))).astype(np.float32)
     x[3] = 0.0
-    q, s = oracle.quant_rows_fp8(x)
+    q, s = oracle.quant_rows_fp8(x, "fp64")
     assert s[3] == 1.0 and not np.any(q[3])
     for r in (0, 1, 2, 4, 5, 6):
         xr = x[r].astype(np.float64)
@@ -98,6 +113,29 @@ def test_row_quantisation():
         ulp = np.where(np.abs(vv) >= 2.0 ** -6,
                        2.0 ** (np.floor(np.log2(np.abs(vv) + 1e-300)) - 3), 2.0 ** -9)
         assert np.all(np.abs(q[r] - vv) <= ulp / 2 * (1 + 1e-12))
+    q32, s32 = oracle.quant_rows_fp8(x, "fp32")
+    rq32, rs32 = _quant_fp32(x)
+    assert np.array_equal(q32, rq32) and np.array_equal(s32, rs32)
+    assert np.all(np.abs(q32).max(axis=1)[[0, 1, 2, 4, 5, 6]] == 448.0)
+    with pytest.raises(ValueError):
+        oracle.quant_rows_fp8(x, "fp16")
+
+
+def test_fp32_decision_on_bf16_rows_with_exact_ties():
+    """bf16 rows (8 significant bits) put x * 448 / a exactly on e4m3
+    midpoints often; the fp32 decision still equals numpy's fp32 arithmetic
+    there, code for code, and all-zero rows get scale 1."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((64, 256)).astype(np.float32) * rng.uniform(
+        0.001, 50, size=(64, 1)).astype(np.float32)
+    x = torch.from_numpy(x).bfloat16().double().numpy()
+    x[9] = 0.0
+    q, s = oracle.quant_rows_fp8(x, "fp32")
+    rq, rs = _quant_fp32(x)
+    assert np.array_equal(q, rq) and np.array_equal(s, rs)
+    assert s[9] == 1.0 and not np.any(q[9])
+    q64, _ = oracle.quant_rows_fp8(x, "fp64")
+    assert (q != q64).sum() > 0     # ties decided differently somewhere
 
 
 def _case(seed, lens, D=32, H=2, d=16, tg=None):
@@ -119,14 +157,9 @@ def _torch_fp8_layer(offs, p, tg, H, d, kw):
     x = t["x"]
     T, D = x.shape
 
-    def quant(m):  # row-wise in fp64, nearest e4m3 by table search
-        # numpy's IEEE division (torch divides by a tensor through a
-        # reciprocal, which is not correctly rounded)
-        mm = m.numpy()
-        a = np.abs(mm).max(axis=1, keepdims=True)
-        s = np.where(a > 0, a / 448.0, 1.0)
-        inv = np.where(a > 0, 448.0 / np.where(a > 0, a, 1.0), 0.0)
-        return torch.from_numpy(_nearest_e4m3(mm * inv)), torch.from_numpy(s)
+    def quant(m):  # row-wise, decided in fp32 by numpy's IEEE arithmetic
+        q, s = _quant_fp32(m.numpy())
+        return torch.from_numpy(q), torch.from_numpy(s[:, None])
 
     n = F.layer_norm(x, (D,), t["ln1_w"], t["ln1_b"], kw["eps"])
     nq, sn = quant(n)
@@ -176,9 +209,9 @@ def test_fp8_layer_is_close_to_the_bf16_layer():
 
 
 def test_fp32_decided_codes_differ_only_near_midpoints():
-    """How often a code decided in fp32 (448 / a, the product and the
-    rounding each one fp32 operation, as a GPU kernel forms them) differs
-    from the oracle's fp64 decision, on the 18-layer stack's Xavier weights
+    """How often the fp32 decision (448 / a, the product and the rounding
+    each one fp32 operation, as the kernels form them) differs from the fp64
+    decision, on the 18-layer stack's Xavier weights
     (bf16) and on LayerNorm-like fp32 rows: only where the fp64 quotient lies
     within fp32 rounding of a point halfway between two neighbouring e4m3
     values, and then by one e4m3 step."""
@@ -190,10 +223,10 @@ def test_fp32_decided_codes_differ_only_near_midpoints():
     tab = _e4m3_table()
     total = flips = 0
     for m in mats:
-        q64, _ = oracle.quant_rows_fp8(m)
+        q64, _ = oracle.quant_rows_fp8(m, "fp64")
+        q32, _ = oracle.quant_rows_fp8(m, "fp32")
         a = np.abs(m).max(axis=1, keepdims=True)
-        p32 = m * (np.float32(448.0) / a)            # fp32 quotient and product
-        q32 = _nearest_e4m3(p32.astype(np.float64))
+        assert np.array_equal(q32, _quant_fp32(m)[0])
         diff = q32 != q64
         total += m.size
         flips += int(diff.sum())
