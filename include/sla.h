@@ -90,40 +90,36 @@ typedef struct {
     int32_t contextual_len;      /* contextual prefix >= 0; K2e = max(k2, this)     */
     int32_t max_seq_len;         /* N of the 1/N output scaling, >= 1               */
     float alpha;                 /* pre-activation factor: SiLU(alpha * q.k)        */
+    int32_t out_f32;             /* 0 or 1.  With dtype SLA_BF16 and 1, the outputs */
+                                 /* O (sla_fwd, sla_fwd_candidates) and dQ, dK, dV  */
+                                 /* (sla_bwd) are written as fp32 (their token      */
+                                 /* strides in fp32 elements); inputs stay bf16.    */
+                                 /* Ignored for SLA_F32.  The STU layer entry       */
+                                 /* points require 0.                               */
 } sla_problem_t;
 
-/* Operation selector for sla_workspace_size (FWD, BWD) and the schedule
- * inspection calls (FWD, BWD, DQ). */
-enum { SLA_OP_FWD = 0, SLA_OP_BWD = 1, SLA_OP_DQ = 2 };
+/* Operation selector for sla_workspace_size and the schedule inspection
+ * calls: FWD = row tiles (forward and dQ), BWD = key tiles (dK/dV). */
+enum { SLA_OP_FWD = 0, SLA_OP_BWD = 1 };
 
 /* Bytes of device workspace sla_fwd (op = SLA_OP_FWD) or sla_bwd
- * (op = SLA_OP_BWD) needs for problem p: the on-device tile schedule and, for
- * the backward, fp32 partial sums of the split global-prefix key tiles plus,
- * on the bf16 path with d in {64, 128} and a bounded window (at most 32 key
- * tiles of 128 per 64-row tile, i.e. about K1 + K2e <= 3.5K), the fp16 dS
- * blocks of all visited (64-row, 128-key) tiles and an fp16 copy of K, from
- * which dQ is computed without recomputing S and dP (about
- * 2 * T * H * 64 * 128 * (slots per row tile / 64) bytes: 1.6 GB for 110K
- * tokens, 4 heads, K1 = 1024, K2e = 128).  Depends only on host-known fields.
- * Returns 0 if p is invalid. */
+ * (op = SLA_OP_BWD) needs for problem p: the on-device tile schedule (about
+ * 20 bytes per sequence) and, for the backward, the fp32 partial dK|dV sums
+ * of the split global-prefix key tiles (at most 4 key tiles of 128 keys per
+ * sequence, each cut into at most 16 row chunks: up to
+ * 64 * 128 * H * (d_qk + d_v) * 4 bytes per sequence, about 17 MB for 8
+ * sequences, 4 heads, d = 128).  Depends only on host-known fields.  Returns 0
+ * if p is invalid. */
 size_t sla_workspace_size(const sla_problem_t *p, int op);
-
-/* Which dQ algorithm sla_bwd runs for problem p: 1 = dQ = dS.K from the fp16
- * dS blocks the dK/dV stage stores in the workspace (bf16, d in {64, 128},
- * at most 32 key tiles of 128 per 64-row tile), 0 = dQ recomputes S and dP
- * from Q, K, V and dO.  Both give the gradient of the forward above within
- * the bf16 tolerance; with 1, SLA_BWD_DQ must follow SLA_BWD_DKDV on the same
- * workspace.  Returns -1 if p is invalid.  Depends only on host-known fields. */
-int sla_bwd_dq_mode(const sla_problem_t *p);
 
 /* SLA forward (ULTRA-HSTU paper, section 4.2.1 Eq.6-7 with Eq.3):
  *   O[i] = (1/N) * sum_{j visible from i} SiLU(alpha * q_i . k_j) * v_j
  * q, k: [T][H][d_qk] with token strides ldq, ldk; v: [T][H][d_v] (ldv);
  * o: [T][H][d_v] (ldo), fully written for every token (rows of empty
- * sequences do not exist).  bf16 path: bf16 storage, fp32 accumulation,
- * SiLU in fp32, P rounded to fp16 (and V converted to fp16) for the P.V
- * product, so |SiLU(alpha s)| must stay below 65504.  f32 path: fp32
- * throughout.  Only the non-empty tiles of the local band, the global prefix
+ * sequences do not exist).  bf16 path: bf16 inputs, bf16 MFMA products with
+ * fp32 accumulation, SiLU in fp32, P rounded to bf16 for the P.V product; O
+ * in bf16, or fp32 with p->out_f32 (bf16 shares fp32's exponent range, so no
+ * range limit beyond fp32's applies).  f32 path: fp32 throughout.  Only the non-empty tiles of the local band, the global prefix
  * and (for targets) the diagonal are visited.
  * Errors: NULL -> SLA_ERR_NULL; bad sizes/strides -> SLA_ERR_INVALID; head dim
  * not in {32,64,128}, d_qk != d_v, ld or pointer not 16-byte aligned ->
@@ -140,9 +136,14 @@ sla_status_t sla_fwd(const sla_problem_t *p, const void *q, int64_t ldq, const v
  * over visible pairs only.  dq/dk/dv may be strided column blocks of one
  * buffer (no concatenation needed, ULTRA-HSTU paper section 4.2.2).  Every
  * output row is written (zero where a token sees / is seen by nothing).  No
- * atomics: dK/dV are owned by key tiles, dQ by row tiles; the global-prefix
- * key tiles are split over row chunks whose fp32 partial sums are added in a
- * fixed order, so results are bitwise reproducible run to run.
+ * atomics: dK/dV are owned by key tiles, dQ by row tiles (which recompute S
+ * and dO.V^T for their rows); the global-prefix key tiles are split over row
+ * chunks whose fp32 partial sums are added in a fixed order, so results are
+ * bitwise reproducible run to run.  bf16 path: bf16 MFMA products with fp32
+ * accumulation; P and dS enter the dV, dK and dQ products rounded to bf16,
+ * except on key tiles that hold global-prefix keys (j < K2e), whose dV and dK
+ * sums run over every later row: there P and dS enter as the sum of two bf16
+ * numbers (16 significant bits).  Outputs bf16, or fp32 with p->out_f32.
  * Errors as sla_fwd, with ws_bytes checked against SLA_OP_BWD. */
 sla_status_t sla_bwd(const sla_problem_t *p, const void *q, int64_t ldq, const void *k,
                      int64_t ldk, const void *v, int64_t ldv, const void *dout, int64_t lddo,
@@ -150,15 +151,13 @@ sla_status_t sla_bwd(const sla_problem_t *p, const void *q, int64_t ldq, const v
                      void *workspace, size_t ws_bytes, void *stream);
 
 /* The backward in stages: sla_bwd(...) equals, on one stream,
- *   sla_bwd_stage(SLA_BWD_PREPARE)  gradient scale + tile schedule (workspace)
- *   sla_bwd_stage(SLA_BWD_DKDV)     dK, dV (key-tile kernel + prefix reduce);
- *                                   also stores dS and fp16 K in the workspace
- *                                   when the workspace holds them
- *   sla_bwd_stage(SLA_BWD_DQ)       dQ (64-row tiles reading the stored dS, or
- *                                   128-row tiles recomputing it)
- * with identical arguments and workspace, in this order: DQ reads what DKDV
- * stored.  A stage ignores the output pointers it does not write (they may
- * be NULL).  SLA_BWD_ALL runs all three. */
+ *   sla_bwd_stage(SLA_BWD_PREPARE)  tile schedule (workspace)
+ *   sla_bwd_stage(SLA_BWD_DKDV)     dK, dV (key-tile kernel + prefix reduce)
+ *   sla_bwd_stage(SLA_BWD_DQ)       dQ (row-tile kernel)
+ * with identical arguments and workspace; PREPARE first, then DKDV and DQ in
+ * either order (they only read the schedule).  A stage ignores the output
+ * pointers it does not write (they may be NULL).  SLA_BWD_ALL runs all
+ * three. */
 enum { SLA_BWD_ALL = 0, SLA_BWD_PREPARE = 1, SLA_BWD_DKDV = 2, SLA_BWD_DQ = 3 };
 sla_status_t sla_bwd_stage(const sla_problem_t *p, int stage, const void *q, int64_t ldq,
                            const void *k, int64_t ldk, const void *v, int64_t ldv,
@@ -168,10 +167,8 @@ sla_status_t sla_bwd_stage(const sla_problem_t *p, int stage, const void *q, int
 
 /* Schedule inspection (the integer part of the hot path, exposed so that it
  * can be checked bit for bit).  Writes the work list the kernels of `op` run:
- *   op = SLA_OP_FWD: row-tile items (forward, and dQ when it recomputes dS)
+ *   op = SLA_OP_FWD: row-tile items (forward and dQ kernels)
  *   op = SLA_OP_BWD: key-tile items (dK/dV kernel)
- *   op = SLA_OP_DQ:  64-row tile items of dQ from stored dS (FWD layout; key
- *                    tiles of 128 keys; their order is the dS slot order)
  * as int32 records of SLA_SCHED_RECORD_INTS fields into `records` (device,
  * capacity `capacity` records) and the record count into `*count` (device
  * int32).  Record fields:
@@ -179,7 +176,7 @@ sla_status_t sla_bwd_stage(const sla_problem_t *p, int stage, const void *q, int
  *                                       within sequence b, [lo, hi))
  *   [3] n_ranges (0..3)
  *   [4..9] up to 3 half-open ranges of the other operand, in tokens within b:
- *        FWD, DQ: key ranges visited, each a union of whole key tiles of
+ *        FWD: key ranges visited, each a union of whole key tiles of
  *             sla_schedule_tile(op, 1) keys (last tile clipped at L_b);
  *        BWD: row ranges visited (history rows, target rows), split into the
  *             chunk this record covers;
@@ -367,9 +364,14 @@ sla_status_t stu_truncate(int32_t batch, int64_t total_tokens, const int64_t *of
  * launch timed with HIP events on `stream`, which is synchronised).  Writes
  * the rate in TFLOP/s to *tflops and the shader clock observed during the
  * timed launch (shader-clock counter over the 100 MHz constant clock) in GHz
- * to *sclk_ghz.  Allocates and frees a small device buffer.  1 <= iters <=
- * 1048576 (4096: about 1 ms). */
-sla_status_t sla_probe_mfma_peak(int32_t iters, double *tflops, double *sclk_ghz, void *stream);
+ * to *sclk_ghz.  scratch: caller-owned device memory of at least
+ * sla_probe_scratch_size() bytes (16-byte aligned; about 1 MB on a 256-CU
+ * device), overwritten; a smaller one -> SLA_ERR_WORKSPACE.  Allocates
+ * nothing.  1 <= iters <= 1048576 (4096: about 1 ms).
+ * sla_probe_scratch_size returns 0 when no device is current. */
+size_t sla_probe_scratch_size(void);
+sla_status_t sla_probe_mfma_peak(int32_t iters, void *scratch, size_t scratch_bytes, double *tflops,
+                                 double *sclk_ghz, void *stream);
 
 const char *sla_status_string(sla_status_t s);
 const char *sla_last_error(void); /* thread-local message of the last failure */

@@ -15,17 +15,18 @@ LIB_PATH = os.path.join(HERE, "libsla_mi355x.so")
 SLA_OK, SLA_ERR_NULL, SLA_ERR_INVALID, SLA_ERR_UNSUPPORTED, SLA_ERR_WORKSPACE, SLA_ERR_HIP, \
     SLA_ERR_DEVICE = range(7)
 SLA_F32, SLA_BF16 = 0, 1
-SLA_OP_FWD, SLA_OP_BWD, SLA_OP_DQ = 0, 1, 2
+SLA_OP_FWD, SLA_OP_BWD = 0, 1
 SLA_SCHED_RECORD_INTS = 12
 SLA_BWD_ALL, SLA_BWD_PREPARE, SLA_BWD_DKDV, SLA_BWD_DQ = 0, 1, 2, 3
 
 # every symbol include/sla.h declares
 EXPORTS = (
-    "sla_workspace_size", "sla_bwd_dq_mode", "sla_fwd", "sla_fwd_candidates_workspace_size",
+    "sla_workspace_size", "sla_fwd", "sla_fwd_candidates_workspace_size",
     "sla_fwd_candidates", "sla_bwd", "sla_bwd_stage", "sla_schedule_capacity", "sla_schedule_tile",
     "sla_schedule", "sla_schedule_host", "sla_count_pairs_host", "stu_layer_workspace_size", "stu_layer_fwd",
     "stu_layer_bwd_workspace_size", "stu_layer_bwd", "stu_quantize_rows_fp8",
-    "stu_layer_fp8_workspace_size", "stu_layer_fwd_fp8", "stu_gather_targets", "stu_truncate", "sla_probe_mfma_peak", "sla_status_string",
+    "stu_layer_fp8_workspace_size", "stu_layer_fwd_fp8", "stu_gather_targets", "stu_truncate", "sla_probe_scratch_size",
+    "sla_probe_mfma_peak", "sla_status_string",
     "sla_last_error",
 )
 
@@ -45,6 +46,7 @@ class SLAProblem(ctypes.Structure):
         ("contextual_len", ctypes.c_int32),
         ("max_seq_len", ctypes.c_int32),
         ("alpha", ctypes.c_float),
+        ("out_f32", ctypes.c_int32),
     ]
 
 
@@ -77,8 +79,6 @@ def load(path: str = LIB_PATH):
         PP = ctypes.POINTER(SLAProblem)
         lib.sla_workspace_size.argtypes = [PP, ctypes.c_int]
         lib.sla_workspace_size.restype = sz
-        lib.sla_bwd_dq_mode.argtypes = [PP]
-        lib.sla_bwd_dq_mode.restype = ctypes.c_int
         lib.sla_fwd.argtypes = [PP, P, i64, P, i64, P, i64, P, i64, P, sz, P]
         lib.sla_fwd.restype = ctypes.c_int
         lib.sla_bwd.argtypes = [PP, P, i64, P, i64, P, i64, P, i64, P, i64, P, i64, P, i64, P, sz,
@@ -103,7 +103,9 @@ def load(path: str = LIB_PATH):
         lib.sla_count_pairs_host.argtypes = [i32, P, P, i32, i32, i32]
         lib.sla_count_pairs_host.restype = i64
         DBL = ctypes.POINTER(ctypes.c_double)
-        lib.sla_probe_mfma_peak.argtypes = [i32, DBL, DBL, P]
+        lib.sla_probe_scratch_size.argtypes = []
+        lib.sla_probe_scratch_size.restype = sz
+        lib.sla_probe_mfma_peak.argtypes = [i32, P, sz, DBL, DBL, P]
         lib.sla_probe_mfma_peak.restype = i32
         DP = ctypes.POINTER(STULayerDesc)
         lib.stu_layer_workspace_size.argtypes = [DP]

@@ -26,7 +26,7 @@ SOURCES = [
     "sla_sched.hip",
     "sla_fwd_bf16.hip",
     "sla_bwd_bf16.hip",
-    "sla_dq_ds.hip",
+    "sla_dq.hip",
     "sla_f32.hip",
     "stu_kernels.hip",
     "stu_bwd.hip",
@@ -43,9 +43,9 @@ COMMON_FLAGS = [
 ]
 # device code only: keep the compiler from emitting packed fp32 arithmetic
 HIP_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-# Per-file code generation choices (none at present: the default machine
-# scheduler gives the dK/dV kernel its best schedule without spills).
-SOURCE_FLAGS: dict = {}
+# Per-file code generation choices.  dK/dV: MFMA results in VGPRs (the S and
+# dP accumulators feed VALU code; left in AGPRs they are copied out first).
+SOURCE_FLAGS: dict = {"sla_bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _hipcc() -> str:

@@ -88,17 +88,21 @@ sla_status_t validate_problem(const sla_problem_t *p)
         return fail(SLA_ERR_INVALID, "k1, k2 and contextual_len must be >= 0");
     if (p->max_seq_len < 1) return fail(SLA_ERR_INVALID, "max_seq_len must be >= 1");
     if (!std::isfinite(p->alpha)) return fail(SLA_ERR_INVALID, "alpha must be finite");
+    if (p->out_f32 != 0 && p->out_f32 != 1) return fail(SLA_ERR_INVALID, "out_f32 must be 0 or 1");
     return SLA_OK;
 }
 
+// elem_f32: the tensor holds fp32 elements (the f32 path, or an output of
+// the bf16 path with out_f32 set), else bf16
 sla_status_t validate_tensor(const char *name, const void *ptr, int64_t ld, const sla_problem_t *p,
-                             int d)
+                             int d, bool output = false)
 {
     if (!ptr) return fail(SLA_ERR_NULL, "%s is NULL", name);
     if (ld < (int64_t)p->num_heads * d)
         return fail(SLA_ERR_INVALID, "%s: token stride %lld < H*d = %d", name, (long long)ld,
                     p->num_heads * d);
-    const int elems16 = p->dtype == SLA_BF16 ? 8 : 4;
+    const bool f32 = p->dtype == SLA_F32 || (output && p->out_f32);
+    const int elems16 = f32 ? 4 : 8;
     if (ld % elems16 != 0)
         return fail(SLA_ERR_UNSUPPORTED, "%s: token stride %lld is not a multiple of 16 bytes",
                     name, (long long)ld);
@@ -154,31 +158,14 @@ WsLayout layout(const sla_problem_t *p, int op)
     w.part_slots = np_max * chunk_sum;
     w.bwd_items = T / BWD_BN + B + 1 + w.part_slots;
     w.red_items = np_max * B;
-    w.rt_items = T / DS_BM + 2 * B + 1;
     w.sched_off = 0;
-    const size_t sched_bytes = sizeof(int32_t) * (5 * (size_t)(B + 1) + (size_t)B) +
-                               sizeof(float) * (ABSMAX_BLOCKS + 1);
+    const size_t sched_bytes = sizeof(int32_t) * (4 * (size_t)(B + 1) + (size_t)B);
     w.part_off = round_up(sched_bytes, 256);
-    size_t part_bytes = 0, ds_bytes = 0, kh_bytes = 0;
-    w.ds_slots = 0;
-    if (op == SLA_OP_BWD) {
+    size_t part_bytes = 0;
+    if (op == SLA_OP_BWD)
         part_bytes = (size_t)w.part_slots * p->num_heads * BWD_BN * (size_t)(p->d_qk + p->d_v) *
                      sizeof(float);
-        // dQ from stored dS: bf16, d in {64, 128}, and a bounded number of key
-        // tiles per row tile (a long local window stores O(L * K1) values)
-        const long long slots = ds_slots_bound(T, p->k1, K2e);
-        if (p->dtype == SLA_BF16 && (p->d_qk == 64 || p->d_qk == 128) && slots <= DS_MAX_SLOTS) {
-            w.ds_slots = (int)slots;
-            // block 0: zeros (written by the schedule kernel), read by dQ for
-            // key tiles a row half does not visit; the last block: discarded
-            // dS stores of the dK/dV kernel
-            ds_bytes = ((size_t)w.rt_items * p->num_heads * (size_t)slots + 2) * DS_BM * DS_BN * 2;
-            kh_bytes = (size_t)T * p->num_heads * p->d_qk * 2;
-        }
-    }
-    w.ds_off = w.part_off + round_up(part_bytes, 256);
-    w.kh_off = w.ds_off + round_up(ds_bytes, 256);
-    w.total = w.kh_off + round_up(kh_bytes, 256);
+    w.total = w.part_off + round_up(part_bytes, 256);
     return w;
 }
 
@@ -190,7 +177,7 @@ sla_status_t make_params(const sla_problem_t *p, int op, void *ws, size_t ws_byt
         return fail(SLA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", ws_bytes, w.total);
     if (!aligned16(ws)) return fail(SLA_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
     const int64_t H = p->num_heads;
-    if (w.fwd_items * H > INT32_MAX || w.bwd_items * H > INT32_MAX || w.rt_items * H > INT32_MAX)
+    if (w.fwd_items * H > INT32_MAX || w.bwd_items * H > INT32_MAX)
         return fail(SLA_ERR_UNSUPPORTED, "problem too large for one launch");
     std::memset(&a, 0, sizeof(a));
     a.offsets = p->offsets;
@@ -204,6 +191,7 @@ sla_status_t make_params(const sla_problem_t *p, int op, void *ws, size_t ws_byt
     a.inv_n = 1.0f / (float)p->max_seq_len;
     a.out_scale = p->alpha / (float)p->max_seq_len;
     a.neg_alpha_log2e = -p->alpha * 1.4426950408889634f;
+    a.out_f32 = p->dtype == SLA_BF16 && p->out_f32;
     int32_t *s = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + w.sched_off);
     const int B1 = p->batch + 1;
     a.s.fwd_base = s;
@@ -211,21 +199,11 @@ sla_status_t make_params(const sla_problem_t *p, int op, void *ws, size_t ws_byt
     a.s.red_base = s + 2 * B1;
     a.s.part_base = s + 3 * B1;
     a.s.nch = s + 4 * B1;
-    a.s.rt_base = s + 4 * B1 + p->batch;
-    a.absmax_part = reinterpret_cast<float *>(s + 5 * B1 + p->batch);
-    a.grad_scale = a.absmax_part + ABSMAX_BLOCKS;
     a.T = p->total_tokens;
     a.partials = reinterpret_cast<float *>(static_cast<char *>(ws) + w.part_off);
     a.grid_fwd = (int)(w.fwd_items * H);
     a.grid_bwd = (int)(w.bwd_items * H);
     a.grid_red = (int)(w.red_items * H);
-    a.grid_rt = (int)(w.rt_items * H);
-    a.ds_slots = w.ds_slots;
-    if (w.ds_slots > 0) {
-        a.ds = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + w.ds_off);
-        a.kh = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + w.kh_off);
-        a.ds_discard = 1 + w.rt_items * H * (int64_t)w.ds_slots;
-    }
     return SLA_OK;
 }
 
@@ -278,9 +256,22 @@ StuBwdLayout stu_bwd_layout(const stu_layer_desc_t *d)
 
 extern "C" {
 
-sla_status_t sla_probe_mfma_peak(int32_t iters, double *tflops, double *sclk_ghz, void *stream)
+size_t sla_probe_scratch_size(void)
 {
-    if (!tflops || !sclk_ghz) return fail(SLA_ERR_NULL, "tflops or sclk_ghz is NULL");
+    int dev = -1, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return 0;
+    // the sink (one float per thread of 4 workgroups of 256 per CU), then the
+    // two clock counters
+    return round_up(sizeof(float) * (size_t)4 * cus * 256, 256) + 2 * sizeof(unsigned long long);
+}
+
+sla_status_t sla_probe_mfma_peak(int32_t iters, void *scratch, size_t scratch_bytes,
+                                 double *tflops, double *sclk_ghz, void *stream)
+{
+    if (!tflops || !sclk_ghz || !scratch) return fail(SLA_ERR_NULL, "tflops, sclk_ghz or scratch is NULL");
     if (iters < 1 || iters > (1 << 20)) return fail(SLA_ERR_INVALID, "iters %d outside [1, 2^20]", iters);
     sla_status_t st = check_device();
     if (st != SLA_OK) return st;
@@ -289,15 +280,19 @@ sla_status_t sla_probe_mfma_peak(int32_t iters, double *tflops, double *sclk_ghz
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return hip_fail(e, "device attributes");
     const int blocks = 4 * cus;
+    const size_t sink_bytes = round_up(sizeof(float) * (size_t)blocks * 256, 256);
+    if (scratch_bytes < sink_bytes + 2 * sizeof(unsigned long long))
+        return fail(SLA_ERR_WORKSPACE, "probe scratch of %zu bytes < %zu required", scratch_bytes,
+                    sink_bytes + 2 * sizeof(unsigned long long));
+    if (!aligned16(scratch)) return fail(SLA_ERR_UNSUPPORTED, "probe scratch is not 16-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    float *sink = nullptr;
-    unsigned long long *clk = nullptr;
+    float *sink = static_cast<float *>(scratch);
+    unsigned long long *clk =
+        reinterpret_cast<unsigned long long *>(static_cast<char *>(scratch) + sink_bytes);
     hipEvent_t e0 = nullptr, e1 = nullptr;
     unsigned long long hclk[2] = {0, 0};
     float ms = 0.0f;
-    e = hipMalloc(&sink, sizeof(float) * (size_t)blocks * 256);
-    if (e == hipSuccess) e = hipMalloc(&clk, 2 * sizeof(unsigned long long));
-    if (e == hipSuccess) e = hipEventCreate(&e0);
+    e = hipEventCreate(&e0);
     if (e == hipSuccess) e = hipEventCreate(&e1);
     if (e == hipSuccess) e = launch_mfma_peak(blocks, iters, sink, clk, s);  // warm-up
     if (e == hipSuccess) e = hipEventRecord(e0, s);
@@ -308,8 +303,6 @@ sla_status_t sla_probe_mfma_peak(int32_t iters, double *tflops, double *sclk_ghz
     if (e == hipSuccess) e = hipMemcpy(hclk, clk, sizeof(hclk), hipMemcpyDeviceToHost);
     if (e0) (void)hipEventDestroy(e0);
     if (e1) (void)hipEventDestroy(e1);
-    if (clk) (void)hipFree(clk);
-    if (sink) (void)hipFree(sink);
     if (e != hipSuccess) return hip_fail(e, "MFMA probe");
     if (!(ms > 0.0f)) return fail(SLA_ERR_DEVICE, "MFMA probe: no elapsed time");
     *tflops = mfma_peak_flops(blocks, iters) / ((double)ms * 1e-3) / 1e12;
@@ -341,25 +334,18 @@ size_t sla_workspace_size(const sla_problem_t *p, int op)
     return layout(p, op).total;
 }
 
-int sla_bwd_dq_mode(const sla_problem_t *p)
-{
-    if (validate_problem(p) != SLA_OK) return -1;
-    return layout(p, SLA_OP_BWD).ds_slots > 0 ? 1 : 0;
-}
-
 int64_t sla_schedule_capacity(const sla_problem_t *p, int op)
 {
     if (validate_problem(p) != SLA_OK) return -1;
-    if (op != SLA_OP_FWD && op != SLA_OP_BWD && op != SLA_OP_DQ) return -1;
+    if (op != SLA_OP_FWD && op != SLA_OP_BWD) return -1;
     const WsLayout w = layout(p, SLA_OP_FWD);
-    return op == SLA_OP_FWD ? w.fwd_items : (op == SLA_OP_BWD ? w.bwd_items : w.rt_items);
+    return op == SLA_OP_FWD ? w.fwd_items : w.bwd_items;
 }
 
 int32_t sla_schedule_tile(int op, int which)
 {
     if (op == SLA_OP_FWD) return which == 0 ? FWD_BM : FWD_BN;
     if (op == SLA_OP_BWD) return which == 0 ? BWD_BN : BWD_BM;
-    if (op == SLA_OP_DQ) return which == 0 ? DS_BM : DS_BN;
     return -1;
 }
 
@@ -368,8 +354,7 @@ sla_status_t sla_schedule(const sla_problem_t *p, int op, int32_t *records, int6
 {
     sla_status_t st = validate_problem(p);
     if (st != SLA_OK) return st;
-    if (op != SLA_OP_FWD && op != SLA_OP_BWD && op != SLA_OP_DQ)
-        return fail(SLA_ERR_INVALID, "bad op %d", op);
+    if (op != SLA_OP_FWD && op != SLA_OP_BWD) return fail(SLA_ERR_INVALID, "bad op %d", op);
     if (!records || !count) return fail(SLA_ERR_NULL, "records or count is NULL");
     if (capacity < sla_schedule_capacity(p, op))
         return fail(SLA_ERR_INVALID, "capacity below sla_schedule_capacity");
@@ -380,7 +365,6 @@ sla_status_t sla_schedule(const sla_problem_t *p, int op, int32_t *records, int6
     if ((st = validate_layout(p->batch, p->total_tokens, p->offsets, p->num_targets, -1, workspace,
                               s)) != SLA_OK)
         return st;
-    a.absmax_part = nullptr;
     hipError_t e = launch_sched(a, s);
     if (e != hipSuccess) return hip_fail(e, "schedule kernel");
     e = launch_sched_dump(a, op, records, capacity, count, s);
@@ -397,7 +381,7 @@ int64_t sla_schedule_host(const sla_problem_t *p, int op, const int64_t *offsets
     hp.num_targets = num_targets_host;
     p = &hp;
     if (validate_problem(p) != SLA_OK) return -1;
-    if (op != SLA_OP_FWD && op != SLA_OP_BWD && op != SLA_OP_DQ) {
+    if (op != SLA_OP_FWD && op != SLA_OP_BWD) {
         fail(SLA_ERR_INVALID, "bad op %d", op);
         return -1;
     }
@@ -434,13 +418,11 @@ sla_status_t sla_fwd(const sla_problem_t *p, const void *q, int64_t ldq, const v
     if ((st = validate_tensor("q", q, ldq, p, p->d_qk)) != SLA_OK) return st;
     if ((st = validate_tensor("k", k, ldk, p, p->d_qk)) != SLA_OK) return st;
     if ((st = validate_tensor("v", v, ldv, p, p->d_v)) != SLA_OK) return st;
-    if ((st = validate_tensor("o", o, ldo, p, p->d_v)) != SLA_OK) return st;
+    if ((st = validate_tensor("o", o, ldo, p, p->d_v, true)) != SLA_OK) return st;
     AttnParams a;
     if ((st = make_params(p, SLA_OP_FWD, workspace, ws_bytes, a)) != SLA_OK) return st;
     if ((st = check_device()) != SLA_OK) return st;
-    if (p->batch == 0 || p->total_tokens == 0) return SLA_OK;
     a.q = q; a.k = k; a.v = v; a.o = o;
-    a.absmax_part = nullptr;
     a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.ldo = ldo;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = validate_layout(p->batch, p->total_tokens, p->offsets, p->num_targets, -1, workspace,
@@ -489,7 +471,7 @@ sla_status_t sla_fwd_candidates(const sla_problem_t *p, const int64_t *cand_offs
     if ((st = validate_tensor("q_c", q_c, ldq, &pc, p->d_qk)) != SLA_OK) return st;
     if ((st = validate_tensor("k_c", k_c, ldkc, &pc, p->d_qk)) != SLA_OK) return st;
     if ((st = validate_tensor("v_c", v_c, ldvc, &pc, p->d_v)) != SLA_OK) return st;
-    if ((st = validate_tensor("o_c", o_c, ldo, &pc, p->d_v)) != SLA_OK) return st;
+    if ((st = validate_tensor("o_c", o_c, ldo, &pc, p->d_v, true)) != SLA_OK) return st;
     sla_problem_t pw = *p;  // workspace and grid bound: the larger row count
     if (total_candidates > pw.total_tokens) pw.total_tokens = total_candidates;
     AttnParams a;
@@ -499,7 +481,6 @@ sla_status_t sla_fwd_candidates(const sla_problem_t *p, const int64_t *cand_offs
     a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.ldo = ldo; a.ldkc = ldkc; a.ldvc = ldvc;
     a.cand_offsets = cand_offsets;
     a.num_targets = nullptr;
-    a.absmax_part = nullptr;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = validate_layout(p->batch, p->total_tokens, p->offsets, nullptr, -1, workspace, s)) !=
         SLA_OK)
@@ -529,10 +510,10 @@ sla_status_t sla_bwd_stage(const sla_problem_t *p, int stage, const void *q, int
     if ((st = validate_tensor("v", v, ldv, p, p->d_v)) != SLA_OK) return st;
     if ((st = validate_tensor("dout", dout, lddo, p, p->d_v)) != SLA_OK) return st;
     if (stage == SLA_BWD_ALL || stage == SLA_BWD_DQ)
-        if ((st = validate_tensor("dq", dq, lddq, p, p->d_qk)) != SLA_OK) return st;
+        if ((st = validate_tensor("dq", dq, lddq, p, p->d_qk, true)) != SLA_OK) return st;
     if (stage == SLA_BWD_ALL || stage == SLA_BWD_DKDV) {
-        if ((st = validate_tensor("dk", dk, lddk, p, p->d_qk)) != SLA_OK) return st;
-        if ((st = validate_tensor("dv", dv, lddv, p, p->d_v)) != SLA_OK) return st;
+        if ((st = validate_tensor("dk", dk, lddk, p, p->d_qk, true)) != SLA_OK) return st;
+        if ((st = validate_tensor("dv", dv, lddv, p, p->d_v, true)) != SLA_OK) return st;
     }
     AttnParams a;
     if ((st = make_params(p, SLA_OP_BWD, workspace, ws_bytes, a)) != SLA_OK) return st;
@@ -546,12 +527,6 @@ sla_status_t sla_bwd_stage(const sla_problem_t *p, int stage, const void *q, int
         return st;
     hipError_t e = hipSuccess;
     if (stage == SLA_BWD_ALL || stage == SLA_BWD_PREPARE) {
-        if (p->dtype == SLA_BF16) {
-            e = launch_absmax(a, s);
-            if (e != hipSuccess) return hip_fail(e, "gradient scale kernel");
-        } else {
-            a.absmax_part = nullptr;
-        }
         e = launch_sched(a, s);
         if (e != hipSuccess) return hip_fail(e, "schedule kernel");
     }
@@ -633,6 +608,7 @@ sla_status_t stu_layer_fwd(const stu_layer_desc_t *d, const void *x, const float
     sla_status_t st = validate_problem(p);
     if (st != SLA_OK) return st;
     if (p->dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "the STU layer is bf16 only");
+    if (p->out_f32) return fail(SLA_ERR_UNSUPPORTED, "the STU layer stores bf16 (out_f32 must be 0)");
     if (!x || !ln1_w || !w_uvqk || !ln2_w || !w_out || !out)
         return fail(SLA_ERR_NULL, "a required layer pointer is NULL");
     const int D = d->hidden, H = p->num_heads, dv = p->d_v, dqk = p->d_qk;
@@ -706,6 +682,7 @@ sla_status_t stu_layer_bwd(const stu_layer_desc_t *d, const void *x, const void 
     sla_status_t st = validate_problem(p);
     if (st != SLA_OK) return st;
     if (p->dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "the STU layer is bf16 only");
+    if (p->out_f32) return fail(SLA_ERR_UNSUPPORTED, "the STU layer stores bf16 (out_f32 must be 0)");
     if (!ln1_w || !w_uvqk || !ln2_w || !w_out)
         return fail(SLA_ERR_NULL, "a required layer pointer is NULL");
     if (p->total_tokens > 0 && (!x || !dout || !dx))
@@ -872,6 +849,7 @@ sla_status_t stu_layer_fwd_fp8(const stu_layer_desc_t *d, const void *x, const f
     sla_status_t st = validate_problem(p);
     if (st != SLA_OK) return st;
     if (p->dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "the STU layer is bf16 only");
+    if (p->out_f32) return fail(SLA_ERR_UNSUPPORTED, "the STU layer stores bf16 (out_f32 must be 0)");
     if (!x || !ln1_w || !w_uvqk_q || !w_uvqk_scale || !ln2_w || !w_out_q || !w_out_scale || !out)
         return fail(SLA_ERR_NULL, "a required layer pointer is NULL");
     const int D = d->hidden, H = p->num_heads, dv = p->d_v, dqk = p->d_qk;

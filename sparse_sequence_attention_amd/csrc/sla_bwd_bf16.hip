@@ -1,56 +1,79 @@
-// sla_bwd_bf16.hip -- SLA backward on gfx950: bf16 MFMA, fp32 accumulation,
-// no atomics.
+// sla_bwd_bf16.hip -- SLA backward dK / dV on gfx950: bf16 MFMA, fp32
+// accumulation, no atomics.
 //
 // With a_ij = SiLU(alpha s_ij), s_ij = q_i . k_j, O_i = (1/N) sum_j a_ij v_j
 // (ULTRA-HSTU paper, section 3 Eq.3 under the semi-local mask of section
 // 4.2.1 Eq.7), the chain rule gives, over visible pairs,
 //   dV_j = (1/N) sum_i a_ij dO_i
 //   dS_ij = (alpha/N) (dO_i . v_j) sigma_ij (1 + t_ij (1 - sigma_ij)),  t = alpha s
-//   dQ_i = sum_j dS_ij k_j,     dK_j = sum_i dS_ij q_i.
-// The kernels keep s*sigma and g*sigma*(1 + t(1 - sigma)) (g = dO.v) in the
-// MFMA operands and apply 1/N and alpha once in the epilogues.  The products
-// that consume P or dS run on fp16 operands (P, dS, dO^T, Q^T, K^T); dS and dO
-// are multiplied by a power of two G that maps max|dO| into [1, 2) (computed on
-// the device before these kernels) so that fp16's range follows the gradient
-// scale, and the epilogues divide it out.
+//   dK_j = sum_i dS_ij q_i.
+// The kernel keeps s*sigma and g*sigma*(1 + t(1 - sigma)) (g = dO.v) as MFMA
+// operands and applies alpha/N once in the epilogue.
 //
-// Ownership split (the KV-parallel / Q-parallel pair of backward schedules the
-// WHALE notes describe): the dK/dV kernel owns a 128-key tile and walks the row
-// tiles that see it; the dQ kernel owns a 128-row tile and walks its key tiles,
-// recomputing S and dP.  Global-prefix key tiles are seen by every later row,
-// so they are cut into row chunks whose fp32 partial sums a third kernel adds
-// in chunk order: results are bitwise reproducible.
+// Ownership (the key-parallel half of the KV- / Q-parallel backward split the
+// WHALE notes describe; dQ is sla_dq.hip's row-parallel kernel): a workgroup
+// owns a 128-key tile of one head and walks the 64-row steps of the rows that
+// see it.  Global-prefix key tiles are seen by every later row, so they are
+// cut into row chunks whose fp32 partial sums a second kernel adds in chunk
+// order: results are bitwise reproducible.
+//
+// Layout: eight waves, two per SIMD.  The bf16 K and V rows of the key tile
+// sit in LDS for the whole item (64 KB at d = 128); the Q and dO rows of the
+// 64-row steps come HBM -> LDS by DMA into a ring of three stages (96 KB),
+// two steps ahead, with one LDS-only barrier per step.  Wave w owns keys
+// 32 (w % 4) .. + 32 and rows 32 (w / 4) .. + 32 of each step:
+//   S  (32 rows x 32 keys) = Q K^T,  dP = dO V^T      row operands from LDS
+//   P, dS in registers (masked only on steps that cross the mask's edges)
+//   dV (32 keys x D) += P^T dO,  dK += dS^T Q          transposing LDS reads
+// and the two row halves of a key block add their dK / dV sums through LDS
+// at the end.  The steps that need no mask (full 64-row history steps that
+// see every key of the tile) run as one branch-free loop between the masked
+// steps before and after them.
+//
+// Precision.  Q.K^T and dO.V^T take the bf16 inputs as stored.  The computed
+// operands of dV = P^T dO and dK = dS^T Q are rounded to bf16 (8 significant
+// bits); their rounding errors are independent across the rows a key sums
+// over.  The keys of the global prefix are seen by every row of the sequence,
+// so their dK and dV are sums of up to L terms and the largest values of the
+// two tensors (tens of times their rms at 16K-token histories); there P and
+// dS enter the products as the sum of two bf16 numbers, hi = bf16(x) and
+// lo = bf16(x - hi) (16 significant bits), at the price of a second MFMA per
+// product on those key tiles only.
 #include <type_traits>
 
 #include "sla_device.h"
 #include "sla_kernels.h"
-#include "sla_tiles.h"
 
 namespace sla {
 
-constexpr int DS_SLOT_TAB = 512;  // steps of a dK/dV item whose dS slot is tabulated
-
-// ---------------------------------------------------------------------------
-// dK / dV
-// ---------------------------------------------------------------------------
-// 16-byte chunk swizzle of the fp16 [64][D] Q / G dO tiles of the dK/dV
-// kernel: logical chunk c of row r sits at c ^ hswz<D>(r).  With u = r*D/128
-// (the 256-byte bank row) and Q4 = D/32, hswz = 4*(u % Q4) + (u / Q4) % 4:
-// the 16 rows that a 16-lane pass of a 16-byte read touches, and the 4 rows x
-// 64 bytes that a 32-lane pass of a transposing read touches, fall in
-// distinct banks (gfx950 serves ds_read_b128 16 lanes and ds_read_b64_tr_b16
-// 32 lanes at a time).
+// 16-byte chunk swizzle of the bf16 [64][D] Q / dO stage tiles: logical chunk
+// c of row r sits at c ^ hswz<D>(r).  With u = r*D/128 (the 256-byte bank row)
+// and Q4 = D/32, hswz = 4*(u % Q4) + (u / Q4) % 4: the 16 rows that a 16-lane
+// pass of a 16-byte read touches, and the 4 rows x 64 bytes that a 32-lane
+// pass of a transposing read touches, fall in distinct banks.
 template <int D>
 __device__ __forceinline__ int hswz(int r)
 {
-    constexpr int Q4 = D / 32;
-    const int u = r * D / 128;
-    return 4 * (u % Q4) + (u / Q4) % 4;
+    // unsigned bit operations: the compiler then sees that adding a multiple
+    // of 32 rows (the second row block) leaves the swizzle unchanged
+    constexpr unsigned Q4 = D / 32;
+    const unsigned u = ((unsigned)r * D) >> 7;
+    return (int)(4u * (u & (Q4 - 1)) + ((u / Q4) & 3u));
 }
 
 constexpr int DKDV_THREADS = 512;
+constexpr int DKDV_STAGES = 3;
 
-template <int D>
+// x - float(hi) for the 8 values of hi = bf16(x), rounded to bf16: the low
+// part of the two-term bf16 representation x ~ hi + lo
+__device__ __forceinline__ bf16x8 lo_part(const float *x, const bf16x8 &hi)
+{
+    const uint4 u = as_u4(hi);
+    return cvt8(x[0] - bf16_lo(u.x), x[1] - bf16_hi(u.x), x[2] - bf16_lo(u.y), x[3] - bf16_hi(u.y),
+                x[4] - bf16_lo(u.z), x[5] - bf16_hi(u.z), x[6] - bf16_lo(u.w), x[7] - bf16_hi(u.w));
+}
+
+template <int D, bool OUTF32>
 __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(AttnParams p)
 {
     constexpr int BN = BWD_BN, BM = BWD_BM;
@@ -58,17 +81,18 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
     constexpr int NC = D / 16, NDB = D / 32, CPR = D / 8;
     constexpr int TILE = BM * D;             // elements of one staged 64-row tile
     constexpr int TCH = BM * CPR;            // 16-byte chunks of one staged tile
-    constexpr int KVS = D + 8;               // padded K / V row: 16-byte reads of 16
-                                             // consecutive keys hit distinct banks
+    constexpr int SPS = 2 * TCH / NT;        // DMA loads per thread and step
+    constexpr int KCH = BN * CPR;            // 16-byte chunks of the K (or V) tile
+    constexpr int KPT = 2 * KCH / NT;        // DMA loads per thread of the K and V tiles
+    constexpr int NST = DKDV_STAGES;
     static_assert(BM == 64 && BN == 128, "64-row steps over 128-key tiles");
-    // kv: K then V of the key tile (fp16, padded rows).  cs0 / cs1: two
-    // stages of Q and G dO rows (swizzled); the DMA brings a step's bf16 rows
-    // into one stage while the other is read, and each thread then converts
-    // its own chunks in place to fp16.  Separate arrays, so that the compiler
-    // can tell the DMA into one stage from the reads of the other.
-    __shared__ __align__(16) uint16_t kv[2 * BN * KVS];
-    __shared__ __align__(16) uint16_t cs0[2 * TILE], cs1[2 * TILE];
-    __shared__ int16_t slot_tab[DS_SLOT_TAB];
+    static_assert((2 * TCH) % NT == 0 && SPS <= 8, "whole DMA rounds, at most 8 per thread");
+    static_assert((2 * KCH) % NT == 0 && KPT <= 8, "whole DMA rounds of the key tile");
+    // [K | V] of the key tile (bf16, swizzled rows), then a ring of NST stages
+    // of [Q | dO] rows filled by DMA NST - 1 steps ahead: 64 + 96 KB at d = 128
+    __shared__ __align__(16) uint16_t lds[2 * BN * D + NST * 2 * TILE];
+    uint16_t *const kvs = lds;
+    uint16_t *const ring = lds + 2 * BN * D;
 
     const int nrec = p.s.bwd_base[p.B];
     const int item = xcd_remap(blockIdx.x, nrec * p.H);
@@ -82,34 +106,18 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
     const BwdItem it = bwd_item(sd.L, sd.U, p.k1, p.k2e, BN, BM, rec - uniform(p.s.bwd_base[b]),
                                 np, nch);
 
-    // 8 waves: wave w owns keys 32*(w%4) .. +32 of the tile and rows
-    // 32*(w/4) .. +32 of every 64-row step; the two row halves of a key block
-    // add their dK/dV sums at the end.  Two waves per SIMD.
+    // 8 waves, two per SIMD: wave w owns keys 32*(w%4) .. +32 of the tile and
+    // rows 32*(w/4) .. +32 of every 64-row step; the two row halves of a key
+    // block add their dK/dV sums at the end (fixed order, deterministic).
     const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
     const int kw = wv & 3, rh = wv >> 2;
     const int l32 = lane & 31, hl = lane >> 5;
-    const int kj = it.c0 + 32 * kw + l32;  // this lane's key (operands, mask)
+    const int kj = it.c0 + 32 * kw + l32;  // this lane's key (mask)
 
     const uint16_t *qg = reinterpret_cast<const uint16_t *>(p.q) + sd.base * p.ldq + h * D;
     const uint16_t *kg = reinterpret_cast<const uint16_t *>(p.k) + sd.base * p.ldk + h * D;
     const uint16_t *vg = reinterpret_cast<const uint16_t *>(p.v) + sd.base * p.ldv + h * D;
     const uint16_t *gg = reinterpret_cast<const uint16_t *>(p.dout) + sd.base * p.lddo + h * D;
-
-    // K and V of the tile into LDS as fp16 (keys past c1 as zeros); the first
-    // chunk of a key tile also writes the fp16 copy of K that dQ = dS K reads
-    // on the stored-dS path
-    const bool write_kh = p.kh != nullptr && it.chunk == 0;
-    for (int i = tid; i < BN * CPR; i += NT) {
-        const int key = i / CPR, c = i % CPR;
-        const halfx8 kh8 = bf16x8_to_halfx8(as_bf16x8(ld16_row(kg, p.ldk, it.c0 + key, it.c1, 8 * c)));
-        const halfx8 vh8 = bf16x8_to_halfx8(as_bf16x8(ld16_row(vg, p.ldv, it.c0 + key, it.c1, 8 * c)));
-        *reinterpret_cast<halfx8 *>(kv + key * KVS + 8 * c) = kh8;
-        *reinterpret_cast<halfx8 *>(kv + (BN + key) * KVS + 8 * c) = vh8;
-        if (write_kh && it.c0 + key < it.c1)
-            *reinterpret_cast<halfx8 *>(p.kh + (sd.base + it.c0 + key) * ((int64_t)p.H * D) +
-                                        h * D + 8 * c) = kh8;
-    }
-    const int rt_first = p.ds != nullptr ? uniform(p.s.rt_base[b]) : 0;
 
     // row steps: history tiles covering [ha, hb), then target tiles covering [ta, tb)
     int h_first = 0, nh = 0, t_first = 0, nt = 0;
@@ -122,101 +130,114 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
         nt = cdiv(it.tb - sd.U, BM) - t_first;
     }
     const int nsteps = uniform(nh + nt);
-    auto step_rows = [&](int s, int &m0, int &m1) {
-        if (s < nh) {
-            m0 = (h_first + s) * BM;
-            m1 = imin(m0 + BM, sd.U);
-        } else {
-            m0 = sd.U + (t_first + s - nh) * BM;
-            m1 = imin(m0 + BM, sd.L);
-        }
+    auto step_rows = [&](int s, int &m0, int &m1) __attribute__((always_inline)) {
+        const bool hist = s < nh;
+        m0 = hist ? (h_first + s) * BM : sd.U + (t_first + s - nh) * BM;
+        m1 = imin(m0 + BM, hist ? sd.U : sd.L);
     };
-    // stored-dS path: the slot of this key tile in the visiting order of the
-    // 64-row tile [m0, m1) that step s covers, tabulated for the first
-    // DS_SLOT_TAB steps before the loop (scalar work kept out of the steps)
-    auto step_slot = [&](int m0, int m1) {
-        const Ranges kr = fwd_key_ranges(sd.L, sd.U, p.k1, p.k2e, m0, m1, DS_BN);
-        return cursor_slot(kr, it.c0, DS_BN);
+    // A full step needs no mask: 64 history rows, all of which see every key
+    // of a whole key tile.  Such steps form one run [s_lo, s_hi) (rows from
+    // the diagonal on, up to the end of the window or of the history); the
+    // steps before and after it run the masked body.
+    const bool key_tile_full = (it.c1 - it.c0 == BN);
+    auto is_full = [&](int s) __attribute__((always_inline)) {
+        int m0, m1;
+        step_rows(s, m0, m1);
+        return (m1 == m0 + BM) && (m1 <= sd.U) && key_tile_full && (it.c0 + BN - 1 <= m0) &&
+               ((m1 - 1 - it.c0 < p.k1) || (it.c0 + BN <= p.k2e));
     };
-    if (p.ds != nullptr) {
-        for (int st = tid; st < imin(nsteps, DS_SLOT_TAB); st += NT) {
-            int a0, a1;
-            step_rows(st, a0, a1);
-            slot_tab[st] = (int16_t)step_slot(a0, a1);
-        }
-    }
+    int s_lo = 0;
+    while (s_lo < nsteps && !is_full(s_lo)) ++s_lo;
+    int s_hi = s_lo;
+    while (s_hi < nsteps && is_full(s_hi)) ++s_hi;
+    s_lo = uniform(s_lo);
+    s_hi = uniform(s_hi);
 
     const float nal2e = p.neg_alpha_log2e, alpha = p.alpha;
-    const float gscale = *p.grad_scale;
-    const bool key_tile_full = (it.c1 - it.c0 == BN);
 
-    // Staging is done by the rh = 0 waves alone: the SIMD issues the older
-    // wave of a pair first, so these finish their products earlier and would
-    // otherwise wait at the barrier.  Staging thread t (< NS) owns chunks
-    // P = i*NS + t of a stage: physical chunk P % CPR of row (P % TCH) / CPR
-    // of tile P / TCH (0: Q, 1: dO); the DMA fills it with logical chunk
-    // (P % CPR) ^ hswz(row) and the same thread converts it in place.
-    constexpr int NS = NT / 2;            // staging threads
-    constexpr int SPS = 2 * TCH / NS;     // DMA loads per staging thread and step
-    static_assert(TCH % NS == 0 && SPS <= 8, "whole DMA rounds, at most 8 per thread");
-    auto chunk_tile = [&](int i) { return (i * NS) / TCH; };
-    auto stage = [&](auto S) -> uint16_t * {
-        if constexpr (decltype(S)::value == 0) return cs0;
-        else return cs1;
+    // DMA (gl_lds16_async: the kernel's own waits and barriers order it
+    // against the reads).  Thread t owns chunks P = i*NT + t: physical chunk
+    // P % CPR of row (P % tile chunks) / CPR of tile P / (tile chunks), filled
+    // with logical chunk (P % CPR) ^ hswz(row).  Key rows at or past c1 read
+    // row c1 - 1 (keys never stored); step rows at or past m1 read row m1 - 1
+    // (masked: such steps are never full).  Every step issues exactly SPS
+    // loads per thread, so the wait counts are static.
+    auto issue_kv = [&]() __attribute__((always_inline)) {
+        const int last = uniform(it.c1 - 1 - it.c0);
+        const char *krow = reinterpret_cast<const char *>(kg + (int64_t)it.c0 * p.ldk);
+        const char *vrow = reinterpret_cast<const char *>(vg + (int64_t)it.c0 * p.ldv);
+        const uint32_t ldk_b = (uint32_t)p.ldk * 2u, ldv_b = (uint32_t)p.ldv * 2u;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int P = i * NT + wv * 64 + lane;
+            const int tile = P / KCH;  // K or V (uniform per wave)
+            const int prow = (P % KCH) / CPR;
+            const uint32_t row = (uint32_t)imin(prow, last);
+            const uint32_t c = (uint32_t)((P % CPR) ^ hswz<D>(prow));
+            const char *src = tile == 0 ? krow + (row * ldk_b + 16u * c) : vrow + (row * ldv_b + 16u * c);
+            gl_lds16_async(src, kvs + (i * NT + wv * 64) * 8);
+        }
     };
-    // DMA of the bf16 rows of step t (clamped to the last step) into a stage:
-    // a workgroup-uniform row base plus a 32-bit per-lane offset; rows at or
-    // past m1 read row m1 - 1 (masked: such steps are never full)
     const uint32_t ldq_b = (uint32_t)p.ldq * 2u, lddo_b = (uint32_t)p.lddo * 2u;
-    auto issue = [&](int t, auto S) {
+    auto issue = [&](int t) __attribute__((always_inline)) {
         int m0, m1;
         step_rows(imin(t, nsteps - 1), m0, m1);
         m0 = uniform(m0);
         const int last = uniform(m1 - 1 - m0);
         const char *qrow = reinterpret_cast<const char *>(qg + (int64_t)m0 * p.ldq);
         const char *grow = reinterpret_cast<const char *>(gg + (int64_t)m0 * p.lddo);
-        uint16_t *sb = stage(S);
+        uint16_t *sb = ring + (t % NST) * (2 * TILE);
 #pragma unroll
         for (int i = 0; i < SPS; ++i) {
-            const int P = i * NS + wv * 64 + lane;
-            const int tile = chunk_tile(i);
+            const int P = i * NT + wv * 64 + lane;
+            const int tile = P / TCH;  // Q or dO (uniform per wave)
             const int prow = (P % TCH) / CPR;
             const uint32_t row = (uint32_t)imin(prow, last);
             const uint32_t c = (uint32_t)((P % CPR) ^ hswz<D>(prow));
             const char *src = tile == 0 ? qrow + (row * ldq_b + 16u * c) : grow + (row * lddo_b + 16u * c);
-            gl_lds16(src, sb + (i * NS + wv * 64) * 8);
-        }
-    };
-    // this thread's chunks of a stage, bf16 -> fp16 in place (dO times G)
-    auto convert = [&](auto S) {
-        uint16_t *sb = stage(S);
-        uint4 raw[SPS];
-#pragma unroll
-        for (int i = 0; i < SPS; ++i) raw[i] = *reinterpret_cast<const uint4 *>(sb + 8 * (i * NS + wv * 64 + lane));
-#pragma unroll
-        for (int i = 0; i < SPS; ++i) {
-            const float sc = chunk_tile(i) == 0 ? 1.0f : gscale;
-            const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-            const halfx8 hv = cvt8h(bf16_lo(w[0]) * sc, bf16_hi(w[0]) * sc, bf16_lo(w[1]) * sc,
-                                    bf16_hi(w[1]) * sc, bf16_lo(w[2]) * sc, bf16_hi(w[2]) * sc,
-                                    bf16_lo(w[3]) * sc, bf16_hi(w[3]) * sc);
-            *reinterpret_cast<halfx8 *>(sb + 8 * (i * NS + wv * 64 + lane)) = hv;
+            gl_lds16_async(src, sb + (i * NT + wv * 64) * 8);
         }
     };
 
-    // per-lane LDS offsets (elements).  Row operands: row ar = 32*rh + l32 of
-    // a staged tile (logical chunk 2c + hl) and key row br = 32*kw + l32 of
-    // K / V.  Transposing reads (quarter q = lane/16, j = lane%16): rows
-    // 32*rh + 16*h2 + 8*rr + 4*(q/2) + j/4, columns 32*db + 16*(q%2) + 4*(j%4).
-    const int ar = 32 * rh + l32, br = 32 * kw + l32;
+    // Per-lane LDS byte offsets, computed once.  Row operands: row
+    // 32*rh + l32 of a staged tile and key row 32*kw + l32 of K / V, logical
+    // chunk 2c + hl.  Transposing reads (quarter q = lane/16, j = lane%16):
+    // rows 32*rh + 16*h2 + 8*rr + 4*(q/2) + j/4, columns 32*db + 16*(q%2) +
+    // 4*(j%4): the row order of the S accumulator (8*(r/4) + 4*hl + r%4) as
+    // the k order of the dV / dK products.  The swizzle of a row does not
+    // change when a multiple of 16 is added to it, so h2 (and the dO tile)
+    // are immediate offsets; a step adds its stage's base once.
     const int q4 = lane >> 4, j16 = lane & 15;
-    auto a_off = [&](int c) { return ar * D + 8 * ((2 * c + hl) ^ hswz<D>(ar)); };
-    const int b_base = br * KVS + 8 * hl;  // + 16 c (K), + BN*KVS (V)
-    auto t_off = [&](int h2, int rr, int db) {
-        const int row = 32 * rh + 16 * h2 + 8 * rr + 4 * (q4 >> 1) + (j16 >> 2);
-        const int col = 32 * db + 16 * (q4 & 1) + 4 * (j16 & 3);
-        return row * D + 8 * ((col >> 3) ^ hswz<D>(row)) + (col & 7);
+    typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8_t;
+    auto lds_row = [](uint32_t addr) __attribute__((always_inline)) {
+        return *reinterpret_cast<lds_bf16x8_t *>(addr);
     };
+    auto lds_tr = [](uint32_t addr) __attribute__((always_inline)) {
+        shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_shortx4_t *>(addr));
+        return __builtin_bit_cast(uint2, v);
+    };
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds;
+    // bytes: the [K | V] region (2 BN D bf16), one [Q | dO] stage (2 TILE
+    // bf16), one staged tile
+    constexpr uint32_t KV_BYTES = 4u * BN * D, STAGE_BYTES = 4u * TILE, TILE_BYTES = 2u * TILE;
+    static_assert(KV_BYTES == 2u * BN * D * sizeof(uint16_t), "ring starts after [K | V]");
+    constexpr uint32_t H2_BYTES = 2u * 16u * D;
+    uint32_t aoffs[NC], koffs[NC], toffs[2][NDB];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int ar = 32 * rh + l32, br = 32 * kw + l32;
+        aoffs[c] = 2u * (uint32_t)(ar * D + 8 * ((2 * c + hl) ^ hswz<D>(ar)));
+        koffs[c] = lds_base + 2u * (uint32_t)(br * D + 8 * ((2 * c + hl) ^ hswz<D>(br)));
+    }
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const int row = 32 * rh + 8 * rr + 4 * (q4 >> 1) + (j16 >> 2);
+            const int col = 32 * db + 16 * (q4 & 1) + 4 * (j16 & 3);
+            toffs[rr][db] = 2u * (uint32_t)(row * D + 8 * ((col >> 3) ^ hswz<D>(row)) + (col & 7));
+        }
+    }
 
     floatx16 dkacc[NDB], dvacc[NDB];
 #pragma unroll
@@ -225,180 +246,119 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
         dvacc[i] = zero16();
     }
 
-    // step t in stage S: publish the stage (converted by every thread) with
-    // a barrier that also frees the other stage (read by step t - 1), start
-    // the DMA of step t + 1 into it, compute S, dP, P, dS, dV and dK, then
-    // wait for that DMA and convert this thread's share of it in place.  One
-    // barrier per step; it waits for LDS only, so the DMA stays in flight.
-    auto step = [&](int t, auto S, auto HAS_DS) {
-        constexpr int sidx = decltype(S)::value;
-        constexpr bool has_ds = decltype(HAS_DS)::value;
+    // One step of this wave's 32 rows x 32 keys: S = Q K^T and dP = dO V^T,
+    // then P = s sigma (= SiLU(t) / alpha) and dS = g sigma (1 + t (1 -
+    // sigma)) = g (sigma + a (alpha - alpha sigma)) in fp32 (exp(-t)
+    // overflowing to inf gives sigma = 0, a = 0 and dS = 0, its limit, with
+    // no NaN), masked on partial steps, rounded to bf16 (with the low parts
+    // when split), and the dV, dK products.  Mask: in terms of x = i - kj
+    // (register r has x = x0 + 8*(r/4) + r%4), rows before m1 of a history
+    // step see the key iff 0 <= x < W, W = m1 - kj, capped at K1 unless kj is
+    // a prefix key; rows of a target step iff x < m1 - kj and (x == 0 or kj
+    // lies in row U's view).  No branch inside a step.
+    auto step = [&](int t, auto FULL, auto SPLIT) __attribute__((always_inline)) {
+        constexpr bool full = decltype(FULL)::value, split = decltype(SPLIT)::value;
+        // wait for this step's DMA (the newest (NST - 2) SPS loads, those of
+        // the following steps, may still be in flight), publish it with a
+        // barrier that also frees stage (t + NST - 1) % NST (read by step
+        // t - 1), and start the DMA of step t + NST - 1 into it
+        vm_wait<(NST - 2) * SPS>();
         barrier_lds();
-        if (rh == 0) issue(t + 1, std::integral_constant<int, 1 - sidx>{});
-        const uint16_t *sq = stage(S), *sg = stage(S) + TILE;
+        issue(t + NST - 1);
+        const uint32_t sb = lds_base + KV_BYTES + (uint32_t)uniform(t % NST) * STAGE_BYTES;
         int m0, m1;
         step_rows(t, m0, m1);
         m0 = uniform(m0);
         m1 = uniform(m1);
 
-        // mask (partial steps only, a workgroup-uniform branch): rows past m1
-        // and invisible pairs get s = g = 0, hence P = dS = 0.  In terms of
-        // x = i - kj (register r has x = x0 + 8*(r/4) + r%4): rows before m1
-        // of a history step see the key iff 0 <= x < W, W = m1 - kj, capped
-        // at K1 unless kj is a prefix key; rows of a target step iff
-        // x < m1 - kj and (x == 0 or kj lies in row U's view)
-        const bool full = uniform((m1 == m0 + BM) && (m1 <= sd.U) && key_tile_full &&
-                                  (it.c0 + BN - 1 <= m0) &&
-                                  ((m1 - 1 - it.c0 < p.k1) || (it.c0 + BN <= p.k2e))) != 0;
-        const int x0 = m0 + 32 * rh + 4 * hl - kj;
-        const bool tstep = m0 >= sd.U;
-        int W = m1 - kj;
-        if (!tstep && kj >= p.k2e) W = imin(W, p.k1);
-        const uint32_t Wu = (uint32_t)imax(W, 0);
-        const bool tv = !tstep || ((kj < sd.U) & ((sd.U - kj < p.k1) | (kj < p.k2e)));
-
-        // S = Q K^T and G dP = (G dO) V^T for this wave's 32 rows x 32 keys
         floatx16 sacc = zero16(), pacc = zero16();
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            const halfx8 aq = *reinterpret_cast<const halfx8 *>(sq + a_off(c));
-            const halfx8 bk = *reinterpret_cast<const halfx8 *>(kv + b_base + 16 * c);
-            sacc = mfma32h(aq, bk, sacc);
-            const halfx8 ag = *reinterpret_cast<const halfx8 *>(sg + a_off(c));
-            const halfx8 bv = *reinterpret_cast<const halfx8 *>(kv + BN * KVS + b_base + 16 * c);
-            pacc = mfma32h(ag, bv, pacc);
+            const uint32_t qa = aoffs[c] + sb;
+            sacc = mfma32(lds_row(qa), lds_row(koffs[c]), sacc);
+            pacc = mfma32(lds_row(qa + TILE_BYTES), lds_row(koffs[c] + BN * D * 2), pacc);
         }
-        if (!full) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int x = x0 + 8 * (r >> 2) + (r & 3);
-                const bool vis = ((uint32_t)x < Wu) & (tv | (x == 0));
-                sacc[r] = vis ? sacc[r] : 0.0f;
-                pacc[r] = vis ? pacc[r] : 0.0f;
-            }
-        }
-        // P = s sigma (= SiLU(t) / alpha) and G dS = G g sigma (1 + t (1 - sigma))
-        // = G g (sigma + a * (alpha - alpha sigma)).  exp(-t) overflowing to
-        // inf gives sigma = 0, a = 0 and dS = 0, its limit, with no NaN.
-        float sgv[16];
+        float pv[16], dv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const float sv = sacc[r];
             const float sgm = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sv * nal2e));
-            sgv[r] = sgm;
-            sacc[r] = sv * sgm;
+            const float a = sv * sgm;
+            pv[r] = a;
+            dv[r] = pacc[r] * fmaf(a, fmaf(-alpha, sgm, alpha), sgm);
         }
-        halfx8 pa[2], da[2];
+        if constexpr (!full) {
+            const int x0 = m0 + 32 * rh + 4 * hl - kj;
+            const bool tstep = m0 >= sd.U;
+            const int Wh = (!tstep && kj >= p.k2e) ? imin(m1 - kj, p.k1) : m1 - kj;
+            const uint32_t Wu = (uint32_t)imax(Wh, 0);
+            const bool tv = !tstep || ((kj < sd.U) & ((sd.U - kj < p.k1) | (kj < p.k2e)));
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int x = x0 + 8 * (r >> 2) + (r & 3);
+                const bool vis = ((uint32_t)x < Wu) & (tv | (x == 0));
+                pv[r] = vis ? pv[r] : 0.0f;
+                dv[r] = vis ? dv[r] : 0.0f;
+            }
+        }
+        uint32_t taddr[2][NDB];
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) taddr[rr][db] = toffs[rr][db] + sb;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
             const int o = 8 * h2;
-            pa[h2] = cvt8h(sacc[o], sacc[o + 1], sacc[o + 2], sacc[o + 3], sacc[o + 4], sacc[o + 5],
-                           sacc[o + 6], sacc[o + 7]);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            pacc[r] = pacc[r] * fmaf(sacc[r], fmaf(-alpha, sgv[r], alpha), sgv[r]);
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-            const int o = 8 * h2;
-            da[h2] = cvt8h(pacc[o], pacc[o + 1], pacc[o + 2], pacc[o + 3], pacc[o + 4], pacc[o + 5],
-                           pacc[o + 6], pacc[o + 7]);
-        }
-        // dV += P^T (G dO), dK += (G dS)^T Q over the two 16-row chunks; the
-        // accumulator's row order (8*(r/4) + 4*hl + r%4) is the k order of
-        // the transposing reads
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
+            const bf16x8 pa = cvt8(pv[o], pv[o + 1], pv[o + 2], pv[o + 3], pv[o + 4], pv[o + 5],
+                                   pv[o + 6], pv[o + 7]);
+            const bf16x8 da = cvt8(dv[o], dv[o + 1], dv[o + 2], dv[o + 3], dv[o + 4], dv[o + 5],
+                                   dv[o + 6], dv[o + 7]);
+            bf16x8 pl, dl;
+            if constexpr (split) {
+                pl = lo_part(pv + o, pa);
+                dl = lo_part(dv + o, da);
+            }
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const uint2 g0 = tr_read_b64(sg + t_off(h2, 0, db));
-                const uint2 g1 = tr_read_b64(sg + t_off(h2, 1, db));
-                dvacc[db] = mfma32h(pa[h2], __builtin_bit_cast(halfx8, make_uint4(g0.x, g0.y, g1.x, g1.y)),
-                                    dvacc[db]);
+                const uint32_t ho = h2 * H2_BYTES;
+                const uint2 g0 = lds_tr(taddr[0][db] + ho + TILE_BYTES);
+                const uint2 g1 = lds_tr(taddr[1][db] + ho + TILE_BYTES);
+                const bf16x8 gfr = __builtin_bit_cast(bf16x8, make_uint4(g0.x, g0.y, g1.x, g1.y));
+                dvacc[db] = mfma32(pa, gfr, dvacc[db]);
+                if constexpr (split) dvacc[db] = mfma32(pl, gfr, dvacc[db]);
+                const uint2 q0 = lds_tr(taddr[0][db] + ho);
+                const uint2 q1 = lds_tr(taddr[1][db] + ho);
+                const bf16x8 qfr = __builtin_bit_cast(bf16x8, make_uint4(q0.x, q0.y, q1.x, q1.y));
+                dkacc[db] = mfma32(da, qfr, dkacc[db]);
+                if constexpr (split) dkacc[db] = mfma32(dl, qfr, dkacc[db]);
             }
-        }
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const uint2 q0 = tr_read_b64(sq + t_off(h2, 0, db));
-                const uint2 q1 = tr_read_b64(sq + t_off(h2, 1, db));
-                dkacc[db] = mfma32h(da[h2], __builtin_bit_cast(halfx8, make_uint4(q0.x, q0.y, q1.x, q1.y)),
-                                    dkacc[db]);
-            }
-        }
-        // schedule: P first (5 VALU per element and its conversion), then
-        // the dV products with dS (3 VALU per element) issued between them,
-        // so that the MFMA pipe and the VALU work at the same time, then dK
-        __builtin_amdgcn_sched_group_barrier(SG_VALU, 88, 0);
-        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 0);
-#pragma unroll
-        for (int i = 0; i < 2 * NDB; ++i) {
-            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(SG_VALU, 7, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 2 * NDB; ++i) {
-            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-            if (i < 2 * NDB - 2) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
-        }
-        // the next stage (its DMA was issued at the top of this step) while
-        // the products run, then this step's dS stores: the next wait, a step
-        // later, finds both the next DMA and these stores long issued
-        if (rh == 0) {
-            vm_wait<0>();
-            convert(std::integral_constant<int, 1 - sidx>{});
-        }
-        // stored-dS path: the block of this key tile's slot among the key
-        // tiles the 64-row tile [m0, m1) visits (the order dQ reads them
-        // in), or the discard block; streamed out (dQ reads it back from HBM
-        // after this kernel)
-        if constexpr (has_ds) {
-            const int rt = m0 < sd.U ? m0 / DS_BM : cdiv(sd.U, DS_BM) + (m0 - sd.U) / DS_BM;
-            const int slot = t < DS_SLOT_TAB ? uniform((int)slot_tab[t])
-                                             : uniform(step_slot(m0, m1));
-            const int64_t blk = (slot >= 0 && slot < p.ds_slots)
-                                    ? 1 + ((int64_t)(rt_first + rt) * p.H + h) * p.ds_slots + slot
-                                    : p.ds_discard;  // block 0 is the zero block
-            uint16_t *dsblk = p.ds + blk * (DS_BM * DS_BN);
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2)
-                st16_nt(dsblk + 8 * ds_frag_chunk(kw, 2 * rh + h2, l32, hl), da[h2]);
         }
     };
-    // the step loop, compiled once with and once without the dS stores so
-    // that the stores are unconditional where they exist; two steps per
-    // iteration so that each stage's addresses are compile-time
-    auto run = [&](auto HAS_DS) {
+    // the key tile, then masked steps [0, s_lo), full steps [s_lo, s_hi) and
+    // masked steps [s_hi, nsteps); split (two-term P and dS) for key tiles
+    // that hold global-prefix keys
+    auto run = [&](auto SPLIT) __attribute__((always_inline)) {
         if (nsteps == 0) return;
-        if (rh == 0) {
-            issue(0, std::integral_constant<int, 0>{});
-            vm_wait<0>();
-            convert(std::integral_constant<int, 0>{});
-        }
-        for (int t = 0; t < nsteps; t += 2) {
-            step(t, std::integral_constant<int, 0>{}, HAS_DS);
-            if (t + 1 < nsteps) step(t + 1, std::integral_constant<int, 1>{}, HAS_DS);
-        }
-        vm_wait<0>();  // no DMA (of the clamped step past the end) left in flight
+        issue_kv();
+#pragma unroll
+        for (int i = 0; i < NST - 1; ++i) issue(i);
+        for (int t = 0; t < s_lo; ++t) step(t, std::false_type{}, SPLIT);
+        for (int t = s_lo; t < s_hi; ++t) step(t, std::true_type{}, SPLIT);
+        for (int t = s_hi; t < nsteps; ++t) step(t, std::false_type{}, SPLIT);
+        vm_wait<0>();  // no DMA (of the clamped steps past the end) left in flight
     };
-    if (p.ds != nullptr) run(std::true_type{});
+    if (it.c0 < p.k2e) run(std::true_type{});
     else run(std::false_type{});
 
     // the two row halves of key block kw: the rh = 1 wave hands its dK sum to
     // the rh = 0 wave and takes the rh = 0 wave's dV sum, through LDS (free
-    // after the barrier); region e holds 32 keys x D floats
+    // after the barrier); region e holds 32 keys x D floats (16 KB at d = 128)
     __syncthreads();
-    auto region = [&](int e) -> float * {
-        // kv holds regions 0-3, cs0 4-5, cs1 6-7
-        uint16_t *a = e < 4 ? kv + (e & 3) * (64 * D) : (e < 6 ? cs0 : cs1) + (e & 1) * (64 * D);
-        return reinterpret_cast<float *>(a);
-    };
+    float *const xreg = reinterpret_cast<float *>(lds);
     floatx16 *mine = rh == 0 ? dkacc : dvacc;    // the sum this wave writes out
     floatx16 *other = rh == 0 ? dvacc : dkacc;   // the sum it hands over
     {
-        float *xo = region(2 * kw + (1 - rh));
+        float *xo = xreg + (2 * kw + (1 - rh)) * (32 * D);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -406,7 +366,7 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
     }
     __syncthreads();
     {
-        const float *xi = region(2 * kw + rh);
+        const float *xi = xreg + (2 * kw + rh) * (32 * D);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -414,12 +374,11 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
     }
 
     // accumulator: lane holds column d = 32*db + l32, register r holds key
-    // 32*kw + 8*(r/4) + 4*hl + r%4 of the tile; dV (P carries 1/alpha) and dK
-    // both scale by alpha / (N G)
-    const float sc = p.out_scale / gscale;
+    // 32*kw + 8*(r/4) + 4*hl + r%4 of the tile; rh = 0 holds dK, rh = 1 dV,
+    // both scaled by alpha / N (P carries 1/alpha)
+    const float sc = p.out_scale;
     if (it.nchunk == 1) {
-        uint16_t *dst = rh == 0 ? reinterpret_cast<uint16_t *>(p.dk) + sd.base * p.lddk + h * D
-                                : reinterpret_cast<uint16_t *>(p.dv) + sd.base * p.lddv + h * D;
+        void *dst = rh == 0 ? p.dk : p.dv;
         const int64_t ld = rh == 0 ? p.lddk : p.lddv;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
@@ -427,8 +386,9 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
             for (int r = 0; r < 16; ++r) {
                 const int j = it.c0 + 32 * kw + 8 * (r >> 2) + 4 * hl + (r & 3);
                 if (j < it.c1) {
-                    const __bf16 v = (__bf16)(mine[db][r] * sc);
-                    dst[(int64_t)j * ld + 32 * db + l32] = __builtin_bit_cast(uint16_t, v);
+                    const int64_t o = (sd.base + j) * ld + h * D + 32 * db + l32;
+                    if constexpr (OUTF32) reinterpret_cast<float *>(dst)[o] = mine[db][r] * sc;
+                    else reinterpret_cast<__bf16 *>(dst)[o] = (__bf16)(mine[db][r] * sc);
                 }
             }
         }
@@ -451,7 +411,7 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
 // (item, slab) handles 1024 consecutive values of the [BN][2D] tile.
 constexpr int RED_SLAB = 1024;
 
-template <int D>
+template <int D, bool OUTF32>
 __global__ __launch_bounds__(256) void sla_bwd_reduce_kernel(AttnParams p)
 {
     constexpr int BN = BWD_BN, W = 2 * D, SLABS = BN * W / RED_SLAB;
@@ -487,191 +447,45 @@ __global__ __launch_bounds__(256) void sla_bwd_reduce_kernel(AttnParams p)
         const float4 v = *reinterpret_cast<const float4 *>(src + c * stride);
         acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
-    const float sc = p.out_scale / *p.grad_scale;
-    uint2 o = cvt4_u2(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
-    uint16_t *dst = col < D
-        ? reinterpret_cast<uint16_t *>(p.dk) + (sd.base + c0 + jl) * p.lddk + h * D + col
-        : reinterpret_cast<uint16_t *>(p.dv) + (sd.base + c0 + jl) * p.lddv + h * D + (col - D);
-    *reinterpret_cast<uint2 *>(dst) = o;
-}
-
-// ---------------------------------------------------------------------------
-// dQ
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256, 1) void sla_bwd_dq_bf16_kernel(AttnParams p)
-{
-    constexpr int BM = FWD_BM, BN = FWD_BN;
-    constexpr int NC = D / 16, NDB = D / 32;
-    __shared__ __align__(16) uint16_t sk[2][BN * D];
-    __shared__ __align__(16) uint16_t sv[2][BN * D];
-    __shared__ __align__(16) uint16_t skt[2][D * BN];
-
-    const int nrec = p.s.fwd_base[p.B];
-    const int item = xcd_remap(blockIdx.x, nrec * p.H);
-    if (item < 0) return;
-    const int h = item / nrec;
-    const int rec = item - h * nrec;
-    const int b = find_seq(p.s.fwd_base, p.B, rec);
-    const SeqDims sd = seq_dims(p.offsets, p.num_targets, b);
-    int r0, r1;
-    row_tile(sd.L, sd.U, BM, rec - uniform(p.s.fwd_base[b]), r0, r1);
-    r0 = uniform(r0);
-    r1 = uniform(r1);
-    const Ranges kr = fwd_key_ranges(sd.L, sd.U, p.k1, p.k2e, r0, r1, BN);
-
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int l32 = lane & 31, hl = lane >> 5;
-
-    const uint16_t *qg = reinterpret_cast<const uint16_t *>(p.q) + sd.base * p.ldq + h * D;
-    const uint16_t *kg = reinterpret_cast<const uint16_t *>(p.k) + sd.base * p.ldk + h * D;
-    const uint16_t *vg = reinterpret_cast<const uint16_t *>(p.v) + sd.base * p.ldv + h * D;
-    const uint16_t *gg = reinterpret_cast<const uint16_t *>(p.dout) + sd.base * p.lddo + h * D;
-
-    // rows at or past r1 are zero, so their dS is zero
-    const int qi = r0 + 32 * wv + l32;
-    bf16x8 qb[NC], gb[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        qb[c] = as_bf16x8(ld16_row(qg, p.ldq, qi, r1, 16 * c + 8 * hl));
-        gb[c] = as_bf16x8(ld16_row(gg, p.lddo, qi, r1, 16 * c + 8 * hl));
-    }
-
-    const TileCursor cur(kr, BN);
-    const int ntiles = uniform(cur.total);
-    floatx16 dqacc[NDB];
-#pragma unroll
-    for (int i = 0; i < NDB; ++i) dqacc[i] = zero16();
-
-    Tile64<D> kt, vt;
-    // keys at or past L hold copies of key L - 1; such tiles are never "full",
-    // and the mask removes them
-    int c_next = cur.start(0, BN);
-    if (ntiles > 0) {
-        kt.load_clamped(kg, p.ldk, c_next, sd.L, tid);
-        vt.load_clamped(vg, p.ldv, c_next, sd.L, tid);
-    }
-    const float nal2e = p.neg_alpha_log2e, alpha = p.alpha;
-    const float gscale = *p.grad_scale;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) gb[c] = scale_bf16x8(gb[c], gscale);
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        const int c0 = uniform(c_next);
-        kt.store_rows(sk[buf], tid);
-        store_transposed_f16<D>(kt, skt[buf], tid, 1.0f);
-        vt.store_rows(sv[buf], tid);
-        c_next = cur.start(t + 1, BN);
-        if (t + 1 < ntiles) {
-            kt.load_clamped(kg, p.ldk, c_next, sd.L, tid);
-            vt.load_clamped(vg, p.ldv, c_next, sd.L, tid);
-        }
-        __syncthreads();
-
-        // S^T = K Q^T, dP^T = V dO^T (rows in the lane dimension)
-        floatx16 sacc[2], pacc[2];
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-            sacc[kb2] = zero16();
-            pacc[kb2] = zero16();
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                bf16x8 ak = lds_row_chunk<D>(sk[buf], 32 * kb2 + l32, 2 * c + hl);
-                sacc[kb2] = mfma32(ak, qb[c], sacc[kb2]);
-                bf16x8 av = lds_row_chunk<D>(sv[buf], 32 * kb2 + l32, 2 * c + hl);
-                pacc[kb2] = mfma32(av, gb[c], pacc[kb2]);
-            }
-        }
-
-        // mask (partial tiles only, a workgroup-uniform branch)
-        const bool full = uniform((r0 < sd.U) && (c0 + BN <= sd.L) && (c0 + BN - 1 <= r0) &&
-                                  ((r1 - 1 - c0 < p.k1) || (c0 + BN <= p.k2e))) != 0;
-        if (!full) {
-#pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int j = c0 + 32 * kb2 + 8 * (r >> 2) + 4 * hl + (r & 3);
-                    const bool vis = visible(qi, j, sd.U, p.k1, p.k2e);
-                    sacc[kb2][r] = vis ? sacc[kb2][r] : 0.0f;
-                    pacc[kb2][r] = vis ? pacc[kb2][r] : 0.0f;
-                }
-            }
-        }
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float s = sacc[kb2][r], g = pacc[kb2][r];
-                float e;
-                const float sg = sigmoid_e(s, nal2e, e);
-                pacc[kb2][r] = g * (sg * (1.0f + alpha * s * sg * e));
-            }
-        }
-
-        // dQ^T += K^T dS^T over four 16-key chunks
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-            const floatx16 &src = pacc[kc >> 1];
-            const int o = 8 * (kc & 1);
-            halfx8 dsb = cvt8h(src[o], src[o + 1], src[o + 2], src[o + 3], src[o + 4],
-                               src[o + 5], src[o + 6], src[o + 7]);
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                halfx8 a = lds_t_chunk_h(skt[buf], 32 * db + l32, 2 * kc + hl);
-                dqacc[db] = mfma32h(a, dsb, dqacc[db]);
-            }
-        }
-    }
-
-    if (qi < r1) {
-        uint16_t *orow = reinterpret_cast<uint16_t *>(p.dq) + (sd.base + qi) * p.lddq + h * D;
-        const float sc = p.out_scale / gscale;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                uint2 v = cvt4_u2(dqacc[db][4 * g] * sc, dqacc[db][4 * g + 1] * sc,
-                                  dqacc[db][4 * g + 2] * sc, dqacc[db][4 * g + 3] * sc);
-                *reinterpret_cast<uint2 *>(orow + 32 * db + 8 * g + 4 * hl) = v;
-            }
-        }
+    const float sc = p.out_scale;
+    const int64_t off = col < D ? (sd.base + c0 + jl) * p.lddk + h * D + col
+                                : (sd.base + c0 + jl) * p.lddv + h * D + (col - D);
+    void *base = col < D ? p.dk : p.dv;
+    if constexpr (OUTF32) {
+        *reinterpret_cast<float4 *>(reinterpret_cast<float *>(base) + off) =
+            make_float4(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
+    } else {
+        *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(base) + off) =
+            cvt4_u2(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
     }
 }
 
-template <int D>
+template <int D, bool OUTF32>
 static hipError_t launch_dkdv_d(const AttnParams &p, hipStream_t st)
 {
-    hipLaunchKernelGGL(sla_bwd_dkdv_bf16_kernel<D>, dim3(p.grid_bwd), dim3(DKDV_THREADS), 0, st,
-                       p);
+    hipLaunchKernelGGL((sla_bwd_dkdv_bf16_kernel<D, OUTF32>), dim3(p.grid_bwd),
+                       dim3(DKDV_THREADS), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.grid_red == 0) return e;
-    hipLaunchKernelGGL(sla_bwd_reduce_kernel<D>, dim3(p.grid_red * (BWD_BN * 2 * D / RED_SLAB)),
-                       dim3(256), 0, st, p);
+    hipLaunchKernelGGL((sla_bwd_reduce_kernel<D, OUTF32>),
+                       dim3(p.grid_red * (BWD_BN * 2 * D / RED_SLAB)), dim3(256), 0, st, p);
     return hipGetLastError();
+}
+
+template <bool OUTF32>
+static hipError_t launch_dkdv_o(const AttnParams &p, hipStream_t st)
+{
+    switch (p.d) {
+    case 32: return launch_dkdv_d<32, OUTF32>(p, st);
+    case 64: return launch_dkdv_d<64, OUTF32>(p, st);
+    case 128: return launch_dkdv_d<128, OUTF32>(p, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_bwd_dkdv_bf16(const AttnParams &p, hipStream_t st)
 {
-    switch (p.d) {
-    case 32: return launch_dkdv_d<32>(p, st);
-    case 64: return launch_dkdv_d<64>(p, st);
-    case 128: return launch_dkdv_d<128>(p, st);
-    default: return hipErrorInvalidValue;
-    }
-}
-
-hipError_t launch_bwd_dq_bf16(const AttnParams &p, hipStream_t st)
-{
-    if (p.ds != nullptr) return launch_bwd_dq_ds_bf16(p, st);
-    dim3 grid(p.grid_fwd), block(256);
-    switch (p.d) {
-    case 32: hipLaunchKernelGGL(sla_bwd_dq_bf16_kernel<32>, grid, block, 0, st, p); break;
-    case 64: hipLaunchKernelGGL(sla_bwd_dq_bf16_kernel<64>, grid, block, 0, st, p); break;
-    case 128: hipLaunchKernelGGL(sla_bwd_dq_bf16_kernel<128>, grid, block, 0, st, p); break;
-    default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    return p.out_f32 ? launch_dkdv_o<true>(p, st) : launch_dkdv_o<false>(p, st);
 }
 
 }  // namespace sla

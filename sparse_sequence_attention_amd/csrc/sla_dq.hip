@@ -1,0 +1,268 @@
+// sla_dq.hip -- SLA backward dQ on gfx950: bf16 MFMA, fp32 accumulation, no
+// atomics (the row tile owns its dQ rows).
+//
+// With a_ij = SiLU(alpha s_ij), s_ij = q_i . k_j and O_i = (1/N) sum_j a_ij v_j
+// (ULTRA-HSTU paper, section 3 Eq.3 under the semi-local mask of section
+// 4.2.1 Eq.7), the chain rule gives over the visible pairs of row i
+//   g_ij  = dO_i . v_j
+//   dS_ij = (alpha / N) g_ij sigma_ij (1 + t_ij (1 - sigma_ij)),  t = alpha s
+//   dQ_i  = sum_j dS_ij k_j.
+// The kernel recomputes s and g for its row tile rather than reading dS
+// stored by the key-tile (dK/dV) kernel: recomputing costs two more products
+// per pair, storing costs 2 bytes per pair written and read back through HBM
+// (about a gigabyte at 16K-token histories), and the stores would sit in the
+// dK/dV kernel's DMA wait counts.
+//
+// Work item: one row tile of up to 128 rows (4 waves x 32) of one head, two
+// workgroups per CU, over the same key tiles as the forward (prefix, band, and
+// for target rows the window of the first target slot plus the diagonal), 64
+// keys per step.  Per 32-key block each wave computes
+//   S^T  (32 keys x 32 rows) = K Q^T          K rows from LDS, Q^T in registers
+//   dP^T (32 keys x 32 rows) = V dO^T         V rows from LDS, dO^T in registers
+//   dS^T = mask(dP^T * sigma (1 + t (1 - sigma)))   in registers, rounded to bf16
+//   dQ^T (D x 32 rows)     += K^T dS^T        K^T by transposing LDS reads
+// Computing S and dP transposed puts the rows in the lane dimension, so dS^T
+// feeds the third product as its B operand straight from the accumulator.
+// The K and V rows of the next step come HBM -> LDS by DMA into the idle one
+// of two stages (the forward's swizzled layout); one LDS-only barrier per
+// step keeps that DMA in flight across it.
+#include <type_traits>
+
+#include "sla_device.h"
+#include "sla_kernels.h"
+
+namespace sla {
+
+// 16-byte chunk swizzle of the [64][D] K and V stage tiles (as the forward):
+// logical chunk c of row r sits at c ^ qswz<D>(r), u = r*D/128 (the 256-byte
+// bank row), Q4 = D/32.
+template <int D>
+__device__ __forceinline__ int qswz(int r)
+{
+    constexpr int Q4 = D / 32;
+    const int u = r * D / 128;
+    return 4 * (u % Q4) + (u / Q4) % 4;
+}
+
+template <int D, bool OUTF32>
+__global__ __launch_bounds__(256, 2) void sla_bwd_dq_kernel(AttnParams p)
+{
+    constexpr int BM = FWD_BM, BN = FWD_BN;
+    constexpr int NT = 256;
+    constexpr int NC = D / 16;   // 16-wide contraction chunks of Q.K and dO.V
+    constexpr int NDB = D / 32;  // 32-wide output blocks
+    constexpr int CPR = D / 8;   // 16-byte chunks per row
+    constexpr int TCH = BN * CPR;   // chunks of one 64-key K (or V) tile
+    constexpr int KPT = TCH / NT;   // DMA loads per thread and tile
+    static_assert(BN == 64 && BM == 128, "64-key steps over 128-row tiles");
+    static_assert(TCH % NT == 0 && 2 * KPT <= 8, "whole DMA rounds, at most 8 per stage");
+    __shared__ __align__(16) uint16_t st0[2 * BN * D], st1[2 * BN * D];
+
+    const int nrec = p.s.fwd_base[p.B];
+    const int item = xcd_remap(blockIdx.x, nrec * p.H);
+    if (item < 0) return;
+    const int h = item / nrec;
+    const int rec = item - h * nrec;
+    const int b = find_seq(p.s.fwd_base, p.B, rec);
+    const SeqDims sd = seq_dims(p.offsets, p.num_targets, b);
+    int r0, r1;
+    row_tile(sd.L, sd.U, BM, rec - uniform(p.s.fwd_base[b]), r0, r1);
+    r0 = uniform(r0);
+    r1 = uniform(r1);
+    const Ranges kr = fwd_key_ranges(sd.L, sd.U, p.k1, p.k2e, r0, r1, BN);
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
+    const int l32 = lane & 31, hl = lane >> 5;
+
+    const uint16_t *qg = reinterpret_cast<const uint16_t *>(p.q) + sd.base * p.ldq + h * D;
+    const uint16_t *kg = reinterpret_cast<const uint16_t *>(p.k) + sd.base * p.ldk + h * D;
+    const uint16_t *vg = reinterpret_cast<const uint16_t *>(p.v) + sd.base * p.ldv + h * D;
+    const uint16_t *gg = reinterpret_cast<const uint16_t *>(p.dout) + sd.base * p.lddo + h * D;
+
+    // Q^T and dO^T operands: lane holds row qi, d-slots 16c + 8*hl .. +8; rows
+    // at or past r1 read as zero (then g = 0 and dS = 0)
+    const int qi = r0 + 32 * wv + l32;
+    bf16x8 qb[NC], gb[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        qb[c] = as_bf16x8(ld16_row(qg, p.ldq, qi, r1, 16 * c + 8 * hl));
+        gb[c] = as_bf16x8(ld16_row(gg, p.lddo, qi, r1, 16 * c + 8 * hl));
+    }
+
+    const TileCursor cur(kr, BN);
+    const int ntiles = uniform(cur.total);
+
+    floatx16 dqacc[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) dqacc[i] = zero16();
+
+    auto stage = [&](auto S) -> uint16_t * {
+        if constexpr (decltype(S)::value == 0) return st0;
+        else return st1;
+    };
+    // DMA of the K and V rows of key tile t into a stage: chunk P = i*NT + tid
+    // of a tile is physical chunk P % CPR of key row P / CPR and holds its
+    // logical chunk (P % CPR) ^ qswz(row); keys at or past L read key L - 1
+    // (such tiles are never "full", and the mask removes them)
+    const uint32_t ldk_b = (uint32_t)p.ldk * 2u, ldv_b = (uint32_t)p.ldv * 2u;
+    auto issue = [&](int t, auto S) {
+        const int c0 = uniform(cur.start(t, BN));
+        const int last = uniform(sd.L - 1 - c0);
+        const char *krow = reinterpret_cast<const char *>(kg + (int64_t)c0 * p.ldk);
+        const char *vrow = reinterpret_cast<const char *>(vg + (int64_t)c0 * p.ldv);
+        uint16_t *sb = stage(S);
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int P = i * NT + tid;
+            const int prow = P / CPR;
+            const uint32_t row = (uint32_t)imin(prow, last);
+            const uint32_t c = (uint32_t)((P % CPR) ^ qswz<D>(prow));
+            gl_lds16(krow + (row * ldk_b + 16u * c), sb + (i * NT + wv * 64) * 8);
+            gl_lds16(vrow + (row * ldv_b + 16u * c), sb + (TCH + i * NT + wv * 64) * 8);
+        }
+    };
+
+    // per-lane LDS offsets (elements).  Row operands: key row 32*kb + l32,
+    // logical chunk 2c + hl.  K^T operand by transposing reads (quarter
+    // q = lane/16, j = lane%16): keys 32*kb + 16*h2 + 8*rr + 4*(q/2) + j/4,
+    // d-columns 32*db + 16*(q%2) + 4*(j%4); the keys come in the order in
+    // which the S^T accumulator hands them to dS^T (8*(r/4) + 4*hl + r%4).
+    const int q4 = lane >> 4, j16 = lane & 15;
+    auto r_off = [&](int kb, int c) {
+        const int r = 32 * kb + l32;
+        return r * D + 8 * ((2 * c + hl) ^ qswz<D>(r));
+    };
+    auto t_off = [&](int kb, int h2, int rr, int db) {
+        const int row = 32 * kb + 16 * h2 + 8 * rr + 4 * (q4 >> 1) + (j16 >> 2);
+        const int col = 32 * db + 16 * (q4 & 1) + 4 * (j16 & 3);
+        return row * D + 8 * ((col >> 3) ^ qswz<D>(row)) + (col & 7);
+    };
+
+    const float nal2e = p.neg_alpha_log2e, alpha = p.alpha;
+    const uint32_t k1u = (uint32_t)p.k1;
+    auto step = [&](int t, auto S) {
+        constexpr int sidx = decltype(S)::value;
+        barrier_lds();  // publishes stage S, frees the other (read by step t - 1)
+        issue(imin(t + 1, ntiles - 1), std::integral_constant<int, 1 - sidx>{});
+        const uint16_t *sk = stage(S), *sv = stage(S) + BN * D;
+        const int c0 = uniform(cur.start(t, BN));
+        // mask: as the forward (workgroup-uniform tests; interval masks for
+        // history tiles wholly inside or outside the global prefix)
+        const bool full = uniform(((r0 < sd.U) & (c0 + BN <= sd.L) & (c0 + BN - 1 <= r0) &
+                                   ((r1 - 1 - c0 < p.k1) | (c0 + BN <= p.k2e))) |
+                                  ((r0 >= sd.U) & (c0 + BN <= sd.U) &
+                                   ((c0 >= sd.U - p.k1 + 1) | (c0 + BN <= p.k2e)))) != 0;
+        const int x0 = qi - c0 - 4 * hl;
+        const int mode = uniform(r0 >= sd.U ? 0 : (c0 >= p.k2e ? 1 : (c0 + BN <= p.k2e ? 2 : 0)));
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            floatx16 sacc = zero16(), pacc = zero16();
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const bf16x8 ak = *reinterpret_cast<const bf16x8 *>(sk + r_off(kb, c));
+                sacc = mfma32(ak, qb[c], sacc);
+                const bf16x8 av = *reinterpret_cast<const bf16x8 *>(sv + r_off(kb, c));
+                pacc = mfma32(av, gb[c], pacc);
+            }
+            // dS = g * (sigma + a * (alpha - alpha * sigma)), a = s * sigma:
+            // 1 + t (1 - sigma) = 1 + alpha a (1 - sigma) / sigma, times sigma.
+            // exp(-t) overflowing to inf gives sigma = 0, a = 0, dS = 0 (its
+            // limit) with no NaN.
+            float ds[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float sv_ = sacc[r];
+                const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sv_ * nal2e));
+                const float a = sv_ * sg;
+                ds[r] = pacc[r] * fmaf(a, fmaf(-alpha, sg, alpha), sg);
+            }
+            if (!full) {
+                if (mode == 1) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int x = x0 - (32 * kb + 8 * (r >> 2) + (r & 3));
+                        ds[r] = (uint32_t)x < k1u ? ds[r] : 0.0f;
+                    }
+                } else if (mode == 2) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int x = x0 - (32 * kb + 8 * (r >> 2) + (r & 3));
+                        ds[r] = x >= 0 ? ds[r] : 0.0f;
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int j = c0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
+                        ds[r] = visible(qi, j, sd.U, p.k1, p.k2e) ? ds[r] : 0.0f;
+                    }
+                }
+            }
+            const bf16x8 d0 = cvt8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+            const bf16x8 d1 = cvt8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const uint2 k0 = tr_read_b64(sk + t_off(kb, h2, 0, db));
+                    const uint2 k1v = tr_read_b64(sk + t_off(kb, h2, 1, db));
+                    dqacc[db] = mfma32(__builtin_bit_cast(bf16x8, make_uint4(k0.x, k0.y, k1v.x, k1v.y)),
+                                       h2 ? d1 : d0, dqacc[db]);
+                }
+            }
+        }
+        // the next stage's DMA (issued at the top of this step) has landed
+        // before the barrier that publishes it
+        vm_wait<0>();
+    };
+
+    if (ntiles > 0) {
+        issue(0, std::integral_constant<int, 0>{});
+        vm_wait<0>();
+        for (int t = 0; t < ntiles; t += 2) {
+            step(t, std::integral_constant<int, 0>{});
+            if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
+        }
+    }
+
+    // epilogue: dQ[qi][d] for d = 32*db + 8*g + 4*hl + 0..3, scaled by alpha / N
+    if (qi < r1) {
+        const float sc = p.out_scale;
+        const int64_t row = sd.base + qi;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float o0 = dqacc[db][4 * g] * sc, o1 = dqacc[db][4 * g + 1] * sc;
+                const float o2 = dqacc[db][4 * g + 2] * sc, o3 = dqacc[db][4 * g + 3] * sc;
+                const int col = h * D + 32 * db + 8 * g + 4 * hl;
+                if constexpr (OUTF32) {
+                    float *orow = reinterpret_cast<float *>(p.dq) + row * p.lddq;
+                    *reinterpret_cast<float4 *>(orow + col) = make_float4(o0, o1, o2, o3);
+                } else {
+                    uint16_t *orow = reinterpret_cast<uint16_t *>(p.dq) + row * p.lddq;
+                    *reinterpret_cast<uint2 *>(orow + col) = cvt4_u2(o0, o1, o2, o3);
+                }
+            }
+        }
+    }
+}
+
+template <bool OUTF32>
+static hipError_t launch_dq_o(const AttnParams &p, hipStream_t st)
+{
+    dim3 grid(p.grid_fwd), block(256);
+    switch (p.d) {
+    case 32: hipLaunchKernelGGL((sla_bwd_dq_kernel<32, OUTF32>), grid, block, 0, st, p); break;
+    case 64: hipLaunchKernelGGL((sla_bwd_dq_kernel<64, OUTF32>), grid, block, 0, st, p); break;
+    case 128: hipLaunchKernelGGL((sla_bwd_dq_kernel<128, OUTF32>), grid, block, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_bf16(const AttnParams &p, hipStream_t st)
+{
+    return p.out_f32 ? launch_dq_o<true>(p, st) : launch_dq_o<false>(p, st);
+}
+
+}  // namespace sla

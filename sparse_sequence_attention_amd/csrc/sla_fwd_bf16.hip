@@ -12,15 +12,18 @@
 // first target plus the diagonal), 64 keys per step.  Per step each wave
 // computes, per 32-key block,
 //   S^T (32 keys x 32 rows) = K Q^T      (K from LDS, Q^T held in registers)
-//   P^T = mask(S^T * sigmoid(alpha S^T))  in registers, rounded to fp16
+//   P^T = mask(S^T * sigmoid(alpha S^T))  in registers, rounded to bf16
 //   O^T (D x 32 rows)     += V^T P^T     (V^T by transposing LDS reads)
 // with the two blocks' products and SiLU interleaved in one wave.
 // Computing S transposed puts the rows in the MFMA's lane dimension, so P^T
-// feeds the second MFMA as its B operand straight from the accumulator.  The
-// K and V rows of the next step come HBM -> LDS by DMA into the idle one of
-// two stages, already in the swizzled layout; after the step's products each
-// thread converts its own V chunks there to fp16 in place.  One LDS-only
-// barrier per step, so the DMA stays in flight across it.
+// feeds the second MFMA as its B operand straight from the accumulator.  Both
+// products are bf16 MFMAs with fp32 accumulation: the bf16 inputs are used as
+// stored, and only P is rounded (to bf16, 8 significant bits; the rounding
+// errors of the ~10^3 terms of a row are independent, so the output moves by
+// ~2^-9 / sqrt(3) of its own size, rms).  The K and V rows of the next step
+// come HBM -> LDS by DMA into the idle one of two stages, already in the
+// swizzled layout.  One LDS-only barrier per step, so the DMA stays in flight
+// across it.  O is written in bf16 or, on request, fp32.
 #include <type_traits>
 
 #include "sla_device.h"
@@ -49,7 +52,7 @@ __device__ __forceinline__ int fswz(int r)
 // candidate's sum runs over the same history tiles in the same order and
 // then its own key, wherever it sits among the candidates: scores do not
 // depend on which other candidates share the call.
-template <int D, bool CAND>
+template <int D, bool CAND, bool OUTF32>
 __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
 {
     constexpr int BM = FWD_BM, BN = FWD_BN;
@@ -61,9 +64,8 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
     constexpr int KPT = TCH / NT;   // DMA loads per thread and tile
     static_assert(BN == 64 && BM == 128, "64-key steps over 128-row tiles");
     static_assert(TCH % NT == 0 && 2 * KPT <= 8, "whole DMA rounds, at most 8 per stage");
-    // two stages of [K | V] rows (K bf16, V fp16 after the in-place
-    // conversion); separate arrays so that the compiler can tell the DMA into
-    // one from the reads of the other
+    // two stages of [K | V] bf16 rows; separate arrays so that the compiler
+    // can tell the DMA into one from the reads of the other
     __shared__ __align__(16) uint16_t st0[2 * BN * D], st1[2 * BN * D];
 
     const int nrec = p.s.fwd_base[p.B];
@@ -159,17 +161,6 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
             gl_lds16(vrow + (row * lv + 16u * c), sb + (TCH + i * NT + wv * 64) * 8);
         }
     };
-    // this thread's V chunks of a stage, bf16 -> fp16 in place
-    auto convert = [&](auto S) {
-        uint16_t *sv = stage(S) + BN * D;
-        uint4 raw[KPT];
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) raw[i] = *reinterpret_cast<const uint4 *>(sv + 8 * (i * NT + tid));
-#pragma unroll
-        for (int i = 0; i < KPT; ++i)
-            *reinterpret_cast<halfx8 *>(sv + 8 * (i * NT + tid)) = bf16x8_to_halfx8(as_bf16x8(raw[i]));
-    };
-
     // per-lane LDS offsets (elements).  K operand: key row 32*kb + l32,
     // logical chunk 2c + hl.  V^T operand by transposing reads (quarter
     // q = lane/16, j = lane%16): keys 32*kb + 16*h2 + 8*rr + 4*(q/2) + j/4,
@@ -254,16 +245,16 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
             }
         };
         auto pv_blk = [&](int kb, const float *f) {
-            const halfx8 p0 = cvt8h(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
-            const halfx8 p1 = cvt8h(f[8], f[9], f[10], f[11], f[12], f[13], f[14], f[15]);
+            const bf16x8 p0 = cvt8(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
+            const bf16x8 p1 = cvt8(f[8], f[9], f[10], f[11], f[12], f[13], f[14], f[15]);
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
                     const uint2 v0 = tr_read_b64(sv + v_off(kb, h2, 0, db));
                     const uint2 v1 = tr_read_b64(sv + v_off(kb, h2, 1, db));
-                    oacc[db] = mfma32h(__builtin_bit_cast(halfx8, make_uint4(v0.x, v0.y, v1.x, v1.y)),
-                                       h2 ? p1 : p0, oacc[db]);
+                    oacc[db] = mfma32(__builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y)),
+                                      h2 ? p1 : p0, oacc[db]);
                 }
             }
         };
@@ -300,17 +291,14 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
         }
         mask_blk(fb, 1);
         pv_blk(1, fb);
-        // the next stage: wait for its DMA (issued at the top of this step)
-        // explicitly, then convert it.  After the last step this re-converts
-        // a stage nobody reads.
+        // the next stage's DMA (issued at the top of this step) has landed
+        // before the barrier that publishes it
         vm_wait<0>();
-        convert(std::integral_constant<int, 1 - sidx>{});
     };
 
     if (ntiles > 0) {
         issue(0, std::integral_constant<int, 0>{});
         vm_wait<0>();
-        convert(std::integral_constant<int, 0>{});
         for (int t = 0; t < ntiles; t += 2) {
             step(t, std::integral_constant<int, 0>{});
             if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
@@ -320,31 +308,43 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
     // epilogue: O[qi][d] for d = 32*db + 8*g + 4*hl + 0..3
     if (qi < r1) {
         const int64_t orow_i = CAND ? cbase + (qi - uc) : sd.base + qi;
-        uint16_t *orow = reinterpret_cast<uint16_t *>(p.o) + orow_i * p.ldo + h * D;
         const float sc = p.out_scale;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                uint2 v = cvt4_u2(oacc[db][4 * g] * sc, oacc[db][4 * g + 1] * sc,
-                                  oacc[db][4 * g + 2] * sc, oacc[db][4 * g + 3] * sc);
-                *reinterpret_cast<uint2 *>(orow + 32 * db + 8 * g + 4 * hl) = v;
+                const float o0 = oacc[db][4 * g] * sc, o1 = oacc[db][4 * g + 1] * sc;
+                const float o2 = oacc[db][4 * g + 2] * sc, o3 = oacc[db][4 * g + 3] * sc;
+                const int col = h * D + 32 * db + 8 * g + 4 * hl;
+                if constexpr (OUTF32) {
+                    float *orow = reinterpret_cast<float *>(p.o) + orow_i * p.ldo;
+                    *reinterpret_cast<float4 *>(orow + col) = make_float4(o0, o1, o2, o3);
+                } else {
+                    uint16_t *orow = reinterpret_cast<uint16_t *>(p.o) + orow_i * p.ldo;
+                    *reinterpret_cast<uint2 *>(orow + col) = cvt4_u2(o0, o1, o2, o3);
+                }
             }
         }
     }
 }
 
-template <bool CAND>
-static hipError_t launch_fwd(const AttnParams &p, hipStream_t st)
+template <bool CAND, bool OUTF32>
+static hipError_t launch_fwd_o(const AttnParams &p, hipStream_t st)
 {
     dim3 grid(p.grid_fwd), block(256);
     switch (p.d) {
-    case 32: hipLaunchKernelGGL((sla_fwd_bf16_kernel<32, CAND>), grid, block, 0, st, p); break;
-    case 64: hipLaunchKernelGGL((sla_fwd_bf16_kernel<64, CAND>), grid, block, 0, st, p); break;
-    case 128: hipLaunchKernelGGL((sla_fwd_bf16_kernel<128, CAND>), grid, block, 0, st, p); break;
+    case 32: hipLaunchKernelGGL((sla_fwd_bf16_kernel<32, CAND, OUTF32>), grid, block, 0, st, p); break;
+    case 64: hipLaunchKernelGGL((sla_fwd_bf16_kernel<64, CAND, OUTF32>), grid, block, 0, st, p); break;
+    case 128: hipLaunchKernelGGL((sla_fwd_bf16_kernel<128, CAND, OUTF32>), grid, block, 0, st, p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <bool CAND>
+static hipError_t launch_fwd(const AttnParams &p, hipStream_t st)
+{
+    return p.out_f32 ? launch_fwd_o<CAND, true>(p, st) : launch_fwd_o<CAND, false>(p, st);
 }
 
 hipError_t launch_fwd_bf16(const AttnParams &p, hipStream_t st) { return launch_fwd<false>(p, st); }

@@ -25,21 +25,10 @@ struct AttnParams {
     float neg_alpha_log2e;  // -alpha * log2(e)
     Sched s;
     float *partials;        // fp32 partial dK|dV of split prefix key tiles
-    float *absmax_part;     // [ABSMAX_BLOCKS] per-block max |dO|
-    float *grad_scale;      // [1] power of two with max|dO| * scale in [1, 2)
     int grid_fwd;           // upper bound of forward / dQ work items (x heads)
     int grid_bwd;           // upper bound of dK/dV work items (x heads)
     int grid_red;           // upper bound of reduce items (x heads)
-    // stored dS (null when dQ recomputes): a zero block, then the fp16 dS
-    // blocks [64-row tile][head][slot][DS_BM x DS_BN] in the dK/dV kernel's
-    // fragment order, then one discard block (the target of dS stores of
-    // tiles that have no slot, so that every step stores the same number of
-    // blocks); and an fp16 copy of K [T][H][d]
-    uint16_t *ds;
-    uint16_t *kh;
-    int64_t ds_discard;     // block index of the discard block
-    int ds_slots;           // slots per (row tile, head)
-    int grid_rt;            // upper bound of 64-row tiles (x heads)
+    int out_f32;            // bf16 path: O, dQ, dK, dV written as fp32
     // candidate scoring against a cached history (null: the ordinary forward).
     // Sequence b is then the history offsets[b] .. offsets[b+1] (keys k, v)
     // followed by the candidates cand_offsets[b] .. cand_offsets[b+1] (rows
@@ -49,14 +38,10 @@ struct AttnParams {
     int64_t ldkc, ldvc;
 };
 
-constexpr int ABSMAX_BLOCKS = 1024;
-
 // Sizes (int32 counts / bytes) of the workspace regions, from host-known data.
 struct WsLayout {
-    size_t sched_off, part_off, ds_off, kh_off, total;
+    size_t sched_off, part_off, total;
     int64_t fwd_items, bwd_items, red_items, part_slots;  // upper bounds (per head)
-    int64_t rt_items;   // upper bound of 64-row tiles (per head)
-    int ds_slots;       // 0: dQ recomputes dS
 };
 
 hipError_t launch_sched(const AttnParams &p, hipStream_t st);
@@ -66,16 +51,11 @@ hipError_t launch_fwd_candidates_bf16(const AttnParams &p, hipStream_t st);
 // (code, sequence).  ctx < 0 skips the truncation check.
 hipError_t launch_validate(const int64_t *offsets, const int32_t *num_targets, int B, int64_t T,
                            int ctx, int32_t *result, hipStream_t st);
-// max |dO| per block into p.absmax_part (the schedule kernel folds it into
-// p.grad_scale when p.absmax_part is set)
-hipError_t launch_absmax(const AttnParams &p, hipStream_t st);
 hipError_t launch_sched_dump(const AttnParams &p, int op, int32_t *records, int64_t capacity,
                              int32_t *count, hipStream_t st);
 hipError_t launch_fwd_bf16(const AttnParams &p, hipStream_t st);
 hipError_t launch_bwd_dkdv_bf16(const AttnParams &p, hipStream_t st);  // + prefix reduce
-// dQ: from the stored dS blocks when p.ds is set, else recomputing S, dP, dS
 hipError_t launch_bwd_dq_bf16(const AttnParams &p, hipStream_t st);
-hipError_t launch_bwd_dq_ds_bf16(const AttnParams &p, hipStream_t st);  // stored-dS kernel
 hipError_t launch_fwd_f32(const AttnParams &p, hipStream_t st);
 hipError_t launch_bwd_dkdv_f32(const AttnParams &p, hipStream_t st);
 hipError_t launch_bwd_dq_f32(const AttnParams &p, hipStream_t st);

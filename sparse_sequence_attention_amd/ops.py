@@ -40,7 +40,7 @@ def _head_tensor(name: str, t: torch.Tensor, T: int, H: int, dtype) -> int:
 
 def make_problem(dtype, offsets: torch.Tensor, num_targets: Optional[torch.Tensor], T: int, H: int,
                  d_qk: int, d_v: int, k1: int, k2: int, contextual_len: int, max_seq_len: int,
-                 alpha: float = 1.0) -> C.SLAProblem:
+                 alpha: float = 1.0, out_f32: bool = False) -> C.SLAProblem:
     if offsets.dtype != torch.int64 or offsets.dim() != 1:
         raise TypeError("offsets must be a 1-D int64 tensor [B+1]")
     if num_targets is not None and (num_targets.dtype != torch.int32 or
@@ -56,16 +56,21 @@ def make_problem(dtype, offsets: torch.Tensor, num_targets: Optional[torch.Tenso
     p.k1, p.k2, p.contextual_len = int(k1), int(k2), int(contextual_len)
     p.max_seq_len = int(max_seq_len)
     p.alpha = float(alpha)
+    p.out_f32 = int(bool(out_f32))
     return p
+
+
+def _out_f32(in_dtype, out_dtype) -> bool:
+    """Whether a bf16 problem writes its outputs in fp32."""
+    if out_dtype is None or out_dtype == in_dtype:
+        return False
+    if in_dtype == torch.bfloat16 and out_dtype == torch.float32:
+        return True
+    raise TypeError(f"outputs of a {in_dtype} problem can be {in_dtype} or float32, not {out_dtype}")
 
 
 def workspace_size(p: C.SLAProblem, op: int) -> int:
     return int(C.load().sla_workspace_size(ctypes.byref(p), op))
-
-
-def bwd_dq_mode(p: C.SLAProblem) -> int:
-    """1 if the backward computes dQ from stored dS blocks, 0 if it recomputes them."""
-    return int(C.load().sla_bwd_dq_mode(ctypes.byref(p)))
 
 
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
@@ -77,19 +82,23 @@ def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
 def sla_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, offsets: torch.Tensor,
             num_targets: Optional[torch.Tensor] = None, *, k1: int, k2: int,
             contextual_len: int = 0, max_seq_len: int, alpha: float = 1.0,
-            out: Optional[torch.Tensor] = None,
+            out: Optional[torch.Tensor] = None, out_dtype=None,
             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """O[T, H, d_v] = (1/N) (SiLU(alpha Q K^T) * M_SLA) V over jagged sequences."""
+    """O[T, H, d_v] = (1/N) (SiLU(alpha Q K^T) * M_SLA) V over jagged sequences.
+    out_dtype: torch.float32 writes O in fp32 from bf16 inputs (the dtype of a
+    given `out` decides when out_dtype is None)."""
     T, H, dqk = q.shape
     dv = v.shape[2]
     ldq = _head_tensor("q", q, T, H, q.dtype)
     ldk = _head_tensor("k", k, T, H, q.dtype)
     ldv = _head_tensor("v", v, T, H, q.dtype)
+    odt = out_dtype if out_dtype is not None else (out.dtype if out is not None else q.dtype)
+    f32o = _out_f32(q.dtype, odt)
     if out is None:
-        out = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
-    ldo = _head_tensor("out", out, T, H, q.dtype)
+        out = torch.empty((T, H, dv), dtype=odt, device=q.device)
+    ldo = _head_tensor("out", out, T, H, odt)
     p = make_problem(q.dtype, offsets, num_targets, T, H, dqk, dv, k1, k2, contextual_len,
-                     max_seq_len, alpha)
+                     max_seq_len, alpha, f32o)
     nbytes = workspace_size(p, C.SLA_OP_FWD)
     ws = _workspace(nbytes, q.device, workspace)
     C.check(C.load().sla_fwd(ctypes.byref(p), _ptr(q), ldq, _ptr(k), ldk, _ptr(v), ldv, _ptr(out),
@@ -101,6 +110,7 @@ def sla_fwd_candidates(k_hist: torch.Tensor, v_hist: torch.Tensor, hist_offsets:
                        q_c: torch.Tensor, k_c: torch.Tensor, v_c: torch.Tensor,
                        cand_offsets: torch.Tensor, *, k1: int, k2: int, contextual_len: int = 0,
                        max_seq_len: int, alpha: float = 1.0, out: Optional[torch.Tensor] = None,
+                       out_dtype=None,
                        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """O_c[C, H, d_v]: candidates scored against the cached history keys/values
     (each sees the history window of the first candidate slot and itself)."""
@@ -113,13 +123,15 @@ def sla_fwd_candidates(k_hist: torch.Tensor, v_hist: torch.Tensor, hist_offsets:
     ldq = _head_tensor("q_c", q_c, Cn, H, dt)
     ldkc = _head_tensor("k_c", k_c, Cn, H, dt)
     ldvc = _head_tensor("v_c", v_c, Cn, H, dt)
+    odt = out_dtype if out_dtype is not None else (out.dtype if out is not None else dt)
+    f32o = _out_f32(dt, odt)
     if out is None:
-        out = torch.empty((Cn, H, dv), dtype=dt, device=q_c.device)
-    ldo = _head_tensor("out", out, Cn, H, dt)
+        out = torch.empty((Cn, H, dv), dtype=odt, device=q_c.device)
+    ldo = _head_tensor("out", out, Cn, H, odt)
     if cand_offsets.dtype != torch.int64 or cand_offsets.numel() != hist_offsets.numel():
         raise TypeError("cand_offsets must be an int64 tensor [B+1] like hist_offsets")
     p = make_problem(dt, hist_offsets, None, Th, H, dqk, dv, k1, k2, contextual_len, max_seq_len,
-                     alpha)
+                     alpha, f32o)
     lib = C.load()
     nbytes = int(lib.sla_fwd_candidates_workspace_size(ctypes.byref(p), Cn))
     ws = _workspace(nbytes, q_c.device, workspace)
@@ -132,22 +144,28 @@ def sla_fwd_candidates(k_hist: torch.Tensor, v_hist: torch.Tensor, hist_offsets:
 
 def sla_bwd(q, k, v, dout, offsets, num_targets=None, *, k1: int, k2: int,
             contextual_len: int = 0, max_seq_len: int, alpha: float = 1.0, dq=None, dk=None,
-            dv=None, workspace: Optional[torch.Tensor] = None, stage: int = C.SLA_BWD_ALL):
-    """(dQ, dK, dV) of sla_fwd given dO (stage: see sla_bwd_stage in sla.h)."""
+            dv=None, grad_dtype=None, workspace: Optional[torch.Tensor] = None,
+            stage: int = C.SLA_BWD_ALL):
+    """(dQ, dK, dV) of sla_fwd given dO (stage: see sla_bwd_stage in sla.h).
+    grad_dtype: torch.float32 writes the gradients in fp32 from bf16 inputs
+    (the dtype of given output tensors decides when grad_dtype is None)."""
     T, H, dqk = q.shape
     dvd = v.shape[2]
     ldq = _head_tensor("q", q, T, H, q.dtype)
     ldk = _head_tensor("k", k, T, H, q.dtype)
     ldv = _head_tensor("v", v, T, H, q.dtype)
     lddo = _head_tensor("dout", dout, T, H, q.dtype)
-    dq = torch.empty((T, H, dqk), dtype=q.dtype, device=q.device) if dq is None else dq
-    dk = torch.empty((T, H, dqk), dtype=q.dtype, device=q.device) if dk is None else dk
-    dv = torch.empty((T, H, dvd), dtype=q.dtype, device=q.device) if dv is None else dv
-    lddq = _head_tensor("dq", dq, T, H, q.dtype)
-    lddk = _head_tensor("dk", dk, T, H, q.dtype)
-    lddv = _head_tensor("dv", dv, T, H, q.dtype)
+    given = [t for t in (dq, dk, dv) if t is not None]
+    gdt = grad_dtype if grad_dtype is not None else (given[0].dtype if given else q.dtype)
+    f32o = _out_f32(q.dtype, gdt)
+    dq = torch.empty((T, H, dqk), dtype=gdt, device=q.device) if dq is None else dq
+    dk = torch.empty((T, H, dqk), dtype=gdt, device=q.device) if dk is None else dk
+    dv = torch.empty((T, H, dvd), dtype=gdt, device=q.device) if dv is None else dv
+    lddq = _head_tensor("dq", dq, T, H, gdt)
+    lddk = _head_tensor("dk", dk, T, H, gdt)
+    lddv = _head_tensor("dv", dv, T, H, gdt)
     p = make_problem(q.dtype, offsets, num_targets, T, H, dqk, dvd, k1, k2, contextual_len,
-                     max_seq_len, alpha)
+                     max_seq_len, alpha, f32o)
     nbytes = workspace_size(p, C.SLA_OP_BWD)
     ws = _workspace(nbytes, q.device, workspace)
     C.check(C.load().sla_bwd_stage(ctypes.byref(p), stage, _ptr(q), ldq, _ptr(k), ldk, _ptr(v),
@@ -221,8 +239,14 @@ def probe_mfma_peak(iters: int = 4096, device=None) -> dict:
     kernel, and the shader clock during it (sla_probe_mfma_peak)."""
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
     tf, ghz = ctypes.c_double(0.0), ctypes.c_double(0.0)
-    C.check(C.load().sla_probe_mfma_peak(int(iters), ctypes.byref(tf), ctypes.byref(ghz),
-                                         _stream(dev)))
+    lib = C.load()
+    with torch.cuda.device(dev):
+        nbytes = int(lib.sla_probe_scratch_size())
+    if nbytes <= 0:
+        C.check(C.SLA_ERR_DEVICE)
+    scratch = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    C.check(lib.sla_probe_mfma_peak(int(iters), _ptr(scratch), nbytes, ctypes.byref(tf),
+                                    ctypes.byref(ghz), _stream(dev)))
     return {"tflops": tf.value, "sclk_ghz": ghz.value}
 
 

@@ -39,19 +39,25 @@ def bf16_ulp(x):
 
 
 def assert_close_bf16(got, ref, what="", ref_rounded=False):
-    """bf16 tolerance: max|got-ref|/rms(ref) <= 2e-2 and mean <= 5e-3.
+    """bf16 tolerance for a result STORED in bf16: max|got-ref|/rms(ref) <= 2e-2
+    and mean <= 5e-3, with a storage allowance.
 
     A bf16 output cannot be closer to the exact value than bf16 rounding of
     that value.  When that rounding alone uses more than half of the 2e-2
-    budget (outputs with max|ref| > ~5 rms, e.g. one-key windows), each element
-    is allowed one bf16 ulp of its reference value on top of 2e-2 * rms.  The
-    same one-ulp allowance applies when the reference is itself rounded to
-    bf16 (the oracle's storage-matched mode): near a rounding boundary the fp32
-    and fp64 values round to neighbouring bf16 numbers."""
+    budget (outputs whose largest elements are several times their rms: the
+    global-prefix rows of dK and dV, one-key windows), each element is allowed
+    one bf16 ulp of its reference value on top of 2e-2 * rms.  The same
+    one-ulp allowance applies when the reference is itself rounded to bf16
+    (the oracle's storage-matched mode): near a rounding boundary the fp32 and
+    fp64 values round to neighbouring bf16 numbers.  The raw max is printed
+    either way; the stated bar itself is checked by assert_close_raw on fp32
+    outputs."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     mx, mn = rel_errors(got, ref)
     floor = bf16_storage_floor(ref)
+    print(f"  {what}: raw max {mx:.3e} mean {mn:.3e} (bf16 storage floor {floor:.3e})",
+          flush=True)
     if floor <= 0.5 * BF16_MAX_TOL and not ref_rounded:
         assert mx <= BF16_MAX_TOL and mn <= BF16_MEAN_TOL, \
             f"{what}: max {mx:.3e} mean {mn:.3e} (storage floor {floor:.3e})"
@@ -63,6 +69,17 @@ def assert_close_bf16(got, ref, what="", ref_rounded=False):
               f"{floor:.3e}: max {mx:.3e}, max excess over one bf16 ulp {ex:.3e}")
         assert ex <= BF16_MAX_TOL and mn <= BF16_MEAN_TOL, \
             f"{what}: max {mx:.3e} (excess {ex:.3e}) mean {mn:.3e} (storage floor {floor:.3e})"
+    return mx, mn
+
+
+def assert_close_raw(got, ref, what=""):
+    """The bf16 contract bar as stated, with no allowance: max|got-ref|/rms(ref)
+    <= 2e-2 and mean <= 5e-3.  Used for the bf16 path with fp32 outputs, where
+    no output rounding stands between the kernels' arithmetic and the bar."""
+    mx, mn = rel_errors(got, ref)
+    print(f"  {what}: raw max {mx:.3e} mean {mn:.3e} (bar {BF16_MAX_TOL:.0e} / {BF16_MEAN_TOL:.0e})",
+          flush=True)
+    assert mx <= BF16_MAX_TOL and mn <= BF16_MEAN_TOL, f"{what}: max {mx:.3e} mean {mn:.3e}"
     return mx, mn
 
 

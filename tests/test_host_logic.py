@@ -134,26 +134,19 @@ def test_schedule_matches_oracle_tiles(seed):
 
 
 @pytest.mark.parametrize("seed", range(12))
-def test_stored_ds_rows_match_dkdv_blocks(seed):
-    """The 64-row dQ items that read stored dS visit exactly the (row tile, key
-    tile) blocks the dK/dV items write: both are the non-empty tiles of the
-    mask at 64 rows x 128 keys, and the slot order is the record's range order."""
+def test_dkdv_items_cover_the_mask_tiles(seed):
+    """The dK/dV items (128-key tiles walking 64-row steps) visit exactly the
+    non-empty (64-row, 128-key) tiles of the mask, each once."""
     rng = np.random.default_rng(100 + seed)
     lens, offs, tg = _rand_case(rng)
     k1 = int(rng.choice([0, 1, 2, 5, 64, 130, 256, 1000]))
     k2 = int(rng.choice([0, 3, 64, 128, 200]))
     ctx = int(rng.choice([0, 2, 16, 150]))
-    bm, bn = ops.schedule_tile(C.SLA_OP_DQ, 0), ops.schedule_tile(C.SLA_OP_DQ, 1)
-    assert (bm, bn) == (ops.schedule_tile(C.SLA_OP_BWD, 1), ops.schedule_tile(C.SLA_OP_BWD, 0))
-    rec = ops.sla_schedule_host(offs, tg, op=C.SLA_OP_DQ, heads=1, d=128, k1=k1, k2=k2,
-                                contextual_len=ctx)
+    bn, bm = ops.schedule_tile(C.SLA_OP_BWD, 0), ops.schedule_tile(C.SLA_OP_BWD, 1)
     ref = {tuple(map(int, x)) for x in oracle.tiles(offs, tg, k1, k2, ctx, bm, bn)}
-    assert _fwd_pairs(rec, bn) == ref
     recb = ops.sla_schedule_host(offs, tg, op=C.SLA_OP_BWD, heads=1, d=128, k1=k1, k2=k2,
                                  contextual_len=ctx)
     assert _bwd_pairs(recb, lens, tg, bm) == ref
-    n_rows = sum(-(-(L - t) // bm) + -(-t // bm) for L, t in zip(lens, tg or [0] * len(lens)))
-    assert len(rec) == n_rows
 
 
 def test_schedule_long_sequence_splits_prefix_tiles():
@@ -234,25 +227,25 @@ def test_workspace_size_is_host_only(lib):
     assert lib.sla_workspace_size(None, C.SLA_OP_FWD) == 0
 
 
-def test_bwd_dq_mode(lib):
-    # stored dS: bf16, d in {64, 128} and at most 32 key tiles per 64-row tile
+def test_backward_workspace_holds_only_the_prefix_partials(lib):
+    """The backward adds to the forward's schedule only the fp32 partial dK|dV
+    sums of the split global-prefix key tiles (at most 4 tiles of 128 keys
+    per sequence, 16 chunks each): no per-pair storage."""
     big = dict(batch=8, total_tokens=106496, k1=1024, k2=128, ctx=16)
-    assert lib.sla_bwd_dq_mode(ctypes.byref(_problem(**big))) == 1
-    assert lib.sla_bwd_dq_mode(ctypes.byref(_problem(d=64, **big))) == 1
-    assert lib.sla_bwd_dq_mode(ctypes.byref(_problem(d=32, **big))) == 0
-    assert lib.sla_bwd_dq_mode(ctypes.byref(_problem(dtype=C.SLA_F32, **big))) == 0
-    # full causal over 5000 tokens: 40 key tiles per row tile -> recompute
-    full = dict(batch=1, total_tokens=5000, k1=2**31 - 1, k2=0)
-    assert lib.sla_bwd_dq_mode(ctypes.byref(_problem(**full))) == 0
-    assert lib.sla_bwd_dq_mode(ctypes.byref(_problem(d=48, dv=48))) == -1
-    assert lib.sla_bwd_dq_mode(None) == -1
-    # the stored blocks are part of the backward workspace
-    p1, p0 = _problem(**big), _problem(dtype=C.SLA_F32, **big)
-    extra = lib.sla_workspace_size(ctypes.byref(p1), C.SLA_OP_BWD) - \
-        lib.sla_workspace_size(ctypes.byref(p1), C.SLA_OP_FWD)
-    extra0 = lib.sla_workspace_size(ctypes.byref(p0), C.SLA_OP_BWD) - \
-        lib.sla_workspace_size(ctypes.byref(p0), C.SLA_OP_FWD)
-    assert extra - extra0 >= 106496 * 4 * 128 * 2  # at least the fp16 copy of K
+    p = _problem(**big)
+    extra = lib.sla_workspace_size(ctypes.byref(p), C.SLA_OP_BWD) - \
+        lib.sla_workspace_size(ctypes.byref(p), C.SLA_OP_FWD)
+    assert 0 < extra <= 8 * 4 * 16 * 4 * 128 * (128 + 128) * 4 + 256
+
+
+def test_out_f32_flag(lib):
+    """out_f32 is 0 or 1; with it, output token strides are counted in fp32
+    elements (16-byte rows need a multiple of 4), inputs stay bf16."""
+    p = _problem()
+    p.out_f32 = 2
+    assert lib.sla_fwd(ctypes.byref(p), FAKE, 512, FAKE, 512, FAKE, 512, FAKE, 512, FAKE,
+                       1 << 30, None) == C.SLA_ERR_INVALID
+    assert lib.sla_workspace_size(ctypes.byref(p), C.SLA_OP_FWD) == 0
 
 
 def test_bwd_and_layer_argument_errors(lib):
@@ -284,10 +277,14 @@ def test_bwd_and_layer_argument_errors(lib):
 def test_mfma_probe_argument_errors(lib):
     import ctypes
     d = ctypes.c_double(0.0)
-    assert lib.sla_probe_mfma_peak(4096, None, ctypes.byref(d), None) == C.SLA_ERR_NULL
-    assert lib.sla_probe_mfma_peak(0, ctypes.byref(d), ctypes.byref(d), None) == C.SLA_ERR_INVALID
-    assert lib.sla_probe_mfma_peak((1 << 20) + 1, ctypes.byref(d), ctypes.byref(d),
+    assert lib.sla_probe_mfma_peak(4096, FAKE, 1 << 20, None, ctypes.byref(d),
+                                   None) == C.SLA_ERR_NULL
+    assert lib.sla_probe_mfma_peak(4096, None, 1 << 20, ctypes.byref(d), ctypes.byref(d),
+                                   None) == C.SLA_ERR_NULL
+    assert lib.sla_probe_mfma_peak(0, FAKE, 1 << 20, ctypes.byref(d), ctypes.byref(d),
                                    None) == C.SLA_ERR_INVALID
+    assert lib.sla_probe_mfma_peak((1 << 20) + 1, FAKE, 1 << 20, ctypes.byref(d),
+                                   ctypes.byref(d), None) == C.SLA_ERR_INVALID
 
 
 def test_stu_config_rules():
