@@ -23,7 +23,8 @@
  * ---------------------------------------
  * Pointers are DEVICE pointers unless marked "host".  The caller allocates and
  * owns every buffer, workspace included; the library never allocates or frees
- * device memory and keeps no device state between calls.  All work is enqueued
+ * device memory and keeps no device state between calls (one exception:
+ * sla_bwd_noalloc's static workspace array).  All work is enqueued
  * on the caller's stream (hipStream_t passed as void*; NULL = default stream)
  * without any host synchronisation; outputs are valid once the stream reaches
  * that point.  Calls are thread-safe.
@@ -149,6 +150,25 @@ sla_status_t sla_bwd(const sla_problem_t *p, const void *q, int64_t ldq, const v
                      int64_t ldk, const void *v, int64_t ldv, const void *dout, int64_t lddo,
                      void *dq, int64_t lddq, void *dk, int64_t lddk, void *dv, int64_t lddv,
                      void *workspace, size_t ws_bytes, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops or harnesses that forbid allocation): sla_bwd with
+ * the same arguments, kernels and results, minus the workspace.  Its
+ * workspace is a static device array of SLA_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * that the library holds on each device it runs on until the process ends
+ * (its address is looked up on the first call on each device).  The call
+ * allocates and frees nothing.  A problem whose sla_workspace_size(p,
+ * SLA_OP_BWD) exceeds the array -> SLA_ERR_WORKSPACE (about 117K tokens with a
+ * one-tile global prefix at H = 4, d = 128).  Every call on one device shares
+ * that device's array and leaves its contents behind; nothing in it needs to
+ * start at zero, but calls that overlap on one device (two streams, two
+ * threads) race on it and must be serialised by the caller.  Other errors as
+ * sla_bwd. */
+#define SLA_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+sla_status_t sla_bwd_noalloc(const sla_problem_t *p, const void *q, int64_t ldq, const void *k,
+                             int64_t ldk, const void *v, int64_t ldv, const void *dout,
+                             int64_t lddo, void *dq, int64_t lddq, void *dk, int64_t lddk,
+                             void *dv, int64_t lddv, void *stream);
 
 /* The backward in stages: sla_bwd(...) equals, on one stream,
  *   sla_bwd_stage(SLA_BWD_PREPARE)  tile schedule (workspace)

@@ -18,11 +18,12 @@ SLA_F32, SLA_BF16 = 0, 1
 SLA_OP_FWD, SLA_OP_BWD = 0, 1
 SLA_SCHED_RECORD_INTS = 12
 SLA_BWD_ALL, SLA_BWD_PREPARE, SLA_BWD_DKDV, SLA_BWD_DQ = 0, 1, 2, 3
+SLA_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 # every symbol include/sla.h declares
 EXPORTS = (
     "sla_workspace_size", "sla_fwd", "sla_fwd_candidates_workspace_size",
-    "sla_fwd_candidates", "sla_bwd", "sla_bwd_stage", "sla_schedule_capacity", "sla_schedule_tile",
+    "sla_fwd_candidates", "sla_bwd", "sla_bwd_noalloc", "sla_bwd_stage", "sla_schedule_capacity", "sla_schedule_tile",
     "sla_schedule", "sla_schedule_host", "sla_count_pairs_host", "stu_layer_workspace_size", "stu_layer_fwd",
     "stu_layer_bwd_workspace_size", "stu_layer_bwd", "stu_quantize_rows_fp8",
     "stu_layer_fp8_workspace_size", "stu_layer_fwd_fp8", "stu_gather_targets", "stu_truncate", "sla_probe_scratch_size",
@@ -84,6 +85,9 @@ def load(path: str = LIB_PATH):
         lib.sla_bwd.argtypes = [PP, P, i64, P, i64, P, i64, P, i64, P, i64, P, i64, P, i64, P, sz,
                                 P]
         lib.sla_bwd.restype = ctypes.c_int
+        lib.sla_bwd_noalloc.argtypes = [PP, P, i64, P, i64, P, i64, P, i64, P, i64, P, i64, P,
+                                        i64, P]
+        lib.sla_bwd_noalloc.restype = ctypes.c_int
         lib.sla_bwd_stage.argtypes = [PP, ctypes.c_int, P, i64, P, i64, P, i64, P, i64, P, i64, P,
                                       i64, P, i64, P, sz, P]
         lib.sla_bwd_stage.restype = ctypes.c_int

@@ -33,6 +33,7 @@ SOURCES = [
     "stu_fp8.hip",
     "gemm_nt.hip",
     "sla_probe.hip",
+    "sla_noalloc.hip",
 ]
 
 ARCH = "gfx950"

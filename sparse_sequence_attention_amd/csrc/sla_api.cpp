@@ -254,6 +254,11 @@ StuBwdLayout stu_bwd_layout(const stu_layer_desc_t *d)
 
 }  // namespace
 
+int sla::set_last_error(int status, const char *msg)
+{
+    return fail(static_cast<sla_status_t>(status), "%s", msg);
+}
+
 extern "C" {
 
 size_t sla_probe_scratch_size(void)

@@ -9,6 +9,10 @@
 
 namespace sla {
 
+// Record msg as the calling thread's last error (sla_last_error) and return
+// status: for entry points implemented outside sla_api.cpp.
+int set_last_error(int status, const char *msg);
+
 struct AttnParams {
     const void *q, *k, *v;
     void *o;

@@ -174,6 +174,31 @@ def sla_bwd(q, k, v, dout, offsets, num_targets=None, *, k1: int, k2: int,
     return dq, dk, dv
 
 
+def sla_bwd_noalloc(q, k, v, dout, offsets, num_targets=None, *, k1: int, k2: int,
+                    contextual_len: int = 0, max_seq_len: int, alpha: float = 1.0, dq, dk, dv):
+    """sla_bwd for callers that cannot allocate device memory: the caller
+    passes the output tensors (bf16 or fp32 from bf16 inputs), and the
+    workspace is the library's static per-device array (see sla_bwd_noalloc in
+    sla.h: at most SLA_NOALLOC_SCRATCH_BYTES; overlapping calls on one device
+    race).  Neither this wrapper nor the call allocates device memory."""
+    T, H, dqk = q.shape
+    dvd = v.shape[2]
+    ldq = _head_tensor("q", q, T, H, q.dtype)
+    ldk = _head_tensor("k", k, T, H, q.dtype)
+    ldv = _head_tensor("v", v, T, H, q.dtype)
+    lddo = _head_tensor("dout", dout, T, H, q.dtype)
+    gdt = dq.dtype
+    lddq = _head_tensor("dq", dq, T, H, gdt)
+    lddk = _head_tensor("dk", dk, T, H, gdt)
+    lddv = _head_tensor("dv", dv, T, H, gdt)
+    p = make_problem(q.dtype, offsets, num_targets, T, H, dqk, dvd, k1, k2, contextual_len,
+                     max_seq_len, alpha, _out_f32(q.dtype, gdt))
+    C.check(C.load().sla_bwd_noalloc(ctypes.byref(p), _ptr(q), ldq, _ptr(k), ldk, _ptr(v), ldv,
+                                     _ptr(dout), lddo, _ptr(dq), lddq, _ptr(dk), lddk, _ptr(dv),
+                                     lddv, _stream(q.device)))
+    return dq, dk, dv
+
+
 def sla_schedule(offsets, num_targets, *, op: int, heads: int, d: int, k1: int, k2: int,
                  contextual_len: int = 0, total_tokens: int, dtype=torch.bfloat16) -> torch.Tensor:
     """The kernels' work list as an int32 tensor [n, SLA_SCHED_RECORD_INTS] (on the device)."""

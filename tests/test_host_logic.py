@@ -248,6 +248,22 @@ def test_out_f32_flag(lib):
     assert lib.sla_workspace_size(ctypes.byref(p), C.SLA_OP_FWD) == 0
 
 
+def test_noalloc_backward_rejects_problems_beyond_its_array(lib):
+    """sla_bwd_noalloc checks the workspace its problem needs against its
+    static array on the host, before any HIP call; an invalid problem gets
+    sla_bwd's own error."""
+    p = _problem(batch=64, total_tokens=1 << 20, k2=128)
+    need = lib.sla_workspace_size(ctypes.byref(p), C.SLA_OP_BWD)
+    assert need > C.SLA_NOALLOC_SCRATCH_BYTES
+    args = [FAKE, 512] * 7 + [None]
+    assert lib.sla_bwd_noalloc(ctypes.byref(p), *args) == C.SLA_ERR_WORKSPACE
+    msg = lib.sla_last_error()
+    msg = msg.decode() if isinstance(msg, bytes) else msg
+    assert "holds at most" in msg and str(need) in msg
+    p.out_f32 = 2
+    assert lib.sla_bwd_noalloc(ctypes.byref(p), *args) == C.SLA_ERR_INVALID
+
+
 def test_bwd_and_layer_argument_errors(lib):
     p = _problem()
     st = lib.sla_bwd(ctypes.byref(p), FAKE, 512, FAKE, 512, FAKE, 512, None, 512, FAKE, 512,
