@@ -377,6 +377,21 @@ sla_status_t stu_truncate(int32_t batch, int64_t total_tokens, const int64_t *of
                           int64_t *new_offsets, int32_t *new_num_targets, int64_t *gather_idx,
                           void *x_out, int64_t capacity, void *stream);
 
+/* Backward of stu_truncate, its adjoint (ULTRA-HSTU paper, section 4.3: the
+ * layers after the truncation see only the kept rows): given dy, the gradient
+ * of the truncated rows [new_offsets[B]][hidden], writes dx [total_tokens]
+ * [hidden] with dx[s] = dy[r] for every source token s that the truncation
+ * kept as row r and dx[s] = 0 for every token it dropped.  offsets,
+ * num_targets, contextual_len and tail_len are those of the stu_truncate call,
+ * new_offsets its output.  Every row of dx is written once: no atomics, no
+ * host synchronisation.  dtype SLA_BF16 or SLA_F32 for dy and dx; hidden rows
+ * a multiple of 16 bytes; dy and dx 16-byte aligned.  B = 0 or T = 0: no-op.
+ * Errors as stu_truncate. */
+sla_status_t stu_truncate_bwd(int32_t batch, int64_t total_tokens, const int64_t *offsets,
+                              const int32_t *num_targets, int32_t contextual_len,
+                              int32_t tail_len, const int64_t *new_offsets, const void *dy,
+                              int32_t hidden, int32_t dtype, void *dx, void *stream);
+
 /* Measurement aid, not part of the attention path: the bf16 dense MFMA rate
  * the current device sustains, measured with an MFMA-only kernel (four
  * workgroups of four waves per CU, each wave `iters` rounds of four

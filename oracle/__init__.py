@@ -27,6 +27,13 @@ Functions whose results are "parity pinned" and the pins (tests/test_oracle_*):
   stu_layer_fwd_fp8 -- a torch fp64 composition that quantises with torch's
       float8_e4m3fn conversion; FP8 error against the bf16 layer.
   truncate  -- direct set construction, identity when tail >= history.
+  truncate_bwd -- the adjoint identity of the gather (exact on integers);
+      kept rows copy dy, dropped rows are zero.
+  stu_stack_fwd / stu_stack_bwd -- central finite differences of the stack
+      (input and weights before and after the truncation); a one-layer
+      stack equals stu_layer_fwd / stu_layer_bwd.
+  target_rows / mot_fwd -- composition of the pinned stacks: one channel
+      gives that stack's candidate rows; channels concatenate in order.
 """
 from __future__ import annotations
 
@@ -324,3 +331,99 @@ def truncate(offsets, num_targets, ctx, tail_len):
     n = _load().oracle_truncate(B, _ptr(offs), _ptr(tg), ctx, tail_len, _ptr(new_offs),
                                 _ptr(gidx))
     return new_offs, gidx[:n].copy()
+
+
+def truncate_bwd(gather_idx, dy, total_tokens):
+    """Adjoint of the truncation gather (ULTRA-HSTU paper, section 4.3: the
+    truncated layers see a subset of the rows, in order).  The forward copies
+    source row gather_idx[r] to row r, so the gradient of each kept source row
+    is the gradient of its copy and every dropped row gets zero:
+    dx [total_tokens, ...] with dx[gather_idx[r]] = dy[r]."""
+    gidx = np.asarray(gather_idx, dtype=np.int64)
+    dy = _f64(dy)
+    dx = np.zeros((int(total_tokens),) + dy.shape[1:])
+    np.add.at(dx, gidx, dy)
+    return dx
+
+
+def stu_stack_fwd(x, offsets, num_targets, layers, *, heads, dqk, dv, k1, k2, ctx, N,
+                  split_layer=None, tail_len=None, alpha=1.0, eps=1e-5, store_bf16=False,
+                  fp8=False):
+    """The STU stack (ULTRA-HSTU paper, section 4.3): len(layers) layers of
+    stu_layer_fwd, with the attention truncation (keep the contextual prefix,
+    the last tail_len history tokens and the targets) applied to the input of
+    layer split_layer when it is given.  layers: dicts of the stu_layer_fwd
+    weights (ln1_w, w_uvqk, ln2_w, w_out and optional biases).  Returns a dict:
+    out (the last layer's output), offsets (the final layout), gather_idx and
+    source_rows (the truncation's source row of each kept row, and the row
+    count before it; absent without truncation), and per layer its input and
+    its layout (inputs, layouts: lists of (offsets, num_targets))."""
+    cur, offs = _f64(x), _offs(offsets)
+    tg = None if num_targets is None else _tg(num_targets)
+    res = dict(inputs=[], layouts=[])
+    for li, w in enumerate(layers):
+        if split_layer is not None and li == split_layer:
+            res["source_rows"] = cur.shape[0]
+            offs, gidx = truncate(offs, tg, ctx, tail_len)
+            cur = cur[gidx]
+            res["gather_idx"] = gidx
+        res["inputs"].append(cur)
+        res["layouts"].append((offs, tg))
+        layer = stu_layer_fwd_fp8 if fp8 else stu_layer_fwd
+        extra = {} if fp8 else dict(store_bf16=store_bf16)
+        cur = layer(cur, offs, tg, w["ln1_w"], w["w_uvqk"], w["ln2_w"], w["w_out"],
+                    heads=heads, dqk=dqk, dv=dv, k1=k1, k2=k2, ctx=ctx, N=N, alpha=alpha,
+                    eps=eps, ln1_b=w.get("ln1_b"), b_uvqk=w.get("b_uvqk"),
+                    ln2_b=w.get("ln2_b"), b_out=w.get("b_out"), **extra)
+    res["out"], res["offsets"] = cur, offs
+    return res
+
+
+def target_rows(x, offsets, num_targets):
+    """The last num_targets[b] rows of every sequence b, in order (the
+    candidate tokens): [sum of num_targets, ...]."""
+    offs = _offs(offsets)
+    rows = [r for b in range(len(offs) - 1)
+            for r in range(int(offs[b + 1]) - int(num_targets[b]), int(offs[b + 1]))]
+    return _f64(x)[np.asarray(rows, dtype=np.int64)]
+
+
+def mot_fwd(channels, num_targets, *, fp8=False, store_bf16=True):
+    """Mixture of Transducers (ULTRA-HSTU paper, section 4.3 and Appendix A;
+    the torcheasyrec page's MoT bullet): each channel runs its own stack over
+    its own sequences (which all end in the same candidates), and the
+    channels' candidate rows are concatenated along the features, channel by
+    channel.  channels: dicts with x, offsets, layers and the stu_stack_fwd
+    keywords (heads, dqk, dv, k1, k2, ctx, N, split_layer, tail_len).
+    Returns [sum of num_targets, sum of the channel widths]."""
+    outs = []
+    for ch in channels:
+        kw = {k: v for k, v in ch.items() if k not in ("x", "offsets", "layers")}
+        r = stu_stack_fwd(ch["x"], ch["offsets"], num_targets, ch["layers"], fp8=fp8,
+                          store_bf16=store_bf16, **kw)
+        outs.append(target_rows(r["out"], r["offsets"], num_targets))
+    return np.concatenate(outs, axis=1)
+
+
+def stu_stack_bwd(fwd, layers, dout, *, heads, dqk, dv, k1, k2, ctx, N, split_layer=None,
+                  alpha=1.0, eps=1e-5, store_bf16=False):
+    """Gradients of stu_stack_fwd's output given dout, by the chain rule over
+    the layers in reverse: each layer's stu_layer_bwd at its saved input and
+    layout, and at the truncation the adjoint of its gather (truncate_bwd).
+    fwd: the dict stu_stack_fwd returned.  Returns dict(dx [rows of the stack
+    input, D], layers=[per-layer gradient dicts])."""
+    g = _f64(dout)
+    grads = [None] * len(layers)
+    for li in reversed(range(len(layers))):
+        w = layers[li]
+        offs, tg = fwd["layouts"][li]
+        r = stu_layer_bwd(fwd["inputs"][li], offs, tg, w["ln1_w"], w["w_uvqk"], w["ln2_w"],
+                          w["w_out"], g, heads=heads, dqk=dqk, dv=dv, k1=k1, k2=k2, ctx=ctx, N=N,
+                          alpha=alpha, eps=eps, ln1_b=w.get("ln1_b"), b_uvqk=w.get("b_uvqk"),
+                          ln2_b=w.get("ln2_b"), b_out=w.get("b_out"), store_bf16=store_bf16)
+        grads[li] = r
+        g = r["dx"]
+        if split_layer is not None and li == split_layer:
+            # copies and zeros only: nothing to round
+            g = truncate_bwd(fwd["gather_idx"], g, fwd["source_rows"])
+    return dict(dx=g, layers=grads)

@@ -12,6 +12,7 @@ from .ops import (  # noqa: F401
     sla_fwd, sla_fwd_candidates, sla_bwd, sla_bwd_noalloc, sla_attention, sla_schedule, sla_schedule_host, schedule_tile, count_pairs_host,
     probe_mfma_peak,
     stu_layer_fwd, stu_layer_bwd, stu_layer_workspace_bytes, stu_quantize_rows_fp8,
-    stu_layer_fwd_fp8, stu_gather_targets, stu_truncate, make_problem, workspace_size,
+    stu_layer_fwd_fp8, stu_gather_targets, stu_truncate, stu_truncate_bwd, make_problem,
+    workspace_size,
 )
-from .stack import MoTChannel, STULayerWeights, mot_fwd, stu_stack_fwd  # noqa: F401
+from .stack import MoTChannel, STULayerWeights, mot_fwd, stu_stack_bwd, stu_stack_fwd  # noqa: F401

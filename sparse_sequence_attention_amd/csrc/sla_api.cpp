@@ -985,4 +985,32 @@ sla_status_t stu_truncate(int32_t batch, int64_t total_tokens, const int64_t *of
     return SLA_OK;
 }
 
+sla_status_t stu_truncate_bwd(int32_t batch, int64_t total_tokens, const int64_t *offsets,
+                              const int32_t *num_targets, int32_t contextual_len,
+                              int32_t tail_len, const int64_t *new_offsets, const void *dy,
+                              int32_t hidden, int32_t dtype, void *dx, void *stream)
+{
+    if (batch < 0 || total_tokens < 0 || contextual_len < 0)
+        return fail(SLA_ERR_INVALID, "negative batch, total_tokens or contextual_len");
+    if (tail_len < 1) return fail(SLA_ERR_INVALID, "tail_len must be >= 1");
+    if (batch == 0 || total_tokens == 0) return SLA_OK;  // nothing is read or written
+    if (!offsets || !new_offsets || !dy || !dx)
+        return fail(SLA_ERR_NULL, "offsets, new_offsets, dy or dx is NULL");
+    if (dtype != SLA_F32 && dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "bad dtype");
+    const int eb = dtype == SLA_BF16 ? 2 : 4;
+    if (hidden <= 0 || ((int64_t)hidden * eb) % 16 != 0)
+        return fail(SLA_ERR_UNSUPPORTED, "hidden row must be a positive multiple of 16 bytes");
+    if (!aligned16(dy) || !aligned16(dx))
+        return fail(SLA_ERR_UNSUPPORTED, "dy / dx not 16-byte aligned");
+    if (total_tokens >= (int64_t)1 << 30)
+        return fail(SLA_ERR_UNSUPPORTED, "total_tokens too large");
+    sla_status_t st = check_device();
+    if (st != SLA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_truncate_bwd(batch, total_tokens, offsets, num_targets, contextual_len,
+                                       tail_len, new_offsets, dy, hidden, eb, dx, s);
+    if (e != hipSuccess) return hip_fail(e, "truncation backward kernel");
+    return SLA_OK;
+}
+
 }  // extern "C"

@@ -147,6 +147,11 @@ hipError_t launch_ln_quant_fp8(bool gated, const void *x, int64_t ldx, const voi
 hipError_t launch_gemm_fp8(const void *A, const float *sa, const void *W, const float *sw,
                            const float *bias, const void *R, int64_t ldr, void *C, int64_t ldc,
                            int64_t M, int N, int K, int epi, hipStream_t st);
+// adjoint of the truncation gather: dx [T][hidden] fully written
+hipError_t launch_truncate_bwd(int B, int64_t T, const int64_t *offsets,
+                               const int32_t *num_targets, int ctx, int tail,
+                               const int64_t *new_offsets, const void *dy, int hidden,
+                               int elem_bytes, void *dx, hipStream_t st);
 hipError_t launch_truncate(int B, int64_t T, const int64_t *offsets, const int32_t *num_targets,
                            int ctx, int tail, const void *x, int hidden, int elem_bytes,
                            int64_t *new_offsets, int32_t *new_num_targets, int64_t *gather_idx,

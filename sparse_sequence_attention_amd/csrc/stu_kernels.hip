@@ -279,6 +279,55 @@ hipError_t launch_truncate(int B, int64_t T, const int64_t *offsets, const int32
     return hipGetLastError();
 }
 
+// The adjoint of the gather (the truncation backward): one wave per SOURCE
+// row s.  Row s of sequence b (li = s - offsets[b]) was kept iff li < c or li
+// >= keep_from, as row new_offsets[b] + (li < c ? li : c + li - keep_from);
+// dx[s] is that row of dy, or zero for a dropped token.  Every dx row is
+// written once, and no two waves write the same row: no atomics.
+__global__ __launch_bounds__(256) void truncate_scatter_kernel(
+    int B, int64_t T, const int64_t *offsets, const int32_t *num_targets, int ctx, int tail,
+    const int64_t *new_offsets, const uint8_t *dy, int row_bytes, uint8_t *dx)
+{
+    const int64_t s = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (s >= T) return;
+    int lo = 0, hi = B - 1;  // last b with offsets[b] <= s
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (offsets[mid] <= s) lo = mid;
+        else hi = mid - 1;
+    }
+    const int b = lo;
+    int L, c, kf;
+    trunc_dims(offsets, num_targets, b, ctx, tail, L, c, kf);
+    const int li = (int)(s - offsets[b]);
+    const bool kept = li < c || li >= kf;
+    const int64_t r = new_offsets[b] + (li < c ? li : c + (li - kf));
+    uint8_t *d = dx + s * row_bytes;
+    if (kept) {  // uniform per wave: dy is read only for kept rows
+        const uint8_t *src = dy + r * row_bytes;
+        for (int e = 16 * lane; e < row_bytes; e += 16 * 64)
+            *reinterpret_cast<uint4 *>(d + e) = *reinterpret_cast<const uint4 *>(src + e);
+    } else {
+        const uint4 z = {0u, 0u, 0u, 0u};
+        for (int e = 16 * lane; e < row_bytes; e += 16 * 64)
+            *reinterpret_cast<uint4 *>(d + e) = z;
+    }
+}
+
+hipError_t launch_truncate_bwd(int B, int64_t T, const int64_t *offsets,
+                               const int32_t *num_targets, int ctx, int tail,
+                               const int64_t *new_offsets, const void *dy, int hidden,
+                               int elem_bytes, void *dx, hipStream_t st)
+{
+    if (T <= 0 || B <= 0) return hipSuccess;
+    dim3 grid((unsigned)((T + 3) / 4)), block(256);
+    hipLaunchKernelGGL(truncate_scatter_kernel, grid, block, 0, st, B, T, offsets, num_targets,
+                       ctx, tail, new_offsets, (const uint8_t *)dy, hidden * elem_bytes,
+                       (uint8_t *)dx);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // target rows (candidates) of a jagged batch, gathered into a column block of
 // a [total targets][ld_out] output (Mixture of Transducers: each channel's

@@ -521,3 +521,24 @@ def stu_truncate(x: Optional[torch.Tensor], offsets: torch.Tensor,
                                   _ptr(new_nt), _ptr(gidx), _ptr(x_out), int(capacity),
                                   _stream(dev)))
     return x_out, new_offsets, new_nt[:B], gidx
+
+
+def stu_truncate_bwd(dy: torch.Tensor, offsets: torch.Tensor, num_targets: Optional[torch.Tensor],
+                     new_offsets: torch.Tensor, *, contextual_len: int, tail_len: int,
+                     total_tokens: int, dx: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gradient of stu_truncate's input rows given dy, the gradient of its kept
+    rows (rows of dy past new_offsets[-1] are not read): dx [total_tokens, D],
+    each kept row's gradient at its source row, zeros for dropped rows."""
+    if dy.dim() != 2 or not dy.is_contiguous():
+        raise TypeError("dy must be a contiguous [rows, D] tensor")
+    B = offsets.numel() - 1
+    hidden = dy.shape[1]
+    if dx is None:
+        dx = torch.empty((total_tokens, hidden), dtype=dy.dtype, device=dy.device)
+    if tuple(dx.shape) != (total_tokens, hidden) or dx.dtype != dy.dtype or not dx.is_contiguous():
+        raise TypeError("dx must be a contiguous [total_tokens, D] tensor of dy's dtype")
+    C.check(C.load().stu_truncate_bwd(B, int(total_tokens), _ptr(offsets), _ptr(num_targets),
+                                      int(contextual_len), int(tail_len), _ptr(new_offsets),
+                                      _ptr(dy), hidden, _DT[dy.dtype], _ptr(dx),
+                                      _stream(dy.device)))
+    return dx

@@ -1,6 +1,8 @@
-"""STU stack forward driver: a loop over stu_layer_fwd with one stu_truncate
-call before the first truncated layer (ULTRA-HSTU paper, section 4.3: after
-N1 full-length layers keep the most recent UIH tokens for the remaining N2).
+"""STU stack drivers: the forward, a loop over stu_layer_fwd with one
+stu_truncate call before the first truncated layer (ULTRA-HSTU paper,
+section 4.3: after N1 full-length layers keep the most recent UIH tokens for
+the remaining N2), and its backward, a reverse loop over stu_layer_bwd with
+stu_truncate_bwd at the truncation.
 
 The driver only sequences C-ABI calls.  It reads the truncated token count
 back once (one device-to-host copy of new_offsets[B]) to size the following
@@ -49,6 +51,11 @@ class StackOutput:
     layer_tokens: List[int] = field(default_factory=list)
     layer_inputs: List[torch.Tensor] = field(default_factory=list)   # with keep_layers
     layer_outputs: List[torch.Tensor] = field(default_factory=list)
+    # (offsets, num_targets) each layer ran on, and the truncation's own
+    # input layout and its new offsets (with keep_layers: what the backward needs)
+    layer_layouts: List[tuple] = field(default_factory=list)
+    trunc_source: Optional[tuple] = None
+    trunc_new_offsets: Optional[torch.Tensor] = None
 
 
 def stu_stack_fwd(cfg: STUConfig, layers: List[STULayerWeights], x: torch.Tensor,
@@ -62,15 +69,19 @@ def stu_stack_fwd(cfg: STUConfig, layers: List[STULayerWeights], x: torch.Tensor
     cur, offs, tg = x, offsets, num_targets
     for li, w in enumerate(layers):
         if cfg.truncation_enabled and li == cfg.attn_truncation_split_layer:
+            if keep_layers:
+                out.trunc_source = (offs, tg, int(cur.shape[0]))
             xt, offs, tg, gidx = ops.stu_truncate(cur, offs, tg,
                                                   contextual_len=cfg.contextual_seq_len,
                                                   tail_len=cfg.attn_truncation_tail_len)
             n = int(offs[-1].item())
             cur = xt[:n]
             out.gather_idx = gidx[:n]
+            out.trunc_new_offsets = offs
         out.layer_tokens.append(int(cur.shape[0]))
         if keep_layers:
             out.layer_inputs.append(cur)
+            out.layer_layouts.append((offs, tg))
         kw = dict(heads=cfg.num_heads, d_qk=cfg.attention_dim, d_v=cfg.hidden_dim,
                   k1=cfg.kernel_k1, k2=cfg.kernel_k2, contextual_len=cfg.contextual_seq_len,
                   max_seq_len=cfg.max_seq_len, alpha=cfg.alpha, ln_eps=cfg.ln_eps,
@@ -86,6 +97,41 @@ def stu_stack_fwd(cfg: STUConfig, layers: List[STULayerWeights], x: torch.Tensor
             out.layer_outputs.append(cur)
     out.x, out.offsets, out.num_targets = cur, offs, tg
     return out
+
+
+def stu_stack_bwd(cfg: STUConfig, layers: List[STULayerWeights], fwd: StackOutput,
+                  dout: torch.Tensor) -> dict:
+    """Backward of stu_stack_fwd (bf16 projections) by the chain rule over the
+    layers in reverse: stu_layer_bwd of each layer at its saved input (the
+    attention output recomputed), and at the truncation stu_truncate_bwd,
+    the adjoint of its gather (ULTRA-HSTU paper, section 4.3; the backward
+    of Code Listing 1 per layer).  fwd: stu_stack_fwd(..., keep_layers=True).
+    dout: gradient of fwd.x.  Returns dict(dx: gradient of the stack input,
+    layers: per-layer gradient dicts of stu_layer_bwd)."""
+    if len(layers) != cfg.attn_num_layers or len(fwd.layer_inputs) != len(layers):
+        raise ValueError("fwd must come from stu_stack_fwd(..., keep_layers=True) on these layers")
+    if tuple(dout.shape) != tuple(fwd.x.shape):
+        raise ValueError("dout must be shaped like the stack output")
+    g = dout.contiguous()
+    grads: List[dict] = [dict() for _ in layers]
+    split = cfg.attn_truncation_split_layer if cfg.truncation_enabled else None
+    for li in reversed(range(len(layers))):
+        w = layers[li]
+        offs, tg = fwd.layer_layouts[li]
+        r = ops.stu_layer_bwd(fwd.layer_inputs[li], g, offs, tg, w.ln1_w, w.w_uvqk, w.ln2_w,
+                              w.w_out, heads=cfg.num_heads, d_qk=cfg.attention_dim,
+                              d_v=cfg.hidden_dim, k1=cfg.kernel_k1, k2=cfg.kernel_k2,
+                              contextual_len=cfg.contextual_seq_len, max_seq_len=cfg.max_seq_len,
+                              alpha=cfg.alpha, ln_eps=cfg.ln_eps, ln1_b=w.ln1_b,
+                              b_uvqk=w.b_uvqk, ln2_b=w.ln2_b, b_out=w.b_out)
+        g = r.pop("dx")
+        grads[li] = r
+        if split is not None and li == split:
+            src_offs, src_tg, src_rows = fwd.trunc_source
+            g = ops.stu_truncate_bwd(g, src_offs, src_tg, fwd.trunc_new_offsets,
+                                     contextual_len=cfg.contextual_seq_len,
+                                     tail_len=cfg.attn_truncation_tail_len, total_tokens=src_rows)
+    return dict(dx=g, layers=grads)
 
 
 @dataclass
