@@ -390,8 +390,11 @@ def bench_stu_stack(args):
     offs = torch.from_numpy(sw.offsets).to(dev)
     tg = torch.from_numpy(sw.num_targets).to(dev)
 
+    lens_host = np.diff(sw.offsets)
+
     def step():
-        return stu_stack_fwd(cfg, layers, x, offs, tg, fp8=args.fp8)
+        return stu_stack_fwd(cfg, layers, x, offs, tg, fp8=args.fp8, lengths_host=lens_host,
+                             num_targets_host=sw.num_targets)
 
     for _ in range(args.warmup):
         res = step()

@@ -271,7 +271,15 @@ typedef struct {
     sla_problem_t attn;
     int32_t hidden;  /* D */
     float ln_eps;    /* LayerNorm epsilon (e.g. 1e-5) */
+    int32_t flags;   /* 0, or STU_REUSE_SCHEDULE (forward calls only)        */
 } stu_layer_desc_t;
+
+/* flags: the workspace already holds the attention tile schedule of this
+ * layout, written by an earlier stu_layer_fwd or stu_layer_fwd_fp8 call on the
+ * same stream with the same workspace, offsets, num_targets, total_tokens,
+ * num_heads, k1, k2 and contextual_len (a stack's layers between two
+ * truncations); the call skips rebuilding it.  stu_layer_bwd requires 0. */
+#define STU_REUSE_SCHEDULE 1
 
 size_t stu_layer_workspace_size(const stu_layer_desc_t *d);
 sla_status_t stu_layer_fwd(const stu_layer_desc_t *d, const void *x, const float *ln1_w,

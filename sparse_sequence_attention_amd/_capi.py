@@ -19,6 +19,7 @@ SLA_OP_FWD, SLA_OP_BWD = 0, 1
 SLA_SCHED_RECORD_INTS = 12
 SLA_BWD_ALL, SLA_BWD_PREPARE, SLA_BWD_DKDV, SLA_BWD_DQ = 0, 1, 2, 3
 SLA_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
+STU_REUSE_SCHEDULE = 1
 
 # every symbol include/sla.h declares
 EXPORTS = (
@@ -52,7 +53,8 @@ class SLAProblem(ctypes.Structure):
 
 
 class STULayerDesc(ctypes.Structure):
-    _fields_ = [("attn", SLAProblem), ("hidden", ctypes.c_int32), ("ln_eps", ctypes.c_float)]
+    _fields_ = [("attn", SLAProblem), ("hidden", ctypes.c_int32), ("ln_eps", ctypes.c_float),
+                ("flags", ctypes.c_int32)]
 
 
 class SLAError(RuntimeError):

@@ -259,6 +259,12 @@ int sla::set_last_error(int status, const char *msg)
     return fail(static_cast<sla_status_t>(status), "%s", msg);
 }
 
+namespace {
+sla_status_t fwd_impl(const sla_problem_t *p, const void *q, int64_t ldq, const void *k,
+                      int64_t ldk, const void *v, int64_t ldv, void *o, int64_t ldo,
+                      void *workspace, size_t ws_bytes, void *stream, bool build_schedule);
+}
+
 extern "C" {
 
 size_t sla_probe_scratch_size(void)
@@ -417,6 +423,18 @@ sla_status_t sla_fwd(const sla_problem_t *p, const void *q, int64_t ldq, const v
                      const void *v, int64_t ldv, void *o, int64_t ldo, void *workspace,
                      size_t ws_bytes, void *stream)
 {
+    return fwd_impl(p, q, ldq, k, ldk, v, ldv, o, ldo, workspace, ws_bytes, stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+// sla_fwd; build_schedule false: the workspace already holds this layout's
+// schedule (a stack's later layers)
+sla_status_t fwd_impl(const sla_problem_t *p, const void *q, int64_t ldq, const void *k,
+                      int64_t ldk, const void *v, int64_t ldv, void *o, int64_t ldo,
+                      void *workspace, size_t ws_bytes, void *stream, bool build_schedule)
+{
     sla_status_t st = validate_problem(p);
     if (st != SLA_OK) return st;
     if (p->batch == 0 || p->total_tokens == 0) return SLA_OK;  // nothing is read or written
@@ -433,12 +451,18 @@ sla_status_t sla_fwd(const sla_problem_t *p, const void *q, int64_t ldq, const v
     if ((st = validate_layout(p->batch, p->total_tokens, p->offsets, p->num_targets, -1, workspace,
                               s)) != SLA_OK)
         return st;
-    hipError_t e = launch_sched(a, s);
-    if (e != hipSuccess) return hip_fail(e, "schedule kernel");
+    hipError_t e = hipSuccess;
+    if (build_schedule) {
+        e = launch_sched(a, s);
+        if (e != hipSuccess) return hip_fail(e, "schedule kernel");
+    }
     e = p->dtype == SLA_BF16 ? launch_fwd_bf16(a, s) : launch_fwd_f32(a, s);
     if (e != hipSuccess) return hip_fail(e, "forward kernel");
     return SLA_OK;
 }
+}  // namespace
+
+extern "C" {
 
 size_t sla_fwd_candidates_workspace_size(const sla_problem_t *p, int64_t total_candidates)
 {
@@ -610,6 +634,7 @@ sla_status_t stu_layer_fwd(const stu_layer_desc_t *d, const void *x, const float
 {
     if (!d) return fail(SLA_ERR_NULL, "layer descriptor is NULL");
     const sla_problem_t *p = &d->attn;
+    if (d->flags & ~STU_REUSE_SCHEDULE) return fail(SLA_ERR_INVALID, "unknown layer flags");
     sla_status_t st = validate_problem(p);
     if (st != SLA_OK) return st;
     if (p->dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "the STU layer is bf16 only");
@@ -658,8 +683,9 @@ sla_status_t stu_layer_fwd(const stu_layer_desc_t *d, const void *x, const float
     e = launch_gemm_bf16(n, D, w_uvqk, D, b_uvqk, nullptr, 0, uvqk, NW, nullptr, 0, T, NW, D, 0, s);
     if (e != hipSuccess) return hip_fail(e, "uvqk projection");
     // U | V | Q | K column blocks of the fused projection
-    st = sla_fwd(p, u16 + 2 * NU, NW, u16 + 2 * NU + H * dqk, NW, u16 + NU, NW, A, NU, attn_ws,
-                 attn_bytes, stream);
+    st = fwd_impl(p, u16 + 2 * NU, NW, u16 + 2 * NU + H * dqk, NW, u16 + NU, NW, A, NU, attn_ws,
+                 attn_bytes, stream,
+                  !(d->flags & STU_REUSE_SCHEDULE));
     if (st != SLA_OK) return st;
     e = launch_gated_layernorm_bf16(A, NU, u16, NW, ln2_w, ln2_b, y, T, NU, d->ln_eps, s);
     if (e != hipSuccess) return hip_fail(e, "gated layernorm");
@@ -684,6 +710,7 @@ sla_status_t stu_layer_bwd(const stu_layer_desc_t *d, const void *x, const void 
 {
     if (!d) return fail(SLA_ERR_NULL, "layer descriptor is NULL");
     const sla_problem_t *p = &d->attn;
+    if (d->flags) return fail(SLA_ERR_INVALID, "stu_layer_bwd takes no layer flags");
     sla_status_t st = validate_problem(p);
     if (st != SLA_OK) return st;
     if (p->dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "the STU layer is bf16 only");
@@ -851,6 +878,7 @@ sla_status_t stu_layer_fwd_fp8(const stu_layer_desc_t *d, const void *x, const f
 {
     if (!d) return fail(SLA_ERR_NULL, "layer descriptor is NULL");
     const sla_problem_t *p = &d->attn;
+    if (d->flags & ~STU_REUSE_SCHEDULE) return fail(SLA_ERR_INVALID, "unknown layer flags");
     sla_status_t st = validate_problem(p);
     if (st != SLA_OK) return st;
     if (p->dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "the STU layer is bf16 only");
@@ -904,8 +932,9 @@ sla_status_t stu_layer_fwd_fp8(const stu_layer_desc_t *d, const void *x, const f
     e = launch_gemm_fp8(nq, sn, w_uvqk_q, w_uvqk_scale, b_uvqk, nullptr, 0, uvqk, NW, T, NW, D, 0,
                         s);
     if (e != hipSuccess) return hip_fail(e, "uvqk projection (fp8)");
-    st = sla_fwd(p, u16 + 2 * NU, NW, u16 + 2 * NU + H * dqk, NW, u16 + NU, NW, A, NU, attn_ws,
-                 attn_bytes, stream);
+    st = fwd_impl(p, u16 + 2 * NU, NW, u16 + 2 * NU + H * dqk, NW, u16 + NU, NW, A, NU, attn_ws,
+                 attn_bytes, stream,
+                  !(d->flags & STU_REUSE_SCHEDULE));
     if (st != SLA_OK) return st;
     e = launch_ln_quant_fp8(true, A, NU, u16, NW, ln2_w, ln2_b, yq, sy, T, NU, d->ln_eps, s);
     if (e != hipSuccess) return hip_fail(e, "gated layernorm + quantisation");

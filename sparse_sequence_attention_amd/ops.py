@@ -79,6 +79,14 @@ def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
+def _reused_workspace(nbytes: int, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    """The caller's workspace, which must already hold a schedule: never
+    replaced by a fresh one."""
+    if ws is None or ws.numel() * ws.element_size() < nbytes:
+        raise ValueError("reuse_schedule needs the workspace of the call that built the schedule")
+    return ws
+
+
 def sla_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, offsets: torch.Tensor,
             num_targets: Optional[torch.Tensor] = None, *, k1: int, k2: int,
             contextual_len: int = 0, max_seq_len: int, alpha: float = 1.0,
@@ -309,11 +317,14 @@ def stu_layer_fwd(x: torch.Tensor, offsets: torch.Tensor, num_targets: Optional[
                   contextual_len: int, max_seq_len: int, alpha: float = 1.0,
                   ln_eps: float = 1e-5, ln1_b=None, b_uvqk=None, ln2_b=None, b_out=None,
                   out: Optional[torch.Tensor] = None, want_uvqk: bool = False,
-                  want_attn: bool = False, workspace: Optional[torch.Tensor] = None):
+                  want_attn: bool = False, workspace: Optional[torch.Tensor] = None,
+                  reuse_schedule: bool = False):
     """One STU layer forward (bf16): LN -> UVQK GEMM + SiLU -> SLA -> LN(A)*U -> GEMM + x.
 
     Returns out, then uvqk [T, NW] if want_uvqk, then the attention output
-    A [T, H*d_v] if want_attn (what stu_layer_bwd keeps from the forward)."""
+    A [T, H*d_v] if want_attn (what stu_layer_bwd keeps from the forward).
+    reuse_schedule: the given workspace holds this layout's attention
+    schedule from an earlier layer call (STU_REUSE_SCHEDULE in sla.h)."""
     if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
         raise TypeError("x must be a contiguous bf16 [T, D] tensor")
     T, D = x.shape
@@ -330,9 +341,11 @@ def stu_layer_fwd(x: torch.Tensor, offsets: torch.Tensor, num_targets: Optional[
                           contextual_len, max_seq_len, alpha)
     d.hidden = D
     d.ln_eps = float(ln_eps)
+    d.flags = C.STU_REUSE_SCHEDULE if reuse_schedule else 0
     lib = C.load()
     nbytes = int(lib.stu_layer_workspace_size(ctypes.byref(d)))
-    ws = _workspace(nbytes, x.device, workspace)
+    ws = _reused_workspace(nbytes, workspace) if reuse_schedule else \
+        _workspace(nbytes, x.device, workspace)
     out = torch.empty_like(x) if out is None else out
     uvqk = torch.empty((T, nw), dtype=torch.bfloat16, device=x.device) if want_uvqk else None
     attn = torch.empty((T, heads * d_v), dtype=torch.bfloat16, device=x.device) if want_attn else None
@@ -363,7 +376,8 @@ def stu_layer_fwd_fp8(x: torch.Tensor, offsets: torch.Tensor, num_targets: Optio
                       max_seq_len: int, alpha: float = 1.0, ln_eps: float = 1e-5, ln1_b=None,
                       b_uvqk=None, ln2_b=None, b_out=None, out: Optional[torch.Tensor] = None,
                       want_uvqk: bool = False, want_attn: bool = False,
-                      workspace: Optional[torch.Tensor] = None):
+                      workspace: Optional[torch.Tensor] = None,
+                      reuse_schedule: bool = False):
     """stu_layer_fwd with both projections in FP8 (weights from
     stu_quantize_rows_fp8).  Returns out (then uvqk, attn if asked)."""
     if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
@@ -385,9 +399,11 @@ def stu_layer_fwd_fp8(x: torch.Tensor, offsets: torch.Tensor, num_targets: Optio
                           contextual_len, max_seq_len, alpha)
     d.hidden = D
     d.ln_eps = float(ln_eps)
+    d.flags = C.STU_REUSE_SCHEDULE if reuse_schedule else 0
     lib = C.load()
     nbytes = int(lib.stu_layer_fp8_workspace_size(ctypes.byref(d)))
-    ws = _workspace(nbytes, x.device, workspace)
+    ws = _reused_workspace(nbytes, workspace) if reuse_schedule else \
+        _workspace(nbytes, x.device, workspace)
     out = torch.empty_like(x) if out is None else out
     uvqk = torch.empty((T, nw), dtype=torch.bfloat16, device=x.device) if want_uvqk else None
     attn = torch.empty((T, nu), dtype=torch.bfloat16, device=x.device) if want_attn else None
@@ -403,15 +419,18 @@ def stu_layer_fwd_fp8(x: torch.Tensor, offsets: torch.Tensor, num_targets: Optio
 def stu_layer_workspace_bytes(T: int, D: int, offsets: torch.Tensor,
                               num_targets: Optional[torch.Tensor], *, heads: int, d_qk: int,
                               d_v: int, k1: int, k2: int, contextual_len: int, max_seq_len: int,
-                              alpha: float = 1.0, backward: bool = False) -> int:
-    """Workspace bytes of stu_layer_fwd (or stu_layer_bwd) for T tokens of width D."""
+                              alpha: float = 1.0, backward: bool = False,
+                              fp8: bool = False) -> int:
+    """Workspace bytes of stu_layer_fwd (stu_layer_bwd, stu_layer_fwd_fp8) for T
+    tokens of width D."""
     d = C.STULayerDesc()
     d.attn = make_problem(torch.bfloat16, offsets, num_targets, T, heads, d_qk, d_v, k1, k2,
                           contextual_len, max_seq_len, alpha)
     d.hidden = D
     d.ln_eps = 1e-5
     lib = C.load()
-    fn = lib.stu_layer_bwd_workspace_size if backward else lib.stu_layer_workspace_size
+    fn = lib.stu_layer_bwd_workspace_size if backward else \
+        lib.stu_layer_fp8_workspace_size if fp8 else lib.stu_layer_workspace_size
     return int(fn(ctypes.byref(d)))
 
 

@@ -4,9 +4,11 @@ section 4.3: after N1 full-length layers keep the most recent UIH tokens for
 the remaining N2), and its backward, a reverse loop over stu_layer_bwd with
 stu_truncate_bwd at the truncation.
 
-The driver only sequences C-ABI calls.  It reads the truncated token count
-back once (one device-to-host copy of new_offsets[B]) to size the following
-layers' buffers.
+The driver only sequences C-ABI calls.  The layers between two truncations
+share one workspace and one attention tile schedule (built by the first of
+them).  The truncated token count sizes the following layers' buffers: it is
+computed on the host from host copies of the layout when the caller gives
+them, else read back once (one device-to-host copy of new_offsets[B]).
 """
 from __future__ import annotations
 
@@ -58,15 +60,35 @@ class StackOutput:
     trunc_new_offsets: Optional[torch.Tensor] = None
 
 
+def truncated_tokens_host(lengths, num_targets, contextual_len: int, tail_len: int) -> int:
+    """Token count after the attention truncation, from host copies of the
+    sequence lengths and target counts: per sequence the contextual prefix
+    min(ctx, U), at most tail_len history tokens and the targets, U = L - nt."""
+    n = 0
+    for b, L in enumerate(lengths):
+        nt = int(num_targets[b]) if num_targets is not None else 0
+        U = int(L) - nt
+        c = min(contextual_len, U)
+        n += c + min(tail_len, U - c) + nt
+    return n
+
+
 def stu_stack_fwd(cfg: STUConfig, layers: List[STULayerWeights], x: torch.Tensor,
                   offsets: torch.Tensor, num_targets: Optional[torch.Tensor],
-                  keep_layers: bool = False, fp8: bool = False) -> StackOutput:
+                  keep_layers: bool = False, fp8: bool = False, lengths_host=None,
+                  num_targets_host=None) -> StackOutput:
     """fp8: both projections of every layer in FP8 (stu_layer_fwd_fp8), with
-    the weights' FP8 copies from STULayerWeights.quantize_fp8()."""
+    the weights' FP8 copies from STULayerWeights.quantize_fp8().
+    lengths_host, num_targets_host: host copies of the sequence lengths and
+    target counts (they must describe the device layout); with them the
+    stack runs without reading anything back from the device."""
     if len(layers) != cfg.attn_num_layers:
         raise ValueError(f"{len(layers)} layer weights for {cfg.attn_num_layers} layers")
+    if lengths_host is not None and len(lengths_host) != offsets.numel() - 1:
+        raise ValueError("lengths_host must hold one length per sequence")
     out = StackOutput(x=x, offsets=offsets, num_targets=num_targets)
     cur, offs, tg = x, offsets, num_targets
+    ws = None   # workspace of the current layout, holding its attention schedule
     for li, w in enumerate(layers):
         if cfg.truncation_enabled and li == cfg.attn_truncation_split_layer:
             if keep_layers:
@@ -74,18 +96,29 @@ def stu_stack_fwd(cfg: STUConfig, layers: List[STULayerWeights], x: torch.Tensor
             xt, offs, tg, gidx = ops.stu_truncate(cur, offs, tg,
                                                   contextual_len=cfg.contextual_seq_len,
                                                   tail_len=cfg.attn_truncation_tail_len)
-            n = int(offs[-1].item())
+            if lengths_host is not None:
+                n = truncated_tokens_host(lengths_host, num_targets_host, cfg.contextual_seq_len,
+                                          cfg.attn_truncation_tail_len)
+            else:
+                n = int(offs[-1].item())
             cur = xt[:n]
             out.gather_idx = gidx[:n]
             out.trunc_new_offsets = offs
+            ws = None
         out.layer_tokens.append(int(cur.shape[0]))
         if keep_layers:
             out.layer_inputs.append(cur)
             out.layer_layouts.append((offs, tg))
         kw = dict(heads=cfg.num_heads, d_qk=cfg.attention_dim, d_v=cfg.hidden_dim,
                   k1=cfg.kernel_k1, k2=cfg.kernel_k2, contextual_len=cfg.contextual_seq_len,
-                  max_seq_len=cfg.max_seq_len, alpha=cfg.alpha, ln_eps=cfg.ln_eps,
-                  ln1_b=w.ln1_b, b_uvqk=w.b_uvqk, ln2_b=w.ln2_b, b_out=w.b_out)
+                  max_seq_len=cfg.max_seq_len, alpha=cfg.alpha)
+        reuse = ws is not None
+        if ws is None:
+            nbytes = ops.stu_layer_workspace_bytes(int(cur.shape[0]), int(cur.shape[1]), offs, tg,
+                                                   fp8=fp8, **kw)
+            ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=cur.device)
+        kw.update(ln_eps=cfg.ln_eps, ln1_b=w.ln1_b, b_uvqk=w.b_uvqk, ln2_b=w.ln2_b,
+                  b_out=w.b_out, workspace=ws, reuse_schedule=reuse)
         if fp8:
             if w.w_uvqk_q is None or w.w_out_q is None:
                 raise ValueError(f"layer {li}: FP8 weights missing (call quantize_fp8())")

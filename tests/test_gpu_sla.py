@@ -195,6 +195,35 @@ def test_large_logits_stay_finite(dtype):
         chk(_np(g), r, name)
 
 
+def test_inputs_beyond_the_fp16_range():
+    """bf16 keeps fp32's exponent range and the bf16 path computes in bf16 and
+    fp32 only: V and dO of magnitude up to ~5e5, and logits s = q.k with
+    |SiLU(s)| past 65504 (fp16's largest value), are no special case.
+    Checked against the oracle at the raw bar with fp32 outputs."""
+    w = make_sla_workload("jagged_2k", seed=41, lengths=[300, 257], heads=2, d=64, k1=64, k2=8,
+                          contextual_len=2, max_seq_len=300, dtype="bf16", with_dout=True)
+    from synthetic import bf16_round_f32
+    w.q[...] = bf16_round_f32(w.q * 90.0)
+    w.k[...] = bf16_round_f32(w.k * 90.0)
+    w.v[...] = bf16_round_f32(w.v * 2.0 ** 17)
+    w.dout[...] = bf16_round_f32(w.dout * 2.0 ** 17)
+    s_max = float(np.abs(np.einsum("thd,shd->hts", w.q[:300].astype(np.float64),
+                                   w.k[:300].astype(np.float64))).max())
+    assert s_max > 65504.0 and float(np.abs(w.v).max()) > 65504.0, s_max
+    _print_case("beyond fp16 range", w)
+    q, k, v, do, offs, tgd = _dev(w)
+    o = sla.sla_fwd(q, k, v, offs, tgd, out_dtype=torch.float32, **_kw(w))
+    dq, dk, dv = sla.sla_bwd(q, k, v, do, offs, tgd, grad_dtype=torch.float32, **_kw(w))
+    torch.cuda.synchronize()
+    ro = oracle.sla_fwd(w.q, w.k, w.v, w.offsets, w.num_targets, w.k1, w.k2, w.contextual_len,
+                        w.max_seq_len)
+    rq, rk, rv = oracle.sla_bwd(w.q, w.k, w.v, w.dout, w.offsets, w.num_targets, w.k1, w.k2,
+                                w.contextual_len, w.max_seq_len)
+    for name, g, r in (("O", o, ro), ("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        assert torch.isfinite(g).all(), name
+        assert_close_raw(_np(g), r, name)
+
+
 def test_alpha_and_strided_views():
     """alpha != 1 and Q/K/V as column blocks of one fused buffer."""
     lens = [300, 77]

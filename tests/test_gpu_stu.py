@@ -217,3 +217,34 @@ def test_stack_18_layers_full_config():
     res = _check_stack(sw, every_layer=False)
     assert res.layer_tokens[:9] == [int(sw.offsets[-1])] * 9
     assert res.layer_tokens[9:] == [8 * (16 + 1024 + 64)] * 9
+
+
+def test_stack_with_host_lengths_equals_device_readback():
+    """Host copies of the layout (no device read-back) and the schedule shared
+    by the layers of one layout give the same stack output, bit for bit, as
+    the read-back path; layer by layer the shared schedule equals a fresh one."""
+    sw = make_stack_workload(seed=5, batch=3, min_len=300, max_len=900, layers=3, split_layer=1,
+                             tail_len=200, k1=128, k2=32, contextual_len=8, num_targets=16)
+    cfg = _stack_cfg(sw)
+    layers = [_layer_weights(sw, li)[0] for li in range(sw.layers)]
+    x = _b(sw.x)
+    offs = torch.from_numpy(sw.offsets).to(DEV)
+    tg = torch.from_numpy(sw.num_targets).to(DEV)
+    print(f"[case] stack host lengths T={int(sw.offsets[-1])}", flush=True)
+    a = stu_stack_fwd(cfg, layers, x, offs, tg, keep_layers=True)
+    b = stu_stack_fwd(cfg, layers, x, offs, tg, lengths_host=np.diff(sw.offsets),
+                      num_targets_host=sw.num_targets)
+    torch.cuda.synchronize()
+    assert a.layer_tokens == b.layer_tokens
+    assert torch.equal(a.x, b.x)
+    # each layer on its own (fresh workspace, schedule rebuilt) gives the same output
+    for li in range(sw.layers):
+        lo, lt = a.layer_layouts[li]
+        w = layers[li]
+        one = sla.stu_layer_fwd(a.layer_inputs[li], lo, lt, w.ln1_w, w.w_uvqk, w.ln2_w, w.w_out,
+                                heads=cfg.num_heads, d_qk=cfg.attention_dim, d_v=cfg.hidden_dim,
+                                k1=cfg.kernel_k1, k2=cfg.kernel_k2,
+                                contextual_len=cfg.contextual_seq_len,
+                                max_seq_len=cfg.max_seq_len)
+        torch.cuda.synchronize()
+        assert torch.equal(one, a.layer_outputs[li]), li

@@ -370,3 +370,22 @@ def test_gather_targets_argument_errors(lib):
     assert call(hidden=12) == C.SLA_ERR_UNSUPPORTED                    # not 16-byte rows
     assert call(col=4) == C.SLA_ERR_UNSUPPORTED                        # misaligned column block
     assert call(dtype=7) == C.SLA_ERR_UNSUPPORTED
+
+
+def test_truncated_token_count_on_the_host_matches_the_oracle():
+    """stu_stack_fwd's host-side count of the truncated layout (used instead
+    of reading new_offsets[B] back) equals the oracle truncation's total."""
+    import numpy as np
+    import oracle
+    from sparse_sequence_attention_amd.stack import truncated_tokens_host
+    rng = np.random.default_rng(7)
+    for _ in range(20):
+        B = int(rng.integers(1, 12))
+        lens = [int(v) for v in rng.integers(0, 400, size=B)]
+        tg = [int(rng.integers(0, L + 1)) for L in lens]
+        ctx, tail = int(rng.integers(0, 20)), int(rng.integers(1, 200))
+        offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+        new_offs, _ = oracle.truncate(offs, tg, ctx, tail)
+        assert truncated_tokens_host(lens, tg, ctx, tail) == int(new_offs[-1])
+        new_offs, _ = oracle.truncate(offs, None, ctx, tail)
+        assert truncated_tokens_host(lens, None, ctx, tail) == int(new_offs[-1])
