@@ -38,7 +38,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--workload", choices=(WORKLOAD, "stu_layer", "stu_stack", "mfalcon"),
+    ap.add_argument("--workload", choices=(WORKLOAD, "stu_layer", "stu_stack", "mfalcon",
+                                           "targets_16k"),
                     default=WORKLOAD,
                     help="long_16k: the SLA forward + backward (default); stu_layer: one full "
                          "STU layer forward + backward at the 18-layer stack's shape; "
@@ -133,6 +134,9 @@ def main():
         return
     if args.workload == "stu_stack":
         bench_stu_stack(args)
+        return
+    if args.workload == "targets_16k":
+        bench_targets_fwd(args)
         return
     import torch
     import sparse_sequence_attention_amd as sla
@@ -444,6 +448,82 @@ def bench_stu_stack(args):
         },
         "tokens_per_s": round(int(sw.offsets[-1]) / (ms * 1e-3), 1),
         "pct_of_bf16_peak": round(100.0 * value / PEAK_MFMA_TFLOPS, 2),
+        "wall_s_timed_region": round(wall, 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_targets_fwd(args):
+    """The target-aware SLA forward at inference (targets_16k: B = 16, each
+    sequence a 16-token contextual prefix + U[8192, 16384] history tokens +
+    256 candidate targets; K1 = 1024, K2 = 128, H = 4, d = 128, bf16 inputs
+    and output).  A candidate sees the prefix, the history under the K1 / K2
+    window of the first target slot, and itself.  A step is one sla_fwd call
+    (schedule included); useful flops are 4d per visible pair and head."""
+    import torch
+    import sparse_sequence_attention_amd as sla
+    from synthetic import make_sla_workload
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = make_sla_workload("targets_16k", seed=args.seed)
+    t = lambda a: torch.from_numpy(a).to(dev).to(torch.bfloat16)  # noqa: E731
+    q, k, v = t(w.q), t(w.k), t(w.v)
+    offs = torch.from_numpy(w.offsets).to(dev)
+    tg = torch.from_numpy(w.num_targets).to(dev)
+    T, H, d = q.shape
+    kw = dict(k1=w.k1, k2=w.k2, contextual_len=w.contextual_len, max_seq_len=w.max_seq_len,
+              alpha=w.alpha)
+    p = sla.make_problem(torch.bfloat16, offs, tg, T, H, d, d, w.k1, w.k2, w.contextual_len,
+                         w.max_seq_len, w.alpha)
+    ws = torch.empty(max(1, sla.workspace_size(p, sla.SLA_OP_FWD)), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty_like(q)
+
+    def step():
+        sla.sla_fwd(q, k, v, offs, tg, out=out, workspace=ws, **kw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+    pairs = sla.count_pairs_host(w.offsets, w.num_targets, w.k1, w.k2, w.contextual_len) * H
+    useful = pairs * 4 * d
+    value = useful / (ms * 1e-3) / 1e12
+    line = {
+        "metric": "target-aware SLA forward useful TFLOP/s and tokens/s at L=16K (inference)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"targets_16k: B=16, 16 ctx + U[8192,16384] history + 256 targets per "
+                        f"sequence (T={T}), K1={w.k1}, K2={w.k2}, H={H}, d={d}, "
+                        f"N={w.max_seq_len}, bf16 in and out, seed {args.seed}",
+            "visible_pairs_all_heads": pairs,
+            "useful_flop_per_step": useful,
+        },
+        "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_MFMA_TFLOPS, 2),
+        "roofline": {"kernel": "fwd", "bound": "mfma", "achieved": round(value, 2),
+                     "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(value / PEAK_MFMA_TFLOPS, 4), "traffic": None},
         "wall_s_timed_region": round(wall, 4),
     }
     print(json.dumps(line), flush=True)

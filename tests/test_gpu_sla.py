@@ -341,7 +341,9 @@ def test_jagged_2k_config_fwd_bwd(seed):
 
 
 def _sample_rows(w, n, rng):
-    """Sampled tokens: first/last rows of sequences, tile edges and random rows."""
+    """Sampled tokens: first/last rows of sequences, tile edges and random rows;
+    with targets, every target row of the first and the last sequence and the
+    rows around every sequence's first target slot U."""
     T = w.total_tokens
     sel = np.zeros(T, np.uint8)
     for b in range(w.batch):
@@ -350,6 +352,13 @@ def _sample_rows(w, n, rng):
                   s1 - 2, s1 - 257):
             if s0 <= r < s1:
                 sel[r] = 1
+        if w.num_targets is not None:
+            u = s1 - int(w.num_targets[b])
+            for r in range(u - 3, u + 3):
+                if s0 <= r < s1:
+                    sel[r] = 1
+            if b in (0, w.batch - 1):
+                sel[u:s1] = 1
     sel[rng.integers(0, T, size=n)] = 1
     return sel
 
