@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--no-peak-probe", action="store_true",
                     help="skip the MFMA-only probe (run after the timed steps) that reports the "
                          "bf16 MFMA rate and shader clock measured on this GPU")
+    ap.add_argument("--issue-probe", action="store_true",
+                    help="long_16k: after the timed steps, run the issue-rate probe (MFMA and "
+                         "VALU overlap on one SIMD, transcendental cost) and add its durations")
     ap.add_argument("--cpu-sample-tokens", type=int, default=65536,
                     help="cpu_baseline: whole sequences from the start of the workload up to "
                          "about this many tokens (long_16k: its four 16384-token sequences)")
@@ -261,6 +264,9 @@ def main():
             "pct_of_measured_peak": round(100.0 * value / pm["tflops"], 2),
             "roofline_frac_of_measured_peak": round(achieved / pm["tflops"], 4),
         }
+    if args.issue_probe:
+        ip = sla.probe_issue_rates()
+        line["issue_probe"] = {k: round(v, 4) for k, v in ip.items()}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
     print(json.dumps(line), flush=True)

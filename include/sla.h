@@ -416,6 +416,23 @@ size_t sla_probe_scratch_size(void);
 sla_status_t sla_probe_mfma_peak(int32_t iters, void *scratch, size_t scratch_bytes, double *tflops,
                                  double *sclk_ghz, void *stream);
 
+/* Measurement aid, not part of the attention path: how far one SIMD of the
+ * current device runs MFMA and VALU instructions concurrently, and the rate
+ * of the SiLU's transcendentals.  One workgroup of eight waves per CU (two
+ * per SIMD); per SIMD every MFMA arrangement issues 2 * iters * 4
+ * v_mfma_f32_32x32x16_bf16 (four independent chains) and every VALU one
+ * 2 * iters * 32 v_fma_f32 (eight independent chains).  ms[0..6] receive the
+ * duration of one launch (after a warm-up, HIP events on `stream`, which is
+ * synchronised) of: 0 MFMA only, 1 FMA only, 2 one wave per SIMD with all the
+ * MFMAs and the other with all the FMAs, 3 both waves half of each,
+ * interleaved, 4 as 2 with the accumulators in AGPRs, 5 v_exp_f32 only and
+ * 6 v_rcp_f32 only (32 per round, in place of the FMAs of 1).  n_ms >= 7.
+ * scratch: caller-owned device memory of at least sla_probe_scratch_size()
+ * bytes (16-byte aligned), overwritten; a smaller one -> SLA_ERR_WORKSPACE.
+ * Allocates nothing.  1 <= iters <= 1048576 (4096: about 0.5 ms per mode). */
+sla_status_t sla_probe_issue_rates(int32_t iters, void *scratch, size_t scratch_bytes, double *ms,
+                                   int32_t n_ms, void *stream);
+
 const char *sla_status_string(sla_status_t s);
 const char *sla_last_error(void); /* thread-local message of the last failure */
 

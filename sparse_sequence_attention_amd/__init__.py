@@ -10,6 +10,7 @@ from ._capi import (  # noqa: F401
 from .config import STUConfig  # noqa: F401
 from .ops import (  # noqa: F401
     sla_fwd, sla_fwd_candidates, sla_bwd, sla_bwd_noalloc, sla_attention, sla_schedule, sla_schedule_host, schedule_tile, count_pairs_host,
+    probe_issue_rates,
     probe_mfma_peak,
     stu_layer_fwd, stu_layer_bwd, stu_layer_workspace_bytes, stu_quantize_rows_fp8,
     stu_layer_fwd_fp8, stu_gather_targets, stu_truncate, stu_truncate_bwd, make_problem,

@@ -28,7 +28,7 @@ EXPORTS = (
     "sla_schedule", "sla_schedule_host", "sla_count_pairs_host", "stu_layer_workspace_size", "stu_layer_fwd",
     "stu_layer_bwd_workspace_size", "stu_layer_bwd", "stu_quantize_rows_fp8",
     "stu_layer_fp8_workspace_size", "stu_layer_fwd_fp8", "stu_gather_targets", "stu_truncate", "stu_truncate_bwd", "sla_probe_scratch_size",
-    "sla_probe_mfma_peak", "sla_status_string",
+    "sla_probe_mfma_peak", "sla_probe_issue_rates", "sla_status_string",
     "sla_last_error",
 )
 
@@ -113,6 +113,8 @@ def load(path: str = LIB_PATH):
         lib.sla_probe_scratch_size.restype = sz
         lib.sla_probe_mfma_peak.argtypes = [i32, P, sz, DBL, DBL, P]
         lib.sla_probe_mfma_peak.restype = i32
+        lib.sla_probe_issue_rates.argtypes = [i32, P, sz, DBL, i32, P]
+        lib.sla_probe_issue_rates.restype = i32
         DP = ctypes.POINTER(STULayerDesc)
         lib.stu_layer_workspace_size.argtypes = [DP]
         lib.stu_layer_workspace_size.restype = sz

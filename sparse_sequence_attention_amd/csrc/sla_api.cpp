@@ -275,7 +275,8 @@ size_t sla_probe_scratch_size(void)
         cus <= 0)
         return 0;
     // the sink (one float per thread of 4 workgroups of 256 per CU), then the
-    // two clock counters
+    // two clock counters; the issue-rate probe's sink (one workgroup of 512
+    // per CU) fits in the same
     return round_up(sizeof(float) * (size_t)4 * cus * 256, 256) + 2 * sizeof(unsigned long long);
 }
 
@@ -319,6 +320,44 @@ sla_status_t sla_probe_mfma_peak(int32_t iters, void *scratch, size_t scratch_by
     *tflops = mfma_peak_flops(blocks, iters) / ((double)ms * 1e-3) / 1e12;
     // the constant clock counts at 100 MHz: GHz = cycles / (ticks * 10)
     *sclk_ghz = hclk[1] > 0 ? (double)hclk[0] / ((double)hclk[1] * 10.0) : 0.0;
+    return SLA_OK;
+}
+
+sla_status_t sla_probe_issue_rates(int32_t iters, void *scratch, size_t scratch_bytes, double *ms,
+                                   int32_t n_ms, void *stream)
+{
+    if (!ms || !scratch) return fail(SLA_ERR_NULL, "ms or scratch is NULL");
+    if (n_ms < ISSUE_MODES) return fail(SLA_ERR_INVALID, "ms holds %d entries < %d modes", n_ms, (int)ISSUE_MODES);
+    if (iters < 1 || iters > (1 << 20)) return fail(SLA_ERR_INVALID, "iters %d outside [1, 2^20]", iters);
+    sla_status_t st = check_device();
+    if (st != SLA_OK) return st;
+    int dev = -1, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "device attributes");
+    const int blocks = cus;  // one 512-thread workgroup per CU
+    const size_t sink_bytes = sizeof(float) * (size_t)blocks * 512;
+    if (scratch_bytes < sink_bytes)
+        return fail(SLA_ERR_WORKSPACE, "probe scratch of %zu bytes < %zu required", scratch_bytes, sink_bytes);
+    if (!aligned16(scratch)) return fail(SLA_ERR_UNSUPPORTED, "probe scratch is not 16-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float *sink = static_cast<float *>(scratch);
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    e = hipEventCreate(&e0);
+    if (e == hipSuccess) e = hipEventCreate(&e1);
+    for (int m = 0; m < ISSUE_MODES && e == hipSuccess; ++m) {
+        float t = 0.0f;
+        e = launch_issue_probe(m, blocks, iters, sink, s);  // warm-up
+        if (e == hipSuccess) e = hipEventRecord(e0, s);
+        if (e == hipSuccess) e = launch_issue_probe(m, blocks, iters, sink, s);
+        if (e == hipSuccess) e = hipEventRecord(e1, s);
+        if (e == hipSuccess) e = hipEventSynchronize(e1);
+        if (e == hipSuccess) e = hipEventElapsedTime(&t, e0, e1);
+        ms[m] = (double)t;
+    }
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    if (e != hipSuccess) return hip_fail(e, "issue-rate probe");
     return SLA_OK;
 }
 

@@ -119,6 +119,11 @@ int ln_bwd_blocks(int64_t rows);
 hipError_t launch_mfma_peak(int blocks, int iters, float *sink, unsigned long long *clk,
                             hipStream_t st);
 double mfma_peak_flops(int blocks, int iters);
+// modes of the issue-rate probe (sla_probe.hip); one workgroup of 512
+// threads per CU, `sink` one float per thread
+enum IssueMode { ISSUE_MFMA = 0, ISSUE_VALU, ISSUE_SPLIT, ISSUE_MIXED, ISSUE_SPLIT_A, ISSUE_EXP, ISSUE_RCP,
+                 ISSUE_MODES };
+hipError_t launch_issue_probe(int mode, int blocks, int iters, float *sink, hipStream_t st);
 hipError_t launch_ln_bwd_bf16(bool gated, const void *x, int64_t ldx, const void *dy, int64_t lddy,
                               const void *u, int64_t ldu, const float *w, const float *b,
                               const void *res, int64_t ldres, void *dx, int64_t lddx, void *du,

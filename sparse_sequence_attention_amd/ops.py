@@ -283,6 +283,34 @@ def probe_mfma_peak(iters: int = 4096, device=None) -> dict:
     return {"tflops": tf.value, "sclk_ghz": ghz.value}
 
 
+ISSUE_PROBE_MODES = ("mfma_only", "fma_only", "split_waves", "mixed_waves", "split_waves_agpr",
+                     "exp_only", "rcp_only")
+
+
+def probe_issue_rates(iters: int = 4096, device=None) -> dict:
+    """Durations (ms) of the issue-rate probe's arrangements on the current
+    device (sla_probe_issue_rates), and two ratios derived from them: the
+    share of the shorter of MFMA-only and FMA-only that a SIMD hides when one
+    wave issues the MFMAs and the other the FMAs (1 = full overlap, 0 = none),
+    and the time of a transcendental relative to an FMA."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    lib = C.load()
+    with torch.cuda.device(dev):
+        nbytes = int(lib.sla_probe_scratch_size())
+    if nbytes <= 0:
+        C.check(C.SLA_ERR_DEVICE)
+    scratch = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    ms = (ctypes.c_double * len(ISSUE_PROBE_MODES))()
+    C.check(lib.sla_probe_issue_rates(int(iters), _ptr(scratch), nbytes, ms, len(ms), _stream(dev)))
+    r = {k: ms[i] for i, k in enumerate(ISSUE_PROBE_MODES)}
+    tm, tv = r["mfma_only"], r["fma_only"]
+    for k in ("split_waves", "mixed_waves", "split_waves_agpr"):
+        r["hidden_" + k] = (tm + tv - r[k]) / min(tm, tv)
+    r["exp_per_fma"] = r["exp_only"] / tv
+    r["rcp_per_fma"] = r["rcp_only"] / tv
+    return r
+
+
 class SLAFunction(torch.autograd.Function):
     """Autograd wrapper: forward sla_fwd, backward sla_bwd."""
 

@@ -96,3 +96,17 @@ def test_mfma_probe_reports_a_plausible_rate_and_clock():
     print(f"[case] mfma probe {pm}", flush=True)
     assert 500.0 < pm["tflops"] < 2600.0
     assert 1.0 < pm["sclk_ghz"] < 3.0
+
+
+def test_issue_probe_reports_every_arrangement():
+    """The issue-rate probe: every arrangement takes time; MFMA and FMA work
+    issued together take at least as long as the slower of the two alone and
+    at most as long as both added (with 5% for launch noise); a
+    transcendental takes at least as long as an FMA."""
+    r = sla.probe_issue_rates(iters=1024)
+    print(f"[case] issue probe {r}", flush=True)
+    tm, tv = r["mfma_only"], r["fma_only"]
+    assert all(r[k] > 0.0 for k in sla.ops.ISSUE_PROBE_MODES)
+    for k in ("split_waves", "mixed_waves", "split_waves_agpr"):
+        assert 0.95 * max(tm, tv) <= r[k] <= 1.05 * (tm + tv), k
+    assert r["exp_per_fma"] >= 0.95 and r["rcp_per_fma"] >= 0.95

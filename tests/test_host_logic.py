@@ -303,6 +303,15 @@ def test_mfma_probe_argument_errors(lib):
                                    ctypes.byref(d), None) == C.SLA_ERR_INVALID
 
 
+def test_issue_probe_argument_errors(lib):
+    import ctypes
+    ms = (ctypes.c_double * 7)()
+    assert lib.sla_probe_issue_rates(4096, FAKE, 1 << 20, None, 7, None) == C.SLA_ERR_NULL
+    assert lib.sla_probe_issue_rates(4096, None, 1 << 20, ms, 7, None) == C.SLA_ERR_NULL
+    assert lib.sla_probe_issue_rates(4096, FAKE, 1 << 20, ms, 6, None) == C.SLA_ERR_INVALID
+    assert lib.sla_probe_issue_rates(0, FAKE, 1 << 20, ms, 7, None) == C.SLA_ERR_INVALID
+
+
 def test_stu_config_rules():
     c = STUConfig(sla_k1=256, sla_k2=32, contextual_seq_len=64)
     assert c.sla_enabled and c.effective_k2 == 64
