@@ -39,12 +39,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--workload", choices=(WORKLOAD, "stu_layer", "stu_stack", "mfalcon",
-                                           "targets_16k"),
+                                           "targets_16k", "jagged_2k"),
                     default=WORKLOAD,
                     help="long_16k: the SLA forward + backward (default); stu_layer: one full "
                          "STU layer forward + backward at the 18-layer stack's shape; "
                          "stu_stack: the 18-layer STU stack forward; mfalcon: candidate "
-                         "scoring against cached history keys/values")
+                         "scoring against cached history keys/values; jagged_2k: the SLA "
+                         "forward + backward at B=32, L U[512,2048], eager and as one HIP "
+                         "graph replay")
     ap.add_argument("--fp8", action="store_true",
                     help="stu_stack: both projections of every layer in FP8")
     ap.add_argument("--candidates", type=int, default=4096,
@@ -140,6 +142,9 @@ def main():
         return
     if args.workload == "targets_16k":
         bench_targets_fwd(args)
+        return
+    if args.workload == "jagged_2k":
+        bench_jagged_graph(args)
         return
     import torch
     import sparse_sequence_attention_amd as sla
@@ -269,6 +274,88 @@ def main():
         line["issue_probe"] = {k: round(v, 4) for k, v in ip.items()}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
+    print(json.dumps(line), flush=True)
+
+
+def bench_jagged_graph(args):
+    """SLA forward + backward on the jagged_2k workload (B = 32, lengths
+    U[512, 2048], H = 4, d = 128, K1 = 256, K2 = 64, ctx 8, fp32 outputs),
+    whose steps are short enough for launch gaps to show: K steps issued
+    eagerly, then the same step recorded once as a HIP graph (torch's
+    CUDAGraph over the library's calls, outputs and workspace owned by the
+    caller) and K replays.  Each run is bracketed by synchronisations and
+    timed with events on the stream; value is the replayed rate."""
+    import torch
+    import sparse_sequence_attention_amd as sla
+    from synthetic import make_sla_workload, CONFIGS
+
+    cfg = CONFIGS["jagged_2k"]
+    w = make_sla_workload(cfg, seed=args.seed, with_dout=True)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    dt = torch.bfloat16
+    q, k, v, do = (torch.from_numpy(a).to(dev).to(dt) for a in (w.q, w.k, w.v, w.dout))
+    offs = torch.from_numpy(w.offsets).to(dev)
+    kw = dict(k1=w.k1, k2=w.k2, contextual_len=w.contextual_len, max_seq_len=w.max_seq_len)
+    H, d = cfg.heads, cfg.d
+    o, dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(4))
+    p = sla.make_problem(dt, offs, None, w.total_tokens, H, d, d, **kw, out_f32=True)
+    ws = torch.empty(max(sla.workspace_size(p, sla.SLA_OP_BWD),
+                         sla.workspace_size(p, sla.SLA_OP_FWD)), dtype=torch.uint8, device=dev)
+
+    def step():
+        sla.sla_fwd(q, k, v, offs, None, out=o, workspace=ws, **kw)
+        sla.sla_bwd(q, k, v, do, offs, None, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    for _ in range(args.warmup):
+        step()
+    eager_ms = timed(step)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(args.warmup):
+        g.replay()
+    graph_ms = timed(g.replay)
+
+    pairs = sla.count_pairs_host(w.offsets, None, w.k1, w.k2, w.contextual_len) * H
+    useful = pairs * (2 * (d + d) + 2 * (3 * d + 2 * d))
+    line = {
+        "metric": "SLA fwd+bwd useful TFLOP/s (jagged_2k, eager and HIP graph replay)",
+        "value": round(useful / (graph_ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(graph_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"jagged_2k: {cfg.description}, N={cfg.max_seq_len}, "
+                               f"seed {args.seed}", "outputs": "f32",
+                   "total_tokens": w.total_tokens, "visible_pairs_all_heads": pairs},
+        "eager_ms_per_step": round(eager_ms, 4),
+        "eager_tflops": round(useful / (eager_ms * 1e-3) / 1e12, 2),
+        "graph_ms_per_step": round(graph_ms, 4),
+        "tokens_per_s": round(w.total_tokens / (graph_ms * 1e-3), 1),
+    }
     print(json.dumps(line), flush=True)
 
 
