@@ -80,10 +80,10 @@ sla_status_t validate_problem(const sla_problem_t *p)
         return fail(SLA_ERR_UNSUPPORTED, "total_tokens %lld too large", (long long)p->total_tokens);
     if (p->batch > 0 && !p->offsets) return fail(SLA_ERR_NULL, "offsets is NULL");
     if (p->num_heads < 1) return fail(SLA_ERR_INVALID, "num_heads must be >= 1");
-    if (p->d_qk != 32 && p->d_qk != 64 && p->d_qk != 128)
-        return fail(SLA_ERR_UNSUPPORTED, "head dim %d not in {32, 64, 128}", p->d_qk);
-    if (p->d_v != p->d_qk)
-        return fail(SLA_ERR_UNSUPPORTED, "d_v (%d) must equal d_qk (%d)", p->d_v, p->d_qk);
+    if (!attn_dims_supported(p->d_qk, p->d_v))
+        return fail(SLA_ERR_UNSUPPORTED,
+                    "head widths d_qk = %d, d_v = %d: supported are d_qk = d_v in {32, 64, 128} "
+                    "and (64, 128), (128, 64)", p->d_qk, p->d_v);
     if (p->k1 < 0 || p->k2 < 0 || p->contextual_len < 0)
         return fail(SLA_ERR_INVALID, "k1, k2 and contextual_len must be >= 0");
     if (p->max_seq_len < 1) return fail(SLA_ERR_INVALID, "max_seq_len must be >= 1");
@@ -185,6 +185,7 @@ sla_status_t make_params(const sla_problem_t *p, int op, void *ws, size_t ws_byt
     a.B = p->batch;
     a.H = p->num_heads;
     a.d = p->d_qk;
+    a.d_v = p->d_v;
     a.k1 = p->k1;
     a.k2e = k2_eff(p);
     a.alpha = p->alpha;

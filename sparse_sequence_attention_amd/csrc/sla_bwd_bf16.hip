@@ -73,26 +73,30 @@ __device__ __forceinline__ bf16x8 lo_part(const float *x, const bf16x8 &hi)
                 x[4] - bf16_lo(u.z), x[5] - bf16_hi(u.z), x[6] - bf16_lo(u.w), x[7] - bf16_hi(u.w));
 }
 
-template <int D, bool OUTF32>
+// DQK: the Q / K (and dK) head width, DV: the V, dO (and dV) width.
+template <int DQK, int DV, bool OUTF32>
 __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(AttnParams p)
 {
     constexpr int BN = BWD_BN, BM = BWD_BM;
     constexpr int NT = DKDV_THREADS;
-    constexpr int NC = D / 16, NDB = D / 32, CPR = D / 8;
-    constexpr int TILE = BM * D;             // elements of one staged 64-row tile
-    constexpr int TCH = BM * CPR;            // 16-byte chunks of one staged tile
-    constexpr int SPS = 2 * TCH / NT;        // DMA loads per thread and step
-    constexpr int KCH = BN * CPR;            // 16-byte chunks of the K (or V) tile
-    constexpr int KPT = 2 * KCH / NT;        // DMA loads per thread of the K and V tiles
+    constexpr int NC = DQK / 16, NCV = DV / 16;     // 16-wide chunks of Q.K, dO.V
+    constexpr int NDB = DQK / 32, NDBV = DV / 32;   // 32-wide blocks of dK, dV
+    constexpr int CPR = DQK / 8, CPRV = DV / 8;     // 16-byte chunks per Q / K, dO / V row
+    constexpr int DW = DQK + DV;                    // a [Q | dO] or [K | V] row pair
+    constexpr int TCH = BM * CPR, TCHV = BM * CPRV; // chunks of a staged Q, dO tile
+    constexpr int SPS = (TCH + TCHV) / NT;          // DMA loads per thread and step
+    constexpr int KCH = BN * CPR, KCHV = BN * CPRV; // chunks of the K, V tile
+    constexpr int KPT = (KCH + KCHV) / NT;          // DMA loads per thread of the K and V tiles
     constexpr int NST = DKDV_STAGES;
     static_assert(BM == 64 && BN == 128, "64-row steps over 128-key tiles");
-    static_assert((2 * TCH) % NT == 0 && SPS <= 8, "whole DMA rounds, at most 8 per thread");
-    static_assert((2 * KCH) % NT == 0 && KPT <= 8, "whole DMA rounds of the key tile");
+    static_assert((TCH + TCHV) % NT == 0 && SPS <= 8, "whole DMA rounds, at most 8 per thread");
+    static_assert(TCH % 64 == 0 && KCH % NT == 0, "the Q / dO and K / V split is wave-uniform");
+    static_assert((KCH + KCHV) % NT == 0 && KPT <= 8, "whole DMA rounds of the key tile");
     // [K | V] of the key tile (bf16, swizzled rows), then a ring of NST stages
     // of [Q | dO] rows filled by DMA NST - 1 steps ahead: 64 + 96 KB at d = 128
-    __shared__ __align__(16) uint16_t lds[2 * BN * D + NST * 2 * TILE];
+    __shared__ __align__(16) uint16_t lds[BN * DW + NST * BM * DW];
     uint16_t *const kvs = lds;
-    uint16_t *const ring = lds + 2 * BN * D;
+    uint16_t *const ring = lds + BN * DW;
 
     const int nrec = p.s.bwd_base[p.B];
     const int item = xcd_remap(blockIdx.x, nrec * p.H);
@@ -114,10 +118,10 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
     const int l32 = lane & 31, hl = lane >> 5;
     const int kj = it.c0 + 32 * kw + l32;  // this lane's key (mask)
 
-    const uint16_t *qg = reinterpret_cast<const uint16_t *>(p.q) + sd.base * p.ldq + h * D;
-    const uint16_t *kg = reinterpret_cast<const uint16_t *>(p.k) + sd.base * p.ldk + h * D;
-    const uint16_t *vg = reinterpret_cast<const uint16_t *>(p.v) + sd.base * p.ldv + h * D;
-    const uint16_t *gg = reinterpret_cast<const uint16_t *>(p.dout) + sd.base * p.lddo + h * D;
+    const uint16_t *qg = reinterpret_cast<const uint16_t *>(p.q) + sd.base * p.ldq + h * DQK;
+    const uint16_t *kg = reinterpret_cast<const uint16_t *>(p.k) + sd.base * p.ldk + h * DQK;
+    const uint16_t *vg = reinterpret_cast<const uint16_t *>(p.v) + sd.base * p.ldv + h * DV;
+    const uint16_t *gg = reinterpret_cast<const uint16_t *>(p.dout) + sd.base * p.lddo + h * DV;
 
     // row steps: history tiles covering [ha, hb), then target tiles covering [ta, tb)
     int h_first = 0, nh = 0, t_first = 0, nt = 0;
@@ -156,9 +160,10 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
     const float nal2e = p.neg_alpha_log2e, alpha = p.alpha;
 
     // DMA (gl_lds16_async: the kernel's own waits and barriers order it
-    // against the reads).  Thread t owns chunks P = i*NT + t: physical chunk
-    // P % CPR of row (P % tile chunks) / CPR of tile P / (tile chunks), filled
-    // with logical chunk (P % CPR) ^ hswz(row).  Key rows at or past c1 read
+    // against the reads).  Thread t owns chunks P = i*NT + t of the [K | V]
+    // (or [Q | dO]) pair, K (Q) first: chunk P' of a tile of row width w is
+    // physical chunk P' % (w/8) of row P' / (w/8), filled with logical chunk
+    // (P' % (w/8)) ^ hswz<w>(row).  Key rows at or past c1 read
     // row c1 - 1 (keys never stored); step rows at or past m1 read row m1 - 1
     // (masked: such steps are never full).  Every step issues exactly SPS
     // loads per thread, so the wait counts are static.
@@ -170,11 +175,25 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int P = i * NT + wv * 64 + lane;
-            const int tile = P / KCH;  // K or V (uniform per wave)
-            const int prow = (P % KCH) / CPR;
-            const uint32_t row = (uint32_t)imin(prow, last);
-            const uint32_t c = (uint32_t)((P % CPR) ^ hswz<D>(prow));
-            const char *src = tile == 0 ? krow + (row * ldk_b + 16u * c) : vrow + (row * ldv_b + 16u * c);
+            const char *src;
+            if constexpr (DQK == DV) {
+                const int tile = P / KCH;  // K or V (uniform per wave)
+                const int prow = (P % KCH) / CPR;
+                const uint32_t row = (uint32_t)imin(prow, last);
+                const uint32_t c = (uint32_t)((P % CPR) ^ hswz<DQK>(prow));
+                src = tile == 0 ? krow + (row * ldk_b + 16u * c) : vrow + (row * ldv_b + 16u * c);
+            } else if (i * NT < KCH) {  // K (whole rounds: KCH is a multiple of NT)
+                const int prow = P / CPR;
+                const uint32_t row = (uint32_t)imin(prow, last);
+                const uint32_t c = (uint32_t)((P % CPR) ^ hswz<DQK>(prow));
+                src = krow + (row * ldk_b + 16u * c);
+            } else {
+                const int Pv = P - KCH;
+                const int prow = Pv / CPRV;
+                const uint32_t row = (uint32_t)imin(prow, last);
+                const uint32_t c = (uint32_t)((Pv % CPRV) ^ hswz<DV>(prow));
+                src = vrow + (row * ldv_b + 16u * c);
+            }
             gl_lds16_async(src, kvs + (i * NT + wv * 64) * 8);
         }
     };
@@ -186,15 +205,31 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
         const int last = uniform(m1 - 1 - m0);
         const char *qrow = reinterpret_cast<const char *>(qg + (int64_t)m0 * p.ldq);
         const char *grow = reinterpret_cast<const char *>(gg + (int64_t)m0 * p.lddo);
-        uint16_t *sb = ring + (t % NST) * (2 * TILE);
+        uint16_t *sb = ring + (t % NST) * (BM * DW);
 #pragma unroll
         for (int i = 0; i < SPS; ++i) {
             const int P = i * NT + wv * 64 + lane;
-            const int tile = P / TCH;  // Q or dO (uniform per wave)
-            const int prow = (P % TCH) / CPR;
-            const uint32_t row = (uint32_t)imin(prow, last);
-            const uint32_t c = (uint32_t)((P % CPR) ^ hswz<D>(prow));
-            const char *src = tile == 0 ? qrow + (row * ldq_b + 16u * c) : grow + (row * lddo_b + 16u * c);
+            const char *src;
+            if constexpr (DQK == DV) {
+                const int tile = P / TCH;  // Q or dO (uniform per wave)
+                const int prow = (P % TCH) / CPR;
+                const uint32_t row = (uint32_t)imin(prow, last);
+                const uint32_t c = (uint32_t)((P % CPR) ^ hswz<DQK>(prow));
+                src = tile == 0 ? qrow + (row * ldq_b + 16u * c) : grow + (row * lddo_b + 16u * c);
+            } else if ((TCH % NT == 0) ? (i * NT < TCH) : (P < TCH)) {
+                // Q or dO: whole rounds when TCH is a multiple of NT, else
+                // uniform per wave (TCH is a multiple of 64)
+                const int prow = P / CPR;
+                const uint32_t row = (uint32_t)imin(prow, last);
+                const uint32_t c = (uint32_t)((P % CPR) ^ hswz<DQK>(prow));
+                src = qrow + (row * ldq_b + 16u * c);
+            } else {
+                const int Pg = P - TCH;
+                const int prow = Pg / CPRV;
+                const uint32_t row = (uint32_t)imin(prow, last);
+                const uint32_t c = (uint32_t)((Pg % CPRV) ^ hswz<DV>(prow));
+                src = grow + (row * lddo_b + 16u * c);
+            }
             gl_lds16_async(src, sb + (i * NT + wv * 64) * 8);
         }
     };
@@ -217,34 +252,56 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
         return __builtin_bit_cast(uint2, v);
     };
     const uint32_t lds_base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds;
-    // bytes: the [K | V] region (2 BN D bf16), one [Q | dO] stage (2 TILE
-    // bf16), one staged tile
-    constexpr uint32_t KV_BYTES = 4u * BN * D, STAGE_BYTES = 4u * TILE, TILE_BYTES = 2u * TILE;
-    static_assert(KV_BYTES == 2u * BN * D * sizeof(uint16_t), "ring starts after [K | V]");
-    constexpr uint32_t H2_BYTES = 2u * 16u * D;
-    uint32_t aoffs[NC], koffs[NC], toffs[2][NDB];
+    // bytes: the [K | V] region (BN DW bf16), one [Q | dO] stage (BM DW
+    // bf16), the staged Q tile (the dO tile follows it), the K tile (V
+    // follows it)
+    constexpr uint32_t KV_BYTES = 2u * BN * DW, STAGE_BYTES = 2u * BM * DW;
+    constexpr uint32_t TILE_BYTES = 2u * BM * DQK, K_BYTES = 2u * BN * DQK;
+    static_assert(KV_BYTES == BN * DW * sizeof(uint16_t), "ring starts after [K | V]");
+    constexpr uint32_t H2_BYTES = 2u * 16u * DQK, H2V_BYTES = 2u * 16u * DV;
+    // row operands: Q and K (width DQK), dO and V (width DV); transposing
+    // reads: Q (dK products) and dO (dV products)
+    uint32_t aoffs[NC], koffs[NC], goffs[NCV], voffs[NCV], toffs[2][NDB], tgoffs[2][NDBV];
+    const int ar = 32 * rh + l32, br = 32 * kw + l32;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        const int ar = 32 * rh + l32, br = 32 * kw + l32;
-        aoffs[c] = 2u * (uint32_t)(ar * D + 8 * ((2 * c + hl) ^ hswz<D>(ar)));
-        koffs[c] = lds_base + 2u * (uint32_t)(br * D + 8 * ((2 * c + hl) ^ hswz<D>(br)));
+        aoffs[c] = 2u * (uint32_t)(ar * DQK + 8 * ((2 * c + hl) ^ hswz<DQK>(ar)));
+        koffs[c] = lds_base + 2u * (uint32_t)(br * DQK + 8 * ((2 * c + hl) ^ hswz<DQK>(br)));
+    }
+#pragma unroll
+    for (int c = 0; c < NCV; ++c) {
+        if constexpr (DV == DQK) {  // the same per-lane offsets, one tile further
+            goffs[c] = aoffs[c] + TILE_BYTES;
+            voffs[c] = koffs[c] + K_BYTES;
+        } else {
+            goffs[c] = TILE_BYTES + 2u * (uint32_t)(ar * DV + 8 * ((2 * c + hl) ^ hswz<DV>(ar)));
+            voffs[c] = lds_base + K_BYTES +
+                       2u * (uint32_t)(br * DV + 8 * ((2 * c + hl) ^ hswz<DV>(br)));
+        }
     }
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
+        const int row = 32 * rh + 8 * rr + 4 * (q4 >> 1) + (j16 >> 2);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-            const int row = 32 * rh + 8 * rr + 4 * (q4 >> 1) + (j16 >> 2);
             const int col = 32 * db + 16 * (q4 & 1) + 4 * (j16 & 3);
-            toffs[rr][db] = 2u * (uint32_t)(row * D + 8 * ((col >> 3) ^ hswz<D>(row)) + (col & 7));
+            toffs[rr][db] = 2u * (uint32_t)(row * DQK + 8 * ((col >> 3) ^ hswz<DQK>(row)) + (col & 7));
+        }
+#pragma unroll
+        for (int db = 0; db < NDBV; ++db) {
+            const int col = 32 * db + 16 * (q4 & 1) + 4 * (j16 & 3);
+            if constexpr (DV == DQK) tgoffs[rr][db] = toffs[rr][db] + TILE_BYTES;
+            else
+                tgoffs[rr][db] = TILE_BYTES + 2u * (uint32_t)(row * DV + 8 * ((col >> 3) ^ hswz<DV>(row)) +
+                                                             (col & 7));
         }
     }
 
-    floatx16 dkacc[NDB], dvacc[NDB];
+    floatx16 dkacc[NDB], dvacc[NDBV];
 #pragma unroll
-    for (int i = 0; i < NDB; ++i) {
-        dkacc[i] = zero16();
-        dvacc[i] = zero16();
-    }
+    for (int i = 0; i < NDB; ++i) dkacc[i] = zero16();
+#pragma unroll
+    for (int i = 0; i < NDBV; ++i) dvacc[i] = zero16();
 
     // One step of this wave's 32 rows x 32 keys: S = Q K^T and dP = dO V^T,
     // then P = s sigma (= SiLU(t) / alpha) and dS = g sigma (1 + t (1 -
@@ -273,10 +330,9 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
 
         floatx16 sacc = zero16(), pacc = zero16();
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const uint32_t qa = aoffs[c] + sb;
-            sacc = mfma32(lds_row(qa), lds_row(koffs[c]), sacc);
-            pacc = mfma32(lds_row(qa + TILE_BYTES), lds_row(koffs[c] + BN * D * 2), pacc);
+        for (int c = 0; c < (NC > NCV ? NC : NCV); ++c) {
+            if (c < NC) sacc = mfma32(lds_row(aoffs[c] + sb), lds_row(koffs[c]), sacc);
+            if (c < NCV) pacc = mfma32(lds_row(goffs[c] + sb), lds_row(voffs[c]), pacc);
         }
         float pv[16], dv[16];
 #pragma unroll
@@ -301,11 +357,14 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
                 dv[r] = vis ? dv[r] : 0.0f;
             }
         }
-        uint32_t taddr[2][NDB];
+        uint32_t taddr[2][NDB], tgaddr[2][NDBV];
 #pragma unroll
-        for (int rr = 0; rr < 2; ++rr)
+        for (int rr = 0; rr < 2; ++rr) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db) taddr[rr][db] = toffs[rr][db] + sb;
+#pragma unroll
+            for (int db = 0; db < NDBV; ++db) tgaddr[rr][db] = tgoffs[rr][db] + sb;
+        }
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
             const int o = 8 * h2;
@@ -318,19 +377,25 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
                 pl = lo_part(pv + o, pa);
                 dl = lo_part(dv + o, da);
             }
+            // dV block db then dK block db, as far as both exist
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const uint32_t ho = h2 * H2_BYTES;
-                const uint2 g0 = lds_tr(taddr[0][db] + ho + TILE_BYTES);
-                const uint2 g1 = lds_tr(taddr[1][db] + ho + TILE_BYTES);
-                const bf16x8 gfr = __builtin_bit_cast(bf16x8, make_uint4(g0.x, g0.y, g1.x, g1.y));
-                dvacc[db] = mfma32(pa, gfr, dvacc[db]);
-                if constexpr (split) dvacc[db] = mfma32(pl, gfr, dvacc[db]);
-                const uint2 q0 = lds_tr(taddr[0][db] + ho);
-                const uint2 q1 = lds_tr(taddr[1][db] + ho);
-                const bf16x8 qfr = __builtin_bit_cast(bf16x8, make_uint4(q0.x, q0.y, q1.x, q1.y));
-                dkacc[db] = mfma32(da, qfr, dkacc[db]);
-                if constexpr (split) dkacc[db] = mfma32(dl, qfr, dkacc[db]);
+            for (int db = 0; db < (NDB > NDBV ? NDB : NDBV); ++db) {
+                if (db < NDBV) {
+                    const uint32_t ho = h2 * H2V_BYTES;
+                    const uint2 g0 = lds_tr(tgaddr[0][db] + ho);
+                    const uint2 g1 = lds_tr(tgaddr[1][db] + ho);
+                    const bf16x8 gfr = __builtin_bit_cast(bf16x8, make_uint4(g0.x, g0.y, g1.x, g1.y));
+                    dvacc[db] = mfma32(pa, gfr, dvacc[db]);
+                    if constexpr (split) dvacc[db] = mfma32(pl, gfr, dvacc[db]);
+                }
+                if (db < NDB) {
+                    const uint32_t ho = h2 * H2_BYTES;
+                    const uint2 q0 = lds_tr(taddr[0][db] + ho);
+                    const uint2 q1 = lds_tr(taddr[1][db] + ho);
+                    const bf16x8 qfr = __builtin_bit_cast(bf16x8, make_uint4(q0.x, q0.y, q1.x, q1.y));
+                    dkacc[db] = mfma32(da, qfr, dkacc[db]);
+                    if constexpr (split) dkacc[db] = mfma32(dl, qfr, dkacc[db]);
+                }
             }
         }
     };
@@ -352,69 +417,132 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
 
     // the two row halves of key block kw: the rh = 1 wave hands its dK sum to
     // the rh = 0 wave and takes the rh = 0 wave's dV sum, through LDS (free
-    // after the barrier); region e holds 32 keys x D floats (16 KB at d = 128)
+    // after the barrier): 32 keys x DQK floats of dK and 32 x DV of dV per
+    // key block, 32 KB at d = 128.  Accumulator: lane holds column
+    // d = 32*db + l32, register r holds key 32*kw + 8*(r/4) + 4*hl + r%4 of
+    // the tile; rh = 0 writes dK, rh = 1 dV, both scaled by alpha / N (P
+    // carries 1/alpha).
     __syncthreads();
-    float *const xreg = reinterpret_cast<float *>(lds);
-    floatx16 *mine = rh == 0 ? dkacc : dvacc;    // the sum this wave writes out
-    floatx16 *other = rh == 0 ? dvacc : dkacc;   // the sum it hands over
-    {
-        float *xo = xreg + (2 * kw + (1 - rh)) * (32 * D);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) xo[(db * 16 + r) * 64 + lane] = other[db][r];
-    }
-    __syncthreads();
-    {
-        const float *xi = xreg + (2 * kw + rh) * (32 * D);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mine[db][r] += xi[(db * 16 + r) * 64 + lane];
-    }
-
-    // accumulator: lane holds column d = 32*db + l32, register r holds key
-    // 32*kw + 8*(r/4) + 4*hl + r%4 of the tile; rh = 0 holds dK, rh = 1 dV,
-    // both scaled by alpha / N (P carries 1/alpha)
     const float sc = p.out_scale;
-    if (it.nchunk == 1) {
-        void *dst = rh == 0 ? p.dk : p.dv;
-        const int64_t ld = rh == 0 ? p.lddk : p.lddv;
+    if constexpr (DQK == DV) {
+        // region 2 kw holds the dK hand-over, 2 kw + 1 the dV one
+        float *const xr = reinterpret_cast<float *>(lds);
+        floatx16 *mine = rh == 0 ? dkacc : dvacc;   // the sum this wave writes out
+        floatx16 *other = rh == 0 ? dvacc : dkacc;  // the sum it hands over
+        {
+            float *xo = xr + (2 * kw + (1 - rh)) * (32 * DQK);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int j = it.c0 + 32 * kw + 8 * (r >> 2) + 4 * hl + (r & 3);
-                if (j < it.c1) {
-                    const int64_t o = (sd.base + j) * ld + h * D + 32 * db + l32;
-                    if constexpr (OUTF32) reinterpret_cast<float *>(dst)[o] = mine[db][r] * sc;
-                    else reinterpret_cast<__bf16 *>(dst)[o] = (__bf16)(mine[db][r] * sc);
+                for (int r = 0; r < 16; ++r) xo[(db * 16 + r) * 64 + lane] = other[db][r];
+        }
+        __syncthreads();
+        {
+            const float *xi = xr + (2 * kw + rh) * (32 * DQK);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mine[db][r] += xi[(db * 16 + r) * 64 + lane];
+        }
+        if (it.nchunk == 1) {
+            void *dst = rh == 0 ? p.dk : p.dv;
+            const int64_t ld = rh == 0 ? p.lddk : p.lddv;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int j = it.c0 + 32 * kw + 8 * (r >> 2) + 4 * hl + (r & 3);
+                    if (j < it.c1) {
+                        const int64_t o = (sd.base + j) * ld + h * DQK + 32 * db + l32;
+                        if constexpr (OUTF32) reinterpret_cast<float *>(dst)[o] = mine[db][r] * sc;
+                        else reinterpret_cast<__bf16 *>(dst)[o] = (__bf16)(mine[db][r] * sc);
+                    }
+                }
+            }
+        } else {
+            // fp32 partials [key][dK | dV] of this chunk
+            const int slot = p.s.part_base[b] + it.tile * nch + it.chunk;
+            float *part = p.partials + ((int64_t)slot * p.H + h) * BN * DW + rh * DQK;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int jl = 32 * kw + 8 * (r >> 2) + 4 * hl + (r & 3);
+                    part[jl * DW + 32 * db + l32] = mine[db][r];
                 }
             }
         }
+        return;
+    }
+    float *const xreg = reinterpret_cast<float *>(lds) + kw * (32 * DW);
+    float *const xk = xreg, *const xv = xreg + 32 * DQK;
+    if (rh == 0) {
+#pragma unroll
+        for (int db = 0; db < NDBV; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) xv[(db * 16 + r) * 64 + lane] = dvacc[db][r];
     } else {
-        // fp32 partials [key][dK | dV] of this chunk
-        const int slot = p.s.part_base[b] + it.tile * nch + it.chunk;
-        float *part = p.partials + ((int64_t)slot * p.H + h) * BN * (2 * D) + rh * D;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int jl = 32 * kw + 8 * (r >> 2) + 4 * hl + (r & 3);
-                part[jl * (2 * D) + 32 * db + l32] = mine[db][r];
+            for (int r = 0; r < 16; ++r) xk[(db * 16 + r) * 64 + lane] = dkacc[db][r];
+    }
+    __syncthreads();
+    if (rh == 0) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dkacc[db][r] += xk[(db * 16 + r) * 64 + lane];
+    } else {
+#pragma unroll
+        for (int db = 0; db < NDBV; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dvacc[db][r] += xv[(db * 16 + r) * 64 + lane];
+    }
+
+    auto write_out = [&](const floatx16 *acc, auto NB, void *dst, int64_t ld, int width, int pcol)
+        __attribute__((always_inline)) {
+        constexpr int nb = decltype(NB)::value;
+        if (it.nchunk == 1) {
+#pragma unroll
+            for (int db = 0; db < nb; ++db) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int j = it.c0 + 32 * kw + 8 * (r >> 2) + 4 * hl + (r & 3);
+                    if (j < it.c1) {
+                        const int64_t o = (sd.base + j) * ld + h * width + 32 * db + l32;
+                        if constexpr (OUTF32) reinterpret_cast<float *>(dst)[o] = acc[db][r] * sc;
+                        else reinterpret_cast<__bf16 *>(dst)[o] = (__bf16)(acc[db][r] * sc);
+                    }
+                }
+            }
+        } else {
+            // fp32 partials [key][dK | dV] of this chunk
+            const int slot = p.s.part_base[b] + it.tile * nch + it.chunk;
+            float *part = p.partials + ((int64_t)slot * p.H + h) * BN * DW + pcol;
+#pragma unroll
+            for (int db = 0; db < nb; ++db) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int jl = 32 * kw + 8 * (r >> 2) + 4 * hl + (r & 3);
+                    part[jl * DW + 32 * db + l32] = acc[db][r];
+                }
             }
         }
-    }
+    };
+    if (rh == 0) write_out(dkacc, std::integral_constant<int, NDB>{}, p.dk, p.lddk, DQK, 0);
+    else write_out(dvacc, std::integral_constant<int, NDBV>{}, p.dv, p.lddv, DV, DQK);
 }
 
 // Sum the chunk partials of each split prefix key tile in chunk order.  Block
 // (item, slab) handles 1024 consecutive values of the [BN][2D] tile.
 constexpr int RED_SLAB = 1024;
 
-template <int D, bool OUTF32>
+template <int DQK, int DV, bool OUTF32>
 __global__ __launch_bounds__(256) void sla_bwd_reduce_kernel(AttnParams p)
 {
-    constexpr int BN = BWD_BN, W = 2 * D, SLABS = BN * W / RED_SLAB;
+    constexpr int BN = BWD_BN, W = DQK + DV, SLABS = BN * W / RED_SLAB;
+    static_assert((BN * W) % RED_SLAB == 0 && DQK % 4 == 0, "whole slabs; no float4 spans dK | dV");
     const int nrec = p.s.red_base[p.B];
     const int item = blockIdx.x / SLABS, slab = blockIdx.x % SLABS;
     if (item >= nrec * p.H) return;
@@ -448,9 +576,9 @@ __global__ __launch_bounds__(256) void sla_bwd_reduce_kernel(AttnParams p)
         acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
     const float sc = p.out_scale;
-    const int64_t off = col < D ? (sd.base + c0 + jl) * p.lddk + h * D + col
-                                : (sd.base + c0 + jl) * p.lddv + h * D + (col - D);
-    void *base = col < D ? p.dk : p.dv;
+    const int64_t off = col < DQK ? (sd.base + c0 + jl) * p.lddk + h * DQK + col
+                                  : (sd.base + c0 + jl) * p.lddv + h * DV + (col - DQK);
+    void *base = col < DQK ? p.dk : p.dv;
     if constexpr (OUTF32) {
         *reinterpret_cast<float4 *>(reinterpret_cast<float *>(base) + off) =
             make_float4(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
@@ -460,27 +588,19 @@ __global__ __launch_bounds__(256) void sla_bwd_reduce_kernel(AttnParams p)
     }
 }
 
-template <int D, bool OUTF32>
-static hipError_t launch_dkdv_d(const AttnParams &p, hipStream_t st)
-{
-    hipLaunchKernelGGL((sla_bwd_dkdv_bf16_kernel<D, OUTF32>), dim3(p.grid_bwd),
-                       dim3(DKDV_THREADS), 0, st, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.grid_red == 0) return e;
-    hipLaunchKernelGGL((sla_bwd_reduce_kernel<D, OUTF32>),
-                       dim3(p.grid_red * (BWD_BN * 2 * D / RED_SLAB)), dim3(256), 0, st, p);
-    return hipGetLastError();
-}
-
 template <bool OUTF32>
 static hipError_t launch_dkdv_o(const AttnParams &p, hipStream_t st)
 {
-    switch (p.d) {
-    case 32: return launch_dkdv_d<32, OUTF32>(p, st);
-    case 64: return launch_dkdv_d<64, OUTF32>(p, st);
-    case 128: return launch_dkdv_d<128, OUTF32>(p, st);
-    default: return hipErrorInvalidValue;
-    }
+    return with_head_dims(p, [&](auto QK, auto V) {
+        constexpr int DQK = decltype(QK)::value, DV = decltype(V)::value;
+        hipLaunchKernelGGL((sla_bwd_dkdv_bf16_kernel<DQK, DV, OUTF32>), dim3(p.grid_bwd),
+                           dim3(DKDV_THREADS), 0, st, p);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || p.grid_red == 0) return e;
+        hipLaunchKernelGGL((sla_bwd_reduce_kernel<DQK, DV, OUTF32>),
+                           dim3(p.grid_red * (BWD_BN * (DQK + DV) / RED_SLAB)), dim3(256), 0, st, p);
+        return hipGetLastError();
+    });
 }
 
 hipError_t launch_bwd_dkdv_bf16(const AttnParams &p, hipStream_t st)

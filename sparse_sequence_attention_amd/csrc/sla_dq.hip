@@ -44,19 +44,21 @@ __device__ __forceinline__ int qswz(int r)
     return 4 * (u % Q4) + (u / Q4) % 4;
 }
 
-template <int D, bool OUTF32>
+// DQK: the Q / K (and dQ) head width, DV: the V and dO width.
+template <int DQK, int DV, bool OUTF32>
 __global__ __launch_bounds__(256, 2) void sla_bwd_dq_kernel(AttnParams p)
 {
     constexpr int BM = FWD_BM, BN = FWD_BN;
     constexpr int NT = 256;
-    constexpr int NC = D / 16;   // 16-wide contraction chunks of Q.K and dO.V
-    constexpr int NDB = D / 32;  // 32-wide output blocks
-    constexpr int CPR = D / 8;   // 16-byte chunks per row
-    constexpr int TCH = BN * CPR;   // chunks of one 64-key K (or V) tile
-    constexpr int KPT = TCH / NT;   // DMA loads per thread and tile
+    constexpr int NC = DQK / 16, NCV = DV / 16;  // 16-wide contraction chunks of Q.K, dO.V
+    constexpr int NDB = DQK / 32;                // 32-wide output blocks
+    constexpr int CPR = DQK / 8, CPRV = DV / 8;     // 16-byte chunks per K / V row
+    constexpr int TCH = BN * CPR, TCHV = BN * CPRV;  // chunks of one 64-key K / V tile
+    constexpr int KPT = TCH / NT, KPTV = TCHV / NT;  // DMA loads per thread and tile
     static_assert(BN == 64 && BM == 128, "64-key steps over 128-row tiles");
-    static_assert(TCH % NT == 0 && 2 * KPT <= 8, "whole DMA rounds, at most 8 per stage");
-    __shared__ __align__(16) uint16_t st0[2 * BN * D], st1[2 * BN * D];
+    static_assert(TCH % NT == 0 && TCHV % NT == 0 && KPT + KPTV <= 8,
+                  "whole DMA rounds, at most 8 per stage");
+    __shared__ __align__(16) uint16_t st0[BN * (DQK + DV)], st1[BN * (DQK + DV)];
 
     const int nrec = p.s.fwd_base[p.B];
     const int item = xcd_remap(blockIdx.x, nrec * p.H);
@@ -74,19 +76,19 @@ __global__ __launch_bounds__(256, 2) void sla_bwd_dq_kernel(AttnParams p)
     const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
     const int l32 = lane & 31, hl = lane >> 5;
 
-    const uint16_t *qg = reinterpret_cast<const uint16_t *>(p.q) + sd.base * p.ldq + h * D;
-    const uint16_t *kg = reinterpret_cast<const uint16_t *>(p.k) + sd.base * p.ldk + h * D;
-    const uint16_t *vg = reinterpret_cast<const uint16_t *>(p.v) + sd.base * p.ldv + h * D;
-    const uint16_t *gg = reinterpret_cast<const uint16_t *>(p.dout) + sd.base * p.lddo + h * D;
+    const uint16_t *qg = reinterpret_cast<const uint16_t *>(p.q) + sd.base * p.ldq + h * DQK;
+    const uint16_t *kg = reinterpret_cast<const uint16_t *>(p.k) + sd.base * p.ldk + h * DQK;
+    const uint16_t *vg = reinterpret_cast<const uint16_t *>(p.v) + sd.base * p.ldv + h * DV;
+    const uint16_t *gg = reinterpret_cast<const uint16_t *>(p.dout) + sd.base * p.lddo + h * DV;
 
     // Q^T and dO^T operands: lane holds row qi, d-slots 16c + 8*hl .. +8; rows
     // at or past r1 read as zero (then g = 0 and dS = 0)
     const int qi = r0 + 32 * wv + l32;
-    bf16x8 qb[NC], gb[NC];
+    bf16x8 qb[NC], gb[NCV];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        qb[c] = as_bf16x8(ld16_row(qg, p.ldq, qi, r1, 16 * c + 8 * hl));
-        gb[c] = as_bf16x8(ld16_row(gg, p.lddo, qi, r1, 16 * c + 8 * hl));
+    for (int c = 0; c < (NC > NCV ? NC : NCV); ++c) {
+        if (c < NC) qb[c] = as_bf16x8(ld16_row(qg, p.ldq, qi, r1, 16 * c + 8 * hl));
+        if (c < NCV) gb[c] = as_bf16x8(ld16_row(gg, p.lddo, qi, r1, 16 * c + 8 * hl));
     }
 
     const TileCursor cur(kr, BN);
@@ -100,10 +102,12 @@ __global__ __launch_bounds__(256, 2) void sla_bwd_dq_kernel(AttnParams p)
         if constexpr (decltype(S)::value == 0) return st0;
         else return st1;
     };
-    // DMA of the K and V rows of key tile t into a stage: chunk P = i*NT + tid
-    // of a tile is physical chunk P % CPR of key row P / CPR and holds its
-    // logical chunk (P % CPR) ^ qswz(row); keys at or past L read key L - 1
-    // (such tiles are never "full", and the mask removes them)
+    // DMA of the K and V rows of key tile t into a stage ([K | V], the V rows
+    // after the BN * DQK elements of K): chunk P = i*NT + tid of a tile is
+    // physical chunk P % CPR of key row P / CPR and holds its logical chunk
+    // (P % CPR) ^ qswz(row) (CPR, qswz of the tile's own width); keys at or
+    // past L read key L - 1 (such tiles are never "full", and the mask
+    // removes them)
     const uint32_t ldk_b = (uint32_t)p.ldk * 2u, ldv_b = (uint32_t)p.ldv * 2u;
     auto issue = [&](int t, auto S) {
         const int c0 = uniform(cur.start(t, BN));
@@ -112,13 +116,20 @@ __global__ __launch_bounds__(256, 2) void sla_bwd_dq_kernel(AttnParams p)
         const char *vrow = reinterpret_cast<const char *>(vg + (int64_t)c0 * p.ldv);
         uint16_t *sb = stage(S);
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
+        for (int i = 0; i < (KPT > KPTV ? KPT : KPTV); ++i) {
             const int P = i * NT + tid;
-            const int prow = P / CPR;
-            const uint32_t row = (uint32_t)imin(prow, last);
-            const uint32_t c = (uint32_t)((P % CPR) ^ qswz<D>(prow));
-            gl_lds16(krow + (row * ldk_b + 16u * c), sb + (i * NT + wv * 64) * 8);
-            gl_lds16(vrow + (row * ldv_b + 16u * c), sb + (TCH + i * NT + wv * 64) * 8);
+            if (i < KPT) {
+                const int prow = P / CPR;
+                const uint32_t row = (uint32_t)imin(prow, last);
+                const uint32_t c = (uint32_t)((P % CPR) ^ qswz<DQK>(prow));
+                gl_lds16(krow + (row * ldk_b + 16u * c), sb + (i * NT + wv * 64) * 8);
+            }
+            if (i < KPTV) {
+                const int prow = P / CPRV;
+                const uint32_t row = (uint32_t)imin(prow, last);
+                const uint32_t c = (uint32_t)((P % CPRV) ^ qswz<DV>(prow));
+                gl_lds16(vrow + (row * ldv_b + 16u * c), sb + (BN * DQK + (i * NT + wv * 64) * 8));
+            }
         }
     };
 
@@ -128,14 +139,18 @@ __global__ __launch_bounds__(256, 2) void sla_bwd_dq_kernel(AttnParams p)
     // d-columns 32*db + 16*(q%2) + 4*(j%4); the keys come in the order in
     // which the S^T accumulator hands them to dS^T (8*(r/4) + 4*hl + r%4).
     const int q4 = lane >> 4, j16 = lane & 15;
-    auto r_off = [&](int kb, int c) {
+    auto r_off = [&](int kb, int c) {  // K rows
         const int r = 32 * kb + l32;
-        return r * D + 8 * ((2 * c + hl) ^ qswz<D>(r));
+        return r * DQK + 8 * ((2 * c + hl) ^ qswz<DQK>(r));
+    };
+    auto rv_off = [&](int kb, int c) {  // V rows
+        const int r = 32 * kb + l32;
+        return r * DV + 8 * ((2 * c + hl) ^ qswz<DV>(r));
     };
     auto t_off = [&](int kb, int h2, int rr, int db) {
         const int row = 32 * kb + 16 * h2 + 8 * rr + 4 * (q4 >> 1) + (j16 >> 2);
         const int col = 32 * db + 16 * (q4 & 1) + 4 * (j16 & 3);
-        return row * D + 8 * ((col >> 3) ^ qswz<D>(row)) + (col & 7);
+        return row * DQK + 8 * ((col >> 3) ^ qswz<DQK>(row)) + (col & 7);
     };
 
     const float nal2e = p.neg_alpha_log2e, alpha = p.alpha;
@@ -144,7 +159,7 @@ __global__ __launch_bounds__(256, 2) void sla_bwd_dq_kernel(AttnParams p)
         constexpr int sidx = decltype(S)::value;
         barrier_lds();  // publishes stage S, frees the other (read by step t - 1)
         issue(imin(t + 1, ntiles - 1), std::integral_constant<int, 1 - sidx>{});
-        const uint16_t *sk = stage(S), *sv = stage(S) + BN * D;
+        const uint16_t *sk = stage(S), *sv = stage(S) + BN * DQK;
         const int c0 = uniform(cur.start(t, BN));
         // mask: as the forward (workgroup-uniform tests; interval masks for
         // history tiles wholly inside or outside the global prefix)
@@ -157,12 +172,26 @@ __global__ __launch_bounds__(256, 2) void sla_bwd_dq_kernel(AttnParams p)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             floatx16 sacc = zero16(), pacc = zero16();
+            if constexpr (NC == NCV) {
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const bf16x8 ak = *reinterpret_cast<const bf16x8 *>(sk + r_off(kb, c));
-                sacc = mfma32(ak, qb[c], sacc);
-                const bf16x8 av = *reinterpret_cast<const bf16x8 *>(sv + r_off(kb, c));
-                pacc = mfma32(av, gb[c], pacc);
+                for (int c = 0; c < NC; ++c) {
+                    const bf16x8 ak = *reinterpret_cast<const bf16x8 *>(sk + r_off(kb, c));
+                    sacc = mfma32(ak, qb[c], sacc);
+                    const bf16x8 av = *reinterpret_cast<const bf16x8 *>(sv + r_off(kb, c));
+                    pacc = mfma32(av, gb[c], pacc);
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < (NC > NCV ? NC : NCV); ++c) {
+                    if (c < NC) {
+                        const bf16x8 ak = *reinterpret_cast<const bf16x8 *>(sk + r_off(kb, c));
+                        sacc = mfma32(ak, qb[c], sacc);
+                    }
+                    if (c < NCV) {
+                        const bf16x8 av = *reinterpret_cast<const bf16x8 *>(sv + rv_off(kb, c));
+                        pacc = mfma32(av, gb[c], pacc);
+                    }
+                }
             }
             // dS = g * (sigma + a * (alpha - alpha * sigma)), a = s * sigma:
             // 1 + t (1 - sigma) = 1 + alpha a (1 - sigma) / sigma, times sigma.
@@ -234,7 +263,7 @@ __global__ __launch_bounds__(256, 2) void sla_bwd_dq_kernel(AttnParams p)
             for (int g = 0; g < 4; ++g) {
                 const float o0 = dqacc[db][4 * g] * sc, o1 = dqacc[db][4 * g + 1] * sc;
                 const float o2 = dqacc[db][4 * g + 2] * sc, o3 = dqacc[db][4 * g + 3] * sc;
-                const int col = h * D + 32 * db + 8 * g + 4 * hl;
+                const int col = h * DQK + 32 * db + 8 * g + 4 * hl;
                 if constexpr (OUTF32) {
                     float *orow = reinterpret_cast<float *>(p.dq) + row * p.lddq;
                     *reinterpret_cast<float4 *>(orow + col) = make_float4(o0, o1, o2, o3);
@@ -250,14 +279,11 @@ __global__ __launch_bounds__(256, 2) void sla_bwd_dq_kernel(AttnParams p)
 template <bool OUTF32>
 static hipError_t launch_dq_o(const AttnParams &p, hipStream_t st)
 {
-    dim3 grid(p.grid_fwd), block(256);
-    switch (p.d) {
-    case 32: hipLaunchKernelGGL((sla_bwd_dq_kernel<32, OUTF32>), grid, block, 0, st, p); break;
-    case 64: hipLaunchKernelGGL((sla_bwd_dq_kernel<64, OUTF32>), grid, block, 0, st, p); break;
-    case 128: hipLaunchKernelGGL((sla_bwd_dq_kernel<128, OUTF32>), grid, block, 0, st, p); break;
-    default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    return with_head_dims(p, [&](auto QK, auto V) {
+        hipLaunchKernelGGL((sla_bwd_dq_kernel<decltype(QK)::value, decltype(V)::value, OUTF32>),
+                           dim3(p.grid_fwd), dim3(256), 0, st, p);
+        return hipGetLastError();
+    });
 }
 
 hipError_t launch_bwd_dq_bf16(const AttnParams &p, hipStream_t st)

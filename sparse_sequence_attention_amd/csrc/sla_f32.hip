@@ -50,12 +50,13 @@ __device__ __forceinline__ void stage_rows_f32(float *lds, const float *g, int64
     }
 }
 
-template <int D>
+// DQK: the Q / K head width, DV: the V width (DQ, DW: their shares per thread)
+template <int DQK, int DV>
 __global__ __launch_bounds__(FWD_BM *F32_TPR) void sla_fwd_f32_kernel(AttnParams p)
 {
-    constexpr int BM = FWD_BM, BN = FWD_BN, DQ = D / F32_TPR;
-    __shared__ __align__(16) float sk[BN * D];
-    __shared__ __align__(16) float sv[BN * D];
+    constexpr int BM = FWD_BM, BN = FWD_BN, DQ = DQK / F32_TPR, DW = DV / F32_TPR;
+    __shared__ __align__(16) float sk[BN * DQK];
+    __shared__ __align__(16) float sv[BN * DV];
     const int nrec = p.s.fwd_base[p.B];
     const int item = xcd_remap(blockIdx.x, nrec * p.H);
     if (item < 0) return;
@@ -66,52 +67,51 @@ __global__ __launch_bounds__(FWD_BM *F32_TPR) void sla_fwd_f32_kernel(AttnParams
     row_tile(sd.L, sd.U, BM, rec - p.s.fwd_base[b], r0, r1);
     const TileCursor cur(fwd_key_ranges(sd.L, sd.U, p.k1, p.k2e, r0, r1, BN), BN);
 
-    const float *qg = reinterpret_cast<const float *>(p.q) + sd.base * p.ldq + h * D;
-    const float *kg = reinterpret_cast<const float *>(p.k) + sd.base * p.ldk + h * D;
-    const float *vg = reinterpret_cast<const float *>(p.v) + sd.base * p.ldv + h * D;
+    const float *qg = reinterpret_cast<const float *>(p.q) + sd.base * p.ldq + h * DQK;
+    const float *kg = reinterpret_cast<const float *>(p.k) + sd.base * p.ldk + h * DQK;
+    const float *vg = reinterpret_cast<const float *>(p.v) + sd.base * p.ldv + h * DV;
     const int row = threadIdx.x / F32_TPR, qt = threadIdx.x % F32_TPR;
     const int i = r0 + row;
-    float q[DQ], acc[DQ];
+    float q[DQ], acc[DW];
 #pragma unroll
-    for (int c = 0; c < DQ; ++c) {
-        q[c] = i < r1 ? qg[(int64_t)i * p.ldq + qt * DQ + c] : 0.0f;
-        acc[c] = 0.0f;
-    }
+    for (int c = 0; c < DQ; ++c) q[c] = i < r1 ? qg[(int64_t)i * p.ldq + qt * DQ + c] : 0.0f;
+#pragma unroll
+    for (int c = 0; c < DW; ++c) acc[c] = 0.0f;
     for (int t = 0; t < cur.total; ++t) {
         const int c0 = cur.start(t, BN);
         __syncthreads();
-        stage_rows_f32<D>(sk, kg, p.ldk, c0, BN, sd.L);
-        stage_rows_f32<D>(sv, vg, p.ldv, c0, BN, sd.L);
+        stage_rows_f32<DQK>(sk, kg, p.ldk, c0, BN, sd.L);
+        stage_rows_f32<DV>(sv, vg, p.ldv, c0, BN, sd.L);
         __syncthreads();
-        float part[DQ];  // per-tile partial sums keep the rounding error growth short
+        float part[DW];  // per-tile partial sums keep the rounding error growth short
 #pragma unroll
-        for (int c = 0; c < DQ; ++c) part[c] = 0.0f;
+        for (int c = 0; c < DW; ++c) part[c] = 0.0f;
         for (int jj = 0; jj < BN; ++jj) {
             float s = 0.0f;
 #pragma unroll
-            for (int c = 0; c < DQ; ++c) s += q[c] * sk[jj * D + qt * DQ + c];
+            for (int c = 0; c < DQ; ++c) s += q[c] * sk[jj * DQK + qt * DQ + c];
             s = quad_sum(s);
             const bool vis = i < r1 && c0 + jj < sd.L && visible(i, c0 + jj, sd.U, p.k1, p.k2e);
             const float a = vis ? silu_f32(p.alpha * s) : 0.0f;
 #pragma unroll
-            for (int c = 0; c < DQ; ++c) part[c] += a * sv[jj * D + qt * DQ + c];
+            for (int c = 0; c < DW; ++c) part[c] += a * sv[jj * DV + qt * DW + c];
         }
 #pragma unroll
-        for (int c = 0; c < DQ; ++c) acc[c] += part[c];
+        for (int c = 0; c < DW; ++c) acc[c] += part[c];
     }
     if (i < r1) {
-        float *o = reinterpret_cast<float *>(p.o) + (sd.base + i) * p.ldo + h * D + qt * DQ;
+        float *o = reinterpret_cast<float *>(p.o) + (sd.base + i) * p.ldo + h * DV + qt * DW;
 #pragma unroll
-        for (int c = 0; c < DQ; ++c) o[c] = acc[c] * p.inv_n;
+        for (int c = 0; c < DW; ++c) o[c] = acc[c] * p.inv_n;
     }
 }
 
-template <int D>
+template <int DQK, int DV>
 __global__ __launch_bounds__(FWD_BM *F32_TPR) void sla_bwd_dq_f32_kernel(AttnParams p)
 {
-    constexpr int BM = FWD_BM, BN = FWD_BN, DQ = D / F32_TPR;
-    __shared__ __align__(16) float sk[BN * D];
-    __shared__ __align__(16) float sv[BN * D];
+    constexpr int BM = FWD_BM, BN = FWD_BN, DQ = DQK / F32_TPR, DW = DV / F32_TPR;
+    __shared__ __align__(16) float sk[BN * DQK];
+    __shared__ __align__(16) float sv[BN * DV];
     const int nrec = p.s.fwd_base[p.B];
     const int item = xcd_remap(blockIdx.x, nrec * p.H);
     if (item < 0) return;
@@ -122,24 +122,25 @@ __global__ __launch_bounds__(FWD_BM *F32_TPR) void sla_bwd_dq_f32_kernel(AttnPar
     row_tile(sd.L, sd.U, BM, rec - p.s.fwd_base[b], r0, r1);
     const TileCursor cur(fwd_key_ranges(sd.L, sd.U, p.k1, p.k2e, r0, r1, BN), BN);
 
-    const float *qg = reinterpret_cast<const float *>(p.q) + sd.base * p.ldq + h * D;
-    const float *kg = reinterpret_cast<const float *>(p.k) + sd.base * p.ldk + h * D;
-    const float *vg = reinterpret_cast<const float *>(p.v) + sd.base * p.ldv + h * D;
-    const float *gg = reinterpret_cast<const float *>(p.dout) + sd.base * p.lddo + h * D;
+    const float *qg = reinterpret_cast<const float *>(p.q) + sd.base * p.ldq + h * DQK;
+    const float *kg = reinterpret_cast<const float *>(p.k) + sd.base * p.ldk + h * DQK;
+    const float *vg = reinterpret_cast<const float *>(p.v) + sd.base * p.ldv + h * DV;
+    const float *gg = reinterpret_cast<const float *>(p.dout) + sd.base * p.lddo + h * DV;
     const int row = threadIdx.x / F32_TPR, qt = threadIdx.x % F32_TPR;
     const int i = r0 + row;
-    float q[DQ], go[DQ], acc[DQ];
+    float q[DQ], go[DW], acc[DQ];
 #pragma unroll
     for (int c = 0; c < DQ; ++c) {
         q[c] = i < r1 ? qg[(int64_t)i * p.ldq + qt * DQ + c] : 0.0f;
-        go[c] = i < r1 ? gg[(int64_t)i * p.lddo + qt * DQ + c] : 0.0f;
         acc[c] = 0.0f;
     }
+#pragma unroll
+    for (int c = 0; c < DW; ++c) go[c] = i < r1 ? gg[(int64_t)i * p.lddo + qt * DW + c] : 0.0f;
     for (int t = 0; t < cur.total; ++t) {
         const int c0 = cur.start(t, BN);
         __syncthreads();
-        stage_rows_f32<D>(sk, kg, p.ldk, c0, BN, sd.L);
-        stage_rows_f32<D>(sv, vg, p.ldv, c0, BN, sd.L);
+        stage_rows_f32<DQK>(sk, kg, p.ldk, c0, BN, sd.L);
+        stage_rows_f32<DV>(sv, vg, p.ldv, c0, BN, sd.L);
         __syncthreads();
         float part[DQ];
 #pragma unroll
@@ -147,33 +148,33 @@ __global__ __launch_bounds__(FWD_BM *F32_TPR) void sla_bwd_dq_f32_kernel(AttnPar
         for (int jj = 0; jj < BN; ++jj) {
             float s = 0.0f, g = 0.0f;
 #pragma unroll
-            for (int c = 0; c < DQ; ++c) {
-                s += q[c] * sk[jj * D + qt * DQ + c];
-                g += go[c] * sv[jj * D + qt * DQ + c];
-            }
+            for (int c = 0; c < DQ; ++c) s += q[c] * sk[jj * DQK + qt * DQ + c];
+#pragma unroll
+            for (int c = 0; c < DW; ++c) g += go[c] * sv[jj * DV + qt * DW + c];
             s = quad_sum(s);
             g = quad_sum(g);
             const bool vis = i < r1 && c0 + jj < sd.L && visible(i, c0 + jj, sd.U, p.k1, p.k2e);
             const float ds = vis ? g * dsilu_f32(p.alpha * s) : 0.0f;
 #pragma unroll
-            for (int c = 0; c < DQ; ++c) part[c] += ds * sk[jj * D + qt * DQ + c];
+            for (int c = 0; c < DQ; ++c) part[c] += ds * sk[jj * DQK + qt * DQ + c];
         }
 #pragma unroll
         for (int c = 0; c < DQ; ++c) acc[c] += part[c];
     }
     if (i < r1) {
-        float *o = reinterpret_cast<float *>(p.dq) + (sd.base + i) * p.lddq + h * D + qt * DQ;
+        float *o = reinterpret_cast<float *>(p.dq) + (sd.base + i) * p.lddq + h * DQK + qt * DQ;
 #pragma unroll
         for (int c = 0; c < DQ; ++c) o[c] = acc[c] * p.out_scale;
     }
 }
 
-template <int D>
+template <int DQK, int DV>
 __global__ __launch_bounds__(BWD_BN *F32_TPR) void sla_bwd_dkdv_f32_kernel(AttnParams p)
 {
-    constexpr int BN = BWD_BN, BM = BWD_BM, DQ = D / F32_TPR;
-    __shared__ __align__(16) float sq[BM * D];
-    __shared__ __align__(16) float sg_[BM * D];
+    constexpr int BN = BWD_BN, BM = BWD_BM, DQ = DQK / F32_TPR, DW = DV / F32_TPR;
+    constexpr int W = DQK + DV;  // a partial row: [dK | dV]
+    __shared__ __align__(16) float sq[BM * DQK];
+    __shared__ __align__(16) float sg_[BM * DV];
     const int nrec = p.s.bwd_base[p.B];
     const int item = xcd_remap(blockIdx.x, nrec * p.H);
     if (item < 0) return;
@@ -184,19 +185,23 @@ __global__ __launch_bounds__(BWD_BN *F32_TPR) void sla_bwd_dkdv_f32_kernel(AttnP
     bwd_items(sd.L, sd.U, p.k2e, BN, BM, np, nch);
     const BwdItem it = bwd_item(sd.L, sd.U, p.k1, p.k2e, BN, BM, rec - p.s.bwd_base[b], np, nch);
 
-    const float *qg = reinterpret_cast<const float *>(p.q) + sd.base * p.ldq + h * D;
-    const float *kg = reinterpret_cast<const float *>(p.k) + sd.base * p.ldk + h * D;
-    const float *vg = reinterpret_cast<const float *>(p.v) + sd.base * p.ldv + h * D;
-    const float *gg = reinterpret_cast<const float *>(p.dout) + sd.base * p.lddo + h * D;
+    const float *qg = reinterpret_cast<const float *>(p.q) + sd.base * p.ldq + h * DQK;
+    const float *kg = reinterpret_cast<const float *>(p.k) + sd.base * p.ldk + h * DQK;
+    const float *vg = reinterpret_cast<const float *>(p.v) + sd.base * p.ldv + h * DV;
+    const float *gg = reinterpret_cast<const float *>(p.dout) + sd.base * p.lddo + h * DV;
     const int kl = threadIdx.x / F32_TPR, qt = threadIdx.x % F32_TPR;
     const int j = it.c0 + kl;
     const bool jok = j < it.c1;
-    float kr[DQ], vr[DQ], dk[DQ], dv[DQ];
+    float kr[DQ], vr[DW], dk[DQ], dv[DW];
 #pragma unroll
     for (int c = 0; c < DQ; ++c) {
         kr[c] = jok ? kg[(int64_t)j * p.ldk + qt * DQ + c] : 0.0f;
-        vr[c] = jok ? vg[(int64_t)j * p.ldv + qt * DQ + c] : 0.0f;
-        dk[c] = dv[c] = 0.0f;
+        dk[c] = 0.0f;
+    }
+#pragma unroll
+    for (int c = 0; c < DW; ++c) {
+        vr[c] = jok ? vg[(int64_t)j * p.ldv + qt * DW + c] : 0.0f;
+        dv[c] = 0.0f;
     }
     int h_first = 0, nh = 0, t_first = 0, nt = 0;
     if (it.ha < it.hb) {
@@ -217,19 +222,20 @@ __global__ __launch_bounds__(BWD_BN *F32_TPR) void sla_bwd_dkdv_f32_kernel(AttnP
             m1 = imin(m0 + BM, sd.L);
         }
         __syncthreads();
-        stage_rows_f32<D>(sq, qg, p.ldq, m0, BM, m1);
-        stage_rows_f32<D>(sg_, gg, p.lddo, m0, BM, m1);
+        stage_rows_f32<DQK>(sq, qg, p.ldq, m0, BM, m1);
+        stage_rows_f32<DV>(sg_, gg, p.lddo, m0, BM, m1);
         __syncthreads();
-        float pk[DQ], pv[DQ];
+        float pk[DQ], pv[DW];
 #pragma unroll
-        for (int c = 0; c < DQ; ++c) pk[c] = pv[c] = 0.0f;
+        for (int c = 0; c < DQ; ++c) pk[c] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < DW; ++c) pv[c] = 0.0f;
         for (int ii = 0; ii < BM; ++ii) {
             float sv = 0.0f, g = 0.0f;
 #pragma unroll
-            for (int c = 0; c < DQ; ++c) {
-                sv += sq[ii * D + qt * DQ + c] * kr[c];
-                g += sg_[ii * D + qt * DQ + c] * vr[c];
-            }
+            for (int c = 0; c < DQ; ++c) sv += sq[ii * DQK + qt * DQ + c] * kr[c];
+#pragma unroll
+            for (int c = 0; c < DW; ++c) g += sg_[ii * DV + qt * DW + c] * vr[c];
             sv = quad_sum(sv);
             g = quad_sum(g);
             const int i = m0 + ii;
@@ -238,44 +244,40 @@ __global__ __launch_bounds__(BWD_BN *F32_TPR) void sla_bwd_dkdv_f32_kernel(AttnP
             const float a = vis ? sv / (1.0f + expf(-tt)) : 0.0f;  // SiLU(alpha s) / alpha
             const float ds = vis ? g * dsilu_f32(tt) : 0.0f;
 #pragma unroll
-            for (int c = 0; c < DQ; ++c) {
-                pv[c] += a * sg_[ii * D + qt * DQ + c];
-                pk[c] += ds * sq[ii * D + qt * DQ + c];
-            }
+            for (int c = 0; c < DW; ++c) pv[c] += a * sg_[ii * DV + qt * DW + c];
+#pragma unroll
+            for (int c = 0; c < DQ; ++c) pk[c] += ds * sq[ii * DQK + qt * DQ + c];
         }
 #pragma unroll
-        for (int c = 0; c < DQ; ++c) {
-            dk[c] += pk[c];
-            dv[c] += pv[c];
-        }
+        for (int c = 0; c < DQ; ++c) dk[c] += pk[c];
+#pragma unroll
+        for (int c = 0; c < DW; ++c) dv[c] += pv[c];
     }
     if (it.nchunk == 1) {
         if (jok) {
-            float *ok = reinterpret_cast<float *>(p.dk) + (sd.base + j) * p.lddk + h * D + qt * DQ;
-            float *ov = reinterpret_cast<float *>(p.dv) + (sd.base + j) * p.lddv + h * D + qt * DQ;
+            float *ok = reinterpret_cast<float *>(p.dk) + (sd.base + j) * p.lddk + h * DQK + qt * DQ;
+            float *ov = reinterpret_cast<float *>(p.dv) + (sd.base + j) * p.lddv + h * DV + qt * DW;
 #pragma unroll
-            for (int c = 0; c < DQ; ++c) {
-                ok[c] = dk[c] * p.out_scale;
-                ov[c] = dv[c] * p.out_scale;
-            }
+            for (int c = 0; c < DQ; ++c) ok[c] = dk[c] * p.out_scale;
+#pragma unroll
+            for (int c = 0; c < DW; ++c) ov[c] = dv[c] * p.out_scale;
         }
     } else {
         const int slot = p.s.part_base[b] + it.tile * nch + it.chunk;
-        float *part = p.partials + ((int64_t)slot * p.H + h) * BN * (2 * D) + kl * (2 * D);
+        float *part = p.partials + ((int64_t)slot * p.H + h) * BN * W + kl * W;
 #pragma unroll
-        for (int c = 0; c < DQ; ++c) {
-            part[qt * DQ + c] = dk[c];
-            part[D + qt * DQ + c] = dv[c];
-        }
+        for (int c = 0; c < DQ; ++c) part[qt * DQ + c] = dk[c];
+#pragma unroll
+        for (int c = 0; c < DW; ++c) part[DQK + qt * DW + c] = dv[c];
     }
 }
 
 // fp32 reduce of split prefix key tiles, in chunk order; dK and dV partials
 // both take the alpha/N scale.
-template <int D>
+template <int DQK, int DV>
 __global__ __launch_bounds__(256) void sla_bwd_reduce_f32_kernel(AttnParams p)
 {
-    constexpr int BN = BWD_BN, W = 2 * D;
+    constexpr int BN = BWD_BN, W = DQK + DV;
     const int nrec = p.s.red_base[p.B];
     const int item = blockIdx.x;
     if (item >= nrec * p.H) return;
@@ -286,61 +288,48 @@ __global__ __launch_bounds__(256) void sla_bwd_reduce_f32_kernel(AttnParams p)
     const int nch = p.s.nch[b];
     const int slot0 = p.s.part_base[b] + tile * nch;
     const int c0 = tile * BN, c1 = imin(c0 + BN, sd.L);
-    float *dkg = reinterpret_cast<float *>(p.dk) + sd.base * p.lddk + h * D;
-    float *dvg = reinterpret_cast<float *>(p.dv) + sd.base * p.lddv + h * D;
+    float *dkg = reinterpret_cast<float *>(p.dk) + sd.base * p.lddk + h * DQK;
+    float *dvg = reinterpret_cast<float *>(p.dv) + sd.base * p.lddv + h * DV;
     for (int e = threadIdx.x; e < BN * W; e += blockDim.x) {
         const int jl = e / W, col = e % W;
         if (c0 + jl >= c1) continue;
         float acc = 0.0f;
         for (int c = 0; c < nch; ++c) acc += p.partials[((int64_t)(slot0 + c) * p.H + h) * BN * W + e];
-        if (col < D) dkg[(int64_t)(c0 + jl) * p.lddk + col] = acc * p.out_scale;
-        else dvg[(int64_t)(c0 + jl) * p.lddv + (col - D)] = acc * p.out_scale;
+        if (col < DQK) dkg[(int64_t)(c0 + jl) * p.lddk + col] = acc * p.out_scale;
+        else dvg[(int64_t)(c0 + jl) * p.lddv + (col - DQK)] = acc * p.out_scale;
     }
 }
 
 hipError_t launch_fwd_f32(const AttnParams &p, hipStream_t st)
 {
-    dim3 grid(p.grid_fwd), block(FWD_BM * F32_TPR);
-    switch (p.d) {
-    case 32: hipLaunchKernelGGL(sla_fwd_f32_kernel<32>, grid, block, 0, st, p); break;
-    case 64: hipLaunchKernelGGL(sla_fwd_f32_kernel<64>, grid, block, 0, st, p); break;
-    case 128: hipLaunchKernelGGL(sla_fwd_f32_kernel<128>, grid, block, 0, st, p); break;
-    default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-}
-
-template <int D>
-static hipError_t launch_dkdv_f32_d(const AttnParams &p, hipStream_t st)
-{
-    hipLaunchKernelGGL(sla_bwd_dkdv_f32_kernel<D>, dim3(p.grid_bwd), dim3(BWD_BN * F32_TPR), 0,
-                       st, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.grid_red == 0) return e;
-    hipLaunchKernelGGL(sla_bwd_reduce_f32_kernel<D>, dim3(p.grid_red), dim3(256), 0, st, p);
-    return hipGetLastError();
+    return with_head_dims(p, [&](auto QK, auto V) {
+        hipLaunchKernelGGL((sla_fwd_f32_kernel<decltype(QK)::value, decltype(V)::value>),
+                           dim3(p.grid_fwd), dim3(FWD_BM * F32_TPR), 0, st, p);
+        return hipGetLastError();
+    });
 }
 
 hipError_t launch_bwd_dkdv_f32(const AttnParams &p, hipStream_t st)
 {
-    switch (p.d) {
-    case 32: return launch_dkdv_f32_d<32>(p, st);
-    case 64: return launch_dkdv_f32_d<64>(p, st);
-    case 128: return launch_dkdv_f32_d<128>(p, st);
-    default: return hipErrorInvalidValue;
-    }
+    return with_head_dims(p, [&](auto QK, auto V) {
+        constexpr int DQK = decltype(QK)::value, DV = decltype(V)::value;
+        hipLaunchKernelGGL((sla_bwd_dkdv_f32_kernel<DQK, DV>), dim3(p.grid_bwd),
+                           dim3(BWD_BN * F32_TPR), 0, st, p);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || p.grid_red == 0) return e;
+        hipLaunchKernelGGL((sla_bwd_reduce_f32_kernel<DQK, DV>), dim3(p.grid_red), dim3(256), 0,
+                           st, p);
+        return hipGetLastError();
+    });
 }
 
 hipError_t launch_bwd_dq_f32(const AttnParams &p, hipStream_t st)
 {
-    dim3 grid(p.grid_fwd), block(FWD_BM * F32_TPR);
-    switch (p.d) {
-    case 32: hipLaunchKernelGGL(sla_bwd_dq_f32_kernel<32>, grid, block, 0, st, p); break;
-    case 64: hipLaunchKernelGGL(sla_bwd_dq_f32_kernel<64>, grid, block, 0, st, p); break;
-    case 128: hipLaunchKernelGGL(sla_bwd_dq_f32_kernel<128>, grid, block, 0, st, p); break;
-    default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    return with_head_dims(p, [&](auto QK, auto V) {
+        hipLaunchKernelGGL((sla_bwd_dq_f32_kernel<decltype(QK)::value, decltype(V)::value>),
+                           dim3(p.grid_fwd), dim3(FWD_BM * F32_TPR), 0, st, p);
+        return hipGetLastError();
+    });
 }
 
 }  // namespace sla

@@ -52,21 +52,23 @@ __device__ __forceinline__ int fswz(int r)
 // candidate's sum runs over the same history tiles in the same order and
 // then its own key, wherever it sits among the candidates: scores do not
 // depend on which other candidates share the call.
-template <int D, bool CAND, bool OUTF32>
+// DQK: the Q / K head width, DV: the V (and O) width.
+template <int DQK, int DV, bool CAND, bool OUTF32>
 __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
 {
     constexpr int BM = FWD_BM, BN = FWD_BN;
     constexpr int NT = 256;
-    constexpr int NC = D / 16;   // 16-wide contraction chunks of Q.K
-    constexpr int NDB = D / 32;  // 32-wide output blocks
-    constexpr int CPR = D / 8;   // 16-byte chunks per row
-    constexpr int TCH = BN * CPR;   // chunks of one 64-key K (or V) tile
-    constexpr int KPT = TCH / NT;   // DMA loads per thread and tile
+    constexpr int NC = DQK / 16;  // 16-wide contraction chunks of Q.K
+    constexpr int NDB = DV / 32;  // 32-wide output blocks
+    constexpr int CPR = DQK / 8, CPRV = DV / 8;     // 16-byte chunks per K / V row
+    constexpr int TCH = BN * CPR, TCHV = BN * CPRV;  // chunks of one 64-key K / V tile
+    constexpr int KPT = TCH / NT, KPTV = TCHV / NT;  // DMA loads per thread and tile
     static_assert(BN == 64 && BM == 128, "64-key steps over 128-row tiles");
-    static_assert(TCH % NT == 0 && 2 * KPT <= 8, "whole DMA rounds, at most 8 per stage");
+    static_assert(TCH % NT == 0 && TCHV % NT == 0 && KPT + KPTV <= 8,
+                  "whole DMA rounds, at most 8 per stage");
     // two stages of [K | V] bf16 rows; separate arrays so that the compiler
     // can tell the DMA into one from the reads of the other
-    __shared__ __align__(16) uint16_t st0[2 * BN * D], st1[2 * BN * D];
+    __shared__ __align__(16) uint16_t st0[BN * (DQK + DV)], st1[BN * (DQK + DV)];
 
     const int nrec = p.s.fwd_base[p.B];
     const int item = xcd_remap(blockIdx.x, nrec * p.H);
@@ -93,14 +95,14 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
     const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
     const int l32 = lane & 31, hl = lane >> 5;
 
-    const uint16_t *qg = reinterpret_cast<const uint16_t *>(p.q) + sd.base * p.ldq + h * D;
-    const uint16_t *kg = reinterpret_cast<const uint16_t *>(p.k) + sd.base * p.ldk + h * D;
-    const uint16_t *vg = reinterpret_cast<const uint16_t *>(p.v) + sd.base * p.ldv + h * D;
+    const uint16_t *qg = reinterpret_cast<const uint16_t *>(p.q) + sd.base * p.ldq + h * DQK;
+    const uint16_t *kg = reinterpret_cast<const uint16_t *>(p.k) + sd.base * p.ldk + h * DQK;
+    const uint16_t *vg = reinterpret_cast<const uint16_t *>(p.v) + sd.base * p.ldv + h * DV;
 
     // Q^T operand: lane holds row qi, d-slots 16c + 8*hl .. +8 (CAND: the
     // candidate rows, qi - U of the sequence's candidates)
     const int qi = r0 + 32 * wv + l32;
-    const uint16_t *qsrc = CAND ? reinterpret_cast<const uint16_t *>(p.q) + cbase * p.ldq + h * D
+    const uint16_t *qsrc = CAND ? reinterpret_cast<const uint16_t *>(p.q) + cbase * p.ldq + h * DQK
                                 : qg;
     const int qrow = CAND ? qi - uc : qi, qlim = CAND ? sd.L - uc : sd.L;
     bf16x8 qb[NC];
@@ -118,18 +120,20 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
         if constexpr (decltype(S)::value == 0) return st0;
         else return st1;
     };
-    // DMA of the K and V rows of key tile t into a stage: chunk P = i*NT + tid
-    // of a tile is physical chunk P % CPR of key row P / CPR and holds its
-    // logical chunk (P % CPR) ^ fswz(row); keys at or past L read key L - 1
-    // (such tiles are never "full", and the mask removes them)
+    // DMA of the K and V rows of key tile t into a stage ([K | V], the V rows
+    // after the BN * DQK elements of K): chunk P = i*NT + tid of a tile is
+    // physical chunk P % CPR of key row P / CPR and holds its logical chunk
+    // (P % CPR) ^ fswz(row) (CPR, fswz of the tile's own width); keys at or
+    // past L read key L - 1 (such tiles are never "full", and the mask
+    // removes them)
     const uint32_t ldk_b = (uint32_t)p.ldk * 2u, ldv_b = (uint32_t)p.ldv * 2u;
     // CAND: keys at or past the history length are the candidates' own
     const char *kcg = nullptr, *vcg = nullptr;
     if constexpr (CAND) {
         kcg = reinterpret_cast<const char *>(reinterpret_cast<const uint16_t *>(p.kc) +
-                                             cbase * p.ldkc + h * D);
+                                             cbase * p.ldkc + h * DQK);
         vcg = reinterpret_cast<const char *>(reinterpret_cast<const uint16_t *>(p.vc) +
-                                             cbase * p.ldvc + h * D);
+                                             cbase * p.ldvc + h * DV);
     }
     auto issue = [&](int t, auto S) {
         const int c0 = uniform(cur.start(t, BN));
@@ -152,13 +156,20 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
         }
         uint16_t *sb = stage(S);
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
+        for (int i = 0; i < (KPT > KPTV ? KPT : KPTV); ++i) {
             const int P = i * NT + tid;
-            const int prow = P / CPR;
-            const uint32_t row = (uint32_t)imin(prow, last);
-            const uint32_t c = (uint32_t)((P % CPR) ^ fswz<D>(prow));
-            gl_lds16(krow + (row * lk + 16u * c), sb + (i * NT + wv * 64) * 8);
-            gl_lds16(vrow + (row * lv + 16u * c), sb + (TCH + i * NT + wv * 64) * 8);
+            if (i < KPT) {
+                const int prow = P / CPR;
+                const uint32_t row = (uint32_t)imin(prow, last);
+                const uint32_t c = (uint32_t)((P % CPR) ^ fswz<DQK>(prow));
+                gl_lds16(krow + (row * lk + 16u * c), sb + (i * NT + wv * 64) * 8);
+            }
+            if (i < KPTV) {
+                const int prow = P / CPRV;
+                const uint32_t row = (uint32_t)imin(prow, last);
+                const uint32_t c = (uint32_t)((P % CPRV) ^ fswz<DV>(prow));
+                gl_lds16(vrow + (row * lv + 16u * c), sb + (BN * DQK + (i * NT + wv * 64) * 8));
+            }
         }
     };
     // per-lane LDS offsets (elements).  K operand: key row 32*kb + l32,
@@ -169,12 +180,12 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
     const int q4 = lane >> 4, j16 = lane & 15;
     auto k_off = [&](int kb, int c) {
         const int r = 32 * kb + l32;
-        return r * D + 8 * ((2 * c + hl) ^ fswz<D>(r));
+        return r * DQK + 8 * ((2 * c + hl) ^ fswz<DQK>(r));
     };
     auto v_off = [&](int kb, int h2, int rr, int db) {
         const int row = 32 * kb + 16 * h2 + 8 * rr + 4 * (q4 >> 1) + (j16 >> 2);
         const int col = 32 * db + 16 * (q4 & 1) + 4 * (j16 & 3);
-        return row * D + 8 * ((col >> 3) ^ fswz<D>(row)) + (col & 7);
+        return row * DV + 8 * ((col >> 3) ^ fswz<DV>(row)) + (col & 7);
     };
 
     const float nal2e = p.neg_alpha_log2e;
@@ -185,7 +196,7 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
         // unconditional (the last step re-reads its own tile): a DMA under a
         // branch costs the compiler its wait counts
         issue(imin(t + 1, ntiles - 1), std::integral_constant<int, 1 - sidx>{});
-        const uint16_t *sk = stage(S), *sv = stage(S) + BN * D;
+        const uint16_t *sk = stage(S), *sv = stage(S) + BN * DQK;
         const int c0 = uniform(cur.start(t, BN));
 
         // mask (partial tiles only, a workgroup-uniform branch).  Element r of
@@ -275,8 +286,11 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
         for (int i = 0; i < 2 * NC; ++i) {
             __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
             if (i < 2 * NC - 2) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
-            if (i < NC) __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
-            else __builtin_amdgcn_sched_group_barrier(SG_VALU, 10, 0);
+            if (i < NC) {
+                if (i < KPT + KPTV) __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
+            } else {
+                __builtin_amdgcn_sched_group_barrier(SG_VALU, 10, 0);
+            }
         }
         mask_blk(fa, 0);
         pv_blk(0, fa);
@@ -315,7 +329,7 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
             for (int g = 0; g < 4; ++g) {
                 const float o0 = oacc[db][4 * g] * sc, o1 = oacc[db][4 * g + 1] * sc;
                 const float o2 = oacc[db][4 * g + 2] * sc, o3 = oacc[db][4 * g + 3] * sc;
-                const int col = h * D + 32 * db + 8 * g + 4 * hl;
+                const int col = h * DV + 32 * db + 8 * g + 4 * hl;
                 if constexpr (OUTF32) {
                     float *orow = reinterpret_cast<float *>(p.o) + orow_i * p.ldo;
                     *reinterpret_cast<float4 *>(orow + col) = make_float4(o0, o1, o2, o3);
@@ -331,14 +345,11 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_bf16_kernel(AttnParams p)
 template <bool CAND, bool OUTF32>
 static hipError_t launch_fwd_o(const AttnParams &p, hipStream_t st)
 {
-    dim3 grid(p.grid_fwd), block(256);
-    switch (p.d) {
-    case 32: hipLaunchKernelGGL((sla_fwd_bf16_kernel<32, CAND, OUTF32>), grid, block, 0, st, p); break;
-    case 64: hipLaunchKernelGGL((sla_fwd_bf16_kernel<64, CAND, OUTF32>), grid, block, 0, st, p); break;
-    case 128: hipLaunchKernelGGL((sla_fwd_bf16_kernel<128, CAND, OUTF32>), grid, block, 0, st, p); break;
-    default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    return with_head_dims(p, [&](auto QK, auto V) {
+        hipLaunchKernelGGL((sla_fwd_bf16_kernel<decltype(QK)::value, decltype(V)::value, CAND, OUTF32>),
+                           dim3(p.grid_fwd), dim3(256), 0, st, p);
+        return hipGetLastError();
+    });
 }
 
 template <bool CAND>

@@ -151,8 +151,9 @@ def make_sla_workload(cfg: SLAConfig | str, seed: int = 0, *, lengths: Optional[
                       k1: Optional[int] = None, k2: Optional[int] = None,
                       contextual_len: Optional[int] = None, heads: Optional[int] = None,
                       d: Optional[int] = None, max_seq_len: Optional[int] = None,
-                      dtype: Optional[str] = None) -> Workload:
-    """Draw one workload.  Keyword overrides let tests build small variants."""
+                      dtype: Optional[str] = None, d_v: Optional[int] = None) -> Workload:
+    """Draw one workload.  Keyword overrides let tests build small variants
+    (d: the Q / K head width; d_v: the V and dO width, d when not given)."""
     if isinstance(cfg, str):
         cfg = CONFIGS[cfg]
     rng = np.random.default_rng(seed)
@@ -166,9 +167,10 @@ def make_sla_workload(cfg: SLAConfig | str, seed: int = 0, *, lengths: Optional[
     T = int(offsets[-1])
     q = _normal(rng, (T, H, dd), cfg.std, dt)
     k = _normal(rng, (T, H, dd), cfg.std, dt)
-    v = _normal(rng, (T, H, dd), cfg.std, dt)
+    dw = dd if d_v is None else d_v
+    v = _normal(rng, (T, H, dw), cfg.std, dt)
     want_do = cfg.backward if with_dout is None else with_dout
-    dout = _normal(rng, (T, H, dd), 1.0, dt) if want_do else None
+    dout = _normal(rng, (T, H, dw), 1.0, dt) if want_do else None
     nt = np.asarray(tg, dtype=np.int32) if any(t != 0 for t in tg) else None
     return Workload(cfg=cfg, seed=seed, lengths=lens, num_targets=nt, offsets=offsets,
                     q=q, k=k, v=v, dout=dout,
