@@ -2,7 +2,10 @@
 // with bf16 or FP8 E4M3 operands (both K-contiguous, as a Linear layer's
 // input and weight), fp32 accumulation and a bf16 output.
 //
-// Tile 256 (M) x BN (N) per workgroup of 8 waves (4 x 2, each 64 x BN/2).
+// Tile BMT (M) x BN (N) per workgroup of NWV waves, each 64 x BN / (NWV / (BMT
+// / 64)): 256 x 128 with 8 waves (4 x 2), or 128 x 128 with 4 waves (2 x 2)
+// for products whose 256-row tiles would leave the GPU's workgroup slots
+// part empty.
 // Operands stream HBM -> LDS by DMA (global_load_lds) through a ring of three
 // or four stages of 64 bytes of K (32 bf16 or 64 fp8 values) per row, the
 // next stages in flight while one is multiplied, one barrier per stage; stage rows
@@ -29,9 +32,7 @@ namespace {
 
 typedef int intx8_t __attribute__((ext_vector_type(8)));
 
-constexpr int GB_M = 256;   // rows of A per tile
 constexpr int GB_RB = 64;   // bytes of K per stage row
-constexpr int GB_NT = 512;  // threads
 
 // stage-row swizzle: 16-byte chunk c of row r sits at c ^ gswz(r)
 __device__ __forceinline__ int gswz(int r)
@@ -47,19 +48,23 @@ __device__ __forceinline__ int wperm(int j)
     return 16 * ((j >> 2) & 1) + 4 * (j >> 3) + (j & 3);
 }
 
-// NS stages (3 or 4); MINB workgroups per CU (2 needs <= 128 VGPRs and
-// 2 x NS x STAGE bytes of LDS)
-template <bool FP8, int BN, int EPI, int NS, int MINB>
-__global__ __launch_bounds__(GB_NT, MINB) void gemm_nt_kernel(
+// NS stages (3 or 4); MINB workgroups per CU (MINB x NS x STAGE bytes of
+// LDS); BMT rows of A per tile with NWV waves
+template <bool FP8, int BN, int EPI, int NS, int MINB, int BMT, int NWV>
+__global__ __launch_bounds__(64 * NWV, MINB) void gemm_nt_kernel(
     const uint8_t *A, int64_t lda, const float *sa, const uint8_t *W, int64_t ldw,
     const float *sw, const float *bias, const uint16_t *R, int64_t ldr, uint16_t *C, int64_t ldc,
     uint16_t *Z, int64_t ldz, int64_t M, int N, int Kb)
 {
+    constexpr int GB_M = BMT;                 // rows of A per tile
+    constexpr int WM = BMT / 64, WN = NWV / WM;  // wave grid: 64-row groups x column groups
+    constexpr int WCOLS = BN / WN;            // columns per wave
     constexpr int ROWS = GB_M + BN;           // stage rows: A then W
     constexpr int STAGE = ROWS * GB_RB;       // bytes
-    constexpr int PER = ROWS / 16 / 8;        // DMA instructions per thread and stage
-    constexpr int NBW = BN / 64;              // 32-column fragments per wave
-    static_assert(ROWS % 128 == 0, "whole DMA rounds");
+    constexpr int PER = ROWS / 16 / NWV;      // DMA instructions per thread and stage
+    constexpr int NBW = WCOLS / 32;           // 32-column fragments per wave
+    static_assert(WM * WN == NWV && WCOLS == 64, "64 x 64 per wave");
+    static_assert(ROWS % (16 * NWV) == 0, "whole DMA rounds");
     static_assert(NS == 3 || NS == 4, "three or four stages");
     __shared__ __align__(16) uint8_t st0[STAGE], st1[STAGE], st2[STAGE];
     __shared__ __align__(16) uint8_t st3[NS == 4 ? STAGE : 16];
@@ -73,7 +78,7 @@ __global__ __launch_bounds__(GB_NT, MINB) void gemm_nt_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
     const int l32 = lane & 31, hl = lane >> 5;
-    const int wm = wv & 3, wn = wv >> 2;
+    const int wm = wv % WM, wn = wv / WM;
 
     auto stage = [&](auto S) -> uint8_t * {
         constexpr int s = decltype(S)::value;
@@ -84,7 +89,7 @@ __global__ __launch_bounds__(GB_NT, MINB) void gemm_nt_kernel(
     };
 
     // DMA of K bytes [kb, kb + 64) of the tile's A and W rows into a stage:
-    // wave-chunk q = i * 8 + wv holds stage rows 16 q .. +16, lane -> row
+    // wave-chunk q = i * NWV + wv holds stage rows 16 q .. +16, lane -> row
     // 16 q + lane / 4, physical chunk lane % 4 (logical chunk ^ gswz)
     const int64_t mlast = M - 1;
     auto issue = [&](int kstep, auto S) {
@@ -92,7 +97,7 @@ __global__ __launch_bounds__(GB_NT, MINB) void gemm_nt_kernel(
         const int kb = kstep * GB_RB;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int q = i * 8 + wv;
+            const int q = i * NWV + wv;
             const int row = 16 * q + (lane >> 2);
             const int lc = (lane & 3) ^ gswz(row);
             const uint8_t *src;
@@ -117,7 +122,7 @@ __global__ __launch_bounds__(GB_NT, MINB) void gemm_nt_kernel(
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
 
-    const int wrow0 = GB_M + wn * (BN / 2);  // this wave's first W stage row
+    const int wrow0 = GB_M + wn * WCOLS;     // this wave's first W stage row
     const int arow0 = 64 * wm;               // and first A stage row
     auto compute = [&](auto S) {
         const uint8_t *sb = stage(S);
@@ -198,11 +203,10 @@ __global__ __launch_bounds__(GB_NT, MINB) void gemm_nt_kernel(
     // block row r at c ^ eswz(r), and stores it back out in row chunks; no
     // barrier after the first (within a wave, LDS accesses complete in
     // order).  EPI 3 does it twice (SiLU(z) to C, then z to Z).
-    constexpr int WCOLS = BN / 2;         // columns per wave
     constexpr int CPW = WCOLS / 8;        // 16-byte chunks per block row
     constexpr int SLICE = 64 * CPW * 16;  // bytes per wave
     constexpr int SPS = STAGE / SLICE;  // wave slices per stage
-    static_assert(SPS * NS >= 8, "every wave has a slice");
+    static_assert(SPS * NS >= NWV, "every wave has a slice");
     uint8_t *slice;
     switch (wv / SPS) {
     case 0: slice = st0; break;
@@ -276,31 +280,44 @@ __global__ __launch_bounds__(GB_NT, MINB) void gemm_nt_kernel(
     }
 }
 
-template <bool FP8, int BN, int NS, int MINB>
+template <bool FP8, int BN, int NS, int MINB, int BMT, int NWV>
 hipError_t launch_nt(const void *A, int64_t lda, const float *sa, const void *W, int64_t ldw,
                      const float *sw, const float *bias, const void *R, int64_t ldr, void *C,
                      int64_t ldc, void *Z, int64_t ldz, int64_t M, int N, int Kb, int epi,
                      hipStream_t st)
 {
-    const int64_t tiles = ((M + GB_M - 1) / GB_M) * (N / BN);
-    dim3 grid((unsigned)tiles), block(GB_NT);
+    const int64_t tiles = ((M + BMT - 1) / BMT) * (N / BN);
+    dim3 grid((unsigned)tiles), block(64 * NWV);
 #define GNT_ARGS                                                                               \
     (const uint8_t *)A, lda, sa, (const uint8_t *)W, ldw, sw, bias, (const uint16_t *)R, ldr, \
         (uint16_t *)C, ldc, (uint16_t *)Z, ldz, M, N, Kb
     switch (epi) {
-    case 0: hipLaunchKernelGGL((gemm_nt_kernel<FP8, BN, 0, NS, MINB>), grid, block, 0, st, GNT_ARGS); break;
-    case 1: hipLaunchKernelGGL((gemm_nt_kernel<FP8, BN, 1, NS, MINB>), grid, block, 0, st, GNT_ARGS); break;
-    case 2: hipLaunchKernelGGL((gemm_nt_kernel<FP8, BN, 2, NS, MINB>), grid, block, 0, st, GNT_ARGS); break;
-    default: hipLaunchKernelGGL((gemm_nt_kernel<FP8, BN, 3, NS, MINB>), grid, block, 0, st, GNT_ARGS); break;
+    case 0: hipLaunchKernelGGL((gemm_nt_kernel<FP8, BN, 0, NS, MINB, BMT, NWV>), grid, block, 0, st, GNT_ARGS); break;
+    case 1: hipLaunchKernelGGL((gemm_nt_kernel<FP8, BN, 1, NS, MINB, BMT, NWV>), grid, block, 0, st, GNT_ARGS); break;
+    case 2: hipLaunchKernelGGL((gemm_nt_kernel<FP8, BN, 2, NS, MINB, BMT, NWV>), grid, block, 0, st, GNT_ARGS); break;
+    default: hipLaunchKernelGGL((gemm_nt_kernel<FP8, BN, 3, NS, MINB, BMT, NWV>), grid, block, 0, st, GNT_ARGS); break;
     }
 #undef GNT_ARGS
     return hipGetLastError();
 }
 
+// whether a bf16 product takes the 128-row tiles: when its 256-row tiles
+// would number fewer than 1024 (two rounds of 512 workgroup slots on 256
+// CUs).  Measured on the STU layer's products (one box): 128-row tiles take
+// the truncated layers' UVQK (M = 8832, N = 2048) from 37.2 to 35.2 us, the
+// output projection (M = 21,930, N = 512) from 27.0 to 25.8 us and the
+// backward's dn (K = 2048) from 67.2 to 65.4 us; the full-length UVQK (1376
+// tiles of 256 rows) is faster with 256-row tiles (78-80 against 83 us).
+static bool gemm_small_tiles(int64_t M, int N)
+{
+    return ((M + 255) / 256) * (N / 128) < 1024;
+}
+
 // bf16: 256 x 128 tiles in a three-stage ring, two workgroups per CU (one
 // workgroup's epilogue runs under the other's products; measured faster than
 // 256 x 256 tiles with one workgroup per CU on every projection shape of the
-// layer).  FP8: the operand fragments take twice the registers, so 256 x 128
+// layer), or 128 x 128 tiles of four waves, three workgroups per CU, for the
+// smaller products (gemm_small_tiles).  FP8: the operand fragments take twice the registers, so 256 x 128
 // tiles with four stages and one workgroup per CU.
 template <bool FP8>
 hipError_t launch_nt_any(const void *A, int64_t lda, const float *sa, const void *W, int64_t ldw,
@@ -309,11 +326,15 @@ hipError_t launch_nt_any(const void *A, int64_t lda, const float *sa, const void
                          hipStream_t st)
 {
     if constexpr (!FP8) {
-        return launch_nt<FP8, 128, 3, 2>(A, lda, sa, W, ldw, sw, bias, R, ldr, C, ldc, Z, ldz, M,
-                                         N, Kb, epi, st);
+        if (gemm_small_tiles(M, N))
+            return launch_nt<FP8, 128, 3, 3, 128, 4>(A, lda, sa, W, ldw, sw, bias, R,
+                                                                   ldr, C, ldc, Z, ldz, M, N, Kb,
+                                                                   epi, st);
+        return launch_nt<FP8, 128, 3, 2, 256, 8>(A, lda, sa, W, ldw, sw, bias, R, ldr, C, ldc, Z,
+                                                 ldz, M, N, Kb, epi, st);
     } else {
-        return launch_nt<FP8, 128, 4, 1>(A, lda, sa, W, ldw, sw, bias, R, ldr, C, ldc, Z, ldz, M,
-                                         N, Kb, epi, st);
+        return launch_nt<FP8, 128, 4, 1, 256, 8>(A, lda, sa, W, ldw, sw, bias, R, ldr, C, ldc, Z,
+                                                 ldz, M, N, Kb, epi, st);
     }
 }
 
