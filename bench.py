@@ -78,8 +78,9 @@ def parse():
 
 
 # kernels whose HBM traffic the bench line reports, by the name rocprofv3 gives them
-PMC_KERNELS = {"fwd": "sla_fwd_bf16_kernel<128, false", "bwd_dkdv": "sla_bwd_dkdv_bf16_kernel<128",
-               "bwd_dq": "sla_bwd_dq_kernel<128"}
+PMC_KERNELS = {"fwd": "sla_fwd_bf16_kernel<128, 128, false",
+               "bwd_dkdv": "sla_bwd_dkdv_bf16_kernel<128, 128",
+               "bwd_dq": "sla_bwd_dq_kernel<128, 128"}
 CALIB_BYTES = 256 * 1024 * 1024
 CALIB_NAME = "neg_kernel_cuda"
 
