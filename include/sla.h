@@ -85,8 +85,8 @@ typedef struct {
     const int32_t *num_targets;  /* device int32 [B], or NULL                       */
     int32_t num_heads;           /* H >= 1                                          */
     int32_t d_qk;                /* head dim of Q and K: 32, 64 or 128              */
-    int32_t d_v;                 /* head dim of V and O: d_qk, or (d_qk, d_v) =     */
-                                 /* (64, 128) or (128, 64)                          */
+    int32_t d_v;                 /* head dim of V and O: 32, 64 or 128 (any pair    */
+                                 /* with d_qk)                                      */
     int32_t k1;                  /* local window K1 >= 0 (keys, the row included)   */
     int32_t k2;                  /* global prefix K2 >= 0                           */
     int32_t contextual_len;      /* contextual prefix >= 0; K2e = max(k2, this)     */
@@ -124,7 +124,7 @@ size_t sla_workspace_size(const sla_problem_t *p, int op);
  * range limit beyond fp32's applies).  f32 path: fp32 throughout.  Only the non-empty tiles of the local band, the global prefix
  * and (for targets) the diagonal are visited.
  * Errors: NULL -> SLA_ERR_NULL; bad sizes/strides -> SLA_ERR_INVALID; head dims
- * other than d_qk = d_v in {32,64,128} or (d_qk, d_v) in {(64,128), (128,64)}, ld or pointer not 16-byte aligned ->
+ * not in {32,64,128}, ld or pointer not 16-byte aligned ->
  * SLA_ERR_UNSUPPORTED; ws_bytes < sla_workspace_size(p, SLA_OP_FWD) ->
  * SLA_ERR_WORKSPACE. */
 sla_status_t sla_fwd(const sla_problem_t *p, const void *q, int64_t ldq, const void *k,

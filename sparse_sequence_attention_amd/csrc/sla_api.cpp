@@ -81,9 +81,8 @@ sla_status_t validate_problem(const sla_problem_t *p)
     if (p->batch > 0 && !p->offsets) return fail(SLA_ERR_NULL, "offsets is NULL");
     if (p->num_heads < 1) return fail(SLA_ERR_INVALID, "num_heads must be >= 1");
     if (!attn_dims_supported(p->d_qk, p->d_v))
-        return fail(SLA_ERR_UNSUPPORTED,
-                    "head widths d_qk = %d, d_v = %d: supported are d_qk = d_v in {32, 64, 128} "
-                    "and (64, 128), (128, 64)", p->d_qk, p->d_v);
+        return fail(SLA_ERR_UNSUPPORTED, "head widths d_qk = %d, d_v = %d not in {32, 64, 128}",
+                    p->d_qk, p->d_v);
     if (p->k1 < 0 || p->k2 < 0 || p->contextual_len < 0)
         return fail(SLA_ERR_INVALID, "k1, k2 and contextual_len must be >= 0");
     if (p->max_seq_len < 1) return fail(SLA_ERR_INVALID, "max_seq_len must be >= 1");

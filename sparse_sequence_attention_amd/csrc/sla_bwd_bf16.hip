@@ -84,17 +84,21 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
     constexpr int CPR = DQK / 8, CPRV = DV / 8;     // 16-byte chunks per Q / K, dO / V row
     constexpr int DW = DQK + DV;                    // a [Q | dO] or [K | V] row pair
     constexpr int TCH = BM * CPR, TCHV = BM * CPRV; // chunks of a staged Q, dO tile
-    constexpr int SPS = (TCH + TCHV) / NT;          // DMA loads per thread and step
+    constexpr int SPS = (TCH + TCHV + NT - 1) / NT; // DMA loads per thread and step
+    // chunk slots of a stage: [Q | dO], then, when the two tiles do not make
+    // whole DMA rounds, padding that the surplus loads fill
+    constexpr int SLOTS = SPS * NT;
     constexpr int KCH = BN * CPR, KCHV = BN * CPRV; // chunks of the K, V tile
     constexpr int KPT = (KCH + KCHV) / NT;          // DMA loads per thread of the K and V tiles
     constexpr int NST = DKDV_STAGES;
     static_assert(BM == 64 && BN == 128, "64-row steps over 128-key tiles");
-    static_assert((TCH + TCHV) % NT == 0 && SPS <= 8, "whole DMA rounds, at most 8 per thread");
-    static_assert(TCH % 64 == 0 && KCH % NT == 0, "the Q / dO and K / V split is wave-uniform");
+    static_assert(SPS <= 8, "at most 8 DMA loads per thread and step");
+    static_assert(TCH % 64 == 0 && TCHV % 64 == 0 && KCH % NT == 0,
+                  "the Q / dO / padding and K / V splits are wave-uniform");
     static_assert((KCH + KCHV) % NT == 0 && KPT <= 8, "whole DMA rounds of the key tile");
     // [K | V] of the key tile (bf16, swizzled rows), then a ring of NST stages
     // of [Q | dO] rows filled by DMA NST - 1 steps ahead: 64 + 96 KB at d = 128
-    __shared__ __align__(16) uint16_t lds[BN * DW + NST * BM * DW];
+    __shared__ __align__(16) uint16_t lds[BN * DW + NST * SLOTS * 8];
     uint16_t *const kvs = lds;
     uint16_t *const ring = lds + BN * DW;
 
@@ -205,7 +209,7 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
         const int last = uniform(m1 - 1 - m0);
         const char *qrow = reinterpret_cast<const char *>(qg + (int64_t)m0 * p.ldq);
         const char *grow = reinterpret_cast<const char *>(gg + (int64_t)m0 * p.lddo);
-        uint16_t *sb = ring + (t % NST) * (BM * DW);
+        uint16_t *sb = ring + (t % NST) * (SLOTS * 8);
 #pragma unroll
         for (int i = 0; i < SPS; ++i) {
             const int P = i * NT + wv * 64 + lane;
@@ -223,6 +227,8 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
                 const uint32_t row = (uint32_t)imin(prow, last);
                 const uint32_t c = (uint32_t)((P % CPR) ^ hswz<DQK>(prow));
                 src = qrow + (row * ldq_b + 16u * c);
+            } else if (P >= TCH + TCHV) {
+                src = qrow;  // padding: Q's first chunk into the stage's spare slots
             } else {
                 const int Pg = P - TCH;
                 const int prow = Pg / CPRV;
@@ -255,7 +261,7 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
     // bytes: the [K | V] region (BN DW bf16), one [Q | dO] stage (BM DW
     // bf16), the staged Q tile (the dO tile follows it), the K tile (V
     // follows it)
-    constexpr uint32_t KV_BYTES = 2u * BN * DW, STAGE_BYTES = 2u * BM * DW;
+    constexpr uint32_t KV_BYTES = 2u * BN * DW, STAGE_BYTES = 16u * SLOTS;
     constexpr uint32_t TILE_BYTES = 2u * BM * DQK, K_BYTES = 2u * BN * DQK;
     static_assert(KV_BYTES == BN * DW * sizeof(uint16_t), "ring starts after [K | V]");
     constexpr uint32_t H2_BYTES = 2u * 16u * DQK, H2V_BYTES = 2u * 16u * DV;

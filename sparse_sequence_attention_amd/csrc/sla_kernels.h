@@ -44,31 +44,37 @@ struct AttnParams {
     int64_t ldkc, ldvc;
 };
 
-// Head widths (d_qk, d_v) the attention kernels are built for: the square
-// heads of 32, 64 and 128, and the rectangular pairs of 64 and 128 (the
-// dK/dV kernel stages the Q and dO rows of a step with whole DMA rounds,
-// which needs d_qk + d_v to be a multiple of 64).
+// Head widths (d_qk, d_v) the attention kernels are built for: each of 32,
+// 64 and 128, in any pair.
 inline bool attn_dims_supported(int dqk, int dv)
 {
     const bool ok_qk = dqk == 32 || dqk == 64 || dqk == 128;
     const bool ok_v = dv == 32 || dv == 64 || dv == 128;
-    return ok_qk && ok_v && (dqk + dv) % 64 == 0;
+    return ok_qk && ok_v;
 }
 
 // f(integral_constant<int, d_qk>, integral_constant<int, d_v>) for the head
-// widths of p, instantiated for the supported pairs only
+// widths of p
 template <typename F>
 hipError_t with_head_dims(const AttnParams &p, F &&f)
 {
     using I32 = std::integral_constant<int, 32>;
     using I64 = std::integral_constant<int, 64>;
     using I128 = std::integral_constant<int, 128>;
-    if (p.d == 32 && p.d_v == 32) return f(I32{}, I32{});
-    if (p.d == 64 && p.d_v == 64) return f(I64{}, I64{});
-    if (p.d == 128 && p.d_v == 128) return f(I128{}, I128{});
-    if (p.d == 64 && p.d_v == 128) return f(I64{}, I128{});
-    if (p.d == 128 && p.d_v == 64) return f(I128{}, I64{});
-    return hipErrorInvalidValue;
+    auto v = [&](auto QK) -> hipError_t {
+        switch (p.d_v) {
+        case 32: return f(QK, I32{});
+        case 64: return f(QK, I64{});
+        case 128: return f(QK, I128{});
+        default: return hipErrorInvalidValue;
+        }
+    };
+    switch (p.d) {
+    case 32: return v(I32{});
+    case 64: return v(I64{});
+    case 128: return v(I128{});
+    default: return hipErrorInvalidValue;
+    }
 }
 
 // Sizes (int32 counts / bytes) of the workspace regions, from host-known data.

@@ -24,6 +24,12 @@ CASES = [
     ([1, 700, 129, 0, 256], None, 130, 64, 8, 128, 64),
     ([513, 64, 1000], [17, 64, 200], 100, 16, 8, 64, 128),
     ([2500, 600], [0, 16], 300, 128, 16, 128, 64),   # prefix tile split into chunks
+    # one width 32: the dK/dV stage of Q and dO rows is not a whole number of
+    # DMA rounds and carries padding
+    ([700, 129, 1], [8, 0, 0], 96, 16, 4, 32, 64),
+    ([2200, 300], None, 200, 64, 8, 64, 32),         # prefix tile split into chunks
+    ([450, 64], [32, 0], 64, 8, 2, 32, 128),
+    ([900, 0, 77], None, 128, 32, 8, 128, 32),
 ]
 MODES = ["bf16o32", "bf16", "f32"]
 
@@ -118,7 +124,7 @@ def _stu_rect(dqk, dv, seed=2):
     return sw, host, dout, kw, okw, dev
 
 
-@pytest.mark.parametrize("dqk,dv", [(64, 128), (128, 64)])
+@pytest.mark.parametrize("dqk,dv", [(64, 128), (128, 64), (32, 64)])
 def test_rect_stu_layer_fwd_bwd(dqk, dv):
     """The STU layer with rectangular heads, forward against the
     storage-matched oracle (the square-head layer test's bar) and backward

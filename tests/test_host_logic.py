@@ -203,10 +203,9 @@ def _fwd(lib, p, ld=512, ws=FAKE, wsb=1 << 30, q=FAKE):
 def test_fwd_argument_errors(lib):
     assert _fwd(lib, _problem(), q=None) == C.SLA_ERR_NULL
     assert _fwd(lib, _problem(d=96, dv=96), ld=384) == C.SLA_ERR_UNSUPPORTED
-    # rectangular heads: (64, 128) and (128, 64) are built; pairs whose sum
-    # is not a multiple of 64 are not
-    for dqk, dv in ((32, 64), (64, 32), (32, 128), (128, 32)):
-        assert _fwd(lib, _problem(d=dqk, dv=dv), ld=512) == C.SLA_ERR_UNSUPPORTED, (dqk, dv)
+    # any pair of widths in {32, 64, 128} is built; others are not
+    for dqk, dv in ((96, 64), (64, 96), (128, 256), (16, 32)):
+        assert _fwd(lib, _problem(d=dqk, dv=dv), ld=1024) == C.SLA_ERR_UNSUPPORTED, (dqk, dv)
     assert _fwd(lib, _problem(), ld=100) == C.SLA_ERR_INVALID          # ld < H*d
     assert _fwd(lib, _problem(), ld=516) == C.SLA_ERR_UNSUPPORTED      # not 16-byte rows
     assert _fwd(lib, _problem(n=0)) == C.SLA_ERR_INVALID
