@@ -23,10 +23,12 @@ def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _head_tensor(name: str, t: torch.Tensor, T: int, H: int, dtype) -> int:
-    """Check a [T, H, d] view with unit inner stride; returns the token stride."""
-    if t.dim() != 3 or t.shape[0] != T or t.shape[1] != H:
-        raise ValueError(f"{name}: expected shape [T={T}, H={H}, d], got {tuple(t.shape)}")
+def _head_tensor(name: str, t: torch.Tensor, T: int, H: int, dtype, width: int) -> int:
+    """Check a [T, H, width] view with unit inner stride; returns the token
+    stride.  The library finds head h at column h * width of a row, so a
+    tensor of another width would be read at the wrong offsets."""
+    if t.dim() != 3 or t.shape[0] != T or t.shape[1] != H or t.shape[2] != width:
+        raise ValueError(f"{name}: expected shape [T={T}, H={H}, {width}], got {tuple(t.shape)}")
     if t.dtype != dtype:
         raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
     if not t.is_cuda:
@@ -97,14 +99,14 @@ def sla_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, offsets: torch.Te
     given `out` decides when out_dtype is None)."""
     T, H, dqk = q.shape
     dv = v.shape[2]
-    ldq = _head_tensor("q", q, T, H, q.dtype)
-    ldk = _head_tensor("k", k, T, H, q.dtype)
-    ldv = _head_tensor("v", v, T, H, q.dtype)
+    ldq = _head_tensor("q", q, T, H, q.dtype, dqk)
+    ldk = _head_tensor("k", k, T, H, q.dtype, dqk)
+    ldv = _head_tensor("v", v, T, H, q.dtype, dv)
     odt = out_dtype if out_dtype is not None else (out.dtype if out is not None else q.dtype)
     f32o = _out_f32(q.dtype, odt)
     if out is None:
         out = torch.empty((T, H, dv), dtype=odt, device=q.device)
-    ldo = _head_tensor("out", out, T, H, odt)
+    ldo = _head_tensor("out", out, T, H, odt, dv)
     p = make_problem(q.dtype, offsets, num_targets, T, H, dqk, dv, k1, k2, contextual_len,
                      max_seq_len, alpha, f32o)
     nbytes = workspace_size(p, C.SLA_OP_FWD)
@@ -126,16 +128,16 @@ def sla_fwd_candidates(k_hist: torch.Tensor, v_hist: torch.Tensor, hist_offsets:
     Cn = q_c.shape[0]
     dv = v_c.shape[2]
     dt = q_c.dtype
-    ldk = _head_tensor("k_hist", k_hist, Th, H, dt)
-    ldv = _head_tensor("v_hist", v_hist, Th, H, dt)
-    ldq = _head_tensor("q_c", q_c, Cn, H, dt)
-    ldkc = _head_tensor("k_c", k_c, Cn, H, dt)
-    ldvc = _head_tensor("v_c", v_c, Cn, H, dt)
+    ldk = _head_tensor("k_hist", k_hist, Th, H, dt, dqk)
+    ldv = _head_tensor("v_hist", v_hist, Th, H, dt, dv)
+    ldq = _head_tensor("q_c", q_c, Cn, H, dt, dqk)
+    ldkc = _head_tensor("k_c", k_c, Cn, H, dt, dqk)
+    ldvc = _head_tensor("v_c", v_c, Cn, H, dt, dv)
     odt = out_dtype if out_dtype is not None else (out.dtype if out is not None else dt)
     f32o = _out_f32(dt, odt)
     if out is None:
         out = torch.empty((Cn, H, dv), dtype=odt, device=q_c.device)
-    ldo = _head_tensor("out", out, Cn, H, odt)
+    ldo = _head_tensor("out", out, Cn, H, odt, dv)
     if cand_offsets.dtype != torch.int64 or cand_offsets.numel() != hist_offsets.numel():
         raise TypeError("cand_offsets must be an int64 tensor [B+1] like hist_offsets")
     p = make_problem(dt, hist_offsets, None, Th, H, dqk, dv, k1, k2, contextual_len, max_seq_len,
@@ -159,19 +161,19 @@ def sla_bwd(q, k, v, dout, offsets, num_targets=None, *, k1: int, k2: int,
     (the dtype of given output tensors decides when grad_dtype is None)."""
     T, H, dqk = q.shape
     dvd = v.shape[2]
-    ldq = _head_tensor("q", q, T, H, q.dtype)
-    ldk = _head_tensor("k", k, T, H, q.dtype)
-    ldv = _head_tensor("v", v, T, H, q.dtype)
-    lddo = _head_tensor("dout", dout, T, H, q.dtype)
+    ldq = _head_tensor("q", q, T, H, q.dtype, dqk)
+    ldk = _head_tensor("k", k, T, H, q.dtype, dqk)
+    ldv = _head_tensor("v", v, T, H, q.dtype, dvd)
+    lddo = _head_tensor("dout", dout, T, H, q.dtype, dvd)
     given = [t for t in (dq, dk, dv) if t is not None]
     gdt = grad_dtype if grad_dtype is not None else (given[0].dtype if given else q.dtype)
     f32o = _out_f32(q.dtype, gdt)
     dq = torch.empty((T, H, dqk), dtype=gdt, device=q.device) if dq is None else dq
     dk = torch.empty((T, H, dqk), dtype=gdt, device=q.device) if dk is None else dk
     dv = torch.empty((T, H, dvd), dtype=gdt, device=q.device) if dv is None else dv
-    lddq = _head_tensor("dq", dq, T, H, gdt)
-    lddk = _head_tensor("dk", dk, T, H, gdt)
-    lddv = _head_tensor("dv", dv, T, H, gdt)
+    lddq = _head_tensor("dq", dq, T, H, gdt, dqk)
+    lddk = _head_tensor("dk", dk, T, H, gdt, dqk)
+    lddv = _head_tensor("dv", dv, T, H, gdt, dvd)
     p = make_problem(q.dtype, offsets, num_targets, T, H, dqk, dvd, k1, k2, contextual_len,
                      max_seq_len, alpha, f32o)
     nbytes = workspace_size(p, C.SLA_OP_BWD)
@@ -191,14 +193,14 @@ def sla_bwd_noalloc(q, k, v, dout, offsets, num_targets=None, *, k1: int, k2: in
     race).  Neither this wrapper nor the call allocates device memory."""
     T, H, dqk = q.shape
     dvd = v.shape[2]
-    ldq = _head_tensor("q", q, T, H, q.dtype)
-    ldk = _head_tensor("k", k, T, H, q.dtype)
-    ldv = _head_tensor("v", v, T, H, q.dtype)
-    lddo = _head_tensor("dout", dout, T, H, q.dtype)
+    ldq = _head_tensor("q", q, T, H, q.dtype, dqk)
+    ldk = _head_tensor("k", k, T, H, q.dtype, dqk)
+    ldv = _head_tensor("v", v, T, H, q.dtype, dvd)
+    lddo = _head_tensor("dout", dout, T, H, q.dtype, dvd)
     gdt = dq.dtype
-    lddq = _head_tensor("dq", dq, T, H, gdt)
-    lddk = _head_tensor("dk", dk, T, H, gdt)
-    lddv = _head_tensor("dv", dv, T, H, gdt)
+    lddq = _head_tensor("dq", dq, T, H, gdt, dqk)
+    lddk = _head_tensor("dk", dk, T, H, gdt, dqk)
+    lddv = _head_tensor("dv", dv, T, H, gdt, dvd)
     p = make_problem(q.dtype, offsets, num_targets, T, H, dqk, dvd, k1, k2, contextual_len,
                      max_seq_len, alpha, _out_f32(q.dtype, gdt))
     C.check(C.load().sla_bwd_noalloc(ctypes.byref(p), _ptr(q), ldq, _ptr(k), ldk, _ptr(v), ldv,

@@ -21,18 +21,20 @@ def _bf(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV).bfloat16()
 
 
-def _case(seed, hist, cands, H=2, d=128, std=0.5):
-    """Seeded history keys/values and candidate q/k/v, bf16-exact values."""
+def _case(seed, hist, cands, H=2, d=128, std=0.5, dv=None):
+    """Seeded history keys/values and candidate q/k/v, bf16-exact values
+    (values of width dv, d when not given)."""
+    dv = d if dv is None else dv
     rng = np.random.default_rng(seed)
     ho = np.concatenate([[0], np.cumsum(hist)]).astype(np.int64)
     co = np.concatenate([[0], np.cumsum(cands)]).astype(np.int64)
 
-    def mk(n):
-        x = (rng.standard_normal((n, H, d), dtype=np.float32) * std)
+    def mk(n, w=d):
+        x = (rng.standard_normal((n, H, w), dtype=np.float32) * std)
         return torch.from_numpy(x).bfloat16().float().numpy()
 
-    return ho, co, mk(int(ho[-1])), mk(int(ho[-1])), mk(int(co[-1])), mk(int(co[-1])), \
-        mk(int(co[-1]))
+    return ho, co, mk(int(ho[-1])), mk(int(ho[-1]), dv), mk(int(co[-1])), mk(int(co[-1])), \
+        mk(int(co[-1]), dv)
 
 
 def _gpu(ho, co, kh, vh, qc, kc, vc, kw, **extra):
@@ -51,6 +53,20 @@ def test_candidates_match_oracle(d):
     ho, co, kh, vh, qc, kc, vc = _case(0, hist, cands, d=d)
     print(f"[case] candidates d={d} hist={hist} cands={cands}", flush=True)
     o = _gpu(ho, co, kh, vh, qc, kc, vc, KW)
+    ref = oracle.sla_fwd_candidates(kh, vh, ho, qc, kc, vc, co, KW["k1"], KW["k2"],
+                                    KW["contextual_len"], KW["max_seq_len"])
+    mx, mn = assert_close_bf16(o.float().cpu().numpy(), ref, "o_c")
+    print(f"  o_c max {mx:.3e} mean {mn:.3e}")
+
+
+@pytest.mark.parametrize("d,dv", [(64, 128), (128, 32), (32, 64)])
+def test_candidates_rect_heads_match_oracle(d, dv):
+    """Query/key width d, value width dv (the forward's rectangular heads)."""
+    hist, cands = [300, 0, 1000, 129], [70, 5, 300, 33]
+    ho, co, kh, vh, qc, kc, vc = _case(3, hist, cands, d=d, dv=dv)
+    print(f"[case] candidates d_qk={d} d_v={dv} hist={hist} cands={cands}", flush=True)
+    o = _gpu(ho, co, kh, vh, qc, kc, vc, KW)
+    assert tuple(o.shape) == (sum(cands), 2, dv)
     ref = oracle.sla_fwd_candidates(kh, vh, ho, qc, kc, vc, co, KW["k1"], KW["k2"],
                                     KW["contextual_len"], KW["max_seq_len"])
     mx, mn = assert_close_bf16(o.float().cpu().numpy(), ref, "o_c")

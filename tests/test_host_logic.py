@@ -400,3 +400,49 @@ def test_truncated_token_count_on_the_host_matches_the_oracle():
         assert truncated_tokens_host(lens, tg, ctx, tail) == int(new_offs[-1])
         new_offs, _ = oracle.truncate(offs, None, ctx, tail)
         assert truncated_tokens_host(lens, None, ctx, tail) == int(new_offs[-1])
+
+
+def test_binding_checks_every_head_width(monkeypatch):
+    """Q, K (and dQ, dK) share the width d_qk, V, dO, O (and dV) the width
+    d_v: the shape check rejects a tensor of another width (the library would
+    read its heads at the wrong column offsets), and every entry point asks
+    for the right width of each tensor.  Host tensors suffice: the calls are
+    stopped before the library."""
+    import torch
+    bf = torch.bfloat16
+    t = lambda w: torch.zeros((4, 2, w), dtype=bf)  # noqa: E731
+    with pytest.raises(ValueError, match=r"k: expected shape \[T=4, H=2, 64\]"):
+        ops._head_tensor("k", t(128), 4, 2, bf, 64)
+
+    seen = {}
+
+    class Stop(Exception):
+        pass
+
+    def record(name, x, T, H, dtype, width):
+        seen[name] = (tuple(x.shape), width)
+        return H * width
+
+    def stop(*a, **k):
+        raise Stop
+
+    monkeypatch.setattr(ops, "_head_tensor", record)
+    monkeypatch.setattr(ops, "make_problem", stop)
+    offs = torch.tensor([0, 4], dtype=torch.int64)
+    kw = dict(k1=8, k2=0, max_seq_len=4)
+    calls = [
+        lambda: ops.sla_fwd(t(64), t(64), t(32), offs, **kw),
+        lambda: ops.sla_bwd(t(64), t(64), t(32), t(32), offs, **kw),
+        lambda: ops.sla_bwd_noalloc(t(64), t(64), t(32), t(32), offs, dq=t(64), dk=t(64),
+                                    dv=t(32), **kw),
+        lambda: ops.sla_fwd_candidates(t(64), t(32), offs, t(64), t(64), t(32), offs, **kw),
+    ]
+    for call in calls:
+        seen.clear()
+        with pytest.raises(Stop):
+            call()
+        assert len(seen) >= 4
+        for name, (shape, width) in seen.items():
+            assert shape[2] == width, (name, shape, width)
+            want = 32 if name in ("v", "v_hist", "v_c", "dout", "dv", "out") else 64
+            assert width == want, (name, width)
