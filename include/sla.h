@@ -101,8 +101,9 @@ typedef struct {
 } sla_problem_t;
 
 /* Operation selector for sla_workspace_size and the schedule inspection
- * calls: FWD = row tiles (forward and dQ), BWD = key tiles (dK/dV). */
-enum { SLA_OP_FWD = 0, SLA_OP_BWD = 1 };
+ * calls: FWD = row tiles (forward and dQ), BWD = key tiles (dK/dV).
+ * BWD_RECOMPUTE (sla_workspace_size only): the smallest backward workspace. */
+enum { SLA_OP_FWD = 0, SLA_OP_BWD = 1, SLA_OP_BWD_RECOMPUTE = 2 };
 
 /* Bytes of device workspace sla_fwd (op = SLA_OP_FWD) or sla_bwd
  * (op = SLA_OP_BWD) needs for problem p: the on-device tile schedule (about
@@ -110,8 +111,17 @@ enum { SLA_OP_FWD = 0, SLA_OP_BWD = 1 };
  * of the split global-prefix key tiles (at most 4 key tiles of 128 keys per
  * sequence, each cut into at most 16 row chunks: up to
  * 64 * 128 * H * (d_qk + d_v) * 4 bytes per sequence, about 17 MB for 8
- * sequences, 4 heads, d = 128).  Depends only on host-known fields.  Returns 0
- * if p is invalid. */
+ * sequences, 4 heads, d = 128).  On the bf16 path with d_qk >= 64,
+ * SLA_OP_BWD adds room for
+ * dS: the dK/dV kernel stores the bf16 dS of every visited 64-row x 128-key
+ * tile (16 KB each, per head) and the dQ kernel reads it back instead of
+ * recomputing S and dO.V^T (an upper bound from the sizes: about 1.1 GB
+ * for 110K tokens, 4 heads, K1 = 1024, K2 = 128, with 2 bytes per visible
+ * pair actually written).  That room is only requested where it stays
+ * within 16 times the bytes of Q, K, V and dO (windows K1 up to about 8K
+ * at d = 128); otherwise, and with SLA_OP_BWD_RECOMPUTE, the size is the
+ * schedule and partials only, with which sla_bwd recomputes in the dQ
+ * kernel.  Depends only on host-known fields.  Returns 0 if p is invalid. */
 size_t sla_workspace_size(const sla_problem_t *p, int op);
 
 /* SLA forward (ULTRA-HSTU paper, section 4.2.1 Eq.6-7 with Eq.3):
@@ -138,10 +148,13 @@ sla_status_t sla_fwd(const sla_problem_t *p, const void *q, int64_t ldq, const v
  * over visible pairs only.  dq/dk/dv may be strided column blocks of one
  * buffer (no concatenation needed, ULTRA-HSTU paper section 4.2.2).  Every
  * output row is written (zero where a token sees / is seen by nothing).  No
- * atomics: dK/dV are owned by key tiles, dQ by row tiles (which recompute S
- * and dO.V^T for their rows); the global-prefix key tiles are split over row
- * chunks whose fp32 partial sums are added in a fixed order, so results are
- * bitwise reproducible run to run.  bf16 path: bf16 MFMA products with fp32
+ * atomics: dK/dV are owned by key tiles, dQ by row tiles; the global-prefix
+ * key tiles are split over row chunks whose fp32 partial sums are added in a
+ * fixed order, so results are bitwise reproducible run to run.  dQ reads the
+ * bf16 dS the dK/dV kernel stored when ws_bytes >= sla_workspace_size(p,
+ * SLA_OP_BWD) includes room for it, and recomputes S and dO.V^T for its
+ * rows when ws_bytes is smaller (at least SLA_OP_BWD_RECOMPUTE's size); the
+ * dS it uses is the same bf16 rounding either way.  bf16 path: bf16 MFMA products with fp32
  * accumulation; P and dS enter the dV, dK and dQ products rounded to bf16,
  * except on key tiles that hold global-prefix keys (j < K2e), whose dV and dK
  * sums run over every later row: there P and dS enter as the sum of two bf16
@@ -154,13 +167,15 @@ sla_status_t sla_bwd(const sla_problem_t *p, const void *q, int64_t ldq, const v
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, serving loops or harnesses that forbid allocation): sla_bwd with
- * the same arguments, kernels and results, minus the workspace.  Its
+ * the same arguments, kernels and results as sla_bwd given a workspace of
+ * SLA_NOALLOC_SCRATCH_BYTES, minus the workspace argument (so dS is stored
+ * where its room fits in that size, and recomputed by dQ otherwise).  Its
  * workspace is a static device array of SLA_NOALLOC_SCRATCH_BYTES (64 MiB)
  * that the library holds on each device it runs on until the process ends
  * (its address is looked up on the first call on each device).  The call
  * allocates and frees nothing.  A problem whose sla_workspace_size(p,
- * SLA_OP_BWD) exceeds the array -> SLA_ERR_WORKSPACE (about 117K tokens with a
- * one-tile global prefix at H = 4, d = 128).  Every call on one device shares
+ * SLA_OP_BWD_RECOMPUTE) exceeds the array -> SLA_ERR_WORKSPACE (about 117K
+ * tokens with a one-tile global prefix at H = 4, d = 128).  Every call on one device shares
  * that device's array and leaves its contents behind; nothing in it needs to
  * start at zero, but calls that overlap on one device (two streams, two
  * threads) race on it and must be serialised by the caller.  Other errors as
@@ -175,10 +190,11 @@ sla_status_t sla_bwd_noalloc(const sla_problem_t *p, const void *q, int64_t ldq,
  *   sla_bwd_stage(SLA_BWD_PREPARE)  tile schedule (workspace)
  *   sla_bwd_stage(SLA_BWD_DKDV)     dK, dV (key-tile kernel + prefix reduce)
  *   sla_bwd_stage(SLA_BWD_DQ)       dQ (row-tile kernel)
- * with identical arguments and workspace; PREPARE first, then DKDV and DQ in
- * either order (they only read the schedule).  A stage ignores the output
- * pointers it does not write (they may be NULL).  SLA_BWD_ALL runs all
- * three. */
+ * with identical arguments and workspace; PREPARE first, then DKDV, then DQ
+ * (with the stored-dS workspace DQ reads the dS that DKDV wrote; with the
+ * recompute workspace the two only read the schedule and may run in either
+ * order).  A stage ignores the output pointers it does not write (they may
+ * be NULL).  SLA_BWD_ALL runs all three. */
 enum { SLA_BWD_ALL = 0, SLA_BWD_PREPARE = 1, SLA_BWD_DKDV = 2, SLA_BWD_DQ = 3 };
 sla_status_t sla_bwd_stage(const sla_problem_t *p, int stage, const void *q, int64_t ldq,
                            const void *k, int64_t ldk, const void *v, int64_t ldv,
@@ -215,6 +231,18 @@ sla_status_t sla_schedule(const sla_problem_t *p, int op, int32_t *records, int6
  * returns the number of records, or -1 on invalid input. */
 int64_t sla_schedule_host(const sla_problem_t *p, int op, const int64_t *offsets_host,
                           const int32_t *num_targets_host, int32_t *records, int64_t capacity);
+
+/* The dS blocks the backward stores with the stored-dS workspace (one head's
+ * worth; the same for every head), from HOST copies of offsets [B+1] and
+ * num_targets [B] (nullable): for each sequence b and each 128-key tile in
+ * key order, the 64-row steps of the rows that see the tile (history steps
+ * from row 0, then target steps from the first target row), as int64 triples
+ * (b, first row of the step, first key of the tile) in block order.  These
+ * are exactly the (64-row step, 128-key tile) pairs holding a visible pair.
+ * Writes at most `capacity` triples (blocks may be NULL to count only) and
+ * returns the number of blocks, or -1 on invalid input. */
+int64_t sla_ds_blocks_host(const sla_problem_t *p, const int64_t *offsets_host,
+                           const int32_t *num_targets_host, int64_t *blocks, int64_t capacity);
 
 /* Useful work: number of visible (row, key) pairs per head, summed over the
  * batch, from HOST copies of offsets [B+1] and num_targets [B] (nullable).

@@ -4,12 +4,12 @@ layer around it and attention truncation, as hand-written HIP kernels behind a
 C ABI (include/sla.h).  This package is the Python binding of that library.
 """
 from ._capi import (  # noqa: F401
-    SLAError, SLA_OP_FWD, SLA_OP_BWD, SLA_SCHED_RECORD_INTS, SLA_BWD_ALL, SLA_BWD_PREPARE,
+    SLAError, SLA_OP_FWD, SLA_OP_BWD, SLA_OP_BWD_RECOMPUTE, SLA_NOALLOC_SCRATCH_BYTES, SLA_SCHED_RECORD_INTS, SLA_BWD_ALL, SLA_BWD_PREPARE,
     SLA_BWD_DKDV, SLA_BWD_DQ,
 )
 from .config import STUConfig  # noqa: F401
 from .ops import (  # noqa: F401
-    sla_fwd, sla_fwd_candidates, sla_bwd, sla_bwd_noalloc, sla_attention, sla_schedule, sla_schedule_host, schedule_tile, count_pairs_host,
+    sla_fwd, sla_fwd_candidates, sla_bwd, sla_bwd_noalloc, sla_attention, sla_schedule, sla_schedule_host, schedule_tile, count_pairs_host, ds_blocks_host,
     probe_issue_rates,
     probe_mfma_peak,
     stu_layer_fwd, stu_layer_bwd, stu_layer_workspace_bytes, stu_quantize_rows_fp8,

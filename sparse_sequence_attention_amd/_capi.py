@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "libsla_mi355x.so")
 SLA_OK, SLA_ERR_NULL, SLA_ERR_INVALID, SLA_ERR_UNSUPPORTED, SLA_ERR_WORKSPACE, SLA_ERR_HIP, \
     SLA_ERR_DEVICE = range(7)
 SLA_F32, SLA_BF16 = 0, 1
-SLA_OP_FWD, SLA_OP_BWD = 0, 1
+SLA_OP_FWD, SLA_OP_BWD, SLA_OP_BWD_RECOMPUTE = 0, 1, 2
 SLA_SCHED_RECORD_INTS = 12
 SLA_BWD_ALL, SLA_BWD_PREPARE, SLA_BWD_DKDV, SLA_BWD_DQ = 0, 1, 2, 3
 SLA_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
@@ -25,7 +25,7 @@ STU_REUSE_SCHEDULE = 1
 EXPORTS = (
     "sla_workspace_size", "sla_fwd", "sla_fwd_candidates_workspace_size",
     "sla_fwd_candidates", "sla_bwd", "sla_bwd_noalloc", "sla_bwd_stage", "sla_schedule_capacity", "sla_schedule_tile",
-    "sla_schedule", "sla_schedule_host", "sla_count_pairs_host", "stu_layer_workspace_size", "stu_layer_fwd",
+    "sla_schedule", "sla_schedule_host", "sla_ds_blocks_host", "sla_count_pairs_host", "stu_layer_workspace_size", "stu_layer_fwd",
     "stu_layer_bwd_workspace_size", "stu_layer_bwd", "stu_quantize_rows_fp8",
     "stu_layer_fp8_workspace_size", "stu_layer_fwd_fp8", "stu_gather_targets", "stu_truncate", "stu_truncate_bwd", "sla_probe_scratch_size",
     "sla_probe_mfma_peak", "sla_probe_issue_rates", "sla_status_string",
@@ -106,6 +106,8 @@ def load(path: str = LIB_PATH):
         lib.sla_schedule.restype = ctypes.c_int
         lib.sla_schedule_host.argtypes = [PP, ctypes.c_int, P, P, P, i64]
         lib.sla_schedule_host.restype = i64
+        lib.sla_ds_blocks_host.argtypes = [PP, P, P, P, i64]
+        lib.sla_ds_blocks_host.restype = i64
         lib.sla_count_pairs_host.argtypes = [i32, P, P, i32, i32, i32]
         lib.sla_count_pairs_host.restype = i64
         DBL = ctypes.POINTER(ctypes.c_double)

@@ -161,16 +161,45 @@ WsLayout layout(const sla_problem_t *p, int op)
     const size_t sched_bytes = sizeof(int32_t) * (4 * (size_t)(B + 1) + (size_t)B);
     w.part_off = round_up(sched_bytes, 256);
     size_t part_bytes = 0;
-    if (op == SLA_OP_BWD)
+    if (op == SLA_OP_BWD || op == SLA_OP_BWD_RECOMPUTE)
         part_bytes = (size_t)w.part_slots * p->num_heads * BWD_BN * (size_t)(p->d_qk + p->d_v) *
                      sizeof(float);
     w.total = w.part_off + round_up(part_bytes, 256);
+    if (op != SLA_OP_BWD || p->dtype != SLA_BF16 || p->d_qk < 64) return w;
+    // Stored dS: an upper bound of the 64-row steps over all key tiles, per
+    // head, from host-known sizes only.  Key tiles: sum ceil(L/128) <= T/128 +
+    // B; a window tile is seen by at most ceil((127 + K1) / 64) steps, a
+    // global-prefix tile by every history step (sum ceil(L/64) <= T/64 + B);
+    // with targets, a tile in the window of the first target slot or the
+    // prefix is seen by every target step, any other by at most 3 steps of
+    // its own targets.
+    const int64_t tiles = T / BWD_BN + B, rsteps = T / BWD_BM + B;
+    int64_t win = ((int64_t)p->k1 + BWD_BN - 1 + BWD_BM - 1) / BWD_BM;
+    if (win > rsteps) win = rsteps;
+    const int64_t npre = (K2e + BWD_BN - 1) / BWD_BN;
+    int64_t blocks = tiles * win + npre * rsteps;
+    if (p->num_targets) {
+        int64_t kt = ((int64_t)p->k1 + BWD_BN - 1) / BWD_BN + 1;
+        if (kt > tiles) kt = tiles;
+        blocks += (npre + kt) * rsteps + 3 * tiles;
+    }
+    // only where dS costs at most 16 times the bytes of Q, K, V and dO
+    const double in_bytes = 4.0 * (double)T * p->num_heads * (p->d_qk + p->d_v);
+    const double ds_bytes = (double)blocks * p->num_heads * DS_BLOCK_BYTES;
+    if (T == 0 || ds_bytes > 16.0 * in_bytes || blocks > INT32_MAX / 2) return w;
+    w.ds_blocks = blocks;
+    w.ktile_off = w.total;
+    w.dsb_off = w.ktile_off + round_up(sizeof(int32_t) * (size_t)(B + 1), 256);
+    w.ds_off = w.dsb_off + round_up(sizeof(int32_t) * (size_t)(tiles + 1), 256);
+    w.total = w.ds_off + (size_t)blocks * p->num_heads * DS_BLOCK_BYTES;
     return w;
 }
 
 sla_status_t make_params(const sla_problem_t *p, int op, void *ws, size_t ws_bytes, AttnParams &a)
 {
-    const WsLayout w = layout(p, op);
+    // the backward stores dS when the workspace holds it, else dQ recomputes
+    WsLayout w = layout(p, op);
+    if (op == SLA_OP_BWD && ws_bytes < w.total) w = layout(p, SLA_OP_BWD_RECOMPUTE);
     if (!ws) return fail(SLA_ERR_WORKSPACE, "workspace is NULL");
     if (ws_bytes < w.total)
         return fail(SLA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", ws_bytes, w.total);
@@ -201,6 +230,13 @@ sla_status_t make_params(const sla_problem_t *p, int op, void *ws, size_t ws_byt
     a.s.nch = s + 4 * B1;
     a.T = p->total_tokens;
     a.partials = reinterpret_cast<float *>(static_cast<char *>(ws) + w.part_off);
+    if (w.ds_blocks > 0) {
+        char *base = static_cast<char *>(ws);
+        a.s.ktile_base = reinterpret_cast<int32_t *>(base + w.ktile_off);
+        a.s.ds_base = reinterpret_cast<int32_t *>(base + w.dsb_off);
+        a.ds = reinterpret_cast<uint8_t *>(base + w.ds_off);
+        a.ds_head_blocks = w.ds_blocks;
+    }
     a.grid_fwd = (int)(w.fwd_items * H);
     a.grid_bwd = (int)(w.bwd_items * H);
     a.grid_red = (int)(w.red_items * H);
@@ -380,7 +416,7 @@ const char *sla_last_error(void) { return g_last_error.c_str(); }
 size_t sla_workspace_size(const sla_problem_t *p, int op)
 {
     if (validate_problem(p) != SLA_OK) return 0;
-    if (op != SLA_OP_FWD && op != SLA_OP_BWD) return 0;
+    if (op != SLA_OP_FWD && op != SLA_OP_BWD && op != SLA_OP_BWD_RECOMPUTE) return 0;
     return layout(p, op).total;
 }
 
@@ -453,6 +489,44 @@ int64_t sla_schedule_host(const sla_problem_t *p, int op, const int64_t *offsets
         for (int li = 0; li < items; ++li, ++n) {
             if (records && n < capacity)
                 fill_record(op, b, L, U, p->k1, K2e, li, records + n * SLA_SCHED_RECORD_INTS);
+        }
+    }
+    return n;
+}
+
+int64_t sla_ds_blocks_host(const sla_problem_t *p, const int64_t *offsets_host,
+                           const int32_t *num_targets_host, int64_t *blocks, int64_t capacity)
+{
+    if (!p) return fail(SLA_ERR_NULL, "problem is NULL"), -1;
+    sla_problem_t hp = *p;  // the device pointers are not used here
+    hp.offsets = offsets_host;
+    hp.num_targets = num_targets_host;
+    p = &hp;
+    if (validate_problem(p) != SLA_OK) return -1;
+    if (p->batch > 0 && !offsets_host) {
+        fail(SLA_ERR_NULL, "offsets_host is NULL");
+        return -1;
+    }
+    const int K2e = k2_eff(p);
+    int64_t n = 0;
+    for (int b = 0; b < p->batch; ++b) {
+        const int64_t L64 = offsets_host[b + 1] - offsets_host[b];
+        const int64_t nt = num_targets_host ? num_targets_host[b] : 0;
+        if (L64 < 0 || L64 >= ((int64_t)1 << 30) || nt < 0 || nt > L64) {
+            fail(SLA_ERR_INVALID, "sequence %d: bad length or target count", b);
+            return -1;
+        }
+        const int L = (int)L64, U = (int)(L64 - nt);
+        for (int c0 = 0; c0 < L; c0 += BWD_BN) {
+            const TileSteps ts = tile_steps(L, U, p->k1, K2e, c0, std::min(c0 + BWD_BN, L), BWD_BM);
+            for (int s = 0; s < ts.nh + ts.nt; ++s, ++n) {
+                if (!blocks || n >= capacity) continue;
+                const int64_t m0 = s < ts.nh ? (int64_t)(ts.h_first + s) * BWD_BM
+                                             : U + (int64_t)(ts.t_first + s - ts.nh) * BWD_BM;
+                blocks[3 * n] = b;
+                blocks[3 * n + 1] = m0;
+                blocks[3 * n + 2] = c0;
+            }
         }
     }
     return n;

@@ -74,7 +74,9 @@ __device__ __forceinline__ bf16x8 lo_part(const float *x, const bf16x8 &hi)
 }
 
 // DQK: the Q / K (and dK) head width, DV: the V, dO (and dV) width.
-template <int DQK, int DV, bool OUTF32>
+// STORE_DS: also write the bf16 dS of every step (the operand of the dK
+// product, as each wave holds it) for the dQ kernel to read back.
+template <int DQK, int DV, bool OUTF32, bool STORE_DS>
 __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(AttnParams p)
 {
     constexpr int BN = BWD_BN, BM = BWD_BM;
@@ -138,6 +140,21 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
         nt = cdiv(it.tb - sd.U, BM) - t_first;
     }
     const int nsteps = uniform(nh + nt);
+    // Stored dS: the blocks of a key tile are its 64-row steps over all its
+    // chunks, history steps first; item step t is block t + ds_dh (history)
+    // or t + ds_dt (targets) of the tile.  Wave wv writes bytes
+    // 2048 wv .. + 2048 of a block: for h2 = 0, 1, lane l's 16 bytes at
+    // 1024 h2 + 16 l (the bf16 A fragment of its dK product).
+    uint8_t *ds_wave = nullptr;
+    int ds_dh = 0, ds_dt = 0;
+    if constexpr (STORE_DS) {
+        const TileSteps ts = tile_steps(sd.L, sd.U, p.k1, p.k2e, it.c0, it.c1, BM);
+        const int gtile = uniform(p.s.ktile_base[b]) + it.c0 / BN;
+        const int64_t blk0 = (int64_t)h * p.ds_head_blocks + uniform(p.s.ds_base[gtile]);
+        ds_dh = uniform(h_first - ts.h_first);
+        ds_dt = uniform(ts.nh + t_first - nh - ts.t_first);
+        ds_wave = p.ds + blk0 * DS_BLOCK_BYTES + wv * 2048;
+    }
     auto step_rows = [&](int s, int &m0, int &m1) __attribute__((always_inline)) {
         const bool hist = s < nh;
         m0 = hist ? (h_first + s) * BM : sd.U + (t_first + s - nh) * BM;
@@ -378,6 +395,11 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
                                    pv[o + 6], pv[o + 7]);
             const bf16x8 da = cvt8(dv[o], dv[o + 1], dv[o + 2], dv[o + 3], dv[o + 4], dv[o + 5],
                                    dv[o + 6], dv[o + 7]);
+            if constexpr (STORE_DS) {
+                const int blk = t + (t < nh ? ds_dh : ds_dt);
+                uint8_t *dst = ds_wave + (int64_t)blk * DS_BLOCK_BYTES + 1024 * h2 + 16 * lane;
+                st16_global(dst, as_u4(da));
+            }
             bf16x8 pl, dl;
             if constexpr (split) {
                 pl = lo_part(pv + o, pa);
@@ -599,8 +621,12 @@ static hipError_t launch_dkdv_o(const AttnParams &p, hipStream_t st)
 {
     return with_head_dims(p, [&](auto QK, auto V) {
         constexpr int DQK = decltype(QK)::value, DV = decltype(V)::value;
-        hipLaunchKernelGGL((sla_bwd_dkdv_bf16_kernel<DQK, DV, OUTF32>), dim3(p.grid_bwd),
-                           dim3(DKDV_THREADS), 0, st, p);
+        if (p.ds)
+            hipLaunchKernelGGL((sla_bwd_dkdv_bf16_kernel<DQK, DV, OUTF32, true>),
+                               dim3(p.grid_bwd), dim3(DKDV_THREADS), 0, st, p);
+        else
+            hipLaunchKernelGGL((sla_bwd_dkdv_bf16_kernel<DQK, DV, OUTF32, false>),
+                               dim3(p.grid_bwd), dim3(DKDV_THREADS), 0, st, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || p.grid_red == 0) return e;
         hipLaunchKernelGGL((sla_bwd_reduce_kernel<DQK, DV, OUTF32>),

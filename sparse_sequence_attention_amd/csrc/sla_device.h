@@ -159,6 +159,33 @@ __device__ __forceinline__ uint2 tr_read_b64(const uint16_t *lds_run)
 
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 
+// Scalar load of a workgroup-uniform int32 that no kernel running alongside
+// writes (a table the schedule kernel filled before this launch).  The
+// compiler cannot use a scalar load for global memory that the kernel itself
+// stores to, and its vector load would come with a wait for every vector
+// memory operation in flight, DMA included; this one waits for the scalar
+// load alone, in the same statement.
+__device__ __forceinline__ int sload_i32(const int32_t *ptr)
+{
+    const uint64_t a = (uint64_t)(uintptr_t)ptr;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint64_t sa = ((uint64_t)hi << 32) | lo;
+    int v;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(sa));
+    return v;
+}
+
+// 16-byte store through a global-address-space pointer (global_store_dwordx4;
+// a generic pointer would give a flat store, which the LDS wait counter
+// tracks too).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st16_global(void *p, const uint4 &v)
+{
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    *(__attribute__((address_space(1))) u32x4 *)p = w;
+}
+
 // 16 bytes at column `col` of row r of a [rows][ld] bf16 tensor, zero when
 // r >= limit.  The load itself is unconditional (row clamped to limit-1, which
 // the caller guarantees is >= 0) so it stays one 16-byte load; the zeroing is

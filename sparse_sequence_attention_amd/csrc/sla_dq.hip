@@ -7,11 +7,11 @@
 //   g_ij  = dO_i . v_j
 //   dS_ij = (alpha / N) g_ij sigma_ij (1 + t_ij (1 - sigma_ij)),  t = alpha s
 //   dQ_i  = sum_j dS_ij k_j.
-// The kernel recomputes s and g for its row tile rather than reading dS
-// stored by the key-tile (dK/dV) kernel: recomputing costs two more products
-// per pair, storing costs 2 bytes per pair written and read back through HBM
-// (about a gigabyte at 16K-token histories), and the stores would sit in the
-// dK/dV kernel's DMA wait counts.
+// Two kernels.  The first recomputes s and g for its row tile: the path of a
+// workspace without room for dS.  The second (further down) reads the bf16
+// dS that the key-tile (dK/dV) kernel stored: 2 bytes per pair written and
+// read back through HBM (about a gigabyte at 16K-token histories) in place
+// of two products and the SiLU' arithmetic per pair.
 //
 // Work item: one row tile of up to 128 rows (4 waves x 32) of one head, two
 // workgroups per CU, over the same key tiles as the forward (prefix, band, and
@@ -276,11 +276,270 @@ __global__ __launch_bounds__(256, 2) void sla_bwd_dq_kernel(AttnParams p)
     }
 }
 
+// dQ from stored dS.  When the workspace holds it, the dK/dV kernel writes the
+// bf16 dS of each 64-row step x 128-key tile it visits (the operand of its dK
+// product: per wave of 32 rows x 32 keys, lane (hl, key) holds the 8 rows
+// 16 h2 + 8 (s / 4) + 4 hl + s % 4, s = 0..7, for h2 = 0, 1), and this
+// kernel reads those blocks instead of recomputing S, dO.V^T and SiLU': per
+// pair 2 bytes read back against 4 d flops and two transcendentals.  The
+// fragment has the keys in the lane dimension; dQ contracts over keys, so
+// the kernel turns it around with two MFMAs against a 0/1 identity (exact:
+// one product of a bf16 value by 1 per output, the rest zeros), which leaves
+// dS^T with the rows in the lane dimension, the B operand layout of
+//   dQ^T (D x 32 rows) += K^T dS^T        (as the recomputing kernel).
+// Same work items (128-row tiles), key tiles and order as the recomputing
+// kernel, and each dQ accumulator adds the same products in the same order,
+// so the two kernels give the same bits.  A 64-row half of the row tile that
+// the dK/dV schedule does not visit for a key tile sees none of its keys and
+// is skipped.
+//
+// The dS stream comes from HBM (no reuse), so the kernel keeps several steps
+// in flight: one workgroup of eight waves per CU, a ring of four stages of
+// [K rows | dS] (16 + 16 KB at d = 128) filled by DMA three steps ahead,
+// with the wait counts of the dK/dV kernel (gl_lds16_async: the DMA is
+// ordered by the kernel's own waits and barriers).  Wave w takes rows
+// 32 (w % 4) .. + 32 of the row tile and the d blocks of half w / 4 of dQ.
+// Needs d_qk >= 64 (two 32-wide halves).
+constexpr int DQS_THREADS = 512;
+constexpr int DQS_STAGES = 4;
+constexpr int DQS_TABLE = 256;  // step table entries (two halves of 128)
+
+template <int DQK, bool OUTF32>
+__global__ __launch_bounds__(DQS_THREADS, 1) void sla_bwd_dq_stored_kernel(AttnParams p)
+{
+    constexpr int BM = FWD_BM, BN = FWD_BN;
+    constexpr int NT = DQS_THREADS, NST = DQS_STAGES;
+    constexpr int NDB = DQK / 32, NDBW = NDB / 2;  // 32-wide d blocks: all, per wave
+    constexpr int CPR = DQK / 8;                   // 16-byte chunks per K row
+    constexpr int TCH = BN * CPR;                  // chunks of a 64-key K tile
+    constexpr int DCH = 1024;                      // chunks of a step's dS (16 KB)
+    constexpr int SPS = (TCH + DCH) / NT;          // DMA loads per thread and step
+    constexpr int STAGE = (TCH + DCH) * 8;         // elements of a stage: [K | dS]
+    static_assert(BN == 64 && BM == 128 && BWD_BN == 128 && BWD_BM == 64,
+                  "64-key steps over 128-row tiles; dS blocks of 64 rows x 128 keys");
+    static_assert(NDB >= 2 && TCH % 128 == 0 && (TCH + DCH) % NT == 0 && SPS <= 8 && NST == 4,
+                  "two d halves; the K / dS split is wave-uniform; whole DMA rounds; a ring of 4");
+    __shared__ __align__(16) uint16_t lds[NST * STAGE];
+    // Step table: {first key, dS block of row half 0, of row half 1 (-1: not
+    // visited)} of steps t, entry t % DQS_TABLE, filled 128 steps at a time
+    // by vector code (one entry per lane) so that the per-step scalar work
+    // stays small: the CU's one scalar unit serves all eight waves.
+    __shared__ int4 stab[DQS_TABLE];
+
+    const int nrec = p.s.fwd_base[p.B];
+    const int item = xcd_remap(blockIdx.x, nrec * p.H);
+    if (item < 0) return;
+    const int h = item / nrec;
+    const int rec = item - h * nrec;
+    const int b = find_seq(p.s.fwd_base, p.B, rec);
+    const SeqDims sd = seq_dims(p.offsets, p.num_targets, b);
+    int r0, r1;
+    row_tile(sd.L, sd.U, BM, rec - uniform(p.s.fwd_base[b]), r0, r1);
+    r0 = uniform(r0);
+    r1 = uniform(r1);
+    const Ranges kr = fwd_key_ranges(sd.L, sd.U, p.k1, p.k2e, r0, r1, BN);
+    const int kt_base = uniform(p.s.ktile_base[b]);
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
+    const int rb = wv & 3, dh = wv >> 2;  // 32-row block, d half
+    const int l32 = lane & 31, hl = lane >> 5;
+    const int qi = r0 + 32 * rb + l32;
+    const uint16_t *kg = reinterpret_cast<const uint16_t *>(p.k) + sd.base * p.ldk + h * DQK;
+
+    const TileCursor cur(kr, BN);
+    const int ntiles = uniform(cur.total);
+
+    // Entry of step t: its first key c0, and for row half sg (rows r0 + 64 sg
+    // ..) the dS block of the pair (row half, 128-key tile holding c0) within
+    // this head's blocks, or -1 when the dK/dV schedule does not visit it
+    // (ds_block_in_tile: the closed form of the schedule's step numbering).
+    const int k1c = imin(p.k1, sd.U);
+    auto fill = [&](int t0) __attribute__((always_inline)) {
+        if (tid < DQS_TABLE / 2) {
+            const int t = t0 + tid;
+            int4 e = make_int4(0, -1, -1, 0);
+            if (t < ntiles) {
+                const int c0 = cur.start(t, BN);
+                const int ct = c0 & ~(BWD_BN - 1);
+                const int tb = p.s.ds_base[kt_base + (ct >> 7)];
+                const int s0 = ds_block_in_tile(sd.L, sd.U, p.k1, k1c, p.k2e, ct, r0);
+                const int s1 = r0 + 64 < r1
+                                   ? ds_block_in_tile(sd.L, sd.U, p.k1, k1c, p.k2e, ct, r0 + 64)
+                                   : -1;
+                e = make_int4(c0, s0 < 0 ? -1 : tb + s0, s1 < 0 ? -1 : tb + s1, 0);
+            }
+            stab[t & (DQS_TABLE - 1)] = e;
+        }
+    };
+    const char *const ds_head = reinterpret_cast<const char *>(p.ds) +
+                                (int64_t)h * p.ds_head_blocks * DS_BLOCK_BYTES;
+
+    // 0/1 identity B operands: lane (hl, n = l32) holds k-slot 8 hl + s, the
+    // fragment row 16 h2 + 8 (s / 4) + 4 hl + s % 4, as 1 when that row is n
+    bf16x8 id0, id1;
+    {
+        uint32_t e0[4], e1[4];
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+            e0[w2] = e1[w2] = 0;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int s2 = 2 * w2 + half;
+                const int row = 8 * (s2 >> 2) + 4 * hl + (s2 & 3);
+                e0[w2] |= (row == l32 ? 0x3F80u : 0u) << (16 * half);
+                e1[w2] |= (row + 16 == l32 ? 0x3F80u : 0u) << (16 * half);
+            }
+        }
+        id0 = as_bf16x8(make_uint4(e0[0], e0[1], e0[2], e0[3]));
+        id1 = as_bf16x8(make_uint4(e1[0], e1[1], e1[2], e1[3]));
+    }
+
+    floatx16 dqacc[NDBW];
+#pragma unroll
+    for (int i = 0; i < NDBW; ++i) dqacc[i] = zero16();
+
+    // DMA of key step t (clamped to the last) into stage t % NST.  Chunk
+    // P = i NT + tid: below TCH the K rows (as the recomputing kernel: chunk P
+    // of the tile is physical chunk P % CPR of row P / CPR holding logical
+    // chunk (P % CPR) ^ qswz(row); keys at or past L read key L - 1), then the
+    // dS: fragment f = (P - TCH) / 128 of the stage (row half f / 4, 32-row
+    // block (f / 2) % 2, 32-key block f % 2), 2 KB each, from its block; a
+    // fragment of an unvisited pair reads the head's first block and is not
+    // used.  Every step issues SPS loads per thread.  The per-lane parts of
+    // the addresses are fixed for the item; the step adds its key offset and
+    // the two blocks.  Returns the two coverage bits of the step.
+    const uint32_t ldk_b = (uint32_t)p.ldk * 2u;
+    uint32_t kprow[SPS], kcol[SPS], dlane[SPS], dfrag[SPS];
+    bool dhalf1[SPS];
+#pragma unroll
+    for (int i = 0; i < SPS; ++i) {
+        const int P = i * NT + wv * 64 + lane;
+        kprow[i] = (uint32_t)(P / CPR);
+        kcol[i] = 16u * (uint32_t)((P % CPR) ^ qswz<DQK>(P / CPR));
+        const int f = imax(i * NT + wv * 64 - TCH, 0) / 128;  // wave-uniform
+        dlane[i] = 16u * (uint32_t)(P & 127);
+        dfrag[i] = (uint32_t)(4 * ((f >> 1) & 1) + (f & 1)) * 2048u;
+        dhalf1[i] = f >= 4;
+    }
+    auto issue = [&](int t) __attribute__((always_inline)) -> uint32_t {
+        const int4 e = stab[imin(t, ntiles - 1) & (DQS_TABLE - 1)];
+        const int c0 = uniform(e.x), blk0 = uniform(e.y), blk1 = uniform(e.z);
+        const uint32_t last = (uint32_t)(sd.L - 1 - c0);
+        const char *krow = reinterpret_cast<const char *>(kg + (int64_t)c0 * p.ldk);
+        const uint32_t kwo = (uint32_t)(c0 & (BWD_BN - 1)) * 64u;  // (key block of c0) x 2 KB
+        const char *b0 = ds_head + (blk0 < 0 ? 0 : (int64_t)blk0 * DS_BLOCK_BYTES + kwo);
+        const char *b1 = ds_head + (blk1 < 0 ? 0 : (int64_t)blk1 * DS_BLOCK_BYTES + kwo);
+        uint16_t *sb = lds + (t & (NST - 1)) * STAGE;
+#pragma unroll
+        for (int i = 0; i < SPS; ++i) {
+            const char *src;
+            if ((TCH % NT == 0) ? (i * NT < TCH) : (i * NT + wv * 64 < TCH))
+                src = krow + ((kprow[i] < last ? kprow[i] : last) * ldk_b + kcol[i]);
+            else
+                src = (dhalf1[i] ? b1 : b0) + (dfrag[i] + dlane[i]);
+            gl_lds16_async(src, sb + (i * NT + wv * 64) * 8);
+        }
+        return (blk0 >= 0 ? 1u : 0u) | (blk1 >= 0 ? 2u : 0u);
+    };
+
+    // K^T operand by transposing reads, as the recomputing kernel
+    const int q4 = lane >> 4, j16 = lane & 15;
+    auto t_off = [&](int kb, int h2, int rr, int db) {
+        const int row = 32 * kb + 16 * h2 + 8 * rr + 4 * (q4 >> 1) + (j16 >> 2);
+        const int col = 32 * db + 16 * (q4 & 1) + 4 * (j16 & 3);
+        return row * DQK + 8 * ((col >> 3) ^ qswz<DQK>(row)) + (col & 7);
+    };
+
+    if (ntiles > 0) {
+        fill(0);
+        fill(DQS_TABLE / 2);
+        __syncthreads();
+        // coverage bits of the steps in flight: 2 bits per stage
+        uint32_t vis = 0;
+#pragma unroll
+        for (int i = 0; i < NST - 1; ++i) vis |= issue(i) << (2 * i);
+        for (int t = 0; t < ntiles; ++t) {
+            // step t's DMA has landed (the newest (NST - 2) SPS loads, those of
+            // steps t + 1 .., may still be in flight); the barrier publishes it
+            // and frees stage (t + NST - 1) % NST, read by step t - 1
+            vm_wait<(NST - 2) * SPS>();
+            barrier_lds();
+            // entries of steps t + 128 .. t + 255 replace those of steps
+            // t - 128 .., all used by now; first read by the issue of step
+            // t + 128 (loop step t + 125), several barriers later
+            if ((t & (DQS_TABLE / 2 - 1)) == 0 && t > 0 && t + DQS_TABLE / 2 < ntiles)
+                fill(t + DQS_TABLE / 2);
+            const uint32_t sh = 2u * (uint32_t)((t + NST - 1) & (NST - 1));
+            vis = (vis & ~(3u << sh)) | (issue(t + NST - 1) << sh);
+            const uint16_t *sk = lds + (t & (NST - 1)) * STAGE;
+            // this wave's row half sees the step
+            if ((vis >> (2 * (t & (NST - 1)) + (rb >> 1))) & 1u) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const uint16_t *fr = sk + TCH * 8 + (2 * rb + kb) * 1024;
+                    const bf16x8 f0 = *reinterpret_cast<const bf16x8 *>(fr + 8 * lane);
+                    const bf16x8 f1 = *reinterpret_cast<const bf16x8 *>(fr + 512 + 8 * lane);
+                    floatx16 tr = mfma32(f0, id0, zero16());
+                    tr = mfma32(f1, id1, tr);
+                    const bf16x8 d0 = cvt8(tr[0], tr[1], tr[2], tr[3], tr[4], tr[5], tr[6], tr[7]);
+                    const bf16x8 d1 =
+                        cvt8(tr[8], tr[9], tr[10], tr[11], tr[12], tr[13], tr[14], tr[15]);
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+                        for (int dw = 0; dw < NDBW; ++dw) {
+                            const int db = dh * NDBW + dw;
+                            const uint2 k0 = tr_read_b64(sk + t_off(kb, h2, 0, db));
+                            const uint2 k1v = tr_read_b64(sk + t_off(kb, h2, 1, db));
+                            dqacc[dw] = mfma32(
+                                __builtin_bit_cast(bf16x8, make_uint4(k0.x, k0.y, k1v.x, k1v.y)),
+                                h2 ? d1 : d0, dqacc[dw]);
+                        }
+                    }
+                }
+            }
+        }
+        vm_wait<0>();  // no DMA (of the clamped steps past the end) left in flight
+    }
+
+    // epilogue: dQ[qi][d] for d = 32 db + 8 g + 4 hl + 0..3, scaled by alpha / N
+    if (qi < r1) {
+        const float sc = p.out_scale;
+        const int64_t row = sd.base + qi;
+#pragma unroll
+        for (int dw = 0; dw < NDBW; ++dw) {
+            const int db = dh * NDBW + dw;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float o0 = dqacc[dw][4 * g] * sc, o1 = dqacc[dw][4 * g + 1] * sc;
+                const float o2 = dqacc[dw][4 * g + 2] * sc, o3 = dqacc[dw][4 * g + 3] * sc;
+                const int col = h * DQK + 32 * db + 8 * g + 4 * hl;
+                if constexpr (OUTF32) {
+                    float *orow = reinterpret_cast<float *>(p.dq) + row * p.lddq;
+                    *reinterpret_cast<float4 *>(orow + col) = make_float4(o0, o1, o2, o3);
+                } else {
+                    uint16_t *orow = reinterpret_cast<uint16_t *>(p.dq) + row * p.lddq;
+                    *reinterpret_cast<uint2 *>(orow + col) = cvt4_u2(o0, o1, o2, o3);
+                }
+            }
+        }
+    }
+}
+
 template <bool OUTF32>
 static hipError_t launch_dq_o(const AttnParams &p, hipStream_t st)
 {
     return with_head_dims(p, [&](auto QK, auto V) {
-        hipLaunchKernelGGL((sla_bwd_dq_kernel<decltype(QK)::value, decltype(V)::value, OUTF32>),
+        constexpr int DQK = decltype(QK)::value;
+        if constexpr (DQK >= 64) {
+            if (p.ds) {
+                hipLaunchKernelGGL((sla_bwd_dq_stored_kernel<DQK, OUTF32>), dim3(p.grid_fwd),
+                                   dim3(DQS_THREADS), 0, st, p);
+                return hipGetLastError();
+            }
+        }
+        if (p.ds) return hipErrorInvalidValue;  // no stored dS below d_qk = 64
+        hipLaunchKernelGGL((sla_bwd_dq_kernel<DQK, decltype(V)::value, OUTF32>),
                            dim3(p.grid_fwd), dim3(256), 0, st, p);
         return hipGetLastError();
     });

@@ -37,7 +37,14 @@ struct Sched {
     int32_t *red_base;   // [B+1] split key tiles to reduce
     int32_t *part_base;  // [B+1] fp32 partial slots
     int32_t *nch;        // [B]   chunks per prefix key tile (1 = unsplit)
+    // stored-dS backward only (null otherwise):
+    int32_t *ktile_base; // [B+1] key tiles of BWD_BN keys per sequence
+    int32_t *ds_base;    // [key tiles + 1] dS blocks (64-row steps) of each key tile
 };
+
+// One stored dS block: the 64-row step x 128-key tile of one head as the
+// dK/dV kernel's eight waves hold it in registers (bf16 MFMA A fragments).
+constexpr int DS_BLOCK_BYTES = 64 * 128 * 2;
 
 struct SeqDims {
     int64_t base;  // first token of the sequence
@@ -206,6 +213,53 @@ __host__ __device__ inline void bwd_rows(int L, int U, int K1, int K2e, int c0, 
     }
     if (ha >= hb) ha = hb = 0;
     if (ta >= tb) ta = tb = 0;
+}
+
+// The 64-row steps (bm rows, history steps counted from row 0, target steps
+// from row U) of all rows that see the key tile [c0, c1): history steps
+// h_first .. h_first + nh, then target steps t_first .. t_first + nt.  The
+// chunks of a split key tile partition these steps; the stored-dS backward
+// numbers a key tile's blocks in this order.
+struct TileSteps {
+    int h_first, nh, t_first, nt;
+};
+
+__host__ __device__ inline TileSteps tile_steps(int L, int U, int K1, int K2e, int c0, int c1,
+                                                int bm)
+{
+    int ha, hb, ta, tb;
+    bwd_rows(L, U, K1, K2e, c0, c1, ha, hb, ta, tb);
+    TileSteps t{0, 0, 0, 0};
+    if (ha < hb) {
+        t.h_first = ha / bm;
+        t.nh = cdiv(hb, bm) - t.h_first;
+    }
+    if (ta < tb) {
+        t.t_first = (ta - U) / bm;
+        t.nt = cdiv(tb - U, bm) - t.t_first;
+    }
+    return t;
+}
+
+// The index, within key tile [ct, ct + 128)'s blocks (tile_steps order, 64-row
+// steps), of the step that starts at row m0 (history rows from 0, target rows
+// from U, in 64-row steps), or -1 when no row of that step sees the tile: the
+// same numbers as tile_steps, without its general case analysis.  K1c =
+// min(K1, U).
+__host__ __device__ inline int ds_block_in_tile(int L, int U, int K1, int K1c, int K2e, int ct,
+                                                int m0)
+{
+    const int jhi = imin(ct + 128, U) - 1;  // last history key of the tile
+    const bool hk = ct < U;
+    const int hb = !hk ? 0 : (ct < K2e ? U : (K1 < 1 ? 0 : imin(jhi + K1c, U)));
+    if (m0 < U) return (m0 >= ct && m0 < hb) ? (m0 - ct) >> 6 : -1;
+    const int nh = hb > ct ? ((hb + 63) >> 6) - (ct >> 6) : 0;
+    const bool all_t = hk && ((U - jhi < K1) || ct < K2e);
+    const int c1 = imin(ct + 128, L);
+    const int ta = all_t ? U : imax(ct, U);
+    const int tb = all_t ? L : (c1 > U ? c1 : 0);
+    const int tf = (ta - U) >> 6, g = (m0 - U) >> 6;
+    return (ta < tb && g >= tf && m0 < tb) ? nh + g - tf : -1;
 }
 
 // Row tiles (of bm rows, aligned as the forward row tiles) overlapping [a, b),

@@ -31,6 +31,11 @@ struct AttnParams {
     float neg_alpha_log2e;  // -alpha * log2(e)
     Sched s;
     float *partials;        // fp32 partial dK|dV of split prefix key tiles
+    // stored-dS backward (null: dQ recomputes S and dP): the dK/dV kernel
+    // writes each 64-row step x 128-key tile of dS (DS_BLOCK_BYTES, bf16) to
+    // block (h * ds_head_blocks + ds_base[key tile] + step), which dQ reads
+    uint8_t *ds;
+    int64_t ds_head_blocks;
     int grid_fwd;           // upper bound of forward / dQ work items (x heads)
     int grid_bwd;           // upper bound of dK/dV work items (x heads)
     int grid_red;           // upper bound of reduce items (x heads)
@@ -81,6 +86,9 @@ hipError_t with_head_dims(const AttnParams &p, F &&f)
 struct WsLayout {
     size_t sched_off, part_off, total;
     int64_t fwd_items, bwd_items, red_items, part_slots;  // upper bounds (per head)
+    // stored-dS backward (ds_blocks == 0: dQ recomputes S and dP)
+    size_t ktile_off, dsb_off, ds_off;
+    int64_t ds_blocks;  // upper bound of dS blocks per head
 };
 
 hipError_t launch_sched(const AttnParams &p, hipStream_t st);

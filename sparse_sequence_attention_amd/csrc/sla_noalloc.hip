@@ -58,7 +58,7 @@ extern "C" sla_status_t sla_bwd_noalloc(const sla_problem_t *p, const void *q, i
                                         void *dk, int64_t lddk, void *dv, int64_t lddv,
                                         void *stream)
 {
-    const size_t need = sla_workspace_size(p, SLA_OP_BWD);
+    const size_t need = sla_workspace_size(p, SLA_OP_BWD_RECOMPUTE);
     if (need == 0)  // an invalid problem: sla_bwd reports which check failed
         return sla_bwd(p, q, ldq, k, ldk, v, ldv, dout, lddo, dq, lddq, dk, lddk, dv, lddv,
                        nullptr, 0, stream);

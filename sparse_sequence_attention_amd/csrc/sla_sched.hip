@@ -12,9 +12,32 @@ namespace sla {
 
 constexpr int SCHED_THREADS = 1024;
 
+// Exclusive prefix sums of v over the workgroup's threads, continued from
+// *carry (LDS, updated to include this round).  Every thread calls it.
+__device__ inline int block_exclusive_scan(int v, int (*buf)[SCHED_THREADS], int *carry)
+{
+    const int tid = threadIdx.x;
+    int cur = 0;
+    buf[cur][tid] = v;
+    __syncthreads();
+    for (int off = 1; off < SCHED_THREADS; off <<= 1) {
+        int a = buf[cur][tid];
+        if (tid >= off) a += buf[cur][tid - off];
+        buf[cur ^ 1][tid] = a;
+        cur ^= 1;
+        __syncthreads();
+    }
+    const int inc = buf[cur][tid];
+    const int c = *carry;
+    __syncthreads();
+    if (tid == SCHED_THREADS - 1) *carry = c + inc;
+    __syncthreads();
+    return c + inc - v;
+}
+
 __global__ __launch_bounds__(SCHED_THREADS) void sla_sched_kernel(const int64_t *offsets,
                                                                   const int32_t *num_targets,
-                                                                  int B, int k2e, Sched s,
+                                                                  int B, int k1, int k2e, Sched s,
                                                                   const int64_t *cand_offsets)
 {
     __shared__ int4 buf[2][SCHED_THREADS];
@@ -72,12 +95,48 @@ __global__ __launch_bounds__(SCHED_THREADS) void sla_sched_kernel(const int64_t 
         s.red_base[B] = c.z;
         s.part_base[B] = c.w;
     }
+    if (!s.ds_base || cand_offsets) return;
+
+    // Stored-dS backward: key tiles per sequence, then the dS blocks of every
+    // key tile (its 64-row steps, all chunks together), as prefix sums.
+    __shared__ int ibuf[2][SCHED_THREADS];
+    __shared__ int icarry;
+    if (tid == 0) icarry = 0;
+    __syncthreads();
+    for (int start = 0; start < B; start += SCHED_THREADS) {
+        const int b = start + tid;
+        int v = 0;
+        if (b < B) v = cdiv((int)(offsets[b + 1] - offsets[b]), BWD_BN);
+        const int e = block_exclusive_scan(v, ibuf, &icarry);
+        if (b < B) s.ktile_base[b] = e;
+    }
+    const int ntiles = icarry;
+    __syncthreads();  // every thread has read icarry before it is reset
+    if (tid == 0) {
+        s.ktile_base[B] = ntiles;
+        icarry = 0;
+    }
+    __syncthreads();  // ktile_base (global, this workgroup's writes) is read below
+    for (int start = 0; start < ntiles; start += SCHED_THREADS) {
+        const int g = start + tid;
+        int v = 0;
+        if (g < ntiles) {
+            const int b = find_seq<false>(s.ktile_base, B, g);
+            const SeqDims sd = seq_dims<false>(offsets, num_targets, b);
+            const int c0 = (g - s.ktile_base[b]) * BWD_BN;
+            const TileSteps ts = tile_steps(sd.L, sd.U, k1, k2e, c0, imin(c0 + BWD_BN, sd.L), BWD_BM);
+            v = ts.nh + ts.nt;
+        }
+        const int e = block_exclusive_scan(v, ibuf, &icarry);
+        if (g < ntiles) s.ds_base[g] = e;
+    }
+    if (tid == 0) s.ds_base[ntiles] = icarry;
 }
 
 hipError_t launch_sched(const AttnParams &p, hipStream_t st)
 {
     hipLaunchKernelGGL(sla_sched_kernel, dim3(1), dim3(SCHED_THREADS), 0, st, p.offsets,
-                       p.num_targets, p.B, p.k2e, p.s, p.cand_offsets);
+                       p.num_targets, p.B, p.k1, p.k2e, p.s, p.cand_offsets);
     return hipGetLastError();
 }
 

@@ -155,10 +155,15 @@ def sla_fwd_candidates(k_hist: torch.Tensor, v_hist: torch.Tensor, hist_offsets:
 def sla_bwd(q, k, v, dout, offsets, num_targets=None, *, k1: int, k2: int,
             contextual_len: int = 0, max_seq_len: int, alpha: float = 1.0, dq=None, dk=None,
             dv=None, grad_dtype=None, workspace: Optional[torch.Tensor] = None,
-            stage: int = C.SLA_BWD_ALL):
+            stage: int = C.SLA_BWD_ALL, recompute_dq: bool = False):
     """(dQ, dK, dV) of sla_fwd given dO (stage: see sla_bwd_stage in sla.h).
     grad_dtype: torch.float32 writes the gradients in fp32 from bf16 inputs
-    (the dtype of given output tensors decides when grad_dtype is None)."""
+    (the dtype of given output tensors decides when grad_dtype is None).
+    The library stores dS for the dQ kernel when the workspace holds it
+    (sla_workspace_size(SLA_OP_BWD), allocated here by default);
+    recompute_dq=True hands it only the smallest workspace, so dQ recomputes
+    S and dO.V^T instead.  A given workspace is used as it is when it holds
+    at least the smallest one (its size then decides)."""
     T, H, dqk = q.shape
     dvd = v.shape[2]
     ldq = _head_tensor("q", q, T, H, q.dtype, dqk)
@@ -176,11 +181,18 @@ def sla_bwd(q, k, v, dout, offsets, num_targets=None, *, k1: int, k2: int,
     lddv = _head_tensor("dv", dv, T, H, gdt, dvd)
     p = make_problem(q.dtype, offsets, num_targets, T, H, dqk, dvd, k1, k2, contextual_len,
                      max_seq_len, alpha, f32o)
-    nbytes = workspace_size(p, C.SLA_OP_BWD)
-    ws = _workspace(nbytes, q.device, workspace)
+    small = workspace_size(p, C.SLA_OP_BWD_RECOMPUTE)
+    nbytes = small if recompute_dq else workspace_size(p, C.SLA_OP_BWD)
+    if workspace is not None and workspace.numel() * workspace.element_size() >= small:
+        ws = workspace
+    else:
+        ws = _workspace(nbytes, q.device, None)
+    ws_bytes = ws.numel() * ws.element_size()
+    if recompute_dq:
+        ws_bytes = min(ws_bytes, small)
     C.check(C.load().sla_bwd_stage(ctypes.byref(p), stage, _ptr(q), ldq, _ptr(k), ldk, _ptr(v),
                                    ldv, _ptr(dout), lddo, _ptr(dq), lddq, _ptr(dk), lddk,
-                                   _ptr(dv), lddv, _ptr(ws), ws.numel(), _stream(q.device)))
+                                   _ptr(dv), lddv, _ptr(ws), ws_bytes, _stream(q.device)))
     return dq, dk, dv
 
 
@@ -250,6 +262,30 @@ def sla_schedule_host(offsets, num_targets, *, op: int, heads: int, d: int, k1: 
     lib.sla_schedule_host(ctypes.byref(p), op, o.ctypes.data_as(ctypes.c_void_p), tp,
                           rec.ctypes.data_as(ctypes.c_void_p), n)
     return rec[:n]
+
+
+def ds_blocks_host(offsets, num_targets, *, k1: int, k2: int, contextual_len: int = 0):
+    """The stored-dS blocks of one head in block order, from host offsets
+    (numpy int64 [n, 3]: sequence, first row of the 64-row step, first key of
+    the 128-key tile)."""
+    import numpy as np
+    o = np.ascontiguousarray(offsets, dtype=np.int64)
+    t = None if num_targets is None else np.ascontiguousarray(num_targets, dtype=np.int32)
+    p = C.SLAProblem()
+    p.dtype = C.SLA_BF16
+    p.batch = len(o) - 1
+    p.total_tokens = int(o[-1])
+    p.num_heads, p.d_qk, p.d_v = 1, 128, 128
+    p.k1, p.k2, p.contextual_len, p.max_seq_len, p.alpha = int(k1), int(k2), int(contextual_len), 1, 1.0
+    lib = C.load()
+    tp = None if t is None else t.ctypes.data_as(ctypes.c_void_p)
+    n = lib.sla_ds_blocks_host(ctypes.byref(p), o.ctypes.data_as(ctypes.c_void_p), tp, None, 0)
+    if n < 0:
+        raise ValueError(lib.sla_last_error().decode())
+    out = np.zeros((max(n, 1), 3), dtype=np.int64)
+    lib.sla_ds_blocks_host(ctypes.byref(p), o.ctypes.data_as(ctypes.c_void_p), tp,
+                           out.ctypes.data_as(ctypes.c_void_p), n)
+    return out[:n]
 
 
 def schedule_tile(op: int, which: int) -> int:

@@ -1,0 +1,87 @@
+"""The two dQ paths of the bf16 backward: dQ from the dS the dK/dV kernel
+stores (the default workspace) and dQ recomputing S and dO.V^T (the smallest
+workspace).  Both round the same fp32 dS to bf16 (S from Q.K^T equals the
+transpose of K.Q^T bit for bit, and the SiLU' arithmetic is the same) and
+add the same products in the same order, so the two dQ agree bit for bit;
+dK and dV too (the dK/dV kernel only adds the stores).  Against the fp64
+oracle at the raw bar (fp32 gradients from bf16 inputs), the one-key window
+at the storage-aware bar, as in the other backward tests; the staged call
+equals the whole call, and the stored path is reproducible bit for bit.
+Cases: targets, global-prefix key tiles split into row chunks, ragged tails,
+empty sequences, square and rectangular heads."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_sequence_attention_amd as sla
+from synthetic import make_sla_workload
+from tests._helpers import assert_close_bf16, assert_close_raw
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+# lengths, targets, k1, k2, ctx, d_qk, d_v, heads
+CASES = [
+    ([700, 129, 0, 256], [16, 0, 0, 64], 130, 64, 8, 128, 128, 2),
+    ([2500, 600], [0, 16], 300, 128, 16, 128, 128, 2),     # prefix tile split into chunks
+    ([3000, 1], None, 1024, 200, 8, 128, 128, 1),          # two prefix tiles, long window
+    ([513, 64, 1000], [17, 64, 200], 100, 16, 8, 64, 128, 2),
+    ([2200, 300], None, 200, 64, 8, 64, 32, 2),
+    ([700, 129, 1], [8, 0, 0], 96, 16, 4, 32, 64, 3),
+    ([64, 64, 65], [64, 1, 0], 1, 0, 0, 128, 64, 2),       # K1 = 1: the diagonal only
+]
+# one-key window: every gradient element is a single term, so the bf16
+# rounding of P and dS is not averaged out (storage-aware bar)
+RAW_EXEMPT = {6}
+
+
+def _work(case, seed):
+    lens, tg, k1, k2, ctx, dqk, dv, heads = CASES[case]
+    w = make_sla_workload("jagged_2k", seed=seed, lengths=lens, num_targets=tg, heads=heads,
+                          d=dqk, d_v=dv, k1=k1, k2=k2, contextual_len=ctx, max_seq_len=max(lens),
+                          dtype="bf16", with_dout=True)
+    print(f"[case] stored dS {case} lens={lens} tg={tg} k1={k1} k2={k2} dqk={dqk} dv={dv} "
+          f"H={heads}", flush=True)
+    t = lambda a: torch.from_numpy(a).to(DEV).to(torch.bfloat16)  # noqa: E731  (exact)
+    offs = torch.from_numpy(w.offsets).to(DEV)
+    tgd = None if w.num_targets is None else torch.from_numpy(w.num_targets).to(DEV)
+    kw = dict(k1=w.k1, k2=w.k2, contextual_len=w.contextual_len, max_seq_len=w.max_seq_len)
+    return w, (t(w.q), t(w.k), t(w.v), t(w.dout), offs, tgd), kw
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_stored_and_recomputed_dq_match_the_oracle(case):
+    w, (q, k, v, do, offs, tgd), kw = _work(case, 300 + case)
+    st = sla.sla_bwd(q, k, v, do, offs, tgd, grad_dtype=torch.float32, **kw)
+    rc = sla.sla_bwd(q, k, v, do, offs, tgd, grad_dtype=torch.float32, recompute_dq=True, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(st[1], rc[1]) and torch.equal(st[2], rc[2]), "dK/dV differ between modes"
+    assert torch.equal(st[0], rc[0]), \
+        f"dQ differs between modes: max |diff| {(st[0] - rc[0]).abs().max().item():.3e}"
+    rq, rk, rv = oracle.sla_bwd(w.q, w.k, w.v, w.dout, w.offsets, w.num_targets, w.k1, w.k2,
+                                w.contextual_len, w.max_seq_len)
+    check = assert_close_bf16 if case in RAW_EXEMPT else assert_close_raw
+    for name, g, r in (("dQ", st[0], rq), ("dK", st[1], rk), ("dV", st[2], rv)):
+        mx, mn = check(g.cpu().numpy().astype(np.float64), r, name)
+        print(f"  {name}: max {mx:.3e} mean {mn:.3e}", flush=True)
+
+
+def test_stored_dq_stages_and_reproducibility():
+    """PREPARE, DKDV, DQ as separate calls on one workspace equal the whole
+    call; two whole calls agree bit for bit (bf16 gradients)."""
+    w, (q, k, v, do, offs, tgd), kw = _work(1, 320)
+    a = sla.sla_bwd(q, k, v, do, offs, tgd, **kw)
+    b = sla.sla_bwd(q, k, v, do, offs, tgd, **kw)
+    ws = torch.empty(sla.ops.workspace_size(
+        sla.ops.make_problem(q.dtype, offs, tgd, q.shape[0], q.shape[1], q.shape[2], v.shape[2],
+                             kw["k1"], kw["k2"], kw["contextual_len"], kw["max_seq_len"]),
+        sla.SLA_OP_BWD), dtype=torch.uint8, device=DEV)
+    got = tuple(torch.full_like(x, float("nan")) for x in a)
+    for stage in (sla.SLA_BWD_PREPARE, sla.SLA_BWD_DKDV, sla.SLA_BWD_DQ):
+        sla.sla_bwd(q, k, v, do, offs, tgd, dq=got[0], dk=got[1], dv=got[2], workspace=ws,
+                    stage=stage, **kw)
+    torch.cuda.synchronize()
+    for name, x, y, z in zip(("dQ", "dK", "dV"), a, b, got):
+        assert torch.equal(x, y), f"{name}: two calls differ"
+        assert torch.equal(x, z), f"{name}: staged call differs"

@@ -229,15 +229,32 @@ def test_workspace_size_is_host_only(lib):
     assert lib.sla_workspace_size(None, C.SLA_OP_FWD) == 0
 
 
-def test_backward_workspace_holds_only_the_prefix_partials(lib):
-    """The backward adds to the forward's schedule only the fp32 partial dK|dV
-    sums of the split global-prefix key tiles (at most 4 tiles of 128 keys
-    per sequence, 16 chunks each): no per-pair storage."""
+def test_backward_workspace_sizes(lib):
+    """The smallest backward workspace adds to the forward's schedule only the
+    fp32 partial dK|dV sums of the split global-prefix key tiles (at most 4
+    tiles of 128 keys per sequence, 16 chunks each): no per-pair storage.
+    The default bf16 one adds room for the stored dS: 16 KB per 64-row step
+    and 128-key tile and head, bounded from the sizes (at 106,496 tokens in 8
+    sequences, K1 = 1024, K2e = 128: 18 steps per key tile of the window, all
+    history steps for the prefix tile), and none for fp32 inputs or where it
+    would exceed 16 times the inputs' bytes."""
     big = dict(batch=8, total_tokens=106496, k1=1024, k2=128, ctx=16)
     p = _problem(**big)
-    extra = lib.sla_workspace_size(ctypes.byref(p), C.SLA_OP_BWD) - \
-        lib.sla_workspace_size(ctypes.byref(p), C.SLA_OP_FWD)
-    assert 0 < extra <= 8 * 4 * 16 * 4 * 128 * (128 + 128) * 4 + 256
+    fwd = lib.sla_workspace_size(ctypes.byref(p), C.SLA_OP_FWD)
+    small = lib.sla_workspace_size(ctypes.byref(p), C.SLA_OP_BWD_RECOMPUTE)
+    full = lib.sla_workspace_size(ctypes.byref(p), C.SLA_OP_BWD)
+    assert 0 < small - fwd <= 8 * 4 * 16 * 4 * 128 * (128 + 128) * 4 + 256
+    tiles, steps = 106496 // 128 + 8, 106496 // 64 + 8
+    blocks = tiles * 18 + steps
+    assert full - small >= 4 * blocks * 16384
+    assert full - small <= 4 * blocks * 16384 + 4 * (tiles + 9) + 1024
+    p32 = _problem(dtype=C.SLA_F32, **big)
+    assert lib.sla_workspace_size(ctypes.byref(p32), C.SLA_OP_BWD) == \
+        lib.sla_workspace_size(ctypes.byref(p32), C.SLA_OP_BWD_RECOMPUTE)
+    wide = _problem(**dict(big, k1=16384))  # 16K-key windows: dS beyond 16x the inputs
+    assert lib.sla_workspace_size(ctypes.byref(wide), C.SLA_OP_BWD) == \
+        lib.sla_workspace_size(ctypes.byref(wide), C.SLA_OP_BWD_RECOMPUTE)
+    assert lib.sla_workspace_size(ctypes.byref(p), 3) == 0
 
 
 def test_out_f32_flag(lib):
@@ -251,11 +268,11 @@ def test_out_f32_flag(lib):
 
 
 def test_noalloc_backward_rejects_problems_beyond_its_array(lib):
-    """sla_bwd_noalloc checks the workspace its problem needs against its
-    static array on the host, before any HIP call; an invalid problem gets
-    sla_bwd's own error."""
+    """sla_bwd_noalloc checks the smallest backward workspace its problem
+    needs against its static array on the host, before any HIP call; an
+    invalid problem gets sla_bwd's own error."""
     p = _problem(batch=64, total_tokens=1 << 20, k2=128)
-    need = lib.sla_workspace_size(ctypes.byref(p), C.SLA_OP_BWD)
+    need = lib.sla_workspace_size(ctypes.byref(p), C.SLA_OP_BWD_RECOMPUTE)
     assert need > C.SLA_NOALLOC_SCRATCH_BYTES
     args = [FAKE, 512] * 7 + [None]
     assert lib.sla_bwd_noalloc(ctypes.byref(p), *args) == C.SLA_ERR_WORKSPACE
@@ -446,3 +463,88 @@ def test_binding_checks_every_head_width(monkeypatch):
             assert shape[2] == width, (name, shape, width)
             want = 32 if name in ("v", "v_hist", "v_c", "dout", "dv", "out") else 64
             assert width == want, (name, width)
+
+
+def _ws_problem(offs, tg, heads, d, dv, k1, k2, ctx):
+    p = _problem(batch=len(offs) - 1, total_tokens=int(offs[-1]), heads=heads, d=d, dv=dv, k1=k1,
+                 k2=k2, ctx=ctx)
+    if tg is not None:
+        p.num_targets = ctypes.c_void_p(0x30000)  # only its presence counts for the size
+    return p
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_stored_ds_blocks(seed, lib):
+    """The stored-dS blocks: exactly the (64-row step, 128-key tile) pairs of
+    the mask that hold a visible pair (brute force), in the order the dK/dV
+    kernel numbers them (sequence, key tile, history then target steps); the
+    dK/dV items' steps land on distinct blocks of their own tile; a row half
+    of a dQ item that finds no block for a 64-key step sees none of its keys;
+    and the workspace bound holds every block."""
+    rng = np.random.default_rng(700 + seed)
+    lens, offs, tg = _rand_case(rng, max_len=900 if seed % 4 else 2600)
+    k1 = int(rng.choice([0, 1, 2, 5, 64, 130, 256, 1000, FULL_CAUSAL_K1]))
+    k2 = int(rng.choice([0, 3, 64, 128, 200, 300]))
+    ctx = int(rng.choice([0, 2, 16, 150]))
+    blocks = ops.ds_blocks_host(offs, tg, k1=k1, k2=k2, contextual_len=ctx)
+    triples = [tuple(map(int, x)) for x in blocks]
+    assert len(set(triples)) == len(triples)
+    ref = {tuple(map(int, x)) for x in oracle.tiles(offs, tg, k1, k2, ctx, 64, 128)}
+    assert set(triples) == ref
+    U = [L - (tg[b] if tg else 0) for b, L in enumerate(lens)]
+    order = [(b, c0, m0 >= U[b], m0) for b, m0, c0 in triples]
+    assert order == sorted(order)
+    index = {t: i for i, t in enumerate(triples)}
+    first = {}
+    for i, (b, m0, c0) in enumerate(triples):
+        first.setdefault((b, c0), i)
+
+    # dK/dV items: step t of an item is block t + (history ? dh : dt) of its tile
+    recb = ops.sla_schedule_host(offs, tg, op=C.SLA_OP_BWD, heads=1, d=128, k1=k1, k2=k2,
+                                 contextual_len=ctx)
+    written = []
+    for r in recb:
+        b, c0 = int(r[0]), int(r[1])
+        ha, hb, ta, tb = (int(x) for x in r[4:8])
+        h_first = ha // 64 if ha < hb else 0
+        nh = (-(-hb // 64) - h_first) if ha < hb else 0
+        t_first = (ta - U[b]) // 64 if ta < tb else 0
+        nt = (-(-(tb - U[b]) // 64) - t_first) if ta < tb else 0
+        tile = [t for t in triples if t[0] == b and t[2] == c0]
+        th = [t for t in tile if t[1] < U[b]]
+        ts_h_first = th[0][1] // 64 if th else 0
+        ts_nh = len(th)
+        tt = [t for t in tile if t[1] >= U[b]]
+        ts_t_first = (tt[0][1] - U[b]) // 64 if tt else 0
+        for t in range(nh + nt):
+            m0 = (h_first + t) * 64 if t < nh else U[b] + (t_first + t - nh) * 64
+            blk = t + (h_first - ts_h_first if t < nh else ts_nh + t_first - nh - ts_t_first)
+            assert 0 <= blk < len(tile)
+            assert index[(b, m0, c0)] == first[(b, c0)] + blk
+            written.append((b, m0, c0))
+    assert sorted(written) == sorted(triples)
+
+    # dQ items: a row half without a block for a key step sees none of its keys
+    recf = ops.sla_schedule_host(offs, tg, op=C.SLA_OP_FWD, heads=1, d=128, k1=k1, k2=k2,
+                                 contextual_len=ctx)
+    masks = {}
+    for r in recf:
+        b, r0, r1, n = int(r[0]), int(r[1]), int(r[2]), int(r[3])
+        if b not in masks:
+            masks[b] = oracle.mask_dense(lens[b], tg[b] if tg else 0, k1, k2, ctx)
+        for i in range(n):
+            for c0 in range(int(r[4 + 2 * i]), int(r[5 + 2 * i]), 64):
+                for sg in range(2):
+                    m0 = r0 + 64 * sg
+                    if m0 >= r1 or (b, m0, c0 - c0 % 128) in index:
+                        continue
+                    assert not masks[b][m0:min(m0 + 64, r1), c0:c0 + 64].any()
+
+    # the stored-dS workspace holds every block (one head: 16 KB each)
+    for heads, d in ((1, 128), (4, 64)):
+        p = _ws_problem(offs, tg, heads, d, d, k1, k2, ctx)
+        full = lib.sla_workspace_size(ctypes.byref(p), C.SLA_OP_BWD)
+        small = lib.sla_workspace_size(ctypes.byref(p), C.SLA_OP_BWD_RECOMPUTE)
+        assert small > 0 and full >= small
+        if full > small:
+            assert full - small >= heads * len(triples) * 64 * 128 * 2

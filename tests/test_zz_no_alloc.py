@@ -2,8 +2,11 @@
 per-device array, for callers that cannot allocate device memory) against
 sla_bwd with a caller-owned workspace.
 
-Both run the same kernels on the same inputs, and the backward is bitwise
-reproducible, so the gradients must agree bit for bit.  Two calls in a row:
+sla_bwd_noalloc equals sla_bwd given a workspace of the array's size (dS is
+stored for the dQ kernel where it fits, recomputed otherwise), so the
+reference call gets a workspace of that size: both then run the same kernels
+on the same inputs, and the backward is bitwise reproducible, so the
+gradients must agree bit for bit.  Two calls in a row:
 the second on a smaller problem, so it runs on the array as the first call
 left it.  The outputs start as NaN, so an element either call fails to write
 shows up."""
@@ -39,7 +42,8 @@ def _run(i, case):
     tgd = None if w.num_targets is None else torch.from_numpy(w.num_targets).to(DEV)
     kw = dict(k1=w.k1, k2=w.k2, contextual_len=w.contextual_len, max_seq_len=w.max_seq_len,
               alpha=w.alpha)
-    ref = sla.sla_bwd(q, k, v, do, offs, tgd, grad_dtype=gdt, **kw)
+    ws = torch.empty(sla.SLA_NOALLOC_SCRATCH_BYTES, dtype=torch.uint8, device=DEV)
+    ref = sla.sla_bwd(q, k, v, do, offs, tgd, grad_dtype=gdt, workspace=ws, **kw)
     got = tuple(torch.full_like(r, float("nan")) for r in ref)
     sla.sla_bwd_noalloc(q, k, v, do, offs, tgd, dq=got[0], dk=got[1], dv=got[2], **kw)
     torch.cuda.synchronize()
