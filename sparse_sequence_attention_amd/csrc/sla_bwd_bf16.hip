@@ -180,7 +180,7 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
 
     const float nal2e = p.neg_alpha_log2e, alpha = p.alpha;
 
-    // DMA (gl_lds16_async: the kernel's own waits and barriers order it
+    // DMA (gl_lds16_at: the kernel's own waits and barriers order it
     // against the reads).  Thread t owns chunks P = i*NT + t of the [K | V]
     // (or [Q | dO]) pair, K (Q) first: chunk P' of a tile of row width w is
     // physical chunk P' % (w/8) of row P' / (w/8), filled with logical chunk
@@ -188,6 +188,9 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
     // row c1 - 1 (keys never stored); step rows at or past m1 read row m1 - 1
     // (masked: such steps are never full).  Every step issues exactly SPS
     // loads per thread, so the wait counts are static.
+    // wave-uniform LDS byte addresses of this wave's DMA destinations
+    const uint32_t kv_lds = uniform((int)(lds_addr(kvs) + 16u * (uint32_t)(wv * 64)));
+    const uint32_t ring_lds = uniform((int)(lds_addr(ring) + 16u * (uint32_t)(wv * 64)));
     auto issue_kv = [&]() __attribute__((always_inline)) {
         const int last = uniform(it.c1 - 1 - it.c0);
         const char *krow = reinterpret_cast<const char *>(kg + (int64_t)it.c0 * p.ldk);
@@ -215,7 +218,7 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
                 const uint32_t c = (uint32_t)((Pv % CPRV) ^ hswz<DV>(prow));
                 src = vrow + (row * ldv_b + 16u * c);
             }
-            gl_lds16_async(src, kvs + (i * NT + wv * 64) * 8);
+            gl_lds16_at(src, kv_lds + 16u * (uint32_t)(i * NT));
         }
     };
     const uint32_t ldq_b = (uint32_t)p.ldq * 2u, lddo_b = (uint32_t)p.lddo * 2u;
@@ -226,7 +229,7 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
         const int last = uniform(m1 - 1 - m0);
         const char *qrow = reinterpret_cast<const char *>(qg + (int64_t)m0 * p.ldq);
         const char *grow = reinterpret_cast<const char *>(gg + (int64_t)m0 * p.lddo);
-        uint16_t *sb = ring + (t % NST) * (SLOTS * 8);
+        const uint32_t sb = ring_lds + (uint32_t)(t % NST) * (16u * SLOTS);
 #pragma unroll
         for (int i = 0; i < SPS; ++i) {
             const int P = i * NT + wv * 64 + lane;
@@ -253,7 +256,7 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
                 const uint32_t c = (uint32_t)((Pg % CPRV) ^ hswz<DV>(prow));
                 src = grow + (row * lddo_b + 16u * c);
             }
-            gl_lds16_async(src, sb + (i * NT + wv * 64) * 8);
+            gl_lds16_at(src, sb + 16u * (uint32_t)(i * NT));
         }
     };
 
@@ -341,8 +344,17 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
         // wait for this step's DMA (the newest (NST - 2) SPS loads, those of
         // the following steps, may still be in flight), publish it with a
         // barrier that also frees stage (t + NST - 1) % NST (read by step
-        // t - 1), and start the DMA of step t + NST - 1 into it
-        vm_wait<(NST - 2) * SPS>();
+        // t - 1), and start the DMA of step t + NST - 1 into it.  With the dS
+        // stores, which the vector memory counter tracks in issue order with
+        // the loads, the two stores of each of steps t - 2 and t - 1 are
+        // newer than this step's DMA too (from step 2 on).
+        if constexpr (STORE_DS) {
+            static_assert(NST == 3, "the store-aware wait counts assume a ring of three");
+            if (t >= 2) vm_wait<SPS + 4>();
+            else vm_wait<SPS>();
+        } else {
+            vm_wait<(NST - 2) * SPS>();
+        }
         barrier_lds();
         issue(t + NST - 1);
         const uint32_t sb = lds_base + KV_BYTES + (uint32_t)uniform(t % NST) * STAGE_BYTES;
@@ -398,7 +410,7 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void sla_bwd_dkdv_bf16_kernel(Attn
             if constexpr (STORE_DS) {
                 const int blk = t + (t < nh ? ds_dh : ds_dt);
                 uint8_t *dst = ds_wave + (int64_t)blk * DS_BLOCK_BYTES + 1024 * h2 + 16 * lane;
-                st16_global(dst, as_u4(da));
+                st16_global_stream(dst, as_u4(da));
             }
             bf16x8 pl, dl;
             if constexpr (split) {

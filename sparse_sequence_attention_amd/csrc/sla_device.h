@@ -112,6 +112,31 @@ __device__ __forceinline__ void gl_lds16_async(const void *src, uint16_t *lds_wa
                  : "memory", "m0");
 }
 
+// As gl_lds16_async with the LDS destination as a wave-uniform byte address
+// (the address-space cast of a generic pointer costs scalar instructions per
+// call; the kernels form these addresses once), and the non-temporal form
+// for data read once (kept from displacing the L2 working set).
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+__device__ __forceinline__ void gl_lds16_at(const void *src, uint32_t lds_byte_addr)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds_byte_addr)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ void gl_lds16_at_stream(const void *src, uint32_t lds_byte_addr)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :
+                 : "v"(src), "s"(lds_byte_addr)
+                 : "memory", "m0");
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding.
 // The s_waitcnt builtin (rather than inline asm) lets the compiler's own wait
 // tracking see the wait, so it adds no conservative vmcnt(0) later; the empty
@@ -176,14 +201,15 @@ __device__ __forceinline__ int sload_i32(const int32_t *ptr)
     return v;
 }
 
-// 16-byte store through a global-address-space pointer (global_store_dwordx4;
-// a generic pointer would give a flat store, which the LDS wait counter
-// tracks too).
+// 16-byte streaming store through a global-address-space pointer
+// (global_store_dwordx4 nt: data read once, by a later kernel, so it should
+// not displace the working set of this one from the L2; a generic pointer
+// would give a flat store, which the LDS wait counter tracks too).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void st16_global(void *p, const uint4 &v)
+__device__ __forceinline__ void st16_global_stream(void *p, const uint4 &v)
 {
     const u32x4 w = {v.x, v.y, v.z, v.w};
-    *(__attribute__((address_space(1))) u32x4 *)p = w;
+    __builtin_nontemporal_store(w, (__attribute__((address_space(1))) u32x4 *)p);
 }
 
 // 16 bytes at column `col` of row r of a [rows][ld] bf16 tensor, zero when

@@ -296,7 +296,7 @@ __global__ __launch_bounds__(256, 2) void sla_bwd_dq_kernel(AttnParams p)
 // The dS stream comes from HBM (no reuse), so the kernel keeps several steps
 // in flight: one workgroup of eight waves per CU, a ring of four stages of
 // [K rows | dS] (16 + 16 KB at d = 128) filled by DMA three steps ahead,
-// with the wait counts of the dK/dV kernel (gl_lds16_async: the DMA is
+// with the wait counts of the dK/dV kernel (gl_lds16_at: the DMA is
 // ordered by the kernel's own waits and barriers).  Wave w takes rows
 // 32 (w % 4) .. + 32 of the row tile and the d blocks of half w / 4 of dQ.
 // Needs d_qk >= 64 (two 32-wide halves).
@@ -409,6 +409,7 @@ __global__ __launch_bounds__(DQS_THREADS, 1) void sla_bwd_dq_stored_kernel(AttnP
     // the addresses are fixed for the item; the step adds its key offset and
     // the two blocks.  Returns the two coverage bits of the step.
     const uint32_t ldk_b = (uint32_t)p.ldk * 2u;
+    const uint32_t wave_lds = uniform((int)(lds_addr(lds) + 16u * (uint32_t)(wv * 64)));
     uint32_t kprow[SPS], kcol[SPS], dlane[SPS], dfrag[SPS];
     bool dhalf1[SPS];
 #pragma unroll
@@ -429,15 +430,15 @@ __global__ __launch_bounds__(DQS_THREADS, 1) void sla_bwd_dq_stored_kernel(AttnP
         const uint32_t kwo = (uint32_t)(c0 & (BWD_BN - 1)) * 64u;  // (key block of c0) x 2 KB
         const char *b0 = ds_head + (blk0 < 0 ? 0 : (int64_t)blk0 * DS_BLOCK_BYTES + kwo);
         const char *b1 = ds_head + (blk1 < 0 ? 0 : (int64_t)blk1 * DS_BLOCK_BYTES + kwo);
-        uint16_t *sb = lds + (t & (NST - 1)) * STAGE;
+        const uint32_t sb = wave_lds + (uint32_t)(t & (NST - 1)) * (2u * STAGE);
 #pragma unroll
         for (int i = 0; i < SPS; ++i) {
-            const char *src;
             if ((TCH % NT == 0) ? (i * NT < TCH) : (i * NT + wv * 64 < TCH))
-                src = krow + ((kprow[i] < last ? kprow[i] : last) * ldk_b + kcol[i]);
-            else
-                src = (dhalf1[i] ? b1 : b0) + (dfrag[i] + dlane[i]);
-            gl_lds16_async(src, sb + (i * NT + wv * 64) * 8);
+                gl_lds16_at(krow + ((kprow[i] < last ? kprow[i] : last) * ldk_b + kcol[i]),
+                            sb + 16u * (uint32_t)(i * NT));
+            else  // dS: read once
+                gl_lds16_at_stream((dhalf1[i] ? b1 : b0) + (dfrag[i] + dlane[i]),
+                                   sb + 16u * (uint32_t)(i * NT));
         }
         return (blk0 >= 0 ? 1u : 0u) | (blk1 >= 0 ? 2u : 0u);
     };
@@ -472,30 +473,50 @@ __global__ __launch_bounds__(DQS_THREADS, 1) void sla_bwd_dq_stored_kernel(AttnP
             const uint32_t sh = 2u * (uint32_t)((t + NST - 1) & (NST - 1));
             vis = (vis & ~(3u << sh)) | (issue(t + NST - 1) << sh);
             const uint16_t *sk = lds + (t & (NST - 1)) * STAGE;
-            // this wave's row half sees the step
+            // this wave's row half sees the step: all LDS reads of the step
+            // first (the four dS fragments, the K^T operands), then the two
+            // independent identity products, then the conversions and the dQ
+            // products, so that no MFMA waits on the one just before it
             if ((vis >> (2 * (t & (NST - 1)) + (rb >> 1))) & 1u) {
+                bf16x8 fr[2][2];
+                uint2 kt[2][2][NDBW][2];
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    const uint16_t *fr = sk + TCH * 8 + (2 * rb + kb) * 1024;
-                    const bf16x8 f0 = *reinterpret_cast<const bf16x8 *>(fr + 8 * lane);
-                    const bf16x8 f1 = *reinterpret_cast<const bf16x8 *>(fr + 512 + 8 * lane);
-                    floatx16 tr = mfma32(f0, id0, zero16());
-                    tr = mfma32(f1, id1, tr);
-                    const bf16x8 d0 = cvt8(tr[0], tr[1], tr[2], tr[3], tr[4], tr[5], tr[6], tr[7]);
-                    const bf16x8 d1 =
-                        cvt8(tr[8], tr[9], tr[10], tr[11], tr[12], tr[13], tr[14], tr[15]);
+                    const uint16_t *f = sk + TCH * 8 + (2 * rb + kb) * 1024 + 8 * lane;
+                    fr[kb][0] = *reinterpret_cast<const bf16x8 *>(f);
+                    fr[kb][1] = *reinterpret_cast<const bf16x8 *>(f + 512);
+                }
 #pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2) {
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                        for (int dw = 0; dw < NDBW; ++dw)
+#pragma unroll
+                            for (int rr = 0; rr < 2; ++rr)
+                                kt[kb][h2][dw][rr] = tr_read_b64(sk + t_off(kb, h2, rr, dh * NDBW + dw));
+                floatx16 tr[2];
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    tr[kb] = mfma32(fr[kb][0], id0, zero16());
+                    tr[kb] = mfma32(fr[kb][1], id1, tr[kb]);
+                }
+                __builtin_amdgcn_sched_barrier(0);  // both pairs issue before any conversion
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const bf16x8 d0 = cvt8(tr[kb][0], tr[kb][1], tr[kb][2], tr[kb][3], tr[kb][4],
+                                           tr[kb][5], tr[kb][6], tr[kb][7]);
+                    const bf16x8 d1 = cvt8(tr[kb][8], tr[kb][9], tr[kb][10], tr[kb][11],
+                                           tr[kb][12], tr[kb][13], tr[kb][14], tr[kb][15]);
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
                         for (int dw = 0; dw < NDBW; ++dw) {
-                            const int db = dh * NDBW + dw;
-                            const uint2 k0 = tr_read_b64(sk + t_off(kb, h2, 0, db));
-                            const uint2 k1v = tr_read_b64(sk + t_off(kb, h2, 1, db));
+                            const uint2 k0 = kt[kb][h2][dw][0], k1v = kt[kb][h2][dw][1];
                             dqacc[dw] = mfma32(
                                 __builtin_bit_cast(bf16x8, make_uint4(k0.x, k0.y, k1v.x, k1v.y)),
                                 h2 ? d1 : d0, dqacc[dw]);
                         }
-                    }
                 }
             }
         }
