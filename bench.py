@@ -80,7 +80,7 @@ def parse():
 # kernels whose HBM traffic the bench line reports, by the name rocprofv3 gives them
 PMC_KERNELS = {"fwd": "sla_fwd_bf16_kernel<128, 128, false",
                "bwd_dkdv": "sla_bwd_dkdv_bf16_kernel<128, 128",
-               "bwd_dq": "sla_bwd_dq_kernel<128, 128"}
+               "bwd_dq": "sla_bwd_dq_stored_kernel<128"}
 CALIB_BYTES = 256 * 1024 * 1024
 CALIB_NAME = "neg_kernel_cuda"
 
@@ -216,9 +216,10 @@ def main():
     value = useful / (ms_step * 1e-3) / 1e12
     tokens_s = w.total_tokens / (ms_step * 1e-3)
     # algorithmic MFMA work of each kernel (per launch): forward S and P.V; dK/dV
-    # kernel S, dP, dV, dK; dQ kernel S, dP, dQ (its S and dP recompute what the
-    # dK/dV kernel formed: 2d of its 6d per pair are useful)
-    kernel_flops = {"fwd": pairs * 4 * d, "bwd_dkdv": pairs * 8 * d, "bwd_dq": pairs * 6 * d}
+    # kernel S, dP, dV, dK; dQ kernel dQ = dS K from the dS the dK/dV kernel
+    # stored (the default workspace holds it; its two transposing products
+    # per 32 x 32 block are not counted)
+    kernel_flops = {"fwd": pairs * 4 * d, "bwd_dkdv": pairs * 8 * d, "bwd_dq": pairs * 2 * d}
     dom = max(kernel_flops, key=lambda n: phase[n])
     achieved = kernel_flops[dom] / (phase[dom] * 1e-3) / 1e12
     traffic = None
