@@ -470,8 +470,6 @@ __global__ __launch_bounds__(DQS_THREADS, 1) void sla_bwd_dq_stored_kernel(AttnP
             // t + 128 (loop step t + 125), several barriers later
             if ((t & (DQS_TABLE / 2 - 1)) == 0 && t > 0 && t + DQS_TABLE / 2 < ntiles)
                 fill(t + DQS_TABLE / 2);
-            const uint32_t sh = 2u * (uint32_t)((t + NST - 1) & (NST - 1));
-            vis = (vis & ~(3u << sh)) | (issue(t + NST - 1) << sh);
             const uint16_t *sk = lds + (t & (NST - 1)) * STAGE;
             // this wave's row half sees the step: all LDS reads of the step
             // first (the four dS fragments, the K^T operands), then the two
@@ -519,6 +517,13 @@ __global__ __launch_bounds__(DQS_THREADS, 1) void sla_bwd_dq_stored_kernel(AttnP
                         }
                 }
             }
+            // the DMA of step t + NST - 1 into the stage step t - 1 read (free
+            // since the barrier), after this step's products: the waves start
+            // their products right after the barrier, and the scalar work of
+            // the issue, on the CU's one scalar unit, runs under other waves'
+            // products
+            const uint32_t sh = 2u * (uint32_t)((t + NST - 1) & (NST - 1));
+            vis = (vis & ~(3u << sh)) | (issue(t + NST - 1) << sh);
         }
         vm_wait<0>();  // no DMA (of the clamped steps past the end) left in flight
     }
