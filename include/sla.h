@@ -112,16 +112,16 @@ enum { SLA_OP_FWD = 0, SLA_OP_BWD = 1, SLA_OP_BWD_RECOMPUTE = 2 };
  * sequence, each cut into at most 16 row chunks: up to
  * 64 * 128 * H * (d_qk + d_v) * 4 bytes per sequence, about 17 MB for 8
  * sequences, 4 heads, d = 128).  On the bf16 path with d_qk >= 64,
- * SLA_OP_BWD adds room for
- * dS: the dK/dV kernel stores the bf16 dS of every visited 64-row x 128-key
- * tile (16 KB each, per head) and the dQ kernel reads it back instead of
- * recomputing S and dO.V^T (an upper bound from the sizes: about 1.1 GB
- * for 110K tokens, 4 heads, K1 = 1024, K2 = 128, with 2 bytes per visible
- * pair actually written).  That room is only requested where it stays
- * within 16 times the bytes of Q, K, V and dO (windows K1 up to about 8K
- * at d = 128); otherwise, and with SLA_OP_BWD_RECOMPUTE, the size is the
- * schedule and partials only, with which sla_bwd recomputes in the dQ
- * kernel.  Depends only on host-known fields.  Returns 0 if p is invalid. */
+ * SLA_OP_BWD adds room for dS: the dK/dV kernel stores the bf16 dS of every
+ * visited 64-row x 128-key tile (16 KB each, per head) and the dQ kernel
+ * reads it back instead of recomputing S and dO.V^T (an upper bound from
+ * the sizes: 1.19 GB for 110K tokens in 8 sequences, 4 heads, K1 = 1024,
+ * K2 = 128, of which 1.08 GB are written).  That room is only requested
+ * where it stays within 16 times the bytes of Q, K, V and dO (windows K1
+ * up to about 8K at d = 128); otherwise, and with SLA_OP_BWD_RECOMPUTE,
+ * the size is the schedule and partials only, with which sla_bwd
+ * recomputes in the dQ kernel.  Depends only on host-known fields.
+ * Returns 0 if p is invalid. */
 size_t sla_workspace_size(const sla_problem_t *p, int op);
 
 /* SLA forward (ULTRA-HSTU paper, section 4.2.1 Eq.6-7 with Eq.3):

@@ -295,9 +295,10 @@ __global__ __launch_bounds__(256, 2) void sla_bwd_dq_kernel(AttnParams p)
 //
 // The dS stream comes from HBM (no reuse), so the kernel keeps several steps
 // in flight: one workgroup of eight waves per CU, a ring of four stages of
-// [K rows | dS] (16 + 16 KB at d = 128) filled by DMA three steps ahead,
-// with the wait counts of the dK/dV kernel (gl_lds16_at: the DMA is
-// ordered by the kernel's own waits and barriers).  Wave w takes rows
+// [K rows | dS] (16 + 16 KB at d = 128) filled by DMA three steps ahead
+// (the dS in the non-temporal form: read once), with the wait counts of the
+// dK/dV kernel (gl_lds16_at: the DMA is ordered by the kernel's own waits
+// and barriers).  Wave w takes rows
 // 32 (w % 4) .. + 32 of the row tile and the d blocks of half w / 4 of dQ.
 // Needs d_qk >= 64 (two 32-wide halves).
 constexpr int DQS_THREADS = 512;
