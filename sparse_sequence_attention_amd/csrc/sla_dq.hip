@@ -283,9 +283,8 @@ __global__ __launch_bounds__(256, 2) void sla_bwd_dq_kernel(AttnParams p)
 // kernel reads those blocks instead of recomputing S, dO.V^T and SiLU': per
 // pair 2 bytes read back against 4 d flops and two transcendentals.  The
 // fragment has the keys in the lane dimension; dQ contracts over keys, so
-// the kernel turns it around with two MFMAs against a 0/1 identity (exact:
-// one product of a bf16 value by 1 per output, the rest zeros), which leaves
-// dS^T with the rows in the lane dimension, the B operand layout of
+// the kernel gathers it with transposing LDS reads into the B operand
+// layout, rows in the lane dimension, of
 //   dQ^T (D x 32 rows) += K^T dS^T        (as the recomputing kernel).
 // Same work items (128-row tiles), key tiles and order as the recomputing
 // kernel, and each dQ accumulator adds the same products in the same order,
@@ -375,24 +374,35 @@ __global__ __launch_bounds__(DQS_THREADS, 1) void sla_bwd_dq_stored_kernel(AttnP
     const char *const ds_head = reinterpret_cast<const char *>(p.ds) +
                                 (int64_t)h * p.ds_head_blocks * DS_BLOCK_BYTES;
 
-    // 0/1 identity B operands: lane (hl, n = l32) holds k-slot 8 hl + s, the
-    // fragment row 16 h2 + 8 (s / 4) + 4 hl + s % 4, as 1 when that row is n
-    bf16x8 id0, id1;
+    // dS^T operands by transposing reads.  A stored fragment (32 keys x 32
+    // rows) is made of 8-byte runs of four consecutive rows at one key: lane
+    // (hl_f, key) of the dK/dV wave holds, for h2 = 0, 1, rows 16 h2 + 4 hl_f
+    // .. + 3, then 16 h2 + 8 + 4 hl_f .. + 3.  In a 16-lane pass of
+    // ds_read_b64_tr_b16, lane j pointing at the run (key k0 + j / 4, rows
+    // 16 h2 + 4 (j % 4) ..) hands lane i row 16 h2 + i at keys k0 .. k0 + 3:
+    // four k-slots of the B operand of dQ^T += K^T dS^T, rows in the lane
+    // dimension.  Two such reads give the slots of a 16-key chunk h2k in the
+    // order of the K^T operand (keys 16 h2k + 4 hl + 0..3, then + 8), the
+    // bf16 values the recomputing kernel converts from its accumulator.  The
+    // DMA stores key k of the hl_f = 1 half at slot k ^ 4, so that the two
+    // halves of a pass fall in different banks.  Element offsets within the
+    // stage's dS area, per (32-key block, 16-key chunk, first / second four
+    // keys):
+    uint32_t dso[2][2][2];
     {
-        uint32_t e0[4], e1[4];
+        const int i16 = lane & 15, g = i16 & 3, h2r = (lane >> 4) & 1;
 #pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) {
-            e0[w2] = e1[w2] = 0;
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int s2 = 2 * w2 + half;
-                const int row = 8 * (s2 >> 2) + 4 * hl + (s2 & 3);
-                e0[w2] |= (row == l32 ? 0x3F80u : 0u) << (16 * half);
-                e1[w2] |= (row + 16 == l32 ? 0x3F80u : 0u) << (16 * half);
-            }
-        }
-        id0 = as_bf16x8(make_uint4(e0[0], e0[1], e0[2], e0[3]));
-        id1 = as_bf16x8(make_uint4(e1[0], e1[1], e1[2], e1[3]));
+            for (int h2k = 0; h2k < 2; ++h2k)
+#pragma unroll
+                for (int part = 0; part < 2; ++part) {
+                    const int key = 16 * h2k + 4 * hl + 8 * part + (i16 >> 2);
+                    const int hf = g & 1;
+                    const int bytes = (2 * rb + kb) * 2048 + h2r * 1024 +
+                                      (hf * 32 + (key ^ (4 * hf))) * 16 + (g >> 1) * 8;
+                    dso[kb][h2k][part] = (uint32_t)(TCH * 8 + bytes / 2);
+                }
     }
 
     floatx16 dqacc[NDBW];
@@ -419,7 +429,10 @@ __global__ __launch_bounds__(DQS_THREADS, 1) void sla_bwd_dq_stored_kernel(AttnP
         kprow[i] = (uint32_t)(P / CPR);
         kcol[i] = 16u * (uint32_t)((P % CPR) ^ qswz<DQK>(P / CPR));
         const int f = imax(i * NT + wv * 64 - TCH, 0) / 128;  // wave-uniform
-        dlane[i] = 16u * (uint32_t)(P & 127);
+        // LDS chunk c of a fragment (h2 = c / 64, lane (hl_f, key) = c % 64)
+        // takes the stored chunk of key key ^ 4 hl_f
+        const int c = P & 127, hf = (c >> 5) & 1;
+        dlane[i] = 16u * (uint32_t)((c & ~31) | ((c & 31) ^ (4 * hf)));
         dfrag[i] = (uint32_t)(4 * ((f >> 1) & 1) + (f & 1)) * 2048u;
         dhalf1[i] = f >= 4;
     }
@@ -473,50 +486,37 @@ __global__ __launch_bounds__(DQS_THREADS, 1) void sla_bwd_dq_stored_kernel(AttnP
                 fill(t + DQS_TABLE / 2);
             const uint16_t *sk = lds + (t & (NST - 1)) * STAGE;
             // this wave's row half sees the step: all LDS reads of the step
-            // first (the four dS fragments, the K^T operands), then the two
-            // independent identity products, then the conversions and the dQ
-            // products, so that no MFMA waits on the one just before it
+            // first (the dS^T and K^T operands), then the products
             if ((vis >> (2 * (t & (NST - 1)) + (rb >> 1))) & 1u) {
-                bf16x8 fr[2][2];
+                uint2 dt[2][2][2];
                 uint2 kt[2][2][NDBW][2];
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const uint16_t *f = sk + TCH * 8 + (2 * rb + kb) * 1024 + 8 * lane;
-                    fr[kb][0] = *reinterpret_cast<const bf16x8 *>(f);
-                    fr[kb][1] = *reinterpret_cast<const bf16x8 *>(f + 512);
-                }
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2)
+                    for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+                        for (int part = 0; part < 2; ++part)
+                            dt[kb][h2][part] = tr_read_b64(sk + dso[kb][h2][part]);
 #pragma unroll
                         for (int dw = 0; dw < NDBW; ++dw)
 #pragma unroll
                             for (int rr = 0; rr < 2; ++rr)
                                 kt[kb][h2][dw][rr] = tr_read_b64(sk + t_off(kb, h2, rr, dh * NDBW + dw));
-                floatx16 tr[2];
+                    }
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    tr[kb] = mfma32(fr[kb][0], id0, zero16());
-                    tr[kb] = mfma32(fr[kb][1], id1, tr[kb]);
-                }
-                __builtin_amdgcn_sched_barrier(0);  // both pairs issue before any conversion
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const bf16x8 d0 = cvt8(tr[kb][0], tr[kb][1], tr[kb][2], tr[kb][3], tr[kb][4],
-                                           tr[kb][5], tr[kb][6], tr[kb][7]);
-                    const bf16x8 d1 = cvt8(tr[kb][8], tr[kb][9], tr[kb][10], tr[kb][11],
-                                           tr[kb][12], tr[kb][13], tr[kb][14], tr[kb][15]);
-#pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2)
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const uint2 a0 = dt[kb][h2][0], a1 = dt[kb][h2][1];
+                        const bf16x8 dsb = __builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y));
 #pragma unroll
                         for (int dw = 0; dw < NDBW; ++dw) {
                             const uint2 k0 = kt[kb][h2][dw][0], k1v = kt[kb][h2][dw][1];
                             dqacc[dw] = mfma32(
-                                __builtin_bit_cast(bf16x8, make_uint4(k0.x, k0.y, k1v.x, k1v.y)),
-                                h2 ? d1 : d0, dqacc[dw]);
+                                __builtin_bit_cast(bf16x8, make_uint4(k0.x, k0.y, k1v.x, k1v.y)), dsb,
+                                dqacc[dw]);
                         }
-                }
+                    }
             }
             // the DMA of step t + NST - 1 into the stage step t - 1 read (free
             // since the barrier), after this step's products: the waves start
