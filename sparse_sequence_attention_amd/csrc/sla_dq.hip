@@ -292,20 +292,21 @@ __global__ __launch_bounds__(256, 2) void sla_bwd_dq_kernel(AttnParams p)
 // the dK/dV schedule does not visit for a key tile sees none of its keys and
 // is skipped.
 //
-// The dS stream comes from HBM (no reuse), so the kernel keeps several steps
-// in flight: one workgroup of eight waves per CU, a ring of four stages of
-// [K rows | dS] (16 + 16 KB at d = 128) filled by DMA three steps ahead
-// (the dS in the non-temporal form: read once), with the wait counts of the
-// dK/dV kernel (gl_lds16_at: the DMA is ordered by the kernel's own waits
-// and barriers).  Wave w takes rows
+// Two workgroups of eight waves per CU (four waves per SIMD, 94 VGPRs), each
+// with a ring of two stages of [K rows | dS] (16 + 16 KB at d = 128) filled
+// by DMA one step ahead (the dS in the non-temporal form: read once), with
+// the wait counts of the dK/dV kernel (gl_lds16_at: the DMA is ordered by the
+// kernel's own waits and barriers); measured 5% faster than one workgroup
+// with four stages three steps ahead: the second workgroup hides the first
+// one's barriers and latencies.  Wave w takes rows
 // 32 (w % 4) .. + 32 of the row tile and the d blocks of half w / 4 of dQ.
 // Needs d_qk >= 64 (two 32-wide halves).
 constexpr int DQS_THREADS = 512;
-constexpr int DQS_STAGES = 4;
+constexpr int DQS_STAGES = 2;
 constexpr int DQS_TABLE = 256;  // step table entries (two halves of 128)
 
 template <int DQK, bool OUTF32>
-__global__ __launch_bounds__(DQS_THREADS, 1) void sla_bwd_dq_stored_kernel(AttnParams p)
+__global__ __launch_bounds__(DQS_THREADS, 2) void sla_bwd_dq_stored_kernel(AttnParams p)
 {
     constexpr int BM = FWD_BM, BN = FWD_BN;
     constexpr int NT = DQS_THREADS, NST = DQS_STAGES;
@@ -317,8 +318,8 @@ __global__ __launch_bounds__(DQS_THREADS, 1) void sla_bwd_dq_stored_kernel(AttnP
     constexpr int STAGE = (TCH + DCH) * 8;         // elements of a stage: [K | dS]
     static_assert(BN == 64 && BM == 128 && BWD_BN == 128 && BWD_BM == 64,
                   "64-key steps over 128-row tiles; dS blocks of 64 rows x 128 keys");
-    static_assert(NDB >= 2 && TCH % 128 == 0 && (TCH + DCH) % NT == 0 && SPS <= 8 && NST == 4,
-                  "two d halves; the K / dS split is wave-uniform; whole DMA rounds; a ring of 4");
+    static_assert(NDB >= 2 && TCH % 128 == 0 && (TCH + DCH) % NT == 0 && SPS <= 8 && (NST & (NST - 1)) == 0,
+                  "two d halves; the K / dS split is wave-uniform; whole DMA rounds; a ring of 2^n");
     __shared__ __align__(16) uint16_t lds[NST * STAGE];
     // Step table: {first key, dS block of row half 0, of row half 1 (-1: not
     // visited)} of steps t, entry t % DQS_TABLE, filled 128 steps at a time
@@ -481,7 +482,7 @@ __global__ __launch_bounds__(DQS_THREADS, 1) void sla_bwd_dq_stored_kernel(AttnP
             barrier_lds();
             // entries of steps t + 128 .. t + 255 replace those of steps
             // t - 128 .., all used by now; first read by the issue of step
-            // t + 128 (loop step t + 125), several barriers later
+            // t + 128 (at the end of loop step t + 128 - NST + 1), barriers later
             if ((t & (DQS_TABLE / 2 - 1)) == 0 && t > 0 && t + DQS_TABLE / 2 < ntiles)
                 fill(t + DQS_TABLE / 2);
             const uint16_t *sk = lds + (t & (NST - 1)) * STAGE;
