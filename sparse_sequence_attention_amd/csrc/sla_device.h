@@ -98,24 +98,13 @@ __device__ __forceinline__ void gl_lds16(const void *src, uint16_t *lds_wave_bas
 // and later LDS reads (its alias tracking of DMA targets is lost at branch
 // joins, after which it waits for every DMA in flight before any LDS read).
 // The caller orders the data itself: vm_wait for its own DMAs, then a
-// barrier, before any wave reads the destination.  M0 carries the LDS
-// address (wave-uniform); lane l's 16 bytes from `src` land at that address
-// + 16 * l.  No register is written, so nothing of the load's result is
-// left for the compiler to reuse early.
-__device__ __forceinline__ void gl_lds16_async(const void *src, uint16_t *lds_wave_base)
-{
-    const uint32_t lds = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds_wave_base);
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(src), "s"(lds)
-                 : "memory", "m0");
-}
-
-// As gl_lds16_async with the LDS destination as a wave-uniform byte address
-// (the address-space cast of a generic pointer costs scalar instructions per
-// call; the kernels form these addresses once), and the non-temporal form
-// for data read once (kept from displacing the L2 working set).
+// barrier, before any wave reads the destination.  M0 carries the LDS byte
+// address of the wave's destination (wave-uniform; the kernels form these
+// addresses once: the address-space cast of a generic pointer costs scalar
+// instructions per call); lane l's 16 bytes from `src` land at that address
+// + 16 * l.  No register is written, so nothing of the load's result is left
+// for the compiler to reuse early.  The _stream form is non-temporal, for
+// data read once (kept from displacing the L2 working set).
 __device__ __forceinline__ uint32_t lds_addr(const void *p)
 {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
@@ -183,23 +172,6 @@ __device__ __forceinline__ uint2 tr_read_b64(const uint16_t *lds_run)
 }
 
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
-
-// Scalar load of a workgroup-uniform int32 that no kernel running alongside
-// writes (a table the schedule kernel filled before this launch).  The
-// compiler cannot use a scalar load for global memory that the kernel itself
-// stores to, and its vector load would come with a wait for every vector
-// memory operation in flight, DMA included; this one waits for the scalar
-// load alone, in the same statement.
-__device__ __forceinline__ int sload_i32(const int32_t *ptr)
-{
-    const uint64_t a = (uint64_t)(uintptr_t)ptr;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-    const uint64_t sa = ((uint64_t)hi << 32) | lo;
-    int v;
-    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(sa));
-    return v;
-}
 
 // 16-byte streaming store through a global-address-space pointer
 // (global_store_dwordx4 nt: data read once, by a later kernel, so it should
