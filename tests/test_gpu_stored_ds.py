@@ -85,3 +85,25 @@ def test_stored_dq_stages_and_reproducibility():
     for name, x, y, z in zip(("dQ", "dK", "dV"), a, b, got):
         assert torch.equal(x, y), f"{name}: two calls differ"
         assert torch.equal(x, z), f"{name}: staged call differs"
+
+
+@pytest.mark.parametrize("name", ["long_16k", "targets_16k"])
+def test_stored_equals_recomputed_at_full_size(name):
+    """At the full sizes (long_16k: 109,796 tokens, every 64-row step of the
+    prefix and 1024-key window tiles; targets_16k: 201,537 tokens with 256
+    target rows per sequence and their all-target key tiles) the stored-dS
+    backward gives the same bits as the recomputing one: every stored block
+    is written and read back where the schedule numbers it."""
+    w = make_sla_workload(name, seed=0, dtype="bf16", with_dout=True)
+    print(f"[case] stored dS full size {name} T={w.total_tokens}", flush=True)
+    t = lambda a: torch.from_numpy(a).to(DEV).to(torch.bfloat16)  # noqa: E731  (exact)
+    q, k, v, do = t(w.q), t(w.k), t(w.v), t(w.dout)
+    offs = torch.from_numpy(w.offsets).to(DEV)
+    tgd = None if w.num_targets is None else torch.from_numpy(w.num_targets).to(DEV)
+    kw = dict(k1=w.k1, k2=w.k2, contextual_len=w.contextual_len, max_seq_len=w.max_seq_len)
+    st = sla.sla_bwd(q, k, v, do, offs, tgd, **kw)
+    rc = sla.sla_bwd(q, k, v, do, offs, tgd, recompute_dq=True, **kw)
+    torch.cuda.synchronize()
+    for nm, a, b in zip(("dQ", "dK", "dV"), st, rc):
+        assert torch.isfinite(a.float()).all(), nm
+        assert torch.equal(a, b), f"{nm} differs between the two paths"

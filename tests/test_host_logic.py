@@ -548,3 +548,17 @@ def test_stored_ds_blocks(seed, lib):
         assert small > 0 and full >= small
         if full > small:
             assert full - small >= heads * len(triples) * 64 * 128 * 2
+
+
+def test_ds_blocks_host_rejects_bad_input(lib):
+    """sla_ds_blocks_host: invalid problems and layouts return -1 with a
+    message; an empty batch has no blocks."""
+    offs = np.array([0, 100, 50], dtype=np.int64)   # decreasing: a negative length
+    with pytest.raises(ValueError):
+        ops.ds_blocks_host(offs, None, k1=8, k2=0)
+    with pytest.raises(ValueError):
+        ops.ds_blocks_host(np.array([0, 10], np.int64), np.array([11], np.int32), k1=8, k2=0)
+    with pytest.raises(ValueError):
+        ops.ds_blocks_host(np.array([0, 10], np.int64), None, k1=-1, k2=0)
+    assert len(ops.ds_blocks_host(np.array([0], np.int64), None, k1=8, k2=0)) == 0
+    assert lib.sla_ds_blocks_host(None, None, None, None, 0) == -1
