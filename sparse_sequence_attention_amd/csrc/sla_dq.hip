@@ -482,10 +482,17 @@ __global__ __launch_bounds__(DQS_THREADS, 2) void sla_bwd_dq_stored_kernel(AttnP
             barrier_lds();
             // entries of steps t + 128 .. t + 255 replace those of steps
             // t - 128 .., all used by now; first read by the issue of step
-            // t + 128 (at the end of loop step t + 128 - NST + 1), barriers later
+            // t + 128 (after the barrier of loop step t + 128 - NST + 1), barriers later
             if ((t & (DQS_TABLE / 2 - 1)) == 0 && t > 0 && t + DQS_TABLE / 2 < ntiles)
                 fill(t + DQS_TABLE / 2);
             const uint16_t *sk = lds + (t & (NST - 1)) * STAGE;
+            // the DMA of step t + NST - 1 into the stage step t - 1 read (free
+            // since the barrier), before this step's products so that it is in
+            // flight under them
+            {
+                const uint32_t sh = 2u * (uint32_t)((t + NST - 1) & (NST - 1));
+                vis = (vis & ~(3u << sh)) | (issue(t + NST - 1) << sh);
+            }
             // this wave's row half sees the step: all LDS reads of the step
             // first (the dS^T and K^T operands), then the products
             if ((vis >> (2 * (t & (NST - 1)) + (rb >> 1))) & 1u) {
@@ -524,8 +531,6 @@ __global__ __launch_bounds__(DQS_THREADS, 2) void sla_bwd_dq_stored_kernel(AttnP
             // their products right after the barrier, and the scalar work of
             // the issue, on the CU's one scalar unit, runs under other waves'
             // products
-            const uint32_t sh = 2u * (uint32_t)((t + NST - 1) & (NST - 1));
-            vis = (vis & ~(3u << sh)) | (issue(t + NST - 1) << sh);
         }
         vm_wait<0>();  // no DMA (of the clamped steps past the end) left in flight
     }
