@@ -46,7 +46,12 @@ COMMON_FLAGS = [
 HIP_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # Per-file code generation choices.  dK/dV: MFMA results in VGPRs (the S and
 # dP accumulators feed VALU code; left in AGPRs they are copied out first).
-SOURCE_FLAGS: dict = {"sla_bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Forward and dK/dV: the instruction-level-parallelism scheduling strategy
+# (measured about 1% faster than the default occupancy-driven one on both, with
+# the same register counts and no spills; slower on dQ).
+_ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
+SOURCE_FLAGS: dict = {"sla_bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"] + _ILP,
+                      "sla_fwd_bf16.hip": _ILP}
 
 
 def _hipcc() -> str:

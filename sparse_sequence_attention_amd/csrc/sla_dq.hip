@@ -447,7 +447,8 @@ __global__ __launch_bounds__(DQS_THREADS, 2) void sla_bwd_dq_stored_kernel(AttnP
         const char *b1 = ds_head + (blk1 < 0 ? 0 : (int64_t)blk1 * DS_BLOCK_BYTES + kwo);
         const uint32_t sb = wave_lds + (uint32_t)(t & (NST - 1)) * (2u * STAGE);
 #pragma unroll
-        for (int i = 0; i < SPS; ++i) {
+        for (int ii = 0; ii < SPS; ++ii) {
+            const int i = SPS - 1 - ii;  // the dS loads (from HBM) first, then the K rows (L2)
             if ((TCH % NT == 0) ? (i * NT < TCH) : (i * NT + wv * 64 < TCH))
                 gl_lds16_at(krow + ((kprow[i] < last ? kprow[i] : last) * ldk_b + kcol[i]),
                             sb + 16u * (uint32_t)(i * NT));
