@@ -337,6 +337,12 @@ def bench_jagged_graph(args):
 
     pairs = sla.count_pairs_host(w.offsets, None, w.k1, w.k2, w.contextual_len) * H
     useful = pairs * (2 * (d + d) + 2 * (3 * d + 2 * d))
+    # compulsory HBM bytes of the step per token and head: the forward reads
+    # q, k, v (bf16) and writes O (fp32); the backward reads q, k, v, dO and
+    # writes dQ, dK, dV (fp32).  At K1 = 256 the arithmetic intensity is below
+    # the ridge, so the step is rated against HBM bandwidth too.
+    compulsory = w.total_tokens * H * ((3 * 2 * d + 4 * d) + (4 * 2 * d + 3 * 4 * d))
+    hbm_gbs = compulsory / (graph_ms * 1e-3) / 1e9
     line = {
         "metric": "SLA fwd+bwd useful TFLOP/s (jagged_2k, eager and HIP graph replay)",
         "value": round(useful / (graph_ms * 1e-3) / 1e12, 2),
@@ -357,6 +363,10 @@ def bench_jagged_graph(args):
         "eager_tflops": round(useful / (eager_ms * 1e-3) / 1e12, 2),
         "graph_ms_per_step": round(graph_ms, 4),
         "tokens_per_s": round(w.total_tokens / (graph_ms * 1e-3), 1),
+        "roofline": {"kernel": "step (fwd + bwd), compulsory bytes", "bound": "hbm",
+                     "achieved": round(hbm_gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(hbm_gbs / 8000.0, 4), "traffic": None,
+                     "compulsory_bytes": int(compulsory)},
     }
     print(json.dumps(line), flush=True)
 
