@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--outputs", choices=("f32", "bf16"), default="f32",
                     help="long_16k: dtype of O, dQ, dK, dV (inputs are bf16 either way); f32 is "
                          "the configuration the parity tests hold to the stated bar")
+    ap.add_argument("--dq", choices=("stored", "recompute"), default="stored",
+                    help="long_16k: dQ from the dS the dK/dV kernel stores (default workspace), "
+                         "or recomputed with the smallest workspace")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peak-probe", action="store_true",
                     help="skip the MFMA-only probe (run after the timed steps) that reports the "
@@ -166,6 +169,8 @@ def main():
     ws = torch.empty(max(sla.workspace_size(p, sla.SLA_OP_BWD),
                          sla.workspace_size(p, sla.SLA_OP_FWD)), dtype=torch.uint8, device=dev)
 
+    recompute = args.dq == "recompute"
+
     def step(ev=None):
         if ev is not None:
             ev[0].record()
@@ -173,15 +178,15 @@ def main():
         if ev is not None:
             ev[1].record()
         sla.sla_bwd(q, k, v, do, offs, None, dq=dq, dk=dk, dv=dv, workspace=ws,
-                    stage=sla.SLA_BWD_PREPARE, **kw)
+                    stage=sla.SLA_BWD_PREPARE, recompute_dq=recompute, **kw)
         if ev is not None:
             ev[2].record()
         sla.sla_bwd(q, k, v, do, offs, None, dq=dq, dk=dk, dv=dv, workspace=ws,
-                    stage=sla.SLA_BWD_DKDV, **kw)
+                    stage=sla.SLA_BWD_DKDV, recompute_dq=recompute, **kw)
         if ev is not None:
             ev[3].record()
         sla.sla_bwd(q, k, v, do, offs, None, dq=dq, dk=dk, dv=dv, workspace=ws,
-                    stage=sla.SLA_BWD_DQ, **kw)
+                    stage=sla.SLA_BWD_DQ, recompute_dq=recompute, **kw)
         if ev is not None:
             ev[4].record()
 
@@ -216,14 +221,14 @@ def main():
     value = useful / (ms_step * 1e-3) / 1e12
     tokens_s = w.total_tokens / (ms_step * 1e-3)
     # algorithmic MFMA work of each kernel (per launch): forward S and P.V; dK/dV
-    # kernel S, dP, dV, dK; dQ kernel dQ = dS K from the dS the dK/dV kernel
-    # stored (the default workspace holds it; its two transposing products
-    # per 32 x 32 block are not counted)
+    # kernel S, dP, dV, dK; dQ kernel dQ = dS K (from the stored dS by default;
+    # with --dq recompute its recomputed S and dP are not counted)
     kernel_flops = {"fwd": pairs * 4 * d, "bwd_dkdv": pairs * 8 * d, "bwd_dq": pairs * 2 * d}
     dom = max(kernel_flops, key=lambda n: phase[n])
     achieved = kernel_flops[dom] / (phase[dom] * 1e-3) / 1e12
     traffic = None
-    if os.path.exists(args.traffic):
+    # the committed counters were taken on the default (stored-dS) backward
+    if os.path.exists(args.traffic) and not (recompute and dom.startswith("bwd")):
         with open(args.traffic) as f:
             traffic = json.load(f).get(dom, {}).get("hbm_bytes")
 
@@ -242,7 +247,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{WORKLOAD}: {cfg.description}, N={cfg.max_seq_len}, seed {args.seed}",
-            "outputs": args.outputs,
+            "outputs": args.outputs, "dq": args.dq,
             "total_tokens": w.total_tokens,
             "visible_pairs_all_heads": pairs,
             "useful_flop_per_step": useful,
